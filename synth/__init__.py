@@ -1,0 +1,128 @@
+"""Seeded synthetic inputs for the mHC pre-mapping forward.
+
+Shared by the tests, the smoke check and the benchmark, and by both sides of
+every comparison (the HIP library and the CPU oracle). It holds no step of the
+method itself: only random draws and the float32 -> bf16 conversion that turns
+drawn activations into the bf16 tensor the operator consumes.
+
+Recipe (per workload, NumPy PCG64 seeded with ``seed``), tensors drawn in this
+order, each in C order:
+  x       [T, n, D]  float32 N(0, 1), then rounded to bf16 (nearest, ties to even);
+                     drawn in chunks of ``X_CHUNK`` values (the stream is identical
+                     to a single draw, the chunking only bounds host memory)
+  phi     [M, n*D]   float32 N(0, 1) / sqrt(n*D)   (std 1/sqrt(n*D): mixes stay O(1))
+  gamma   [n, D]     float32 U(0.5, 1.5)            (only when the workload has gamma)
+  alpha   [3] or [2] float32 U(0.5, 1.5)
+  bias    [M]        float32 N(0, 0.1)               (0.1 is the standard deviation)
+  pre_mix [T, n]     float32 U(0, 1)                 (only when the workload has pre_mix)
+with M = n*n + 2n for a 3-entry alpha and 2n for a 2-entry alpha.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+X_CHUNK = 1 << 24
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); returns uint16 bits.
+
+    NaN stays NaN (quiet); values that round past the largest bf16 become inf.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    rounded = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x0040)).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class Workload:
+    name: str
+    T: int
+    n: int
+    D: int
+    n_alpha: int = 3
+    gamma: bool = False
+    pre_mix: bool = False
+    need_backward: bool = False
+    num_iters: int = 20
+    norm_eps: float = 1e-6
+    hc_eps: float = 1e-6
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def M(self) -> int:
+        return self.n * self.n + 2 * self.n if self.n_alpha == 3 else 2 * self.n
+
+    @property
+    def K(self) -> int:
+        return self.n * self.D
+
+
+# The five workloads the method is measured on (sizes and distributions as stated
+# for this build's configurations; seeds 1001..1005).
+WORKLOADS = {
+    "tiny": Workload("tiny", T=128, n=4, D=256, seed=1001,
+                     note="T=128, n=4, D=256, no gamma, needBackward=false"),
+    "mid_prefill": Workload("mid_prefill", T=4096, n=4, D=4096, gamma=True, seed=1002,
+                            note="T=4096 (b=1, s=4096), n=4, D=4096, gamma [4, 4096]"),
+    "large_prefill_bwd": Workload("large_prefill_bwd", T=16384, n=4, D=7168,
+                                  need_backward=True, seed=1003,
+                                  note="T=16384 (b=4, s=4096), n=4, D=7168, needBackward=true"),
+    "decode": Workload("decode", T=64, n=4, D=7168, seed=1004,
+                       note="T=64, n=4, D=7168, 1000 back-to-back launches"),
+    "wide_premix": Workload("wide_premix", T=32768, n=8, D=2048, n_alpha=2, pre_mix=True,
+                            seed=1005,
+                            note="T=32768, n=8, D=2048, alpha[2], external pre_mix [T, 8]"),
+}
+
+
+@dataclass
+class Inputs:
+    wl: Workload
+    x: np.ndarray            # uint16 bf16 bits [T, n, D]
+    phi: np.ndarray          # float32 [M, n*D]
+    alpha: np.ndarray        # float32 [n_alpha]
+    bias: np.ndarray         # float32 [M]
+    gamma: np.ndarray | None = None    # float32 [n, D]
+    pre_mix: np.ndarray | None = None  # float32 [T, n]
+    extra: dict = field(default_factory=dict)
+
+
+def generate(wl: Workload, seed: int | None = None) -> Inputs:
+    """Draw one workload's inputs with the recipe in the module docstring."""
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    total = wl.T * wl.n * wl.D
+    x = np.empty(total, dtype=np.uint16)
+    for start in range(0, total, X_CHUNK):
+        stop = min(total, start + X_CHUNK)
+        x[start:stop] = f32_to_bf16_bits(rng.standard_normal(stop - start, dtype=np.float32))
+    x = x.reshape(wl.T, wl.n, wl.D)
+    K = wl.K
+    phi = (rng.standard_normal((wl.M, K), dtype=np.float32) / np.float32(np.sqrt(K))).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, size=(wl.n, wl.D)).astype(np.float32) if wl.gamma else None
+    alpha = rng.uniform(0.5, 1.5, size=(wl.n_alpha,)).astype(np.float32)
+    bias = (rng.standard_normal(wl.M) * 0.1).astype(np.float32)
+    pre_mix = rng.uniform(0.0, 1.0, size=(wl.T, wl.n)).astype(np.float32) if wl.pre_mix else None
+    return Inputs(wl, x, phi, alpha, bias, gamma, pre_mix)
+
+
+def custom(T: int, n: int, D: int, *, n_alpha: int = 3, gamma: bool = False,
+           pre_mix: bool = False, need_backward: bool = False, num_iters: int = 20,
+           seed: int = 7, name: str = "custom") -> Inputs:
+    """Same distributions at any shape (test sizes: tails, page example shapes)."""
+    wl = Workload(name, T=T, n=n, D=D, n_alpha=n_alpha, gamma=gamma, pre_mix=pre_mix,
+                  need_backward=need_backward, num_iters=num_iters, seed=seed)
+    return generate(wl)
