@@ -1,0 +1,153 @@
+/*
+ * mhc.h -- C ABI of the fused mHC pre-mapping forward for AMD Instinct MI355X (gfx950).
+ *
+ * What one call computes, per token t (x viewed as xFlat of length K = n*D):
+ *   invRms = (mean(xFlat^2) + normEps)^(-1/2)
+ *   hMix   = (xFlat (.) gammaFlat) . phi^T            (gamma optional)
+ *   w      = hMix * invRms, split [n, n, n*n] (alpha has 3 entries) or [n, n] (2 entries)
+ *   hPre   = sigmoid(alpha0 * wPre + biasPre) + hcEps
+ *   hPost  = 2 sigmoid(alpha1 * wPost + biasPost)   (+ hcEps when alpha has 2 entries)
+ *   hRes   = Sinkhorn(alpha2 * wRes + biasRes)       (0 when alpha has 2 entries)
+ *   hIn[d] = sum_i weight_i * x[i][d], weight = pre_mix[t] if given, else hPre
+ * Sources:
+ *   - aclnnMhcPreV2 guide (kwkr.cn/news/422178), section 3 (math semantics) and
+ *     section 5 (inputs/outputs, optional outputs, shapes);
+ *   - aclnnMhcPreSinkhorn guide (m.mzlw.cn/news/197063), section 3.2 (Sinkhorn steps:
+ *     a row softmax + hcEps, then alternating column/row normalisations with + hcEps on
+ *     every sum, 2*numIters steps, hRes = normOut[2*numIters-1]), section 4 (two-phase
+ *     call), section 5.1 (needBackward outputs and their shapes), section 6 (error codes);
+ *   - HcPre guide (mhpn.cn/news/2282827), function prototype (pre_mix, hc_pre output)
+ *     and parameter defaults (numIters 20, normEps = hcEps = 1e-6).
+ *
+ * Layout and ownership. Every tensor is a caller-owned, contiguous, row-major device
+ * buffer in the TND layout (a [B, S, n, D] input is the same bytes as [B*S, n, D]).
+ * bf16 tensors are passed as raw 16-bit patterns. The library allocates nothing,
+ * keeps no state between calls, and never synchronises the stream.
+ *
+ * Errors. Every entry point validates on the host before any HIP call and returns:
+ *   MHC_OK                 success (also for T == 0: nothing is launched);
+ *   MHC_ERR_NULLPTR        a required pointer is NULL;
+ *   MHC_ERR_PARAM_INVALID  unsupported size or attribute, inconsistent output set,
+ *                          misaligned pointer, or a buffer smaller than required;
+ *   MHC_ERR_RUNTIME        a HIP call (kernel launch) failed.
+ * The three codes have the values the aclnnMhcPreSinkhorn guide (section 6) lists for
+ * the same three classes. Kernel faults surface at the caller's next synchronisation.
+ */
+#ifndef MHC_H
+#define MHC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mhc_status;
+
+#define MHC_OK 0
+#define MHC_ERR_NULLPTR 161001
+#define MHC_ERR_PARAM_INVALID 161002
+#define MHC_ERR_RUNTIME 361001
+
+/* Problem description (host memory; read during the call only).
+ *   T              tokens, >= 0
+ *   n              hyper-streams (hcMult): 4 or 8
+ *   D              hidden size per stream: > 0 and a multiple of 8
+ *   n_alpha        3 (pre/post/res branches, phi has n*n+2n rows) or
+ *                  2 (pre/post only, phi has 2n rows, hRes = 0)
+ *   num_iters      Sinkhorn iterations, >= 1 (ignored when n_alpha == 2)
+ *   norm_eps       > 0 (RMS guard);  hc_eps >= 0 (gate / Sinkhorn guard)
+ *   need_backward  0 or 1; with 1 the backward intermediates are mandatory outputs
+ *   reserved       must be 0 */
+typedef struct mhc_pre_params {
+    int64_t T;
+    int32_t n;
+    int32_t D;
+    int32_t n_alpha;
+    int32_t num_iters;
+    double norm_eps;
+    double hc_eps;
+    int32_t need_backward;
+    int32_t reserved;
+} mhc_pre_params;
+
+/* Device pointers. M = n*n + 2n (n_alpha == 3) or 2n (n_alpha == 2); it = num_iters.
+ * Inputs:
+ *   x          bf16 [T, n, D], 16-byte aligned                           required
+ *   phi        f32  [M, n*D]                          required unless phi_packed is given
+ *   alpha      f32  [n_alpha]                                            required
+ *   bias       f32  [M]                                                  required
+ *   gamma      f32  [n, D]          scales the projection input only     optional
+ *   pre_mix    f32  [T, n]          hIn weights instead of hPre          optional
+ *   phi_packed from mhc_pre_prepack for these (n, D, n_alpha, gamma)     optional; when
+ *              given, phi and gamma are not read
+ * Outputs (must not alias inputs or each other):
+ *   h_in       bf16 [T, D], 16-byte aligned                              required
+ *   h_post     f32  [T, n]                                               required
+ *   h_res      f32  [T, n, n]    required when n_alpha == 3; with n_alpha == 2 it may be
+ *                                NULL, else it is filled with zeros
+ *   inv_rms    f32  [T]          optional (required with need_backward)
+ *   h_mix      f32  [T, M]       un-normalised projection; optional (required with need_backward)
+ *   h_pre      f32  [T, n]       optional (required with need_backward)
+ *   sum_out    f32  [2*it, T, n]       step-major Sinkhorn sums; only with n_alpha == 3;
+ *                                optional (required with need_backward and n_alpha == 3);
+ *                                plane 0 holds the row softmax denominators
+ *   norm_out   f32  [2*it, T, n, n]    step-major Sinkhorn matrices; same rules as sum_out */
+typedef struct mhc_pre_tensors {
+    const uint16_t* x;
+    const float* phi;
+    const float* alpha;
+    const float* bias;
+    const float* gamma;
+    const float* pre_mix;
+    const void* phi_packed;
+    uint16_t* h_in;
+    float* h_post;
+    float* h_res;
+    float* inv_rms;
+    float* h_mix;
+    float* h_pre;
+    float* sum_out;
+    float* norm_out;
+} mhc_pre_tensors;
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mhc_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* mhc_status_string(mhc_status status);
+
+/* Bytes of the packed projection weights for this problem (phi with gamma folded in,
+ * split into three bf16 terms and ordered for the matrix cores). Host only; T is
+ * ignored. Errors: NULLPTR, PARAM_INVALID. */
+mhc_status mhc_pre_packed_size(const mhc_pre_params* params, size_t* bytes);
+
+/* Bytes of device workspace mhc_pre_forward needs for this problem. Host only.
+ * The workspace must be zero-filled once after allocation; every call leaves its
+ * internal counters at zero again, so it can be reused without clearing.
+ * Concurrent calls need distinct workspaces. Errors: NULLPTR, PARAM_INVALID. */
+mhc_status mhc_pre_workspace_size(const mhc_pre_params* params, size_t* bytes);
+
+/* Packs phi (f32 [M, n*D]) and the optional gamma (f32 [n, D]) into phi_packed
+ * (device, >= mhc_pre_packed_size bytes, 16-byte aligned) asynchronously on `stream`
+ * (a hipStream_t; NULL = the default stream). Weights are static across calls, so a
+ * caller can pack once and pass phi_packed to every forward. T is ignored.
+ * Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
+mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const float* gamma,
+                           void* phi_packed, size_t packed_bytes, void* stream);
+
+/* The fused forward, asynchronous on `stream` (a hipStream_t; NULL = default stream).
+ * Emits every non-NULL output listed in mhc_pre_tensors. `workspace` is device memory
+ * of at least mhc_pre_workspace_size bytes, 256-byte aligned, zero-filled once after
+ * allocation. When tensors->phi_packed is NULL the weights are packed into the
+ * workspace first (one extra kernel). Results are bitwise reproducible for the same
+ * inputs and parameters. Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
+mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHC_H */

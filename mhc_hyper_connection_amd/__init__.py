@@ -1,0 +1,184 @@
+"""Fused mHC pre-mapping forward for AMD Instinct MI355X (gfx950).
+
+Python face of the C-ABI library libmhc.so (include/mhc.h). Per token it computes
+invRms, the projection hMix = (x * gamma) . phi^T, the sigmoid pre/post gates, a
+2*numIters-step Sinkhorn of the n x n residual block and the collapse
+hIn = sum_i weight_i * x_i (aclnnMhcPreV2 guide, kwkr.cn/news/422178, section 3;
+aclnnMhcPreSinkhorn guide, m.mzlw.cn/news/197063, section 3.2; HcPre guide,
+mhpn.cn/news/2282827, function prototype for pre_mix).
+
+PyTorch is used for device memory and the current HIP stream only; the work runs in
+the library's kernels, and nothing here falls back to another implementation.
+"""
+from __future__ import annotations
+
+import math
+
+from ._binding import (MHC_ERR_NULLPTR, MHC_ERR_PARAM_INVALID, MHC_ERR_RUNTIME, MHC_OK,
+                       MhcError, Params, load, make_params, packed_size, raw_forward,
+                       raw_prepack, status_string, version, workspace_size)
+
+__all__ = ["PreForward", "mhc_pre", "prepack", "version", "status_string", "MhcError",
+           "make_params", "packed_size", "workspace_size", "load",
+           "MHC_OK", "MHC_ERR_NULLPTR", "MHC_ERR_PARAM_INVALID", "MHC_ERR_RUNTIME"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes_void(torch.cuda.current_stream(device).cuda_stream)
+
+
+def ctypes_void(handle):
+    import ctypes
+    return ctypes.c_void_p(handle) if handle else None
+
+
+def _check(t, name, dtype, shape, device):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+class PreForward:
+    """Launcher for one problem size. Owns a workspace zero-filled once at creation.
+
+    Calls issued through one instance must not overlap (they share the workspace);
+    calls on one stream are ordered by the stream and are safe.
+    """
+
+    def __init__(self, T, n, D, n_alpha=3, *, num_iters=20, norm_eps=1e-6, hc_eps=1e-6,
+                 need_backward=False, device="cuda"):
+        torch = _torch()
+        load()
+        self.T, self.n, self.D, self.n_alpha = int(T), int(n), int(D), int(n_alpha)
+        self.num_iters = int(num_iters)
+        self.need_backward = bool(need_backward)
+        self.M = n * n + 2 * n if n_alpha == 3 else 2 * n
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.params = make_params(T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward)
+        self.ws_bytes = workspace_size(self.params)
+        self.packed_bytes = packed_size(self.params)
+        self.workspace = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+
+    # -- outputs -----------------------------------------------------------------------
+    def alloc_outputs(self, *, intermediates=None):
+        """torch.empty outputs. intermediates: None (what need_backward requires),
+        True (all of them) or False (only hIn, hPost, hRes)."""
+        torch = _torch()
+        T, n, D, M, dev = self.T, self.n, self.D, self.M, self.device
+        f32 = dict(dtype=torch.float32, device=dev)
+        want = self.need_backward if intermediates is None else bool(intermediates)
+        out = {"h_in": torch.empty((T, D), dtype=torch.bfloat16, device=dev),
+               "h_post": torch.empty((T, n), **f32),
+               "h_res": torch.empty((T, n, n), **f32)}
+        if want:
+            out["inv_rms"] = torch.empty((T,), **f32)
+            out["h_mix"] = torch.empty((T, M), **f32)
+            out["h_pre"] = torch.empty((T, n), **f32)
+            if self.n_alpha == 3:
+                out["sum_out"] = torch.empty((2 * self.num_iters, T, n), **f32)
+                out["norm_out"] = torch.empty((2 * self.num_iters, T, n, n), **f32)
+        return out
+
+    # -- weights -----------------------------------------------------------------------
+    def prepack(self, phi, gamma=None, out=None):
+        torch = _torch()
+        _check(phi, "phi", torch.float32, (self.M, self.n * self.D), self.device)
+        _check(gamma, "gamma", torch.float32, (self.n, self.D), self.device)
+        if out is None:
+            out = torch.empty(self.packed_bytes, dtype=torch.uint8, device=self.device)
+        st = raw_prepack(self.params, _ptr(phi), _ptr(gamma), _ptr(out), out.numel(),
+                         _stream(self.device))
+        if st != MHC_OK:
+            raise MhcError(st, "mhc_pre_prepack")
+        return out
+
+    # -- forward -----------------------------------------------------------------------
+    def __call__(self, x, phi, alpha, bias, gamma=None, pre_mix=None, *, phi_packed=None,
+                 out=None):
+        torch = _torch()
+        T, n, D, M, dev = self.T, self.n, self.D, self.M, self.device
+        _check(x, "x", torch.bfloat16, (T, n, D), dev)
+        if phi_packed is None:
+            _check(phi, "phi", torch.float32, (M, n * D), dev)
+        _check(alpha, "alpha", torch.float32, (self.n_alpha,), dev)
+        _check(bias, "bias", torch.float32, (M,), dev)
+        _check(gamma, "gamma", torch.float32, (n, D), dev)
+        _check(pre_mix, "pre_mix", torch.float32, (T, n), dev)
+        if out is None:
+            out = self.alloc_outputs()
+        ptrs = {"x": _ptr(x), "phi": _ptr(phi), "alpha": _ptr(alpha), "bias": _ptr(bias),
+                "gamma": _ptr(gamma), "pre_mix": _ptr(pre_mix), "phi_packed": _ptr(phi_packed)}
+        for k, v in out.items():
+            ptrs[k] = _ptr(v)
+        st = raw_forward(self.params, ptrs, _ptr(self.workspace), self.ws_bytes,
+                         _stream(dev))
+        if st != MHC_OK:
+            raise MhcError(st, "mhc_pre_forward")
+        return out
+
+
+_RUNNERS: dict = {}
+
+
+def _runner(T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward, device):
+    key = (T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward, str(device))
+    r = _RUNNERS.get(key)
+    if r is None:
+        r = PreForward(T, n, D, n_alpha, num_iters=num_iters, norm_eps=norm_eps, hc_eps=hc_eps,
+                       need_backward=need_backward, device=device)
+        _RUNNERS[key] = r
+    return r
+
+
+def prepack(phi, gamma=None, *, n, n_alpha=3):
+    """Pack static weights once; pass the result as phi_packed to mhc_pre."""
+    D = phi.shape[1] // n
+    return _runner(1, n, D, n_alpha, 20, 1e-6, 1e-6, False, phi.device).prepack(phi, gamma)
+
+
+def mhc_pre(x, phi, alpha, bias, gamma=None, pre_mix=None, *, num_iters=20, norm_eps=1e-6,
+            hc_eps=1e-6, need_backward=False, phi_packed=None):
+    """Fused pre-mapping forward. x: bf16 [T, n, D] or [B, S, n, D].
+
+    Returns (h_in, h_post, h_res, extras); extras holds inv_rms, h_mix, h_pre, sum_out
+    and norm_out when need_backward is set. Shapes follow x's leading dimensions.
+    """
+    lead = tuple(x.shape[:-2])
+    n, D = int(x.shape[-2]), int(x.shape[-1])
+    T = math.prod(lead) if lead else 1
+    n_alpha = int(alpha.shape[0])
+    r = _runner(T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward, x.device)
+    xf = x.reshape(T, n, D)
+    pm = None if pre_mix is None else pre_mix.reshape(T, n)
+    out = r(xf, phi, alpha, bias, gamma, pm, phi_packed=phi_packed)
+    h_in = out.pop("h_in").reshape(*lead, D)
+    h_post = out.pop("h_post").reshape(*lead, n)
+    h_res = out.pop("h_res").reshape(*lead, n, n)
+    extras = {}
+    for k, v in out.items():
+        if k in ("sum_out", "norm_out"):
+            extras[k] = v.reshape(v.shape[0], *lead, *v.shape[2:])
+        elif k == "inv_rms":
+            extras[k] = v.reshape(*lead)
+        else:
+            extras[k] = v.reshape(*lead, v.shape[-1])
+    return h_in, h_post, h_res, extras

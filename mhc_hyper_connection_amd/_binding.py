@@ -1,0 +1,114 @@
+"""ctypes binding of libmhc.so (include/mhc.h). Argument marshalling only.
+
+PyTorch supplies device memory (torch.empty / torch.zeros) and the HIP stream
+(torch.cuda.current_stream); every step of the computation runs in the library's
+HIP kernels. There is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmhc.so")
+
+MHC_OK = 0
+MHC_ERR_NULLPTR = 161001
+MHC_ERR_PARAM_INVALID = 161002
+MHC_ERR_RUNTIME = 361001
+
+
+class MhcError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("n_alpha", ctypes.c_int32), ("num_iters", ctypes.c_int32),
+                ("norm_eps", ctypes.c_double), ("hc_eps", ctypes.c_double),
+                ("need_backward", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+TENSOR_FIELDS = ("x", "phi", "alpha", "bias", "gamma", "pre_mix", "phi_packed", "h_in",
+                 "h_post", "h_res", "inv_rms", "h_mix", "h_pre", "sum_out", "norm_out")
+
+
+class Tensors(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in TENSOR_FIELDS]
+
+
+EXPORTS = ("mhc_version", "mhc_status_string", "mhc_pre_packed_size",
+           "mhc_pre_workspace_size", "mhc_pre_prepack", "mhc_pre_forward")
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load and bind libmhc.so. Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m mhc_hyper_connection_amd.build` "
+                           "(there is no CPU fallback)")
+    lib = ctypes.CDLL(p)
+    lib.mhc_version.restype = ctypes.c_int
+    lib.mhc_version.argtypes = []
+    lib.mhc_status_string.restype = ctypes.c_char_p
+    lib.mhc_status_string.argtypes = [ctypes.c_int32]
+    lib.mhc_pre_packed_size.restype = ctypes.c_int32
+    lib.mhc_pre_packed_size.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(ctypes.c_size_t)]
+    lib.mhc_pre_workspace_size.restype = ctypes.c_int32
+    lib.mhc_pre_workspace_size.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(ctypes.c_size_t)]
+    lib.mhc_pre_prepack.restype = ctypes.c_int32
+    lib.mhc_pre_prepack.argtypes = [ctypes.POINTER(Params), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.mhc_pre_forward.restype = ctypes.c_int32
+    lib.mhc_pre_forward.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Tensors),
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def version() -> int:
+    return int(load().mhc_version())
+
+
+def status_string(status: int) -> str:
+    return load().mhc_status_string(int(status)).decode()
+
+
+def make_params(T, n, D, n_alpha=3, num_iters=20, norm_eps=1e-6, hc_eps=1e-6,
+                need_backward=False) -> Params:
+    return Params(int(T), int(n), int(D), int(n_alpha), int(num_iters), float(norm_eps),
+                  float(hc_eps), int(bool(need_backward)), 0)
+
+
+def packed_size(params: Params) -> int:
+    out = ctypes.c_size_t(0)
+    st = load().mhc_pre_packed_size(ctypes.byref(params), ctypes.byref(out))
+    if st != MHC_OK:
+        raise MhcError(st, "mhc_pre_packed_size")
+    return int(out.value)
+
+
+def workspace_size(params: Params) -> int:
+    out = ctypes.c_size_t(0)
+    st = load().mhc_pre_workspace_size(ctypes.byref(params), ctypes.byref(out))
+    if st != MHC_OK:
+        raise MhcError(st, "mhc_pre_workspace_size")
+    return int(out.value)
+
+
+def raw_prepack(params: Params, phi_ptr, gamma_ptr, packed_ptr, packed_bytes, stream) -> int:
+    return int(load().mhc_pre_prepack(ctypes.byref(params), phi_ptr, gamma_ptr, packed_ptr,
+                                      packed_bytes, stream))
+
+
+def raw_forward(params: Params, ptrs: dict, ws_ptr, ws_bytes, stream) -> int:
+    t = Tensors(*[ptrs.get(f) for f in TENSOR_FIELDS])
+    return int(load().mhc_pre_forward(ctypes.byref(params), ctypes.byref(t), ws_ptr, ws_bytes, stream))

@@ -1,0 +1,159 @@
+// mhc_api.cpp -- the exported C entry points: validation, planning, dispatch.
+//
+// No HIP header is included here: every check runs on the host before the first HIP
+// call, so the whole file builds with a plain C++ compiler and its error paths can be
+// exercised without a GPU. Kernel launches go through mhc::launch_* (mhc_kernels.hip).
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/mhc.h"
+#include "mhc_plan.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Attribute checks shared by every entry point (the aclnn guides reject unsupported
+// hcMult / numIters / shapes with the invalid-parameter class). T is checked by callers
+// that use it.
+mhc_status check_params(const mhc_pre_params* p, mhc::Geometry* g)
+{
+    if (!p) return MHC_ERR_NULLPTR;
+    if (p->reserved != 0) return MHC_ERR_PARAM_INVALID;
+    if (p->need_backward != 0 && p->need_backward != 1) return MHC_ERR_PARAM_INVALID;
+    if (!(p->norm_eps > 0.0)) return MHC_ERR_PARAM_INVALID;      // also rejects NaN
+    if (!(p->hc_eps >= 0.0)) return MHC_ERR_PARAM_INVALID;
+    if (p->n_alpha == 3 && p->num_iters < 1) return MHC_ERR_PARAM_INVALID;
+    if (p->num_iters < 0 || p->num_iters > 1000) return MHC_ERR_PARAM_INVALID;
+    if (!mhc::make_geometry(p->n, p->D, p->n_alpha, g)) return MHC_ERR_PARAM_INVALID;
+    return MHC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mhc_version(void) { return kVersion; }
+
+const char* mhc_status_string(mhc_status s)
+{
+    switch (s) {
+    case MHC_OK: return "MHC_OK: success";
+    case MHC_ERR_NULLPTR: return "MHC_ERR_NULLPTR: a required pointer is NULL";
+    case MHC_ERR_PARAM_INVALID:
+        return "MHC_ERR_PARAM_INVALID: unsupported size/attribute, inconsistent outputs, "
+               "misaligned pointer or buffer too small";
+    case MHC_ERR_RUNTIME: return "MHC_ERR_RUNTIME: a HIP call failed";
+    default: return "unknown mhc_status";
+    }
+}
+
+mhc_status mhc_pre_packed_size(const mhc_pre_params* params, size_t* bytes)
+{
+    if (!params || !bytes) return MHC_ERR_NULLPTR;
+    mhc::Geometry g;
+    mhc_status st = check_params(params, &g);
+    if (st != MHC_OK) return st;
+    *bytes = g.packed_bytes;
+    return MHC_OK;
+}
+
+mhc_status mhc_pre_workspace_size(const mhc_pre_params* params, size_t* bytes)
+{
+    if (!params || !bytes) return MHC_ERR_NULLPTR;
+    mhc::Geometry g;
+    mhc_status st = check_params(params, &g);
+    if (st != MHC_OK) return st;
+    if (params->T < 0) return MHC_ERR_PARAM_INVALID;
+    *bytes = mhc::make_plan(g, params->T).ws_bytes;
+    return MHC_OK;
+}
+
+mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const float* gamma,
+                           void* phi_packed, size_t packed_bytes, void* stream)
+{
+    if (!params || !phi || !phi_packed) return MHC_ERR_NULLPTR;
+    mhc::Geometry g;
+    mhc_status st = check_params(params, &g);
+    if (st != MHC_OK) return st;
+    if (packed_bytes < g.packed_bytes) return MHC_ERR_PARAM_INVALID;
+    if (!aligned(phi_packed, 16) || !aligned(phi, 4) || (gamma && !aligned(gamma, 4)))
+        return MHC_ERR_PARAM_INVALID;
+    return mhc::launch_prepack(g, phi, gamma, phi_packed, stream) == 0 ? MHC_OK : MHC_ERR_RUNTIME;
+}
+
+mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* t,
+                           void* workspace, size_t workspace_bytes, void* stream)
+{
+    // 1. required pointers
+    if (!params || !t) return MHC_ERR_NULLPTR;
+    if (!t->x || !t->alpha || !t->bias || !t->h_in || !t->h_post) return MHC_ERR_NULLPTR;
+    if (!t->phi && !t->phi_packed) return MHC_ERR_NULLPTR;
+    if (params->n_alpha == 3 && !t->h_res) return MHC_ERR_NULLPTR;
+    if (!workspace) return MHC_ERR_NULLPTR;
+
+    // 2. attributes and sizes
+    mhc::Geometry g;
+    mhc_status st = check_params(params, &g);
+    if (st != MHC_OK) return st;
+    if (params->T < 0) return MHC_ERR_PARAM_INVALID;
+
+    // 3. output set: needBackward makes the intermediates mandatory; the Sinkhorn planes
+    //    exist only with the res branch.
+    const bool res_branch = params->n_alpha == 3;
+    if (!res_branch && (t->sum_out || t->norm_out)) return MHC_ERR_PARAM_INVALID;
+    if (params->need_backward) {
+        if (!t->inv_rms || !t->h_mix || !t->h_pre) return MHC_ERR_PARAM_INVALID;
+        if (res_branch && (!t->sum_out || !t->norm_out)) return MHC_ERR_PARAM_INVALID;
+    }
+
+    // 4. workspace
+    const mhc::Plan plan = mhc::make_plan(g, params->T);
+    if (workspace_bytes < plan.ws_bytes) return MHC_ERR_PARAM_INVALID;
+
+    // 5. alignment: 16-byte vector access to x and hIn, 256-byte workspace sections
+    if (!aligned(t->x, 16) || !aligned(t->h_in, 16) || !aligned(workspace, 256))
+        return MHC_ERR_PARAM_INVALID;
+    if (t->phi_packed && !aligned(t->phi_packed, 16)) return MHC_ERR_PARAM_INVALID;
+    const void* f32s[] = {t->phi, t->alpha, t->bias, t->gamma, t->pre_mix, t->h_post, t->h_res,
+                          t->inv_rms, t->h_mix, t->h_pre, t->sum_out, t->norm_out};
+    for (const void* q : f32s)
+        if (q && !aligned(q, 4)) return MHC_ERR_PARAM_INVALID;
+
+    if (params->T == 0) return MHC_OK;   // empty input: success, nothing launched
+
+    char* ws = static_cast<char*>(workspace);
+    const void* packed = t->phi_packed;
+    if (!packed) {
+        void* dst = ws + plan.off_packed;
+        if (mhc::launch_prepack(g, t->phi, t->gamma, dst, stream) != 0) return MHC_ERR_RUNTIME;
+        packed = dst;
+    }
+
+    mhc::ForwardArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = t->x;
+    a.packed = packed;
+    a.alpha = t->alpha;
+    a.bias = t->bias;
+    a.pre_mix = t->pre_mix;
+    a.h_in = t->h_in;
+    a.h_post = t->h_post;
+    a.h_res = t->h_res;
+    a.inv_rms = t->inv_rms;
+    a.h_mix = t->h_mix;
+    a.h_pre = t->h_pre;
+    a.sum_out = res_branch ? t->sum_out : nullptr;
+    a.norm_out = res_branch ? t->norm_out : nullptr;
+    a.tickets = reinterpret_cast<int32_t*>(ws + plan.off_tickets);
+    a.wts = reinterpret_cast<float*>(ws + plan.off_wts);
+    a.part = reinterpret_cast<float*>(ws + plan.off_part);
+    a.num_iters = params->num_iters;
+    a.norm_eps = params->norm_eps;
+    a.hc_eps = params->hc_eps;
+    return mhc::launch_forward(plan, a, stream) == 0 ? MHC_OK : MHC_ERR_RUNTIME;
+}
+
+}  // extern "C"
