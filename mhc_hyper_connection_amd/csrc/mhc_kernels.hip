@@ -10,14 +10,15 @@
 //                   octet-major order the projection consumes (layout in mhc_plan.h).
 //   proj_kernel     one workgroup = 64 tokens x one d-slice of the reduction. x goes from
 //                   HBM straight into MFMA A-registers (16-byte loads, no LDS); the packed
-//                   weights of each 128-element chunk are staged in LDS and shared by the
-//                   4 waves. v_mfma_f32_16x16x32_bf16 accumulates the 3*M columns; the
+//                   weights of each 128-element chunk are staged in LDS (double-buffered,
+//                   prefetched one chunk ahead) and shared by the 4 waves; x is prefetched
+//                   two chunks ahead. v_mfma_f32_16x16x32_bf16 accumulates the 3*M columns; the
 //                   "hi" columns are moved into fp64 every kFlush chunks so long fp32
 //                   chains do not limit hMix accuracy. Squares are summed on the VALU
 //                   from the same registers. Each workgroup writes fp32 partial sums; the
 //                   last of the S workgroups of a tile (atomic ticket) reduces them in a
-//                   fixed order (deterministic), then runs the gates and the Sinkhorn and
-//                   writes every output except hIn, plus the hIn weights.
+//                   fixed order (deterministic), then runs the gates and a lane-parallel
+//                   Sinkhorn and writes every output except hIn, plus the hIn weights.
 //   hin_kernel      hIn[t, d] = sum_i w[t, i] x[t, i, d], fp32 FMA, one rounding to bf16.
 #include <hip/hip_runtime.h>
 
@@ -101,134 +102,239 @@ prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
     packed[u] = w;
 }
 
-// ------------------------------------------------------------------ epilogue (one token)
+// ------------------------------------------------------------------ cross-workgroup data
 
-__device__ __forceinline__ double sigmoid_d(double z)
+// Partial records travel between workgroups of one launch (possibly on different XCDs,
+// each with its own L2). Agent-scope relaxed atomic stores/loads are coherent across
+// XCDs without the whole-L2 write-back and invalidate a device-scope fence costs: the
+// writer waits for its stores to complete before taking the ticket, and the reader's
+// coherent loads are issued after it observed the ticket.
+__device__ __forceinline__ void st_coherent(float* p, float v)
 {
-    if (z >= 0.0) return 1.0 / (1.0 + exp(-z));
-    const double e = exp(z);
-    return e / (1.0 + e);
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_vmem_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// ------------------------------------------------------------------ tile epilogue
+
+__device__ __forceinline__ float sigmoidf_stable(float z)
+{
+    if (z >= 0.f) return 1.f / (1.f + expf(-z));
+    const float e = expf(z);
+    return e / (1.f + e);
 }
 
-// Reduces the S partial records of token t in slice order, then the gates, Sinkhorn and
-// every per-token output. Runs on one thread per token (the tile's last workgroup).
 template <int N>
-__device__ void epilogue_token(const KArgs& k, int64_t t)
+__device__ __forceinline__ float row_sum(float v)
 {
+#pragma unroll
+    for (int m = 1; m < N; m <<= 1) v += __shfl_xor(v, m);
+    return v;
+}
+template <int N>
+__device__ __forceinline__ float row_max(float v)
+{
+#pragma unroll
+    for (int m = 1; m < N; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+template <int N>
+__device__ __forceinline__ float col_sum(float v)
+{
+#pragma unroll
+    for (int m = N; m < N * N; m <<= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+// Runs on all threads of the tile's last workgroup. `scratch` is LDS of at least
+// 64*(M+1)*8 + 64*8 + 64*N*N*4 bytes.
+//   A  sum the S partial records of each (token, value) in slice order (fp64)
+//   B  invRms per token
+//   C  hMix, gates and residual logits, one (token, row) item per thread
+//   D  Sinkhorn with one lane per matrix entry: 2*num_iters steps, row / column sums by
+//      cross-lane shuffles, coalesced stores of every plane
+template <int N>
+__device__ void tile_epilogue(const KArgs& k, int64_t tile, char* scratch)
+{
+    constexpr int NN = N * N;
     const ForwardArgs& a = k.a;
+    const int tid = threadIdx.x;
     const int M = k.M;
+    const int R = M + 1;
     const int64_t T = k.T;
-    const float* part = a.part + t * k.pstride;
-    const int64_t sstride = T * (int64_t)k.pstride;
+    const int64_t t0 = tile * kTileTokens;
+    double* hm = reinterpret_cast<double*>(scratch);                  // [64][R]
+    double* inv = hm + kTileTokens * R;                               // [64]
+    float* Ls = reinterpret_cast<float*>(inv + kTileTokens);          // [64][NN]
 
-    double ss = 0.0;
-    for (int s = 0; s < k.S; ++s) ss += (double)part[s * sstride + M];
-    const double inv_rms = 1.0 / sqrt(ss / (double)k.K + a.norm_eps);
-    if (a.inv_rms) a.inv_rms[t] = (float)inv_rms;
-
-    const double eps = a.hc_eps;
-    const double a0 = a.alpha[0], a1 = a.alpha[1];
-    const double a2 = k.n_alpha == 3 ? (double)a.alpha[2] : 0.0;
-    float L[N * N];
+    // A: partial sums, eight slices in flight at a time, added in slice order
+    for (int idx = tid; idx < kTileTokens * R; idx += kThreads) {
+        const int tl = idx / R, m = idx % R;
+        const int64_t t = t0 + tl;
+        double acc = 0.0;
+        if (t < T) {
+            const float* p = a.part + t * k.pstride + m;
+            const int64_t ss = T * (int64_t)k.pstride;
+            for (int s = 0; s < k.S; s += 8) {
+                float v[8];
 #pragma unroll
-    for (int i = 0; i < N * N; ++i) L[i] = 0.f;
-
-    for (int m = 0; m < M; ++m) {
-        double hm = 0.0;
-        for (int s = 0; s < k.S; ++s) hm += (double)part[s * sstride + m];
-        if (a.h_mix) a.h_mix[t * M + m] = (float)hm;
-        const double w = hm * inv_rms;
-        if (m < N) {
-            const double hp = sigmoid_d(a0 * w + (double)a.bias[m]) + eps;
-            if (a.h_pre) a.h_pre[t * N + m] = (float)hp;
-            a.wts[t * N + m] = a.pre_mix ? a.pre_mix[t * N + m] : (float)hp;
-        } else if (m < 2 * N) {
-            double hq = 2.0 * sigmoid_d(a1 * w + (double)a.bias[m]);
-            if (k.n_alpha == 2) hq += eps;
-            a.h_post[t * N + (m - N)] = (float)hq;
-        } else {
-            const float z = (float)(a2 * w + (double)a.bias[m]);
+                for (int i = 0; i < 8; ++i) v[i] = (s + i < k.S) ? ld_coherent(p + (s + i) * ss) : 0.f;
 #pragma unroll
-            for (int i = 0; i < N * N; ++i)
-                if (i == m - 2 * N) L[i] = z;
-        }
-    }
-
-    if (k.n_alpha != 3) {
-        if (a.h_res)
-            for (int i = 0; i < N * N; ++i) a.h_res[t * N * N + i] = 0.f;
-        return;
-    }
-
-    // Sinkhorn: step 0 softmax over each row + eps; odd steps normalise columns, even
-    // steps rows; every sum gets + eps; 2*num_iters steps.
-    const float epsf = (float)eps;
-    const int steps = 2 * a.num_iters;
-    float sums[N];
-#pragma unroll
-    for (int r = 0; r < N; ++r) {
-        float mx = L[r * N];
-#pragma unroll
-        for (int c = 1; c < N; ++c) mx = fmaxf(mx, L[r * N + c]);
-        float sum = 0.f;
-#pragma unroll
-        for (int c = 0; c < N; ++c) {
-            L[r * N + c] = expf(L[r * N + c] - mx);
-            sum += L[r * N + c];
-        }
-#pragma unroll
-        for (int c = 0; c < N; ++c) L[r * N + c] = L[r * N + c] / sum + epsf;
-        sums[r] = sum;
-    }
-    for (int step = 0; step < steps; ++step) {
-        if (step > 0) {
-            if (step & 1) {
-#pragma unroll
-                for (int c = 0; c < N; ++c) {
-                    float sum = 0.f;
-#pragma unroll
-                    for (int r = 0; r < N; ++r) sum += L[r * N + c];
-                    sum += epsf;
-#pragma unroll
-                    for (int r = 0; r < N; ++r) L[r * N + c] = L[r * N + c] / sum;
-                    sums[c] = sum;
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < N; ++r) {
-                    float sum = 0.f;
-#pragma unroll
-                    for (int c = 0; c < N; ++c) sum += L[r * N + c];
-                    sum += epsf;
-#pragma unroll
-                    for (int c = 0; c < N; ++c) L[r * N + c] = L[r * N + c] / sum;
-                    sums[r] = sum;
-                }
+                for (int i = 0; i < 8; ++i) acc += (double)v[i];
             }
         }
-        if (a.sum_out) {
-            float* so = a.sum_out + ((int64_t)step * T + t) * N;
-#pragma unroll
-            for (int i = 0; i < N; ++i) so[i] = sums[i];
-        }
-        if (a.norm_out) {
-            float* no = a.norm_out + ((int64_t)step * T + t) * (N * N);
-#pragma unroll
-            for (int i = 0; i < N * N; ++i) no[i] = L[i];
+        hm[idx] = acc;
+    }
+    __syncthreads();
+
+    // B: invRms = (mean of squares over n*D + normEps)^(-1/2)
+    if (tid < kTileTokens) {
+        const int64_t t = t0 + tid;
+        const double r = 1.0 / sqrt(hm[tid * R + M] / (double)k.K + a.norm_eps);
+        inv[tid] = r;
+        if (t < T && a.inv_rms) a.inv_rms[t] = (float)r;
+    }
+    __syncthreads();
+
+    // C: w = hMix * invRms; pre / post gates; residual logits
+    const float eps = (float)a.hc_eps;
+    for (int idx = tid; idx < kTileTokens * M; idx += kThreads) {
+        const int tl = idx / M, m = idx % M;
+        const int64_t t = t0 + tl;
+        const double h = hm[tl * R + m];
+        const double w = h * inv[tl];
+        if (t < T && a.h_mix) a.h_mix[t * M + m] = (float)h;
+        if (m < N) {
+            const float hp = sigmoidf_stable((float)((double)a.alpha[0] * w + (double)a.bias[m])) + eps;
+            if (t < T) {
+                if (a.h_pre) a.h_pre[t * N + m] = hp;
+                a.wts[t * N + m] = a.pre_mix ? a.pre_mix[t * N + m] : hp;
+            }
+        } else if (m < 2 * N) {
+            float hq = 2.f * sigmoidf_stable((float)((double)a.alpha[1] * w + (double)a.bias[m]));
+            if (k.n_alpha == 2) hq += eps;
+            if (t < T) a.h_post[t * N + (m - N)] = hq;
+        } else {
+            Ls[tl * NN + (m - 2 * N)] = (float)((double)a.alpha[2] * w + (double)a.bias[m]);
         }
     }
-#pragma unroll
-    for (int i = 0; i < N * N; ++i) a.h_res[t * N * N + i] = L[i];
+    if (k.n_alpha != 3) {
+        if (a.h_res)
+            for (int idx = tid; idx < kTileTokens * NN; idx += kThreads)
+                if (t0 + idx / NN < T) a.h_res[t0 * NN + idx] = 0.f;
+        return;
+    }
+    __syncthreads();
+
+    // D: Sinkhorn. Lane = (token slot, r, c) with c in the low bits: row sums are xor
+    // shuffles over the c bits, column sums over the r bits.
+    constexpr int TPW = 64 / NN;                        // tokens per wave per round
+    const int lane = tid & 63, wave = tid >> 6;
+    const int e = lane % NN, r = e / N, c = e % N;
+    const int steps = 2 * a.num_iters;
+    for (int base = 0; base < kTileTokens; base += kWaves * TPW) {
+        const int tl = base + wave * TPW + lane / NN;
+        const int64_t t = t0 + tl;
+        const bool live = t < T;
+        float v = Ls[tl * NN + e];
+        const float mx = row_max<N>(v);
+        const float ex = expf(v - mx);
+        float sum = row_sum<N>(ex);
+        v = ex / sum + eps;
+        for (int step = 0; step < steps; ++step) {
+            if (step > 0) {
+                if (step & 1) sum = col_sum<N>(v) + eps;
+                else sum = row_sum<N>(v) + eps;
+                v = v / sum;
+            }
+            if (live) {
+                if (a.sum_out) {
+                    const bool writer = (step & 1) ? (r == 0) : (c == 0);
+                    if (writer) a.sum_out[((int64_t)step * T + t) * N + ((step & 1) ? c : r)] = sum;
+                }
+                if (a.norm_out) a.norm_out[((int64_t)step * T + t) * NN + e] = v;
+            }
+        }
+        if (live) a.h_res[t * NN + e] = v;
+    }
 }
 
 // ------------------------------------------------------------------ projection
+
+// One 128-element chunk of the reduction for this workgroup's 64 tokens, software
+// pipelined: while the chunk's MFMAs run from x registers `xr` and LDS buffer BUF,
+// the next chunk's packed weights are fetched into registers (written to the other
+// LDS buffer at the end) and `xr` is refilled with the chunk two steps ahead. One
+// barrier per chunk.
+template <int NT, int NTHI, int N, int BUF>
+__device__ __forceinline__ void proj_chunk(int ch, int ch1, int tid, int grp, int j, const KArgs& k,
+                                           const uint16_t* xrow, const int (&off)[4],
+                                           const int (&dof)[4], u32x4 (&xr)[4],
+                                           u32x4 (*lds)[kOctets * 16 * NT], f32x4 (&acc)[NT],
+                                           double (&hacc)[NTHI][4], float& ssq, int& since_flush)
+{
+    constexpr int NC = 16 * NT;
+    constexpr int UNITS = kOctets * NC;
+    const u32x4* packed = static_cast<const u32x4*>(k.a.packed);
+    const bool has_next = ch + 1 < ch1;
+    u32x4 pre[NT];
+    if (has_next) {
+        const u32x4* src = packed + (int64_t)(ch + 1) * UNITS;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) pre[i] = src[tid + kThreads * i];
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const u32x4 av = xr[st];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float lo = bf16_lo(av[e]), hi = bf16_hi(av[e]);
+            ssq = fmaf(lo, lo, ssq);
+            ssq = fmaf(hi, hi, ssq);
+        }
+        const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const u32x4 bv = lds[BUF][(4 * st + grp) * NC + nt * 16 + j];
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bv),
+                                                              acc[nt], 0, 0, 0);
+        }
+    }
+    if (++since_flush == kFlush) {
+        since_flush = 0;
+#pragma unroll
+        for (int nt = 0; nt < NTHI; ++nt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hacc[nt][r] += (double)acc[nt][r];
+            acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    if (ch + 2 < ch1) {
+        const int dbase = (ch + 2) * k.dc;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            xr[st] = u32x4{0u, 0u, 0u, 0u};
+            if (dbase + dof[st] < k.D) xr[st] = *reinterpret_cast<const u32x4*>(xrow + off[st] + dbase);
+        }
+    }
+    if (has_next) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) lds[BUF ^ 1][tid + kThreads * i] = pre[i];
+    }
+    __syncthreads();
+}
 
 template <int NT, int NTHI, int N>
 __global__ void __launch_bounds__(kThreads)
 proj_kernel(KArgs k)
 {
     constexpr int NC = 16 * NT;
-    __shared__ u32x4 lds[kOctets * NC];                 // one chunk of packed weights
+    constexpr int UNITS = kOctets * NC;
+    __shared__ u32x4 lds[2][UNITS];                     // double-buffered weight chunks
     __shared__ float lds_ss[kTileTokens][4];
     __shared__ int s_last;
 
@@ -265,43 +371,34 @@ proj_kernel(KArgs k)
 #pragma unroll
         for (int r = 0; r < 4; ++r) hacc[nt][r] = 0.0;
     float ssq = 0.f;
-
-    const u32x4* packed = static_cast<const u32x4*>(k.a.packed);
     int since_flush = 0;
-    for (int ch = ch0; ch < ch1; ++ch) {
-        __syncthreads();
-        const u32x4* src = packed + (int64_t)ch * (kOctets * NC);
+
+    // Prologue: x for the first two chunks in flight, first weight chunk into LDS.
+    u32x4 xa[4], xb[4];
 #pragma unroll
-        for (int i = 0; i < NT; ++i) lds[tid + kThreads * i] = src[tid + kThreads * i];
-        __syncthreads();
-        const int dbase = ch * k.dc;
+    for (int st = 0; st < 4; ++st) { xa[st] = u32x4{0u, 0u, 0u, 0u}; xb[st] = xa[st]; }
+    if (ch0 < ch1) {
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            u32x4 av = {0u, 0u, 0u, 0u};
-            if (dbase + dof[st] < k.D) av = *reinterpret_cast<const u32x4*>(xrow + off[st] + dbase);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float lo = bf16_lo(av[e]), hi = bf16_hi(av[e]);
-                ssq = fmaf(lo, lo, ssq);
-                ssq = fmaf(hi, hi, ssq);
-            }
-            const bf16x8 A = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const u32x4 bv = lds[(4 * st + grp) * NC + nt * 16 + j];
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bv),
-                                                                  acc[nt], 0, 0, 0);
-            }
+            const int d0 = ch0 * k.dc + dof[st];
+            if (d0 < k.D) xa[st] = *reinterpret_cast<const u32x4*>(xrow + off[st] + ch0 * k.dc);
+            const int d1 = (ch0 + 1) * k.dc + dof[st];
+            if (ch0 + 1 < ch1 && d1 < k.D)
+                xb[st] = *reinterpret_cast<const u32x4*>(xrow + off[st] + (ch0 + 1) * k.dc);
         }
-        if (++since_flush == kFlush) {
-            since_flush = 0;
+        const u32x4* src = static_cast<const u32x4*>(k.a.packed) + (int64_t)ch0 * UNITS;
 #pragma unroll
-            for (int nt = 0; nt < NTHI; ++nt) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) hacc[nt][r] += (double)acc[nt][r];
-                acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
+        for (int i = 0; i < NT; ++i) lds[0][tid + kThreads * i] = src[tid + kThreads * i];
+    }
+    __syncthreads();
+
+    for (int ch = ch0; ch < ch1;) {
+        proj_chunk<NT, NTHI, N, 0>(ch, ch1, tid, grp, j, k, xrow, off, dof, xa, lds, acc, hacc, ssq,
+                                   since_flush);
+        if (++ch >= ch1) break;
+        proj_chunk<NT, NTHI, N, 1>(ch, ch1, tid, grp, j, k, xrow, off, dof, xb, lds, acc, hacc, ssq,
+                                   since_flush);
+        ++ch;
     }
 #pragma unroll
     for (int nt = 0; nt < NTHI; ++nt)
@@ -309,8 +406,8 @@ proj_kernel(KArgs k)
         for (int r = 0; r < 4; ++r) hacc[nt][r] += (double)acc[nt][r];
 
     // Per-column totals of this slice into LDS ([64 tokens][NC], fp32), squares per group.
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(lds);
+    // (The last proj_chunk ended with a barrier, so LDS buffer 0 is free.)
+    float* red = reinterpret_cast<float*>(&lds[0][0]);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -322,33 +419,36 @@ proj_kernel(KArgs k)
     lds_ss[wave * 16 + j][grp] = ssq;
     __syncthreads();
 
-    if (tid < kTileTokens) {
-        const int64_t t = tile * kTileTokens + tid;
-        if (t < k.T) {
-            float* dst = k.a.part + ((int64_t)s * k.T + t) * k.pstride;
-            const float* rr = red + tid * NC;
-            for (int m = 0; m < k.M; ++m)
-                dst[m] = (float)((double)rr[m] + (double)rr[k.M + m] + (double)rr[2 * k.M + m]);
-            dst[k.M] = (lds_ss[tid][0] + lds_ss[tid][1]) + (lds_ss[tid][2] + lds_ss[tid][3]);
+    // Partial record of this slice: M projections (hi + mid + lo) and the square sum.
+    const int R = k.M + 1;
+    for (int idx = tid; idx < kTileTokens * R; idx += kThreads) {
+        const int tl = idx / R, m = idx % R;
+        const int64_t t = tile * kTileTokens + tl;
+        if (t >= k.T) continue;
+        float v;
+        if (m < k.M) {
+            const float* rr = red + tl * NC;
+            v = (float)((double)rr[m] + (double)rr[k.M + m] + (double)rr[2 * k.M + m]);
+        } else {
+            v = (lds_ss[tl][0] + lds_ss[tl][1]) + (lds_ss[tl][2] + lds_ss[tl][3]);
         }
+        st_coherent(k.a.part + ((int64_t)s * k.T + t) * k.pstride + m, v);
     }
 
-    // Last-arriver hand-off: the S workgroups of this tile take a ticket; the one that
-    // completes the count owns the epilogue and resets the counter for the next call.
+    // Last-arriver hand-off: the S workgroups of this tile take a ticket once their
+    // records are complete; the one that completes the count owns the epilogue and
+    // resets the counter for the next call.
+    wait_vmem_stores();
     __syncthreads();
     if (tid == 0) {
-        __threadfence();
-        const int prev = atomicAdd(&k.a.tickets[tile], 1);
+        const int prev = __hip_atomic_fetch_add(&k.a.tickets[tile], 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == k.S - 1);
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    if (tid == 0) k.a.tickets[tile] = 0;
-    if (tid < kTileTokens) {
-        const int64_t t = tile * kTileTokens + tid;
-        if (t < k.T) epilogue_token<N>(k, t);
-    }
+    if (tid == 0) __hip_atomic_store(&k.a.tickets[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tile_epilogue<N>(k, tile, reinterpret_cast<char*>(&lds[0][0]));
 }
 
 // ------------------------------------------------------------------ hIn

@@ -1,0 +1,75 @@
+"""The five measured workloads at their full sizes, in the launch configuration the
+benchmark times (one mhc_pre_forward call with unpacked weights).
+
+Where the oracle finishes in seconds every token is compared; at the two largest
+sizes a sample of tokens (first and last tiles plus a seeded random draw) is
+compared element by element, and properties that hold at any size are checked on
+every token: gate ranges, Sinkhorn column sums after the last (column) step, and the
+step relation normOut[k] = normOut[k-1] / sumOut[k] between the emitted planes.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import compare, gpu_forward, run_oracle, summary
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _inputs(name):
+    if name not in _CACHE:
+        _CACHE.clear()
+        _CACHE[name] = synth.generate(synth.WORKLOADS[name])
+    return _CACHE[name]
+
+
+def _sample(T, seed=7, k=448):
+    rng = np.random.default_rng(seed)
+    pick = np.concatenate([np.arange(min(T, 32)), np.arange(max(0, T - 32), T),
+                           rng.choice(T, size=min(T, k), replace=False)])
+    return np.unique(pick)
+
+
+def _log(name, rep):
+    print(f"[workload] {name}: {summary(rep)}", file=sys.stderr, flush=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid_prefill", "decode"])
+def test_workload_full_compare(name):
+    inp = _inputs(name)
+    print(f"[case] {name} full compare", file=sys.stderr, flush=True)
+    g = gpu_forward(inp, intermediates=True)
+    rep = compare(g, run_oracle(inp), inp)
+    _log(name, rep)
+
+
+@pytest.mark.parametrize("name", ["large_prefill_bwd", "wide_premix"])
+def test_workload_sampled_and_properties(name):
+    inp = _inputs(name)
+    wl = inp.wl
+    print(f"[case] {name} sampled compare", file=sys.stderr, flush=True)
+    g = gpu_forward(inp, intermediates=True)
+    tok = _sample(wl.T)
+    rep = compare(g, run_oracle(inp, tokens=tok), inp, tokens=tok)
+    _log(name, rep)
+
+    eps = wl.hc_eps
+    h_pre, h_post = g["h_pre"].astype(np.float64), g["h_post"].astype(np.float64)
+    assert np.all((h_pre > eps) & (h_pre < 1 + eps + 1e-6))
+    if wl.n_alpha == 3:
+        assert np.all((h_post > 0) & (h_post < 2))
+        cols = g["h_res"].astype(np.float64).sum(axis=1)            # [T, n]
+        assert np.all(np.abs(cols - 1.0) <= 1e-5), float(np.abs(cols - 1).max())
+        no, so = g["norm_out"].astype(np.float64), g["sum_out"].astype(np.float64)
+        for k in range(1, no.shape[0]):
+            axis_b = (slice(None), None, slice(None)) if k % 2 else (slice(None), slice(None), None)
+            pred = no[k - 1] / so[k][axis_b]
+            assert np.all(np.abs(no[k] - pred) <= 1e-6 + 1e-5 * np.abs(pred)), k
+        assert np.array_equal(g["h_res"], g["norm_out"][-1])
+    else:
+        assert np.all((h_post > eps) & (h_post < 2 + eps + 1e-6))
+        assert np.all(g["h_res"] == 0.0)
