@@ -124,9 +124,9 @@ const char* mhc_status_string(mhc_status status);
 mhc_status mhc_pre_packed_size(const mhc_pre_params* params, size_t* bytes);
 
 /* Bytes of device workspace mhc_pre_forward needs for this problem. Host only.
- * The workspace must be zero-filled once after allocation; every call leaves its
- * internal counters at zero again, so it can be reused without clearing.
- * Concurrent calls need distinct workspaces. Errors: NULLPTR, PARAM_INVALID. */
+ * The workspace holds per-call intermediate results only (no state carries over
+ * between calls), so it needs no initialisation. Concurrent calls need distinct
+ * workspaces. Errors: NULLPTR, PARAM_INVALID. */
 mhc_status mhc_pre_workspace_size(const mhc_pre_params* params, size_t* bytes);
 
 /* Packs phi (f32 [M, n*D]) and the optional gamma (f32 [n, D]) into phi_packed
@@ -139,8 +139,7 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
 
 /* The fused forward, asynchronous on `stream` (a hipStream_t; NULL = default stream).
  * Emits every non-NULL output listed in mhc_pre_tensors. `workspace` is device memory
- * of at least mhc_pre_workspace_size bytes, 256-byte aligned, zero-filled once after
- * allocation. When tensors->phi_packed is NULL the weights are packed into the
+ * of at least mhc_pre_workspace_size bytes, 256-byte aligned. When tensors->phi_packed is NULL the weights are packed into the
  * workspace first (one extra kernel). Results are bitwise reproducible for the same
  * inputs and parameters. Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
 mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* tensors,

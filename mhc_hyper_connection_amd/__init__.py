@@ -56,7 +56,7 @@ def _check(t, name, dtype, shape, device):
 
 
 class PreForward:
-    """Launcher for one problem size. Owns a workspace zero-filled once at creation.
+    """Launcher for one problem size. Owns the workspace the library needs.
 
     Calls issued through one instance must not overlap (they share the workspace);
     calls on one stream are ordered by the stream and are safe.
@@ -76,7 +76,7 @@ class PreForward:
         self.params = make_params(T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward)
         self.ws_bytes = workspace_size(self.params)
         self.packed_bytes = packed_size(self.params)
-        self.workspace = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
 
     # -- outputs -----------------------------------------------------------------------
     def alloc_outputs(self, *, intermediates=None):

@@ -147,7 +147,6 @@ mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* 
     a.h_pre = t->h_pre;
     a.sum_out = res_branch ? t->sum_out : nullptr;
     a.norm_out = res_branch ? t->norm_out : nullptr;
-    a.tickets = reinterpret_cast<int32_t*>(ws + plan.off_tickets);
     a.wts = reinterpret_cast<float*>(ws + plan.off_wts);
     a.part = reinterpret_cast<float*>(ws + plan.off_part);
     a.num_iters = params->num_iters;

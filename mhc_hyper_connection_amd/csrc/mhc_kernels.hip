@@ -8,14 +8,14 @@
 // Kernels
 //   prepack_kernel  phi (f32) * gamma -> three bf16 terms (hi, mid, lo) in the chunked,
 //                   octet-major order the projection consumes (layout in mhc_plan.h).
-//   proj_kernel     one workgroup = 64 tokens x one d-slice of the reduction. x goes from
+//   proj_kernel     one workgroup = 64 tokens x one K-slice of the reduction. x goes from
 //                   HBM straight into MFMA A-registers (16-byte loads, no LDS); the packed
 //                   weights of each 128-element chunk are staged in LDS (double-buffered,
 //                   prefetched one chunk ahead) and shared by the 4 waves; x is prefetched
 //                   two chunks ahead. v_mfma_f32_16x16x32_bf16 accumulates the 3*M columns; the
 //                   "hi" columns are moved into fp64 every kFlush chunks so long fp32
-//                   chains do not limit hMix accuracy. Squares are summed on the VALU
-//                   from the same registers. Each workgroup writes fp32 partial sums; the
+//                   chains do not limit hMix accuracy. Squares come from the diagonal of
+//                   x x^T on the matrix cores, from the same registers. Each workgroup writes fp32 partial sums; the
 //                   last of the S workgroups of a tile (atomic ticket) reduces them in a
 //                   fixed order (deterministic), then runs the gates and a lane-parallel
 //                   Sinkhorn and writes every output except hIn, plus the hIn weights.
@@ -60,7 +60,6 @@ struct KArgs {
     int M;
     int S;
     int nch;
-    int dc;
     int pstride;
     int n_alpha;
 };
@@ -69,22 +68,20 @@ struct KArgs {
 
 __global__ void __launch_bounds__(256)
 prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
-               u32x4* __restrict__ packed, int n, int D, int M, int NC, int dc, int nch)
+               u32x4* __restrict__ packed, int64_t K, int M, int NC, int nch)
 {
     const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)nch * kOctets * NC;
+    const int64_t total = (int64_t)(nch + 1) * kOctets * NC;
     if (u >= total) return;
     const int c = (int)(u % NC);
     const int64_t r = u / NC;
     const int q = (int)(r % kOctets);
-    const int ch = (int)(r / kOctets);
-    const int d0 = ch * dc + 8 * (q / n);
+    const int64_t ch = r / kOctets;
+    const int64_t k0 = ch * kChunk + 8 * q;
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (c < 3 * M && d0 < D) {
+    if (c < 3 * M && k0 < K) {
         const int term = c / M;
         const int m = c % M;
-        const int64_t K = (int64_t)n * D;
-        const int64_t k0 = (int64_t)(q % n) * D + d0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             // exact product in double, then hi/mid/lo each the nearest bf16 of what is left
@@ -101,23 +98,6 @@ prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
     }
     packed[u] = w;
 }
-
-// ------------------------------------------------------------------ cross-workgroup data
-
-// Partial records travel between workgroups of one launch (possibly on different XCDs,
-// each with its own L2). Agent-scope relaxed atomic stores/loads are coherent across
-// XCDs without the whole-L2 write-back and invalidate a device-scope fence costs: the
-// writer waits for its stores to complete before taking the ticket, and the reader's
-// coherent loads are issued after it observed the ticket.
-__device__ __forceinline__ void st_coherent(float* p, float v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_coherent(const float* p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_vmem_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // ------------------------------------------------------------------ tile epilogue
 
@@ -182,7 +162,7 @@ __device__ void tile_epilogue(const KArgs& k, int64_t tile, char* scratch)
             for (int s = 0; s < k.S; s += 8) {
                 float v[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = (s + i < k.S) ? ld_coherent(p + (s + i) * ss) : 0.f;
+                for (int i = 0; i < 8; ++i) v[i] = (s + i < k.S) ? p[(s + i) * ss] : 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc += (double)v[i];
             }
@@ -265,41 +245,47 @@ __device__ void tile_epilogue(const KArgs& k, int64_t tile, char* scratch)
 
 // ------------------------------------------------------------------ projection
 
-// One 128-element chunk of the reduction for this workgroup's 64 tokens, software
-// pipelined: while the chunk's MFMAs run from x registers `xr` and LDS buffer BUF,
-// the next chunk's packed weights are fetched into registers (written to the other
-// LDS buffer at the end) and `xr` is refilled with the chunk two steps ahead. One
-// barrier per chunk.
-template <int NT, int NTHI, int N, int BUF>
-__device__ __forceinline__ void proj_chunk(int ch, int ch1, int tid, int grp, int j, const KArgs& k,
-                                           const uint16_t* xrow, const int (&off)[4],
-                                           const int (&dof)[4], u32x4 (&xr)[4],
-                                           u32x4 (*lds)[kOctets * 16 * NT], f32x4 (&acc)[NT],
-                                           double (&hacc)[NTHI][4], float& ssq, int& since_flush)
+// x for one full chunk: lane (token row, group g) takes octets g, 4+g, 8+g, 12+g of
+// the chunk, i.e. 16 bytes at element offset 8*(4*st + g) for K-step st. The four loads
+// of a lane cover 64 of the row's 256 contiguous bytes; the 4 groups together cover
+// both cache lines.
+__device__ __forceinline__ void load_x_full(const uint16_t* xrow, int64_t base, int grp, u32x4 (&xr)[4])
+{
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+        xr[st] = *reinterpret_cast<const u32x4*>(xrow + base + 8 * (4 * st + grp));
+}
+
+// The same for the last chunk of a row when K is not a multiple of 128: octets at or
+// beyond K read as zero.
+__device__ __forceinline__ void load_x_tail(const uint16_t* xrow, int64_t base, int64_t K, int grp,
+                                            u32x4 (&xr)[4])
+{
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int64_t k0 = base + 8 * (4 * st + grp);
+        xr[st] = k0 < K ? *reinterpret_cast<const u32x4*>(xrow + k0) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Matrix-core work of one chunk held in x registers `xr` and LDS weight buffer `w`:
+// 4 K-steps x NT column tiles, plus the x tile times its own transpose, whose diagonal
+// accumulates each token's sum of squares (exact bf16 products, fp32 sums), and the
+// periodic fp64 flush of the hi columns.
+template <int NT, int NTHI>
+__device__ __forceinline__ void mma_chunk(const u32x4 (&xr)[4], const u32x4* w, int grp, int j,
+                                          f32x4 (&acc)[NT], double (&hacc)[NTHI][4], f32x4& sq,
+                                          int& since_flush)
 {
     constexpr int NC = 16 * NT;
-    constexpr int UNITS = kOctets * NC;
-    const u32x4* packed = static_cast<const u32x4*>(k.a.packed);
-    const bool has_next = ch + 1 < ch1;
-    u32x4 pre[NT];
-    if (has_next) {
-        const u32x4* src = packed + (int64_t)(ch + 1) * UNITS;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) pre[i] = src[tid + kThreads * i];
-    }
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
         const u32x4 av = xr[st];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float lo = bf16_lo(av[e]), hi = bf16_hi(av[e]);
-            ssq = fmaf(lo, lo, ssq);
-            ssq = fmaf(hi, hi, ssq);
-        }
         const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+        sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, A, sq, 0, 0, 0);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const u32x4 bv = lds[BUF][(4 * st + grp) * NC + nt * 16 + j];
+            const u32x4 bv = w[(4 * st + grp) * NC + nt * 16 + j];
             acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bv),
                                                               acc[nt], 0, 0, 0);
         }
@@ -313,18 +299,31 @@ __device__ __forceinline__ void proj_chunk(int ch, int ch1, int tid, int grp, in
             acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    if (ch + 2 < ch1) {
-        const int dbase = (ch + 2) * k.dc;
+}
+
+// One pipelined step over full chunk `ch`: first the weight loads of chunk ch+1 into
+// registers and the x loads of chunk ch+2 into `xn` (whose last readers were the
+// previous step's MFMAs, behind that step's barrier); then the chunk's MFMAs from `xc` and
+// LDS buffer BUF; then the weights go to the other LDS buffer and one barrier closes
+// the step. The packed weights end with a zero chunk, so the weight prefetch never
+// needs a bounds test.
+template <int NT, int NTHI>
+__device__ __forceinline__ void proj_step(int BUF, int ch, int chf, int tid, int grp, int j, const KArgs& k,
+                                          const uint16_t* xrow, const u32x4 (&xc)[4], u32x4 (&xn)[4],
+                                          u32x4 (*lds)[kOctets * 16 * NT], f32x4 (&acc)[NT],
+                                          double (&hacc)[NTHI][4], f32x4& sq, int& since_flush)
+{
+    constexpr int UNITS = kOctets * 16 * NT;
+    // Weights first: the load counter retires in issue order, so the wait for them at
+    // the end of the step must not also cover the x prefetch issued after them.
+    const u32x4* src = static_cast<const u32x4*>(k.a.packed) + (int64_t)(ch + 1) * UNITS;
+    u32x4 pre[NT];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            xr[st] = u32x4{0u, 0u, 0u, 0u};
-            if (dbase + dof[st] < k.D) xr[st] = *reinterpret_cast<const u32x4*>(xrow + off[st] + dbase);
-        }
-    }
-    if (has_next) {
+    for (int i = 0; i < NT; ++i) pre[i] = src[tid + kThreads * i];
+    if (ch + 2 < chf) load_x_full(xrow, (int64_t)(ch + 2) * kChunk, grp, xn);
+    mma_chunk<NT, NTHI>(xc, lds[BUF], grp, j, acc, hacc, sq, since_flush);
 #pragma unroll
-        for (int i = 0; i < NT; ++i) lds[BUF ^ 1][tid + kThreads * i] = pre[i];
-    }
+    for (int i = 0; i < NT; ++i) lds[BUF ^ 1][tid + kThreads * i] = pre[i];
     __syncthreads();
 }
 
@@ -335,9 +334,7 @@ proj_kernel(KArgs k)
     constexpr int NC = 16 * NT;
     constexpr int UNITS = kOctets * NC;
     __shared__ u32x4 lds[2][UNITS];                     // double-buffered weight chunks
-    __shared__ float lds_ss[kTileTokens][4];
-    __shared__ int s_last;
-
+    __shared__ float lds_ss[kTileTokens];
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -353,15 +350,6 @@ proj_kernel(KArgs k)
     if (tok > k.T - 1) tok = k.T - 1;
     const uint16_t* xrow = k.a.x + tok * k.K;
 
-    // Element offset inside a chunk, and d-offset, of the octet this lane feeds at K-step st.
-    int off[4], dof[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const int q = 4 * st + grp;
-        dof[st] = 8 * (q / N);
-        off[st] = (q % N) * k.D + dof[st];
-    }
-
     f32x4 acc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -370,35 +358,38 @@ proj_kernel(KArgs k)
     for (int nt = 0; nt < NTHI; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) hacc[nt][r] = 0.0;
-    float ssq = 0.f;
+    f32x4 sq = {0.f, 0.f, 0.f, 0.f};   // x x^T of this wave's 16 tokens; diagonal = squares
     int since_flush = 0;
 
-    // Prologue: x for the first two chunks in flight, first weight chunk into LDS.
-    u32x4 xa[4], xb[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) { xa[st] = u32x4{0u, 0u, 0u, 0u}; xb[st] = xa[st]; }
+    // Full chunks [ch0, chf) run through a 3-buffer x pipeline (two chunks in flight
+    // ahead of the one being multiplied) and a 2-buffer LDS weight pipeline; a partial
+    // last chunk of the row (K not a multiple of 128) is done after it.
+    const int nfull = (int)(k.K / kChunk);
+    const int chf = ch1 < nfull ? ch1 : nfull;
+    u32x4 x0[4], x1[4], x2[4];
+    const u32x4* packed = static_cast<const u32x4*>(k.a.packed);
+    if (ch0 < chf) load_x_full(xrow, (int64_t)ch0 * kChunk, grp, x0);
+    if (ch0 + 1 < chf) load_x_full(xrow, (int64_t)(ch0 + 1) * kChunk, grp, x1);
     if (ch0 < ch1) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int d0 = ch0 * k.dc + dof[st];
-            if (d0 < k.D) xa[st] = *reinterpret_cast<const u32x4*>(xrow + off[st] + ch0 * k.dc);
-            const int d1 = (ch0 + 1) * k.dc + dof[st];
-            if (ch0 + 1 < ch1 && d1 < k.D)
-                xb[st] = *reinterpret_cast<const u32x4*>(xrow + off[st] + (ch0 + 1) * k.dc);
-        }
-        const u32x4* src = static_cast<const u32x4*>(k.a.packed) + (int64_t)ch0 * UNITS;
-#pragma unroll
-        for (int i = 0; i < NT; ++i) lds[0][tid + kThreads * i] = src[tid + kThreads * i];
+        for (int i = 0; i < NT; ++i) lds[0][tid + kThreads * i] = packed[(int64_t)ch0 * UNITS + tid + kThreads * i];
     }
     __syncthreads();
 
-    for (int ch = ch0; ch < ch1;) {
-        proj_chunk<NT, NTHI, N, 0>(ch, ch1, tid, grp, j, k, xrow, off, dof, xa, lds, acc, hacc, ssq,
-                                   since_flush);
-        if (++ch >= ch1) break;
-        proj_chunk<NT, NTHI, N, 1>(ch, ch1, tid, grp, j, k, xrow, off, dof, xb, lds, acc, hacc, ssq,
-                                   since_flush);
+    int ch = ch0;
+    while (ch < chf) {
+        proj_step<NT, NTHI>((ch - ch0) & 1, ch, chf, tid, grp, j, k, xrow, x0, x2, lds, acc, hacc, sq, since_flush);
+        if (++ch >= chf) break;
+        proj_step<NT, NTHI>((ch - ch0) & 1, ch, chf, tid, grp, j, k, xrow, x1, x0, lds, acc, hacc, sq, since_flush);
+        if (++ch >= chf) break;
+        proj_step<NT, NTHI>((ch - ch0) & 1, ch, chf, tid, grp, j, k, xrow, x2, x1, lds, acc, hacc, sq, since_flush);
         ++ch;
+    }
+    if (chf < ch1) {
+        // partial last chunk; its weights are in LDS buffer (chf - ch0) & 1
+        load_x_tail(xrow, (int64_t)chf * kChunk, k.K, grp, x0);
+        mma_chunk<NT, NTHI>(x0, lds[(chf - ch0) & 1], grp, j, acc, hacc, sq, since_flush);
+        __syncthreads();
     }
 #pragma unroll
     for (int nt = 0; nt < NTHI; ++nt)
@@ -406,7 +397,7 @@ proj_kernel(KArgs k)
         for (int r = 0; r < 4; ++r) hacc[nt][r] += (double)acc[nt][r];
 
     // Per-column totals of this slice into LDS ([64 tokens][NC], fp32), squares per group.
-    // (The last proj_chunk ended with a barrier, so LDS buffer 0 is free.)
+    // (The last step ended with a barrier, so LDS buffer 0 is free.)
     float* red = reinterpret_cast<float*>(&lds[0][0]);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -416,7 +407,12 @@ proj_kernel(KArgs k)
             const float v = nt < NTHI ? (float)hacc[nt < NTHI ? nt : 0][r] : acc[nt][r];
             red[row * NC + nt * 16 + j] = v;
         }
-    lds_ss[wave * 16 + j][grp] = ssq;
+    // diagonal element (i, i) of x x^T sits in lane i + 12*(i/4) (i % 16 == lane % 16),
+    // register i % 4
+    {
+        const int rr = j - 4 * grp;
+        if (rr >= 0 && rr < 4) lds_ss[wave * 16 + j] = sq[rr];
+    }
     __syncthreads();
 
     // Partial record of this slice: M projections (hi + mid + lo) and the square sum.
@@ -430,25 +426,22 @@ proj_kernel(KArgs k)
             const float* rr = red + tl * NC;
             v = (float)((double)rr[m] + (double)rr[k.M + m] + (double)rr[2 * k.M + m]);
         } else {
-            v = (lds_ss[tl][0] + lds_ss[tl][1]) + (lds_ss[tl][2] + lds_ss[tl][3]);
+            v = lds_ss[tl];
         }
-        st_coherent(k.a.part + ((int64_t)s * k.T + t) * k.pstride + m, v);
+        k.a.part[((int64_t)s * k.T + t) * k.pstride + m] = v;
     }
+}
 
-    // Last-arriver hand-off: the S workgroups of this tile take a ticket once their
-    // records are complete; the one that completes the count owns the epilogue and
-    // resets the counter for the next call.
-    wait_vmem_stores();
-    __syncthreads();
-    if (tid == 0) {
-        const int prev = __hip_atomic_fetch_add(&k.a.tickets[tile], 1, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == k.S - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    if (tid == 0) __hip_atomic_store(&k.a.tickets[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    tile_epilogue<N>(k, tile, reinterpret_cast<char*>(&lds[0][0]));
+// One workgroup per 64-token tile: reduce the tile's S partial records (written by the
+// projection launch that precedes this one on the stream), then gates, Sinkhorn and
+// all per-token outputs.
+template <int N>
+__global__ void __launch_bounds__(kThreads)
+epilogue_kernel(KArgs k)
+{
+    constexpr int MMAX = N * N + 2 * N;
+    __shared__ double scratch[kTileTokens * (MMAX + 1) + kTileTokens + kTileTokens * N * N / 2];
+    tile_epilogue<N>(k, blockIdx.x, reinterpret_cast<char*>(scratch));
 }
 
 // ------------------------------------------------------------------ hIn
@@ -497,10 +490,10 @@ hipError_t launch_proj(const Plan& p, const KArgs& k, hipStream_t st)
 int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void* packed,
                    void* stream)
 {
-    const int64_t total = (int64_t)g.nch * kOctets * g.NC;
+    const int64_t total = (int64_t)(g.nch + 1) * kOctets * g.NC;
     const unsigned blocks = (unsigned)((total + 255) / 256);
     hipLaunchKernelGGL(prepack_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, phi, gamma,
-                       static_cast<u32x4*>(packed), g.n, g.D, g.M, g.NC, g.dc, g.nch);
+                       static_cast<u32x4*>(packed), g.K, g.M, g.NC, g.nch);
     return (int)hipGetLastError();
 }
 
@@ -516,7 +509,6 @@ int launch_forward(const Plan& p, const ForwardArgs& a, void* stream)
     k.M = p.g.M;
     k.S = p.S;
     k.nch = p.g.nch;
-    k.dc = p.g.dc;
     k.pstride = p.pstride;
     k.n_alpha = p.g.n_alpha;
 
@@ -526,6 +518,12 @@ int launch_forward(const Plan& p, const ForwardArgs& a, void* stream)
     else if (p.g.n == 8 && p.g.n_alpha == 3) e = launch_proj<15, 5, 8>(p, k, st);
     else if (p.g.n == 8 && p.g.n_alpha == 2) e = launch_proj<3, 1, 8>(p, k, st);
     else return (int)hipErrorInvalidValue;
+    if (e != hipSuccess) return (int)e;
+    if (p.g.n == 4)
+        hipLaunchKernelGGL(epilogue_kernel<4>, dim3((unsigned)p.tiles), dim3(kThreads), 0, st, k);
+    else
+        hipLaunchKernelGGL(epilogue_kernel<8>, dim3((unsigned)p.tiles), dim3(kThreads), 0, st, k);
+    e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
 
     const int64_t items = p.T * (int64_t)(p.g.D / 8);

@@ -5,16 +5,17 @@
 //
 // Data layout the kernels rely on
 //   xFlat of token t is x[t*K .. t*K + K) with K = n*D (TND, row-major; stream i occupies
-//   [i*D, (i+1)*D)). The reduction dimension K is walked in chunks of 128 elements:
-//   chunk ch covers the d-range [ch*dc, ch*dc + dc) of every stream, dc = 128 / n, as
-//   16 "octets" of 8 consecutive bf16. Octet q of a chunk is stream (q % n), d-offset
-//   8*(q / n). The matrix-core K-step s of a chunk consumes octets 4s .. 4s+3, lane group
-//   g (= lane / 16) holding octet 4s + g. Any order of K gives the same dot product, so
-//   the packed weights only need to use this same order.
+//   [i*D, (i+1)*D)). The reduction dimension K is walked in chunks of 128 consecutive
+//   xFlat elements (256 bytes of a token row: two whole cache lines), as 16 "octets" of
+//   8 bf16. The matrix-core K-step s of a chunk consumes octets 4s .. 4s+3, lane group g
+//   (= lane / 16) holding octet 4s + g. Any order of K gives the same dot product, so
+//   the packed weights only need to use this same order. D % 8 == 0 keeps every octet
+//   inside one stream.
 //   Packed weights: for each chunk, 16 octet rows x NC columns of 8 bf16 (16 bytes),
 //   octet-major. Column c < 3M is term (c / M) of phi row (c % M) with gamma folded in:
 //   term 0 = hi, 1 = mid, 2 = lo, hi + mid + lo = phi * gamma to ~2^-26 relative.
-//   Columns >= 3M and octets beyond D are zero.
+//   Columns >= 3M, octets at or beyond K, and one extra all-zero chunk at the end (so the
+//   one-chunk-ahead weight prefetch never needs a bounds test) hold zeros.
 #pragma once
 
 #include <cstddef>
@@ -33,7 +34,8 @@ namespace mhc {
 constexpr int kThreads = 256;          // workgroup: 4 waves of 64
 constexpr int kWaves = 4;
 constexpr int kTileTokens = 64;        // tokens per projection tile: 4 waves x 16 rows
-constexpr int kOctets = 16;            // octets per chunk (128 elements of xFlat)
+constexpr int kOctets = 16;            // octets per chunk
+constexpr int kChunk = 8 * kOctets;    // xFlat elements per chunk
 constexpr int kMaxN = 8;
 constexpr int kTargetBlocks = 2048;    // projection workgroups to aim for (256 CUs)
 
@@ -46,8 +48,7 @@ struct Geometry {
     int NT = 0;          // 16-wide column tiles covering the 3*M packed columns
     int NC = 0;          // 16 * NT
     int NTHI = 0;        // column tiles holding the "hi" term (accumulated in fp64)
-    int dc = 0;          // d per chunk: 128 / n
-    int nch = 0;         // chunks along d: ceil(D / dc)
+    int nch = 0;         // chunks of 128 xFlat elements: ceil(K / 128)
     size_t packed_bytes = 0;
 };
 
@@ -68,9 +69,8 @@ inline bool make_geometry(int n, int D, int n_alpha, Geometry* g)
     r.NT = (3 * r.M + 15) / 16;
     r.NC = 16 * r.NT;
     r.NTHI = (r.M + 15) / 16;
-    r.dc = 128 / n;
-    r.nch = (D + r.dc - 1) / r.dc;
-    r.packed_bytes = (size_t)r.nch * kOctets * r.NC * 16;
+    r.nch = (int)((r.K + kChunk - 1) / kChunk);
+    r.packed_bytes = (size_t)(r.nch + 1) * kOctets * r.NC * 16;
     *g = r;
     return true;
 }
@@ -79,10 +79,10 @@ struct Plan {
     Geometry g;
     int64_t T = 0;
     int64_t tiles = 0;        // ceil(T / kTileTokens)
-    int S = 0;                // d-slices (split of the reduction across workgroups)
+    int S = 0;                // K-slices (split of the reduction across workgroups)
     int64_t blocks = 0;       // projection workgroups = tiles * S
     int pstride = 0;          // floats per token in a partial record: M sums + 1 square sum
-    size_t off_packed = 0, off_tickets = 0, off_wts = 0, off_part = 0, ws_bytes = 0;
+    size_t off_packed = 0, off_wts = 0, off_part = 0, ws_bytes = 0;
 };
 
 // First chunk of slice s when nch chunks are split into S nearly equal ranges.
@@ -109,8 +109,6 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     size_t off = 0;
     p.off_packed = off;
     off = align_up(off + g.packed_bytes, 256);
-    p.off_tickets = off;
-    off = align_up(off + (size_t)p.tiles * sizeof(int32_t), 256);
     p.off_wts = off;
     off = align_up(off + (size_t)T * g.n * sizeof(float), 256);
     p.off_part = off;
@@ -134,7 +132,6 @@ struct ForwardArgs {
     float* h_pre;
     float* sum_out;
     float* norm_out;
-    int32_t* tickets;
     float* wts;
     float* part;
     int num_iters;

@@ -62,8 +62,8 @@ def fwd(params, ptrs=None, ws=FAKE, ws_bytes=WS_BIG):
 def test_sizes():
     p = _p(T=16384, D=7168)
     packed = B.packed_size(p)
-    # 224 chunks x 16 octet rows x 80 columns x 16 bytes
-    assert packed == 224 * 16 * 80 * 16
+    # (224 chunks + 1 zero chunk) x 16 octet rows x 80 columns x 16 bytes
+    assert packed == 225 * 16 * 80 * 16
     ws = B.workspace_size(p)
     assert ws >= packed + 16384 * 4 * 4 + 8 * 16384 * 25 * 4
     assert B.workspace_size(_p(T=0, D=7168)) >= packed
