@@ -53,7 +53,8 @@ typedef int32_t mhc_status;
 /* Problem description (host memory; read during the call only).
  *   T              tokens, >= 0
  *   n              hyper-streams (hcMult): 4 or 8
- *   D              hidden size per stream: > 0 and a multiple of 8
+ *   D              hidden size per stream: a multiple of 8 in [8, 16384]; with n == 8 and
+ *                  n_alpha == 3 at most 8192
  *   n_alpha        3 (pre/post/res branches, phi has n*n+2n rows) or
  *                  2 (pre/post only, phi has 2n rows, hRes = 0)
  *   num_iters      Sinkhorn iterations, >= 1 (ignored when n_alpha == 2)
@@ -124,9 +125,9 @@ const char* mhc_status_string(mhc_status status);
 mhc_status mhc_pre_packed_size(const mhc_pre_params* params, size_t* bytes);
 
 /* Bytes of device workspace mhc_pre_forward needs for this problem. Host only.
- * The workspace holds per-call intermediate results only (no state carries over
- * between calls), so it needs no initialisation. Concurrent calls need distinct
- * workspaces. Errors: NULLPTR, PARAM_INVALID. */
+ * The workspace holds per-call intermediate results only (partial sums and the hIn
+ * weights; no state carries over between calls), so it needs no initialisation.
+ * Concurrent calls need distinct workspaces. Errors: NULLPTR, PARAM_INVALID. */
 mhc_status mhc_pre_workspace_size(const mhc_pre_params* params, size_t* bytes);
 
 /* Packs phi (f32 [M, n*D]) and the optional gamma (f32 [n, D]) into phi_packed
@@ -137,11 +138,13 @@ mhc_status mhc_pre_workspace_size(const mhc_pre_params* params, size_t* bytes);
 mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const float* gamma,
                            void* phi_packed, size_t packed_bytes, void* stream);
 
-/* The fused forward, asynchronous on `stream` (a hipStream_t; NULL = default stream).
- * Emits every non-NULL output listed in mhc_pre_tensors. `workspace` is device memory
- * of at least mhc_pre_workspace_size bytes, 256-byte aligned. When tensors->phi_packed is NULL the weights are packed into the
- * workspace first (one extra kernel). Results are bitwise reproducible for the same
- * inputs and parameters. Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
+/* The forward, asynchronous on `stream` (a hipStream_t; NULL = default stream). Emits
+ * every non-NULL output listed in mhc_pre_tensors. `workspace` is device memory of at
+ * least mhc_pre_workspace_size bytes, 256-byte aligned. When tensors->phi_packed is NULL
+ * the weights are packed into the workspace first (one extra kernel). Then a projection
+ * kernel (which with pre_mix also writes hIn), a per-token epilogue and, without pre_mix,
+ * an hIn kernel. Results are bitwise reproducible for the same inputs and parameters.
+ * Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
 mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
                            void* workspace, size_t workspace_bytes, void* stream);
 

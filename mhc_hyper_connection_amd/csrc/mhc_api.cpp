@@ -148,7 +148,7 @@ mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* 
     a.sum_out = res_branch ? t->sum_out : nullptr;
     a.norm_out = res_branch ? t->norm_out : nullptr;
     a.wts = reinterpret_cast<float*>(ws + plan.off_wts);
-    a.part = reinterpret_cast<float*>(ws + plan.off_part);
+    a.rec = reinterpret_cast<float*>(ws + plan.off_rec);
     a.num_iters = params->num_iters;
     a.norm_eps = params->norm_eps;
     a.hc_eps = params->hc_eps;

@@ -1,25 +1,28 @@
-// mhc_kernels.hip -- gfx950 kernels of the fused mHC pre-mapping forward.
+// mhc_kernels.hip -- gfx950 kernels of the mHC pre-mapping forward.
 //
 // Method (aclnnMhcPreV2 guide, kwkr.cn/news/422178, section 3; aclnnMhcPreSinkhorn guide,
 // m.mzlw.cn/news/197063, section 3.2): per token, invRms over the n*D entries, the
 // projection hMix = (x * gamma) . phi^T, sigmoid gates, a 2*numIters-step Sinkhorn of
 // the n x n residual logits, and hIn = sum_i weight_i * x_i.
 //
-// Kernels
-//   prepack_kernel  phi (f32) * gamma -> three bf16 terms (hi, mid, lo) in the chunked,
-//                   octet-major order the projection consumes (layout in mhc_plan.h).
-//   proj_kernel     one workgroup = 64 tokens x one K-slice of the reduction. x goes from
-//                   HBM straight into MFMA A-registers (16-byte loads, no LDS); the packed
-//                   weights of each 128-element chunk are staged in LDS (double-buffered,
-//                   prefetched one chunk ahead) and shared by the 4 waves; x is prefetched
-//                   two chunks ahead. v_mfma_f32_16x16x32_bf16 accumulates the 3*M columns; the
-//                   "hi" columns are moved into fp64 every kFlush chunks so long fp32
-//                   chains do not limit hMix accuracy. Squares come from the diagonal of
-//                   x x^T on the matrix cores, from the same registers. Each workgroup writes fp32 partial sums; the
-//                   last of the S workgroups of a tile (atomic ticket) reduces them in a
-//                   fixed order (deterministic), then runs the gates and a lane-parallel
-//                   Sinkhorn and writes every output except hIn, plus the hIn weights.
-//   hin_kernel      hIn[t, d] = sum_i w[t, i] x[t, i, d], fp32 FMA, one rounding to bf16.
+// Kernels (one launch each, in this order on the caller's stream)
+//   prepack_kernel   phi (f32) * gamma -> three bf16 terms (hi, mid, lo) in the K-step
+//                    order the projection consumes (layout in mhc_plan.h); only when the
+//                    caller passes no packed weights.
+//   proj_kernel      one workgroup per task = 64 tokens x one d-slice (the same positions
+//                    of all n streams). The task's x goes from HBM into registers once,
+//                    already in matrix-core operand order; the packed weights of the slice
+//                    stream into an LDS ring by direct-to-LDS loads issued ahead of the x
+//                    loads, and are shared by the 4 waves. v_mfma_f32_16x16x32_bf16
+//                    accumulates the 3M columns; the squares come from the diagonal of
+//                    x x^T. The task writes one partial record per token. With pre_mix the
+//                    hIn weights are inputs, and the task also writes its slice of hIn
+//                    from the registers it already holds (x is read once).
+//   epilogue_kernel  one workgroup per 8 tokens: sums the S partial records of each token
+//                    in a fixed order (fp64), then invRms, hMix, the gates, the Sinkhorn
+//                    planes (one lane per matrix entry, sums across lanes by DPP) and,
+//                    without pre_mix, the hIn weights.
+//   hin_kernel       without pre_mix: hIn[t, d] = sum_i hPre[t, i] x[t, i, d].
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -32,8 +35,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kFlush = 2;   // chunks (8 MFMA K-steps) between fp64 flushes of the hi columns
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -52,34 +53,91 @@ __device__ __forceinline__ double bf16_bits_to_double(uint32_t b)
     return (double)__uint_as_float(b << 16);
 }
 
+// s_waitcnt vmcnt(n): at most n vector memory operations of this wave outstanding. Called
+// from fully unrolled loops with n a constant after unrolling; each case is one instruction.
+#define MHC_VM_CASE(n) \
+    case n: __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00); break;
+#define MHC_VM_CASE8(b) MHC_VM_CASE(b) MHC_VM_CASE(b + 1) MHC_VM_CASE(b + 2) MHC_VM_CASE(b + 3) \
+    MHC_VM_CASE(b + 4) MHC_VM_CASE(b + 5) MHC_VM_CASE(b + 6) MHC_VM_CASE(b + 7)
+__device__ __forceinline__ void wait_vm(int n)
+{
+    switch (n < 0 ? 0 : (n > 63 ? 63 : n)) {
+        MHC_VM_CASE8(0) MHC_VM_CASE8(8) MHC_VM_CASE8(16) MHC_VM_CASE8(24)
+        MHC_VM_CASE8(32) MHC_VM_CASE8(40) MHC_VM_CASE8(48) MHC_VM_CASE8(56)
+        default: break;
+    }
+}
+#undef MHC_VM_CASE8
+#undef MHC_VM_CASE
+
+// Buffer resources: a base address and a byte range in four scalar registers; vector
+// accesses take a 32-bit byte offset, and loads outside the range return zero (stores
+// outside it are dropped), which bounds every access of a ragged tile in hardware.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) buffer on gfx9-family targets
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ void st_buf(rsrc_t r, uint32_t off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
+}
+
+// ------------------------------------------------------------------ configuration
+
+template <int N, int A>
+struct Cfg {
+    static constexpr int M = A == 3 ? N * N + 2 * N : 2 * N;
+    static constexpr int NT = (3 * M + 15) / 16;
+    static constexpr int NC = 16 * NT;
+    static constexpr int SK = (A == 3) ? 1 : (N == 4 ? 4 : 2);   // K-steps per stage
+    static constexpr int RING = (N == 8 && A == 3) ? 3 : (A == 3 ? 7 : 5);   // LDS weight slots: stages in flight + 1
+    static constexpr int NN = N * N;
+    static constexpr int PPS = (N + 4) / 4 * 4;   // pre-branch record: n sums, square, padding
+    static constexpr int V = PPS + (M - N);       // floats per partial record
+    static constexpr int CH = V / 4;              // 16-byte chunks per record
+    static constexpr int KU = 4 * NC;             // 16-byte units per K-step of packed weights
+    static constexpr int STAGE_U = SK * KU;
+    static constexpr int OB = kOutTokens;         // tokens per epilogue workgroup
+    static_assert(STAGE_U % 64 == 0, "a stage is whole 64-lane load instructions");
+    static constexpr int PROJ_LDS = RING * STAGE_U * 16 > kTileTokens * NC * 4 ? RING * STAGE_U * 16 : kTileTokens * NC * 4;
+};
+
 struct KArgs {
     ForwardArgs a;
     int64_t T;
     int64_t K;
     int D;
-    int M;
     int S;
-    int nch;
-    int pstride;
-    int n_alpha;
+    int GS;
+    int NG;
 };
+
+__device__ __forceinline__ int tile_tokens(const KArgs& k, int64_t t0)
+{
+    return (int)(k.T - t0 < kTileTokens ? k.T - t0 : kTileTokens);
+}
 
 // ------------------------------------------------------------------ weight pre-pack
 
 __global__ void __launch_bounds__(256)
 prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
-               u32x4* __restrict__ packed, int64_t K, int M, int NC, int nch)
+               u32x4* __restrict__ packed, int n, int D, int M, int NC, int nks, int64_t total)
 {
     const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)(nch + 1) * kOctets * NC;
     if (u >= total) return;
     const int c = (int)(u % NC);
     const int64_t r = u / NC;
-    const int q = (int)(r % kOctets);
-    const int64_t ch = r / kOctets;
-    const int64_t k0 = ch * kChunk + 8 * q;
+    const int g = (int)(r % 4);
+    const int64_t k = r / 4;
+    const int64_t K = (int64_t)n * D;
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (c < 3 * M && k0 < K) {
+    const int d = kBlock * (int)(k / n) + 8 * g;
+    if (c < 3 * M && k < nks && d < D) {
+        const int64_t k0 = (k % n) * (int64_t)D + d;
         const int term = c / M;
         const int m = c % M;
 #pragma unroll
@@ -99,7 +157,210 @@ prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
     packed[u] = w;
 }
 
-// ------------------------------------------------------------------ tile epilogue
+// ------------------------------------------------------------------ hIn from registers
+
+// hIn[t, d] = sum_i w_i x[t, i, d] for the lane's token and its octet of each d-block of
+// the slice: the n K-steps of a d-block hold the n streams of the same 8 positions, so
+// the sum is local to the lane. fp32 FMA in stream order, one rounding to bf16. `hres`
+// covers the tile's rows of hIn (rows past T are dropped by its range); `lim` excludes
+// octets past D.
+template <int N, int NKS>
+__device__ __forceinline__ void hin_store(rsrc_t hres, uint32_t off, const u32x4 (&xr)[NKS],
+                                          const float (&w)[N], int lim)
+{
+#pragma unroll
+    for (int blk = 0; blk < NKS / N; ++blk) {
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const u32x4 v = xr[blk * N + i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = fmaf(w[i], bf16_lo(v[e]), acc[2 * e]);
+                acc[2 * e + 1] = fmaf(w[i], bf16_hi(v[e]), acc[2 * e + 1]);
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = f32_to_bf16_bits(acc[2 * e]) | (f32_to_bf16_bits(acc[2 * e + 1]) << 16);
+        if (kBlock * blk < lim)
+            __builtin_amdgcn_raw_buffer_store_b128(o, hres, (int)(off + 2 * kBlock * blk), 0, 0);
+    }
+}
+
+// ------------------------------------------------------------------ projection
+
+// One weight stage (STAGE_U 16-byte units) moves from global memory straight into LDS:
+// wave w's i-th instruction moves units [256 i + 64 w, +64), one per lane, to the same
+// place in the destination slot (the LDS address is M0 plus 16 bytes per lane). The
+// instruction is issued from inline assembly so that the compiler neither tracks it nor
+// inserts waits of its own before LDS reads; the kernel waits for it explicitly with the
+// in-order vector memory counter.
+__device__ __forceinline__ void dma16(const u32x4* g, uint32_t lds_wave_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds_wave_base) : "memory");
+}
+template <int STAGE_U>
+__device__ __forceinline__ void dma_stage(const u32x4* src, const u32x4* dst, int wave, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < (STAGE_U + kThreads - 1) / kThreads; ++i) {
+        const int base = kThreads * i + 64 * wave;
+        if (STAGE_U % kThreads == 0 || base < STAGE_U)
+            dma16(src + base + lane,
+                  __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(dst + base)));
+    }
+}
+// Direct-to-LDS instructions every wave issues per stage (the fewest over the waves).
+template <int STAGE_U>
+constexpr int dma_ops_min() { return STAGE_U / kThreads; }
+
+// Vector memory operations a wave has issued after the DMA of stage c when it waits for
+// stage c at iteration c: stages 0 .. DEPTH-1 go out before the NKS x loads, stage c + DEPTH
+// after the barrier of iteration c. Counting the fewest DMA instructions per stage can
+// only undercount, which makes the wait stronger than needed, never weaker.
+template <int NKS, int NSTAGE, int DEPTH, int OPS>
+constexpr int younger_than_stage(int c)
+{
+    int n = 0;
+    if (c < DEPTH) {
+        n += (DEPTH - 1 - c) * OPS + NKS;
+        for (int it = 0; it < c; ++it)
+            if (it + DEPTH < NSTAGE) n += OPS;
+    } else {
+        for (int it = c - DEPTH + 1; it < c; ++it)
+            if (it + DEPTH < NSTAGE) n += OPS;
+    }
+    return n;
+}
+
+template <int N, int A, int NKS>
+__global__ void __launch_bounds__(kThreads, 3)
+proj_kernel(KArgs k)
+{
+    using C = Cfg<N, A>;
+    constexpr int NT = C::NT, NC = C::NC, SK = C::SK, M = C::M, CH = C::CH, PPS = C::PPS;
+    constexpr int STAGE_U = C::STAGE_U;
+    constexpr int NSTAGE = NKS / SK;
+    constexpr int DEPTH = C::RING - 1 < NSTAGE ? C::RING - 1 : NSTAGE;   // stages in flight
+    constexpr int R = DEPTH + 1;                                           // LDS slots
+    constexpr int OPS = dma_ops_min<STAGE_U>();
+    static_assert(NKS % SK == 0 && NKS % N == 0, "a slice is whole stages and whole d-blocks");
+    static_assert(NKS <= kPadSteps, "the zero tail of the packed weights covers one slice");
+    static_assert(OPS >= 1, "every wave moves part of each stage");
+    __shared__ __attribute__((aligned(16))) char lds[C::PROJ_LDS];   // R weight slots; then column totals
+    __shared__ float lds_ss[kTileTokens];
+    const u32x4* ring = reinterpret_cast<const u32x4*>(lds);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int j = lane & 15;      // A row (token) / B column / D column
+    const int grp = lane >> 4;    // K-group of A and B; row block of D
+    const int row = wave * 16 + j;   // the lane's token within the tile
+    const int64_t tile = blockIdx.x / k.S;
+    const int s = (int)(blockIdx.x % k.S);
+    const int64_t t0 = tile * kTileTokens;
+    const int ntile = tile_tokens(k, t0);
+    const int b0 = s * (NKS / N);
+    // octets of d-block b0 + blk exist for this lane iff kBlock * blk < lim
+    const int lim = k.D - kBlock * b0 - 8 * grp;
+    const u32x4* pk = static_cast<const u32x4*>(k.a.packed) + packed_slice(s, NKS, NC);
+
+    // Weight stages 0 .. DEPTH-1 first, then all of the task's x: the load counter retires
+    // in issue order, so waiting for a weight stage never waits for x. Rows past T lie
+    // outside the tile's x range and read as zero.
+#pragma unroll
+    for (int st = 0; st < DEPTH; ++st) dma_stage<STAGE_U>(pk + st * STAGE_U, ring + st * STAGE_U, wave, lane);
+    const rsrc_t xres = make_rsrc(k.a.x + t0 * k.K, (int64_t)ntile * k.K * 2);
+    u32x4 xr[NKS];
+    uint32_t xo[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) xo[i] = x_lane_off(k.K, k.D, row, grp, b0, i);
+#pragma unroll
+    for (int st = 0; st < NKS; ++st)   // in K-step order: the loop below consumes them in order
+        xr[st] = __builtin_amdgcn_raw_buffer_load_b128(xres, (int)(xo[st % N] + 2 * kBlock * (st / N)), 0, 0);
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 sq = {0.f, 0.f, 0.f, 0.f};   // x x^T of this wave's 16 tokens; diagonal = squares
+#pragma unroll
+    for (int c = 0; c < NSTAGE; ++c) {
+        wait_vm(younger_than_stage<NKS, NSTAGE, DEPTH, OPS>(c));   // this wave's part of stage c
+        // every wave's part of stage c is in LDS; every wave is done with stage c - 1,
+        // whose slot the next DMA overwrites
+        __syncthreads();
+        if (c + DEPTH < NSTAGE)
+            dma_stage<STAGE_U>(pk + (c + DEPTH) * STAGE_U, ring + ((c + DEPTH) % R) * STAGE_U, wave, lane);
+        const u32x4* w = ring + (c % R) * STAGE_U + grp * NC + j;
+#pragma unroll
+        for (int kk = 0; kk < SK; ++kk) {
+            const int st = c * SK + kk;
+            if constexpr (NT > 8) __builtin_amdgcn_sched_barrier(0);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 xa = kBlock * (st / N) < lim ? xr[st] : z;
+            const bf16x8 Av = __builtin_bit_cast(bf16x8, xa);
+            sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Av, sq, 0, 0, 0);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const u32x4 bv = w[kk * 4 * NC + nt * 16];
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, __builtin_bit_cast(bf16x8, bv),
+                                                                  acc[nt], 0, 0, 0);
+            }
+        }
+    }
+    __syncthreads();   // the ring is free
+
+    // Column totals of this slice into LDS ([64 tokens][NC]); the square of token i is
+    // element (i, i) of x x^T: lane i + 16 * (i / 4), register i % 4.
+    float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[(wave * 16 + 4 * grp + r) * NC + nt * 16 + j] = acc[nt][r];
+    {
+        const int rr = j - 4 * grp;
+        if (rr >= 0 && rr < 4) lds_ss[wave * 16 + j] = sq[rr];
+    }
+
+    // With pre_mix the hIn weights are known: the slice's hIn from the x registers.
+    if (k.a.pre_mix) {
+        const int64_t tok = t0 + row < k.T ? t0 + row : k.T - 1;
+        float wv[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) wv[i] = k.a.pre_mix[tok * N + i];
+        const rsrc_t hres = make_rsrc(k.a.h_in + t0 * k.D, (int64_t)ntile * k.D * 2);
+        hin_store<N, NKS>(hres, (uint32_t)(((int64_t)row * k.D + kBlock * b0 + 8 * grp) * 2), xr, wv, lim);
+    }
+    __syncthreads();
+
+    // Partial records (hi + mid + lo of each phi row, added in fp64, rounded once),
+    // 16 bytes per store.
+    const rsrc_t rec = make_rsrc(k.a.rec + rec_tile(tile, k.S, N, M), (int64_t)k.S * kTileTokens * C::V * 4);
+    for (int idx = tid; idx < kTileTokens * CH; idx += kThreads) {
+        const int tl = idx / CH, ch = idx % CH;
+        const float* rr = red + tl * NC;
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int v = 4 * ch + e;
+            const int m = v < N ? v : N + (v - PPS);
+            float val;
+            if (v == N) val = lds_ss[tl];
+            else if (v > N && v < PPS) val = 0.f;
+            else val = (float)((double)rr[m] + (double)rr[M + m] + (double)rr[2 * M + m]);
+            o[e] = __float_as_uint(val);
+        }
+        const uint32_t off = tl < ntile ? (uint32_t)(rec_loc(s, tl, N, M) + 4 * ch) * 4 : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(o, rec, (int)off, 0, 0);
+    }
+}
+
+// ------------------------------------------------------------------ per-token math
 
 __device__ __forceinline__ float sigmoidf_stable(float z)
 {
@@ -108,119 +369,89 @@ __device__ __forceinline__ float sigmoidf_stable(float z)
     return e / (1.f + e);
 }
 
+__device__ __forceinline__ double inv_rms_of(double sq, double K, double eps)
+{
+    return 1.0 / sqrt(sq / K + eps);
+}
+__device__ __forceinline__ float gate_pre(double h, double inv, float alpha, float bias, float eps)
+{
+    return sigmoidf_stable((float)fma((double)alpha, h * inv, (double)bias)) + eps;
+}
+__device__ __forceinline__ float gate_post(double h, double inv, float alpha, float bias, float eps,
+                                           bool plus_eps)
+{
+    const float g = 2.f * sigmoidf_stable((float)fma((double)alpha, h * inv, (double)bias));
+    return plus_eps ? g + eps : g;
+}
+__device__ __forceinline__ float res_logit(double h, double inv, float alpha, float bias)
+{
+    return (float)fma((double)alpha, h * inv, (double)bias);
+}
+
+// Cross-lane sums and maxima over the rows / columns of an n x n matrix held one entry
+// per lane, entry (r, c) in lane n*r + c of an n*n-lane group (16 lanes for n = 4, the
+// whole wave for n = 8). DPP moves within 16-lane rows; the column sums of n = 8 cross
+// rows with lane shuffles. Every lane of a row (column) ends with the same total.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, true));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+constexpr int kRowHalfMirror = 0x141;
+
 template <int N>
 __device__ __forceinline__ float row_sum(float v)
 {
-#pragma unroll
-    for (int m = 1; m < N; m <<= 1) v += __shfl_xor(v, m);
+    v += dpp<kQuadXor1>(v);
+    v += dpp<kQuadXor2>(v);
+    if constexpr (N == 8) v += dpp<kRowHalfMirror>(v);
     return v;
 }
 template <int N>
 __device__ __forceinline__ float row_max(float v)
 {
-#pragma unroll
-    for (int m = 1; m < N; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+    v = fmaxf(v, dpp<kQuadXor1>(v));
+    v = fmaxf(v, dpp<kQuadXor2>(v));
+    if constexpr (N == 8) v = fmaxf(v, dpp<kRowHalfMirror>(v));
     return v;
 }
 template <int N>
 __device__ __forceinline__ float col_sum(float v)
 {
-#pragma unroll
-    for (int m = N; m < N * N; m <<= 1) v += __shfl_xor(v, m);
+    if constexpr (N == 4) {
+        v += dpp<kRowRor4>(v);
+        v += dpp<kRowRor8>(v);
+    } else {
+        v += dpp<kRowRor8>(v);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+    }
     return v;
 }
 
-// Runs on all threads of the tile's last workgroup. `scratch` is LDS of at least
-// 64*(M+1)*8 + 64*8 + 64*N*N*4 bytes.
-//   A  sum the S partial records of each (token, value) in slice order (fp64)
-//   B  invRms per token
-//   C  hMix, gates and residual logits, one (token, row) item per thread
-//   D  Sinkhorn with one lane per matrix entry: 2*num_iters steps, row / column sums by
-//      cross-lane shuffles, coalesced stores of every plane
+// Sinkhorn of nb tokens (the first is token tfirst) whose logits are in Ls ([nb][N*N]):
+// one lane per matrix entry, 2*num_iters steps, every plane stored.
 template <int N>
-__device__ void tile_epilogue(const KArgs& k, int64_t tile, char* scratch)
+__device__ void sinkhorn(const KArgs& k, const float* Ls, int64_t tfirst, int nb)
 {
     constexpr int NN = N * N;
     const ForwardArgs& a = k.a;
     const int tid = threadIdx.x;
-    const int M = k.M;
-    const int R = M + 1;
-    const int64_t T = k.T;
-    const int64_t t0 = tile * kTileTokens;
-    double* hm = reinterpret_cast<double*>(scratch);                  // [64][R]
-    double* inv = hm + kTileTokens * R;                               // [64]
-    float* Ls = reinterpret_cast<float*>(inv + kTileTokens);          // [64][NN]
-
-    // A: partial sums, eight slices in flight at a time, added in slice order
-    for (int idx = tid; idx < kTileTokens * R; idx += kThreads) {
-        const int tl = idx / R, m = idx % R;
-        const int64_t t = t0 + tl;
-        double acc = 0.0;
-        if (t < T) {
-            const float* p = a.part + t * k.pstride + m;
-            const int64_t ss = T * (int64_t)k.pstride;
-            for (int s = 0; s < k.S; s += 8) {
-                float v[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[i] = (s + i < k.S) ? p[(s + i) * ss] : 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc += (double)v[i];
-            }
-        }
-        hm[idx] = acc;
-    }
-    __syncthreads();
-
-    // B: invRms = (mean of squares over n*D + normEps)^(-1/2)
-    if (tid < kTileTokens) {
-        const int64_t t = t0 + tid;
-        const double r = 1.0 / sqrt(hm[tid * R + M] / (double)k.K + a.norm_eps);
-        inv[tid] = r;
-        if (t < T && a.inv_rms) a.inv_rms[t] = (float)r;
-    }
-    __syncthreads();
-
-    // C: w = hMix * invRms; pre / post gates; residual logits
+    const int e = tid % NN, r = e / N, c = e % N;
     const float eps = (float)a.hc_eps;
-    for (int idx = tid; idx < kTileTokens * M; idx += kThreads) {
-        const int tl = idx / M, m = idx % M;
-        const int64_t t = t0 + tl;
-        const double h = hm[tl * R + m];
-        const double w = h * inv[tl];
-        if (t < T && a.h_mix) a.h_mix[t * M + m] = (float)h;
-        if (m < N) {
-            const float hp = sigmoidf_stable((float)((double)a.alpha[0] * w + (double)a.bias[m])) + eps;
-            if (t < T) {
-                if (a.h_pre) a.h_pre[t * N + m] = hp;
-                a.wts[t * N + m] = a.pre_mix ? a.pre_mix[t * N + m] : hp;
-            }
-        } else if (m < 2 * N) {
-            float hq = 2.f * sigmoidf_stable((float)((double)a.alpha[1] * w + (double)a.bias[m]));
-            if (k.n_alpha == 2) hq += eps;
-            if (t < T) a.h_post[t * N + (m - N)] = hq;
-        } else {
-            Ls[tl * NN + (m - 2 * N)] = (float)((double)a.alpha[2] * w + (double)a.bias[m]);
-        }
-    }
-    if (k.n_alpha != 3) {
-        if (a.h_res)
-            for (int idx = tid; idx < kTileTokens * NN; idx += kThreads)
-                if (t0 + idx / NN < T) a.h_res[t0 * NN + idx] = 0.f;
-        return;
-    }
-    __syncthreads();
-
-    // D: Sinkhorn. Lane = (token slot, r, c) with c in the low bits: row sums are xor
-    // shuffles over the c bits, column sums over the r bits.
-    constexpr int TPW = 64 / NN;                        // tokens per wave per round
-    const int lane = tid & 63, wave = tid >> 6;
-    const int e = lane % NN, r = e / N, c = e % N;
     const int steps = 2 * a.num_iters;
-    for (int base = 0; base < kTileTokens; base += kWaves * TPW) {
-        const int tl = base + wave * TPW + lane / NN;
-        const int64_t t = t0 + tl;
-        const bool live = t < T;
-        float v = Ls[tl * NN + e];
+    for (int base = 0; base < nb * NN; base += kThreads) {
+        const int q = (base + tid) / NN;
+        const bool live = q < nb;
+        const int64_t t1 = tfirst + base / NN;   // first token of this pass
+        const int nlive = nb - base / NN;          // tokens of this pass that exist
+        const int qq = q - base / NN;              // token within the pass
+        float v = live ? Ls[q * NN + e] : 0.f;
         const float mx = row_max<N>(v);
         const float ex = expf(v - mx);
         float sum = row_sum<N>(ex);
@@ -231,217 +462,107 @@ __device__ void tile_epilogue(const KArgs& k, int64_t tile, char* scratch)
                 else sum = row_sum<N>(v) + eps;
                 v = v / sum;
             }
-            if (live) {
-                if (a.sum_out) {
-                    const bool writer = (step & 1) ? (r == 0) : (c == 0);
-                    if (writer) a.sum_out[((int64_t)step * T + t) * N + ((step & 1) ? c : r)] = sum;
-                }
-                if (a.norm_out) a.norm_out[((int64_t)step * T + t) * NN + e] = v;
+            // this pass's tokens of plane `step`; lanes past them fall outside the range
+            if (a.sum_out) {
+                const rsrc_t rs = make_rsrc(a.sum_out + ((int64_t)step * k.T + t1) * N, (int64_t)nlive * N * 4);
+                const bool writer = (step & 1) ? (r == 0) : (c == 0);
+                if (writer) st_buf(rs, (uint32_t)(qq * N + ((step & 1) ? c : r)) * 4, sum);
+            }
+            if (a.norm_out) {
+                const rsrc_t rn = make_rsrc(a.norm_out + ((int64_t)step * k.T + t1) * NN, (int64_t)nlive * NN * 4);
+                st_buf(rn, (uint32_t)(qq * NN + e) * 4, v);
             }
         }
-        if (live) a.h_res[t * NN + e] = v;
+        const rsrc_t rh = make_rsrc(a.h_res + t1 * NN, (int64_t)nlive * NN * 4);
+        st_buf(rh, (uint32_t)(qq * NN + e) * 4, v);
     }
 }
 
-// ------------------------------------------------------------------ projection
+// ------------------------------------------------------------------ epilogue
 
-// x for one full chunk: lane (token row, group g) takes octets g, 4+g, 8+g, 12+g of
-// the chunk, i.e. 16 bytes at element offset 8*(4*st + g) for K-step st. The four loads
-// of a lane cover 64 of the row's 256 contiguous bytes; the 4 groups together cover
-// both cache lines.
-__device__ __forceinline__ void load_x_full(const uint16_t* xrow, int64_t base, int grp, u32x4 (&xr)[4])
-{
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-        xr[st] = *reinterpret_cast<const u32x4*>(xrow + base + 8 * (4 * st + grp));
-}
-
-// The same for the last chunk of a row when K is not a multiple of 128: octets at or
-// beyond K read as zero.
-__device__ __forceinline__ void load_x_tail(const uint16_t* xrow, int64_t base, int64_t K, int grp,
-                                            u32x4 (&xr)[4])
-{
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const int64_t k0 = base + 8 * (4 * st + grp);
-        xr[st] = k0 < K ? *reinterpret_cast<const u32x4*>(xrow + k0) : u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-// Matrix-core work of one chunk held in x registers `xr` and LDS weight buffer `w`:
-// 4 K-steps x NT column tiles, plus the x tile times its own transpose, whose diagonal
-// accumulates each token's sum of squares (exact bf16 products, fp32 sums), and the
-// periodic fp64 flush of the hi columns.
-template <int NT, int NTHI>
-__device__ __forceinline__ void mma_chunk(const u32x4 (&xr)[4], const u32x4* w, int grp, int j,
-                                          f32x4 (&acc)[NT], double (&hacc)[NTHI][4], f32x4& sq,
-                                          int& since_flush)
-{
-    constexpr int NC = 16 * NT;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const u32x4 av = xr[st];
-        const bf16x8 A = __builtin_bit_cast(bf16x8, av);
-        sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, A, sq, 0, 0, 0);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const u32x4 bv = w[(4 * st + grp) * NC + nt * 16 + j];
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, bv),
-                                                              acc[nt], 0, 0, 0);
-        }
-    }
-    if (++since_flush == kFlush) {
-        since_flush = 0;
-#pragma unroll
-        for (int nt = 0; nt < NTHI; ++nt) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) hacc[nt][r] += (double)acc[nt][r];
-            acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-    }
-}
-
-// One pipelined step over full chunk `ch`: first the weight loads of chunk ch+1 into
-// registers and the x loads of chunk ch+2 into `xn` (whose last readers were the
-// previous step's MFMAs, behind that step's barrier); then the chunk's MFMAs from `xc` and
-// LDS buffer BUF; then the weights go to the other LDS buffer and one barrier closes
-// the step. The packed weights end with a zero chunk, so the weight prefetch never
-// needs a bounds test.
-template <int NT, int NTHI>
-__device__ __forceinline__ void proj_step(int BUF, int ch, int chf, int tid, int grp, int j, const KArgs& k,
-                                          const uint16_t* xrow, const u32x4 (&xc)[4], u32x4 (&xn)[4],
-                                          u32x4 (*lds)[kOctets * 16 * NT], f32x4 (&acc)[NT],
-                                          double (&hacc)[NTHI][4], f32x4& sq, int& since_flush)
-{
-    constexpr int UNITS = kOctets * 16 * NT;
-    // Weights first: the load counter retires in issue order, so the wait for them at
-    // the end of the step must not also cover the x prefetch issued after them.
-    const u32x4* src = static_cast<const u32x4*>(k.a.packed) + (int64_t)(ch + 1) * UNITS;
-    u32x4 pre[NT];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) pre[i] = src[tid + kThreads * i];
-    if (ch + 2 < chf) load_x_full(xrow, (int64_t)(ch + 2) * kChunk, grp, xn);
-    mma_chunk<NT, NTHI>(xc, lds[BUF], grp, j, acc, hacc, sq, since_flush);
-#pragma unroll
-    for (int i = 0; i < NT; ++i) lds[BUF ^ 1][tid + kThreads * i] = pre[i];
-    __syncthreads();
-}
-
-template <int NT, int NTHI, int N>
-__global__ void __launch_bounds__(kThreads)
-proj_kernel(KArgs k)
-{
-    constexpr int NC = 16 * NT;
-    constexpr int UNITS = kOctets * NC;
-    __shared__ u32x4 lds[2][UNITS];                     // double-buffered weight chunks
-    __shared__ float lds_ss[kTileTokens];
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int j = lane & 15;      // A row (token) / B column / D column
-    const int grp = lane >> 4;    // K-group of A and B; row block of D
-    const int64_t tile = blockIdx.x / k.S;
-    const int s = (int)(blockIdx.x % k.S);
-    const int ch0 = slice_begin(k.nch, k.S, s);
-    const int ch1 = slice_begin(k.nch, k.S, s + 1);
-
-    // A-operand token of this lane; rows past T re-read the last token, results dropped.
-    int64_t tok = tile * kTileTokens + wave * 16 + j;
-    if (tok > k.T - 1) tok = k.T - 1;
-    const uint16_t* xrow = k.a.x + tok * k.K;
-
-    f32x4 acc[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    double hacc[NTHI][4];
-#pragma unroll
-    for (int nt = 0; nt < NTHI; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hacc[nt][r] = 0.0;
-    f32x4 sq = {0.f, 0.f, 0.f, 0.f};   // x x^T of this wave's 16 tokens; diagonal = squares
-    int since_flush = 0;
-
-    // Full chunks [ch0, chf) run through a 3-buffer x pipeline (two chunks in flight
-    // ahead of the one being multiplied) and a 2-buffer LDS weight pipeline; a partial
-    // last chunk of the row (K not a multiple of 128) is done after it.
-    const int nfull = (int)(k.K / kChunk);
-    const int chf = ch1 < nfull ? ch1 : nfull;
-    u32x4 x0[4], x1[4], x2[4];
-    const u32x4* packed = static_cast<const u32x4*>(k.a.packed);
-    if (ch0 < chf) load_x_full(xrow, (int64_t)ch0 * kChunk, grp, x0);
-    if (ch0 + 1 < chf) load_x_full(xrow, (int64_t)(ch0 + 1) * kChunk, grp, x1);
-    if (ch0 < ch1) {
-#pragma unroll
-        for (int i = 0; i < NT; ++i) lds[0][tid + kThreads * i] = packed[(int64_t)ch0 * UNITS + tid + kThreads * i];
-    }
-    __syncthreads();
-
-    int ch = ch0;
-    while (ch < chf) {
-        proj_step<NT, NTHI>((ch - ch0) & 1, ch, chf, tid, grp, j, k, xrow, x0, x2, lds, acc, hacc, sq, since_flush);
-        if (++ch >= chf) break;
-        proj_step<NT, NTHI>((ch - ch0) & 1, ch, chf, tid, grp, j, k, xrow, x1, x0, lds, acc, hacc, sq, since_flush);
-        if (++ch >= chf) break;
-        proj_step<NT, NTHI>((ch - ch0) & 1, ch, chf, tid, grp, j, k, xrow, x2, x1, lds, acc, hacc, sq, since_flush);
-        ++ch;
-    }
-    if (chf < ch1) {
-        // partial last chunk; its weights are in LDS buffer (chf - ch0) & 1
-        load_x_tail(xrow, (int64_t)chf * kChunk, k.K, grp, x0);
-        mma_chunk<NT, NTHI>(x0, lds[(chf - ch0) & 1], grp, j, acc, hacc, sq, since_flush);
-        __syncthreads();
-    }
-#pragma unroll
-    for (int nt = 0; nt < NTHI; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hacc[nt][r] += (double)acc[nt][r];
-
-    // Per-column totals of this slice into LDS ([64 tokens][NC], fp32), squares per group.
-    // (The last step ended with a barrier, so LDS buffer 0 is free.)
-    float* red = reinterpret_cast<float*>(&lds[0][0]);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = wave * 16 + 4 * grp + r;
-            const float v = nt < NTHI ? (float)hacc[nt < NTHI ? nt : 0][r] : acc[nt][r];
-            red[row * NC + nt * 16 + j] = v;
-        }
-    // diagonal element (i, i) of x x^T sits in lane i + 12*(i/4) (i % 16 == lane % 16),
-    // register i % 4
-    {
-        const int rr = j - 4 * grp;
-        if (rr >= 0 && rr < 4) lds_ss[wave * 16 + j] = sq[rr];
-    }
-    __syncthreads();
-
-    // Partial record of this slice: M projections (hi + mid + lo) and the square sum.
-    const int R = k.M + 1;
-    for (int idx = tid; idx < kTileTokens * R; idx += kThreads) {
-        const int tl = idx / R, m = idx % R;
-        const int64_t t = tile * kTileTokens + tl;
-        if (t >= k.T) continue;
-        float v;
-        if (m < k.M) {
-            const float* rr = red + tl * NC;
-            v = (float)((double)rr[m] + (double)rr[k.M + m] + (double)rr[2 * k.M + m]);
-        } else {
-            v = lds_ss[tl];
-        }
-        k.a.part[((int64_t)s * k.T + t) * k.pstride + m] = v;
-    }
-}
-
-// One workgroup per 64-token tile: reduce the tile's S partial records (written by the
-// projection launch that precedes this one on the stream), then gates, Sinkhorn and
-// all per-token outputs.
-template <int N>
+// Tokens [8 b, 8 b + 8) of workgroup b (all in one tile). A load item is (token, group,
+// chunk): one 16-byte chunk of the token's record from the slices of one summation group
+// (slices [g GS, (g+1) GS)), summed in slice order in fp64; the group sums are then added
+// in group order. Every output of the tokens follows from the totals.
+template <int N, int A>
 __global__ void __launch_bounds__(kThreads)
 epilogue_kernel(KArgs k)
 {
-    constexpr int MMAX = N * N + 2 * N;
-    __shared__ double scratch[kTileTokens * (MMAX + 1) + kTileTokens + kTileTokens * N * N / 2];
-    tile_epilogue<N>(k, blockIdx.x, reinterpret_cast<char*>(scratch));
+    using C = Cfg<N, A>;
+    constexpr int NN = C::NN, V = C::V, CH = C::CH, M = C::M, PPS = C::PPS, OB = C::OB;
+    static_assert(kTileTokens % OB == 0, "a workgroup's tokens lie in one tile");
+    __shared__ double gs[OB * V * 8];    // [token][value][group]; group 0 then holds the total
+    __shared__ float Ls[OB * NN];
+    __shared__ float gpar[3 + M];        // alpha, bias
+    const ForwardArgs& a = k.a;
+    const int tid = threadIdx.x;
+    const int64_t tf = (int64_t)blockIdx.x * OB;
+    const int nb = k.T - tf < OB ? (int)(k.T - tf) : OB;
+    const int64_t tile = tf / kTileTokens;
+    const int tl0 = (int)(tf % kTileTokens);
+    if (tid < A) gpar[tid] = a.alpha[tid];
+    for (int i = tid; i < M; i += kThreads) gpar[3 + i] = a.bias[i];
+
+    const rsrc_t rec = make_rsrc(a.rec + rec_tile(tile, k.S, N, M), (int64_t)k.S * kTileTokens * V * 4);
+    const int items = nb * k.NG * CH;
+    for (int it = tid; it < items; it += kThreads) {
+        const int ch = it % CH, g = (it / CH) % k.NG, q = it / (CH * k.NG);
+        const int sb = group_begin(k.GS, g), se = group_end(k.S, k.GS, g);
+        double acc[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int c0 = sb; c0 < se; c0 += 4) {
+            u32x4 ov[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t off = c0 + c < se ? (uint32_t)(rec_loc(c0 + c, tl0 + q, N, M) + 4 * ch) * 4 : kOutOfRange;
+                ov[c] = __builtin_amdgcn_raw_buffer_load_b128(rec, (int)off, 0, 0);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                if (c0 + c < se) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(ov[c][e]);
+                }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gs[(q * V + 4 * ch + e) * 8 + g] = acc[e];
+    }
+    __syncthreads();
+    for (int it = tid; it < nb * V; it += kThreads) {
+        double t = 0.0;
+        for (int g = 0; g < k.NG; ++g) t += gs[it * 8 + g];
+        gs[it * 8] = t;
+    }
+    __syncthreads();
+
+    const float eps = (float)a.hc_eps;
+    const rsrc_t r_mix = make_rsrc(a.h_mix + tf * M, a.h_mix ? (int64_t)nb * M * 4 : 0);
+    const rsrc_t r_inv = make_rsrc(a.inv_rms + tf, a.inv_rms ? (int64_t)nb * 4 : 0);
+    const rsrc_t r_pre = make_rsrc(a.h_pre + tf * N, a.h_pre ? (int64_t)nb * N * 4 : 0);
+    const rsrc_t r_wts = make_rsrc(a.wts + tf * N, a.pre_mix ? 0 : (int64_t)nb * N * 4);
+    const rsrc_t r_post = make_rsrc(a.h_post + tf * N, (int64_t)nb * N * 4);
+    for (int it = tid; it < nb * M; it += kThreads) {
+        const int q = it / M, m = it % M;
+        const double inv = inv_rms_of(gs[(q * V + N) * 8], (double)k.K, a.norm_eps);
+        const double h = gs[(q * V + (m < N ? m : PPS + (m - N))) * 8];
+        st_buf(r_mix, (uint32_t)it * 4, (float)h);
+        if (m == 0) st_buf(r_inv, (uint32_t)q * 4, (float)inv);
+        if (m < N) {
+            const float hp = gate_pre(h, inv, gpar[0], gpar[3 + m], eps);
+            st_buf(r_pre, (uint32_t)(q * N + m) * 4, hp);
+            st_buf(r_wts, (uint32_t)(q * N + m) * 4, hp);
+        } else if (m < 2 * N) {
+            st_buf(r_post, (uint32_t)(q * N + m - N) * 4, gate_post(h, inv, gpar[1], gpar[3 + m], eps, A == 2));
+        } else {
+            Ls[q * NN + (m - 2 * N)] = res_logit(h, inv, gpar[2], gpar[3 + m]);
+        }
+    }
+    if constexpr (A == 3) {
+        __syncthreads();
+        sinkhorn<N>(k, Ls, tf, nb);
+    } else {
+        const rsrc_t r_res = make_rsrc(a.h_res + tf * NN, a.h_res ? (int64_t)nb * NN * 4 : 0);
+        for (int it = tid; it < nb * NN; it += kThreads) st_buf(r_res, (uint32_t)it * 4, 0.f);
+    }
 }
 
 // ------------------------------------------------------------------ hIn
@@ -478,10 +599,20 @@ hin_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wts,
     *reinterpret_cast<u32x4*>(h_in + t * (int64_t)D + d8 * 8) = o;
 }
 
-template <int NT, int NTHI, int N>
-hipError_t launch_proj(const Plan& p, const KArgs& k, hipStream_t st)
+template <int N, int A, int NKS>
+hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st)
 {
-    hipLaunchKernelGGL((proj_kernel<NT, NTHI, N>), dim3((unsigned)p.blocks), dim3(kThreads), 0, st, k);
+    // The slices of one tile are consecutive workgroups: with S a multiple of 8, slice s
+    // runs on XCD s % 8 for every tile, so each XCD's L2 holds the weights of its slices.
+    hipLaunchKernelGGL((proj_kernel<N, A, NKS>), dim3((unsigned)p.tasks), dim3(kThreads), 0, st, k);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((epilogue_kernel<N, A>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
+    e = hipGetLastError();
+    if (e != hipSuccess || k.a.pre_mix) return e;
+    const int64_t items = p.T * (int64_t)(p.g.D / 8);
+    hipLaunchKernelGGL(hin_kernel<N>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, k.a.x, k.a.wts,
+                       k.a.h_in, p.T, p.g.D);
     return hipGetLastError();
 }
 
@@ -490,10 +621,10 @@ hipError_t launch_proj(const Plan& p, const KArgs& k, hipStream_t st)
 int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void* packed,
                    void* stream)
 {
-    const int64_t total = (int64_t)(g.nch + 1) * kOctets * g.NC;
+    const int64_t total = (int64_t)(g.nks + kPadSteps) * 4 * g.NC;
     const unsigned blocks = (unsigned)((total + 255) / 256);
     hipLaunchKernelGGL(prepack_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, phi, gamma,
-                       static_cast<u32x4*>(packed), g.K, g.M, g.NC, g.nch);
+                       static_cast<u32x4*>(packed), g.n, g.D, g.M, g.NC, g.nks, total);
     return (int)hipGetLastError();
 }
 
@@ -506,33 +637,22 @@ int launch_forward(const Plan& p, const ForwardArgs& a, void* stream)
     k.T = p.T;
     k.K = p.g.K;
     k.D = p.g.D;
-    k.M = p.g.M;
     k.S = p.S;
-    k.nch = p.g.nch;
-    k.pstride = p.pstride;
-    k.n_alpha = p.g.n_alpha;
-
-    hipError_t e;
-    if (p.g.n == 4 && p.g.n_alpha == 3) e = launch_proj<5, 2, 4>(p, k, st);
-    else if (p.g.n == 4 && p.g.n_alpha == 2) e = launch_proj<2, 1, 4>(p, k, st);
-    else if (p.g.n == 8 && p.g.n_alpha == 3) e = launch_proj<15, 5, 8>(p, k, st);
-    else if (p.g.n == 8 && p.g.n_alpha == 2) e = launch_proj<3, 1, 8>(p, k, st);
-    else return (int)hipErrorInvalidValue;
-    if (e != hipSuccess) return (int)e;
-    if (p.g.n == 4)
-        hipLaunchKernelGGL(epilogue_kernel<4>, dim3((unsigned)p.tiles), dim3(kThreads), 0, st, k);
-    else
-        hipLaunchKernelGGL(epilogue_kernel<8>, dim3((unsigned)p.tiles), dim3(kThreads), 0, st, k);
-    e = hipGetLastError();
-    if (e != hipSuccess) return (int)e;
-
-    const int64_t items = p.T * (int64_t)(p.g.D / 8);
-    const unsigned hb = (unsigned)((items + 255) / 256);
-    if (p.g.n == 4)
-        hipLaunchKernelGGL(hin_kernel<4>, dim3(hb), dim3(256), 0, st, a.x, a.wts, a.h_in, p.T, p.g.D);
-    else
-        hipLaunchKernelGGL(hin_kernel<8>, dim3(hb), dim3(256), 0, st, a.x, a.wts, a.h_in, p.T, p.g.D);
-    return (int)hipGetLastError();
+    k.GS = p.GS;
+    k.NG = p.NG;
+    const int n = p.g.n, na = p.g.n_alpha, nks = p.NKS;
+    const Variant v = variant_of(n, na);
+    if (n == 4 && na == 3 && (v.nt != Cfg<4, 3>::NT || v.sk != Cfg<4, 3>::SK)) return (int)hipErrorInvalidValue;
+    if (n == 4 && na == 2 && (v.nt != Cfg<4, 2>::NT || v.sk != Cfg<4, 2>::SK)) return (int)hipErrorInvalidValue;
+    if (n == 8 && na == 3 && (v.nt != Cfg<8, 3>::NT || v.sk != Cfg<8, 3>::SK)) return (int)hipErrorInvalidValue;
+    if (n == 8 && na == 2 && (v.nt != Cfg<8, 2>::NT || v.sk != Cfg<8, 2>::SK)) return (int)hipErrorInvalidValue;
+    hipError_t e = hipErrorInvalidValue;
+    if (n == 4 && na == 3 && nks == 16) e = launch_group<4, 3, 16>(p, k, st);
+    else if (n == 4 && na == 2 && nks == 32) e = launch_group<4, 2, 32>(p, k, st);
+    else if (n == 4 && na == 2 && nks == 16) e = launch_group<4, 2, 16>(p, k, st);
+    else if (n == 8 && na == 3 && nks == 8) e = launch_group<8, 3, 8>(p, k, st);
+    else if (n == 8 && na == 2 && nks == 16) e = launch_group<8, 2, 16>(p, k, st);
+    return (int)e;
 }
 
 }  // namespace mhc

@@ -1,21 +1,29 @@
-// mhc_plan.h -- launch geometry and workspace layout of the fused mHC pre forward.
+// mhc_plan.h -- launch geometry, packed-weight order and workspace layout of the mHC pre
+// forward.
 //
-// Host-side and plain C++ (no HIP headers): the validation / planning code that uses it
-// can be built and tested on a machine without a GPU.
+// Host-side and plain C++ (no HIP headers): the validation / planning code that uses it,
+// and the index checks of the tests, build and run on a machine without a GPU. The
+// offset helpers below are the ones the kernels use.
 //
-// Data layout the kernels rely on
-//   xFlat of token t is x[t*K .. t*K + K) with K = n*D (TND, row-major; stream i occupies
-//   [i*D, (i+1)*D)). The reduction dimension K is walked in chunks of 128 consecutive
-//   xFlat elements (256 bytes of a token row: two whole cache lines), as 16 "octets" of
-//   8 bf16. The matrix-core K-step s of a chunk consumes octets 4s .. 4s+3, lane group g
-//   (= lane / 16) holding octet 4s + g. Any order of K gives the same dot product, so
-//   the packed weights only need to use this same order. D % 8 == 0 keeps every octet
-//   inside one stream.
-//   Packed weights: for each chunk, 16 octet rows x NC columns of 8 bf16 (16 bytes),
-//   octet-major. Column c < 3M is term (c / M) of phi row (c % M) with gamma folded in:
-//   term 0 = hi, 1 = mid, 2 = lo, hi + mid + lo = phi * gamma to ~2^-26 relative.
-//   Columns >= 3M, octets at or beyond K, and one extra all-zero chunk at the end (so the
-//   one-chunk-ahead weight prefetch never needs a bounds test) hold zeros.
+// Work decomposition
+//   The projection runs as tasks of one tile of 64 tokens x one d-slice: the same range
+//   of hidden positions d in every one of the n streams, so that with pre_mix (hIn weights
+//   given) the task's x, loaded once, also yields the slice's part of hIn = sum_i w_i x_i.
+//   Each task writes a partial record per token; a per-token epilogue sums the S records
+//   of a token and computes every other output; without pre_mix a last pass computes hIn
+//   from the epilogue's hPre.
+//
+// Reduction order ("K-steps")
+//   Positions are grouped in d-blocks of 32 (four octets of 8 bf16). K-step k = (block
+//   b = k / n, stream i = k % n) covers xFlat elements i*D + 32b + [0, 32); matrix-core
+//   lane group g (= lane / 16) takes octet g of it. A slice is a run of NKS consecutive
+//   K-steps (NKS a multiple of n: whole d-blocks). Any order of the reduction gives the
+//   same dot product; the packed weights use this same order.
+//   Packed weights: for each K-step, 4 octet rows (g) x NC columns of 8 bf16 (16 bytes),
+//   row-major. Column c < 3M is term (c / M) of phi row (c % M) with gamma folded in:
+//   term 0 = hi, 1 = mid, 2 = lo, hi + mid + lo = phi * gamma to ~2^-26 relative. Columns
+//   >= 3M, octets at or beyond D, and kPadSteps trailing K-steps hold zeros (the last
+//   slice may run past the data).
 #pragma once
 
 #include <cstddef>
@@ -33,11 +41,14 @@ namespace mhc {
 
 constexpr int kThreads = 256;          // workgroup: 4 waves of 64
 constexpr int kWaves = 4;
-constexpr int kTileTokens = 64;        // tokens per projection tile: 4 waves x 16 rows
-constexpr int kOctets = 16;            // octets per chunk
-constexpr int kChunk = 8 * kOctets;    // xFlat elements per chunk
+constexpr int kTileTokens = 64;        // tokens per task: 4 waves x 16 matrix rows
+constexpr int kBlock = 32;             // positions per d-block
+constexpr int kPadSteps = 32;          // zero K-steps after the data (>= the largest NKS)
+constexpr int kMaxD = 16384;
 constexpr int kMaxN = 8;
-constexpr int kTargetBlocks = 2048;    // projection workgroups to aim for (256 CUs)
+constexpr int64_t kBigTasks = 1024;    // prefer the large slice when it still gives this many tasks
+constexpr int kMaxSlices = 256;        // slices per tile
+constexpr int kOutTokens = 8;          // tokens per epilogue workgroup
 
 struct Geometry {
     int n = 0;
@@ -47,18 +58,38 @@ struct Geometry {
     int64_t K = 0;       // n * D
     int NT = 0;          // 16-wide column tiles covering the 3*M packed columns
     int NC = 0;          // 16 * NT
-    int NTHI = 0;        // column tiles holding the "hi" term (accumulated in fp64)
-    int nch = 0;         // chunks of 128 xFlat elements: ceil(K / 128)
+    int nblk = 0;        // d-blocks: ceil(D / 32)
+    int nks = 0;         // K-steps holding data: nblk * n
     size_t packed_bytes = 0;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+
+// Kernel variant of an (n, n_alpha) pair: column tiles, K-steps per LDS weight stage,
+// and the two slice lengths (K-steps) compiled for it.
+struct Variant {
+    int nt = 0;
+    int sk = 0;
+    int nks_big = 0;
+    int nks_small = 0;
+};
+
+inline Variant variant_of(int n, int n_alpha)
+{
+    Variant v;
+    if (n == 4 && n_alpha == 3) { v.nt = 5; v.sk = 1; v.nks_big = 16; v.nks_small = 16; }
+    else if (n == 4 && n_alpha == 2) { v.nt = 2; v.sk = 4; v.nks_big = 32; v.nks_small = 16; }
+    else if (n == 8 && n_alpha == 3) { v.nt = 15; v.sk = 1; v.nks_big = 8; v.nks_small = 8; }
+    else if (n == 8 && n_alpha == 2) { v.nt = 3; v.sk = 2; v.nks_big = 16; v.nks_small = 16; }
+    return v;
+}
+
 // Returns false for a combination the kernels do not support.
 inline bool make_geometry(int n, int D, int n_alpha, Geometry* g)
 {
     if (n != 4 && n != 8) return false;
-    if (D <= 0 || D % 8 != 0) return false;
+    if (D <= 0 || D % 8 != 0 || D > kMaxD) return false;
     if (n_alpha != 2 && n_alpha != 3) return false;
     Geometry r;
     r.n = n;
@@ -68,9 +99,12 @@ inline bool make_geometry(int n, int D, int n_alpha, Geometry* g)
     r.K = (int64_t)n * D;
     r.NT = (3 * r.M + 15) / 16;
     r.NC = 16 * r.NT;
-    r.NTHI = (r.M + 15) / 16;
-    r.nch = (int)((r.K + kChunk - 1) / kChunk);
-    r.packed_bytes = (size_t)(r.nch + 1) * kOctets * r.NC * 16;
+    r.nblk = (D + kBlock - 1) / kBlock;
+    r.nks = r.nblk * n;
+    r.packed_bytes = (size_t)(r.nks + kPadSteps) * 4 * r.NC * 16;
+    // bounded number of partial records per token
+    const Variant v = variant_of(n, n_alpha);
+    if ((r.nks + v.nks_small - 1) / v.nks_small > kMaxSlices) return false;
     *g = r;
     return true;
 }
@@ -78,19 +112,18 @@ inline bool make_geometry(int n, int D, int n_alpha, Geometry* g)
 struct Plan {
     Geometry g;
     int64_t T = 0;
-    int64_t tiles = 0;        // ceil(T / kTileTokens)
-    int S = 0;                // K-slices (split of the reduction across workgroups)
-    int64_t blocks = 0;       // projection workgroups = tiles * S
-    int pstride = 0;          // floats per token in a partial record: M sums + 1 square sum
-    size_t off_packed = 0, off_wts = 0, off_part = 0, ws_bytes = 0;
+    int64_t tiles = 0;        // ceil(T / 64)
+    int NKS = 0;              // K-steps per slice
+    int S = 0;                // slices per tile
+    int GS = 0;               // slices per summation group: ceil(S / 8)
+    int NG = 0;               // summation groups: ceil(S / GS) <= 8
+    int64_t tasks = 0;        // projection workgroups: tiles * S
+    int64_t out_blocks = 0;   // epilogue workgroups: ceil(T / kOutTokens)
+    size_t off_packed = 0, off_wts = 0, off_rec = 0, ws_bytes = 0;
 };
 
-// First chunk of slice s when nch chunks are split into S nearly equal ranges.
-MHC_HOST_DEVICE inline int slice_begin(int nch, int S, int s)
-{
-    const int base = nch / S, rem = nch % S;
-    return s * base + (s < rem ? s : rem);
-}
+MHC_HOST_DEVICE inline int pp_stride(int n);
+MHC_HOST_DEVICE inline int rec_stride(int n, int M);
 
 inline Plan make_plan(const Geometry& g, int64_t T)
 {
@@ -98,24 +131,60 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     p.g = g;
     p.T = T;
     p.tiles = (T + kTileTokens - 1) / kTileTokens;
-    int64_t want = p.tiles > 0 ? (kTargetBlocks + p.tiles - 1) / p.tiles : 1;
-    if (want > g.nch) want = g.nch;
-    if (want < 1) want = 1;
-    int S = (int)want;
-    if (S >= 8) S -= S % 8;   // a multiple of 8 maps each slice onto one XCD
-    p.S = S;
-    p.blocks = p.tiles * S;
-    p.pstride = g.M + 1;
+    const Variant v = variant_of(g.n, g.n_alpha);
+    const int s_big = (g.nks + v.nks_big - 1) / v.nks_big;
+    p.NKS = p.tiles * s_big >= kBigTasks ? v.nks_big : v.nks_small;
+    p.S = (g.nks + p.NKS - 1) / p.NKS;
+    p.GS = (p.S + 7) / 8;
+    p.NG = (p.S + p.GS - 1) / p.GS;
+    p.tasks = p.tiles * p.S;
+    p.out_blocks = (T + kOutTokens - 1) / kOutTokens;
     size_t off = 0;
     p.off_packed = off;
     off = align_up(off + g.packed_bytes, 256);
     p.off_wts = off;
     off = align_up(off + (size_t)T * g.n * sizeof(float), 256);
-    p.off_part = off;
-    off = align_up(off + (size_t)S * (size_t)T * p.pstride * sizeof(float), 256);
+    p.off_rec = off;
+    off = align_up(off + (size_t)p.tasks * kTileTokens * rec_stride(g.n, g.M) * sizeof(float), 256);
     p.ws_bytes = off;
     return p;
 }
+
+// ---- offsets shared by the kernels and the host-side index checks (in elements) ----
+
+// First slice-local summation group member: slices [g*GS, min(S, (g+1)*GS)).
+MHC_HOST_DEVICE inline int group_begin(int GS, int g) { return g * GS; }
+MHC_HOST_DEVICE inline int group_end(int S, int GS, int g)
+{
+    const int e = (g + 1) * GS;
+    return e < S ? e : S;
+}
+
+// Tokens [tok_begin, tok_end) of a tile whose per-token outputs task (tile, s) writes.
+MHC_HOST_DEVICE inline int out_tok_begin(int S, int s) { return (kTileTokens * s) / S; }
+MHC_HOST_DEVICE inline int out_tok_end(int S, int s) { return (kTileTokens * (s + 1)) / S; }
+
+// Byte offset, within the 64-token tile, of lane (row, grp)'s octet of stream i in the
+// first d-block of the slice starting at d-block b0; d-block a of the slice adds 64 * a.
+MHC_HOST_DEVICE inline uint32_t x_lane_off(int64_t K, int D, int row, int grp, int b0, int i)
+{
+    return (uint32_t)(((int64_t)row * K + (int64_t)i * D + kBlock * b0 + 8 * grp) * 2);
+}
+
+// 16-byte unit offset of the first packed unit of slice s.
+MHC_HOST_DEVICE inline int64_t packed_slice(int s, int NKS, int NC) { return (int64_t)s * NKS * 4 * NC; }
+
+// Partial record of a task for one token: the pre-branch sums and the square sum,
+// padded to pp_stride(n) floats ([pre_0 .. pre_{n-1}, sq, 0...], a 16-byte multiple),
+// then the remaining M - n projections; rec_stride floats in all. A tile's records
+// form one block of S * 64 records, slice-major. Offsets in floats.
+MHC_HOST_DEVICE inline int pp_stride(int n) { return (n + 1 + 3) / 4 * 4; }
+MHC_HOST_DEVICE inline int rec_stride(int n, int M) { return pp_stride(n) + (M - n); }
+MHC_HOST_DEVICE inline int64_t rec_tile(int64_t tile, int S, int n, int M)
+{
+    return tile * S * kTileTokens * rec_stride(n, M);
+}
+MHC_HOST_DEVICE inline int rec_loc(int s, int tl, int n, int M) { return (s * kTileTokens + tl) * rec_stride(n, M); }
 
 // Everything a forward launch needs (device pointers are raw).
 struct ForwardArgs {
@@ -132,8 +201,8 @@ struct ForwardArgs {
     float* h_pre;
     float* sum_out;
     float* norm_out;
-    float* wts;
-    float* part;
+    float* wts;        // [T][n] hIn weights (hPre) from the epilogue
+    float* rec;        // partial records, one block per tile
     int num_iters;
     double norm_eps;
     double hc_eps;

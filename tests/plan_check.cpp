@@ -1,0 +1,116 @@
+// plan_check.cpp -- host-side bounds checks of the fused forward's launch plan.
+//
+// Built with g++ by tests/test_plan_bounds.py (no GPU, no HIP headers). For a sweep of
+// problem sizes it replays, with the offset helpers the kernels use (mhc_plan.h), every
+// index the fused kernel forms from the plan -- packed-weight stage loads, x / hIn byte
+// offsets, partial-record blocks, summation groups, output token shares, workspace
+// sections -- and checks each against the extent of the buffer it addresses. Prints
+// "ok <cases>" or the first violation and exits non-zero.
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "mhc_plan.h"
+
+using namespace mhc;
+
+static int fail(const char* what, int n, int D, int na, long long T, long long a, long long b)
+{
+    std::printf("FAIL %s n=%d D=%d n_alpha=%d T=%lld (%lld vs %lld)\n", what, n, D, na, T, a, b);
+    return 1;
+}
+
+static int check(int n, int D, int na, long long T)
+{
+    Geometry g;
+    if (!make_geometry(n, D, na, &g)) {
+        // refused only when a token would need more than kMaxSlices partial records
+        const Variant v0 = variant_of(n, na);
+        const int nks = (D + kBlock - 1) / kBlock * n;
+        if ((nks + v0.nks_small - 1) / v0.nks_small > kMaxSlices) return 0;
+        return fail("geometry", n, D, na, T, 0, 0);
+    }
+    const Plan p = make_plan(g, T);
+    const Variant v = variant_of(n, na);
+    if (v.nt != g.NT) return fail("variant nt", n, D, na, T, v.nt, g.NT);
+    if (p.NKS % n || p.NKS % v.sk) return fail("slice not whole blocks/stages", n, D, na, T, p.NKS, v.sk);
+    if (p.NKS > kPadSteps) return fail("slice longer than the zero tail", n, D, na, T, p.NKS, kPadSteps);
+    // every K-step with data is in some slice; the last slice's loads stay in the packed buffer
+    if ((long long)p.S * p.NKS < g.nks) return fail("slices miss K-steps", n, D, na, T, p.S * p.NKS, g.nks);
+    const long long units = (long long)(g.nks + kPadSteps) * 4 * g.NC;
+    if ((long long)g.packed_bytes != units * 16) return fail("packed bytes", n, D, na, T, g.packed_bytes, units * 16);
+    const long long last_unit = packed_slice(p.S - 1, p.NKS, g.NC) + (long long)p.NKS * 4 * g.NC;
+    if (last_unit > units) return fail("packed stage load past end", n, D, na, T, last_unit, units);
+    // bounded records per token
+    if (p.S > kMaxSlices) return fail("too many slices", n, D, na, T, p.S, kMaxSlices);
+    // summation groups: at most 8, contiguous, covering [0, S)
+    if (p.NG < 1 || p.NG > 8) return fail("groups", n, D, na, T, p.NG, 8);
+    int next = 0;
+    for (int gi = 0; gi < p.NG; ++gi) {
+        const int b = group_begin(p.GS, gi), e = group_end(p.S, p.GS, gi);
+        if (b != next || e <= b) return fail("group partition", n, D, na, T, b, next);
+        next = e;
+    }
+    if (next != p.S) return fail("group cover", n, D, na, T, next, p.S);
+    // output token shares partition [0, 64)
+    next = 0;
+    for (int s = 0; s < p.S; ++s) {
+        const int b = out_tok_begin(p.S, s), e = out_tok_end(p.S, s);
+        if (b != next || e < b) return fail("token shares", n, D, na, T, b, next);
+        next = e;
+    }
+    if (next != kTileTokens) return fail("token cover", n, D, na, T, next, kTileTokens);
+    // x byte offsets within a tile fit the 32-bit buffer offset; the largest one any lane
+    // forms (row 63, last stream, last block of the last slice, group 3, 16 bytes)
+    const int bps = p.NKS / n;
+    const long long xmax = (long long)x_lane_off(g.K, D, 63, 3, (p.S - 1) * bps, n - 1) +
+                           2LL * kBlock * (bps - 1) + 16;
+    const long long xexact = ((63LL * g.K) + (long long)(n - 1) * D + kBlock * ((long long)(p.S - 1) * bps + bps - 1) + 24 + 8) * 2;
+    if (xmax != xexact) return fail("x offset helper", n, D, na, T, xmax, xexact);
+    if (xmax >= (1LL << 31)) return fail("x offset overflow", n, D, na, T, xmax, 1LL << 31);
+    if (64LL * g.K * 2 >= (1LL << 31)) return fail("x tile range overflow", n, D, na, T, 64LL * g.K * 2, 1LL << 31);
+    // hIn offsets: row 63, last block of the last slice
+    const long long hmax = ((63LL * D) + kBlock * ((long long)(p.S - 1) * bps + bps - 1) + 24 + 8) * 2;
+    if (hmax >= (1LL << 31)) return fail("hIn offset overflow", n, D, na, T, hmax, 1LL << 31);
+    // partial-record blocks: per-tile byte ranges fit the buffer offsets; records of
+    // different (slice, token) pairs do not overlap; 16-byte chunks stay 16-byte aligned
+    const long long pps = pp_stride(n), rs = rec_stride(n, g.M);
+    if (pps % 4 || rs % 4 || pps < n + 1 || rs != pps + g.M - n) return fail("record strides", n, D, na, T, pps, rs);
+    const long long recb = (long long)p.S * kTileTokens * rs * 4;
+    if (recb >= (1LL << 31)) return fail("record block overflow", n, D, na, T, recb, 1LL << 31);
+    if (rec_tile(1, p.S, n, g.M) * 4 != recb) return fail("record tile stride", n, D, na, T, rec_tile(1, p.S, n, g.M) * 4, recb);
+    if (((long long)rec_loc(p.S - 1, 63, n, g.M) + rs) * 4 != recb)
+        return fail("record local", n, D, na, T, rec_loc(p.S - 1, 63, n, g.M), recb / 4);
+    if ((rec_loc(0, 1, n, g.M) * 4) % 16) return fail("record alignment", n, D, na, T, 0, 0);
+    // epilogue workgroups: 8 tokens each, inside one tile
+    if (kTileTokens % kOutTokens) return fail("epilogue tokens", n, D, na, T, kOutTokens, 0);
+    if (p.out_blocks * kOutTokens < T || (p.out_blocks - 1) * kOutTokens >= T) return fail("epilogue grid", n, D, na, T, p.out_blocks, 0);
+    // workspace sections: ordered, 256-aligned, large enough
+    const size_t secs[] = {p.off_packed, p.off_wts, p.off_rec, p.ws_bytes};
+    for (int i = 0; i < 4; ++i)
+        if (secs[i] % 256) return fail("section alignment", n, D, na, T, i, secs[i]);
+    if (p.off_wts < p.off_packed + g.packed_bytes) return fail("packed size", n, D, na, T, p.off_wts, 0);
+    if (p.off_rec < p.off_wts + (size_t)T * n * 4) return fail("wts size", n, D, na, T, p.off_rec, 0);
+    if (p.ws_bytes < p.off_rec + (size_t)p.tiles * recb) return fail("record size", n, D, na, T, p.ws_bytes, 0);
+    return 0;
+}
+
+int main()
+{
+    long long cases = 0;
+    const long long Ts[] = {1, 2, 15, 63, 64, 65, 127, 128, 200, 1000, 4096, 16384, 32768, 100000};
+    std::vector<int> Ds;
+    for (int d = 8; d <= 1024; d += 8) Ds.push_back(d);
+    for (int d = 1032; d <= kMaxD; d += 8 * 37) Ds.push_back(d);
+    const int fixed[] = {2048, 2560, 4096, 5120, 7168, 8192, 16384};
+    for (int d : fixed) Ds.push_back(d);
+    for (int n : {4, 8})
+        for (int na : {2, 3})
+            for (int D : Ds)
+                for (long long T : Ts) {
+                    if (check(n, D, na, T)) return 1;
+                    ++cases;
+                }
+    std::printf("ok %lld\n", cases);
+    return 0;
+}

@@ -62,10 +62,12 @@ def fwd(params, ptrs=None, ws=FAKE, ws_bytes=WS_BIG):
 def test_sizes():
     p = _p(T=16384, D=7168)
     packed = B.packed_size(p)
-    # (224 chunks + 1 zero chunk) x 16 octet rows x 80 columns x 16 bytes
-    assert packed == 225 * 16 * 80 * 16
+    # (224 d-blocks x 4 streams + 32 zero K-steps) x 4 octet rows x 80 columns x 16 bytes
+    assert packed == (896 + 32) * 4 * 80 * 16
     ws = B.workspace_size(p)
-    assert ws >= packed + 16384 * 4 * 4 + 8 * 16384 * 25 * 4
+    # packed weights, hIn weights, and 32 slices of partial records (8 + 20 floats per
+    # token) for each of the 256 tiles
+    assert ws >= packed + 16384 * 4 * 4 + 32 * 16384 * 28 * 4
     assert B.workspace_size(_p(T=0, D=7168)) >= packed
 
 
@@ -87,6 +89,7 @@ def test_null_params_workspace_and_weights():
 
 
 @pytest.mark.parametrize("kw", [dict(n=6), dict(n=2), dict(n=16), dict(D=0), dict(D=-8), dict(D=12),
+                                dict(D=16392), dict(n=8, D=8200),
                                 dict(n_alpha=4), dict(n_alpha=1), dict(num_iters=0),
                                 dict(norm_eps=0.0), dict(norm_eps=float("nan")),
                                 dict(hc_eps=-1e-6), dict(T=-1)])
