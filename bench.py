@@ -1,31 +1,47 @@
-"""Benchmark of the fused mHC pre-mapping forward on one MI355X.
+"""Benchmark of the mHC pre-mapping forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole path over one batch: pack the weights (phi with
-gamma folded in) and run the fused forward, i.e. one mhc_pre_forward call with
-unpacked phi. Inputs are seeded synthetic tensors (synth), resident in HBM before
-timing. Prints one JSON line; the GPU timing, the roofline of the dominant launch
-(HIP events on the launch stream) and the CPU oracle baseline are all measured in
-this run.
+gamma folded in) and run the forward, i.e. one mhc_pre_forward call with unpacked
+phi (pack, projection, per-token epilogue, hIn kernels). Inputs are seeded synthetic
+tensors (synth), resident in HBM before timing. Prints one JSON line.
+
+Measured in this run:
+  value        tokens/s over exactly K steps, wall clock between two device syncs;
+  roofline     of the dominant kernel (the one with the largest average duration),
+               its duration from HIP events that the library records on the launch
+               stream around each of its kernels (mhc_pre_forward_timed);
+  cpu_baseline the fp64 C oracle on the host cores, on a bounded sample of tokens.
+Read from profiles/ (measured by rocprofv3 counter runs of this same script):
+  roofline.traffic  HBM bytes per launch of that kernel from FETCH_SIZE and
+               WRITE_SIZE, each divided by the factor the same counter reads for a
+               plain device copy of known size; null when no counter summary exists
+               for this kernel and workload, or when the kernel source has changed
+               since it was taken (source SHA-256 recorded beside the counts).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 METRIC = "tokens/s and achieved HBM GB/s (% of peak) for fused mHC pre fwd, n=4"
+KERNEL_SOURCES = ("mhc_hyper_connection_amd/csrc/mhc_kernels.hip",
+                  "mhc_hyper_connection_amd/csrc/mhc_plan.h")
+KERNEL_NAMES = {"pack": "prepack_kernel", "projection": "proj_kernel",
+                "epilogue": "epilogue_kernel", "hin": "hin_kernel"}
 
 
 def algorithmic_bytes(wl, *, intermediates: bool) -> int:
-    """Bytes the method must move once: x, phi, alpha, bias, gamma, pre_mix read once,
-    every requested output written once (per token: 2K + 2D + 4n + 4n^2, plus
-    4 + 4M + 4n + 2it*4n + 2it*4n^2 with the backward intermediates)."""
+    """Bytes the method must move once for the whole call: x, phi, alpha, bias, gamma,
+    pre_mix read once, every requested output written once (per token: 2K + 2D + 4n
+    + 4n^2, plus 4 + 4M + 4n + 2it*4n + 2it*4n^2 with the backward intermediates)."""
     T, n, D, M, it = wl.T, wl.n, wl.D, wl.M, wl.num_iters
     K = n * D
     b = T * 2 * K + M * K * 4 + wl.n_alpha * 4 + M * 4
@@ -41,6 +57,68 @@ def algorithmic_bytes(wl, *, intermediates: bool) -> int:
         if wl.n_alpha == 3:
             b += 2 * it * T * n * 4 + 2 * it * T * n * n * 4
     return b
+
+
+def stage_bytes(wl, stage: str) -> int:
+    """Algorithmic bytes of one launch of a kernel: what that step of the method must
+    read and write once. Intermediates of this implementation (packed weights, partial
+    records, the hIn weights) are not counted.
+      pack        phi (+ gamma) read once: 4MK (+ 4K)
+      projection  x read once (2K per token) and phi once (4MK); with pre_mix it also
+                  reads pre_mix (4n per token) and writes hIn (2D per token)
+      epilogue    the per-token outputs: hPost, hRes, and the requested intermediates
+      hin         x read once and hIn written once (2K + 2D per token)"""
+    T, n, D, M, it = wl.T, wl.n, wl.D, wl.M, wl.num_iters
+    K = n * D
+    if stage == "pack":
+        return M * K * 4 + (K * 4 if wl.gamma else 0)
+    if stage == "projection":
+        b = T * 2 * K + M * K * 4
+        if wl.pre_mix:
+            b += T * n * 4 + T * D * 2
+        return b
+    if stage == "epilogue":
+        b = T * n * 4 + (T * n * n * 4 if wl.n_alpha == 3 else 0)
+        if wl.need_backward:
+            b += T * 4 + T * M * 4 + T * n * 4
+            if wl.n_alpha == 3:
+                b += 2 * it * T * n * 4 + 2 * it * T * n * n * 4
+        return b
+    if stage == "hin":
+        return 0 if wl.pre_mix else T * 2 * K + T * D * 2
+    raise ValueError(stage)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(stage: str, workload: str):
+    """HBM bytes per launch from profiles/<kernel>_<workload>_counters.md, or None."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAMES[stage]}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip().strip("`").strip()
+            if ":" in line and line.split(":", 1)[0].strip() in (
+                    "source_sha256", "fetch_kib_per_dispatch", "write_kib_per_dispatch",
+                    "fetch_factor", "write_factor"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    try:
+        if vals["source_sha256"] != kernel_source_sha():
+            return None, "kernel changed since the counters were taken"
+        fetch = float(vals["fetch_kib_per_dispatch"]) * 1024 / float(vals["fetch_factor"])
+        write = float(vals["write_kib_per_dispatch"]) * 1024 / float(vals["write_factor"])
+    except (KeyError, ValueError):
+        return None, "counter summary incomplete"
+    return fetch + write, os.path.relpath(path, ROOT)
 
 
 def cpu_baseline(inp, max_tokens: int):
@@ -61,18 +139,32 @@ def cpu_baseline(inp, max_tokens: int):
                       f"fp64 C oracle, {threads} OpenMP threads, {dt:.2f} s"}
 
 
+def calibration_copy(torch, dev, mib: int, reps: int = 3):
+    """A plain device copy of `mib` MiB, `reps` times: the known-size reference the
+    counter runs divide FETCH_SIZE and WRITE_SIZE by (src read once, dst written once)."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="large_prefill_bwd")
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=65536,
+                    help="tokens of the workload the CPU oracle baseline runs on (bounded)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run a plain copy of this size first (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this operator has no cross-GPU step and the "
-              f"build targets a single MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the forward has no cross-GPU step and this "
+              f"build runs on a single MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -100,33 +192,47 @@ def main():
     out = run.alloc_outputs()
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        run(x, phi, alpha, bias, gamma, pre_mix, out=out)
+    if args.calib_copy_mib > 0:
+        print(f"[bench] calibration copy {args.calib_copy_mib} MiB", file=sys.stderr, flush=True)
+        calibration_copy(torch, dev, args.calib_copy_mib)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        step()
+        run(x, phi, alpha, bias, gamma, pre_mix, out=out)
     torch.cuda.synchronize(dev)
 
-    # timed region: exactly K steps, bracketed by device synchronisation; per-step HIP
-    # events on the launch stream give the launch-group duration for the roofline
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # one set of events per timed step; each is recorded once here so that its HIP
+    # event exists before the library records it
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(mhc.FORWARD_EVENTS)]
            for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    for row in evs:
+        for e in row:
+            e.record(stream)
     torch.cuda.synchronize(dev)
+
+    # timed region: exactly K steps, bracketed by device synchronisation
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        e0.record(stream)
-        step()
-        e1.record(stream)
+    for row in evs:
+        run(x, phi, alpha, bias, gamma, pre_mix, out=out, events=row)
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
-    ev_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     ms_step = elapsed * 1e3 / args.steps
-    ev_avg = sum(ev_ms) / len(ev_ms)
 
-    b_alg = algorithmic_bytes(wl, intermediates=wl.need_backward)
-    achieved = b_alg / (ev_avg * 1e-3) / 1e9
+    kernels = {}
+    for i, stage in enumerate(mhc.STAGES):
+        ms = [row[i].elapsed_time(row[i + 1]) for row in evs]
+        kernels[stage] = {"kernel": KERNEL_NAMES[stage], "avg_us": 1e3 * sum(ms) / len(ms),
+                          "min_us": 1e3 * min(ms),
+                          "algorithmic_bytes": stage_bytes(wl, stage)}
+    call_us = [1e3 * row[0].elapsed_time(row[-1]) for row in evs]
+    dom = max(kernels, key=lambda s: kernels[s]["avg_us"])
+    kd = kernels[dom]
+    achieved = kd["algorithmic_bytes"] / (kd["avg_us"] * 1e-6) / 1e9
+    traffic, traffic_src = counter_traffic(dom, wl.name)
+    b_call = algorithmic_bytes(wl, intermediates=wl.need_backward)
+    call_avg = sum(call_us) / len(call_us)
+
     line = {
         "metric": METRIC,
         "value": wl.T / (ms_step * 1e-3),
@@ -142,12 +248,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "n": wl.n, "D": wl.D, "n_alpha": wl.n_alpha,
                    "gamma": wl.gamma, "pre_mix": wl.pre_mix, "need_backward": wl.need_backward,
-                   "num_iters": wl.num_iters, "step": "weight pack + fused forward (one mhc_pre_forward call)"},
+                   "num_iters": wl.num_iters,
+                   "step": "weight pack + forward (one mhc_pre_forward call, unpacked phi)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "mhc_pre_forward launch group (pack + projection + hIn)",
-                     "algorithmic_bytes": b_alg, "avg_launch_ms": ev_avg,
-                     "min_launch_ms": min(ev_ms)},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": kd["kernel"], "algorithmic_bytes": kd["algorithmic_bytes"],
+                     "avg_launch_us": kd["avg_us"], "traffic_source": traffic_src},
+        "call": {"algorithmic_bytes": b_call, "avg_us": call_avg,
+                 "achieved_GBs": b_call / (call_avg * 1e-6) / 1e9,
+                 "frac": b_call / (call_avg * 1e-6) / 1e9 / HBM_PEAK_GBS},
+        "kernels": kernels,
     }
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)

@@ -148,6 +148,28 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
 mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Events mhc_pre_forward_timed records: one before the first kernel and one after each
+ * of the forward's four kernels. */
+#define MHC_FORWARD_EVENTS 5
+
+/* mhc_pre_forward, plus per-kernel timing: also records the caller's events (hipEvent_t
+ * handles, created by the caller, who keeps ownership) on `stream`, in this order:
+ *   events[0] before the weight-pack kernel,
+ *   events[1] after it, before the projection kernel,
+ *   events[2] after the projection kernel,
+ *   events[3] after the per-token epilogue kernel,
+ *   events[4] after the hIn kernel.
+ * A kernel the call does not launch (the pack when phi_packed is given, the hIn kernel
+ * when pre_mix is given: the projection writes hIn then) has its two events recorded
+ * back to back, so elapsed time between events[i] and events[i+1] is kernel i's duration
+ * (plus the launch gap) whatever the inputs; with T == 0 all five are recorded back to
+ * back. Computes exactly what mhc_pre_forward computes.
+ * Errors: as mhc_pre_forward; NULLPTR also for a NULL events array or handle;
+ * PARAM_INVALID when num_events != MHC_FORWARD_EVENTS. */
+mhc_status mhc_pre_forward_timed(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* events, int32_t num_events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,11 +14,13 @@ from __future__ import annotations
 
 import math
 
-from ._binding import (MHC_ERR_NULLPTR, MHC_ERR_PARAM_INVALID, MHC_ERR_RUNTIME, MHC_OK,
-                       MhcError, Params, load, make_params, packed_size, raw_forward,
-                       raw_prepack, status_string, version, workspace_size)
+from ._binding import (FORWARD_EVENTS, MHC_ERR_NULLPTR, MHC_ERR_PARAM_INVALID,
+                       MHC_ERR_RUNTIME, MHC_OK, STAGES, MhcError, Params, load, make_params,
+                       packed_size, raw_forward, raw_forward_timed, raw_prepack,
+                       status_string, version, workspace_size)
 
 __all__ = ["PreForward", "mhc_pre", "prepack", "version", "status_string", "MhcError",
+           "FORWARD_EVENTS", "STAGES",
            "make_params", "packed_size", "workspace_size", "load",
            "MHC_OK", "MHC_ERR_NULLPTR", "MHC_ERR_PARAM_INVALID", "MHC_ERR_RUNTIME"]
 
@@ -113,7 +115,10 @@ class PreForward:
 
     # -- forward -----------------------------------------------------------------------
     def __call__(self, x, phi, alpha, bias, gamma=None, pre_mix=None, *, phi_packed=None,
-                 out=None):
+                 out=None, events=None):
+        """events: optional list of FORWARD_EVENTS torch.cuda.Event(enable_timing=True),
+        each recorded at least once before (so that its HIP event exists); the call then
+        records them around its kernels (STAGES order), see mhc_pre_forward_timed."""
         torch = _torch()
         T, n, D, M, dev = self.T, self.n, self.D, self.M, self.device
         _check(x, "x", torch.bfloat16, (T, n, D), dev)
@@ -129,10 +134,16 @@ class PreForward:
                 "gamma": _ptr(gamma), "pre_mix": _ptr(pre_mix), "phi_packed": _ptr(phi_packed)}
         for k, v in out.items():
             ptrs[k] = _ptr(v)
-        st = raw_forward(self.params, ptrs, _ptr(self.workspace), self.ws_bytes,
-                         _stream(dev))
-        if st != MHC_OK:
-            raise MhcError(st, "mhc_pre_forward")
+        if events is None:
+            st = raw_forward(self.params, ptrs, _ptr(self.workspace), self.ws_bytes,
+                             _stream(dev))
+            if st != MHC_OK:
+                raise MhcError(st, "mhc_pre_forward")
+        else:
+            st = raw_forward_timed(self.params, ptrs, _ptr(self.workspace), self.ws_bytes,
+                                   _stream(dev), [e.cuda_event or None for e in events])
+            if st != MHC_OK:
+                raise MhcError(st, "mhc_pre_forward_timed")
         return out
 
 

@@ -40,7 +40,13 @@ class Tensors(ctypes.Structure):
 
 
 EXPORTS = ("mhc_version", "mhc_status_string", "mhc_pre_packed_size",
-           "mhc_pre_workspace_size", "mhc_pre_prepack", "mhc_pre_forward")
+           "mhc_pre_workspace_size", "mhc_pre_prepack", "mhc_pre_forward",
+           "mhc_pre_forward_timed")
+
+# MHC_FORWARD_EVENTS: events of mhc_pre_forward_timed (before the first kernel, then one
+# after each of pack, projection, epilogue, hIn)
+FORWARD_EVENTS = 5
+STAGES = ("pack", "projection", "epilogue", "hin")
 
 _lib = None
 
@@ -69,6 +75,10 @@ def load(path: str | None = None):
     lib.mhc_pre_forward.restype = ctypes.c_int32
     lib.mhc_pre_forward.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Tensors),
                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.mhc_pre_forward_timed.restype = ctypes.c_int32
+    lib.mhc_pre_forward_timed.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Tensors),
+                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
     if path is None:
         _lib = lib
     return lib
@@ -112,3 +122,11 @@ def raw_prepack(params: Params, phi_ptr, gamma_ptr, packed_ptr, packed_bytes, st
 def raw_forward(params: Params, ptrs: dict, ws_ptr, ws_bytes, stream) -> int:
     t = Tensors(*[ptrs.get(f) for f in TENSOR_FIELDS])
     return int(load().mhc_pre_forward(ctypes.byref(params), ctypes.byref(t), ws_ptr, ws_bytes, stream))
+
+
+def raw_forward_timed(params: Params, ptrs: dict, ws_ptr, ws_bytes, stream, events) -> int:
+    """events: sequence of raw hipEvent_t handles (ints or None)."""
+    t = Tensors(*[ptrs.get(f) for f in TENSOR_FIELDS])
+    arr = (ctypes.c_void_p * max(len(events), 1))(*events)
+    return int(load().mhc_pre_forward_timed(ctypes.byref(params), ctypes.byref(t), ws_ptr, ws_bytes,
+                                            stream, arr, len(events)))

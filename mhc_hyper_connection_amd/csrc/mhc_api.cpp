@@ -84,8 +84,14 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
     return mhc::launch_prepack(g, phi, gamma, phi_packed, stream) == 0 ? MHC_OK : MHC_ERR_RUNTIME;
 }
 
-mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* t,
-                           void* workspace, size_t workspace_bytes, void* stream)
+}  // extern "C"
+
+namespace {
+
+// The forward; events is NULL or mhc::kStages + 1 validated, non-NULL hipEvent_t handles.
+mhc_status forward_impl(const mhc_pre_params* params, const mhc_pre_tensors* t,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        void* const* events)
 {
     // 1. required pointers
     if (!params || !t) return MHC_ERR_NULLPTR;
@@ -122,15 +128,21 @@ mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* 
     for (const void* q : f32s)
         if (q && !aligned(q, 4)) return MHC_ERR_PARAM_INVALID;
 
-    if (params->T == 0) return MHC_OK;   // empty input: success, nothing launched
+    if (params->T == 0) {   // empty input: success, no kernel launched
+        for (int i = 0; events && i <= mhc::kStages; ++i)
+            if (mhc::record_event(events[i], stream) != 0) return MHC_ERR_RUNTIME;
+        return MHC_OK;
+    }
 
     char* ws = static_cast<char*>(workspace);
     const void* packed = t->phi_packed;
+    if (events && mhc::record_event(events[mhc::kStagePack], stream) != 0) return MHC_ERR_RUNTIME;
     if (!packed) {
         void* dst = ws + plan.off_packed;
         if (mhc::launch_prepack(g, t->phi, t->gamma, dst, stream) != 0) return MHC_ERR_RUNTIME;
         packed = dst;
     }
+    if (events && mhc::record_event(events[mhc::kStageProj], stream) != 0) return MHC_ERR_RUNTIME;
 
     mhc::ForwardArgs a;
     std::memset(&a, 0, sizeof a);
@@ -152,7 +164,30 @@ mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* 
     a.num_iters = params->num_iters;
     a.norm_eps = params->norm_eps;
     a.hc_eps = params->hc_eps;
-    return mhc::launch_forward(plan, a, stream) == 0 ? MHC_OK : MHC_ERR_RUNTIME;
+    return mhc::launch_forward(plan, a, stream, events) == 0 ? MHC_OK : MHC_ERR_RUNTIME;
+}
+
+}  // namespace
+
+extern "C" {
+
+mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* t,
+                           void* workspace, size_t workspace_bytes, void* stream)
+{
+    return forward_impl(params, t, workspace, workspace_bytes, stream, nullptr);
+}
+
+static_assert(MHC_FORWARD_EVENTS == mhc::kStages + 1, "one event per kernel boundary");
+
+mhc_status mhc_pre_forward_timed(const mhc_pre_params* params, const mhc_pre_tensors* t,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* events, int32_t num_events)
+{
+    if (!events) return MHC_ERR_NULLPTR;
+    for (int i = 0; i < num_events && i <= mhc::kStages; ++i)
+        if (!events[i]) return MHC_ERR_NULLPTR;
+    if (num_events != MHC_FORWARD_EVENTS) return MHC_ERR_PARAM_INVALID;
+    return forward_impl(params, t, workspace, workspace_bytes, stream, events);
 }
 
 }  // extern "C"

@@ -110,6 +110,7 @@ struct KArgs {
     ForwardArgs a;
     int64_t T;
     int64_t K;
+    int64_t tiles;
     int D;
     int S;
     int GS;
@@ -261,8 +262,9 @@ proj_kernel(KArgs k)
     const int j = lane & 15;      // A row (token) / B column / D column
     const int grp = lane >> 4;    // K-group of A and B; row block of D
     const int row = wave * 16 + j;   // the lane's token within the tile
-    const int64_t tile = blockIdx.x / k.S;
-    const int s = (int)(blockIdx.x % k.S);
+    int64_t tile;
+    int s;
+    if (!task_of_block(blockIdx.x, k.tiles, k.S, &tile, &s)) return;   // padding workgroup
     const int64_t t0 = tile * kTileTokens;
     const int ntile = tile_tokens(k, t0);
     const int b0 = s * (NKS / N);
@@ -596,24 +598,35 @@ hin_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wts,
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         o[e] = f32_to_bf16_bits(acc[2 * e]) | (f32_to_bf16_bits(acc[2 * e + 1]) << 16);
-    *reinterpret_cast<u32x4*>(h_in + t * (int64_t)D + d8 * 8) = o;
+    // hIn is not read again by this forward: stream it past the caches
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(h_in + t * (int64_t)D + d8 * 8));
+}
+
+// Records events[i] (a caller-created hipEvent_t) on the stream when events is given.
+hipError_t mark(void* const* events, int i, hipStream_t st)
+{
+    return events ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
 }
 
 template <int N, int A, int NKS>
-hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st)
+hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st, void* const* events)
 {
-    // The slices of one tile are consecutive workgroups: with S a multiple of 8, slice s
-    // runs on XCD s % 8 for every tile, so each XCD's L2 holds the weights of its slices.
-    hipLaunchKernelGGL((proj_kernel<N, A, NKS>), dim3((unsigned)p.tasks), dim3(kThreads), 0, st, k);
+    // Workgroups map to tasks so that each XCD's L2 holds the weights of a few slices
+    // only (task_of_block).
+    hipLaunchKernelGGL((proj_kernel<N, A, NKS>), dim3((unsigned)p.proj_blocks), dim3(kThreads), 0, st, k);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = mark(events, kStageProj + 1, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((epilogue_kernel<N, A>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
     e = hipGetLastError();
+    if (e == hipSuccess) e = mark(events, kStageEpi + 1, st);
+    if (e == hipSuccess && k.a.pre_mix) e = mark(events, kStageHin + 1, st);
     if (e != hipSuccess || k.a.pre_mix) return e;
     const int64_t items = p.T * (int64_t)(p.g.D / 8);
     hipLaunchKernelGGL(hin_kernel<N>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, k.a.x, k.a.wts,
                        k.a.h_in, p.T, p.g.D);
-    return hipGetLastError();
+    e = hipGetLastError();
+    return e == hipSuccess ? mark(events, kStageHin + 1, st) : e;
 }
 
 }  // namespace
@@ -628,7 +641,12 @@ int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void
     return (int)hipGetLastError();
 }
 
-int launch_forward(const Plan& p, const ForwardArgs& a, void* stream)
+int record_event(void* event, void* stream)
+{
+    return (int)hipEventRecord((hipEvent_t)event, (hipStream_t)stream);
+}
+
+int launch_forward(const Plan& p, const ForwardArgs& a, void* stream, void* const* events)
 {
     if (p.T <= 0) return 0;
     hipStream_t st = (hipStream_t)stream;
@@ -636,6 +654,7 @@ int launch_forward(const Plan& p, const ForwardArgs& a, void* stream)
     k.a = a;
     k.T = p.T;
     k.K = p.g.K;
+    k.tiles = p.tiles;
     k.D = p.g.D;
     k.S = p.S;
     k.GS = p.GS;
@@ -647,11 +666,11 @@ int launch_forward(const Plan& p, const ForwardArgs& a, void* stream)
     if (n == 8 && na == 3 && (v.nt != Cfg<8, 3>::NT || v.sk != Cfg<8, 3>::SK)) return (int)hipErrorInvalidValue;
     if (n == 8 && na == 2 && (v.nt != Cfg<8, 2>::NT || v.sk != Cfg<8, 2>::SK)) return (int)hipErrorInvalidValue;
     hipError_t e = hipErrorInvalidValue;
-    if (n == 4 && na == 3 && nks == 16) e = launch_group<4, 3, 16>(p, k, st);
-    else if (n == 4 && na == 2 && nks == 32) e = launch_group<4, 2, 32>(p, k, st);
-    else if (n == 4 && na == 2 && nks == 16) e = launch_group<4, 2, 16>(p, k, st);
-    else if (n == 8 && na == 3 && nks == 8) e = launch_group<8, 3, 8>(p, k, st);
-    else if (n == 8 && na == 2 && nks == 16) e = launch_group<8, 2, 16>(p, k, st);
+    if (n == 4 && na == 3 && nks == 16) e = launch_group<4, 3, 16>(p, k, st, events);
+    else if (n == 4 && na == 2 && nks == 32) e = launch_group<4, 2, 32>(p, k, st, events);
+    else if (n == 4 && na == 2 && nks == 16) e = launch_group<4, 2, 16>(p, k, st, events);
+    else if (n == 8 && na == 3 && nks == 8) e = launch_group<8, 3, 8>(p, k, st, events);
+    else if (n == 8 && na == 2 && nks == 16) e = launch_group<8, 2, 16>(p, k, st, events);
     return (int)e;
 }
 

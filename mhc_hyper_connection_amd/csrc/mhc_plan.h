@@ -109,6 +109,28 @@ inline bool make_geometry(int n, int D, int n_alpha, Geometry* g)
     return true;
 }
 
+// Projection workgroup -> task. Workgroup b runs on XCD b % 8 (the hardware deals
+// workgroups to the 8 XCDs in turn). The XCDs are split into G groups of 8 / G, G the
+// largest of 8, 4, 2, 1 dividing S: an XCD of group g works only on the slices
+// s = g + G j, so its L2 holds S / G slices of the weights, and the XCDs of one group
+// share out the tiles. Returns false for the padding workgroups of the last round.
+MHC_HOST_DEVICE inline int xcd_groups(int S) { return S % 8 == 0 ? 8 : (S % 4 == 0 ? 4 : (S % 2 == 0 ? 2 : 1)); }
+MHC_HOST_DEVICE inline int64_t proj_blocks(int64_t tiles, int S)
+{
+    const int G = xcd_groups(S), per = 8 / G;                 // XCDs per group
+    const int64_t rounds = (tiles + per - 1) / per;           // tiles per XCD (rounded up)
+    return rounds * (int64_t)(S / G) * 8;
+}
+MHC_HOST_DEVICE inline bool task_of_block(int64_t b, int64_t tiles, int S, int64_t* tile, int* s)
+{
+    const int G = xcd_groups(S), per = 8 / G, spg = S / G;
+    const int q = (int)(b % 8);
+    const int64_t r = b / 8;
+    *s = q % G + G * (int)(r % spg);
+    *tile = (r / spg) * per + q / G;
+    return *tile < tiles;
+}
+
 struct Plan {
     Geometry g;
     int64_t T = 0;
@@ -117,7 +139,8 @@ struct Plan {
     int S = 0;                // slices per tile
     int GS = 0;               // slices per summation group: ceil(S / 8)
     int NG = 0;               // summation groups: ceil(S / GS) <= 8
-    int64_t tasks = 0;        // projection workgroups: tiles * S
+    int64_t tasks = 0;        // tiles * S
+    int64_t proj_blocks = 0;  // projection workgroups (tasks plus padding, see task_of_block)
     int64_t out_blocks = 0;   // epilogue workgroups: ceil(T / kOutTokens)
     size_t off_packed = 0, off_wts = 0, off_rec = 0, ws_bytes = 0;
 };
@@ -138,6 +161,7 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     p.GS = (p.S + 7) / 8;
     p.NG = (p.S + p.GS - 1) / p.GS;
     p.tasks = p.tiles * p.S;
+    p.proj_blocks = proj_blocks(p.tiles, p.S);
     p.out_blocks = (T + kOutTokens - 1) / kOutTokens;
     size_t off = 0;
     p.off_packed = off;
@@ -208,9 +232,18 @@ struct ForwardArgs {
     double hc_eps;
 };
 
+// Kernels of one forward, in launch order, for per-kernel event timing: events[i] is
+// recorded before stage i's kernel and events[i + 1] after it; a stage that launches
+// nothing (pack with packed weights given, hIn with pre_mix) records its two events
+// back to back.
+constexpr int kStagePack = 0, kStageProj = 1, kStageEpi = 2, kStageHin = 3, kStages = 4;
+
 // Implemented in mhc_kernels.hip. Return 0 on success, else the HIP error code.
 int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void* packed,
                    void* stream);
-int launch_forward(const Plan& p, const ForwardArgs& a, void* stream);
+// events: NULL, or kStages + 1 caller-created events (hipEvent_t) recorded around the
+// projection, epilogue and hIn kernels (events[kStageProj] is recorded by the caller).
+int launch_forward(const Plan& p, const ForwardArgs& a, void* stream, void* const* events);
+int record_event(void* event, void* stream);
 
 }  // namespace mhc

@@ -52,6 +52,26 @@ static int check(int n, int D, int na, long long T)
         next = e;
     }
     if (next != p.S) return fail("group cover", n, D, na, T, next, p.S);
+    // projection workgroups cover every (tile, slice) exactly once, each XCD (b % 8) works
+    // on at most ceil(S / 8) distinct slices when S is even... (S / xcd_groups(S) slices)
+    if (p.tiles > 0 && p.tiles * (long long)p.S <= 4000000) {
+        std::vector<unsigned char> seen((size_t)(p.tiles * p.S), 0);
+        std::vector<std::vector<unsigned char>> xs(8, std::vector<unsigned char>(p.S, 0));
+        for (long long b = 0; b < p.proj_blocks; ++b) {
+            int64_t tile; int s;
+            if (!task_of_block(b, p.tiles, p.S, &tile, &s)) continue;
+            if (tile < 0 || tile >= p.tiles || s < 0 || s >= p.S) return fail("task range", n, D, na, T, tile, s);
+            if (seen[(size_t)(tile * p.S + s)]++) return fail("task twice", n, D, na, T, tile, s);
+            xs[b % 8][s] = 1;
+        }
+        for (size_t i = 0; i < seen.size(); ++i)
+            if (!seen[i]) return fail("task missed", n, D, na, T, (long long)i, 0);
+        for (int q = 0; q < 8; ++q) {
+            int cnt = 0;
+            for (int s = 0; s < p.S; ++s) cnt += xs[q][s];
+            if (cnt > p.S / xcd_groups(p.S)) return fail("slices per XCD", n, D, na, T, cnt, p.S / xcd_groups(p.S));
+        }
+    }
     // output token shares partition [0, 64)
     next = 0;
     for (int s = 0; s < p.S; ++s) {

@@ -148,3 +148,20 @@ def test_prepack_validation():
     assert B.raw_prepack(p, FAKE, None, FAKE, need - 16, None) == B.MHC_ERR_PARAM_INVALID
     assert B.raw_prepack(_p(n=5), FAKE, None, FAKE, need, None) == B.MHC_ERR_PARAM_INVALID
     assert B.raw_prepack(p, FAKE, None, FAKE + 4, need, None) == B.MHC_ERR_PARAM_INVALID
+
+
+def test_timed_forward_validates_events_first():
+    lib = B.load()
+    t = B.Tensors(*[_ptrs().get(f) for f in B.TENSOR_FIELDS])
+    five = (ctypes.c_void_p * 5)(*([FAKE] * 5))
+    # NULL array or a NULL handle: NULLPTR; wrong count: PARAM_INVALID
+    assert lib.mhc_pre_forward_timed(ctypes.byref(_p()), ctypes.byref(t), FAKE, WS_BIG, None,
+                                     None, 5) == B.MHC_ERR_NULLPTR
+    holes = (ctypes.c_void_p * 5)(FAKE, FAKE, None, FAKE, FAKE)
+    assert lib.mhc_pre_forward_timed(ctypes.byref(_p()), ctypes.byref(t), FAKE, WS_BIG, None,
+                                     holes, 5) == B.MHC_ERR_NULLPTR
+    assert lib.mhc_pre_forward_timed(ctypes.byref(_p()), ctypes.byref(t), FAKE, WS_BIG, None,
+                                     five, 4) == B.MHC_ERR_PARAM_INVALID
+    # then the forward's own validation, before any HIP call
+    assert B.raw_forward_timed(_p(n=6), _ptrs(), FAKE, WS_BIG, None, [FAKE] * 5) == B.MHC_ERR_PARAM_INVALID
+    assert B.raw_forward_timed(_p(), _ptrs(x=None), FAKE, WS_BIG, None, [FAKE] * 5) == B.MHC_ERR_NULLPTR
