@@ -19,6 +19,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mhc_oracle.c")
+_SRC_BWD = os.path.join(_HERE, "mhc_oracle_bwd.c")
 _LIB = os.path.join(_HERE, "libmhc_oracle.so")
 
 
@@ -27,7 +28,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+               "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_BWD, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -45,6 +46,21 @@ class _Out(ctypes.Structure):
                  "norm_out", "h_in", "h_in_bf16")]
 
 
+class _BwdIn(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("hc_eps", ctypes.c_double)] + [
+        (name, ctypes.c_void_p) for name in
+        ("x", "phi", "alpha", "grad_h_in", "grad_h_post", "grad_h_res", "inv_rms",
+         "h_mix", "h_pre", "h_post", "gamma", "grad_x_post")]
+
+
+class _BwdOut(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("grad_x", "grad_x_bf16", "grad_x_abs", "grad_phi", "grad_phi_abs",
+                 "grad_alpha", "grad_alpha_abs", "grad_bias", "grad_bias_abs",
+                 "grad_gamma", "grad_gamma_abs", "g_mix")]
+
+
 def _bind(lib):
     lib.oracle_pre_forward.restype = ctypes.c_int
     lib.oracle_pre_forward.argtypes = [
@@ -56,6 +72,14 @@ def _bind(lib):
     lib.oracle_bf16_to_double.restype = ctypes.c_double
     lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_max_threads.restype = ctypes.c_int
+    dp = ctypes.c_void_p
+    lib.oracle_mhcpre_forward_f64.restype = ctypes.c_int
+    lib.oracle_mhcpre_forward_f64.argtypes = [
+        ctypes.c_int64, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp,
+        ctypes.c_double, ctypes.c_double, dp, dp, dp, dp, dp, dp]
+    lib.oracle_pre_backward.restype = ctypes.c_int
+    lib.oracle_pre_backward.argtypes = [ctypes.POINTER(_BwdIn), dp, ctypes.c_int64,
+                                        ctypes.POINTER(_BwdOut), ctypes.c_int]
     return lib
 
 
@@ -155,3 +179,97 @@ def forward(x_bits, phi, alpha, bias, gamma=None, pre_mix=None, *, num_iters=20,
     if rc != 0:
         raise ValueError("oracle rejected the problem description")
     return res
+
+
+@dataclass
+class MhcPreF64:
+    inv_rms: np.ndarray
+    h_mix: np.ndarray
+    h_pre: np.ndarray
+    h_post: np.ndarray
+    h_res: np.ndarray
+    h_in: np.ndarray
+
+
+def mhcpre_forward_f64(x, phi, alpha, bias, gamma=None, *, norm_eps=1e-6, hc_eps=1e-6,
+                       lib=None) -> MhcPreF64:
+    """The MhcPre forward (affine hRes, no Sinkhorn) on float64 inputs: the function whose
+    gradient ``backward`` returns. x: [T, n, D]; phi: [n*n + 2n, n*D]; alpha: [3];
+    bias: [n*n + 2n]; gamma: [n, D] or None. All results float64, hIn unrounded."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    T, n, D = x.shape
+    M = n * n + 2 * n
+    phi = np.ascontiguousarray(phi, dtype=np.float64).reshape(M, n * D)
+    alpha = np.ascontiguousarray(alpha, dtype=np.float64).reshape(3)
+    bias = np.ascontiguousarray(bias, dtype=np.float64).reshape(M)
+    if gamma is not None:
+        gamma = np.ascontiguousarray(gamma, dtype=np.float64).reshape(n, D)
+    r = MhcPreF64(np.empty(T), np.empty((T, M)), np.empty((T, n)), np.empty((T, n)),
+                  np.empty((T, n, n)), np.empty((T, D)))
+    rc = (lib or _load()).oracle_mhcpre_forward_f64(
+        T, n, D, _ptr(x), _ptr(phi), _ptr(alpha), _ptr(bias), _ptr(gamma),
+        float(norm_eps), float(hc_eps), _ptr(r.inv_rms), _ptr(r.h_mix), _ptr(r.h_pre),
+        _ptr(r.h_post), _ptr(r.h_res), _ptr(r.h_in))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem description")
+    return r
+
+
+@dataclass
+class BackwardResult:
+    grad_x: np.ndarray        # [ntok, n, D] float64, unrounded
+    grad_x_bf16: np.ndarray   # [ntok, n, D] bf16 bits
+    grad_x_abs: np.ndarray    # sum of |terms| per gradX element
+    grad_phi: np.ndarray      # [M, n*D]
+    grad_phi_abs: np.ndarray
+    grad_alpha: np.ndarray    # [3]
+    grad_alpha_abs: np.ndarray
+    grad_bias: np.ndarray     # [M]
+    grad_bias_abs: np.ndarray
+    grad_gamma: np.ndarray | None
+    grad_gamma_abs: np.ndarray | None
+    g_mix: np.ndarray         # [T, M]: gradient with respect to hMix
+
+
+def backward(x_bits, phi, alpha, grad_h_in_bits, grad_h_post, grad_h_res, inv_rms, h_mix,
+             h_pre, h_post, gamma=None, grad_x_post_bits=None, *, hc_eps=1e-6, tokens=None,
+             nthreads=0, lib=None) -> BackwardResult:
+    """The MhcPre backward in fp64 from the inputs the GPU receives: x, gradHIn and
+    gradXPost as bf16 bits; phi [n*n + 2n, n*D], alpha [3], gradHPost [T, n],
+    gradHRes [T, n, n], invRms [T], hMix [T, M], hPre [T, n], hPost [T, n], gamma [n, D]
+    as float32. gradX rows are returned for ``tokens`` (default: all); every other
+    gradient sums over all tokens."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, n, D = x_bits.shape
+    M = n * n + 2 * n
+    K = n * D
+    f32 = lambda a, shape: np.ascontiguousarray(a, dtype=np.float32).reshape(shape)
+    phi = f32(phi, (M, K))
+    alpha = f32(alpha, (3,))
+    ghin = np.ascontiguousarray(grad_h_in_bits, dtype=np.uint16).reshape(T, D)
+    ghpost = f32(grad_h_post, (T, n))
+    ghres = f32(grad_h_res, (T, n, n))
+    inv_rms = f32(inv_rms, (T,))
+    h_mix = f32(h_mix, (T, M))
+    h_pre = f32(h_pre, (T, n))
+    h_post = f32(h_post, (T, n))
+    if gamma is not None:
+        gamma = f32(gamma, (n, D))
+    if grad_x_post_bits is not None:
+        grad_x_post_bits = np.ascontiguousarray(grad_x_post_bits, dtype=np.uint16).reshape(T, n, D)
+    tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int64).reshape(-1)
+    ntok = T if tok is None else int(tok.shape[0])
+    g = gamma is not None
+    r = BackwardResult(
+        np.empty((ntok, n, D)), np.empty((ntok, n, D), dtype=np.uint16), np.empty((ntok, n, D)),
+        np.empty((M, K)), np.empty((M, K)), np.empty(3), np.empty(3), np.empty(M), np.empty(M),
+        np.empty((n, D)) if g else None, np.empty((n, D)) if g else None, np.empty((T, M)))
+    bin_ = _BwdIn(T, n, D, float(hc_eps), *[_ptr(a) for a in (
+        x_bits, phi, alpha, ghin, ghpost, ghres, inv_rms, h_mix, h_pre, h_post, gamma,
+        grad_x_post_bits)])
+    bout = _BwdOut(*[_ptr(getattr(r, f)) for f, _ in _BwdOut._fields_])
+    rc = (lib or _load()).oracle_pre_backward(ctypes.byref(bin_), _ptr(tok), ntok,
+                                              ctypes.byref(bout), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem description")
+    return r
