@@ -13,6 +13,7 @@ import oracle
 import oracle_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "mhc_oracle.c")
+BWD = os.path.join(os.path.dirname(oracle.__file__), "mhc_oracle_bwd.c")   # built beside it, unchanged
 
 MUTANTS = {
     "rms_mean_over_D": ("ss / (double)K + c->norm_eps", "ss / (double)D + c->norm_eps"),
@@ -62,7 +63,7 @@ def test_pins_catch_mutant(name, source, tmp_path):
     so_path = tmp_path / "libmutant.so"
     c_path.write_text(mutated)
     subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-w",
-                    "-o", str(so_path), str(c_path), "-lm"], check=True)
+                    "-o", str(so_path), str(c_path), BWD, "-lm"], check=True)
     lib = oracle.load_library(str(so_path))
     caught = []
     for pin in oracle_pins.ALL_PINS:
