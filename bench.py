@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 METRIC = "tokens/s and achieved HBM GB/s (% of peak) for fused mHC pre fwd, n=4"
 KERNEL_SOURCES = ("mhc_hyper_connection_amd/csrc/mhc_kernels.hip",
+                  "mhc_hyper_connection_amd/csrc/mhc_device.h",
                   "mhc_hyper_connection_amd/csrc/mhc_plan.h")
 KERNEL_NAMES = {"pack": "prepack_kernel", "projection": "proj_kernel",
                 "epilogue": "epilogue_kernel", "hin": "hin_kernel"}

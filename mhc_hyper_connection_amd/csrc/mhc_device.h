@@ -1,0 +1,70 @@
+// mhc_device.h -- device helpers shared by the kernel files: vector types, bf16 bit
+// conversions, an explicit vector-memory wait, and raw buffer resources.
+//
+// Everything is in an unnamed namespace inside mhc: each translation unit that includes
+// it gets its own internal copy (no device symbols cross translation units).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace mhc {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ double bf16_bits_to_double(uint32_t b)
+{
+    return (double)__uint_as_float(b << 16);
+}
+
+// s_waitcnt vmcnt(n): at most n vector memory operations of this wave outstanding. Called
+// from fully unrolled loops with n a constant after unrolling; each case is one instruction.
+#define MHC_VM_CASE(n) \
+    case n: __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00); break;
+#define MHC_VM_CASE8(b) MHC_VM_CASE(b) MHC_VM_CASE(b + 1) MHC_VM_CASE(b + 2) MHC_VM_CASE(b + 3) \
+    MHC_VM_CASE(b + 4) MHC_VM_CASE(b + 5) MHC_VM_CASE(b + 6) MHC_VM_CASE(b + 7)
+__device__ __forceinline__ void wait_vm(int n)
+{
+    switch (n < 0 ? 0 : (n > 63 ? 63 : n)) {
+        MHC_VM_CASE8(0) MHC_VM_CASE8(8) MHC_VM_CASE8(16) MHC_VM_CASE8(24)
+        MHC_VM_CASE8(32) MHC_VM_CASE8(40) MHC_VM_CASE8(48) MHC_VM_CASE8(56)
+        default: break;
+    }
+}
+#undef MHC_VM_CASE8
+#undef MHC_VM_CASE
+
+// Buffer resources: a base address and a byte range in four scalar registers; vector
+// accesses take a 32-bit byte offset, and loads outside the range return zero (stores
+// outside it are dropped), which bounds every access of a ragged tile in hardware.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) buffer on gfx9-family targets
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ void st_buf(rsrc_t r, uint32_t off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
+}
+
+}  // namespace
+}  // namespace mhc
