@@ -1,5 +1,6 @@
 /*
- * mhc.h -- C ABI of the fused mHC pre-mapping forward for AMD Instinct MI355X (gfx950).
+ * mhc.h -- C ABI of the fused mHC pre-mapping forward, and of the MhcPre backward, for
+ * AMD Instinct MI355X (gfx950).
  *
  * What one call computes, per token t (x viewed as xFlat of length K = n*D):
  *   invRms = (mean(xFlat^2) + normEps)^(-1/2)
@@ -169,6 +170,95 @@ mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* 
 mhc_status mhc_pre_forward_timed(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  void* const* events, int32_t num_events);
+
+/* ------------------------------------------------------------------ MhcPre backward
+ *
+ * The gradient of the MhcPre forward (aclnnMhcPreV2 guide, section 3: the same invRms,
+ * hMix, gates and hIn as above, with hRes = alpha2 * wRes + biasRes, no Sinkhorn) with
+ * respect to x, phi, alpha, bias and gamma, for the scalar whose gradients with respect to
+ * hIn, hPost and hRes are given. Source: MhcPreBackward guide (0539edu.com/news/4871844),
+ * section 3 (stages 3.1-3.8), section 6.1 (inputs and outputs), section 8.2 (shapes and
+ * types: gradX takes gradHIn's type, the other gradients are float32, gradAlpha has 3
+ * entries). Per token t, with s = hPre - hcEps and w = hMix * invRms:
+ *   gHPre_i = sum_d gradHIn[d] x[i][d]
+ *   gW      = [gHPre s(1-s) alpha0 | gradHPost hPost(1-hPost/2) alpha1 | gradHRes alpha2]
+ *   gMix    = gW invRms;  gInv = sum_m gW[m] hMix[m]
+ *   gradX   = gradHIn[d] hPre_i + (gMix . phi)[k] gamma[k] - gInv invRms^3 x[k] / (n D)
+ *             + gradXPost[k]                                   (k = i D + d)
+ *   gradPhi[m][k] = sum_t gMix[t][m] x[t][k] gamma[k];  gradGamma[k] = sum_t x[t][k] (gMix[t] . phi)[k]
+ *   gradAlpha = sums over t of (gate term * w) per branch;  gradBias = sums of the gate terms
+ * The RMS term uses raw x (invRms is defined on raw x); the guide writes x_rs there,
+ * which is the same value when gamma is absent. Only the three-entry alpha (n*n + 2n phi
+ * rows) has a backward (section 5 of the guide).
+ *
+ * Problem description (host memory):
+ *   T        tokens, >= 0
+ *   n        4 or 8;  D  a multiple of 8 in [8, 16384]
+ *   hc_eps   >= 0: the hcEps the forward used (hPre = sigmoid(...) + hcEps)
+ *   reserved must be 0 */
+typedef struct mhc_pre_bwd_params {
+    int64_t T;
+    int32_t n;
+    int32_t D;
+    double hc_eps;
+    int32_t reserved;
+    int32_t reserved2;
+} mhc_pre_bwd_params;
+
+/* Device pointers, M = n*n + 2n, K = n*D. Inputs (x, grad_h_in and grad_x_post bf16
+ * bits, the rest float32):
+ *   x            [T, n, D], 16-byte aligned                            required
+ *   phi          [M, K]                                                required
+ *   alpha        [3]                                                   required
+ *   grad_h_in    [T, D], 16-byte aligned                               required
+ *   grad_h_post  [T, n]                                                required
+ *   grad_h_res   [T, n, n]                                             required
+ *   inv_rms      [T]        the forward's saved invRms                  required
+ *   h_mix        [T, M]     the forward's saved (un-normalised) hMix    required
+ *   h_pre        [T, n]     the forward's saved hPre                    required
+ *   h_post       [T, n]     the forward's saved hPost                   required
+ *   gamma        [n, D]                                                optional
+ *   grad_x_post  [T, n, D], 16-byte aligned: added to gradX            optional
+ * Outputs (must not alias inputs or each other):
+ *   grad_x       bf16 [T, n, D], 16-byte aligned                       required
+ *   grad_phi     [M, K]                                                required
+ *   grad_alpha   [3]                                                   required
+ *   grad_bias    [M]                                                   required
+ *   grad_gamma   [n, D]     required when gamma is given, else ignored
+ * With T == 0 the per-token tensors (x, grad_h_in, grad_h_post, grad_h_res, inv_rms,
+ * h_mix, h_pre, h_post, grad_x_post, grad_x) are empty and may be NULL. */
+typedef struct mhc_pre_bwd_tensors {
+    const uint16_t* x;
+    const float* phi;
+    const float* alpha;
+    const uint16_t* grad_h_in;
+    const float* grad_h_post;
+    const float* grad_h_res;
+    const float* inv_rms;
+    const float* h_mix;
+    const float* h_pre;
+    const float* h_post;
+    const float* gamma;
+    const uint16_t* grad_x_post;
+    uint16_t* grad_x;
+    float* grad_phi;
+    float* grad_alpha;
+    float* grad_bias;
+    float* grad_gamma;
+} mhc_pre_bwd_tensors;
+
+/* Bytes of device workspace mhc_pre_backward needs. Host only. The workspace holds
+ * per-call intermediates only (packed phi, per-token gradients, per-group partial sums)
+ * and needs no initialisation. Errors: NULLPTR, PARAM_INVALID. */
+mhc_status mhc_pre_backward_workspace_size(const mhc_pre_bwd_params* params, size_t* bytes);
+
+/* The backward, asynchronous on `stream` (a hipStream_t; NULL = default stream).
+ * `workspace`: device memory of at least mhc_pre_backward_workspace_size bytes, 256-byte
+ * aligned. Every cross-token sum runs in a fixed order, so results are bitwise
+ * reproducible for the same inputs. With T == 0, gradPhi, gradAlpha, gradBias and
+ * gradGamma are set to zero. Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
+mhc_status mhc_pre_backward(const mhc_pre_bwd_params* params, const mhc_pre_bwd_tensors* tensors,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

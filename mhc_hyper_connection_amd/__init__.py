@@ -15,12 +15,13 @@ from __future__ import annotations
 import math
 
 from ._binding import (FORWARD_EVENTS, MHC_ERR_NULLPTR, MHC_ERR_PARAM_INVALID,
-                       MHC_ERR_RUNTIME, MHC_OK, STAGES, MhcError, Params, load, make_params,
-                       packed_size, raw_forward, raw_forward_timed, raw_prepack,
-                       status_string, version, workspace_size)
+                       MHC_ERR_RUNTIME, MHC_OK, STAGES, MhcError, Params, bwd_workspace_size,
+                       load, make_bwd_params, make_params, packed_size, raw_backward,
+                       raw_forward, raw_forward_timed, raw_prepack, status_string, version,
+                       workspace_size)
 
-__all__ = ["PreForward", "mhc_pre", "prepack", "version", "status_string", "MhcError",
-           "FORWARD_EVENTS", "STAGES",
+__all__ = ["PreForward", "PreBackward", "mhc_pre", "mhc_pre_backward", "prepack", "version",
+           "status_string", "MhcError", "FORWARD_EVENTS", "STAGES",
            "make_params", "packed_size", "workspace_size", "load",
            "MHC_OK", "MHC_ERR_NULLPTR", "MHC_ERR_PARAM_INVALID", "MHC_ERR_RUNTIME"]
 
@@ -193,3 +194,83 @@ def mhc_pre(x, phi, alpha, bias, gamma=None, pre_mix=None, *, num_iters=20, norm
         else:
             extras[k] = v.reshape(*lead, v.shape[-1])
     return h_in, h_post, h_res, extras
+
+
+class PreBackward:
+    """Launcher of the MhcPre backward for one problem size (MhcPreBackward guide,
+    0539edu.com/news/4871844, section 3). Owns its workspace; calls through one instance
+    must not overlap."""
+
+    def __init__(self, T, n, D, *, hc_eps=1e-6, device="cuda"):
+        torch = _torch()
+        load()
+        self.T, self.n, self.D = int(T), int(n), int(D)
+        self.M = n * n + 2 * n
+        self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.params = make_bwd_params(T, n, D, hc_eps)
+        self.ws_bytes = bwd_workspace_size(self.params)
+        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+
+    def alloc_outputs(self, gamma=False):
+        torch = _torch()
+        T, n, D, M, dev = self.T, self.n, self.D, self.M, self.device
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = {"grad_x": torch.empty((T, n, D), dtype=torch.bfloat16, device=dev),
+               "grad_phi": torch.empty((M, n * D), **f32), "grad_alpha": torch.empty((3,), **f32),
+               "grad_bias": torch.empty((M,), **f32)}
+        if gamma:
+            out["grad_gamma"] = torch.empty((n, D), **f32)
+        return out
+
+    def __call__(self, x, phi, alpha, grad_h_in, grad_h_post, grad_h_res, inv_rms, h_mix, h_pre,
+                 h_post, gamma=None, grad_x_post=None, *, out=None):
+        torch = _torch()
+        T, n, D, M, dev = self.T, self.n, self.D, self.M, self.device
+        bf, f32 = torch.bfloat16, torch.float32
+        for t, name, dt, shape in ((x, "x", bf, (T, n, D)), (phi, "phi", f32, (M, n * D)),
+                                   (alpha, "alpha", f32, (3,)), (grad_h_in, "grad_h_in", bf, (T, D)),
+                                   (grad_h_post, "grad_h_post", f32, (T, n)),
+                                   (grad_h_res, "grad_h_res", f32, (T, n, n)),
+                                   (inv_rms, "inv_rms", f32, (T,)), (h_mix, "h_mix", f32, (T, M)),
+                                   (h_pre, "h_pre", f32, (T, n)), (h_post, "h_post", f32, (T, n)),
+                                   (gamma, "gamma", f32, (n, D)),
+                                   (grad_x_post, "grad_x_post", bf, (T, n, D))):
+            _check(t, name, dt, shape, dev)
+        if out is None:
+            out = self.alloc_outputs(gamma is not None)
+        ptrs = {"x": _ptr(x), "phi": _ptr(phi), "alpha": _ptr(alpha), "grad_h_in": _ptr(grad_h_in),
+                "grad_h_post": _ptr(grad_h_post), "grad_h_res": _ptr(grad_h_res),
+                "inv_rms": _ptr(inv_rms), "h_mix": _ptr(h_mix), "h_pre": _ptr(h_pre),
+                "h_post": _ptr(h_post), "gamma": _ptr(gamma), "grad_x_post": _ptr(grad_x_post)}
+        for k, v in out.items():
+            ptrs[k] = _ptr(v)
+        st = raw_backward(self.params, ptrs, _ptr(self.workspace), self.ws_bytes, _stream(dev))
+        if st != MHC_OK:
+            raise MhcError(st, "mhc_pre_backward")
+        return out
+
+
+_BWD_RUNNERS: dict = {}
+
+
+def mhc_pre_backward(x, phi, alpha, grad_h_in, grad_h_post, grad_h_res, inv_rms, h_mix, h_pre,
+                     h_post, gamma=None, grad_x_post=None, *, hc_eps=1e-6):
+    """MhcPre backward. x: bf16 [T, n, D] or [B, S, n, D]; the other per-token tensors
+    follow x's leading dimensions. Returns dict grad_x, grad_phi, grad_alpha, grad_bias
+    (and grad_gamma when gamma is given)."""
+    lead = tuple(x.shape[:-2])
+    n, D = int(x.shape[-2]), int(x.shape[-1])
+    T = math.prod(lead) if lead else 1
+    key = (T, n, D, hc_eps, str(x.device))
+    r = _BWD_RUNNERS.get(key)
+    if r is None:
+        r = _BWD_RUNNERS[key] = PreBackward(T, n, D, hc_eps=hc_eps, device=x.device)
+    M = n * n + 2 * n
+    rs = lambda t, *shape: None if t is None else t.reshape(*shape)
+    out = r(x.reshape(T, n, D), phi, alpha, rs(grad_h_in, T, D), rs(grad_h_post, T, n),
+            rs(grad_h_res, T, n, n), rs(inv_rms, T), rs(h_mix, T, M), rs(h_pre, T, n),
+            rs(h_post, T, n), gamma, rs(grad_x_post, T, n, D))
+    out["grad_x"] = out["grad_x"].reshape(*lead, n, D)
+    return out

@@ -39,9 +39,24 @@ class Tensors(ctypes.Structure):
     _fields_ = [(f, ctypes.c_void_p) for f in TENSOR_FIELDS]
 
 
+class BwdParams(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("hc_eps", ctypes.c_double), ("reserved", ctypes.c_int32),
+                ("reserved2", ctypes.c_int32)]
+
+
+BWD_TENSOR_FIELDS = ("x", "phi", "alpha", "grad_h_in", "grad_h_post", "grad_h_res", "inv_rms",
+                     "h_mix", "h_pre", "h_post", "gamma", "grad_x_post", "grad_x", "grad_phi",
+                     "grad_alpha", "grad_bias", "grad_gamma")
+
+
+class BwdTensors(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in BWD_TENSOR_FIELDS]
+
+
 EXPORTS = ("mhc_version", "mhc_status_string", "mhc_pre_packed_size",
            "mhc_pre_workspace_size", "mhc_pre_prepack", "mhc_pre_forward",
-           "mhc_pre_forward_timed")
+           "mhc_pre_forward_timed", "mhc_pre_backward_workspace_size", "mhc_pre_backward")
 
 # MHC_FORWARD_EVENTS: events of mhc_pre_forward_timed (before the first kernel, then one
 # after each of pack, projection, epilogue, hIn)
@@ -79,6 +94,11 @@ def load(path: str | None = None):
     lib.mhc_pre_forward_timed.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Tensors),
                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                           ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
+    lib.mhc_pre_backward_workspace_size.restype = ctypes.c_int32
+    lib.mhc_pre_backward_workspace_size.argtypes = [ctypes.POINTER(BwdParams), ctypes.POINTER(ctypes.c_size_t)]
+    lib.mhc_pre_backward.restype = ctypes.c_int32
+    lib.mhc_pre_backward.argtypes = [ctypes.POINTER(BwdParams), ctypes.POINTER(BwdTensors),
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     if path is None:
         _lib = lib
     return lib
@@ -130,3 +150,20 @@ def raw_forward_timed(params: Params, ptrs: dict, ws_ptr, ws_bytes, stream, even
     arr = (ctypes.c_void_p * max(len(events), 1))(*events)
     return int(load().mhc_pre_forward_timed(ctypes.byref(params), ctypes.byref(t), ws_ptr, ws_bytes,
                                             stream, arr, len(events)))
+
+
+def make_bwd_params(T, n, D, hc_eps=1e-6) -> BwdParams:
+    return BwdParams(int(T), int(n), int(D), float(hc_eps), 0, 0)
+
+
+def bwd_workspace_size(params: BwdParams) -> int:
+    out = ctypes.c_size_t(0)
+    st = load().mhc_pre_backward_workspace_size(ctypes.byref(params), ctypes.byref(out))
+    if st != MHC_OK:
+        raise MhcError(st, "mhc_pre_backward_workspace_size")
+    return int(out.value)
+
+
+def raw_backward(params: BwdParams, ptrs: dict, ws_ptr, ws_bytes, stream) -> int:
+    t = BwdTensors(*[ptrs.get(f) for f in BWD_TENSOR_FIELDS])
+    return int(load().mhc_pre_backward(ctypes.byref(params), ctypes.byref(t), ws_ptr, ws_bytes, stream))

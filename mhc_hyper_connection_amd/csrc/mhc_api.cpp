@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "../../include/mhc.h"
+#include "mhc_bwd_plan.h"
 #include "mhc_plan.h"
 
 namespace {
@@ -188,6 +189,84 @@ mhc_status mhc_pre_forward_timed(const mhc_pre_params* params, const mhc_pre_ten
         if (!events[i]) return MHC_ERR_NULLPTR;
     if (num_events != MHC_FORWARD_EVENTS) return MHC_ERR_PARAM_INVALID;
     return forward_impl(params, t, workspace, workspace_bytes, stream, events);
+}
+
+}  // extern "C"
+
+namespace {
+
+mhc_status check_bwd_params(const mhc_pre_bwd_params* p, mhc::bwd::Geometry* g)
+{
+    if (!p) return MHC_ERR_NULLPTR;
+    if (p->reserved != 0 || p->reserved2 != 0) return MHC_ERR_PARAM_INVALID;
+    if (!(p->hc_eps >= 0.0)) return MHC_ERR_PARAM_INVALID;    // also rejects NaN
+    if (p->T < 0) return MHC_ERR_PARAM_INVALID;
+    if (!mhc::bwd::make_geometry(p->n, p->D, g)) return MHC_ERR_PARAM_INVALID;
+    return MHC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mhc_status mhc_pre_backward_workspace_size(const mhc_pre_bwd_params* params, size_t* bytes)
+{
+    if (!params || !bytes) return MHC_ERR_NULLPTR;
+    mhc::bwd::Geometry g;
+    mhc_status st = check_bwd_params(params, &g);
+    if (st != MHC_OK) return st;
+    *bytes = mhc::bwd::make_plan(g, params->T).ws_bytes;
+    return MHC_OK;
+}
+
+mhc_status mhc_pre_backward(const mhc_pre_bwd_params* params, const mhc_pre_bwd_tensors* t,
+                            void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!params || !t) return MHC_ERR_NULLPTR;
+    mhc::bwd::Geometry g;
+    mhc_status st = check_bwd_params(params, &g);
+    if (st != MHC_OK) return st;
+    // per-token tensors are empty (and may be NULL) when T == 0
+    const bool tok = params->T > 0;
+    if (!t->phi || !t->alpha || !t->grad_phi || !t->grad_alpha || !t->grad_bias || !workspace)
+        return MHC_ERR_NULLPTR;
+    if (tok && (!t->x || !t->grad_h_in || !t->grad_h_post || !t->grad_h_res || !t->inv_rms ||
+                !t->h_mix || !t->h_pre || !t->h_post || !t->grad_x))
+        return MHC_ERR_NULLPTR;
+    if (t->gamma && !t->grad_gamma) return MHC_ERR_NULLPTR;
+    const mhc::bwd::Plan plan = mhc::bwd::make_plan(g, params->T);
+    if (workspace_bytes < plan.ws_bytes) return MHC_ERR_PARAM_INVALID;
+    if (!aligned(t->x, 16) || !aligned(t->grad_h_in, 16) || !aligned(t->grad_x, 16) ||
+        (t->grad_x_post && !aligned(t->grad_x_post, 16)) || !aligned(workspace, 256))
+        return MHC_ERR_PARAM_INVALID;
+
+    mhc::bwd::Args a;
+    a.x = t->x;
+    a.phi = t->phi;
+    a.alpha = t->alpha;
+    a.grad_h_in = t->grad_h_in;
+    a.grad_h_post = t->grad_h_post;
+    a.grad_h_res = t->grad_h_res;
+    a.inv_rms = t->inv_rms;
+    a.h_mix = t->h_mix;
+    a.h_pre = t->h_pre;
+    a.h_post = t->h_post;
+    a.gamma = t->gamma;
+    a.grad_x_post = t->grad_x_post;
+    a.grad_x = t->grad_x;
+    a.grad_phi = t->grad_phi;
+    a.grad_alpha = t->grad_alpha;
+    a.grad_bias = t->grad_bias;
+    a.grad_gamma = t->gamma ? t->grad_gamma : nullptr;
+    a.hc_eps = params->hc_eps;
+    char* ws = static_cast<char*>(workspace);
+    a.pack = ws + plan.off_pack;
+    a.gmix = reinterpret_cast<float*>(ws + plan.off_gmix);
+    a.c3 = reinterpret_cast<float*>(ws + plan.off_c3);
+    a.terms = reinterpret_cast<double*>(ws + plan.off_terms);
+    a.pphi = reinterpret_cast<float*>(ws + plan.off_pphi);
+    a.pgam = reinterpret_cast<float*>(ws + plan.off_pgam);
+    return mhc::bwd::launch_backward(plan, a, stream) == 0 ? MHC_OK : MHC_ERR_RUNTIME;
 }
 
 }  // extern "C"

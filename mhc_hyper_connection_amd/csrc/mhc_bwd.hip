@@ -1,0 +1,515 @@
+// mhc_bwd.hip -- gfx950 kernels of the MhcPre backward.
+//
+// Method (MhcPreBackward guide, 0539edu.com/news/4871844, section 3; forward in the
+// aclnnMhcPreV2 guide, kwkr.cn/news/422178, section 3). Per token t, with the forward's
+// saved invRms, hMix, hPre, hPost:
+//   gHPre_i  = sum_d gradHIn[d] x[i, d]                                      (3.1)
+//   gW       = [ gHPre s(1-s) alpha0 | gradHPost hPost(1-hPost/2) alpha1 |
+//                gradHRes alpha2 ],  s = hPre - hcEps                        (3.2-3.4)
+//   gMix     = gW invRms,  gInv = gW . hMix                                  (3.5)
+//   xrsGrad  = gMix . phi                                                    (3.6)
+//   gradX    = gradHIn hPre_i + xrsGrad gamma - gInv invRms^3 x / (n D)
+//              (+ gradXPost)                                                 (3.7, 3.8)
+// and over tokens: gradPhi = gamma (.) sum_t gMix^T x, gradGamma = sum_t x xrsGrad,
+// gradAlpha / gradBias = sums of the gate terms.
+//
+// Kernels, in launch order on the caller's stream:
+//   bwd_pack_kernel     phi -> three bf16 terms, ordered as the A operand of xrsGrad^T
+//                       = phi^T . gMix^T per (d-block, stream, half, K-step, term)
+//   bwd_token_kernel    one wave per token: the hPre gradient in fp64, the gate backward,
+//                       gMix, c3 = gInv invRms^3 / (n D), and the token's alpha/bias terms
+//   bwd_main_kernel     one workgroup per (token group, d-block, stream group): per tile
+//                       of 64 tokens, xrsGrad on the matrix cores (phi terms x gMix terms,
+//                       six products), gradX, the gradGamma sums, and gMix^T . x on the
+//                       matrix cores with x transposed through LDS; group sums to partials
+//   bwd_reduce_*        fixed-order fp64 sums of the partials (gradPhi, gradGamma) and
+//                       of the per-token terms (gradAlpha, gradBias)
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "mhc_bwd_plan.h"
+#include "mhc_device.h"
+
+namespace mhc {
+namespace bwd {
+namespace {
+
+// fp32 -> three bf16 terms whose sum is the value: hi = RNE(v), mid = RNE(v - hi),
+// lo = RNE(v - hi - mid). Both differences are exact in fp32 (each removes the leading
+// 8 significant bits), and lo holds the last 8.
+struct Split3 {
+    uint32_t t[3];
+};
+__device__ __forceinline__ Split3 split3(float v)
+{
+    Split3 s;
+    s.t[0] = f32_to_bf16_bits(v);
+    const float r1 = v - __uint_as_float(s.t[0] << 16);
+    s.t[1] = f32_to_bf16_bits(r1);
+    const float r2 = r1 - __uint_as_float(s.t[1] << 16);
+    s.t[2] = f32_to_bf16_bits(r2);
+    return s;
+}
+// Eight floats -> the three bf16x8 term vectors.
+__device__ __forceinline__ void split8(const float (&v)[8], bf16x8 (&out)[3])
+{
+    u32x4 w[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const Split3 s = split3(v[e]);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) w[p][e >> 1] |= s.t[p] << (16 * (e & 1));
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) out[p] = __builtin_bit_cast(bf16x8, w[p]);
+}
+
+// ------------------------------------------------------------------ weight pack
+
+// Unit u = (((((b * n + i) * 2 + h) * KS + ks) * 3 + p) * 64 + lane holds, for lane
+// (row = lane % 16, g = lane / 16), term p of phi[m][i D + d] for m = 32 ks + 8 g + e,
+// e = 0..7, at d = 32 b + pack_col(h, row); zero past M or D.
+__global__ void __launch_bounds__(256)
+bwd_pack_kernel(const float* __restrict__ phi, u32x4* __restrict__ pack, int n, int D, int M, int KS,
+                int64_t total)
+{
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= total) return;
+    const int lane = (int)(u % 64);
+    int64_t r = u / 64;
+    const int p = (int)(r % 3);
+    r /= 3;
+    const int ks = (int)(r % KS);
+    r /= KS;
+    const int h = (int)(r % 2);
+    r /= 2;
+    const int i = (int)(r % n);
+    const int b = (int)(r / n);
+    const int row = lane % 16, g = lane / 16;
+    const int d = kDBlock * b + pack_col(h, row);
+    const int64_t K = (int64_t)n * D;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (d < D) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int m = 32 * ks + 8 * g + e;
+            if (m < M) w[e >> 1] |= split3(phi[(int64_t)m * K + (int64_t)i * D + d]).t[p] << (16 * (e & 1));
+        }
+    }
+    pack[u] = w;
+}
+
+// ------------------------------------------------------------------ token pass
+
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// One wave per token (4 per workgroup). Outputs: gMix [T][MP] (f32, zero past M),
+// c3 [T], terms [T][3 + M] (fp64: the token's alpha terms, then its bias terms).
+template <int N>
+__global__ void __launch_bounds__(256)
+bwd_token_kernel(Args a, int64_t T, int D)
+{
+    constexpr int M = N * N + 2 * N;
+    constexpr int MP = 32 * ((M + 31) / 32);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const int64_t K = (int64_t)N * D;
+
+    // 3.1: gHPre_i = sum_d gradHIn[d] x[i, d]; a bf16 x bf16 product is exact in fp32,
+    // the sums run in fp64 (per lane, then across lanes)
+    double acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.0;
+    const uint16_t* xt = a.x + t * K;
+    const uint16_t* gt = a.grad_h_in + t * D;
+    for (int o = lane; o < D / 8; o += 64) {
+        const u32x4 gh = *reinterpret_cast<const u32x4*>(gt + 8 * o);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(xt + (int64_t)i * D + 8 * o);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[i] += (double)(bf16_lo(gh[e]) * bf16_lo(xv[e]));
+                acc[i] += (double)(bf16_hi(gh[e]) * bf16_hi(xv[e]));
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = wave_sum(acc[i]);
+
+    // 3.2-3.5, one lane per phi row m (two passes when MP > 64)
+    const double eps = a.hc_eps;
+    const double inv = (double)a.inv_rms[t];
+    const double a0 = a.alpha[0], a1 = a.alpha[1], a2 = a.alpha[2];
+    double gi = 0.0, ta0 = 0.0, ta1 = 0.0, ta2 = 0.0;
+    for (int m = lane; m < MP; m += 64) {
+        double gw = 0.0;
+        if (m < M) {
+            const double w = (double)a.h_mix[t * M + m] * inv;   // the gate input
+            double tb;
+            if (m < N) {
+                double ghp = 0.0;
+#pragma unroll
+                for (int i = 0; i < N; ++i) ghp = i == m ? acc[i] : ghp;
+                const double s = (double)a.h_pre[t * N + m] - eps;
+                tb = ghp * s * (1.0 - s);
+                gw = tb * a0;
+                ta0 += tb * w;
+            } else if (m < 2 * N) {
+                const double hq = a.h_post[t * N + (m - N)];
+                tb = (double)a.grad_h_post[t * N + (m - N)] * hq * (1.0 - hq / 2.0);
+                gw = tb * a1;
+                ta1 += tb * w;
+            } else {
+                tb = a.grad_h_res[t * N * N + (m - 2 * N)];
+                gw = tb * a2;
+                ta2 += tb * w;
+            }
+            gi += gw * (double)a.h_mix[t * M + m];
+            a.terms[t * (3 + M) + 3 + m] = tb;
+        }
+        a.gmix[t * MP + m] = (float)(gw * inv);
+    }
+    gi = wave_sum(gi);
+    ta0 = wave_sum(ta0);
+    ta1 = wave_sum(ta1);
+    ta2 = wave_sum(ta2);
+    if (lane == 0) {
+        a.c3[t] = (float)(gi * inv * inv * inv / (double)K);
+        a.terms[t * (3 + M) + 0] = ta0;
+        a.terms[t * (3 + M) + 1] = ta1;
+        a.terms[t * (3 + M) + 2] = ta2;
+    }
+}
+
+// ------------------------------------------------------------------ main pass
+
+// Products of A terms (phi) and B terms (gMix) kept for xrsGrad, smallest first: every
+// pair (p, q) with p + q <= 2, i.e. down to 2^-16 of the leading product; the dropped
+// pairs are below 2^-24 of it.
+constexpr int kPairs = 6;
+constexpr int pair_a(int q) { return q == 0 ? 2 : (q == 1 ? 0 : (q == 2 ? 1 : (q == 3 ? 1 : 0))); }
+constexpr int pair_b(int q) { return q == 0 ? 0 : (q == 1 ? 2 : (q == 2 ? 1 : (q == 3 ? 0 : (q == 4 ? 1 : 0)))); }
+
+template <int N, int SGN, int KS>
+struct MainCfg {
+    static constexpr int M = N * N + 2 * N;
+    static constexpr int MP = 32 * KS;
+    static constexpr int NCOL = kDBlock * SGN;           // local columns of a workgroup
+    static constexpr int RB = MP / 16;                    // gradPhi row blocks
+    static constexpr int CB = NCOL / 16;                  // gradPhi column blocks
+    static constexpr int BPW = RB * CB / 4;               // gradPhi blocks per wave
+    static constexpr int PACK_U = SGN * 2 * KS * 3 * 64;  // 16-byte units of packed phi
+    static constexpr int XS = kTile + 8;                  // bf16 per transposed-x row
+    static constexpr int GS = kTile + 4;                  // floats per transposed-gMix row
+    static constexpr int PACK_BYTES = PACK_U * 16;
+    static constexpr int XT_BYTES = NCOL * XS * 2;
+    static constexpr int GT_BYTES = MP * GS * 4;
+    static constexpr int RED_BYTES = kTile * NCOL * 4;    // gradGamma reduction at the end
+    static constexpr int MAIN_BYTES = PACK_BYTES + XT_BYTES + GT_BYTES;
+    static constexpr int LDS_BYTES = MAIN_BYTES > RED_BYTES ? MAIN_BYTES : RED_BYTES;
+    static_assert((RB * CB) % 4 == 0, "gradPhi blocks divide among the four waves");
+    static_assert(XT_BYTES % 16 == 0 && PACK_BYTES % 16 == 0, "LDS regions stay 16-byte aligned");
+};
+
+template <int N, int SGN, int KS>
+__global__ void __launch_bounds__(kThreads, 2)
+bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles)
+{
+    using C = MainCfg<N, SGN, KS>;
+    constexpr int M = C::M, MP = C::MP, NCOL = C::NCOL, CB = C::CB, BPW = C::BPW;
+    constexpr int XS = C::XS, GS = C::GS;
+    constexpr int NSG = N / SGN;
+    __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
+    u32x4* sp = reinterpret_cast<u32x4*>(lds);
+    uint16_t* xT = reinterpret_cast<uint16_t*>(lds + C::PACK_BYTES);
+    float* gT = reinterpret_cast<float*>(lds + C::PACK_BYTES + C::XT_BYTES);
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int j = lane & 15, grp = lane >> 4;
+    int64_t g;
+    int b, sg;
+    main_task(blockIdx.x, nblk, NSG, &g, &b, &sg);
+    const int64_t K = (int64_t)N * D;
+    const int d0 = kDBlock * b + 8 * grp;          // the lane's 8 positions d0 .. d0+7
+    const bool dval = d0 < D;                        // D % 8 == 0: all 8 or none
+
+    // the workgroup's packed phi (its d-block, its streams) into LDS
+    {
+        const u32x4* src = static_cast<const u32x4*>(a.pack) + pack_at(b, sg * SGN, N, KS);
+        for (int u = tid; u < C::PACK_U; u += kThreads) sp[u] = src[u];
+    }
+    float gam[SGN][8];
+#pragma unroll
+    for (int s = 0; s < SGN; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            gam[s][e] = (a.gamma && dval) ? a.gamma[(int64_t)(sg * SGN + s) * D + d0 + e] : 1.f;
+
+    float gg[SGN][8];
+#pragma unroll
+    for (int s = 0; s < SGN; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gg[s][e] = 0.f;
+    f32x4 pacc[BPW];
+#pragma unroll
+    for (int q = 0; q < BPW; ++q) pacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+
+    const int64_t tile_end = (g + 1) * tpg < tiles ? (g + 1) * tpg : tiles;
+    for (int64_t tile = g * tpg; tile < tile_end; ++tile) {
+        const int64_t t0 = tile * kTile;
+        const int ntile = (int)(T - t0 < kTile ? T - t0 : kTile);
+        const int row = 16 * wave + j;               // the lane's token in the tile
+        const int64_t tok = t0 + row;
+        const bool tval = row < ntile;
+
+        // loads (rows past the tile and positions past D read as zero)
+        const rsrc_t rx = make_rsrc(a.x + t0 * K, (int64_t)ntile * K * 2);
+        const rsrc_t rgh = make_rsrc(a.grad_h_in + t0 * D, (int64_t)ntile * D * 2);
+        const rsrc_t rgm = make_rsrc(a.gmix + t0 * MP, (int64_t)ntile * MP * 4);
+        u32x4 xv[SGN], xp[SGN];
+#pragma unroll
+        for (int s = 0; s < SGN; ++s) {
+            const uint32_t off = dval ? (uint32_t)(((int64_t)row * K + (int64_t)(sg * SGN + s) * D + d0) * 2) : kOutOfRange;
+            xv[s] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+        }
+        if (a.grad_x_post) {
+            const rsrc_t rxp = make_rsrc(a.grad_x_post + t0 * K, (int64_t)ntile * K * 2);
+#pragma unroll
+            for (int s = 0; s < SGN; ++s) {
+                const uint32_t off = dval ? (uint32_t)(((int64_t)row * K + (int64_t)(sg * SGN + s) * D + d0) * 2) : kOutOfRange;
+                xp[s] = __builtin_amdgcn_raw_buffer_load_b128(rxp, (int)off, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < SGN; ++s) xp[s] = u32x4{0u, 0u, 0u, 0u};
+        }
+        const u32x4 gh = __builtin_amdgcn_raw_buffer_load_b128(
+            rgh, dval ? (int)(((int64_t)row * D + d0) * 2) : (int)kOutOfRange, 0, 0);
+        float gm[KS][8];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+                    rgm, (int)(((int64_t)row * MP + 32 * ks + 8 * grp + 4 * hh) * 4), 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gm[ks][4 * hh + e] = __uint_as_float(v[e]);
+            }
+        }
+        float hp[SGN];
+#pragma unroll
+        for (int s = 0; s < SGN; ++s) hp[s] = tval ? a.h_pre[tok * N + sg * SGN + s] : 0.f;
+        const float c3 = tval ? a.c3[tok] : 0.f;
+
+        // xrsGrad^T = phi^T . gMix^T: A = packed phi (columns as rows), B = gMix (tokens)
+        bf16x8 bt[KS][3];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) split8(gm[ks], bt[ks]);
+        const rsrc_t rgx = make_rsrc(a.grad_x + t0 * K, (int64_t)ntile * K * 2);
+#pragma unroll
+        for (int s = 0; s < SGN; ++s) {
+            float xg[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int q = 0; q < kPairs; ++q) {
+                        const bf16x8 av = __builtin_bit_cast(
+                            bf16x8, sp[(((s * 2 + h) * KS + ks) * 3 + pair_a(q)) * 64 + lane]);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bt[ks][pair_b(q)], acc, 0, 0, 0);
+                    }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xg[4 * h + r] = acc[r];
+            }
+            // gradX = gradHIn hPre + xrsGrad gamma - c3 x (+ gradXPost), one RNE to bf16
+            u32x4 o;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                uint32_t bits[2];
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl) {
+                    const int e = 2 * e2 + hl;
+                    const float xe = hl ? bf16_hi(xv[s][e2]) : bf16_lo(xv[s][e2]);
+                    const float ge = hl ? bf16_hi(gh[e2]) : bf16_lo(gh[e2]);
+                    const float pe = hl ? bf16_hi(xp[s][e2]) : bf16_lo(xp[s][e2]);
+                    float v = fmaf(ge, hp[s], xg[e] * gam[s][e]);
+                    v = fmaf(-c3, xe, v) + pe;
+                    bits[hl] = f32_to_bf16_bits(v);
+                    gg[s][e] = fmaf(xe, xg[e], gg[s][e]);
+                }
+                o[e2] = bits[0] | (bits[1] << 16);
+            }
+            const uint32_t off = dval ? (uint32_t)(((int64_t)row * K + (int64_t)(sg * SGN + s) * D + d0) * 2) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(o, rgx, (int)off, 0, 0);
+            // x of this tile, transposed: xT[local column][token]
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                xT[(s * kDBlock + 8 * grp + e) * XS + row] = (uint16_t)((xv[s][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        }
+        // gMix of this tile, transposed: gT[m][token]
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gT[(32 * ks + 8 * grp + e) * GS + row] = gm[ks][e];
+        __syncthreads();
+
+        // gradPhi partial: C[m][col] += sum over the tile's tokens of gMix[t][m] x[t][col];
+        // A = gMix^T (rows m, three terms), B = x (columns), 32 tokens per K-step
+#pragma unroll
+        for (int q = 0; q < BPW; ++q) {
+            const int bi = wave + 4 * q;
+            const int rb = bi / CB, cb = bi % CB;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                float av[8];
+                const float* gsrc = gT + (16 * rb + j) * GS + 32 * kt + 8 * grp;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) av[e] = gsrc[e];
+                bf16x8 at[3];
+                split8(av, at);
+                const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xT + (16 * cb + j) * XS + 32 * kt + 8 * grp);
+#pragma unroll
+                for (int p = 2; p >= 0; --p)
+                    pacc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at[p], bv, pacc[q], 0, 0, 0);
+            }
+        }
+        __syncthreads();   // xT and gT are rewritten by the next tile
+    }
+
+    // gradPhi partial of the group: P[g][m][k], k = stream * D + d
+    float* const P = a.pphi + g * (int64_t)M * K;
+#pragma unroll
+    for (int q = 0; q < BPW; ++q) {
+        const int bi = wave + 4 * q;
+        const int rb = bi / CB, cb = bi % CB;
+        const int col = 16 * cb + j;                 // local column
+        const int s = col / kDBlock, dd = kDBlock * b + col % kDBlock;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 16 * rb + 4 * grp + r;
+            if (m < M && dd < D) P[(int64_t)m * K + (int64_t)(sg * SGN + s) * D + dd] = pacc[q][r];
+        }
+    }
+    // gradGamma partial of the group: sum the 64 token lanes of each column in a fixed order
+    if (a.gamma) {
+        float* red = reinterpret_cast<float*>(lds);   // [64 token lanes][NCOL]
+#pragma unroll
+        for (int s = 0; s < SGN; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[(16 * wave + j) * NCOL + s * kDBlock + 8 * grp + e] = gg[s][e];
+        __syncthreads();
+        for (int col = tid; col < NCOL; col += kThreads) {
+            float v = 0.f;
+            for (int rr = 0; rr < kTile; ++rr) v += red[rr * NCOL + col];
+            const int s = col / kDBlock, dd = kDBlock * b + col % kDBlock;
+            if (dd < D) a.pgam[g * K + (int64_t)(sg * SGN + s) * D + dd] = v;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ reductions
+
+// gradPhi[m][k] = gamma[k] * sum_g P[g][m][k]; gradGamma[k] = sum_g Q[g][k] (fp64, g order)
+__global__ void __launch_bounds__(256)
+bwd_reduce_cols_kernel(Args a, int64_t MK, int64_t K, int64_t G)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx < MK) {
+        double s = 0.0;
+        for (int64_t gg = 0; gg < G; ++gg) s += (double)a.pphi[gg * MK + idx];
+        if (a.gamma) s *= (double)a.gamma[idx % K];
+        a.grad_phi[idx] = (float)s;
+    } else if (idx < MK + K && a.gamma) {
+        const int64_t k = idx - MK;
+        double s = 0.0;
+        for (int64_t gg = 0; gg < G; ++gg) s += (double)a.pgam[gg * K + k];
+        a.grad_gamma[k] = (float)s;
+    }
+}
+
+// Workgroup c sums column c of terms [T][3 + M] over the tokens: thread-strided fp64
+// sums, then a fixed tree. c < 3: gradAlpha[c]; else gradBias[c - 3].
+__global__ void __launch_bounds__(256)
+bwd_reduce_terms_kernel(Args a, int64_t T, int M)
+{
+    __shared__ double part[256];
+    const int c = blockIdx.x, tid = threadIdx.x;
+    double s = 0.0;
+    for (int64_t t = tid; t < T; t += 256) s += a.terms[t * (3 + M) + c];
+    part[tid] = s;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if (tid < w) part[tid] += part[tid + w];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        if (c < 3) a.grad_alpha[c] = (float)part[0];
+        else a.grad_bias[c - 3] = (float)part[0];
+    }
+}
+
+// T == 0: every cross-token gradient is an empty sum.
+__global__ void __launch_bounds__(256)
+bwd_zero_kernel(Args a, int64_t MK, int64_t K, int M)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx < MK) a.grad_phi[idx] = 0.f;
+    if (idx < K && a.gamma) a.grad_gamma[idx] = 0.f;
+    if (idx < 3) a.grad_alpha[idx] = 0.f;
+    if (idx < M) a.grad_bias[idx] = 0.f;
+}
+
+template <int N, int SGN, int KS>
+hipError_t launch_all(const Plan& p, const Args& a, hipStream_t st)
+{
+    const Geometry& g = p.g;
+    const int64_t units = (int64_t)g.nblk * g.n * pack_units_per_stream(g.KS);
+    hipLaunchKernelGGL(bwd_pack_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, a.phi,
+                       static_cast<u32x4*>(a.pack), g.n, g.D, g.M, g.KS, units);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_token_kernel<N>, dim3((unsigned)p.token_blocks), dim3(256), 0, st, a, p.T, g.D);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_main_kernel<N, SGN, KS>), dim3((unsigned)p.main_blocks), dim3(kThreads), 0, st, a,
+                       p.T, g.D, g.nblk, p.tpg, p.tiles);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t MK = (int64_t)g.M * g.K;
+    hipLaunchKernelGGL(bwd_reduce_cols_kernel, dim3((unsigned)((MK + g.K + 255) / 256)), dim3(256), 0, st, a,
+                       MK, g.K, p.G);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_reduce_terms_kernel, dim3((unsigned)(3 + g.M)), dim3(256), 0, st, a, p.T, g.M);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_backward(const Plan& p, const Args& a, void* stream)
+{
+    hipStream_t st = (hipStream_t)stream;
+    const Geometry& g = p.g;
+    if (p.T == 0) {
+        const int64_t MK = (int64_t)g.M * g.K;
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((MK + 255) / 256)), dim3(256), 0, st, a, MK, g.K, g.M);
+        return (int)hipGetLastError();
+    }
+    if (g.n == 4 && g.SGN == 4 && g.KS == 1) return (int)launch_all<4, 4, 1>(p, a, st);
+    if (g.n == 8 && g.SGN == 2 && g.KS == 3) return (int)launch_all<8, 2, 3>(p, a, st);
+    return (int)hipErrorInvalidValue;
+}
+
+}  // namespace bwd
+}  // namespace mhc

@@ -16,6 +16,22 @@ order, each in C order:
   bias    [M]        float32 N(0, 0.1)               (0.1 is the standard deviation)
   pre_mix [T, n]     float32 U(0, 1)                 (only when the workload has pre_mix)
 with M = n*n + 2n for a 3-entry alpha and 2n for a 2-entry alpha.
+
+MhcPre backward inputs (``backward_inputs``; M = n*n + 2n), drawn in this order:
+  x            [T, n, D]  N(0, 1) -> bf16 (chunked as above)
+  phi          [M, n*D]   N(0, 1) / sqrt(n*D)
+  alpha        [3]        U(0.5, 1.5)
+  grad_h_in    [T, D]     N(0, 1) -> bf16
+  grad_h_post  [T, n]     N(0, 1)
+  grad_h_res   [T, n, n]  N(0, 1)
+  inv_rms      [T]        U(0.5, 1.5)
+  h_mix        [T, M]     N(0, 1)
+  h_pre        [T, n]     U(0, 1) + 1e-6   (the range of sigmoid + hcEps)
+  h_post       [T, n]     U(0, 2)          (the range of 2 sigmoid)
+  gamma        [n, D]     U(0.5, 1.5)      (when asked for)
+  grad_x_post  [T, n, D]  N(0, 1) -> bf16  (when asked for)
+The saved forward values are drawn independently, in the ranges the forward produces:
+the backward is a function of all of them, whatever forward they came from.
 """
 from __future__ import annotations
 
@@ -126,3 +142,55 @@ def custom(T: int, n: int, D: int, *, n_alpha: int = 3, gamma: bool = False,
     wl = Workload(name, T=T, n=n, D=D, n_alpha=n_alpha, gamma=gamma, pre_mix=pre_mix,
                   need_backward=need_backward, num_iters=num_iters, seed=seed)
     return generate(wl)
+
+
+def _bf16_normal(rng, count: int) -> np.ndarray:
+    out = np.empty(count, dtype=np.uint16)
+    for start in range(0, count, X_CHUNK):
+        stop = min(count, start + X_CHUNK)
+        out[start:stop] = f32_to_bf16_bits(rng.standard_normal(stop - start, dtype=np.float32))
+    return out
+
+
+@dataclass
+class BwdInputs:
+    T: int
+    n: int
+    D: int
+    x: np.ndarray              # uint16 bf16 bits [T, n, D]
+    phi: np.ndarray            # float32 [M, n*D]
+    alpha: np.ndarray          # float32 [3]
+    grad_h_in: np.ndarray      # uint16 bf16 bits [T, D]
+    grad_h_post: np.ndarray    # float32 [T, n]
+    grad_h_res: np.ndarray     # float32 [T, n, n]
+    inv_rms: np.ndarray        # float32 [T]
+    h_mix: np.ndarray          # float32 [T, M]
+    h_pre: np.ndarray          # float32 [T, n]
+    h_post: np.ndarray         # float32 [T, n]
+    gamma: np.ndarray | None = None        # float32 [n, D]
+    grad_x_post: np.ndarray | None = None  # uint16 bf16 bits [T, n, D]
+    hc_eps: float = 1e-6
+
+    @property
+    def M(self) -> int:
+        return self.n * self.n + 2 * self.n
+
+
+def backward_inputs(T: int, n: int, D: int, *, gamma: bool = False, x_post: bool = False,
+                    seed: int = 11) -> BwdInputs:
+    """Inputs of the MhcPre backward with the recipe in the module docstring."""
+    rng = np.random.default_rng(seed)
+    M, K = n * n + 2 * n, n * D
+    x = _bf16_normal(rng, T * K).reshape(T, n, D)
+    phi = (rng.standard_normal((M, K), dtype=np.float32) / np.float32(np.sqrt(K))).astype(np.float32)
+    alpha = rng.uniform(0.5, 1.5, size=3).astype(np.float32)
+    ghin = _bf16_normal(rng, T * D).reshape(T, D)
+    ghpost = rng.standard_normal((T, n), dtype=np.float32)
+    ghres = rng.standard_normal((T, n, n), dtype=np.float32)
+    inv = rng.uniform(0.5, 1.5, size=T).astype(np.float32)
+    hmix = rng.standard_normal((T, M), dtype=np.float32)
+    hpre = (rng.uniform(0.0, 1.0, size=(T, n)) + 1e-6).astype(np.float32)
+    hpost = rng.uniform(0.0, 2.0, size=(T, n)).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, size=(n, D)).astype(np.float32) if gamma else None
+    gxp = _bf16_normal(rng, T * K).reshape(T, n, D) if x_post else None
+    return BwdInputs(T, n, D, x, phi, alpha, ghin, ghpost, ghres, inv, hmix, hpre, hpost, g, gxp)

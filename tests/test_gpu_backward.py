@@ -1,0 +1,145 @@
+"""GPU parity of the MhcPre backward: the HIP library (through the C-ABI) against the
+fp64 oracle (oracle/mhc_oracle_bwd.c), on seeded synthetic inputs (synth.backward_inputs).
+
+Acceptance rule, derived from the arithmetic of the GPU path:
+  gradX (bf16), every element: within 1 bf16 ulp of the oracle's correctly rounded value,
+      or |gpu - ref| <= 2^-18 * A, A = the sum of |terms| of the element (the oracle's
+      grad_x_abs). gradX is formed in fp32 from five terms, one of them a split-bf16
+      matrix-core product accurate to ~2^-22 of its terms, so the fp32 error is far below
+      2^-18 A; the branch matters only where the terms cancel.
+  gradPhi, gradGamma (f32), every element: |gpu - ref| <= 2e-4 |ref| + 2^-14 A, A the
+      oracle's sum of |terms|. Each is an fp32 sum over the tokens of one group (up to a
+      few hundred rounding steps into the accumulator, each <= 2^-24 of a partial sum
+      <= A), then an fp64 sum over groups; 2^-14 A leaves a 4x margin over that bound,
+      and 2e-4 |ref| is the forward's relative tolerance.
+  gradAlpha, gradBias (f32): fp64 per-token terms summed in fp64, one rounding to f32:
+      |gpu - ref| <= 1e-6 |ref| + 2^-30 A.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_helpers import bf16_ordered, device, to_dev, to_host
+from synth import bf16_bits_to_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_backward(bi, repeat=1):
+    import mhc_hyper_connection_amd as mhc
+    import torch
+    dev = device()
+    r = mhc.PreBackward(bi.T, bi.n, bi.D, hc_eps=bi.hc_eps, device=dev)
+    args = [to_dev(a, dev) for a in (bi.x, bi.phi, bi.alpha, bi.grad_h_in, bi.grad_h_post,
+                                     bi.grad_h_res, bi.inv_rms, bi.h_mix, bi.h_pre, bi.h_post,
+                                     bi.gamma, bi.grad_x_post)]
+    out = r.alloc_outputs(bi.gamma is not None)
+    results = []
+    for _ in range(repeat):
+        for v in out.values():
+            if v.dtype == torch.bfloat16:
+                v.view(torch.int16).fill_(0x7FC0)   # NaN: anything not written shows
+            else:
+                v.fill_(float("nan"))
+        r(*args, out=out)
+        torch.cuda.synchronize(dev)
+        results.append({k: to_host(v) for k, v in out.items()})
+    return results if repeat > 1 else results[0]
+
+
+def run_oracle(bi, tokens=None):
+    return oracle.backward(bi.x, bi.phi, bi.alpha, bi.grad_h_in, bi.grad_h_post, bi.grad_h_res,
+                           bi.inv_rms, bi.h_mix, bi.h_pre, bi.h_post, bi.gamma, bi.grad_x_post,
+                           hc_eps=bi.hc_eps, tokens=tokens)
+
+
+def _bound_check(name, g, r, a, rtol, atab, rep):
+    g = np.asarray(g, dtype=np.float64)
+    err = np.abs(g - r)
+    lim = rtol * np.abs(r) + atab * a
+    bad = ~(err <= lim)
+    ratio = np.where(lim > 0, err / np.where(lim > 0, lim, 1), np.where(err > 0, np.inf, 0))
+    rep[name] = dict(n=int(err.size), fail=int(bad.sum()), max_abs=float(np.nanmax(err)) if err.size else 0,
+                     max_ratio=float(np.nanmax(ratio)) if err.size else 0)
+
+
+def compare(g, o, bi, tokens=None):
+    tok = np.arange(bi.T) if tokens is None else np.asarray(tokens)
+    rep = {}
+    gx = g["grad_x"][tok]
+    dist = np.abs(bf16_ordered(gx) - bf16_ordered(o.grad_x_bf16))
+    cancel = np.abs(bf16_bits_to_f32(gx).astype(np.float64) - o.grad_x) <= 2.0 ** -18 * o.grad_x_abs
+    ok = (dist <= 1) | cancel
+    rep["grad_x"] = dict(n=int(dist.size), fail=int((~ok).sum()), max_ulp=int(dist.max()) if dist.size else 0,
+                         cancel_branch=int(((dist > 1) & cancel).sum()))
+    _bound_check("grad_phi", g["grad_phi"], o.grad_phi, o.grad_phi_abs, 2e-4, 2.0 ** -14, rep)
+    _bound_check("grad_alpha", g["grad_alpha"], o.grad_alpha, o.grad_alpha_abs, 1e-6, 2.0 ** -30, rep)
+    _bound_check("grad_bias", g["grad_bias"], o.grad_bias, o.grad_bias_abs, 1e-6, 2.0 ** -30, rep)
+    if bi.gamma is not None:
+        _bound_check("grad_gamma", g["grad_gamma"], o.grad_gamma, o.grad_gamma_abs, 2e-4, 2.0 ** -14, rep)
+    print(f"[parity-bwd] " + " ".join(f"{k}:fail={v['fail']}/{v['n']}" for k, v in rep.items()),
+          file=sys.stderr, flush=True)
+    bad = {k: v for k, v in rep.items() if v["fail"]}
+    assert not bad, f"backward parity failures: {bad}"
+    return rep
+
+
+CASES = [
+    # (name, T, n, D, gamma, grad_x_post, seed)
+    ("T1_D8", 1, 4, 8, False, False, 1),
+    ("T10_D8_gamma_post", 10, 4, 8, True, True, 2),
+    ("T65_D40_ragged", 65, 4, 40, False, True, 3),
+    ("T130_D512_gamma", 130, 4, 512, True, False, 4),
+    ("T64_D7168", 64, 4, 7168, False, False, 5),
+    ("T200_D7168_gamma_post", 200, 4, 7168, True, True, 6),
+    ("T300_D1000", 300, 4, 1000, False, False, 7),
+    ("n8_T17_D24", 17, 8, 24, False, False, 8),
+    ("n8_T70_D256_gamma_post", 70, 8, 256, True, True, 9),
+    ("n8_T129_D2048", 129, 8, 2048, False, False, 10),
+    ("T4097_D256_groups", 4097, 4, 256, True, False, 11),
+]
+
+
+@pytest.mark.parametrize("name,T,n,D,gamma,post,seed", CASES, ids=[c[0] for c in CASES])
+def test_backward_parity(name, T, n, D, gamma, post, seed):
+    print(f"[case] backward {name} T={T} n={n} D={D} gamma={gamma} post={post}", file=sys.stderr, flush=True)
+    bi = synth.backward_inputs(T, n, D, gamma=gamma, x_post=post, seed=seed)
+    compare(gpu_backward(bi), run_oracle(bi), bi)
+
+
+def test_backward_empty_tokens():
+    print("[case] backward T=0", file=sys.stderr, flush=True)
+    bi = synth.backward_inputs(0, 4, 256, gamma=True, seed=12)
+    g = gpu_backward(bi)
+    for k in ("grad_phi", "grad_alpha", "grad_bias", "grad_gamma"):
+        assert np.all(g[k] == 0.0), k
+
+
+def test_backward_bitwise_reproducible():
+    print("[case] backward determinism T=300 D=2048", file=sys.stderr, flush=True)
+    bi = synth.backward_inputs(300, 4, 2048, gamma=True, x_post=True, seed=13)
+    a, b = gpu_backward(bi, repeat=2)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+
+
+def test_backward_mid_workload_shape():
+    # the mid prefill shape (T = 4096, n = 4, D = 4096, gamma): every cross-token
+    # gradient in full, gradX on sampled rows (first, last, tile edges, random)
+    print("[case] backward mid T=4096 D=4096 gamma", file=sys.stderr, flush=True)
+    bi = synth.backward_inputs(4096, 4, 4096, gamma=True, seed=14)
+    rng = np.random.default_rng(0)
+    tok = np.unique(np.concatenate([[0, 63, 64, 2047, 2048, 4095], rng.integers(0, 4096, 26)]))
+    compare(gpu_backward(bi), run_oracle(bi, tokens=tok), bi, tokens=tok)
+
+
+def test_backward_large_workload_shape():
+    # the large prefill shape (T = 16384, n = 4, D = 7168), as the benchmark runs it
+    print("[case] backward large T=16384 D=7168", file=sys.stderr, flush=True)
+    bi = synth.backward_inputs(16384, 4, 7168, seed=15)
+    rng = np.random.default_rng(1)
+    tok = np.unique(np.concatenate([[0, 1, 63, 64, 8191, 16383], rng.integers(0, 16384, 26)]))
+    compare(gpu_backward(bi), run_oracle(bi, tokens=tok), bi, tokens=tok)

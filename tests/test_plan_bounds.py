@@ -23,3 +23,14 @@ def test_plan_indices_stay_in_bounds(tmp_path):
     res = subprocess.run([str(exe)], capture_output=True, text=True)
     assert res.returncode == 0, res.stdout + res.stderr
     assert res.stdout.startswith("ok ")
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+def test_backward_plan_indices_stay_in_bounds(tmp_path):
+    exe = tmp_path / "bwd_plan_check"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall",
+                    f"-I{os.path.join(ROOT, 'mhc_hyper_connection_amd', 'csrc')}",
+                    os.path.join(HERE, "bwd_plan_check.cpp"), "-o", str(exe)], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert res.stdout.startswith("ok ")
