@@ -261,7 +261,7 @@ mhc_status mhc_pre_backward(const mhc_pre_bwd_params* params, const mhc_pre_bwd_
     a.hc_eps = params->hc_eps;
     char* ws = static_cast<char*>(workspace);
     a.pack = ws + plan.off_pack;
-    a.gmix = reinterpret_cast<float*>(ws + plan.off_gmix);
+    a.gmix = reinterpret_cast<uint16_t*>(ws + plan.off_gmix);
     a.c3 = reinterpret_cast<float*>(ws + plan.off_c3);
     a.terms = reinterpret_cast<double*>(ws + plan.off_terms);
     a.pphi = reinterpret_cast<float*>(ws + plan.off_pphi);

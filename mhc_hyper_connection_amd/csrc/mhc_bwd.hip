@@ -51,20 +51,6 @@ __device__ __forceinline__ Split3 split3(float v)
     s.t[2] = f32_to_bf16_bits(r2);
     return s;
 }
-// Eight floats -> the three bf16x8 term vectors.
-__device__ __forceinline__ void split8(const float (&v)[8], bf16x8 (&out)[3])
-{
-    u32x4 w[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const Split3 s = split3(v[e]);
-#pragma unroll
-        for (int p = 0; p < 3; ++p) w[p][e >> 1] |= s.t[p] << (16 * (e & 1));
-    }
-#pragma unroll
-    for (int p = 0; p < 3; ++p) out[p] = __builtin_bit_cast(bf16x8, w[p]);
-}
-
 // ------------------------------------------------------------------ weight pack
 
 // Unit u = (((((b * n + i) * 2 + h) * KS + ks) * 3 + p) * 64 + lane holds, for lane
@@ -109,8 +95,9 @@ __device__ __forceinline__ double wave_sum(double v)
     return v;
 }
 
-// One wave per token (4 per workgroup). Outputs: gMix [T][MP] (f32, zero past M),
-// c3 [T], terms [T][3 + M] (fp64: the token's alpha terms, then its bias terms).
+// One wave per token (4 per workgroup). Outputs: gMix [T][KS][3][32] (three bf16 terms
+// of each f32 value, zero past M), c3 [T], terms [3 + M][T] (fp64: the token's alpha
+// terms, then its bias terms).
 template <int N>
 __global__ void __launch_bounds__(256)
 bwd_token_kernel(Args a, int64_t T, int D)
@@ -173,9 +160,12 @@ bwd_token_kernel(Args a, int64_t T, int D)
                 ta2 += tb * w;
             }
             gi += gw * (double)a.h_mix[t * M + m];
-            a.terms[t * (3 + M) + 3 + m] = tb;
+            a.terms[(3 + m) * T + t] = tb;
         }
-        a.gmix[t * MP + m] = (float)(gw * inv);
+        const Split3 sp = split3((float)(gw * inv));
+        uint16_t* dst = a.gmix + (t * (MP / 32) + m / 32) * 3 * 32 + m % 32;
+#pragma unroll
+        for (int p = 0; p < 3; ++p) dst[32 * p] = (uint16_t)sp.t[p];
     }
     gi = wave_sum(gi);
     ta0 = wave_sum(ta0);
@@ -183,9 +173,9 @@ bwd_token_kernel(Args a, int64_t T, int D)
     ta2 = wave_sum(ta2);
     if (lane == 0) {
         a.c3[t] = (float)(gi * inv * inv * inv / (double)K);
-        a.terms[t * (3 + M) + 0] = ta0;
-        a.terms[t * (3 + M) + 1] = ta1;
-        a.terms[t * (3 + M) + 2] = ta2;
+        a.terms[0 * T + t] = ta0;
+        a.terms[1 * T + t] = ta1;
+        a.terms[2 * T + t] = ta2;
     }
 }
 
@@ -198,6 +188,14 @@ constexpr int kPairs = 6;
 constexpr int pair_a(int q) { return q == 0 ? 2 : (q == 1 ? 0 : (q == 2 ? 1 : (q == 3 ? 1 : 0))); }
 constexpr int pair_b(int q) { return q == 0 ? 0 : (q == 1 ? 2 : (q == 2 ? 1 : (q == 3 ? 0 : (q == 4 ? 1 : 0)))); }
 
+// Transposed LDS rows ([column or m][64 tokens], 128 bytes) hold their eight 8-token
+// chunks in a row-dependent order: chunk c of row r sits at c ^ swz(r). A 16-byte
+// operand read (8 consecutive tokens of 16 rows r0..r0+15) then spreads over all banks,
+// and so do the scattered 2-byte writes of one instruction (8 positions g*8 + e of a
+// token, for the four lane groups g).
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ (((r >> 3) & 3) << 1); }
+__device__ __forceinline__ int tslot(int r, int tok) { return r * kTile + (((tok >> 3) ^ swz(r)) << 3) + (tok & 7); }
+
 template <int N, int SGN, int KS>
 struct MainCfg {
     static constexpr int M = N * N + 2 * N;
@@ -207,11 +205,11 @@ struct MainCfg {
     static constexpr int CB = NCOL / 16;                  // gradPhi column blocks
     static constexpr int BPW = RB * CB / 4;               // gradPhi blocks per wave
     static constexpr int PACK_U = SGN * 2 * KS * 3 * 64;  // 16-byte units of packed phi
-    static constexpr int XS = kTile + 8;                  // bf16 per transposed-x row
-    static constexpr int GS = kTile + 4;                  // floats per transposed-gMix row
+    static constexpr int XS = kTile;                      // bf16 per transposed-x row
+    static constexpr int GXS = kTile;                     // bf16 per transposed-gMix row
     static constexpr int PACK_BYTES = PACK_U * 16;
     static constexpr int XT_BYTES = NCOL * XS * 2;
-    static constexpr int GT_BYTES = MP * GS * 4;
+    static constexpr int GT_BYTES = 3 * MP * GXS * 2;     // three terms
     static constexpr int RED_BYTES = kTile * NCOL * 4;    // gradGamma reduction at the end
     static constexpr int MAIN_BYTES = PACK_BYTES + XT_BYTES + GT_BYTES;
     static constexpr int LDS_BYTES = MAIN_BYTES > RED_BYTES ? MAIN_BYTES : RED_BYTES;
@@ -219,24 +217,24 @@ struct MainCfg {
     static_assert(XT_BYTES % 16 == 0 && PACK_BYTES % 16 == 0, "LDS regions stay 16-byte aligned");
 };
 
-template <int N, int SGN, int KS>
-__global__ void __launch_bounds__(kThreads, 2)
-bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles)
+// GAMMA: gamma given (gradX scales xrsGrad, gradGamma is summed); XPOST: gradXPost given.
+template <int N, int SGN, int KS, bool GAMMA, bool XPOST>
+__global__ void __launch_bounds__(kThreads, GAMMA ? 2 : 3)
+bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, int64_t tasks)
 {
     using C = MainCfg<N, SGN, KS>;
     constexpr int M = C::M, MP = C::MP, NCOL = C::NCOL, CB = C::CB, BPW = C::BPW;
-    constexpr int XS = C::XS, GS = C::GS;
     constexpr int NSG = N / SGN;
     __shared__ __attribute__((aligned(16))) char lds[C::LDS_BYTES];
     u32x4* sp = reinterpret_cast<u32x4*>(lds);
     uint16_t* xT = reinterpret_cast<uint16_t*>(lds + C::PACK_BYTES);
-    float* gT = reinterpret_cast<float*>(lds + C::PACK_BYTES + C::XT_BYTES);
+    uint16_t* gT = reinterpret_cast<uint16_t*>(lds + C::PACK_BYTES + C::XT_BYTES);   // [term][m][token]
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, grp = lane >> 4;
     int64_t g;
     int b, sg;
-    main_task(blockIdx.x, nblk, NSG, &g, &b, &sg);
+    if (!main_task(blockIdx.x, nblk, NSG, tasks, &g, &b, &sg)) return;   // padding workgroup
     const int64_t K = (int64_t)N * D;
     const int d0 = kDBlock * b + 8 * grp;          // the lane's 8 positions d0 .. d0+7
     const bool dval = d0 < D;                        // D % 8 == 0: all 8 or none
@@ -246,16 +244,17 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles)
         const u32x4* src = static_cast<const u32x4*>(a.pack) + pack_at(b, sg * SGN, N, KS);
         for (int u = tid; u < C::PACK_U; u += kThreads) sp[u] = src[u];
     }
-    float gam[SGN][8];
+    float gam[GAMMA ? SGN : 1][8];
+    if constexpr (GAMMA) {
 #pragma unroll
-    for (int s = 0; s < SGN; ++s)
+        for (int s = 0; s < SGN; ++s)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            gam[s][e] = (a.gamma && dval) ? a.gamma[(int64_t)(sg * SGN + s) * D + d0 + e] : 1.f;
+            for (int e = 0; e < 8; ++e) gam[s][e] = dval ? a.gamma[(int64_t)(sg * SGN + s) * D + d0 + e] : 1.f;
+    }
 
-    float gg[SGN][8];
+    float gg[GAMMA ? SGN : 1][8];
 #pragma unroll
-    for (int s = 0; s < SGN; ++s)
+    for (int s = 0; s < (GAMMA ? SGN : 1); ++s)
 #pragma unroll
         for (int e = 0; e < 8; ++e) gg[s][e] = 0.f;
     f32x4 pacc[BPW];
@@ -263,57 +262,58 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles)
     for (int q = 0; q < BPW; ++q) pacc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();
 
-    const int64_t tile_end = (g + 1) * tpg < tiles ? (g + 1) * tpg : tiles;
-    for (int64_t tile = g * tpg; tile < tile_end; ++tile) {
-        const int64_t t0 = tile * kTile;
+    // A tile's per-lane inputs, loaded one tile ahead: the next tile's loads go out as
+    // soon as the current tile's registers are consumed and stay in flight through the
+    // gradPhi phase. Rows past the tile and positions past D read as zero.
+    const int row = 16 * wave + j;                   // the lane's token in a tile
+    u32x4 xv[SGN], xp[SGN], gh, gmt[KS][3];
+    float hp[SGN], c3;
+    auto load_tile = [&](int64_t tl) {
+        const int64_t t0 = tl * kTile;
         const int ntile = (int)(T - t0 < kTile ? T - t0 : kTile);
-        const int row = 16 * wave + j;               // the lane's token in the tile
         const int64_t tok = t0 + row;
         const bool tval = row < ntile;
-
-        // loads (rows past the tile and positions past D read as zero)
         const rsrc_t rx = make_rsrc(a.x + t0 * K, (int64_t)ntile * K * 2);
         const rsrc_t rgh = make_rsrc(a.grad_h_in + t0 * D, (int64_t)ntile * D * 2);
-        const rsrc_t rgm = make_rsrc(a.gmix + t0 * MP, (int64_t)ntile * MP * 4);
-        u32x4 xv[SGN], xp[SGN];
+        const rsrc_t rgm = make_rsrc(a.gmix + t0 * (3 * MP), (int64_t)ntile * 3 * MP * 2);
 #pragma unroll
         for (int s = 0; s < SGN; ++s) {
             const uint32_t off = dval ? (uint32_t)(((int64_t)row * K + (int64_t)(sg * SGN + s) * D + d0) * 2) : kOutOfRange;
             xv[s] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
         }
-        if (a.grad_x_post) {
+        if constexpr (XPOST) {
             const rsrc_t rxp = make_rsrc(a.grad_x_post + t0 * K, (int64_t)ntile * K * 2);
 #pragma unroll
             for (int s = 0; s < SGN; ++s) {
                 const uint32_t off = dval ? (uint32_t)(((int64_t)row * K + (int64_t)(sg * SGN + s) * D + d0) * 2) : kOutOfRange;
                 xp[s] = __builtin_amdgcn_raw_buffer_load_b128(rxp, (int)off, 0, 0);
             }
-        } else {
-#pragma unroll
-            for (int s = 0; s < SGN; ++s) xp[s] = u32x4{0u, 0u, 0u, 0u};
         }
-        const u32x4 gh = __builtin_amdgcn_raw_buffer_load_b128(
-            rgh, dval ? (int)(((int64_t)row * D + d0) * 2) : (int)kOutOfRange, 0, 0);
-        float gm[KS][8];
+        gh = __builtin_amdgcn_raw_buffer_load_b128(rgh, dval ? (int)(((int64_t)row * D + d0) * 2) : (int)kOutOfRange, 0, 0);
+        // gMix terms of the lane's token: B operand of xrsGrad (K-step ks, term p)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-                    rgm, (int)(((int64_t)row * MP + 32 * ks + 8 * grp + 4 * hh) * 4), 0, 0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) gm[ks][4 * hh + e] = __uint_as_float(v[e]);
-            }
-        }
-        float hp[SGN];
+            for (int p = 0; p < 3; ++p)
+                gmt[ks][p] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rgm, (int)((((int64_t)row * KS + ks) * 3 * 32 + 32 * p + 8 * grp) * 2), 0, 0);
 #pragma unroll
         for (int s = 0; s < SGN; ++s) hp[s] = tval ? a.h_pre[tok * N + sg * SGN + s] : 0.f;
-        const float c3 = tval ? a.c3[tok] : 0.f;
+        c3 = tval ? a.c3[tok] : 0.f;
+    };
+
+    const int64_t tile_end = (g + 1) * tpg < tiles ? (g + 1) * tpg : tiles;
+    load_tile(g * tpg);
+    for (int64_t tile = g * tpg; tile < tile_end; ++tile) {
+        const int64_t t0 = tile * kTile;
+        const int ntile = (int)(T - t0 < kTile ? T - t0 : kTile);
 
         // xrsGrad^T = phi^T . gMix^T: A = packed phi (columns as rows), B = gMix (tokens)
         bf16x8 bt[KS][3];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) split8(gm[ks], bt[ks]);
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int p = 0; p < 3; ++p) bt[ks][p] = __builtin_bit_cast(bf16x8, gmt[ks][p]);
         const rsrc_t rgx = make_rsrc(a.grad_x + t0 * K, (int64_t)ntile * K * 2);
 #pragma unroll
         for (int s = 0; s < SGN; ++s) {
@@ -336,32 +336,36 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles)
             u32x4 o;
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
-                uint32_t bits[2];
+                float v[2];
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl) {
                     const int e = 2 * e2 + hl;
                     const float xe = hl ? bf16_hi(xv[s][e2]) : bf16_lo(xv[s][e2]);
                     const float ge = hl ? bf16_hi(gh[e2]) : bf16_lo(gh[e2]);
-                    const float pe = hl ? bf16_hi(xp[s][e2]) : bf16_lo(xp[s][e2]);
-                    float v = fmaf(ge, hp[s], xg[e] * gam[s][e]);
-                    v = fmaf(-c3, xe, v) + pe;
-                    bits[hl] = f32_to_bf16_bits(v);
-                    gg[s][e] = fmaf(xe, xg[e], gg[s][e]);
+                    v[hl] = fmaf(ge, hp[s], GAMMA ? xg[e] * gam[GAMMA ? s : 0][e] : xg[e]);
+                    v[hl] = fmaf(-c3, xe, v[hl]);
+                    if constexpr (XPOST) v[hl] += hl ? bf16_hi(xp[s][e2]) : bf16_lo(xp[s][e2]);
+                    if constexpr (GAMMA) gg[s][e] = fmaf(xe, xg[e], gg[s][e]);
                 }
-                o[e2] = bits[0] | (bits[1] << 16);
+                o[e2] = pack_bf16x2(v[0], v[1]);
             }
             const uint32_t off = dval ? (uint32_t)(((int64_t)row * K + (int64_t)(sg * SGN + s) * D + d0) * 2) : kOutOfRange;
             __builtin_amdgcn_raw_buffer_store_b128(o, rgx, (int)off, 0, 0);
             // x of this tile, transposed: xT[local column][token]
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                xT[(s * kDBlock + 8 * grp + e) * XS + row] = (uint16_t)((xv[s][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+                xT[tslot(s * kDBlock + 8 * grp + e, row)] = (uint16_t)((xv[s][e >> 1] >> (16 * (e & 1))) & 0xffffu);
         }
-        // gMix of this tile, transposed: gT[m][token]
+        // gMix terms of this tile, transposed: gT[p][m][token]
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) gT[(32 * ks + 8 * grp + e) * GS + row] = gm[ks][e];
+            for (int p = 0; p < 3; ++p)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    gT[tslot(p * MP + 32 * ks + 8 * grp + e, row)] =
+                        (uint16_t)((gmt[ks][p][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        if (tile + 1 < tile_end) load_tile(tile + 1);
         __syncthreads();
 
         // gradPhi partial: C[m][col] += sum over the tile's tokens of gMix[t][m] x[t][col];
@@ -372,13 +376,11 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles)
             const int rb = bi / CB, cb = bi % CB;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                float av[8];
-                const float* gsrc = gT + (16 * rb + j) * GS + 32 * kt + 8 * grp;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) av[e] = gsrc[e];
                 bf16x8 at[3];
-                split8(av, at);
-                const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xT + (16 * cb + j) * XS + 32 * kt + 8 * grp);
+#pragma unroll
+                for (int p = 0; p < 3; ++p)
+                    at[p] = *reinterpret_cast<const bf16x8*>(gT + tslot(p * MP + 16 * rb + j, 32 * kt + 8 * grp));
+                const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xT + tslot(16 * cb + j, 32 * kt + 8 * grp));
 #pragma unroll
                 for (int p = 2; p >= 0; --p)
                     pacc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at[p], bv, pacc[q], 0, 0, 0);
@@ -402,7 +404,7 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles)
         }
     }
     // gradGamma partial of the group: sum the 64 token lanes of each column in a fixed order
-    if (a.gamma) {
+    if constexpr (GAMMA) {
         float* red = reinterpret_cast<float*>(lds);   // [64 token lanes][NCOL]
 #pragma unroll
         for (int s = 0; s < SGN; ++s)
@@ -438,18 +440,30 @@ bwd_reduce_cols_kernel(Args a, int64_t MK, int64_t K, int64_t G)
     }
 }
 
-// Workgroup c sums column c of terms [T][3 + M] over the tokens: thread-strided fp64
-// sums, then a fixed tree. c < 3: gradAlpha[c]; else gradBias[c - 3].
-__global__ void __launch_bounds__(256)
+// Workgroup c sums row c of terms [3 + M][T] over the tokens: 1024 threads, thread i
+// summing tokens i, i + 1024, ... in that order (four loads in flight), then a fixed
+// tree. c < 3: gradAlpha[c]; else gradBias[c - 3].
+constexpr int kRedThreads = 1024;
+__global__ void __launch_bounds__(kRedThreads)
 bwd_reduce_terms_kernel(Args a, int64_t T, int M)
 {
-    __shared__ double part[256];
+    __shared__ double part[kRedThreads];
     const int c = blockIdx.x, tid = threadIdx.x;
+    const double* row = a.terms + c * T;
     double s = 0.0;
-    for (int64_t t = tid; t < T; t += 256) s += a.terms[t * (3 + M) + c];
+    int64_t t = tid;
+    for (; t + 3 * kRedThreads < T; t += 4 * kRedThreads) {
+        const double v0 = row[t], v1 = row[t + kRedThreads], v2 = row[t + 2 * kRedThreads],
+                     v3 = row[t + 3 * kRedThreads];
+        s += v0;
+        s += v1;
+        s += v2;
+        s += v3;
+    }
+    for (; t < T; t += kRedThreads) s += row[t];
     part[tid] = s;
     __syncthreads();
-    for (int w = 128; w >= 1; w >>= 1) {
+    for (int w = kRedThreads / 2; w >= 1; w >>= 1) {
         if (tid < w) part[tid] += part[tid + w];
         __syncthreads();
     }
@@ -470,6 +484,13 @@ bwd_zero_kernel(Args a, int64_t MK, int64_t K, int M)
     if (idx < M) a.grad_bias[idx] = 0.f;
 }
 
+template <int N, int SGN, int KS, bool GAMMA, bool XPOST>
+void launch_main(const Plan& p, const Args& a, hipStream_t st)
+{
+    hipLaunchKernelGGL((bwd_main_kernel<N, SGN, KS, GAMMA, XPOST>), dim3((unsigned)p.main_blocks),
+                       dim3(kThreads), 0, st, a, p.T, p.g.D, p.g.nblk, p.tpg, p.tiles, p.main_tasks);
+}
+
 template <int N, int SGN, int KS>
 hipError_t launch_all(const Plan& p, const Args& a, hipStream_t st)
 {
@@ -482,8 +503,13 @@ hipError_t launch_all(const Plan& p, const Args& a, hipStream_t st)
     hipLaunchKernelGGL(bwd_token_kernel<N>, dim3((unsigned)p.token_blocks), dim3(256), 0, st, a, p.T, g.D);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_main_kernel<N, SGN, KS>), dim3((unsigned)p.main_blocks), dim3(kThreads), 0, st, a,
-                       p.T, g.D, g.nblk, p.tpg, p.tiles);
+    if (a.gamma) {
+        if (a.grad_x_post) launch_main<N, SGN, KS, true, true>(p, a, st);
+        else launch_main<N, SGN, KS, true, false>(p, a, st);
+    } else {
+        if (a.grad_x_post) launch_main<N, SGN, KS, false, true>(p, a, st);
+        else launch_main<N, SGN, KS, false, false>(p, a, st);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t MK = (int64_t)g.M * g.K;
@@ -491,7 +517,7 @@ hipError_t launch_all(const Plan& p, const Args& a, hipStream_t st)
                        MK, g.K, p.G);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_reduce_terms_kernel, dim3((unsigned)(3 + g.M)), dim3(256), 0, st, a, p.T, g.M);
+    hipLaunchKernelGGL(bwd_reduce_terms_kernel, dim3((unsigned)(3 + g.M)), dim3(kRedThreads), 0, st, a, p.T, g.M);
     return hipGetLastError();
 }
 

@@ -7,9 +7,10 @@
 //
 // Work decomposition
 //   token pass   one wave per token: the hPre gradient (gradHIn . x_i over d, fp64), the
-//                gate and residual backward, the gradient with respect to hMix
-//                (gMix [T][MP], zero past M), c3 = dL/dinvRms * invRms^3 / (n D), and the
-//                token's terms of the alpha and bias gradients (fp64).
+//                gate and residual backward, the gradient with respect to hMix as three
+//                bf16 terms (gMix [T][KS][3][32], zero past M: the matrix-core operand
+//                layout), c3 = dL/dinvRms * invRms^3 / (n D), and the token's terms of the
+//                alpha and bias gradients (fp64, [3 + M][T]).
 //   main pass    one workgroup per (token group, d-block of 32 positions, stream group of
 //                SGN streams): for each tile of 64 tokens, xrsGrad = gMix . phi on the
 //                matrix cores (phi^T as the A operand, packed per d-block; gMix as B),
@@ -85,13 +86,34 @@ inline bool make_geometry(int n, int D, Geometry* g)
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Main-pass workgroup -> task (token group, stream group, d-block), tasks numbered with
+// the d-block fastest. Workgroups b and b + 8 run on the same XCD (the hardware deals
+// workgroups to the 8 XCDs in turn), and they take tasks 2u and 2u + 1: adjacent
+// d-blocks, whose 64-byte pieces of a token row share 128-byte lines, so each line of
+// x, gradHIn and gradX goes through one XCD's L2 only. Workgroups in flight still cover
+// nearby columns of the same rows. Returns false for the padding workgroups.
+MHC_BWD_HOST_DEVICE inline int64_t main_blocks_for(int64_t tasks) { return (tasks + 15) / 16 * 16; }
+MHC_BWD_HOST_DEVICE inline bool main_task(int64_t blk, int nblk, int NSG, int64_t tasks, int64_t* grp,
+                                          int* b, int* sg)
+{
+    const int64_t q = blk % 8, r = blk / 8;
+    const int64_t t = ((r / 2) * 8 + q) * 2 + (r % 2);
+    if (t >= tasks) return false;
+    *b = (int)(t % nblk);
+    const int64_t gs = t / nblk;
+    *sg = (int)(gs % NSG);
+    *grp = gs / NSG;
+    return true;
+}
+
 struct Plan {
     Geometry g;
     int64_t T = 0;
     int64_t tiles = 0;        // ceil(T / 64)
     int64_t G = 0;            // token groups
     int64_t tpg = 0;          // tiles per group (the last group may have fewer)
-    int64_t main_blocks = 0;  // G * nblk * NSG
+    int64_t main_tasks = 0;   // G * nblk * NSG
+    int64_t main_blocks = 0;  // main_tasks rounded up to 16 (see main_task)
     int64_t token_blocks = 0; // ceil(T / 4): one wave per token
     size_t off_pack = 0, off_gmix = 0, off_c3 = 0, off_terms = 0, off_pphi = 0, off_pgam = 0;
     size_t ws_bytes = 0;
@@ -109,13 +131,14 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     if (G < 1) G = 1;
     p.tpg = (p.tiles + G - 1) / G;
     p.G = p.tiles > 0 ? (p.tiles + p.tpg - 1) / p.tpg : 1;   // no empty group
-    p.main_blocks = p.G * per_group;
+    p.main_tasks = p.G * per_group;
+    p.main_blocks = main_blocks_for(p.main_tasks);
     p.token_blocks = (T + 3) / 4;
     size_t off = 0;
     p.off_pack = off;
     off = align_up(off + g.pack_bytes, 256);
     p.off_gmix = off;
-    off = align_up(off + (size_t)T * g.MP * 4, 256);
+    off = align_up(off + (size_t)T * g.KS * 3 * 32 * 2, 256);
     p.off_c3 = off;
     off = align_up(off + (size_t)T * 4, 256);
     p.off_terms = off;
@@ -126,17 +149,6 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     off = align_up(off + (size_t)p.G * g.K * 4, 256);
     p.ws_bytes = off;
     return p;
-}
-
-// Main-pass workgroup -> (token group, d-block, stream group). Consecutive workgroups
-// take adjacent d-blocks of the same tokens, so the ones in flight read nearby columns
-// of the same rows.
-MHC_BWD_HOST_DEVICE inline void main_task(int64_t blk, int nblk, int NSG, int64_t* grp, int* b, int* sg)
-{
-    *sg = (int)(blk % NSG);
-    const int64_t r = blk / NSG;
-    *b = (int)(r % nblk);
-    *grp = r / nblk;
 }
 
 // Device pointers of one backward call.
@@ -161,9 +173,9 @@ struct Args {
     double hc_eps;
     // workspace
     void* pack;
-    float* gmix;
+    uint16_t* gmix;    // [T][KS][3][32] bf16 terms of the hMix gradient
     float* c3;
-    double* terms;
+    double* terms;     // [3 + M][T]
     float* pphi;
     float* pgam;
 };

@@ -19,13 +19,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+// float -> bf16 bits by the hardware conversion (v_cvt_pk_bf16_f32 on gfx950): round to
+// nearest, ties to even, in the default rounding mode; NaN stays NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// Two floats -> a packed bf16 pair (lo in bits 0-15), one conversion instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ double bf16_bits_to_double(uint32_t b)

@@ -133,7 +133,7 @@ __device__ __forceinline__ void hin_store(rsrc_t hres, uint32_t off, const u32x4
         u32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            o[e] = f32_to_bf16_bits(acc[2 * e]) | (f32_to_bf16_bits(acc[2 * e + 1]) << 16);
+            o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
         if (kBlock * blk < lim)
             __builtin_amdgcn_raw_buffer_store_b128(o, hres, (int)(off + 2 * kBlock * blk), 0, 0);
     }
@@ -544,7 +544,7 @@ hin_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wts,
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        o[e] = f32_to_bf16_bits(acc[2 * e]) | (f32_to_bf16_bits(acc[2 * e + 1]) << 16);
+        o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
     // hIn is not read again by this forward: stream it past the caches
     __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(h_in + t * (int64_t)D + d8 * 8));
 }

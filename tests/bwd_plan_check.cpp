@@ -53,31 +53,39 @@ static int check(int n, int D, long long T)
     // token groups: non-empty, covering [0, tiles)
     if (p.G < 1 || p.G * p.tpg < p.tiles || (p.G - 1) * p.tpg >= p.tiles)
         return fail("token groups", n, D, T, p.G, p.tpg);
-    if (p.main_blocks != p.G * g.nblk * g.NSG) return fail("main blocks", n, D, T, p.main_blocks, p.G);
+    if (p.main_tasks != p.G * g.nblk * g.NSG) return fail("main tasks", n, D, T, p.main_tasks, p.G);
+    if (p.main_blocks < p.main_tasks || p.main_blocks % 16) return fail("main blocks", n, D, T, p.main_blocks, p.main_tasks);
     if (p.token_blocks * 4 < T) return fail("token blocks", n, D, T, p.token_blocks, T);
     if (p.main_blocks <= 4000000) {
-        std::vector<unsigned char> seen((size_t)p.main_blocks, 0);
+        // every task exactly once; the two d-blocks of a pair (2u, 2u + 1, same token
+        // group and stream group) go to workgroups 8 apart, i.e. the same XCD
+        std::vector<long long> at((size_t)p.main_tasks, -1);
         for (long long blk = 0; blk < p.main_blocks; ++blk) {
             int64_t gr;
             int b, sg;
-            main_task(blk, g.nblk, g.NSG, &gr, &b, &sg);
+            if (!main_task(blk, g.nblk, g.NSG, p.main_tasks, &gr, &b, &sg)) continue;
             if (gr < 0 || gr >= p.G || b < 0 || b >= g.nblk || sg < 0 || sg >= g.NSG)
                 return fail("main task range", n, D, T, gr, b);
-            const size_t id = ((size_t)gr * g.nblk + b) * g.NSG + sg;
-            if (seen[id]++) return fail("main task twice", n, D, T, blk, (long long)id);
+            const size_t id = ((size_t)gr * g.NSG + sg) * g.nblk + b;
+            if (at[id] >= 0) return fail("main task twice", n, D, T, blk, (long long)id);
+            at[id] = blk;
+        }
+        for (size_t id = 0; id < at.size(); ++id) {
+            if (at[id] < 0) return fail("main task missing", n, D, T, (long long)id, 0);
+            if (id % 2 == 1 && at[id] - at[id - 1] != 8) return fail("pair not on one XCD", n, D, T, at[id - 1], at[id]);
         }
     }
     // byte offsets the main pass forms inside one tile stay below 2^31 (buffer offsets)
     const long long K = g.K;
     const long long xoff = (long long)(kTile - 1) * K * 2 + (long long)(n - 1) * D * 2 + (long long)(D - 8) * 2 + 16;
     if (xoff >= (1LL << 31)) return fail("x offset", n, D, T, xoff, 1LL << 31);
-    const long long goff = ((long long)(kTile - 1) * g.MP + g.MP) * 4;
+    const long long goff = ((long long)(kTile - 1) * g.KS * 3 * 32 + (long long)g.KS * 3 * 32) * 2;
     if (goff >= (1LL << 31)) return fail("gMix offset", n, D, T, goff, 1LL << 31);
     // partial sums: P[g][m][k] and Q[g][k]; per-token terms [T][3 + M]
     const long long pmax = (p.G - 1) * (long long)g.M * K + (long long)(g.M - 1) * K + (K - 1);
     if (pmax >= p.G * (long long)g.M * K) return fail("gradPhi partial index", n, D, T, pmax, 0);
     // workspace sections in order, each large enough, inside ws_bytes
-    const size_t need[] = {g.pack_bytes, (size_t)T * g.MP * 4, (size_t)T * 4, (size_t)T * (3 + g.M) * 8,
+    const size_t need[] = {g.pack_bytes, (size_t)T * g.KS * 3 * 32 * 2, (size_t)T * 4, (size_t)T * (3 + g.M) * 8,
                            (size_t)p.G * g.M * K * 4, (size_t)p.G * K * 4};
     const size_t off[] = {p.off_pack, p.off_gmix, p.off_c3, p.off_terms, p.off_pphi, p.off_pgam, p.ws_bytes};
     for (int s = 0; s < 6; ++s) {
