@@ -51,7 +51,8 @@ class _BwdIn(ctypes.Structure):
                 ("hc_eps", ctypes.c_double)] + [
         (name, ctypes.c_void_p) for name in
         ("x", "phi", "alpha", "grad_h_in", "grad_h_post", "grad_h_res", "inv_rms",
-         "h_mix", "h_pre", "h_post", "gamma", "grad_x_post")]
+         "h_mix", "h_pre", "h_post", "gamma", "grad_x_post")] + [
+        ("num_iters", ctypes.c_int32), ("sum_out", ctypes.c_void_p), ("norm_out", ctypes.c_void_p)]
 
 
 class _BwdOut(ctypes.Structure):
@@ -76,7 +77,7 @@ def _bind(lib):
     lib.oracle_mhcpre_forward_f64.restype = ctypes.c_int
     lib.oracle_mhcpre_forward_f64.argtypes = [
         ctypes.c_int64, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp,
-        ctypes.c_double, ctypes.c_double, dp, dp, dp, dp, dp, dp]
+        ctypes.c_double, ctypes.c_double, ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp]
     lib.oracle_pre_backward.restype = ctypes.c_int
     lib.oracle_pre_backward.argtypes = [ctypes.POINTER(_BwdIn), dp, ctypes.c_int64,
                                         ctypes.POINTER(_BwdOut), ctypes.c_int]
@@ -189,12 +190,15 @@ class MhcPreF64:
     h_post: np.ndarray
     h_res: np.ndarray
     h_in: np.ndarray
+    sum_out: np.ndarray | None = None
+    norm_out: np.ndarray | None = None
 
 
 def mhcpre_forward_f64(x, phi, alpha, bias, gamma=None, *, norm_eps=1e-6, hc_eps=1e-6,
-                       lib=None) -> MhcPreF64:
-    """The MhcPre forward (affine hRes, no Sinkhorn) on float64 inputs: the function whose
-    gradient ``backward`` returns. x: [T, n, D]; phi: [n*n + 2n, n*D]; alpha: [3];
+                       num_iters=0, lib=None) -> MhcPreF64:
+    """The forward on float64 inputs: the function whose gradient ``backward`` returns.
+    num_iters == 0: MhcPre (affine hRes); >= 1: MhcPreSinkhorn (hRes the Sinkhorn of it,
+    with the sum_out / norm_out planes). x: [T, n, D]; phi: [n*n + 2n, n*D]; alpha: [3];
     bias: [n*n + 2n]; gamma: [n, D] or None. All results float64, hIn unrounded."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     T, n, D = x.shape
@@ -204,12 +208,16 @@ def mhcpre_forward_f64(x, phi, alpha, bias, gamma=None, *, norm_eps=1e-6, hc_eps
     bias = np.ascontiguousarray(bias, dtype=np.float64).reshape(M)
     if gamma is not None:
         gamma = np.ascontiguousarray(gamma, dtype=np.float64).reshape(n, D)
+    steps = 2 * int(num_iters)
     r = MhcPreF64(np.empty(T), np.empty((T, M)), np.empty((T, n)), np.empty((T, n)),
-                  np.empty((T, n, n)), np.empty((T, D)))
+                  np.empty((T, n, n)), np.empty((T, D)),
+                  np.empty((steps, T, n)) if steps else None,
+                  np.empty((steps, T, n, n)) if steps else None)
     rc = (lib or _load()).oracle_mhcpre_forward_f64(
         T, n, D, _ptr(x), _ptr(phi), _ptr(alpha), _ptr(bias), _ptr(gamma),
-        float(norm_eps), float(hc_eps), _ptr(r.inv_rms), _ptr(r.h_mix), _ptr(r.h_pre),
-        _ptr(r.h_post), _ptr(r.h_res), _ptr(r.h_in))
+        float(norm_eps), float(hc_eps), int(num_iters), _ptr(r.inv_rms), _ptr(r.h_mix),
+        _ptr(r.h_pre), _ptr(r.h_post), _ptr(r.h_res), _ptr(r.h_in), _ptr(r.sum_out),
+        _ptr(r.norm_out))
     if rc != 0:
         raise ValueError("oracle rejected the problem description")
     return r
@@ -233,12 +241,13 @@ class BackwardResult:
 
 def backward(x_bits, phi, alpha, grad_h_in_bits, grad_h_post, grad_h_res, inv_rms, h_mix,
              h_pre, h_post, gamma=None, grad_x_post_bits=None, *, hc_eps=1e-6, tokens=None,
-             nthreads=0, lib=None) -> BackwardResult:
+             num_iters=0, sum_out=None, norm_out=None, nthreads=0, lib=None) -> BackwardResult:
     """The MhcPre backward in fp64 from the inputs the GPU receives: x, gradHIn and
     gradXPost as bf16 bits; phi [n*n + 2n, n*D], alpha [3], gradHPost [T, n],
     gradHRes [T, n, n], invRms [T], hMix [T, M], hPre [T, n], hPost [T, n], gamma [n, D]
     as float32. gradX rows are returned for ``tokens`` (default: all); every other
-    gradient sums over all tokens."""
+    gradient sums over all tokens. num_iters >= 1: the MhcPreSinkhorn backward, reading
+    the forward's saved planes sum_out [2it, T, n] and norm_out [2it, T, n, n] (float32)."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     T, n, D = x_bits.shape
     M = n * n + 2 * n
@@ -264,9 +273,13 @@ def backward(x_bits, phi, alpha, grad_h_in_bits, grad_h_post, grad_h_res, inv_rm
         np.empty((ntok, n, D)), np.empty((ntok, n, D), dtype=np.uint16), np.empty((ntok, n, D)),
         np.empty((M, K)), np.empty((M, K)), np.empty(3), np.empty(3), np.empty(M), np.empty(M),
         np.empty((n, D)) if g else None, np.empty((n, D)) if g else None, np.empty((T, M)))
+    if num_iters:
+        sum_out = f32(sum_out, (2 * num_iters, T, n))
+        norm_out = f32(norm_out, (2 * num_iters, T, n, n))
     bin_ = _BwdIn(T, n, D, float(hc_eps), *[_ptr(a) for a in (
         x_bits, phi, alpha, ghin, ghpost, ghres, inv_rms, h_mix, h_pre, h_post, gamma,
-        grad_x_post_bits)])
+        grad_x_post_bits)], int(num_iters), _ptr(sum_out) if num_iters else None,
+        _ptr(norm_out) if num_iters else None)
     bout = _BwdOut(*[_ptr(getattr(r, f)) for f, _ in _BwdOut._fields_])
     rc = (lib or _load()).oracle_pre_backward(ctypes.byref(bin_), _ptr(tok), ntok,
                                               ctypes.byref(bout), int(nthreads))

@@ -13,6 +13,13 @@
  *   [V2]  "CANN ops-transformer 中 aclnnMhcPreV2 算子接口全解析" (kwkr.cn/news/422178),
  *         section 3: the MhcPre forward (affine hRes = pRes * alpha2 + bias2, no Sinkhorn).
  *
+ *   [SK]  "CANN ops-transformer 算子详解：aclnnMhcPreSinkhorn 接口与 MhcPreSinkhorn 实现剖析"
+ *         (m.mzlw.cn/news/197063): section 1 names the MhcPreSinkhornBackward operator and
+ *         says the forward's hPre, hMix, invRms, normOut and sumOut are its inputs;
+ *         section 3.2 gives the Sinkhorn steps. The pages give no formula for that
+ *         backward: with num_iters >= 1 the res branch below is the derivative of those
+ *         steps, worked out by hand (reading B6).
+ *
  * The backward takes the forward's saved values (invRms, hMix, hPre, hPost) as inputs, as
  * [BW] section 1 describes, and does not recompute them. Every input converts to double
  * exactly; every sum and product is in double; gradX is also returned rounded once to
@@ -31,6 +38,13 @@
  *      token order. Alongside each, the sum of the absolute values of its terms is
  *      returned: the scale of the rounding error of any summation order, which the
  *      tests use to bound the error of a float32 evaluation.
+ *   B6 MhcPreSinkhorn (num_iters >= 1): hRes = Sinkhorn(L), L = alpha2 pRes + biasRes, with
+ *      the forward's steps ([SK] 3.2, as in mhc_oracle.c): A_0 = rowsoftmax(L) + eps, then
+ *      for k = 1 .. 2 it - 1 A_k = A_{k-1} / s_k with s_k the column (k odd) or row (k
+ *      even) sums of A_{k-1} plus eps. Given G = dLoss/dA_k, a column step passes back
+ *      (G[r][c] - sum_r' G[r'][c] A_k[r'][c]) / s_k[c] (rows likewise), and the softmax
+ *      step dL[r][c] = P[r][c] (G[r][c] - sum_c' G[r][c'] P[r][c']), P = A_0 - eps. The
+ *      saved planes normOut[k] = A_k and sumOut[k] = s_k are the inputs it reads.
  */
 #include <math.h>
 #include <stddef.h>
@@ -54,14 +68,47 @@ static double sigm(double z)
 /* ---------------------------------------------------------------- MhcPre forward, doubles */
 
 /* [V2] section 3 on double inputs, all tokens: invRms [T], hMix [T][M], hPre [T][n],
- * hPost [T][n], hRes [T][n][n] (affine), hIn [T][D] (unrounded). gamma may be NULL.
- * M = n*n + 2n (alpha has 3 entries). Any output may be NULL. */
+ * hPost [T][n], hRes [T][n][n], hIn [T][D] (unrounded). gamma may be NULL. M = n*n + 2n
+ * (alpha has 3 entries). num_iters == 0: hRes is the affine map of MhcPre; num_iters
+ * >= 1: hRes is the Sinkhorn of that map ([SK] 3.2, 2 num_iters steps), with the planes
+ * in sum_out [2it][T][n] and norm_out [2it][T][n][n] (step-major). Any output may be NULL. */
+static void sinkhorn_f64(double* A, int n, double eps, int steps, int64_t T, int64_t t,
+                         double* sum_out, double* norm_out)
+{
+    double s[8];
+    for (int k = 0; k < steps; ++k) {
+        if (k == 0) {
+            for (int r = 0; r < n; ++r) {
+                double mx = A[r * n];
+                for (int c = 1; c < n; ++c) mx = A[r * n + c] > mx ? A[r * n + c] : mx;
+                double sum = 0.0;
+                for (int c = 0; c < n; ++c) { A[r * n + c] = exp(A[r * n + c] - mx); sum += A[r * n + c]; }
+                for (int c = 0; c < n; ++c) A[r * n + c] = A[r * n + c] / sum + eps;
+                s[r] = sum;
+            }
+        } else {
+            for (int i = 0; i < n; ++i) {
+                double sum = eps;
+                for (int j = 0; j < n; ++j) sum += (k % 2) ? A[j * n + i] : A[i * n + j];
+                for (int j = 0; j < n; ++j) {
+                    if (k % 2) A[j * n + i] /= sum;
+                    else A[i * n + j] /= sum;
+                }
+                s[i] = sum;
+            }
+        }
+        for (int i = 0; i < n && sum_out; ++i) sum_out[((int64_t)k * T + t) * n + i] = s[i];
+        for (int e = 0; e < n * n && norm_out; ++e) norm_out[((int64_t)k * T + t) * n * n + e] = A[e];
+    }
+}
+
 int oracle_mhcpre_forward_f64(int64_t T, int n, int D, const double* x, const double* phi,
                               const double* alpha, const double* bias, const double* gamma,
-                              double norm_eps, double hc_eps, double* inv_rms, double* h_mix,
-                              double* h_pre, double* h_post, double* h_res, double* h_in)
+                              double norm_eps, double hc_eps, int num_iters, double* inv_rms,
+                              double* h_mix, double* h_pre, double* h_post, double* h_res,
+                              double* h_in, double* sum_out, double* norm_out)
 {
-    if (T < 0 || n < 1 || n > 8 || D < 1 || !x || !phi || !alpha || !bias) return -1;
+    if (T < 0 || n < 1 || n > 8 || D < 1 || num_iters < 0 || !x || !phi || !alpha || !bias) return -1;
     const int M = n * n + 2 * n;
     const int64_t K = (int64_t)n * D;
     for (int64_t t = 0; t < T; ++t) {
@@ -81,8 +128,10 @@ int oracle_mhcpre_forward_f64(int64_t T, int n, int D, const double* x, const do
             if (h_pre) h_pre[t * n + i] = hp[i];
             if (h_post) h_post[t * n + i] = 2.0 * sigm(alpha[1] * (hm[n + i] * inv) + bias[n + i]);
         }
-        for (int e = 0; e < n * n && h_res; ++e)
-            h_res[t * n * n + e] = alpha[2] * (hm[2 * n + e] * inv) + bias[2 * n + e];
+        double L[64];
+        for (int e = 0; e < n * n; ++e) L[e] = alpha[2] * (hm[2 * n + e] * inv) + bias[2 * n + e];
+        if (num_iters > 0) sinkhorn_f64(L, n, hc_eps, 2 * num_iters, T, t, sum_out, norm_out);
+        for (int e = 0; e < n * n && h_res; ++e) h_res[t * n * n + e] = L[e];
         if (inv_rms) inv_rms[t] = inv;
         for (int m = 0; m < M && h_mix; ++m) h_mix[t * M + m] = hm[m];
         for (int d = 0; d < D && h_in; ++d) {
@@ -113,6 +162,9 @@ typedef struct oracle_bwd_in {
     const float* h_post;          /* [T][n] */
     const float* gamma;           /* [n][D] or NULL */
     const uint16_t* grad_x_post;  /* bf16 [T][n][D] or NULL */
+    int32_t num_iters;            /* 0: MhcPre; >= 1: MhcPreSinkhorn (planes below) */
+    const float* sum_out;         /* [2 it][T][n] */
+    const float* norm_out;        /* [2 it][T][n][n] */
 } oracle_bwd_in;
 
 /* gradX rows are produced for the listed tokens (ntok rows, request order); the other
@@ -167,10 +219,37 @@ static void token_head(const oracle_bwd_in* in, int64_t t, double* gmix, double*
         ta[1] += g2 * ((double)in->h_mix[t * M + n + i] * inv);
         tb[n + i] = g2;
     }
-    /* 3.4 res branch: hRes = alpha2 pRes + bias_res (reading B1) */
+    /* 3.4 res branch: hRes = alpha2 pRes + bias_res (reading B1), or its Sinkhorn (B6):
+     * then the gradient of the logits comes back through the saved planes first */
+    double gl[64];
+    for (int e = 0; e < n * n; ++e) gl[e] = in->grad_h_res[t * n * n + e];
+    if (in->num_iters > 0) {
+        const int64_t T = in->T;
+        for (int k = 2 * in->num_iters - 1; k >= 1; --k) {
+            const float* A = in->norm_out + ((int64_t)k * T + t) * n * n;
+            const float* sk = in->sum_out + ((int64_t)k * T + t) * n;
+            for (int i = 0; i < n; ++i) {
+                double u = 0.0;   /* column i (k odd) or row i (k even) of G . A_k */
+                for (int j = 0; j < n; ++j) {
+                    const int e = (k % 2) ? j * n + i : i * n + j;
+                    u += gl[e] * (double)A[e];
+                }
+                for (int j = 0; j < n; ++j) {
+                    const int e = (k % 2) ? j * n + i : i * n + j;
+                    gl[e] = (gl[e] - u) / (double)sk[i];
+                }
+            }
+        }
+        const float* A0 = in->norm_out + t * n * n;    /* step 0: row softmax + eps */
+        for (int r = 0; r < n; ++r) {
+            double u = 0.0;
+            for (int c = 0; c < n; ++c) u += gl[r * n + c] * ((double)A0[r * n + c] - eps);
+            for (int c = 0; c < n; ++c) gl[r * n + c] = ((double)A0[r * n + c] - eps) * (gl[r * n + c] - u);
+        }
+    }
     ta[2] = 0.0;
     for (int e = 0; e < n * n; ++e) {
-        const double g = in->grad_h_res[t * n * n + e];
+        const double g = gl[e];
         gw[2 * n + e] = g * a2;
         ta[2] += g * ((double)in->h_mix[t * M + 2 * n + e] * inv);
         tb[2 * n + e] = g;
@@ -190,7 +269,8 @@ int oracle_pre_backward(const oracle_bwd_in* in, const int64_t* tokens, int64_t 
     if (!in || !o || !in->x || !in->phi || !in->alpha || !in->grad_h_in || !in->grad_h_post ||
         !in->grad_h_res || !in->inv_rms || !in->h_mix || !in->h_pre || !in->h_post)
         return -1;
-    if (in->n < 1 || in->n > 8 || in->D < 1 || in->T < 0 || ntok < 0) return -1;
+    if (in->n < 1 || in->n > 8 || in->D < 1 || in->T < 0 || ntok < 0 || in->num_iters < 0) return -1;
+    if (in->num_iters > 0 && (!in->sum_out || !in->norm_out)) return -1;
     if (tokens == NULL && ntok != in->T) return -1;
     for (int64_t j = 0; tokens && j < ntok; ++j)
         if (tokens[j] < 0 || tokens[j] >= in->T) return -1;

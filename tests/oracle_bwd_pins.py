@@ -18,6 +18,12 @@ What pins what:
                        guide, section 7): closed forms derived by hand below
   summation scale      the returned sums of |terms| bound the sums and equal them
                        when every term is non-negative
+  Sinkhorn backward    (MhcPreSinkhorn: hRes is the Sinkhorn of the affine logits) the
+                       same finite differences through the double forward with the
+                       Sinkhorn steps, n = 4 and 8, 1 to 20 iterations; the double
+                       forward's planes against the pinned bf16 forward oracle; adding a
+                       constant to a row of logits changes no plane, so the logit
+                       gradient (gradBias of the res entries) has zero row sums
 """
 from __future__ import annotations
 
@@ -70,7 +76,7 @@ def forward64(p, x=None, phi=None, alpha=None, bias=None, gamma="same", lib=None
     return oracle.mhcpre_forward_f64(
         p["x"] if x is None else x, p["phi"] if phi is None else phi,
         p["alpha"] if alpha is None else alpha, p["bias"] if bias is None else bias,
-        g, lib=lib)
+        g, num_iters=p.get("num_iters", 0), lib=lib)
 
 
 def loss(p, lib=None, **kw):
@@ -81,9 +87,11 @@ def loss(p, lib=None, **kw):
 
 def backward(p, fwd=None, lib=None, **kw):
     f = fwd or forward64(p, lib=lib)
+    it = p.get("num_iters", 0)
     return oracle.backward(p["x_bits"], p["phi"], p["alpha"], p["ghin_bits"], p["ghpost"],
                            p["ghres"], f.inv_rms, f.h_mix, f.h_pre, f.h_post, p["gamma"],
-                           p["gxp_bits"], lib=lib, **kw)
+                           p["gxp_bits"], num_iters=it, sum_out=f.sum_out, norm_out=f.norm_out,
+                           lib=lib, **kw)
 
 
 def _fd(p, name, lib=None):
@@ -218,6 +226,48 @@ def pin_token_subset(lib=None):
     sub = backward(p, fwd=f, lib=lib, tokens=[6, 0, 3])
     assert np.array_equal(sub.grad_x, full.grad_x[[6, 0, 3]]), "gradX rows follow the token list"
     assert np.array_equal(sub.grad_phi, full.grad_phi), "gradPhi sums over all tokens"
+
+
+def _sinkhorn_problem(T, n, D, it, seed, gamma=True):
+    p = problem(T=T, n=n, D=D, gamma=gamma, x_post=False, seed=seed)
+    p["num_iters"] = it
+    return p
+
+
+def pin_fd_sinkhorn_n4(lib=None):
+    _check_fd(_sinkhorn_problem(2, 4, 8, 3, seed=21), lib)
+
+
+def pin_fd_sinkhorn_n4_20_iters(lib=None):
+    _check_fd(_sinkhorn_problem(1, 4, 8, 20, seed=22, gamma=False), lib)
+
+
+def pin_fd_sinkhorn_n8(lib=None):
+    _check_fd(_sinkhorn_problem(1, 8, 4, 2, seed=23), lib)
+
+
+def pin_fd_sinkhorn_one_iter(lib=None):
+    _check_fd(_sinkhorn_problem(2, 4, 8, 1, seed=24), lib)
+
+
+def pin_sinkhorn_forward64_matches_forward(lib=None):
+    p = _sinkhorn_problem(5, 4, 16, 4, seed=25)
+    f = forward64(p, lib=lib)
+    r = oracle.forward(p["x_bits"], p["phi"], p["alpha"], p["bias"], p["gamma"], num_iters=4)
+    _close(f.h_res, r.h_res, 1e-13, 1e-15, what="hRes (Sinkhorn)")
+    _close(f.sum_out, r.sum_out, 1e-13, 1e-15, what="sumOut")
+    _close(f.norm_out, r.norm_out, 1e-13, 1e-15, what="normOut")
+
+
+def pin_sinkhorn_logit_gradient_row_sums(lib=None):
+    # one token, no other gradient reaching the res logits: gradBias[2n:] is the logit
+    # gradient, and a constant added to a row of logits leaves every plane unchanged
+    p = _sinkhorn_problem(1, 4, 8, 5, seed=26)
+    r = backward(p, lib=lib)
+    g = r.grad_bias[8:].reshape(4, 4)
+    scale = float(np.max(np.abs(g)))
+    assert scale > 1e-3, "the test needs a non-trivial logit gradient"
+    _close(g.sum(axis=1), np.zeros(4), 0.0, 1e-6 * scale, what="row sums of the logit gradient")
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -50,6 +50,18 @@ MUTANTS = {
                             "const double p = gmix[t * M + m] * (double)in->phi[(int64_t)(k % M) * K + (k / M) + m];"),
     "hpre_grad_reads_stream_0": ("oracle_bf16_to_double(in->x[t * K + (int64_t)i * D + d]);",
                                  "oracle_bf16_to_double(in->x[t * K + d]);"),
+    "sk_bwd_reads_previous_plane": ("const float* A = in->norm_out + ((int64_t)k * T + t) * n * n;",
+                                    "const float* A = in->norm_out + ((int64_t)(k - 1) * T + t) * n * n;"),
+    "sk_bwd_no_division": ("gl[e] = (gl[e] - u) / (double)sk[i];", "gl[e] = (gl[e] - u);"),
+    "sk_bwd_rows_for_columns": ("const int e = (k % 2) ? j * n + i : i * n + j;\n                    u +=",
+                                "const int e = (k % 2) ? i * n + j : j * n + i;\n                    u +="),
+    "sk_bwd_softmax_keeps_eps": ("for (int c = 0; c < n; ++c) u += gl[r * n + c] * ((double)A0[r * n + c] - eps);",
+                                 "for (int c = 0; c < n; ++c) u += gl[r * n + c] * (double)A0[r * n + c];"),
+    "sk_bwd_skips_last_step": ("for (int k = 2 * in->num_iters - 1; k >= 1; --k) {",
+                               "for (int k = 2 * in->num_iters - 2; k >= 1; --k) {"),
+    "sk_bwd_no_softmax_step": ("            for (int c = 0; c < n; ++c) gl[r * n + c] = ((double)A0[r * n + c] - eps) * (gl[r * n + c] - u);",
+                               "            (void)u;"),
+    "fwd64_sinkhorn_sums_without_eps": ("double sum = eps;", "double sum = 0.0;"),
     "fwd64_res_unnormalised": ("alpha[2] * (hm[2 * n + e] * inv) + bias[2 * n + e]", "alpha[2] * hm[2 * n + e] + bias[2 * n + e]"),
     "fwd64_hin_uses_hpost_eps": ("hp[i] = sigm(alpha[0] * (hm[i] * inv) + bias[i]) + hc_eps;",
                                  "hp[i] = sigm(alpha[0] * (hm[i] * inv) + bias[i]);"),
