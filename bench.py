@@ -151,15 +151,16 @@ def calibration_copy(torch, dev, mib: int, reps: int = 3):
     del src, dst
 
 
-BWD_METRIC = "tokens/s and achieved HBM GB/s (% of peak) for the MhcPre backward, n=4"
+BWD_METRIC = "tokens/s and achieved HBM GB/s (% of peak) for the MhcPre(Sinkhorn) backward, n=4"
 
 
-def bwd_algorithmic_bytes(T, n, D, gamma=False, x_post=False) -> int:
+def bwd_algorithmic_bytes(T, n, D, gamma=False, x_post=False, num_iters=0) -> int:
     """Bytes the MhcPre backward must move once: x, gradHIn read and gradX written once
     (2K + 2D + 2K per token), the per-token gradients and saved values (gradHPost,
     gradHRes, invRms, hMix, hPre, hPost), phi read and gradPhi written once (4MK each),
     alpha / gradAlpha, gradBias, and with gamma: gamma read and gradGamma written (4K
-    each); with gradXPost: it is read once (2K per token)."""
+    each); with gradXPost: it is read once (2K per token); with Sinkhorn iterations the
+    saved planes are read once (2 it (4n + 4n^2) per token)."""
     M, K = n * n + 2 * n, n * D
     b = T * (2 * K + 2 * D + 2 * K + 4 * n + 4 * n * n + 4 + 4 * M + 4 * n + 4 * n)
     b += 2 * M * K * 4 + 3 * 4 * 2 + M * 4
@@ -167,6 +168,7 @@ def bwd_algorithmic_bytes(T, n, D, gamma=False, x_post=False) -> int:
         b += 2 * K * 4
     if x_post:
         b += T * 2 * K
+    b += T * 2 * num_iters * (4 * n + 4 * n * n)
     return b
 
 
@@ -177,10 +179,13 @@ def cpu_baseline_bwd(bi, max_tokens: int):
     ntok = min(bi.T, max_tokens)
     threads = oracle.max_threads()
     t0 = time.perf_counter()
+    it = bi.num_iters
     oracle.backward(bi.x[:ntok], bi.phi, bi.alpha, bi.grad_h_in[:ntok], bi.grad_h_post[:ntok],
                     bi.grad_h_res[:ntok], bi.inv_rms[:ntok], bi.h_mix[:ntok], bi.h_pre[:ntok],
                     bi.h_post[:ntok], bi.gamma, None if bi.grad_x_post is None else bi.grad_x_post[:ntok],
-                    hc_eps=bi.hc_eps)
+                    hc_eps=bi.hc_eps, num_iters=it,
+                    sum_out=bi.sum_out[:, :ntok] if it else None,
+                    norm_out=bi.norm_out[:, :ntok] if it else None)
     dt = time.perf_counter() - t0
     return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {ntok} of {bi.T} tokens as a problem of their own, every gradient, "
@@ -189,7 +194,8 @@ def cpu_baseline_bwd(bi, max_tokens: int):
 
 def main_backward(args):
     """--op backward: one step = one mhc_pre_backward call at the large prefill shape
-    (T = 16384, n = 4, D = 7168, no gamma, no gradXPost)."""
+    (T = 16384, n = 4, D = 7168, no gamma, no gradXPost), through --bwd-iters Sinkhorn
+    iterations (20, as the forward's; 0 = the MhcPre backward)."""
     import torch
 
     import mhc_hyper_connection_amd as mhc
@@ -197,7 +203,8 @@ def main_backward(args):
 
     T, n, D = 16384, 4, 7168
     print(f"[bench] generating backward inputs T={T} n={n} D={D}", file=sys.stderr, flush=True)
-    bi = synth.backward_inputs(T, n, D, seed=1003)
+    it = args.bwd_iters
+    bi = synth.backward_inputs(T, n, D, sinkhorn_iters=it, seed=1003)
     dev = torch.device("cuda", 0)
 
     def up(a):
@@ -209,12 +216,13 @@ def main_backward(args):
 
     args_dev = [up(a) for a in (bi.x, bi.phi, bi.alpha, bi.grad_h_in, bi.grad_h_post, bi.grad_h_res,
                                 bi.inv_rms, bi.h_mix, bi.h_pre, bi.h_post, bi.gamma, bi.grad_x_post)]
-    run = mhc.PreBackward(T, n, D, hc_eps=bi.hc_eps, device=dev)
+    run = mhc.PreBackward(T, n, D, hc_eps=bi.hc_eps, num_iters=it, device=dev)
     out = run.alloc_outputs(bi.gamma is not None)
+    planes = {"sum_out": up(bi.sum_out), "norm_out": up(bi.norm_out)} if it else {}
     stream = torch.cuda.current_stream(dev)
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        run(*args_dev, out=out)
+        run(*args_dev, out=out, **planes)
     torch.cuda.synchronize(dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
@@ -222,13 +230,13 @@ def main_backward(args):
     t0 = time.perf_counter()
     for a, b in evs:
         a.record(stream)
-        run(*args_dev, out=out)
+        run(*args_dev, out=out, **planes)
         b.record(stream)
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
     call_us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / len(evs)
-    ab = bwd_algorithmic_bytes(T, n, D)
+    ab = bwd_algorithmic_bytes(T, n, D, num_iters=it)
     achieved = ab / (call_us * 1e-6) / 1e9
     line = {
         "metric": BWD_METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -236,7 +244,8 @@ def main_backward(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "large_prefill_backward", "T": T, "n": n, "D": D, "gamma": False,
-                   "grad_x_post": False, "step": "one mhc_pre_backward call (all five kernels)"},
+                   "grad_x_post": False, "num_iters": it,
+                   "step": "one mhc_pre_backward call (all five kernels)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "whole call",
                      "algorithmic_bytes": ab, "avg_launch_us": call_us},
@@ -261,6 +270,8 @@ def main():
     ap.add_argument("--op", choices=("forward", "backward"), default="forward",
                     help="forward (default): the pre-mapping forward line; backward: the "
                          "MhcPre backward at the large prefill shape")
+    ap.add_argument("--bwd-iters", type=int, default=20,
+                    help="Sinkhorn iterations of the backward (0: the MhcPre backward)")
     ap.add_argument("--cpu-tokens-bwd", type=int, default=16384,
                     help="tokens the CPU oracle baseline of the backward runs on (bounded)")
     args = ap.parse_args()

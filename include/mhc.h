@@ -191,18 +191,30 @@ mhc_status mhc_pre_forward_timed(const mhc_pre_params* params, const mhc_pre_ten
  * which is the same value when gamma is absent. Only the three-entry alpha (n*n + 2n phi
  * rows) has a backward (section 5 of the guide).
  *
+ * With num_iters >= 1 the same call is the MhcPreSinkhorn backward: the forward's hRes
+ * is then Sinkhorn(alpha2 * wRes + biasRes) (2 num_iters steps, as mhc_pre_forward
+ * computes it), and the residual logits' gradient comes back through the forward's saved
+ * sum_out / norm_out planes (the aclnnMhcPreSinkhorn guide, section 1, names that
+ * backward and those inputs; it gives no formula). With G = gradHRes, for k = 2 it - 1
+ * down to 1: a column step (k odd) passes back (G[r][c] - sum_r' G[r'][c] A_k[r'][c]) /
+ * s_k[c], a row step (k even) the same along rows, with A_k = norm_out[k] and s_k =
+ * sum_out[k]; the first step (row softmax + hcEps) passes back P (G - rowsum(G P)),
+ * P = norm_out[0] - hcEps. That logit gradient takes gradHRes's place above.
+ *
  * Problem description (host memory):
- *   T        tokens, >= 0
- *   n        4 or 8;  D  a multiple of 8 in [8, 16384]
- *   hc_eps   >= 0: the hcEps the forward used (hPre = sigmoid(...) + hcEps)
- *   reserved must be 0 */
+ *   T          tokens, >= 0
+ *   n          4 or 8;  D  a multiple of 8 in [8, 16384]
+ *   hc_eps     >= 0: the hcEps the forward used (hPre = sigmoid(...) + hcEps)
+ *   num_iters  0: MhcPre backward (affine hRes); 1 .. 1000: MhcPreSinkhorn backward with
+ *              that many Sinkhorn iterations
+ *   reserved   must be 0 */
 typedef struct mhc_pre_bwd_params {
     int64_t T;
     int32_t n;
     int32_t D;
     double hc_eps;
+    int32_t num_iters;
     int32_t reserved;
-    int32_t reserved2;
 } mhc_pre_bwd_params;
 
 /* Device pointers, M = n*n + 2n, K = n*D. Inputs (x, grad_h_in and grad_x_post bf16
@@ -225,8 +237,12 @@ typedef struct mhc_pre_bwd_params {
  *   grad_alpha   [3]                                                   required
  *   grad_bias    [M]                                                   required
  *   grad_gamma   [n, D]     required when gamma is given, else ignored
+ * Saved Sinkhorn planes (inputs; required when num_iters >= 1, else ignored):
+ *   sum_out      [2 it, T, n]       the forward's sum_out (step-major)
+ *   norm_out     [2 it, T, n, n]    the forward's norm_out (step-major)
  * With T == 0 the per-token tensors (x, grad_h_in, grad_h_post, grad_h_res, inv_rms,
- * h_mix, h_pre, h_post, grad_x_post, grad_x) are empty and may be NULL. */
+ * h_mix, h_pre, h_post, grad_x_post, grad_x, sum_out, norm_out) are empty and may be
+ * NULL. */
 typedef struct mhc_pre_bwd_tensors {
     const uint16_t* x;
     const float* phi;
@@ -245,6 +261,8 @@ typedef struct mhc_pre_bwd_tensors {
     float* grad_alpha;
     float* grad_bias;
     float* grad_gamma;
+    const float* sum_out;
+    const float* norm_out;
 } mhc_pre_bwd_tensors;
 
 /* Bytes of device workspace mhc_pre_backward needs. Host only. The workspace holds

@@ -198,10 +198,11 @@ def mhc_pre(x, phi, alpha, bias, gamma=None, pre_mix=None, *, num_iters=20, norm
 
 class PreBackward:
     """Launcher of the MhcPre backward for one problem size (MhcPreBackward guide,
-    0539edu.com/news/4871844, section 3). Owns its workspace; calls through one instance
-    must not overlap."""
+    0539edu.com/news/4871844, section 3); with num_iters >= 1 the MhcPreSinkhorn backward
+    (the forward's Sinkhorn planes are then inputs). Owns its workspace; calls through
+    one instance must not overlap."""
 
-    def __init__(self, T, n, D, *, hc_eps=1e-6, device="cuda"):
+    def __init__(self, T, n, D, *, hc_eps=1e-6, num_iters=0, device="cuda"):
         torch = _torch()
         load()
         self.T, self.n, self.D = int(T), int(n), int(D)
@@ -209,7 +210,8 @@ class PreBackward:
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
-        self.params = make_bwd_params(T, n, D, hc_eps)
+        self.num_iters = int(num_iters)
+        self.params = make_bwd_params(T, n, D, hc_eps, num_iters)
         self.ws_bytes = bwd_workspace_size(self.params)
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
 
@@ -225,7 +227,7 @@ class PreBackward:
         return out
 
     def __call__(self, x, phi, alpha, grad_h_in, grad_h_post, grad_h_res, inv_rms, h_mix, h_pre,
-                 h_post, gamma=None, grad_x_post=None, *, out=None):
+                 h_post, gamma=None, grad_x_post=None, *, sum_out=None, norm_out=None, out=None):
         torch = _torch()
         T, n, D, M, dev = self.T, self.n, self.D, self.M, self.device
         bf, f32 = torch.bfloat16, torch.float32
@@ -238,12 +240,19 @@ class PreBackward:
                                    (gamma, "gamma", f32, (n, D)),
                                    (grad_x_post, "grad_x_post", bf, (T, n, D))):
             _check(t, name, dt, shape, dev)
+        it = self.num_iters
+        if it:
+            if sum_out is None or norm_out is None:
+                raise ValueError("num_iters >= 1 needs the forward's sum_out and norm_out")
+            _check(sum_out, "sum_out", f32, (2 * it, T, n), dev)
+            _check(norm_out, "norm_out", f32, (2 * it, T, n, n), dev)
         if out is None:
             out = self.alloc_outputs(gamma is not None)
         ptrs = {"x": _ptr(x), "phi": _ptr(phi), "alpha": _ptr(alpha), "grad_h_in": _ptr(grad_h_in),
                 "grad_h_post": _ptr(grad_h_post), "grad_h_res": _ptr(grad_h_res),
                 "inv_rms": _ptr(inv_rms), "h_mix": _ptr(h_mix), "h_pre": _ptr(h_pre),
-                "h_post": _ptr(h_post), "gamma": _ptr(gamma), "grad_x_post": _ptr(grad_x_post)}
+                "h_post": _ptr(h_post), "gamma": _ptr(gamma), "grad_x_post": _ptr(grad_x_post),
+                "sum_out": _ptr(sum_out) if it else None, "norm_out": _ptr(norm_out) if it else None}
         for k, v in out.items():
             ptrs[k] = _ptr(v)
         st = raw_backward(self.params, ptrs, _ptr(self.workspace), self.ws_bytes, _stream(dev))
@@ -256,21 +265,25 @@ _BWD_RUNNERS: dict = {}
 
 
 def mhc_pre_backward(x, phi, alpha, grad_h_in, grad_h_post, grad_h_res, inv_rms, h_mix, h_pre,
-                     h_post, gamma=None, grad_x_post=None, *, hc_eps=1e-6):
-    """MhcPre backward. x: bf16 [T, n, D] or [B, S, n, D]; the other per-token tensors
-    follow x's leading dimensions. Returns dict grad_x, grad_phi, grad_alpha, grad_bias
-    (and grad_gamma when gamma is given)."""
+                     h_post, gamma=None, grad_x_post=None, *, hc_eps=1e-6, num_iters=0,
+                     sum_out=None, norm_out=None):
+    """MhcPre backward (num_iters == 0) or MhcPreSinkhorn backward (num_iters >= 1, with
+    the forward's sum_out [2it, ..., n] and norm_out [2it, ..., n, n]). x: bf16 [T, n, D]
+    or [B, S, n, D]; the other per-token tensors follow x's leading dimensions. Returns
+    dict grad_x, grad_phi, grad_alpha, grad_bias (and grad_gamma when gamma is given)."""
     lead = tuple(x.shape[:-2])
     n, D = int(x.shape[-2]), int(x.shape[-1])
     T = math.prod(lead) if lead else 1
-    key = (T, n, D, hc_eps, str(x.device))
+    key = (T, n, D, hc_eps, num_iters, str(x.device))
     r = _BWD_RUNNERS.get(key)
     if r is None:
-        r = _BWD_RUNNERS[key] = PreBackward(T, n, D, hc_eps=hc_eps, device=x.device)
+        r = _BWD_RUNNERS[key] = PreBackward(T, n, D, hc_eps=hc_eps, num_iters=num_iters,
+                                            device=x.device)
     M = n * n + 2 * n
     rs = lambda t, *shape: None if t is None else t.reshape(*shape)
     out = r(x.reshape(T, n, D), phi, alpha, rs(grad_h_in, T, D), rs(grad_h_post, T, n),
             rs(grad_h_res, T, n, n), rs(inv_rms, T), rs(h_mix, T, M), rs(h_pre, T, n),
-            rs(h_post, T, n), gamma, rs(grad_x_post, T, n, D))
+            rs(h_post, T, n), gamma, rs(grad_x_post, T, n, D),
+            sum_out=rs(sum_out, 2 * num_iters, T, n), norm_out=rs(norm_out, 2 * num_iters, T, n, n))
     out["grad_x"] = out["grad_x"].reshape(*lead, n, D)
     return out

@@ -41,13 +41,13 @@ class Tensors(ctypes.Structure):
 
 class BwdParams(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("D", ctypes.c_int32),
-                ("hc_eps", ctypes.c_double), ("reserved", ctypes.c_int32),
-                ("reserved2", ctypes.c_int32)]
+                ("hc_eps", ctypes.c_double), ("num_iters", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 BWD_TENSOR_FIELDS = ("x", "phi", "alpha", "grad_h_in", "grad_h_post", "grad_h_res", "inv_rms",
                      "h_mix", "h_pre", "h_post", "gamma", "grad_x_post", "grad_x", "grad_phi",
-                     "grad_alpha", "grad_bias", "grad_gamma")
+                     "grad_alpha", "grad_bias", "grad_gamma", "sum_out", "norm_out")
 
 
 class BwdTensors(ctypes.Structure):
@@ -152,8 +152,8 @@ def raw_forward_timed(params: Params, ptrs: dict, ws_ptr, ws_bytes, stream, even
                                             stream, arr, len(events)))
 
 
-def make_bwd_params(T, n, D, hc_eps=1e-6) -> BwdParams:
-    return BwdParams(int(T), int(n), int(D), float(hc_eps), 0, 0)
+def make_bwd_params(T, n, D, hc_eps=1e-6, num_iters=0) -> BwdParams:
+    return BwdParams(int(T), int(n), int(D), float(hc_eps), int(num_iters), 0)
 
 
 def bwd_workspace_size(params: BwdParams) -> int:

@@ -198,7 +198,8 @@ namespace {
 mhc_status check_bwd_params(const mhc_pre_bwd_params* p, mhc::bwd::Geometry* g)
 {
     if (!p) return MHC_ERR_NULLPTR;
-    if (p->reserved != 0 || p->reserved2 != 0) return MHC_ERR_PARAM_INVALID;
+    if (p->reserved != 0) return MHC_ERR_PARAM_INVALID;
+    if (p->num_iters < 0 || p->num_iters > 1000) return MHC_ERR_PARAM_INVALID;
     if (!(p->hc_eps >= 0.0)) return MHC_ERR_PARAM_INVALID;    // also rejects NaN
     if (p->T < 0) return MHC_ERR_PARAM_INVALID;
     if (!mhc::bwd::make_geometry(p->n, p->D, g)) return MHC_ERR_PARAM_INVALID;
@@ -233,6 +234,7 @@ mhc_status mhc_pre_backward(const mhc_pre_bwd_params* params, const mhc_pre_bwd_
     if (tok && (!t->x || !t->grad_h_in || !t->grad_h_post || !t->grad_h_res || !t->inv_rms ||
                 !t->h_mix || !t->h_pre || !t->h_post || !t->grad_x))
         return MHC_ERR_NULLPTR;
+    if (tok && params->num_iters > 0 && (!t->sum_out || !t->norm_out)) return MHC_ERR_NULLPTR;
     if (t->gamma && !t->grad_gamma) return MHC_ERR_NULLPTR;
     const mhc::bwd::Plan plan = mhc::bwd::make_plan(g, params->T);
     if (workspace_bytes < plan.ws_bytes) return MHC_ERR_PARAM_INVALID;
@@ -259,6 +261,9 @@ mhc_status mhc_pre_backward(const mhc_pre_bwd_params* params, const mhc_pre_bwd_
     a.grad_bias = t->grad_bias;
     a.grad_gamma = t->gamma ? t->grad_gamma : nullptr;
     a.hc_eps = params->hc_eps;
+    a.num_iters = params->num_iters;
+    a.sum_out = params->num_iters > 0 ? t->sum_out : nullptr;
+    a.norm_out = params->num_iters > 0 ? t->norm_out : nullptr;
     char* ws = static_cast<char*>(workspace);
     a.pack = ws + plan.off_pack;
     a.gmix = reinterpret_cast<uint16_t*>(ws + plan.off_gmix);

@@ -130,14 +130,60 @@ bwd_token_kernel(Args a, int64_t T, int D)
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = wave_sum(acc[i]);
+    const double eps = a.hc_eps;
+
+    // The residual logits' gradient, one lane per matrix entry e = r N + c. MhcPre:
+    // gradHRes itself. MhcPreSinkhorn: back through the saved planes, last step first: a
+    // column step (k odd) passes G -> (G - sum_r G A_k) / s_k[c], a row step (k even) the
+    // same along the row, the row softmax P (G - rowsum(G P)) with P = A_0 - eps; fp64,
+    // the planes' loads issued eight steps at a time.
+    constexpr int NN = N * N;
+    const bool ent = lane < NN;
+    const int er = lane / N, ec = lane % N;
+    double gres = ent ? (double)a.grad_h_res[t * NN + lane] : 0.0;
+    if (a.num_iters > 0) {
+        constexpr int CHUNK = 8;
+        for (int k0 = 2 * a.num_iters - 1; k0 >= 1; k0 -= CHUNK) {
+            float Ak[CHUNK], sk[CHUNK];
+#pragma unroll
+            for (int j = 0; j < CHUNK; ++j) {
+                const int k = k0 - j;
+                const bool on = ent && k >= 1;
+                Ak[j] = on ? a.norm_out[((int64_t)k * T + t) * NN + lane] : 0.f;
+                sk[j] = on ? a.sum_out[((int64_t)k * T + t) * N + ((k & 1) ? ec : er)] : 1.f;
+            }
+#pragma unroll
+            for (int j = 0; j < CHUNK; ++j) {
+                const int k = k0 - j;
+                if (k < 1) break;                 // uniform across the wave
+                double u = gres * (double)Ak[j];
+                if (k & 1) {
+#pragma unroll
+                    for (int off = N; off < NN; off <<= 1) u += __shfl_xor(u, off);
+                } else {
+#pragma unroll
+                    for (int off = 1; off < N; off <<= 1) u += __shfl_xor(u, off);
+                }
+                gres = (gres - u) / (double)sk[j];
+            }
+        }
+        const double P = ent ? (double)a.norm_out[t * NN + lane] - eps : 0.0;
+        double u = gres * P;
+#pragma unroll
+        for (int off = 1; off < N; off <<= 1) u += __shfl_xor(u, off);
+        gres = P * (gres - u);
+    }
 
     // 3.2-3.5, one lane per phi row m (two passes when MP > 64)
-    const double eps = a.hc_eps;
     const double inv = (double)a.inv_rms[t];
     const double a0 = a.alpha[0], a1 = a.alpha[1], a2 = a.alpha[2];
     double gi = 0.0, ta0 = 0.0, ta1 = 0.0, ta2 = 0.0;
+    // the logit gradient of phi row m (m >= 2N) sits in lane m - 2N; fetched here, with
+    // every lane active, for both passes of the loop below
+    const double gl_pass[2] = {__shfl(gres, (lane - 2 * N) & 63), __shfl(gres, (lane + 64 - 2 * N) & 63)};
     for (int m = lane; m < MP; m += 64) {
         double gw = 0.0;
+        const double gl = gl_pass[m >= 64];
         if (m < M) {
             const double w = (double)a.h_mix[t * M + m] * inv;   // the gate input
             double tb;
@@ -155,7 +201,7 @@ bwd_token_kernel(Args a, int64_t T, int D)
                 gw = tb * a1;
                 ta1 += tb * w;
             } else {
-                tb = a.grad_h_res[t * N * N + (m - 2 * N)];
+                tb = gl;
                 gw = tb * a2;
                 ta2 += tb * w;
             }

@@ -171,6 +171,9 @@ struct Args {
     float* grad_bias;
     float* grad_gamma;
     double hc_eps;
+    int num_iters;             // 0: MhcPre; >= 1: MhcPreSinkhorn (the planes below)
+    const float* sum_out;      // [2 it][T][n]
+    const float* norm_out;     // [2 it][T][n][n]
     // workspace
     void* pack;
     uint16_t* gmix;    // [T][KS][3][32] bf16 terms of the hMix gradient

@@ -30,8 +30,12 @@ MhcPre backward inputs (``backward_inputs``; M = n*n + 2n), drawn in this order:
   h_post       [T, n]     U(0, 2)          (the range of 2 sigmoid)
   gamma        [n, D]     U(0.5, 1.5)      (when asked for)
   grad_x_post  [T, n, D]  N(0, 1) -> bf16  (when asked for)
+  sum_out      [2 it, T, n]     U(0.9, 1.1)    (when Sinkhorn planes are asked for)
+  norm_out     [2 it, T, n, n]  U(0.05, 0.45)
 The saved forward values are drawn independently, in the ranges the forward produces:
-the backward is a function of all of them, whatever forward they came from.
+the backward is a function of all of them, whatever forward they came from. (Parity
+tests of the Sinkhorn backward take the planes from the oracle's forward instead, so
+that they are consistent; the benchmark only needs their ranges.)
 """
 from __future__ import annotations
 
@@ -170,6 +174,9 @@ class BwdInputs:
     gamma: np.ndarray | None = None        # float32 [n, D]
     grad_x_post: np.ndarray | None = None  # uint16 bf16 bits [T, n, D]
     hc_eps: float = 1e-6
+    num_iters: int = 0                     # >= 1: Sinkhorn planes below
+    sum_out: np.ndarray | None = None      # float32 [2 it, T, n]
+    norm_out: np.ndarray | None = None     # float32 [2 it, T, n, n]
 
     @property
     def M(self) -> int:
@@ -177,7 +184,7 @@ class BwdInputs:
 
 
 def backward_inputs(T: int, n: int, D: int, *, gamma: bool = False, x_post: bool = False,
-                    seed: int = 11) -> BwdInputs:
+                    sinkhorn_iters: int = 0, seed: int = 11) -> BwdInputs:
     """Inputs of the MhcPre backward with the recipe in the module docstring."""
     rng = np.random.default_rng(seed)
     M, K = n * n + 2 * n, n * D
@@ -193,4 +200,9 @@ def backward_inputs(T: int, n: int, D: int, *, gamma: bool = False, x_post: bool
     hpost = rng.uniform(0.0, 2.0, size=(T, n)).astype(np.float32)
     g = rng.uniform(0.5, 1.5, size=(n, D)).astype(np.float32) if gamma else None
     gxp = _bf16_normal(rng, T * K).reshape(T, n, D) if x_post else None
-    return BwdInputs(T, n, D, x, phi, alpha, ghin, ghpost, ghres, inv, hmix, hpre, hpost, g, gxp)
+    bi = BwdInputs(T, n, D, x, phi, alpha, ghin, ghpost, ghres, inv, hmix, hpre, hpost, g, gxp)
+    if sinkhorn_iters:
+        bi.num_iters = sinkhorn_iters
+        bi.sum_out = rng.uniform(0.9, 1.1, size=(2 * sinkhorn_iters, T, n)).astype(np.float32)
+        bi.norm_out = rng.uniform(0.05, 0.45, size=(2 * sinkhorn_iters, T, n, n)).astype(np.float32)
+    return bi

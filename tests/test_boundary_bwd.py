@@ -63,9 +63,18 @@ def test_reserved_fields():
     p = B.make_bwd_params(128, 4, 256)
     p.reserved = 1
     assert bwd(p) == B.MHC_ERR_PARAM_INVALID
-    p = B.make_bwd_params(128, 4, 256)
-    p.reserved2 = 7
-    assert bwd(p) == B.MHC_ERR_PARAM_INVALID
+    for it in (-1, 1001):
+        p = B.make_bwd_params(128, 4, 256, num_iters=it)
+        assert bwd(p) == B.MHC_ERR_PARAM_INVALID, it
+
+
+def test_sinkhorn_backward_needs_the_planes():
+    p = B.make_bwd_params(128, 4, 256, num_iters=20)
+    assert bwd(p) == B.MHC_ERR_NULLPTR
+    assert bwd(p, _ptrs(sum_out=FAKE)) == B.MHC_ERR_NULLPTR
+    assert bwd(p, _ptrs(norm_out=FAKE)) == B.MHC_ERR_NULLPTR
+    # the same workspace size as the MhcPre backward
+    assert B.bwd_workspace_size(p) == B.bwd_workspace_size(B.make_bwd_params(128, 4, 256))
 
 
 def test_workspace_too_small_and_alignment():

@@ -32,10 +32,14 @@ def gpu_backward(bi, repeat=1):
     import mhc_hyper_connection_amd as mhc
     import torch
     dev = device()
-    r = mhc.PreBackward(bi.T, bi.n, bi.D, hc_eps=bi.hc_eps, device=dev)
+    it = bi.num_iters
+    r = mhc.PreBackward(bi.T, bi.n, bi.D, hc_eps=bi.hc_eps, num_iters=it, device=dev)
     args = [to_dev(a, dev) for a in (bi.x, bi.phi, bi.alpha, bi.grad_h_in, bi.grad_h_post,
                                      bi.grad_h_res, bi.inv_rms, bi.h_mix, bi.h_pre, bi.h_post,
                                      bi.gamma, bi.grad_x_post)]
+    planes = {}
+    if it:
+        planes = {"sum_out": to_dev(bi.sum_out, dev), "norm_out": to_dev(bi.norm_out, dev)}
     out = r.alloc_outputs(bi.gamma is not None)
     results = []
     for _ in range(repeat):
@@ -44,7 +48,7 @@ def gpu_backward(bi, repeat=1):
                 v.view(torch.int16).fill_(0x7FC0)   # NaN: anything not written shows
             else:
                 v.fill_(float("nan"))
-        r(*args, out=out)
+        r(*args, out=out, **planes)
         torch.cuda.synchronize(dev)
         results.append({k: to_host(v) for k, v in out.items()})
     return results if repeat > 1 else results[0]
@@ -53,7 +57,23 @@ def gpu_backward(bi, repeat=1):
 def run_oracle(bi, tokens=None):
     return oracle.backward(bi.x, bi.phi, bi.alpha, bi.grad_h_in, bi.grad_h_post, bi.grad_h_res,
                            bi.inv_rms, bi.h_mix, bi.h_pre, bi.h_post, bi.gamma, bi.grad_x_post,
-                           hc_eps=bi.hc_eps, tokens=tokens)
+                           hc_eps=bi.hc_eps, tokens=tokens, num_iters=bi.num_iters,
+                           sum_out=bi.sum_out, norm_out=bi.norm_out)
+
+
+def sinkhorn_inputs(T, n, D, it, *, gamma=False, post=False, seed=31):
+    """MhcPreSinkhorn backward inputs: the forward's saved values (invRms, hMix, hPre,
+    hPost, sumOut, normOut) come from the fp64 oracle forward on seeded inputs, rounded
+    to float32 as the forward emits them; the incoming gradients are seeded draws."""
+    inp = synth.custom(T, n, D, gamma=gamma, need_backward=True, num_iters=it, seed=seed)
+    f = oracle.forward(inp.x, inp.phi, inp.alpha, inp.bias, inp.gamma, num_iters=it,
+                       want_h_in=False)
+    g = synth.backward_inputs(T, n, D, x_post=post, seed=seed + 1000)
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    return synth.BwdInputs(T, n, D, inp.x, inp.phi, inp.alpha, g.grad_h_in, g.grad_h_post,
+                           g.grad_h_res, f32(f.inv_rms), f32(f.h_mix), f32(f.h_pre), f32(f.h_post),
+                           inp.gamma, g.grad_x_post, num_iters=it, sum_out=f32(f.sum_out),
+                           norm_out=f32(f.norm_out))
 
 
 def _bound_check(name, g, r, a, rtol, atab, rep):
@@ -141,5 +161,32 @@ def test_backward_large_workload_shape():
     print("[case] backward large T=16384 D=7168", file=sys.stderr, flush=True)
     bi = synth.backward_inputs(16384, 4, 7168, seed=15)
     rng = np.random.default_rng(1)
+    tok = np.unique(np.concatenate([[0, 1, 63, 64, 8191, 16383], rng.integers(0, 16384, 26)]))
+    compare(gpu_backward(bi), run_oracle(bi, tokens=tok), bi, tokens=tok)
+
+
+SINKHORN_CASES = [
+    # (name, T, n, D, iterations, gamma, grad_x_post, seed)
+    ("sk_T64_D256_20it", 64, 4, 256, 20, False, False, 41),
+    ("sk_T130_D512_3it_gamma_post", 130, 4, 512, 3, True, True, 42),
+    ("sk_T1_D8_1it", 1, 4, 8, 1, False, False, 43),
+    ("sk_n8_T17_D64_2it", 17, 8, 64, 2, True, False, 44),
+    ("sk_n8_T70_D256_20it", 70, 8, 256, 20, False, True, 45),
+    ("sk_T200_D7168_20it", 200, 4, 7168, 20, False, False, 46),
+]
+
+
+@pytest.mark.parametrize("name,T,n,D,it,gamma,post,seed", SINKHORN_CASES, ids=[c[0] for c in SINKHORN_CASES])
+def test_sinkhorn_backward_parity(name, T, n, D, it, gamma, post, seed):
+    print(f"[case] sinkhorn backward {name} T={T} n={n} D={D} it={it}", file=sys.stderr, flush=True)
+    bi = sinkhorn_inputs(T, n, D, it, gamma=gamma, post=post, seed=seed)
+    compare(gpu_backward(bi), run_oracle(bi), bi)
+
+
+def test_sinkhorn_backward_large_workload_shape():
+    # the large prefill shape with its 20 Sinkhorn iterations: the training step's backward
+    print("[case] sinkhorn backward large T=16384 D=7168 it=20", file=sys.stderr, flush=True)
+    bi = sinkhorn_inputs(16384, 4, 7168, 20, seed=47)
+    rng = np.random.default_rng(2)
     tok = np.unique(np.concatenate([[0, 1, 63, 64, 8191, 16383], rng.integers(0, 16384, 26)]))
     compare(gpu_backward(bi), run_oracle(bi, tokens=tok), bi, tokens=tok)
