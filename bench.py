@@ -245,7 +245,7 @@ def main_backward(args):
         "data": "synthetic",
         "config": {"workload": "large_prefill_backward", "T": T, "n": n, "D": D, "gamma": False,
                    "grad_x_post": False, "num_iters": it,
-                   "step": "one mhc_pre_backward call (all five kernels)"},
+                   "step": "one mhc_pre_backward call (all of its kernels)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "whole call",
                      "algorithmic_bytes": ab, "avg_launch_us": call_us},

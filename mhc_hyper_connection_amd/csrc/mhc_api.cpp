@@ -271,6 +271,7 @@ mhc_status mhc_pre_backward(const mhc_pre_bwd_params* params, const mhc_pre_bwd_
     a.terms = reinterpret_cast<double*>(ws + plan.off_terms);
     a.pphi = reinterpret_cast<float*>(ws + plan.off_pphi);
     a.pgam = reinterpret_cast<float*>(ws + plan.off_pgam);
+    a.glog = reinterpret_cast<double*>(ws + plan.off_glog);
     return mhc::bwd::launch_backward(plan, a, stream) == 0 ? MHC_OK : MHC_ERR_RUNTIME;
 }
 

@@ -86,6 +86,106 @@ bwd_pack_kernel(const float* __restrict__ phi, u32x4* __restrict__ pack, int n, 
     pack[u] = w;
 }
 
+// ------------------------------------------------------------------ Sinkhorn backward
+
+// MhcPreSinkhorn only: the residual logits' gradient through the forward's saved planes,
+// fp64. 64 / (N*N) tokens per wave, one lane per matrix entry e = r N + c. With G =
+// gradHRes and, for k = 2 it - 1 down to 1, A_k = norm_out[k], s_k = sum_out[k]: a column
+// step (k odd) passes G -> (G - sum_r G A_k) / s_k[c], a row step the same along the row;
+// the first step (row softmax + eps) passes P (G - rowsum(G P)), P = A_0 - eps. The
+// planes' loads and the reciprocals 1 / s_k go out ahead of the chain (all steps up to
+// kSkAll, else kSkChunk at a time); row and column sums move values by DPP within a
+// 16-lane row (across rows by __shfl_xor for the n = 8 columns).
+constexpr int kSkAll = 40;
+constexpr int kSkChunk = 8;
+template <int N>
+__device__ __forceinline__ double sk_row_sum(double v)
+{
+    v += dpp<kQuadXor1>(v);
+    v += dpp<kQuadXor2>(v);
+    if constexpr (N == 8) v += dpp<kRowHalfMirror>(v);
+    return v;
+}
+template <int N>
+__device__ __forceinline__ double sk_col_sum(double v)
+{
+    if constexpr (N == 4) {
+        v += dpp<kRowRor4>(v);
+        v += dpp<kRowRor8>(v);
+    } else {
+        v += dpp<kRowRor8>(v);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+    }
+    return v;
+}
+template <int N>
+__device__ __forceinline__ double sk_step(double G, float A, double rs, int k)
+{
+    const double u = (k & 1) ? sk_col_sum<N>(G * (double)A) : sk_row_sum<N>(G * (double)A);
+    return (G - u) * rs;
+}
+
+template <int N>
+__global__ void __launch_bounds__(256)
+bwd_sinkhorn_kernel(Args a, int64_t T)
+{
+    constexpr int NN = N * N;
+    constexpr int TPW = 64 / NN;                    // tokens per wave
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int e = lane % NN, er = e / N, ec = e % N;
+    const int64_t t = ((int64_t)blockIdx.x * 4 + wave) * TPW + lane / NN;
+    const bool live = t < T;                        // groups of NN lanes: live or not as a whole
+    const int64_t tt = live ? t : T - 1;            // loads stay in bounds and unpredicated
+    const int steps = 2 * a.num_iters;
+    // Loads under a branch make the compiler wait for each one before the next; every
+    // load here is issued unconditionally from a clamped address and its value selected.
+    auto A_at = [&](int k) {
+        const float v = a.norm_out[((int64_t)(k >= 0 ? k : 0) * T + tt) * NN + e];
+        return (live && k >= 0) ? v : 0.f;
+    };
+    auto s_at = [&](int k) {
+        const float v = a.sum_out[((int64_t)(k >= 0 ? k : 0) * T + tt) * N + ((k & 1) ? ec : er)];
+        return (live && k >= 0) ? v : 1.f;
+    };
+    const float g0 = a.grad_h_res[tt * NN + e];
+    double G = live ? (double)g0 : 0.0;
+    if (steps <= kSkAll) {
+        float A[kSkAll];
+        double R[kSkAll];
+#pragma unroll
+        for (int j = 0; j < kSkAll; ++j) {
+            const int k = steps - 1 - j;
+            A[j] = A_at(k);
+            R[j] = 1.0 / (double)s_at(k);
+        }
+#pragma unroll
+        for (int j = 0; j < kSkAll; ++j) {
+            const int k = steps - 1 - j;
+            if (k >= 1) G = sk_step<N>(G, A[j], R[j], k);   // uniform across the wave
+        }
+    } else {
+        for (int k0 = steps - 1; k0 >= 1; k0 -= kSkChunk) {
+            float A[kSkChunk];
+            double R[kSkChunk];
+#pragma unroll
+            for (int j = 0; j < kSkChunk; ++j) {
+                const int k = k0 - j;
+                A[j] = A_at(k);
+                R[j] = 1.0 / (double)s_at(k);
+            }
+#pragma unroll
+            for (int j = 0; j < kSkChunk; ++j) {
+                const int k = k0 - j;
+                if (k >= 1) G = sk_step<N>(G, A[j], R[j], k);
+            }
+        }
+    }
+    const double P = (double)A_at(0) - a.hc_eps;
+    const double u = sk_row_sum<N>(G * P);
+    if (live) a.glog[t * NN + e] = P * (G - u);
+}
+
 // ------------------------------------------------------------------ token pass
 
 __device__ __forceinline__ double wave_sum(double v)
@@ -132,47 +232,12 @@ bwd_token_kernel(Args a, int64_t T, int D)
     for (int i = 0; i < N; ++i) acc[i] = wave_sum(acc[i]);
     const double eps = a.hc_eps;
 
-    // The residual logits' gradient, one lane per matrix entry e = r N + c. MhcPre:
-    // gradHRes itself. MhcPreSinkhorn: back through the saved planes, last step first: a
-    // column step (k odd) passes G -> (G - sum_r G A_k) / s_k[c], a row step (k even) the
-    // same along the row, the row softmax P (G - rowsum(G P)) with P = A_0 - eps; fp64,
-    // the planes' loads issued eight steps at a time.
+    // The residual logits' gradient, one lane per matrix entry: gradHRes itself (MhcPre),
+    // or what bwd_sinkhorn_kernel passed back through the Sinkhorn planes.
     constexpr int NN = N * N;
     const bool ent = lane < NN;
-    const int er = lane / N, ec = lane % N;
-    double gres = ent ? (double)a.grad_h_res[t * NN + lane] : 0.0;
-    if (a.num_iters > 0) {
-        constexpr int CHUNK = 8;
-        for (int k0 = 2 * a.num_iters - 1; k0 >= 1; k0 -= CHUNK) {
-            float Ak[CHUNK], sk[CHUNK];
-#pragma unroll
-            for (int j = 0; j < CHUNK; ++j) {
-                const int k = k0 - j;
-                const bool on = ent && k >= 1;
-                Ak[j] = on ? a.norm_out[((int64_t)k * T + t) * NN + lane] : 0.f;
-                sk[j] = on ? a.sum_out[((int64_t)k * T + t) * N + ((k & 1) ? ec : er)] : 1.f;
-            }
-#pragma unroll
-            for (int j = 0; j < CHUNK; ++j) {
-                const int k = k0 - j;
-                if (k < 1) break;                 // uniform across the wave
-                double u = gres * (double)Ak[j];
-                if (k & 1) {
-#pragma unroll
-                    for (int off = N; off < NN; off <<= 1) u += __shfl_xor(u, off);
-                } else {
-#pragma unroll
-                    for (int off = 1; off < N; off <<= 1) u += __shfl_xor(u, off);
-                }
-                gres = (gres - u) / (double)sk[j];
-            }
-        }
-        const double P = ent ? (double)a.norm_out[t * NN + lane] - eps : 0.0;
-        double u = gres * P;
-#pragma unroll
-        for (int off = 1; off < N; off <<= 1) u += __shfl_xor(u, off);
-        gres = P * (gres - u);
-    }
+    const double gres = !ent ? 0.0
+                      : (a.num_iters > 0 ? a.glog[t * NN + lane] : (double)a.grad_h_res[t * NN + lane]);
 
     // 3.2-3.5, one lane per phi row m (two passes when MP > 64)
     const double inv = (double)a.inv_rms[t];
@@ -546,6 +611,13 @@ hipError_t launch_all(const Plan& p, const Args& a, hipStream_t st)
                        static_cast<u32x4*>(a.pack), g.n, g.D, g.M, g.KS, units);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.num_iters > 0) {
+        constexpr int tok_per_block = 4 * (64 / (N * N));
+        hipLaunchKernelGGL(bwd_sinkhorn_kernel<N>, dim3((unsigned)((p.T + tok_per_block - 1) / tok_per_block)),
+                           dim3(256), 0, st, a, p.T);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(bwd_token_kernel<N>, dim3((unsigned)p.token_blocks), dim3(256), 0, st, a, p.T, g.D);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

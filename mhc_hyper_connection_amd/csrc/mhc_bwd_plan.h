@@ -19,6 +19,9 @@
 //                sums go to partial buffers.
 //   reduction    gradPhi = gamma (.) sum over groups, gradGamma = sum over groups, gradAlpha
 //                and gradBias = sums over tokens; every sum in a fixed order in fp64.
+//   Sinkhorn     (MhcPreSinkhorn backward only, before the token pass) the residual
+//                logits' gradient through the saved planes, 64 / (n*n) tokens per wave,
+//                into glog [T][n*n] (fp64).
 #pragma once
 
 #include <cstddef>
@@ -115,7 +118,7 @@ struct Plan {
     int64_t main_tasks = 0;   // G * nblk * NSG
     int64_t main_blocks = 0;  // main_tasks rounded up to 16 (see main_task)
     int64_t token_blocks = 0; // ceil(T / 4): one wave per token
-    size_t off_pack = 0, off_gmix = 0, off_c3 = 0, off_terms = 0, off_pphi = 0, off_pgam = 0;
+    size_t off_pack = 0, off_gmix = 0, off_c3 = 0, off_terms = 0, off_pphi = 0, off_pgam = 0, off_glog = 0;
     size_t ws_bytes = 0;
 };
 
@@ -147,6 +150,8 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     off = align_up(off + (size_t)p.G * g.M * g.K * 4, 256);
     p.off_pgam = off;
     off = align_up(off + (size_t)p.G * g.K * 4, 256);
+    p.off_glog = off;
+    off = align_up(off + (size_t)T * g.n * g.n * 8, 256);
     p.ws_bytes = off;
     return p;
 }
@@ -181,6 +186,7 @@ struct Args {
     double* terms;     // [3 + M][T]
     float* pphi;
     float* pgam;
+    double* glog;      // [T][n*n] residual logits' gradient (Sinkhorn backward)
 };
 
 // Implemented in mhc_bwd.hip. Returns 0 or the HIP error code.

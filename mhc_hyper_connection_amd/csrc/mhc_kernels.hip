@@ -341,17 +341,6 @@ __device__ __forceinline__ float res_logit(double h, double inv, float alpha, fl
 // per lane, entry (r, c) in lane n*r + c of an n*n-lane group (16 lanes for n = 4, the
 // whole wave for n = 8). DPP moves within 16-lane rows; the column sums of n = 8 cross
 // rows with lane shuffles. Every lane of a row (column) ends with the same total.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                                 0xF, 0xF, true));
-}
-constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
-constexpr int kRowRor4 = 0x124;
-constexpr int kRowRor8 = 0x128;
-constexpr int kRowHalfMirror = 0x141;
 
 template <int N>
 __device__ __forceinline__ float row_sum(float v)

@@ -86,9 +86,10 @@ static int check(int n, int D, long long T)
     if (pmax >= p.G * (long long)g.M * K) return fail("gradPhi partial index", n, D, T, pmax, 0);
     // workspace sections in order, each large enough, inside ws_bytes
     const size_t need[] = {g.pack_bytes, (size_t)T * g.KS * 3 * 32 * 2, (size_t)T * 4, (size_t)T * (3 + g.M) * 8,
-                           (size_t)p.G * g.M * K * 4, (size_t)p.G * K * 4};
-    const size_t off[] = {p.off_pack, p.off_gmix, p.off_c3, p.off_terms, p.off_pphi, p.off_pgam, p.ws_bytes};
-    for (int s = 0; s < 6; ++s) {
+                           (size_t)p.G * g.M * K * 4, (size_t)p.G * K * 4, (size_t)T * n * n * 8};
+    const size_t off[] = {p.off_pack, p.off_gmix, p.off_c3, p.off_terms, p.off_pphi, p.off_pgam, p.off_glog,
+                          p.ws_bytes};
+    for (int s = 0; s < 7; ++s) {
         if (off[s] % 256) return fail("section alignment", n, D, T, s, off[s]);
         if (off[s] + need[s] > off[s + 1]) return fail("section overlap", n, D, T, s, off[s + 1]);
     }
