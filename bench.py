@@ -37,6 +37,8 @@ KERNEL_SOURCES = ("mhc_hyper_connection_amd/csrc/mhc_kernels.hip",
                   "mhc_hyper_connection_amd/csrc/mhc_plan.h")
 KERNEL_NAMES = {"pack": "prepack_kernel", "projection": "proj_kernel",
                 "epilogue": "epilogue_kernel", "hin": "hin_kernel"}
+# the single-read path runs one kernel in the projection stage and none in the hIn stage
+KERNEL_NAMES_SINGLE_READ = dict(KERNEL_NAMES, projection="fused_kernel", hin="(none)")
 
 
 def algorithmic_bytes(wl, *, intermediates: bool) -> int:
@@ -60,15 +62,17 @@ def algorithmic_bytes(wl, *, intermediates: bool) -> int:
     return b
 
 
-def stage_bytes(wl, stage: str) -> int:
+def stage_bytes(wl, stage: str, single_read: bool = False) -> int:
     """Algorithmic bytes of one launch of a kernel: what that step of the method must
     read and write once. Intermediates of this implementation (packed weights, partial
-    records, the hIn weights) are not counted.
+    records, the hIn weights, the values exchanged between workgroups) are not counted.
       pack        phi (+ gamma) read once: 4MK (+ 4K)
       projection  x read once (2K per token) and phi once (4MK); with pre_mix it also
-                  reads pre_mix (4n per token) and writes hIn (2D per token)
+                  reads pre_mix (4n per token) and writes hIn (2D per token); the
+                  single-read kernel writes hIn too (2D per token)
       epilogue    the per-token outputs: hPost, hRes, and the requested intermediates
-      hin         x read once and hIn written once (2K + 2D per token)"""
+      hin         x read once and hIn written once (2K + 2D per token); nothing on the
+                  single-read path"""
     T, n, D, M, it = wl.T, wl.n, wl.D, wl.M, wl.num_iters
     K = n * D
     if stage == "pack":
@@ -77,6 +81,8 @@ def stage_bytes(wl, stage: str) -> int:
         b = T * 2 * K + M * K * 4
         if wl.pre_mix:
             b += T * n * 4 + T * D * 2
+        elif single_read:
+            b += T * D * 2
         return b
     if stage == "epilogue":
         b = T * n * 4 + (T * n * n * 4 if wl.n_alpha == 3 else 0)
@@ -86,7 +92,7 @@ def stage_bytes(wl, stage: str) -> int:
                 b += 2 * it * T * n * 4 + 2 * it * T * n * n * 4
         return b
     if stage == "hin":
-        return 0 if wl.pre_mix else T * 2 * K + T * D * 2
+        return 0 if wl.pre_mix or single_read else T * 2 * K + T * D * 2
     raise ValueError(stage)
 
 
@@ -98,9 +104,9 @@ def kernel_source_sha() -> str:
     return h.hexdigest()
 
 
-def counter_traffic(stage: str, workload: str):
+def counter_traffic(kernel: str, workload: str):
     """HBM bytes per launch from profiles/<kernel>_<workload>_counters.md, or None."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAMES[stage]}_{workload}_counters.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
     if not os.path.exists(path):
         return None, "no counter summary"
     vals = {}
@@ -307,6 +313,8 @@ def main():
                          need_backward=wl.need_backward, device=dev)
     out = run.alloc_outputs()
     stream = torch.cuda.current_stream(dev)
+    single_read = run.path(pre_mix is not None) == 1
+    names = KERNEL_NAMES_SINGLE_READ if single_read else KERNEL_NAMES
 
     if args.calib_copy_mib > 0:
         print(f"[bench] calibration copy {args.calib_copy_mib} MiB", file=sys.stderr, flush=True)
@@ -338,14 +346,14 @@ def main():
     kernels = {}
     for i, stage in enumerate(mhc.STAGES):
         ms = [row[i].elapsed_time(row[i + 1]) for row in evs]
-        kernels[stage] = {"kernel": KERNEL_NAMES[stage], "avg_us": 1e3 * sum(ms) / len(ms),
+        kernels[stage] = {"kernel": names[stage], "avg_us": 1e3 * sum(ms) / len(ms),
                           "min_us": 1e3 * min(ms),
-                          "algorithmic_bytes": stage_bytes(wl, stage)}
+                          "algorithmic_bytes": stage_bytes(wl, stage, single_read)}
     call_us = [1e3 * row[0].elapsed_time(row[-1]) for row in evs]
     dom = max(kernels, key=lambda s: kernels[s]["avg_us"])
     kd = kernels[dom]
     achieved = kd["algorithmic_bytes"] / (kd["avg_us"] * 1e-6) / 1e9
-    traffic, traffic_src = counter_traffic(dom, wl.name)
+    traffic, traffic_src = counter_traffic(names[dom], wl.name)
     b_call = algorithmic_bytes(wl, intermediates=wl.need_backward)
     call_avg = sum(call_us) / len(call_us)
 
@@ -365,6 +373,7 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "n": wl.n, "D": wl.D, "n_alpha": wl.n_alpha,
                    "gamma": wl.gamma, "pre_mix": wl.pre_mix, "need_backward": wl.need_backward,
                    "num_iters": wl.num_iters,
+                   "path": "single-read" if single_read else "four-kernel",
                    "step": "weight pack + forward (one mhc_pre_forward call, unpacked phi)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

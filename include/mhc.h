@@ -126,9 +126,12 @@ const char* mhc_status_string(mhc_status status);
 mhc_status mhc_pre_packed_size(const mhc_pre_params* params, size_t* bytes);
 
 /* Bytes of device workspace mhc_pre_forward needs for this problem. Host only.
- * The workspace holds per-call intermediate results only (partial sums and the hIn
- * weights; no state carries over between calls), so it needs no initialisation.
- * Concurrent calls need distinct workspaces. Errors: NULLPTR, PARAM_INVALID. */
+ * The workspace holds per-call intermediate results (partial sums, the hIn weights, the
+ * values workgroups of the single-read kernel exchange) and, in its first 256 bytes, a
+ * call counter that tags those exchanged values with the call that wrote them. Zero-fill
+ * it once after allocating it and then leave it to the library; it may serve calls of
+ * any size that fit it, one at a time. Concurrent calls need distinct workspaces.
+ * Errors: NULLPTR, PARAM_INVALID. */
 mhc_status mhc_pre_workspace_size(const mhc_pre_params* params, size_t* bytes);
 
 /* Packs phi (f32 [M, n*D]) and the optional gamma (f32 [n, D]) into phi_packed
@@ -141,13 +144,30 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
 
 /* The forward, asynchronous on `stream` (a hipStream_t; NULL = default stream). Emits
  * every non-NULL output listed in mhc_pre_tensors. `workspace` is device memory of at
- * least mhc_pre_workspace_size bytes, 256-byte aligned. When tensors->phi_packed is NULL
- * the weights are packed into the workspace first (one extra kernel). Then a projection
- * kernel (which with pre_mix also writes hIn), a per-token epilogue and, without pre_mix,
- * an hIn kernel. Results are bitwise reproducible for the same inputs and parameters.
+ * least mhc_pre_workspace_size bytes, 256-byte aligned, zero-filled before its first use.
+ * When tensors->phi_packed is NULL the weights are packed into the workspace first (one
+ * extra kernel). Then one of two kernel sequences (mhc_pre_forward_path tells which):
+ *   four-kernel path: a projection kernel (which with pre_mix also writes hIn), a
+ *     per-token epilogue and, without pre_mix, an hIn kernel (x is read twice);
+ *   single-read path (n == 4, n_alpha == 3, no pre_mix, 992 < D <= 7168 (32 to 224
+ *     blocks of 32 positions), T >= 8192, not while
+ *     the stream is capturing a graph): one cooperative kernel computes the projection,
+ *     hPre and hIn, x read once, then the per-token epilogue. It occupies every compute
+ *     unit until done; its workgroups wait on each other, each wait bounded (a wait that
+ *     times out leaves NaN in hIn for the tokens concerned).
+ * The two paths sum the projection's partial products in different groupings, so their
+ * outputs may differ in the last bits; each meets the same accuracy. Within a call, hIn
+ * uses exactly the hPre it emits. Results are bitwise reproducible for the same inputs,
+ * parameters and path. The environment variable MHC_FORWARD_PATH = "classic" or
+ * "fused" (for tests) overrides the choice where the single-read kernel can run.
  * Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
 mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Which path mhc_pre_forward would take for these parameters on the current device:
+ * *path = 1 the single-read kernel, 0 the four-kernel path (has_pre_mix: whether pre_mix
+ * will be given). Errors: NULLPTR, PARAM_INVALID. */
+mhc_status mhc_pre_forward_path(const mhc_pre_params* params, int32_t has_pre_mix, int32_t* path);
 
 /* Events mhc_pre_forward_timed records: one before the first kernel and one after each
  * of the forward's four kernels. */

@@ -16,6 +16,7 @@ import math
 
 from ._binding import (FORWARD_EVENTS, MHC_ERR_NULLPTR, MHC_ERR_PARAM_INVALID,
                        MHC_ERR_RUNTIME, MHC_OK, STAGES, MhcError, Params, bwd_workspace_size,
+                       forward_path,
                        load, make_bwd_params, make_params, packed_size, raw_backward,
                        raw_forward, raw_forward_timed, raw_prepack, status_string, version,
                        workspace_size)
@@ -79,7 +80,12 @@ class PreForward:
         self.params = make_params(T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward)
         self.ws_bytes = workspace_size(self.params)
         self.packed_bytes = packed_size(self.params)
-        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+        # zero-filled once: its first bytes hold the call counter the library keeps
+        self.workspace = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
+
+    def path(self, has_pre_mix=False):
+        """1 when calls take the single-read kernel on this device, else 0."""
+        return forward_path(self.params, has_pre_mix)
 
     # -- outputs -----------------------------------------------------------------------
     def alloc_outputs(self, *, intermediates=None):

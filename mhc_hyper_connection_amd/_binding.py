@@ -56,7 +56,8 @@ class BwdTensors(ctypes.Structure):
 
 EXPORTS = ("mhc_version", "mhc_status_string", "mhc_pre_packed_size",
            "mhc_pre_workspace_size", "mhc_pre_prepack", "mhc_pre_forward",
-           "mhc_pre_forward_timed", "mhc_pre_backward_workspace_size", "mhc_pre_backward")
+           "mhc_pre_forward_timed", "mhc_pre_forward_path", "mhc_pre_backward_workspace_size",
+           "mhc_pre_backward")
 
 # MHC_FORWARD_EVENTS: events of mhc_pre_forward_timed (before the first kernel, then one
 # after each of pack, projection, epilogue, hIn)
@@ -97,6 +98,8 @@ def load(path: str | None = None):
     lib.mhc_pre_backward_workspace_size.restype = ctypes.c_int32
     lib.mhc_pre_backward_workspace_size.argtypes = [ctypes.POINTER(BwdParams), ctypes.POINTER(ctypes.c_size_t)]
     lib.mhc_pre_backward.restype = ctypes.c_int32
+    lib.mhc_pre_forward_path.restype = ctypes.c_int32
+    lib.mhc_pre_forward_path.argtypes = [ctypes.POINTER(Params), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.mhc_pre_backward.argtypes = [ctypes.POINTER(BwdParams), ctypes.POINTER(BwdTensors),
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     if path is None:
@@ -131,6 +134,15 @@ def workspace_size(params: Params) -> int:
     st = load().mhc_pre_workspace_size(ctypes.byref(params), ctypes.byref(out))
     if st != MHC_OK:
         raise MhcError(st, "mhc_pre_workspace_size")
+    return int(out.value)
+
+
+def forward_path(params: Params, has_pre_mix: bool) -> int:
+    """1 when mhc_pre_forward takes the single-read kernel on the current device, else 0."""
+    out = ctypes.c_int32(0)
+    st = load().mhc_pre_forward_path(ctypes.byref(params), int(bool(has_pre_mix)), ctypes.byref(out))
+    if st != MHC_OK:
+        raise MhcError(st, "mhc_pre_forward_path")
     return int(out.value)
 
 

@@ -72,6 +72,17 @@ mhc_status mhc_pre_workspace_size(const mhc_pre_params* params, size_t* bytes)
     return MHC_OK;
 }
 
+mhc_status mhc_pre_forward_path(const mhc_pre_params* params, int32_t has_pre_mix, int32_t* path)
+{
+    if (!params || !path) return MHC_ERR_NULLPTR;
+    mhc::Geometry g;
+    mhc_status st = check_params(params, &g);
+    if (st != MHC_OK) return st;
+    if (params->T < 0) return MHC_ERR_PARAM_INVALID;
+    *path = mhc::forward_path(mhc::make_plan(g, params->T), has_pre_mix != 0);
+    return MHC_OK;
+}
+
 mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const float* gamma,
                            void* phi_packed, size_t packed_bytes, void* stream)
 {
@@ -162,6 +173,9 @@ mhc_status forward_impl(const mhc_pre_params* params, const mhc_pre_tensors* t,
     a.norm_out = res_branch ? t->norm_out : nullptr;
     a.wts = reinterpret_cast<float*>(ws + plan.off_wts);
     a.rec = reinterpret_cast<float*>(ws + plan.off_rec);
+    a.prx = plan.fused_geom ? reinterpret_cast<uint64_t*>(ws + plan.off_prx) : nullptr;
+    a.hpx = plan.fused_geom ? reinterpret_cast<uint64_t*>(ws + plan.off_hpx) : nullptr;
+    a.sync = reinterpret_cast<uint32_t*>(ws + plan.off_sync);
     a.num_iters = params->num_iters;
     a.norm_eps = params->norm_eps;
     a.hc_eps = params->hc_eps;

@@ -23,9 +23,16 @@
 //                    planes (one lane per matrix entry, sums across lanes by DPP) and,
 //                    without pre_mix, the hIn weights.
 //   hin_kernel       without pre_mix: hIn[t, d] = sum_i hPre[t, i] x[t, i, d].
+//   fused_kernel     the single-read path (n = 4, alpha[3], no pre_mix, large T), in place
+//                    of proj_kernel and hin_kernel: one cooperative launch whose workgroups
+//                    keep their weights in LDS and each tile's x in registers until its hPre
+//                    (summed by a designated workgroup, exchanged through tagged words) is
+//                    known, so x is read once; the epilogue follows.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "mhc_device.h"
 #include "mhc_plan.h"
@@ -440,6 +447,8 @@ epilogue_kernel(KArgs k)
     const int tl0 = (int)(tf % kTileTokens);
     if (tid < A) gpar[tid] = a.alpha[tid];
     for (int i = tid; i < M; i += kThreads) gpar[3 + i] = a.bias[i];
+    // the epilogue is the call's last reader of the counter's value: the next call's tag
+    if (blockIdx.x == 0 && tid == 0) a.sync[0] = a.sync[0] + 1u;
 
     const rsrc_t rec = make_rsrc(a.rec + rec_tile(tile, k.S, N, M), (int64_t)k.S * kTileTokens * V * 4);
     const int items = nb * k.NG * CH;
@@ -538,6 +547,375 @@ hin_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wts,
     __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(h_in + t * (int64_t)D + d8 * 8));
 }
 
+// ------------------------------------------------------------------ single-read forward
+
+// A 64-bit word carrying a value and the tag of the call that wrote it; written and read
+// as one relaxed device-scope atomic, so a reader sees either an older word or the whole
+// new one, on whatever XCD it runs.
+__device__ __forceinline__ void put_tagged(uint64_t* p, uint32_t tag, float v)
+{
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t get_tagged(const uint64_t* p)
+{
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool tag_is(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+__device__ __forceinline__ float tagged_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+constexpr int kSpinLimit = 1 << 18;   // polls of global memory before a wait gives up (about 0.3 s)
+constexpr int kLdsSpinLimit = 1 << 24;   // polls of an LDS word (a guard: these waits end by construction)
+
+// x loads for the register ring, issued from inline assembly: the compiler's own wait
+// insertion cannot follow loads whose registers are consumed several iterations of a
+// loop later (it drains them every iteration), so these loads are invisible to it and
+// the kernel waits for them explicitly (wait_vm_only, ring_ready). A ring register is read
+// only after its wait; every load issued is consumed, so none lands in a register the compiler
+// has given to something else.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 raw_desc(const void* base, uint32_t bytes)
+{
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int32_t)(uint32_t)p, (int32_t)((uint32_t)(p >> 32) & 0xffffu), (int32_t)bytes, kRsrcWord3};
+}
+__device__ __forceinline__ u32x4 load_ring(i32x4 desc, uint32_t off)
+{
+    u32x4 v;
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v) : "v"(off), "s"(desc) : "memory");
+    return v;
+}
+// s_waitcnt vmcnt(K) alone (no register operands: the count may depend on a branch, and
+// a register operand inside a branch makes the compiler copy the register, unloaded, to
+// merge the branches); then ring_ready, an empty statement tied to the four registers, so
+// that no read of them moves above the wait.
+template <int K>
+__device__ __forceinline__ void wait_vm_only()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(K) : "memory");
+}
+__device__ __forceinline__ void ring_ready(u32x4 (&v)[4])
+{
+    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]) : : "memory");
+}
+
+struct FArgs {
+    ForwardArgs a;
+    int64_t T;
+    int64_t K;
+    int64_t tiles16;
+    int D;
+    int nblk;
+    int G;       // groups (of kFMembers members)
+};
+
+// One workgroup = member s of group g (blockIdx = s G + g). Waves 0 .. 6 compute: wave w
+// owns d-block member_begin + w and, for a tile of 16 tokens, its n K-steps (the n streams
+// of the block), so a lane holds the n streams of one octet and hIn is local to it. Wave 7
+// is the control wave: it alone waits on other workgroups. Round r of the group is tile
+// r G + g. Per round (one workgroup barrier, at its middle):
+//   compute waves: project the round's tile (x loaded kFAhead rounds ago), fold each phi
+//     row's hi, mid and lo sums and put them in LDS; hIn of the tile of round r - kFLag
+//     from the registers still holding its x and the hPre the control wave placed in LDS;
+//     then the x loads of round r + kFAhead into the registers just freed.
+//   control wave: the hPre of round r + 1 - kFLag (polled last round) into LDS; if this
+//     member is designated for round r - 2 (designated = round mod P), sums the pre-branch
+//     records of that tile (loaded last round) in the epilogue's order and publishes its
+//     hPre; if designated for round r - 1, loads that tile's records; polls the hPre of
+//     round r + 2 - kFLag.
+//   barrier
+//   compute waves: one value each of the tile's partial record (totals over the waves),
+//     stored for the epilogue and, for the pre sums and the square, tagged for the
+//     designated member.
+// Every wait at round r is for work other members finish by their round r - 1, so with
+// all workgroups resident (cooperative launch) the waits end; a wait that does not end
+// within kSpinLimit polls sets sync[1] and yields NaN hPre for that tile.
+template <int N, int A>
+__global__ void __launch_bounds__(kFThreads, 1)
+fused_kernel(FArgs f)
+{
+    using C = Cfg<N, A>;
+    constexpr int M = C::M, NT = C::NT, NC = C::NC, PPS = C::PPS, V = C::V, CH = C::CH;
+    constexpr int NCL = 3 * M;                 // packed columns kept in LDS
+    constexpr int NW = kFMaxBlocks;            // compute waves
+    constexpr int CTRL = kFWaves - 1;
+    static_assert(N == 4 && A == 3, "single-read kernel: n = 4 with alpha[3]");
+    static_assert(NW == CTRL, "one compute wave per d-block, then the control wave");
+    constexpr int P = kFMembers;               // members per group
+    constexpr int GS = (P + 7) / 8;            // the epilogue's summation groups over members
+    static_assert(P % GS == 0, "whole summation groups");
+    static_assert(NT == 5 && NCL == 72 && M == 24, "column pairing of hi, mid and lo below");
+    static_assert(kFTok * V == 64 * NW, "one record value per compute lane");
+    __shared__ u32x4 wl[NW * N * 4 * NCL];        // the member's packed weights
+    __shared__ float part[2][NW][kFTok][M];      // each compute wave's row sums, by round parity
+    __shared__ float part_sq[2][NW][kFTok];      // and its squares
+    constexpr int NS = 4;                        // hPre slots handed from the control wave
+    __shared__ float hp_lds[NS][kFTok * N];
+    __shared__ uint32_t hp_flag[NS];             // 1 + the round whose hPre the slot holds
+    __shared__ uint32_t cbar;                    // compute-wave arrivals (NW per round)
+    const ForwardArgs& a = f.a;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int j = lane & 15, grp = lane >> 4;
+    const int g = (int)(blockIdx.x % f.G), s = (int)(blockIdx.x / f.G);
+    const int b_lo = member_begin(s, f.nblk, P);
+    const int nb = member_begin(s + 1, f.nblk, P) - b_lo;
+    const int64_t R = g < f.tiles16 ? (f.tiles16 - g + f.G - 1) / f.G : 0;   // rounds of group g
+    const uint32_t tag = (f.a.sync[0] << 1) | 1u;
+
+    {   // the member's K-steps of the packed weights, without the zero columns past 3M
+        const u32x4* src = static_cast<const u32x4*>(a.packed) + (int64_t)b_lo * N * 4 * NC;
+        const int units = nb * N * 4 * NCL;
+        for (int u = tid; u < units; u += kFThreads) wl[u] = src[(int64_t)(u / NCL) * NC + u % NCL];
+    }
+    if (tid < NS) hp_flag[tid] = 0u;
+    if (tid == 0) cbar = 0u;
+    __syncthreads();   // the only barrier of all eight waves
+    // LDS words the waves poll: relaxed atomics; asm statements with a memory clobber keep
+    // the compiler from moving other LDS accesses across them (a wave's LDS operations
+    // execute in order)
+    auto lds_get = [](uint32_t* w) { return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); };
+    auto wait_lds_at_least = [&](uint32_t* w, uint32_t target) {
+        for (int it = 0; lds_get(w) < target && it < kLdsSpinLimit; ++it) __builtin_amdgcn_s_sleep(1);
+        asm volatile("" : : : "memory");
+    };
+
+    if (wave != CTRL) {
+        const bool has_blk = wave < nb;
+        const int b = b_lo + wave;
+        const bool oct_ok = has_blk && kBlock * b + 8 * grp < f.D;
+        const uint32_t xo = (uint32_t)(((int64_t)j * f.K + kBlock * b + 8 * grp) * 2);
+        const uint32_t ho = (uint32_t)(((int64_t)j * f.D + kBlock * b + 8 * grp) * 2);
+        const u32x4* wb = wl + wave * N * 4 * NCL + grp * NCL;
+        u32x4 xr[kFRing][N];
+        // x of round q (tile q G + g) into dst; only rounds < R and waves with a block
+        // load, so the untracked loads in flight are exactly those of the next rounds
+        auto load_round = [&](int64_t q, u32x4 (&dst)[N]) {
+            const int64_t t0 = (q * f.G + g) * kFTok;
+            const int64_t nt = f.T - t0 < kFTok ? f.T - t0 : kFTok;
+            const i32x4 desc = raw_desc(a.x + t0 * f.K, (uint32_t)(nt * f.K * 2));
+#pragma unroll
+            for (int i = 0; i < N; ++i) dst[i] = load_ring(desc, xo + 2 * (uint32_t)f.D * i);
+        };
+        static_assert(N == 4 && kFAhead == 2, "wait counts: four loads per round, one younger round");
+        if (has_blk) {
+#pragma unroll
+            for (int q = 0; q < kFAhead; ++q)
+                if (q < R) load_round(q, xr[q]);
+        }
+
+        // One barrier per round (B). Partial sums alternate between two LDS buffers by
+        // round parity: a wave writes buffer r & 1 in round r only after every wave has
+        // passed barrier r - 1, so after every read of round r - 2's sums; the hPre slot
+        // the compute waves read in round r was written before barrier r - 1 and is
+        // rewritten only after barrier r.
+        for (int64_t r0 = 0; r0 < R + kFLag; r0 += kFRing) {
+#pragma unroll
+            for (int u = 0; u < kFRing; ++u) {
+                const int64_t r = r0 + u;
+                if (r >= R + kFLag) break;
+                const int pb = (int)(r & 1);
+                if (r < R && has_blk) {
+                    // this round's x: the loads issued after it are those of the next
+                    // kFAhead - 1 rounds, where they exist
+                    if (r + 1 < R) wait_vm_only<N>();
+                    else wait_vm_only<0>();
+                    ring_ready(xr[u]);
+                    f32x4 acc[NT];
+                    f32x4 sq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    // the weight operands from LDS two K-steps at a time, all issued before
+                    // their first product (columns past 3M feed only output columns nobody
+                    // reads: any in-bounds LDS column serves)
+#pragma unroll
+                    for (int i0 = 0; i0 < N; i0 += 2) {
+                        u32x4 bw[2][NT];
+#pragma unroll
+                        for (int di = 0; di < 2; ++di)
+#pragma unroll
+                            for (int nt = 0; nt < NT; ++nt) {
+                                const int col = 16 * nt + j < NCL ? 16 * nt + j : 16 * nt + j - 16;
+                                bw[di][nt] = wb[(i0 + di) * 4 * NCL + col];
+                            }
+                        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
+#pragma unroll
+                        for (int di = 0; di < 2; ++di) {
+                            const u32x4 z = {0u, 0u, 0u, 0u};
+                            const bf16x8 Av = __builtin_bit_cast(bf16x8, oct_ok ? xr[u][i0 + di] : z);
+                            sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Av, sq, 0, 0, 0);
+#pragma unroll
+                            for (int nt = 0; nt < NT; ++nt)
+                                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    Av, __builtin_bit_cast(bf16x8, bw[di][nt]), acc[nt], 0, 0, 0);
+                        }
+                    }
+                    // phi row m's hi, mid and lo are columns m, M + m, 2M + m: for lane j of
+                    // a 16-lane row, row j (and 16 + j when j < 8) takes its mid term from
+                    // lane (j + 8) mod 16; the three are added in fp64 and rounded once
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int t = 4 * grp + q;
+                        const float m1 = dpp<kRowRor8>(acc[1][q]), m2 = dpp<kRowRor8>(acc[2][q]);
+                        if (j < 8) {
+                            part[pb][wave][t][j] = (float)((double)acc[0][q] + (double)m1 + (double)acc[3][q]);
+                            part[pb][wave][t][16 + j] = (float)((double)acc[1][q] + (double)m2 + (double)acc[4][q]);
+                        } else {
+                            part[pb][wave][t][j] = (float)((double)acc[0][q] + (double)m2 + (double)acc[3][q]);
+                        }
+                    }
+                    const int rr = j - 4 * grp;
+                    if (rr >= 0 && rr < 4) part_sq[pb][wave][j] = sq[rr];
+                }
+                // hIn of round r - kFLag from the registers that still hold its x
+                const int us = (u + kFAhead) % kFRing;
+                const int64_t rh = r - kFLag;
+                if (rh >= 0 && has_blk) {
+                    const int64_t t0 = (rh * f.G + g) * kFTok;
+                    const int64_t nt = f.T - t0 < kFTok ? f.T - t0 : kFTok;
+                    wait_lds_at_least(&hp_flag[rh % NS], (uint32_t)rh + 1u);   // the control wave's hand-over
+                    float w[N];
+#pragma unroll
+                    for (int i = 0; i < N; ++i) w[i] = hp_lds[rh % NS][j * N + i];
+                    float hacc[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hacc[e] = 0.f;
+#pragma unroll
+                    for (int i = 0; i < N; ++i) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            hacc[2 * e] = fmaf(w[i], bf16_lo(xr[us][i][e]), hacc[2 * e]);
+                            hacc[2 * e + 1] = fmaf(w[i], bf16_hi(xr[us][i][e]), hacc[2 * e + 1]);
+                        }
+                    }
+                    u32x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(hacc[2 * e], hacc[2 * e + 1]);
+                    const rsrc_t hres = make_rsrc(a.h_in + t0 * f.D, nt * f.D * 2);
+                    __builtin_amdgcn_raw_buffer_store_b128(o, hres, (int)(oct_ok ? ho : kOutOfRange), 0, 0);
+                }
+                if (has_blk && r + kFAhead < R) load_round(r + kFAhead, xr[us]);
+                // barrier of the compute waves: every wave's sums of this round are in LDS
+                asm volatile("" : : : "memory");
+                if (lane == 0) __hip_atomic_fetch_add(&cbar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                wait_lds_at_least(&cbar, (uint32_t)(NW * (r + 1)));
+
+                if (r < R) {
+                    // one value of the tile's partial record per compute lane: token t,
+                    // record value v (the n pre sums, the square, padding, the other
+                    // M - n sums), summed over the compute waves in wave order
+                    const int L = wave * 64 + lane;
+                    const int t = L / V, v = L % V;
+                    const int m = v < N ? v : (v < PPS ? 0 : N + (v - PPS));   // square / padding: row 0, unused
+                    float qv[NW], qs[NW];
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {   // all reads first, then the sums
+                        qv[w] = part[pb][w][t][m];
+                        qs[w] = part_sq[pb][w][t];
+                    }
+                    double hsum = 0.0;
+                    float ssum = 0.f;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {
+                        hsum += w < nb ? (double)qv[w] : 0.0;
+                        ssum += w < nb ? qs[w] : 0.f;
+                    }
+                    const float val = v == N ? ssum : (v > N && v < PPS) ? 0.f : (float)hsum;
+                    const int64_t jt = r * f.G + g;
+                    const int64_t t0 = jt * kFTok;
+                    const int ntile = (int)(f.T - t0 < kFTok ? f.T - t0 : kFTok);
+                    // the epilogue's record layout: slice = member, 64-token tiles
+                    const rsrc_t rec = make_rsrc(a.rec + rec_tile(jt / 4, P, N, M), (int64_t)P * kTileTokens * V * 4);
+                    const int tl = kFTok * (int)(jt % 4) + t;
+                    st_buf(rec, t < ntile ? (uint32_t)(rec_loc(s, tl, N, M) + v) * 4 : kOutOfRange, val);
+                    // the tagged pre-branch sums and square for the designated member
+                    if (v <= N) put_tagged(a.prx + prx_at(jt, P, s, t, v, N), tag, val);
+                }
+            }
+        }
+    } else {
+        // control wave
+        const int tq = lane / N, iq = lane % N;   // (token, stream) of this lane's hPre word
+        bool failed = false;
+        auto fail = [&]() {
+            if (!failed && lane == 0)
+                __hip_atomic_store(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            failed = true;
+        };
+        uint64_t pre[P], pss[P];
+        auto load_records = [&](int64_t jt) {
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                pre[q] = get_tagged(a.prx + prx_at(jt, P, q, tq, iq, N));
+                pss[q] = get_tagged(a.prx + prx_at(jt, P, q, tq, N, N));
+            }
+        };
+        auto records_ready = [&]() {
+            bool ok = true;
+#pragma unroll
+            for (int q = 0; q < P; ++q) ok &= tag_is(pre[q], tag) & tag_is(pss[q], tag);
+            return __all(ok);
+        };
+        const float alpha0 = a.alpha[0];
+        const float bias_i = a.bias[iq];
+        const float eps = (float)a.hc_eps;
+        // Iteration k: the designated duty for tile round k, then the hand-over of round
+        // k - 2's hPre. Both wait first for the compute waves to pass their barrier of
+        // round k + 1, i.e. to have stored their records of round k (the other members'
+        // are then nearly always visible too); the hand-over slot's previous round
+        // (k - 2 - NS) was consumed in compute round k - 2 - NS + kFLag <= k + 1. The
+        // compute waves need round k - 2's hPre only in their round k - 2 + kFLag.
+        static_assert(kFLag >= 5 && NS >= 4, "the hand-over comes at least one round before its use");
+        for (int64_t k = 0; k < R + 2; ++k) {
+            wait_lds_at_least(&cbar, (uint32_t)(NW * (k + 2 < R + kFLag ? k + 2 : R + kFLag)));
+            if (k < R && k % P == s) {
+                const int64_t jt = k * f.G + g;
+                load_records(jt);
+                bool ok = records_ready();
+                for (int it = 0; !ok && !failed; ++it) {
+                    if (it == kSpinLimit) { fail(); break; }
+                    __builtin_amdgcn_s_sleep(2);
+                    load_records(jt);
+                    ok = records_ready();
+                }
+                // the epilogue's order: members in groups of GS, each group in member
+                // order from 0.0, then the group totals in order from 0.0
+                double hs = 0.0, ss = 0.0;
+#pragma unroll
+                for (int q0 = 0; q0 < P; q0 += GS) {
+                    double ga = 0.0, gb = 0.0;
+#pragma unroll
+                    for (int q = q0; q < q0 + GS; ++q) {
+                        ga += (double)tagged_value(pre[q]);
+                        gb += (double)tagged_value(pss[q]);
+                    }
+                    hs += ga;
+                    ss += gb;
+                }
+                const double inv = inv_rms_of(ss, (double)f.K, a.norm_eps);
+                const float hp = ok ? gate_pre(hs, inv, alpha0, bias_i, eps) : __builtin_nanf("");
+                put_tagged(a.hpx + hpx_at(jt, tq, iq, N), tag, hp);
+            }
+            const int64_t rp = k - 2;
+            if (rp >= 0 && rp < R) {
+                const uint64_t* src = a.hpx + hpx_at(rp * f.G + g, tq, iq, N);
+                uint64_t w = get_tagged(src);
+                bool ok = tag_is(w, tag);
+                for (int it = 0; !__all(ok) && !failed; ++it) {
+                    if (it == kSpinLimit) { fail(); break; }
+                    __builtin_amdgcn_s_sleep(2);
+                    w = get_tagged(src);
+                    ok = tag_is(w, tag);
+                }
+                hp_lds[rp % NS][lane] = ok ? tagged_value(w) : __builtin_nanf("");
+                asm volatile("" : : : "memory");
+                if (lane == 0) __hip_atomic_store(&hp_flag[rp % NS], (uint32_t)rp + 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+    }
+}
+
 // Records events[i] (a caller-created hipEvent_t) on the stream when events is given.
 hipError_t mark(void* const* events, int i, hipStream_t st)
 {
@@ -565,7 +943,71 @@ hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st, void* con
     return e == hipSuccess ? mark(events, kStageHin + 1, st) : e;
 }
 
+// Groups of the single-read kernel on the current device, 0 when it cannot run here.
+int fused_groups(const Plan& p)
+{
+    int dev = 0, coop = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<4, 3>, kFThreads, 0) != hipSuccess ||
+        per_cu < 1)
+        return 0;
+    int64_t G = (int64_t)cus * per_cu / p.FP;
+    if (G > p.tiles16) G = p.tiles16;
+    return (int)G;
+}
+
+bool fused_wanted(const Plan& p, bool has_pre_mix)
+{
+    if (!p.fused_geom || has_pre_mix || p.T <= 0) return false;
+    const char* env = std::getenv("MHC_FORWARD_PATH");
+    if (env && std::strcmp(env, "classic") == 0) return false;
+    const bool forced = env && std::strcmp(env, "fused") == 0;
+    return forced || p.T >= kFMinTokens;
+}
+
+// *launched is false when the cooperative launch itself was refused (nothing ran).
+hipError_t launch_fused(const Plan& p, const ForwardArgs& a, int G, hipStream_t st, void* const* events,
+                        bool* launched)
+{
+    FArgs f;
+    f.a = a;
+    f.T = p.T;
+    f.K = p.g.K;
+    f.tiles16 = p.tiles16;
+    f.D = p.g.D;
+    f.nblk = p.g.nblk;
+    f.G = G;
+    void* args[] = {&f};
+    hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fused_kernel<4, 3>),
+                                              dim3((unsigned)(G * p.FP)), dim3(kFThreads), args, 0, st);
+    if (e == hipSuccess) e = hipGetLastError();
+    *launched = e == hipSuccess;
+    if (e == hipSuccess) e = mark(events, kStageProj + 1, st);
+    if (e != hipSuccess) return e;
+    KArgs k;
+    k.a = a;
+    k.T = p.T;
+    k.K = p.g.K;
+    k.tiles = p.tiles;
+    k.D = p.g.D;
+    k.S = p.FP;
+    k.GS = p.FGS;
+    k.NG = p.FNG;
+    hipLaunchKernelGGL((epilogue_kernel<4, 3>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark(events, kStageEpi + 1, st);
+    if (e == hipSuccess) e = mark(events, kStageHin + 1, st);
+    return e;
+}
+
 }  // namespace
+
+int forward_path(const Plan& p, bool has_pre_mix)
+{
+    return fused_wanted(p, has_pre_mix) && fused_groups(p) > 0 ? 1 : 0;
+}
 
 int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void* packed,
                    void* stream)
@@ -595,6 +1037,18 @@ int launch_forward(const Plan& p, const ForwardArgs& a, void* stream, void* cons
     k.S = p.S;
     k.GS = p.GS;
     k.NG = p.NG;
+    if (fused_wanted(p, a.pre_mix != nullptr)) {
+        // a cooperative launch is not taken into a graph being captured: the four-kernel
+        // path serves then
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        const int G = fused_groups(p);
+        if (G > 0 && hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) {
+            bool launched = false;
+            const hipError_t e = launch_fused(p, a, G, st, events, &launched);
+            if (launched) return (int)e;
+            (void)hipGetLastError();   // refused: the four-kernel path below serves
+        }
+    }
     const int n = p.g.n, na = p.g.n_alpha, nks = p.NKS;
     const Variant v = variant_of(n, na);
     if (n == 4 && na == 3 && (v.nt != Cfg<4, 3>::NT || v.sk != Cfg<4, 3>::SK)) return (int)hipErrorInvalidValue;

@@ -12,6 +12,14 @@
 //   Each task writes a partial record per token; a per-token epilogue sums the S records
 //   of a token and computes every other output; without pre_mix a last pass computes hIn
 //   from the epilogue's hPre.
+//   Single-read variant (n = 4, alpha[3], no pre_mix, 32 to 224 d-blocks): the
+//   workgroups form G groups of P members; member s of a group keeps the packed weights
+//   of its run of d-blocks in LDS for the whole call, and the group walks its tiles of 16
+//   tokens in rounds. Each round a member projects one tile (one d-block per compute
+//   wave), writes its partial record and, tagged for this call, the record's pre-branch
+//   sums and square; the tile's designated member (round mod P) sums those, publishes
+//   hPre, and every member computes its share of hIn from the x it still holds in
+//   registers kFLag rounds later. x is read from HBM once.
 //
 // Reduction order ("K-steps")
 //   Positions are grouped in d-blocks of 32 (four octets of 8 bf16). K-step k = (block
@@ -49,6 +57,17 @@ constexpr int kMaxN = 8;
 constexpr int64_t kBigTasks = 1024;    // prefer the large slice when it still gives this many tasks
 constexpr int kMaxSlices = 256;        // slices per tile
 constexpr int kOutTokens = 8;          // tokens per epilogue workgroup
+
+// Single-read kernel (see above).
+constexpr int kFTok = 16;              // tokens per tile
+constexpr int kFMembers = 32;          // members per group
+constexpr int kFMaxBlocks = 7;         // d-blocks per member: one per compute wave
+constexpr int kFWaves = 8;             // 7 compute waves + 1 control wave
+constexpr int kFThreads = 64 * kFWaves;
+constexpr int kFRing = 8;              // x register slots, one per round
+constexpr int kFAhead = 2;             // rounds between a tile's x loads and its projection
+constexpr int kFLag = kFRing - kFAhead;   // rounds between a tile's projection and its hIn
+constexpr int64_t kFMinTokens = 8192;  // below this the four-kernel path is used (ramp and drain dominate)
 
 struct Geometry {
     int n = 0;
@@ -142,6 +161,12 @@ struct Plan {
     int64_t tasks = 0;        // tiles * S
     int64_t proj_blocks = 0;  // projection workgroups (tasks plus padding, see task_of_block)
     int64_t out_blocks = 0;   // epilogue workgroups: ceil(T / kOutTokens)
+    // single-read variant
+    bool fused_geom = false;  // the geometry admits it (n = 4, alpha[3], <= 7 blocks per member)
+    int FP = 0;               // members per group
+    int FGS = 0, FNG = 0;     // summation groups over the FP member records (as GS, NG)
+    int64_t tiles16 = 0;      // ceil(T / 16)
+    size_t off_prx = 0, off_hpx = 0, off_sync = 0;
     size_t off_packed = 0, off_wts = 0, off_rec = 0, ws_bytes = 0;
 };
 
@@ -163,13 +188,28 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     p.tasks = p.tiles * p.S;
     p.proj_blocks = proj_blocks(p.tiles, p.S);
     p.out_blocks = (T + kOutTokens - 1) / kOutTokens;
+    p.FP = kFMembers;
+    p.fused_geom = g.n == 4 && g.n_alpha == 3 && g.nblk >= kFMembers && (g.nblk + p.FP - 1) / p.FP <= kFMaxBlocks;
+    p.FGS = (p.FP + 7) / 8;
+    p.FNG = (p.FP + p.FGS - 1) / p.FGS;
+    p.tiles16 = (T + kFTok - 1) / kFTok;
+    const int rec_slices = p.fused_geom && p.FP > p.S ? p.FP : p.S;
+    // the call counter first, at the same offset for every problem size
     size_t off = 0;
+    p.off_sync = off;
+    off += 256;
     p.off_packed = off;
     off = align_up(off + g.packed_bytes, 256);
     p.off_wts = off;
     off = align_up(off + (size_t)T * g.n * sizeof(float), 256);
     p.off_rec = off;
-    off = align_up(off + (size_t)p.tasks * kTileTokens * rec_stride(g.n, g.M) * sizeof(float), 256);
+    off = align_up(off + (size_t)p.tiles * rec_slices * kTileTokens * rec_stride(g.n, g.M) * sizeof(float), 256);
+    if (p.fused_geom) {
+        p.off_prx = off;
+        off = align_up(off + (size_t)p.tiles16 * p.FP * kFTok * (g.n + 1) * 8, 256);
+        p.off_hpx = off;
+        off = align_up(off + (size_t)p.tiles16 * kFTok * g.n * 8, 256);
+    }
     p.ws_bytes = off;
     return p;
 }
@@ -210,6 +250,17 @@ MHC_HOST_DEVICE inline int64_t rec_tile(int64_t tile, int S, int n, int M)
 }
 MHC_HOST_DEVICE inline int rec_loc(int s, int tl, int n, int M) { return (s * kTileTokens + tl) * rec_stride(n, M); }
 
+// Single-read kernel: first d-block of member s (members take consecutive runs of the
+// nblk d-blocks, sizes differing by at most one); word of the tagged pre-branch record of
+// (tile jt, member s, token t, value v: the n pre sums, then the square); word of the
+// published hPre of (tile jt, token t, stream i).
+MHC_HOST_DEVICE inline int member_begin(int s, int nblk, int P) { return (int)((int64_t)s * nblk / P); }
+MHC_HOST_DEVICE inline int64_t prx_at(int64_t jt, int P, int s, int t, int v, int n)
+{
+    return ((jt * P + s) * kFTok + t) * (n + 1) + v;
+}
+MHC_HOST_DEVICE inline int64_t hpx_at(int64_t jt, int t, int i, int n) { return (jt * kFTok + t) * n + i; }
+
 // Everything a forward launch needs (device pointers are raw).
 struct ForwardArgs {
     const uint16_t* x;
@@ -227,6 +278,10 @@ struct ForwardArgs {
     float* norm_out;
     float* wts;        // [T][n] hIn weights (hPre) from the epilogue
     float* rec;        // partial records, one block per tile
+    uint64_t* prx;     // single-read kernel: tagged pre-branch records
+    uint64_t* hpx;     // single-read kernel: tagged hPre per tile
+    uint32_t* sync;    // [0] call counter (the epilogue adds 1; the single-read kernel's tag),
+                       // [1] set when a single-read wait timed out
     int num_iters;
     double norm_eps;
     double hc_eps;
@@ -244,6 +299,9 @@ int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void
 // events: NULL, or kStages + 1 caller-created events (hipEvent_t) recorded around the
 // projection, epilogue and hIn kernels (events[kStageProj] is recorded by the caller).
 int launch_forward(const Plan& p, const ForwardArgs& a, void* stream, void* const* events);
+// Which kernels launch_forward runs for this plan and these arguments on the current
+// device: 1 the single-read kernel, 0 the four-kernel path.
+int forward_path(const Plan& p, bool has_pre_mix);
 int record_event(void* event, void* stream);
 
 }  // namespace mhc

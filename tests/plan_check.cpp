@@ -112,6 +112,47 @@ static int check(int n, int D, int na, long long T)
     if (p.off_wts < p.off_packed + g.packed_bytes) return fail("packed size", n, D, na, T, p.off_wts, 0);
     if (p.off_rec < p.off_wts + (size_t)T * n * 4) return fail("wts size", n, D, na, T, p.off_rec, 0);
     if (p.ws_bytes < p.off_rec + (size_t)p.tiles * recb) return fail("record size", n, D, na, T, p.ws_bytes, 0);
+    // the call counter sits first, at the same offset for every size
+    if (p.off_sync != 0 || p.off_packed < 256) return fail("sync section", n, D, na, T, p.off_sync, p.off_packed);
+    // single-read variant
+    const bool want = n == 4 && na == 3 && g.nblk >= kFMembers && (g.nblk + kFMembers - 1) / kFMembers <= kFMaxBlocks;
+    if (p.fused_geom != want) return fail("single-read admission", n, D, na, T, p.fused_geom, want);
+    if (p.fused_geom) {
+        if (p.FP != kFMembers || p.FGS * 8 < p.FP || p.FP % p.FGS || p.FNG > 8)
+            return fail("member groups", n, D, na, T, p.FP, p.FGS);
+        int prev = 0;
+        for (int s = 0; s < p.FP; ++s) {
+            const int b0 = member_begin(s, g.nblk, p.FP), b1 = member_begin(s + 1, g.nblk, p.FP);
+            if (b0 != prev || b1 - b0 < 1 || b1 - b0 > kFMaxBlocks) return fail("member blocks", n, D, na, T, b0, b1);
+            // the member's weights: whole K-steps inside the packed buffer
+            if ((long long)b1 * n * 4 * g.NC > (long long)(g.nks + kPadSteps) * 4 * g.NC)
+                return fail("member weights", n, D, na, T, b1, g.nks);
+            prev = b1;
+        }
+        if (prev != g.nblk) return fail("member cover", n, D, na, T, prev, g.nblk);
+        // LDS: weights (3M columns), two buffers of every compute wave's row sums and
+        // squares, two hPre slots
+        const long long lds = (long long)kFMaxBlocks * n * 4 * 3 * g.M * 16 +
+                              2LL * kFMaxBlocks * kFTok * (g.M + 1) * 4 + 2 * kFTok * n * 4;
+        if (lds > 160 * 1024) return fail("single-read LDS", n, D, na, T, lds, 160 * 1024);
+        if (T > 0 && (p.tiles16 * kFTok < T || (p.tiles16 - 1) * kFTok >= T)) return fail("tiles16", n, D, na, T, p.tiles16, 0);
+        // 16-token x tile: the largest lane offset (row 15, last stream, last block, octet 3)
+        const long long xo = ((15LL * g.K) + (long long)(n - 1) * D + kBlock * (g.nblk - 1LL) + 24) * 2 + 16;
+        if (xo >= (1LL << 31) || 16LL * g.K * 2 >= (1LL << 31)) return fail("single-read x offsets", n, D, na, T, xo, 0);
+        // records with slice = member fill the record area
+        const long long frec = (long long)p.FP * kTileTokens * rs * 4;
+        if (rec_tile(p.tiles, p.FP, n, g.M) * 4 != p.tiles * frec) return fail("member record tiles", n, D, na, T, 0, 0);
+        if ((size_t)(p.tiles * frec) > p.off_prx - p.off_rec) return fail("member record area", n, D, na, T, p.tiles * frec, 0);
+        // tagged exchange areas
+        if (p.tiles16 > 0) {
+            const long long pw = p.tiles16 * p.FP * kFTok * (n + 1);
+            if (prx_at(p.tiles16 - 1, p.FP, p.FP - 1, kFTok - 1, n, n) + 1 != pw) return fail("prx index", n, D, na, T, pw, 0);
+            if (p.off_hpx < p.off_prx + (size_t)pw * 8 || p.off_hpx % 256) return fail("prx area", n, D, na, T, p.off_hpx, 0);
+            const long long hw = p.tiles16 * kFTok * n;
+            if (hpx_at(p.tiles16 - 1, kFTok - 1, n - 1, n) + 1 != hw) return fail("hpx index", n, D, na, T, hw, 0);
+            if (p.ws_bytes < p.off_hpx + (size_t)hw * 8) return fail("hpx area", n, D, na, T, p.ws_bytes, 0);
+        }
+    }
     return 0;
 }
 

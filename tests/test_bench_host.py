@@ -32,6 +32,19 @@ def test_stage_bytes_cover_the_call():
         assert stages - extra_x + wl.n_alpha * 4 + wl.M * 4 + gamma == call, name
 
 
+def test_single_read_stage_bytes_cover_the_call():
+    # on the single-read path x is read once: the projection stage reads x and writes hIn,
+    # the hIn stage moves nothing
+    for name, wl in synth.WORKLOADS.items():
+        if wl.pre_mix:
+            continue
+        stages = sum(bench.stage_bytes(wl, s, True) for s in ("projection", "epilogue", "hin"))
+        call = bench.algorithmic_bytes(wl, intermediates=wl.need_backward)
+        gamma = wl.K * 4 if wl.gamma else 0
+        assert bench.stage_bytes(wl, "hin", True) == 0
+        assert stages + wl.n_alpha * 4 + wl.M * 4 + gamma == call, name
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
@@ -43,7 +56,7 @@ def test_counter_summary_reader(tmp_path, monkeypatch):
     # missing file -> None; stale source hash -> None; matching hash -> scaled bytes
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     (tmp_path / "profiles").mkdir()
-    assert bench.counter_traffic("projection", "w")[0] is None
+    assert bench.counter_traffic("proj_kernel", "w")[0] is None
     for rel in bench.KERNEL_SOURCES:
         p = tmp_path / rel
         p.parent.mkdir(parents=True, exist_ok=True)
@@ -53,7 +66,7 @@ def test_counter_summary_reader(tmp_path, monkeypatch):
     body = ("source_sha256: {}\nfetch_kib_per_dispatch: 2048\nwrite_kib_per_dispatch: 1024\n"
             "fetch_factor: 2.0\nwrite_factor: 1.0\n")
     f.write_text(body.format(sha))
-    traffic, src = bench.counter_traffic("projection", "w")
+    traffic, src = bench.counter_traffic("proj_kernel", "w")
     assert traffic == 1024 * 1024 + 1024 * 1024
     f.write_text(body.format("0" * 64))
-    assert bench.counter_traffic("projection", "w")[0] is None
+    assert bench.counter_traffic("proj_kernel", "w")[0] is None

@@ -1,0 +1,89 @@
+"""The single-read forward kernel (n = 4, alpha[3], no pre_mix, 1024 <= D <= 7168): path
+selection on the device, and parity with the fp64 oracle under the acceptance rule of
+gpu_helpers, at the sizes where it is chosen by itself (the large workload test covers that at
+full size) and, forced by MHC_FORWARD_PATH=fused, at small and ragged sizes: partial last
+tiles of 16 tokens, groups with unequal numbers of tiles, members with unequal numbers of
+d-blocks, a partial last d-block, gamma, and the output set without intermediates."""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import compare, device, gpu_forward, run_oracle, summary
+
+pytestmark = pytest.mark.gpu
+
+
+def _runner(wl, nb):
+    import mhc_hyper_connection_amd as mhc
+    return mhc.PreForward(wl.T, wl.n, wl.D, wl.n_alpha, num_iters=wl.num_iters, norm_eps=wl.norm_eps,
+                          hc_eps=wl.hc_eps, need_backward=nb, device=device())
+
+
+def _timeout_flag(runner):
+    # the library's wait time-out flag: the second 32-bit word of the workspace
+    return int(runner.workspace[4:8].cpu().numpy().view(np.uint32)[0])
+
+
+@pytest.mark.parametrize("T,D,pre_mix,n,n_alpha,want", [
+    (16384, 7168, False, 4, 3, 1), (8192, 4096, False, 4, 3, 1), (8192, 1024, False, 4, 3, 1),
+    (64, 7168, False, 4, 3, 0), (8191, 4096, False, 4, 3, 0), (4096, 4096, False, 4, 3, 0),
+    (16384, 7168, True, 4, 3, 0), (8192, 8192, False, 4, 3, 0), (8192, 992, False, 4, 3, 0),
+    (8192, 1016, False, 4, 3, 1), (8192, 2048, False, 8, 3, 0), (8192, 2048, False, 4, 2, 0)])
+def test_path_selection(T, D, pre_mix, n, n_alpha, want, monkeypatch):
+    import mhc_hyper_connection_amd as mhc
+    monkeypatch.delenv("MHC_FORWARD_PATH", raising=False)
+    device()
+    p = mhc.make_params(T, n, D, n_alpha)
+    assert mhc.forward_path(p, pre_mix) == want
+
+
+CASES = [
+    # (name, T, D, gamma, need_backward, intermediates, seed)
+    ("T1_D1024", 1, 1024, False, True, True, 51),
+    ("T17_D1024_bwd", 17, 1024, False, True, True, 52),
+    ("T100_D1032_gamma", 100, 1032, True, False, True, 53),
+    ("T129_D2048_no_intermediates", 129, 2048, False, False, False, 54),
+    ("T300_D4096_gamma_bwd", 300, 4096, True, True, True, 55),
+    ("T1000_D7168_bwd", 1000, 7168, False, True, True, 56),
+    ("T2100_D3000_gamma", 2100, 3000, True, False, True, 57),
+]
+
+
+@pytest.mark.parametrize("name,T,D,gamma,nb,inter,seed", CASES, ids=[c[0] for c in CASES])
+def test_forced_single_read_parity(name, T, D, gamma, nb, inter, seed, monkeypatch):
+    monkeypatch.setenv("MHC_FORWARD_PATH", "fused")
+    print(f"[case] single-read {name} T={T} D={D} gamma={gamma} need_backward={nb}", file=sys.stderr, flush=True)
+    inp = synth.custom(T, 4, D, gamma=gamma, need_backward=nb, seed=seed)
+    r = _runner(inp.wl, nb)
+    assert r.path() == 1
+    gpu = gpu_forward(inp, runner=r, intermediates=inter)
+    rep = compare(gpu, run_oracle(inp), inp)
+    print(f"[single-read] {name}: {summary(rep)}", file=sys.stderr, flush=True)
+    assert _timeout_flag(r) == 0
+
+
+def test_single_read_reproducible_and_repeated_calls(monkeypatch):
+    # several calls through one workspace (the call counter advances each time): bitwise
+    # equal results, and no wait ever timed out
+    monkeypatch.setenv("MHC_FORWARD_PATH", "fused")
+    print("[case] single-read repeated T=3000 D=2048", file=sys.stderr, flush=True)
+    inp = synth.custom(3000, 4, 2048, gamma=True, need_backward=True, seed=58)
+    r = _runner(inp.wl, True)
+    runs = gpu_forward(inp, runner=r, repeat=3)
+    for k in runs[0]:
+        for other in runs[1:]:
+            assert np.array_equal(runs[0][k].view(np.uint8), other[k].view(np.uint8)), k
+    compare(runs[-1], run_oracle(inp), inp)
+    assert _timeout_flag(r) == 0
+
+
+def test_classic_path_still_served(monkeypatch):
+    # the four-kernel path on a shape the single-read kernel would take
+    monkeypatch.setenv("MHC_FORWARD_PATH", "classic")
+    print("[case] classic forced T=8192 D=2048", file=sys.stderr, flush=True)
+    inp = synth.custom(8192, 4, 2048, need_backward=True, seed=59)
+    r = _runner(inp.wl, True)
+    assert r.path() == 0
+    compare(gpu_forward(inp, runner=r), run_oracle(inp), inp)
