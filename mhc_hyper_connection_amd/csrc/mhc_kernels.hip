@@ -614,18 +614,19 @@ struct FArgs {
 // is the control wave: it alone waits on other workgroups. Round r of the group is tile
 // r G + g. Per round (one workgroup barrier, at its middle):
 //   compute waves: project the round's tile (x loaded kFAhead rounds ago), fold each phi
-//     row's hi, mid and lo sums and put them in LDS; hIn of the tile of round r - kFLag
-//     from the registers still holding its x and the hPre the control wave placed in LDS;
-//     then the x loads of round r + kFAhead into the registers just freed.
-//   control wave: the hPre of round r + 1 - kFLag (polled last round) into LDS; if this
-//     member is designated for round r - 2 (designated = round mod P), sums the pre-branch
-//     records of that tile (loaded last round) in the epilogue's order and publishes its
-//     hPre; if designated for round r - 1, loads that tile's records; polls the hPre of
-//     round r + 2 - kFLag.
-//   barrier
-//   compute waves: one value each of the tile's partial record (totals over the waves),
-//     stored for the epilogue and, for the pre sums and the square, tagged for the
-//     designated member.
+//     row's hi, mid and lo sums and put them in LDS; barrier of the compute waves; one
+//     value each of the tile's partial record (totals over the waves), stored for the
+//     epilogue and, for the pre sums and the square, tagged for the designated member;
+//     hIn of the tile of round r - kFLag from the registers still holding its x and the
+//     hPre the control wave placed in LDS; then the x loads of round r + kFAhead into the
+//     registers just freed (stores first, loads last: the wait for a round's x counts the
+//     stores issued after its loads).
+//   control wave (outside the barrier): iteration k, once the compute waves have passed
+//     their barrier of round k + 1 (so their records of round k are stored): if this
+//     member is designated for round k (designated = round mod P), sums the members'
+//     tagged pre-branch records of that tile in the epilogue's order and publishes its
+//     hPre; then polls the hPre of round k - 2 and hands it to the compute waves through
+//     LDS slot (k - 2) mod 4 and its flag.
 // Every wait at round r is for work other members finish by their round r - 1, so with
 // all workgroups resident (cooperative launch) the waits end; a wait that does not end
 // within kSpinLimit polls sets sync[1] and yields NaN hPre for that tile.
@@ -644,9 +645,9 @@ fused_kernel(FArgs f)
     constexpr int GS = (P + 7) / 8;            // the epilogue's summation groups over members
     static_assert(P % GS == 0, "whole summation groups");
     static_assert(NT == 5 && NCL == 72 && M == 24, "column pairing of hi, mid and lo below");
-    static_assert(kFTok * V == 64 * NW, "one record value per compute lane");
     __shared__ u32x4 wl[NW * N * 4 * NCL];        // the member's packed weights
-    __shared__ float part[2][NW][kFTok][M];      // each compute wave's row sums, by round parity
+    constexpr int MP = 32;                       // row stride: lanes 8..15 write into the padding
+    __shared__ float part[2][NW][kFTok][MP];     // each compute wave's row sums, by round parity
     __shared__ float part_sq[2][NW][kFTok];      // and its squares
     constexpr int NS = 4;                        // hPre slots handed from the control wave
     __shared__ float hp_lds[NS][kFTok * N];
@@ -716,10 +717,20 @@ fused_kernel(FArgs f)
                 if (r >= R + kFLag) break;
                 const int pb = (int)(r & 1);
                 if (r < R && has_blk) {
-                    // this round's x: the loads issued after it are those of the next
-                    // kFAhead - 1 rounds, where they exist
-                    if (r + 1 < R) wait_vm_only<N>();
-                    else wait_vm_only<0>();
+                    // this round's x. Issued after its loads, in round r - 1: that round's
+                    // two record stores (every round < R has them), its hIn store (from round
+                    // kFLag on) and the loads of round r + 1 (where it exists); memory
+                    // operations complete in issue order
+                    const bool st1 = r >= 1, hs1 = r - 1 >= kFLag, ld1 = r + 1 < R;
+                    if (ld1) {
+                        if (st1 && hs1) wait_vm_only<2 + 1 + N>();
+                        else if (st1) wait_vm_only<2 + N>();
+                        else wait_vm_only<N>();
+                    } else {
+                        if (st1 && hs1) wait_vm_only<2 + 1>();
+                        else if (st1) wait_vm_only<2>();
+                        else wait_vm_only<0>();
+                    }
                     ring_ready(xr[u]);
                     f32x4 acc[NT];
                     f32x4 sq = {0.f, 0.f, 0.f, 0.f};
@@ -750,24 +761,69 @@ fused_kernel(FArgs f)
                                     Av, __builtin_bit_cast(bf16x8, bw[di][nt]), acc[nt], 0, 0, 0);
                         }
                     }
-                    // phi row m's hi, mid and lo are columns m, M + m, 2M + m: for lane j of
-                    // a 16-lane row, row j (and 16 + j when j < 8) takes its mid term from
-                    // lane (j + 8) mod 16; the three are added in fp64 and rounded once
+                    // phi row m's hi, mid and lo are columns m, M + m, 2M + m: lane j of a
+                    // 16-lane row holds row m = j (and m = 16 + j when j < 8), its mid term
+                    // in lane (j + 8) mod 16; added in fp32 (hi, then mid, then lo: two
+                    // roundings of the wave's sum, well inside the accuracy kept)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int t = 4 * grp + q;
                         const float m1 = dpp<kRowRor8>(acc[1][q]), m2 = dpp<kRowRor8>(acc[2][q]);
-                        if (j < 8) {
-                            part[pb][wave][t][j] = (float)((double)acc[0][q] + (double)m1 + (double)acc[3][q]);
-                            part[pb][wave][t][16 + j] = (float)((double)acc[1][q] + (double)m2 + (double)acc[4][q]);
-                        } else {
-                            part[pb][wave][t][j] = (float)((double)acc[0][q] + (double)m2 + (double)acc[3][q]);
-                        }
+                        part[pb][wave][t][j] = (acc[0][q] + (j < 8 ? m1 : m2)) + acc[3][q];
+                        part[pb][wave][t][16 + j] = (acc[1][q] + m2) + acc[4][q];   // j >= 8: padding
                     }
                     const int rr = j - 4 * grp;
                     if (rr >= 0 && rr < 4) part_sq[pb][wave][j] = sq[rr];
                 }
-                // hIn of round r - kFLag from the registers that still hold its x
+                // barrier of the compute waves: every wave's sums of this round are in LDS
+                asm volatile("" : : : "memory");
+                if (lane == 0) __hip_atomic_fetch_add(&cbar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                wait_lds_at_least(&cbar, (uint32_t)(NW * (r + 1)));
+
+                if (r < R) {
+                    // the tile's partial record, one value per compute lane: token t, record
+                    // value v (the n pre sums, the square, padding, the other M - n sums),
+                    // summed over the compute waves in wave order. Two stores per wave (the
+                    // record value, the tagged word: some lane of every wave has v <= n).
+                    const int64_t jt = r * f.G + g;
+                    const int64_t t0 = jt * kFTok;
+                    const int ntile = (int)(f.T - t0 < kFTok ? f.T - t0 : kFTok);
+                    // the epilogue's record layout: slice = member, 64-token tiles
+                    const rsrc_t rec = make_rsrc(a.rec + rec_tile(jt / 4, P, N, M), (int64_t)P * kTileTokens * V * 4);
+                    const int tl0 = kFTok * (int)(jt % 4);
+                    uint64_t* prx_tile = a.prx + prx_at(jt, P, s, 0, 0, N);
+                    auto reduce_item = [&](int L) {
+                        const int t = L / V, v = L % V;
+                        const int m = v < N ? v : (v < PPS ? 0 : N + (v - PPS));   // square / padding: row 0, unused
+                        float qv[NW], qs[NW];
+#pragma unroll
+                        for (int w = 0; w < NW; ++w) {   // all reads first, then the sums
+                            qv[w] = part[pb][w][t][m];
+                            qs[w] = part_sq[pb][w][t];
+                        }
+                        float hsum = 0.f, ssum = 0.f;   // fp32, in wave order
+                        if (nb == NW) {
+#pragma unroll
+                            for (int w = 0; w < NW; ++w) {
+                                hsum += qv[w];
+                                ssum += qs[w];
+                            }
+                        } else {
+#pragma unroll
+                            for (int w = 0; w < NW; ++w) {
+                                hsum += w < nb ? qv[w] : 0.f;
+                                ssum += w < nb ? qs[w] : 0.f;
+                            }
+                        }
+                        const float val = v == N ? ssum : (v > N && v < PPS) ? 0.f : hsum;
+                        st_buf(rec, t < ntile ? (uint32_t)(rec_loc(s, tl0 + t, N, M) + v) * 4 : kOutOfRange, val);
+                        // the tagged pre-branch sums and square for the designated member
+                        if (v <= N) put_tagged(prx_tile + t * (N + 1) + v, tag, val);
+                    };
+                    static_assert(kFTok * V == 64 * NW, "one record value per compute lane");
+                    reduce_item(wave * 64 + lane);
+                }
+                // hIn of round r - kFLag from the registers that still hold its x (one store)
                 const int us = (u + kFAhead) % kFRing;
                 const int64_t rh = r - kFLag;
                 if (rh >= 0 && has_blk) {
@@ -795,42 +851,6 @@ fused_kernel(FArgs f)
                     __builtin_amdgcn_raw_buffer_store_b128(o, hres, (int)(oct_ok ? ho : kOutOfRange), 0, 0);
                 }
                 if (has_blk && r + kFAhead < R) load_round(r + kFAhead, xr[us]);
-                // barrier of the compute waves: every wave's sums of this round are in LDS
-                asm volatile("" : : : "memory");
-                if (lane == 0) __hip_atomic_fetch_add(&cbar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                wait_lds_at_least(&cbar, (uint32_t)(NW * (r + 1)));
-
-                if (r < R) {
-                    // one value of the tile's partial record per compute lane: token t,
-                    // record value v (the n pre sums, the square, padding, the other
-                    // M - n sums), summed over the compute waves in wave order
-                    const int L = wave * 64 + lane;
-                    const int t = L / V, v = L % V;
-                    const int m = v < N ? v : (v < PPS ? 0 : N + (v - PPS));   // square / padding: row 0, unused
-                    float qv[NW], qs[NW];
-#pragma unroll
-                    for (int w = 0; w < NW; ++w) {   // all reads first, then the sums
-                        qv[w] = part[pb][w][t][m];
-                        qs[w] = part_sq[pb][w][t];
-                    }
-                    double hsum = 0.0;
-                    float ssum = 0.f;
-#pragma unroll
-                    for (int w = 0; w < NW; ++w) {
-                        hsum += w < nb ? (double)qv[w] : 0.0;
-                        ssum += w < nb ? qs[w] : 0.f;
-                    }
-                    const float val = v == N ? ssum : (v > N && v < PPS) ? 0.f : (float)hsum;
-                    const int64_t jt = r * f.G + g;
-                    const int64_t t0 = jt * kFTok;
-                    const int ntile = (int)(f.T - t0 < kFTok ? f.T - t0 : kFTok);
-                    // the epilogue's record layout: slice = member, 64-token tiles
-                    const rsrc_t rec = make_rsrc(a.rec + rec_tile(jt / 4, P, N, M), (int64_t)P * kTileTokens * V * 4);
-                    const int tl = kFTok * (int)(jt % 4) + t;
-                    st_buf(rec, t < ntile ? (uint32_t)(rec_loc(s, tl, N, M) + v) * 4 : kOutOfRange, val);
-                    // the tagged pre-branch sums and square for the designated member
-                    if (v <= N) put_tagged(a.prx + prx_at(jt, P, s, t, v, N), tag, val);
-                }
             }
         }
     } else {

@@ -130,10 +130,10 @@ static int check(int n, int D, int na, long long T)
             prev = b1;
         }
         if (prev != g.nblk) return fail("member cover", n, D, na, T, prev, g.nblk);
-        // LDS: weights (3M columns), two buffers of every compute wave's row sums and
-        // squares, two hPre slots
+        // LDS: weights (3M columns), two buffers of every compute wave's row sums (rows
+        // padded to 32) and squares, four hPre slots and their flags, the barrier count
         const long long lds = (long long)kFMaxBlocks * n * 4 * 3 * g.M * 16 +
-                              2LL * kFMaxBlocks * kFTok * (g.M + 1) * 4 + 2 * kFTok * n * 4;
+                              2LL * kFMaxBlocks * kFTok * (32 + 1) * 4 + 4 * kFTok * n * 4 + 5 * 4;
         if (lds > 160 * 1024) return fail("single-read LDS", n, D, na, T, lds, 160 * 1024);
         if (T > 0 && (p.tiles16 * kFTok < T || (p.tiles16 - 1) * kFTok >= T)) return fail("tiles16", n, D, na, T, p.tiles16, 0);
         // 16-token x tile: the largest lane offset (row 15, last stream, last block, octet 3)
