@@ -145,8 +145,9 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
 /* The forward, asynchronous on `stream` (a hipStream_t; NULL = default stream). Emits
  * every non-NULL output listed in mhc_pre_tensors. `workspace` is device memory of at
  * least mhc_pre_workspace_size bytes, 256-byte aligned, zero-filled before its first use.
- * When tensors->phi_packed is NULL the weights are packed into the workspace first (one
- * extra kernel). Then one of two kernel sequences (mhc_pre_forward_path tells which):
+ * When tensors->phi_packed is NULL the weights are packed from phi (and gamma): by a pack
+ * kernel into the workspace on the four-kernel path, inside the kernel on the single-read
+ * path. Then one of two kernel sequences (mhc_pre_forward_path tells which):
  *   four-kernel path: a projection kernel (which with pre_mix also writes hIn), a
  *     per-token epilogue and, without pre_mix, an hIn kernel (x is read twice);
  *   single-read path (n == 4, n_alpha == 3, no pre_mix, 992 < D <= 7168 (32 to 224
@@ -180,8 +181,9 @@ mhc_status mhc_pre_forward_path(const mhc_pre_params* params, int32_t has_pre_mi
  *   events[2] after the projection kernel,
  *   events[3] after the per-token epilogue kernel,
  *   events[4] after the hIn kernel.
- * A kernel the call does not launch (the pack when phi_packed is given, the hIn kernel
- * when pre_mix is given: the projection writes hIn then) has its two events recorded
+ * A kernel the call does not launch (the pack when phi_packed is given or on the
+ * single-read path, which packs inside its kernel; the hIn kernel when pre_mix is given
+ * or on the single-read path: the projection writes hIn then) has its two events recorded
  * back to back, so elapsed time between events[i] and events[i+1] is kernel i's duration
  * (plus the launch gap) whatever the inputs; with T == 0 all five are recorded back to
  * back. Computes exactly what mhc_pre_forward computes.

@@ -147,19 +147,14 @@ mhc_status forward_impl(const mhc_pre_params* params, const mhc_pre_tensors* t,
     }
 
     char* ws = static_cast<char*>(workspace);
-    const void* packed = t->phi_packed;
-    if (events && mhc::record_event(events[mhc::kStagePack], stream) != 0) return MHC_ERR_RUNTIME;
-    if (!packed) {
-        void* dst = ws + plan.off_packed;
-        if (mhc::launch_prepack(g, t->phi, t->gamma, dst, stream) != 0) return MHC_ERR_RUNTIME;
-        packed = dst;
-    }
-    if (events && mhc::record_event(events[mhc::kStageProj], stream) != 0) return MHC_ERR_RUNTIME;
 
     mhc::ForwardArgs a;
     std::memset(&a, 0, sizeof a);
     a.x = t->x;
-    a.packed = packed;
+    a.packed = t->phi_packed;   // NULL: packed by the launch (in the kernel or by the pack kernel)
+    a.phi = t->phi;
+    a.gamma = t->gamma;
+    a.packed_ws = ws + plan.off_packed;
     a.alpha = t->alpha;
     a.bias = t->bias;
     a.pre_mix = t->pre_mix;

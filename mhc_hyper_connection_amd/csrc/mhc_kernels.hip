@@ -78,6 +78,17 @@ __device__ __forceinline__ int tile_tokens(const KArgs& k, int64_t t0)
 
 // ------------------------------------------------------------------ weight pre-pack
 
+// phi * gamma (the exact product in double) as three bf16 terms, each the nearest bf16 of
+// what the previous ones leave: hi + mid + lo equals the product to ~2^-26 relative.
+__device__ __forceinline__ void split3(double p, uint32_t (&tb)[3])
+{
+    tb[0] = f32_to_bf16_bits((float)p);
+    const double r1 = p - bf16_bits_to_double(tb[0]);
+    tb[1] = f32_to_bf16_bits((float)r1);
+    const double r2 = r1 - bf16_bits_to_double(tb[1]);
+    tb[2] = f32_to_bf16_bits((float)r2);
+}
+
 __global__ void __launch_bounds__(256)
 prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
                u32x4* __restrict__ packed, int n, int D, int M, int NC, int nks, int64_t total)
@@ -97,16 +108,11 @@ prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
         const int m = c % M;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            // exact product in double, then hi/mid/lo each the nearest bf16 of what is left
             double p = (double)phi[(int64_t)m * K + k0 + e];
             if (gamma) p *= (double)gamma[k0 + e];
-            const uint32_t hb = f32_to_bf16_bits((float)p);
-            const double r1 = p - bf16_bits_to_double(hb);
-            const uint32_t mb = f32_to_bf16_bits((float)r1);
-            const double r2 = r1 - bf16_bits_to_double(mb);
-            const uint32_t lb = f32_to_bf16_bits((float)r2);
-            const uint32_t bits = term == 0 ? hb : (term == 1 ? mb : lb);
-            w[e >> 1] |= bits << (16 * (e & 1));
+            uint32_t tb[3];
+            split3(p, tb);
+            w[e >> 1] |= tb[term] << (16 * (e & 1));
         }
     }
     packed[u] = w;
@@ -664,10 +670,33 @@ fused_kernel(FArgs f)
     const int64_t R = g < f.tiles16 ? (f.tiles16 - g + f.G - 1) / f.G : 0;   // rounds of group g
     const uint32_t tag = (f.a.sync[0] << 1) | 1u;
 
-    {   // the member's K-steps of the packed weights, without the zero columns past 3M
+    if (a.packed) {   // the member's K-steps of the packed weights, without the zero columns past 3M
         const u32x4* src = static_cast<const u32x4*>(a.packed) + (int64_t)b_lo * N * 4 * NC;
         const int units = nb * N * 4 * NCL;
         for (int u = tid; u < units; u += kFThreads) wl[u] = src[(int64_t)(u / NCL) * NC + u % NCL];
+    } else {          // packed here from phi (and gamma), as prepack_kernel packs them
+        const int items = nb * N * 4 * M;   // (K-step, octet row, phi row): three LDS units each
+        for (int it = tid; it < items; it += kFThreads) {
+            const int m = it % M, row = it / M;        // row = K-step * 4 + octet
+            const int kk = row / 4, og = row % 4;
+            const int k = b_lo * N + kk;               // K-step: d-block k / N, stream k % N
+            const int d = kBlock * (k / N) + 8 * og;
+            u32x4 w3[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+            if (d < f.D) {
+                const int64_t k0 = (int64_t)(k % N) * f.D + d;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    double p = (double)a.phi[(int64_t)m * f.K + k0 + e];
+                    if (a.gamma) p *= (double)a.gamma[k0 + e];
+                    uint32_t tb[3];
+                    split3(p, tb);
+#pragma unroll
+                    for (int term = 0; term < 3; ++term) w3[term][e >> 1] |= tb[term] << (16 * (e & 1));
+                }
+            }
+#pragma unroll
+            for (int term = 0; term < 3; ++term) wl[row * NCL + term * M + m] = w3[term];
+        }
     }
     if (tid < NS) hp_flag[tid] = 0u;
     if (tid == 0) cbar = 0u;
@@ -1044,10 +1073,34 @@ int record_event(void* event, void* stream)
     return (int)hipEventRecord((hipEvent_t)event, (hipStream_t)stream);
 }
 
-int launch_forward(const Plan& p, const ForwardArgs& a, void* stream, void* const* events)
+int launch_forward(const Plan& p, const ForwardArgs& a_in, void* stream, void* const* events)
 {
     if (p.T <= 0) return 0;
     hipStream_t st = (hipStream_t)stream;
+    ForwardArgs a = a_in;
+    if (mark(events, kStagePack, st) != hipSuccess) return (int)hipErrorUnknown;
+    if (fused_wanted(p, a.pre_mix != nullptr)) {
+        // a cooperative launch is not taken into a graph being captured: the four-kernel
+        // path serves then. Unpacked weights are packed inside the kernel.
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        const int G = fused_groups(p);
+        if (G > 0 && hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) {
+            hipError_t e = mark(events, kStagePack + 1, st);
+            if (e != hipSuccess) return (int)e;
+            bool launched = false;
+            e = launch_fused(p, a, G, st, events, &launched);
+            if (launched) return (int)e;
+            (void)hipGetLastError();   // refused: the four-kernel path below serves
+        }
+    }
+    if (!a.packed) {
+        if (launch_prepack(p.g, a.phi, a.gamma, a.packed_ws, stream) != 0) return (int)hipErrorUnknown;
+        a.packed = a.packed_ws;
+    }
+    {
+        const hipError_t e = mark(events, kStagePack + 1, st);
+        if (e != hipSuccess) return (int)e;
+    }
     KArgs k;
     k.a = a;
     k.T = p.T;
@@ -1057,18 +1110,6 @@ int launch_forward(const Plan& p, const ForwardArgs& a, void* stream, void* cons
     k.S = p.S;
     k.GS = p.GS;
     k.NG = p.NG;
-    if (fused_wanted(p, a.pre_mix != nullptr)) {
-        // a cooperative launch is not taken into a graph being captured: the four-kernel
-        // path serves then
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        const int G = fused_groups(p);
-        if (G > 0 && hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) {
-            bool launched = false;
-            const hipError_t e = launch_fused(p, a, G, st, events, &launched);
-            if (launched) return (int)e;
-            (void)hipGetLastError();   // refused: the four-kernel path below serves
-        }
-    }
     const int n = p.g.n, na = p.g.n_alpha, nks = p.NKS;
     const Variant v = variant_of(n, na);
     if (n == 4 && na == 3 && (v.nt != Cfg<4, 3>::NT || v.sk != Cfg<4, 3>::SK)) return (int)hipErrorInvalidValue;

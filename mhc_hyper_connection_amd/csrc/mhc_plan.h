@@ -264,7 +264,10 @@ MHC_HOST_DEVICE inline int64_t hpx_at(int64_t jt, int t, int i, int n) { return 
 // Everything a forward launch needs (device pointers are raw).
 struct ForwardArgs {
     const uint16_t* x;
-    const void* packed;
+    const void* packed;    // packed weights, or NULL: packed from phi / gamma into packed_ws
+    const float* phi;
+    const float* gamma;
+    void* packed_ws;       // workspace section for the packed weights
     const float* alpha;
     const float* bias;
     const float* pre_mix;
@@ -297,7 +300,7 @@ constexpr int kStagePack = 0, kStageProj = 1, kStageEpi = 2, kStageHin = 3, kSta
 int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void* packed,
                    void* stream);
 // events: NULL, or kStages + 1 caller-created events (hipEvent_t) recorded around the
-// projection, epilogue and hIn kernels (events[kStageProj] is recorded by the caller).
+// weight pack, projection, epilogue and hIn kernels.
 int launch_forward(const Plan& p, const ForwardArgs& a, void* stream, void* const* events);
 // Which kernels launch_forward runs for this plan and these arguments on the current
 // device: 1 the single-read kernel, 0 the four-kernel path.

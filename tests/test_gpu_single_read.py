@@ -87,3 +87,19 @@ def test_classic_path_still_served(monkeypatch):
     r = _runner(inp.wl, True)
     assert r.path() == 0
     compare(gpu_forward(inp, runner=r), run_oracle(inp), inp)
+
+
+def test_single_read_with_prepacked_weights(monkeypatch):
+    # phi packed once by mhc_pre_prepack and passed in (the kernel then copies the packed
+    # slices instead of packing phi itself): same acceptance, and the same bits as packing
+    # inside the kernel
+    monkeypatch.setenv("MHC_FORWARD_PATH", "fused")
+    print("[case] single-read prepacked T=500 D=2048 gamma", file=sys.stderr, flush=True)
+    inp = synth.custom(500, 4, 2048, gamma=True, need_backward=True, seed=60)
+    r = _runner(inp.wl, True)
+    g_packed = gpu_forward(inp, runner=r, packed=True)
+    compare(g_packed, run_oracle(inp), inp)
+    g_inline = gpu_forward(inp, runner=r, packed=False)
+    for k in g_packed:
+        assert np.array_equal(g_packed[k].view(np.uint8), g_inline[k].view(np.uint8)), k
+    assert _timeout_flag(r) == 0
