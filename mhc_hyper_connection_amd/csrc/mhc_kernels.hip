@@ -567,6 +567,17 @@ __device__ __forceinline__ uint64_t get_tagged(const uint64_t* p)
     return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ bool tag_is(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+// The same 64-bit word read through the XCD's L2 (sc0: past the CU's L1 only) and waited
+// for in the same statement. Cheaper than get_tagged when writer and reader share an XCD;
+// from another XCD the L2 may hold an older copy, whose tag then does not match, so
+// callers fall back to get_tagged. A naturally aligned 64-bit load is single-copy atomic
+// (it is how get_tagged itself compiles, with the device-coherence bit).
+__device__ __forceinline__ uint64_t get_tagged_l2(const uint64_t* p)
+{
+    uint64_t w;
+    asm volatile("global_load_dwordx2 %0, %1, off sc0\n\ts_waitcnt vmcnt(0)" : "=v"(w) : "v"(p) : "memory");
+    return w;
+}
 __device__ __forceinline__ float tagged_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
 constexpr int kSpinLimit = 1 << 18;   // polls of global memory before a wait gives up (about 0.3 s)
@@ -948,12 +959,12 @@ fused_kernel(FArgs f)
             const int64_t rp = k - 2;
             if (rp >= 0 && rp < R) {
                 const uint64_t* src = a.hpx + hpx_at(rp * f.G + g, tq, iq, N);
-                uint64_t w = get_tagged(src);
+                uint64_t w = get_tagged_l2(src);
                 bool ok = tag_is(w, tag);
                 for (int it = 0; !__all(ok) && !failed; ++it) {
                     if (it == kSpinLimit) { fail(); break; }
-                    __builtin_amdgcn_s_sleep(2);
-                    w = get_tagged(src);
+                    __builtin_amdgcn_s_sleep(1);
+                    w = (it & 1) ? get_tagged(src) : get_tagged_l2(src);   // every other poll device-coherent
                     ok = tag_is(w, tag);
                 }
                 hp_lds[rp % NS][lane] = ok ? tagged_value(w) : __builtin_nanf("");
