@@ -20,6 +20,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mhc_oracle.c")
 _SRC_BWD = os.path.join(_HERE, "mhc_oracle_bwd.c")
+_SRC_POST = os.path.join(_HERE, "mhc_oracle_post.c")
 _LIB = os.path.join(_HERE, "libmhc_oracle.so")
 
 
@@ -28,7 +29,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-               "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_BWD, "-lm"]
+               "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_BWD, _SRC_POST, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -78,6 +79,10 @@ def _bind(lib):
     lib.oracle_mhcpre_forward_f64.argtypes = [
         ctypes.c_int64, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp, dp,
         ctypes.c_double, ctypes.c_double, ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp]
+    if hasattr(lib, "oracle_mhc_post"):   # builds of altered copies may leave it out
+        lib.oracle_mhc_post.restype = ctypes.c_int
+        lib.oracle_mhc_post.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp,
+                                        dp, dp, dp]
     lib.oracle_pre_backward.restype = ctypes.c_int
     lib.oracle_pre_backward.argtypes = [ctypes.POINTER(_BwdIn), dp, ctypes.c_int64,
                                         ctypes.POINTER(_BwdOut), ctypes.c_int]
@@ -286,3 +291,30 @@ def backward(x_bits, phi, alpha, grad_h_in_bits, grad_h_post, grad_h_res, inv_rm
     if rc != 0:
         raise ValueError("oracle rejected the problem description")
     return r
+
+
+@dataclass
+class PostResult:
+    out_bf16: np.ndarray   # uint16 [T, n, D]
+    out: np.ndarray        # float64 [T, n, D], before rounding
+    out_abs: np.ndarray    # float64 [T, n, D], sum of |terms|
+
+
+def post(x_bits, residual_bits, post_w, comb, lib=None) -> PostResult:
+    """hc_post: out[t, i, d] = post[t, i] x[t, d] + sum_j comb[t, i, j] residual[t, j, d]
+    (x [T, D] and residual [T, n, D] as bf16 bits, post [T, n], comb [T, n, n] float32)."""
+    lib = lib or _load()
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    residual_bits = np.ascontiguousarray(residual_bits, dtype=np.uint16)
+    post_w = np.ascontiguousarray(post_w, dtype=np.float32)
+    comb = np.ascontiguousarray(comb, dtype=np.float32)
+    T, n, D = residual_bits.shape
+    assert x_bits.shape == (T, D) and post_w.shape == (T, n) and comb.shape == (T, n, n)
+    ob = np.zeros((T, n, D), dtype=np.uint16)
+    o = np.zeros((T, n, D), dtype=np.float64)
+    oa = np.zeros((T, n, D), dtype=np.float64)
+    st = lib.oracle_mhc_post(T, n, D, _ptr(x_bits), _ptr(residual_bits), _ptr(post_w), _ptr(comb),
+                             _ptr(ob), _ptr(o), _ptr(oa))
+    if st != 0:
+        raise ValueError(f"oracle_mhc_post status {st}")
+    return PostResult(ob, o, oa)

@@ -1,0 +1,49 @@
+/* mhc_oracle_post.c -- fp64 oracle of hc_post, the mHC post-mapping (TEST INFRASTRUCTURE).
+ *
+ * Source: HcPre guide (mhpn.cn/news/2282827), section "mHC 架构与 HcPre 的定位": the
+ * layer output is expanded back into the n streams by the post mapping and added to the
+ * streams after the res mapping has fused them across streams. The expression printed
+ * there sums comb over its second index against a residual indexed by comb's first index,
+ * which mixes nothing (each stream is only scaled by its row sum of comb); the reading
+ * taken keeps the summed index on comb and puts it on the residual:
+ *     out[t][i][d] = post[t][i] * x[t][d] + sum_j comb[t][i][j] * residual[t][j][d]
+ * x and residual are bf16 (exact in double), post and comb f32; the sum is exact in
+ * double up to one rounding per addition, then rounded once to bf16 (nearest, ties to
+ * even). out_abs is the sum of |terms| of each element (for the acceptance rule).
+ * Parity pins: tests/test_oracle_post.py (permutation mixing, post-only, a library
+ * einsum, planted mistakes).
+ */
+#include <stdint.h>
+#include <math.h>
+
+double oracle_bf16_to_double(uint16_t bits);
+uint16_t oracle_bf16_from_double(double v);
+
+int oracle_mhc_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* residual,
+                    const float* post, const float* comb, uint16_t* out_bf16, double* out,
+                    double* out_abs)
+{
+    if (T < 0 || n < 1 || D < 1) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int i = 0; i < n; ++i) {
+            const double p = (double)post[t * n + i];
+            for (int d = 0; d < D; ++d) {
+                const double xv = oracle_bf16_to_double(x[t * D + d]);
+                double acc = p * xv;
+                double mag = fabs(p * xv);
+                for (int j = 0; j < n; ++j) {
+                    const double c = (double)comb[(t * n + i) * n + j];
+                    const double r = oracle_bf16_to_double(residual[(t * n + j) * (int64_t)D + d]);
+                    acc += c * r;
+                    mag += fabs(c * r);
+                }
+                const int64_t o = (t * n + i) * (int64_t)D + d;
+                if (out) out[o] = acc;
+                if (out_abs) out_abs[o] = mag;
+                if (out_bf16) out_bf16[o] = oracle_bf16_from_double(acc);
+            }
+        }
+    }
+    return 0;
+}

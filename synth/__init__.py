@@ -32,6 +32,11 @@ MhcPre backward inputs (``backward_inputs``; M = n*n + 2n), drawn in this order:
   grad_x_post  [T, n, D]  N(0, 1) -> bf16  (when asked for)
   sum_out      [2 it, T, n]     U(0.9, 1.1)    (when Sinkhorn planes are asked for)
   norm_out     [2 it, T, n, n]  U(0.05, 0.45)
+hc_post inputs (``post_inputs``), drawn in this order:
+  x         [T, D]     N(0, 1) -> bf16   (the layer output)
+  residual  [T, n, D]  N(0, 1) -> bf16   (the n streams; chunked as above)
+  post      [T, n]     U(0, 2)           (the range of 2 sigmoid)
+  comb      [T, n, n]  U(0.05, 0.45)     (the range of the Sinkhorn matrix entries at n = 4)
 The saved forward values are drawn independently, in the ranges the forward produces:
 the backward is a function of all of them, whatever forward they came from. (Parity
 tests of the Sinkhorn backward take the planes from the oracle's forward instead, so
@@ -206,3 +211,24 @@ def backward_inputs(T: int, n: int, D: int, *, gamma: bool = False, x_post: bool
         bi.sum_out = rng.uniform(0.9, 1.1, size=(2 * sinkhorn_iters, T, n)).astype(np.float32)
         bi.norm_out = rng.uniform(0.05, 0.45, size=(2 * sinkhorn_iters, T, n, n)).astype(np.float32)
     return bi
+
+
+@dataclass
+class PostInputs:
+    T: int
+    n: int
+    D: int
+    x: np.ndarray          # uint16 [T, D] bf16 bits
+    residual: np.ndarray   # uint16 [T, n, D] bf16 bits
+    post: np.ndarray       # float32 [T, n]
+    comb: np.ndarray       # float32 [T, n, n]
+
+
+def post_inputs(T: int, n: int, D: int, *, seed: int = 21) -> PostInputs:
+    """Inputs of hc_post with the recipe in the module docstring."""
+    rng = np.random.default_rng(seed)
+    x = _bf16_normal(rng, T * D).reshape(T, D)
+    residual = _bf16_normal(rng, T * n * D).reshape(T, n, D)
+    post = rng.uniform(0.0, 2.0, size=(T, n)).astype(np.float32)
+    comb = rng.uniform(0.05, 0.45, size=(T, n, n)).astype(np.float32)
+    return PostInputs(T, n, D, x, residual, post, comb)

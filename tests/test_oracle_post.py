@@ -1,0 +1,120 @@
+"""The fp64 hc_post oracle (oracle/mhc_oracle_post.c) against what pins it, and the pins
+against planted mistakes.
+
+Pins:
+  permutation  comb[t] a permutation matrix that is not symmetric (a 4-cycle, and its
+               8-stream analogue) and post = 0: every output row is exactly the residual
+               row the permutation picks (bf16 passes through unchanged). Catches a
+               transposed comb, a residual indexed by the output stream, a dropped or
+               doubled residual term.
+  post only    residual = 0: out = bf16(post[i] * x[d]), rounded by this file's own
+               float64 -> bf16 rounding.
+  einsum       random inputs: the unrounded output equals NumPy's float64 einsum of the
+               same two terms to 1e-12 relative (a library routine as the second
+               implementation), and the bf16 output is its nearest bf16.
+Mutants: textual changes to the oracle source, each compiled and run through the pins.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+HERE = os.path.dirname(oracle.__file__)
+SRC = os.path.join(HERE, "mhc_oracle_post.c")
+FWD = os.path.join(HERE, "mhc_oracle.c")
+BWD = os.path.join(HERE, "mhc_oracle_bwd.c")
+
+
+def _bf16_round(v: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bits, nearest with ties to even, via exact float64 arithmetic."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    for idx, val in np.ndenumerate(v):
+        if val == 0.0:
+            out[idx] = 0x8000 if np.signbit(val) else 0
+            continue
+        m, e = np.frexp(abs(val))                  # val = m 2^e, m in [0.5, 1)
+        q = np.ldexp(m, 8)                         # 8 significant bits
+        lo = np.floor(q)
+        r = q - lo
+        q = lo + (1.0 if (r > 0.5 or (r == 0.5 and int(lo) % 2 == 1)) else 0.0)
+        f = np.float32(np.ldexp(q, e - 8) * (1 if val > 0 else -1))
+        out[idx] = np.frombuffer(np.float32(f).tobytes(), dtype=np.uint32)[0] >> 16
+    return out
+
+
+def pin_permutation(lib):
+    for n in (4, 8):
+        T, D = 3, 24
+        inp = synth.post_inputs(T, n, D, seed=5 + n)
+        perm = [(i + 1) % n for i in range(n)]          # a cycle: not its own transpose
+        comb = np.zeros((T, n, n), dtype=np.float32)
+        for i in range(n):
+            comb[:, i, perm[i]] = 1.0
+        r = oracle.post(inp.x, inp.residual, np.zeros((T, n), np.float32), comb, lib=lib)
+        for i in range(n):
+            assert np.array_equal(r.out_bf16[:, i, :], inp.residual[:, perm[i], :]), (n, i)
+
+
+def pin_post_only(lib):
+    T, n, D = 4, 4, 16
+    inp = synth.post_inputs(T, n, D, seed=9)
+    zeros = np.zeros_like(inp.residual)
+    r = oracle.post(inp.x, zeros, inp.post, inp.comb, lib=lib)
+    xf = synth.bf16_bits_to_f32(inp.x).astype(np.float64)
+    want = _bf16_round(inp.post.astype(np.float64)[:, :, None] * xf[:, None, :])
+    assert np.array_equal(r.out_bf16, want)
+
+
+def pin_einsum(lib):
+    T, n, D = 5, 4, 40
+    inp = synth.post_inputs(T, n, D, seed=13)
+    r = oracle.post(inp.x, inp.residual, inp.post, inp.comb, lib=lib)
+    xf = synth.bf16_bits_to_f32(inp.x).astype(np.float64)
+    rf = synth.bf16_bits_to_f32(inp.residual).astype(np.float64)
+    want = (np.einsum("ti,td->tid", inp.post.astype(np.float64), xf)
+            + np.einsum("tij,tjd->tid", inp.comb.astype(np.float64), rf))
+    assert np.allclose(r.out, want, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(r.out_bf16, _bf16_round(r.out))
+    assert np.all(r.out_abs >= np.abs(r.out) - 1e-12)
+
+
+PINS = [pin_permutation, pin_post_only, pin_einsum]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(None)
+
+
+MUTANTS = {
+    "comb_transposed": ("comb[(t * n + i) * n + j]", "comb[(t * n + j) * n + i]"),
+    "residual_by_output_stream": ("residual[(t * n + j) * (int64_t)D + d]", "residual[(t * n + i) * (int64_t)D + d]"),
+    "post_term_dropped": ("double acc = p * xv;", "double acc = 0.0;"),
+    "post_from_next_stream": ("const double p = (double)post[t * n + i];", "const double p = (double)post[t * n + (i + 1) % n];"),
+    "residual_term_dropped": ("acc += c * r;", "(void)r;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    src = open(SRC).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, name
+    c_path = tmp_path / "mutant_post.c"
+    so_path = tmp_path / "libmutant.so"
+    c_path.write_text(src.replace(old, new))
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-w", "-o", str(so_path),
+                    FWD, BWD, str(c_path), "-lm"], check=True)
+    lib = oracle.load_library(str(so_path))
+    caught = []
+    for pin in PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches mutant {name}"
