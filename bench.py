@@ -262,6 +262,76 @@ def main_backward(args):
     print(json.dumps(line), flush=True)
 
 
+POST_METRIC = "tokens/s and achieved HBM GB/s (% of peak) for hc_post (the mHC post-mapping), n=4"
+
+
+def post_algorithmic_bytes(T, n, D) -> int:
+    """hc_post moves x (2D) and the n streams (2nD) in, the n output streams (2nD) out,
+    plus post (4n) and comb (4n^2), once per token."""
+    return T * (2 * D + 2 * n * D + 4 * n + 4 * n * n + 2 * n * D)
+
+
+def main_post(args):
+    """--op post: one step = one mhc_post call at the large prefill shape (T = 16384,
+    n = 4, D = 7168)."""
+    import numpy as np
+    import torch
+
+    import mhc_hyper_connection_amd as mhc
+    import synth
+
+    T, n, D = 16384, 4, 7168
+    print(f"[bench] generating hc_post inputs T={T} n={n} D={D}", file=sys.stderr, flush=True)
+    pi = synth.post_inputs(T, n, D, seed=1004)
+    dev = torch.device("cuda", 0)
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    x, res, post, comb = (up(a) for a in (pi.x, pi.residual, pi.post, pi.comb))
+    out = torch.empty((T, n, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        mhc.mhc_post(x, res, post, comb, out=out)
+    torch.cuda.synchronize(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        mhc.mhc_post(x, res, post, comb, out=out)
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    call_us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / len(evs)
+    ab = post_algorithmic_bytes(T, n, D)
+    achieved = ab / (call_us * 1e-6) / 1e9
+    line = {
+        "metric": POST_METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "large_prefill_post", "T": T, "n": n, "D": D,
+                   "step": "one mhc_post call (one kernel)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "post_kernel",
+                     "algorithmic_bytes": ab, "avg_launch_us": call_us},
+    }
+    if not args.no_cpu:
+        import oracle
+        ntok = min(T, 4096)
+        threads = oracle.max_threads()
+        c0 = time.perf_counter()
+        oracle.post(pi.x[:ntok], pi.residual[:ntok], pi.post[:ntok], pi.comb[:ntok])
+        dt = time.perf_counter() - c0
+        line["cpu_baseline"] = {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                                "sample": f"first {ntok} of {T} tokens, fp64 C oracle, {threads} OpenMP threads, "
+                                          f"{dt:.2f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,9 +343,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain copy of this size first (for counter calibration)")
-    ap.add_argument("--op", choices=("forward", "backward"), default="forward",
+    ap.add_argument("--op", choices=("forward", "backward", "post"), default="forward",
                     help="forward (default): the pre-mapping forward line; backward: the "
-                         "MhcPre backward at the large prefill shape")
+                         "MhcPre backward at the large prefill shape; post: hc_post at that shape")
     ap.add_argument("--bwd-iters", type=int, default=20,
                     help="Sinkhorn iterations of the backward (0: the MhcPre backward)")
     ap.add_argument("--cpu-tokens-bwd", type=int, default=16384,
@@ -287,6 +357,9 @@ def main():
         sys.exit(2)
     if args.op == "backward":
         main_backward(args)
+        return
+    if args.op == "post":
+        main_post(args)
         return
 
     import torch

@@ -300,6 +300,40 @@ mhc_status mhc_pre_backward_workspace_size(const mhc_pre_bwd_params* params, siz
 mhc_status mhc_pre_backward(const mhc_pre_bwd_params* params, const mhc_pre_bwd_tensors* tensors,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ hc_post
+ *
+ * The mHC post-mapping (HcPre guide, mhpn.cn/news/2282827, section "mHC 架构与 HcPre 的
+ * 定位"): the layer output x is expanded back into the n streams by post (the forward's
+ * hPost) and added to the streams fused across streams by comb (the forward's hRes):
+ *     out[t][i][d] = post[t][i] x[t][d] + sum_j comb[t][i][j] residual[t][j][d]
+ * The expression the guide prints sums comb over its second index against a residual
+ * indexed by comb's first index, which fuses nothing although the text says the streams
+ * are fused; the sum runs over the residual's stream here. fp32 fused multiply-adds
+ * (post term first, then j in order), one rounding to bf16.
+ *   T >= 0; n: 4 or 8; D: a multiple of 8 in [8, 16384]
+ *   x        bf16 [T, D]       16-byte aligned    (the attention / MLP output)
+ *   residual bf16 [T, n, D]    16-byte aligned    (the n streams)
+ *   post     f32  [T, n]
+ *   comb     f32  [T, n, n]
+ *   out      bf16 [T, n, D]    16-byte aligned; must not alias the inputs
+ * Pointers may be NULL only when T == 0 (nothing is launched). Asynchronous on `stream`,
+ * no workspace, no allocation. Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
+typedef struct mhc_post_params {
+    int64_t T;
+    int32_t n;
+    int32_t D;
+} mhc_post_params;
+
+typedef struct mhc_post_tensors {
+    const uint16_t* x;
+    const uint16_t* residual;
+    const float* post;
+    const float* comb;
+    uint16_t* out;
+} mhc_post_tensors;
+
+mhc_status mhc_post(const mhc_post_params* params, const mhc_post_tensors* tensors, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,12 +16,12 @@ import math
 
 from ._binding import (FORWARD_EVENTS, MHC_ERR_NULLPTR, MHC_ERR_PARAM_INVALID,
                        MHC_ERR_RUNTIME, MHC_OK, STAGES, MhcError, Params, bwd_workspace_size,
-                       forward_path,
+                       forward_path, raw_post,
                        load, make_bwd_params, make_params, packed_size, raw_backward,
                        raw_forward, raw_forward_timed, raw_prepack, status_string, version,
                        workspace_size)
 
-__all__ = ["PreForward", "PreBackward", "mhc_pre", "mhc_pre_backward", "prepack", "version",
+__all__ = ["PreForward", "PreBackward", "mhc_pre", "mhc_pre_backward", "mhc_post", "prepack", "version",
            "status_string", "MhcError", "FORWARD_EVENTS", "STAGES",
            "make_params", "packed_size", "workspace_size", "load",
            "MHC_OK", "MHC_ERR_NULLPTR", "MHC_ERR_PARAM_INVALID", "MHC_ERR_RUNTIME"]
@@ -292,4 +292,24 @@ def mhc_pre_backward(x, phi, alpha, grad_h_in, grad_h_post, grad_h_res, inv_rms,
             rs(h_post, T, n), gamma, rs(grad_x_post, T, n, D),
             sum_out=rs(sum_out, 2 * num_iters, T, n), norm_out=rs(norm_out, 2 * num_iters, T, n, n))
     out["grad_x"] = out["grad_x"].reshape(*lead, n, D)
+    return out
+
+
+def mhc_post(x, residual, post, comb, *, out=None):
+    """hc_post: out[t, i, d] = post[t, i] x[t, d] + sum_j comb[t, i, j] residual[t, j, d].
+    x bf16 [T, D], residual bf16 [T, n, D], post f32 [T, n], comb f32 [T, n, n] on one
+    device; returns (or fills) bf16 [T, n, D]. The stream is torch's current stream."""
+    torch = _torch()
+    T, n, D = residual.shape
+    dev = residual.device
+    _check(x, "x", torch.bfloat16, (T, D), dev)
+    _check(residual, "residual", torch.bfloat16, (T, n, D), dev)
+    _check(post, "post", torch.float32, (T, n), dev)
+    _check(comb, "comb", torch.float32, (T, n, n), dev)
+    if out is None:
+        out = torch.empty((T, n, D), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, n, D), dev)
+    st = raw_post(T, n, D, _ptr(x), _ptr(residual), _ptr(post), _ptr(comb), _ptr(out), _stream(dev))
+    if st != MHC_OK:
+        raise MhcError(st, "mhc_post")
     return out

@@ -57,7 +57,7 @@ class BwdTensors(ctypes.Structure):
 EXPORTS = ("mhc_version", "mhc_status_string", "mhc_pre_packed_size",
            "mhc_pre_workspace_size", "mhc_pre_prepack", "mhc_pre_forward",
            "mhc_pre_forward_timed", "mhc_pre_forward_path", "mhc_pre_backward_workspace_size",
-           "mhc_pre_backward")
+           "mhc_pre_backward", "mhc_post")
 
 # MHC_FORWARD_EVENTS: events of mhc_pre_forward_timed (before the first kernel, then one
 # after each of pack, projection, epilogue, hIn)
@@ -65,6 +65,14 @@ FORWARD_EVENTS = 5
 STAGES = ("pack", "projection", "epilogue", "hin")
 
 _lib = None
+
+
+class PostParams(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
+class PostTensors(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in ("x", "residual", "post", "comb", "out")]
 
 
 def load(path: str | None = None):
@@ -98,6 +106,8 @@ def load(path: str | None = None):
     lib.mhc_pre_backward_workspace_size.restype = ctypes.c_int32
     lib.mhc_pre_backward_workspace_size.argtypes = [ctypes.POINTER(BwdParams), ctypes.POINTER(ctypes.c_size_t)]
     lib.mhc_pre_backward.restype = ctypes.c_int32
+    lib.mhc_post.restype = ctypes.c_int32
+    lib.mhc_post.argtypes = [ctypes.POINTER(PostParams), ctypes.POINTER(PostTensors), ctypes.c_void_p]
     lib.mhc_pre_forward_path.restype = ctypes.c_int32
     lib.mhc_pre_forward_path.argtypes = [ctypes.POINTER(Params), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.mhc_pre_backward.argtypes = [ctypes.POINTER(BwdParams), ctypes.POINTER(BwdTensors),
@@ -179,3 +189,9 @@ def bwd_workspace_size(params: BwdParams) -> int:
 def raw_backward(params: BwdParams, ptrs: dict, ws_ptr, ws_bytes, stream) -> int:
     t = BwdTensors(*[ptrs.get(f) for f in BWD_TENSOR_FIELDS])
     return int(load().mhc_pre_backward(ctypes.byref(params), ctypes.byref(t), ws_ptr, ws_bytes, stream))
+
+
+def raw_post(T, n, D, x_ptr, residual_ptr, post_ptr, comb_ptr, out_ptr, stream) -> int:
+    p = PostParams(int(T), int(n), int(D))
+    t = PostTensors(x_ptr, residual_ptr, post_ptr, comb_ptr, out_ptr)
+    return int(load().mhc_post(ctypes.byref(p), ctypes.byref(t), stream))

@@ -285,3 +285,23 @@ mhc_status mhc_pre_backward(const mhc_pre_bwd_params* params, const mhc_pre_bwd_
 }
 
 }  // extern "C"
+
+extern "C" {
+
+mhc_status mhc_post(const mhc_post_params* params, const mhc_post_tensors* t, void* stream)
+{
+    if (!params || !t) return MHC_ERR_NULLPTR;
+    if (params->T < 0 || (params->n != 4 && params->n != 8)) return MHC_ERR_PARAM_INVALID;
+    if (params->D < 8 || params->D % 8 != 0 || params->D > mhc::kMaxD) return MHC_ERR_PARAM_INVALID;
+    if (params->T == 0) return MHC_OK;
+    if (!t->x || !t->residual || !t->post || !t->comb || !t->out) return MHC_ERR_NULLPTR;
+    if (!aligned(t->x, 16) || !aligned(t->residual, 16) || !aligned(t->out, 16) || !aligned(t->post, 4) ||
+        !aligned(t->comb, 4))
+        return MHC_ERR_PARAM_INVALID;
+    return mhc::launch_post(params->T, params->n, params->D, t->x, t->residual, t->post, t->comb, t->out,
+                            stream) == 0
+               ? MHC_OK
+               : MHC_ERR_RUNTIME;
+}
+
+}  // extern "C"

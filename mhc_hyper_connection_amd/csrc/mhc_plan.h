@@ -306,5 +306,8 @@ int launch_forward(const Plan& p, const ForwardArgs& a, void* stream, void* cons
 // device: 1 the single-read kernel, 0 the four-kernel path.
 int forward_path(const Plan& p, bool has_pre_mix);
 int record_event(void* event, void* stream);
+// hc_post (mhc_post.hip): out = post x + comb residual per token; 0 or the HIP error code.
+int launch_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* residual, const float* post,
+                const float* comb, uint16_t* out, void* stream);
 
 }  // namespace mhc

@@ -1,0 +1,82 @@
+// mhc_post.hip -- gfx950 kernel of hc_post, the mHC post-mapping (HcPre guide,
+// mhpn.cn/news/2282827, section "mHC 架构与 HcPre 的定位": the layer output expanded into
+// the n streams by post, added to the streams fused across streams by comb):
+//     out[t][i][d] = post[t][i] x[t][d] + sum_j comb[t][i][j] residual[t][j][d]
+// (the guide's printed expression mixes nothing; the summed index of comb is the
+// residual's stream, the usual res-mapping product).
+//
+// One thread per octet (8 positions) of one token: it reads the octet of x and of each of
+// the n residual streams (16-byte loads, consecutive threads on consecutive octets), the
+// token's post and comb (shared by the token's threads, cached), and writes the octet of
+// each of the n output streams. fp32 fused multiply-adds in the order post term, then
+// j = 0 .. n-1; one rounding to bf16. Memory-bound: per token 2D + 2nD bytes read
+// (+ 4n + 4n^2), 2nD written.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "mhc_device.h"
+#include "mhc_plan.h"
+
+namespace mhc {
+namespace {
+
+template <int N>
+__global__ void __launch_bounds__(256)
+post_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ residual,
+            const float* __restrict__ post, const float* __restrict__ comb,
+            uint16_t* __restrict__ out, int64_t T, int D)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int D8 = D / 8;
+    const int64_t t = idx / D8;
+    const int d8 = (int)(idx % D8);
+    if (t >= T) return;
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(x + t * (int64_t)D + d8 * 8);
+    u32x4 rv[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+        rv[j] = *reinterpret_cast<const u32x4*>(residual + (t * N + j) * (int64_t)D + d8 * 8);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float p = post[t * N + i];
+        float c[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) c[j] = comb[(t * N + i) * N + j];
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = p * bf16_lo(xv[e]);
+            acc[2 * e + 1] = p * bf16_hi(xv[e]);
+        }
+#pragma unroll
+        for (int j = 0; j < N; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = fmaf(c[j], bf16_lo(rv[j][e]), acc[2 * e]);
+                acc[2 * e + 1] = fmaf(c[j], bf16_hi(rv[j][e]), acc[2 * e + 1]);
+            }
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+        // the output is not read again here: stream it past the caches
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + (t * N + i) * (int64_t)D + d8 * 8));
+    }
+}
+
+}  // namespace
+
+int launch_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* residual, const float* post,
+                const float* comb, uint16_t* out, void* stream)
+{
+    if (T <= 0) return 0;
+    const int64_t items = T * (int64_t)(D / 8);
+    const dim3 grid((unsigned)((items + 255) / 256));
+    hipStream_t st = (hipStream_t)stream;
+    if (n == 4) hipLaunchKernelGGL(post_kernel<4>, grid, dim3(256), 0, st, x, residual, post, comb, out, T, D);
+    else if (n == 8) hipLaunchKernelGGL(post_kernel<8>, grid, dim3(256), 0, st, x, residual, post, comb, out, T, D);
+    else return (int)hipErrorInvalidValue;
+    return (int)hipGetLastError();
+}
+
+}  // namespace mhc
