@@ -83,6 +83,12 @@ def _bind(lib):
         lib.oracle_mhc_post.restype = ctypes.c_int
         lib.oracle_mhc_post.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp,
                                         dp, dp, dp]
+    if hasattr(lib, "oracle_pre_sinkhorn"):
+        lib.oracle_inv_rms.restype = ctypes.c_int
+        lib.oracle_inv_rms.argtypes = [ctypes.POINTER(_Cfg), dp, dp, ctypes.c_int]
+        lib.oracle_pre_sinkhorn.restype = ctypes.c_int
+        lib.oracle_pre_sinkhorn.argtypes = [ctypes.POINTER(_Cfg), dp, dp, dp, dp, dp, dp,
+                                            ctypes.POINTER(_Out), ctypes.c_int]
     lib.oracle_pre_backward.restype = ctypes.c_int
     lib.oracle_pre_backward.argtypes = [ctypes.POINTER(_BwdIn), dp, ctypes.c_int64,
                                         ctypes.POINTER(_BwdOut), ctypes.c_int]
@@ -182,6 +188,57 @@ def forward(x_bits, phi, alpha, bias, gamma=None, pre_mix=None, *, num_iters=20,
     rc = (lib or _load()).oracle_pre_forward(
         ctypes.byref(cfg), _ptr(x_bits), _ptr(phi), _ptr(alpha), _ptr(bias), _ptr(gamma),
         _ptr(pre_mix), _ptr(tok), ntok, ctypes.byref(out), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem description")
+    return res
+
+
+def inv_rms(x_bits, *, norm_eps=1e-6, nthreads=0, lib=None) -> np.ndarray:
+    """invRms alone: x_bits uint16 bf16 bits [T, n, D] -> float64 [T]."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    if x_bits.ndim != 3:
+        raise ValueError("x must be [T, n, D]")
+    T, n, D = x_bits.shape
+    out = np.empty(T)
+    cfg = _Cfg(T, n, D, 3, 1, float(norm_eps), 0.0)
+    if (lib or _load()).oracle_inv_rms(ctypes.byref(cfg), _ptr(x_bits), _ptr(out), int(nthreads)) != 0:
+        raise ValueError("oracle rejected the problem description")
+    return out
+
+
+def pre_sinkhorn(x_bits, h_mix, inv_rms_in, alpha, bias, pre_mix=None, *, num_iters=20,
+                 hc_eps=1e-6, want_sinkhorn_steps=True, nthreads=0, lib=None) -> OracleResult:
+    """The Sinkhorn stage alone: from given mixes h_mix [T, M] and invRms [T] (converted
+    to float64 exactly) and x [T, n, D] to hPre, hPost, hRes, the Sinkhorn planes and hIn.
+    The result's inv_rms and h_mix fields echo the inputs."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    if x_bits.ndim != 3:
+        raise ValueError("x must be [T, n, D]")
+    T, n, D = x_bits.shape
+    alpha = np.ascontiguousarray(alpha, dtype=np.float32).reshape(-1)
+    n_alpha = int(alpha.shape[0])
+    M = n * n + 2 * n if n_alpha == 3 else 2 * n
+    bias = np.ascontiguousarray(bias, dtype=np.float32).reshape(-1)
+    h_mix = np.ascontiguousarray(h_mix, dtype=np.float64).reshape(T, M)
+    inv_in = np.ascontiguousarray(inv_rms_in, dtype=np.float64).reshape(T)
+    if bias.shape != (M,):
+        raise ValueError(f"bias must be [{M}]")
+    if pre_mix is not None:
+        pre_mix = np.ascontiguousarray(pre_mix, dtype=np.float32).reshape(T, n)
+    steps = 2 * num_iters if n_alpha == 3 else 0
+    res = OracleResult(
+        inv_rms=inv_in.copy(), h_mix=h_mix.copy(), h_pre=np.empty((T, n)),
+        h_post=np.empty((T, n)), h_res=np.empty((T, n, n)),
+        sum_out=np.empty((steps, T, n)) if (steps and want_sinkhorn_steps) else None,
+        norm_out=np.empty((steps, T, n, n)) if (steps and want_sinkhorn_steps) else None,
+        h_in=np.empty((T, D)), h_in_bf16=np.empty((T, D), dtype=np.uint16))
+    ptrs = {f: _ptr(getattr(res, f)) for f, _ in _Out._fields_}
+    ptrs["inv_rms"] = ptrs["h_mix"] = None
+    out = _Out(*[ptrs[f] for f, _ in _Out._fields_])
+    cfg = _Cfg(T, n, D, n_alpha, int(num_iters), 1e-6, float(hc_eps))
+    rc = (lib or _load()).oracle_pre_sinkhorn(
+        ctypes.byref(cfg), _ptr(x_bits), _ptr(h_mix), _ptr(inv_in), _ptr(alpha), _ptr(bias),
+        _ptr(pre_mix), ctypes.byref(out), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the problem description")
     return res

@@ -134,42 +134,36 @@ static int mix_rows(const oracle_cfg* c)
     return c->n_alpha == 3 ? c->n * c->n + 2 * c->n : 2 * c->n;
 }
 
-/* One token. `slot` is the token's position in the output arrays, `t` its index in x. */
-static void one_token(const oracle_cfg* c, int64_t ntok, int64_t slot, int64_t t,
-                      const uint16_t* x, const float* phi, const float* alpha,
-                      const float* bias, const float* gamma, const float* pre_mix,
-                      const oracle_out* o, double* scratch)
+/* invRms = (mean(xFlat^2) + normEps)^(-1/2) of one token's K = n*D entries xt, the
+ * mean taken over all of them (R1, R2). */
+static double token_inv_rms(const uint16_t* xt, int n, int D, double norm_eps)
 {
-    const int n = c->n;
-    const int D = c->D;
-    const int64_t K = (int64_t)n * D;           /* length of xFlat */
-    const int M = mix_rows(c);
-    const double eps = c->hc_eps;
-    const uint16_t* xt = x + t * K;
-
-    double* hmix = scratch;                     /* [M]   */
-    double* A = scratch + M;                    /* [n*n] */
-    double* s = A + n * n;                      /* [n]   */
-
-    /* invRms = (mean(xFlat^2) + normEps)^(-1/2), mean over all n*D entries (R1, R2). */
+    const int64_t K = (int64_t)n * D;
     double ss = 0.0;
     for (int64_t k = 0; k < K; ++k) {
         double v = oracle_bf16_to_double(xt[k]);
         ss += v * v;
     }
-    const double inv_rms = 1.0 / sqrt(ss / (double)K + c->norm_eps);
+    return 1.0 / sqrt(ss / (double)K + norm_eps);
+}
 
-    /* hMix = xGamma . phi^T with xGamma = xFlat (.) gammaFlat (R3). */
-    for (int m = 0; m < M; ++m) {
-        const float* row = phi + (int64_t)m * K;
-        double acc = 0.0;
-        for (int64_t k = 0; k < K; ++k) {
-            double xg = oracle_bf16_to_double(xt[k]);
-            if (gamma) xg *= (double)gamma[k];
-            acc += xg * (double)row[k];
-        }
-        hmix[m] = acc;
-    }
+/* Everything of one token that follows from its mixes hmix [M] and its invRms: the
+ * gates, the Sinkhorn and hIn. `slot` is the token's position in the output arrays,
+ * `t` its index in x. scratch holds n*n + n doubles. */
+static void finish_token(const oracle_cfg* c, int64_t ntok, int64_t slot, int64_t t,
+                         const uint16_t* x, const double* hmix, double inv_rms,
+                         const float* alpha, const float* bias, const float* pre_mix,
+                         const oracle_out* o, double* scratch)
+{
+    const int n = c->n;
+    const int D = c->D;
+    const int64_t K = (int64_t)n * D;
+    const int M = mix_rows(c);
+    const double eps = c->hc_eps;
+    const uint16_t* xt = x + t * K;
+
+    double* A = scratch;                        /* [n*n] */
+    double* s = A + n * n;                      /* [n]   */
 
     /* w = hMix * invRms, split into pPre = w[0:n], pPost = w[n:2n], pRes = w[2n:] (R4). */
     double hpre[8], hpost[8];
@@ -259,6 +253,33 @@ static void one_token(const oracle_cfg* c, int64_t ntok, int64_t slot, int64_t t
     }
 }
 
+/* One token of the whole forward. scratch holds M + n*n + n doubles. */
+static void one_token(const oracle_cfg* c, int64_t ntok, int64_t slot, int64_t t,
+                      const uint16_t* x, const float* phi, const float* alpha,
+                      const float* bias, const float* gamma, const float* pre_mix,
+                      const oracle_out* o, double* scratch)
+{
+    const int64_t K = (int64_t)c->n * c->D;     /* length of xFlat */
+    const int M = mix_rows(c);
+    const uint16_t* xt = x + t * K;
+    double* hmix = scratch;                     /* [M] */
+
+    const double inv_rms = token_inv_rms(xt, c->n, c->D, c->norm_eps);
+
+    /* hMix = xGamma . phi^T with xGamma = xFlat (.) gammaFlat (R3). */
+    for (int m = 0; m < M; ++m) {
+        const float* row = phi + (int64_t)m * K;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double xg = oracle_bf16_to_double(xt[k]);
+            if (gamma) xg *= (double)gamma[k];
+            acc += xg * (double)row[k];
+        }
+        hmix[m] = acc;
+    }
+    finish_token(c, ntok, slot, t, x, hmix, inv_rms, alpha, bias, pre_mix, o, scratch + M);
+}
+
 /* Forward for the listed tokens (tokens == NULL: all T tokens, in order).
  * Returns 0 on success, -1 on an invalid description. nthreads <= 0: OpenMP default. */
 int oracle_pre_forward(const oracle_cfg* c, const uint16_t* x, const float* phi,
@@ -294,6 +315,62 @@ int oracle_pre_forward(const oracle_cfg* c, const uint16_t* x, const float* phi,
                 int64_t t = tokens ? tokens[j] : j;
                 one_token(c, ntok, j, t, x, phi, alpha, bias, gamma, pre_mix, o, scratch);
             }
+            free(scratch);
+        }
+    }
+    return failed ? -1 : 0;
+}
+
+/* InvRms on its own, the standalone form of the normalisation step ([HC] "function
+ * description": the reciprocal of the RMS over the token's n*D entries, plus normEps
+ * under the root). inv_rms: [T] doubles. Returns 0, or -1 on an invalid description. */
+int oracle_inv_rms(const oracle_cfg* c, const uint16_t* x, double* inv_rms, int nthreads)
+{
+    if (!c || !x || !inv_rms) return -1;
+    if (c->n < 1 || c->n > 8 || c->D < 1 || c->T < 0) return -1;
+    const int64_t K = (int64_t)c->n * c->D;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < c->T; ++t) inv_rms[t] = token_inv_rms(x + t * K, c->n, c->D, c->norm_eps);
+    return 0;
+}
+
+/* The Sinkhorn stage on its own ([HC] "function description": the standalone operator
+ * takes the mixes and the rsqrt instead of computing them): given hMix [T][M] and invRms
+ * [T] (doubles), every output that follows from them -- hPre, hPost, hRes, the Sinkhorn
+ * planes and hIn -- exactly as the whole forward derives them (R4 to R10). o->inv_rms
+ * and o->h_mix must be NULL. Returns 0, or -1 on an invalid description. */
+int oracle_pre_sinkhorn(const oracle_cfg* c, const uint16_t* x, const double* h_mix,
+                        const double* inv_rms, const float* alpha, const float* bias,
+                        const float* pre_mix, const oracle_out* o, int nthreads)
+{
+    if (!c || !x || !h_mix || !inv_rms || !alpha || !bias || !o) return -1;
+    if (o->inv_rms || o->h_mix) return -1;
+    if (c->n < 1 || c->n > 8 || c->D < 1 || c->T < 0) return -1;
+    if (c->n_alpha != 2 && c->n_alpha != 3) return -1;
+    if (c->n_alpha == 3 && c->num_iters < 1) return -1;
+    const int M = mix_rows(c);
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double* scratch = (double*)malloc(((size_t)c->n * c->n + (size_t)c->n) * sizeof(double));
+        if (!scratch) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t t = 0; t < c->T; ++t)
+                finish_token(c, c->T, t, t, x, h_mix + t * M, inv_rms[t], alpha, bias, pre_mix, o,
+                             scratch);
             free(scratch);
         }
     }

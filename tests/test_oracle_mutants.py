@@ -16,10 +16,10 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "mhc_oracle.c")
 BWD = os.path.join(os.path.dirname(oracle.__file__), "mhc_oracle_bwd.c")   # built beside it, unchanged
 
 MUTANTS = {
-    "rms_mean_over_D": ("ss / (double)K + c->norm_eps", "ss / (double)D + c->norm_eps"),
-    "rms_without_norm_eps": ("sqrt(ss / (double)K + c->norm_eps)", "sqrt(ss / (double)K)"),
-    "rms_on_gamma_scaled_x": ("ss += v * v;", "ss += v * v * (gamma ? (double)gamma[k] * gamma[k] : 1.0);"),
-    "gamma_indexed_by_d_only": ("if (gamma) xg *= (double)gamma[k];", "if (gamma) xg *= (double)gamma[k % D];"),
+    "rms_mean_over_D": ("ss / (double)K + norm_eps", "ss / (double)D + norm_eps"),
+    "rms_without_norm_eps": ("sqrt(ss / (double)K + norm_eps)", "sqrt(ss / (double)K)"),
+    "rms_on_x_squared_twice": ("ss += v * v;", "ss += v * v * v * v;"),
+    "gamma_indexed_by_d_only": ("if (gamma) xg *= (double)gamma[k];", "if (gamma) xg *= (double)gamma[k % c->D];"),
     "phi_transposed": ("acc += xg * (double)row[k];", "acc += xg * (double)phi[k * M + m]; (void)row;"),
     "w_not_normalised": ("double p_pre = hmix[i] * inv_rms;", "double p_pre = hmix[i];"),
     "hpre_without_eps": ("hpre[i] = sigmoid((double)alpha[0] * p_pre + (double)bias[i]) + eps;",
