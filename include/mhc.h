@@ -300,6 +300,58 @@ mhc_status mhc_pre_backward_workspace_size(const mhc_pre_bwd_params* params, siz
 mhc_status mhc_pre_backward(const mhc_pre_bwd_params* params, const mhc_pre_bwd_tensors* tensors,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ standalone stages
+ *
+ * The HcPre guide (mhpn.cn/news/2282827, "功能说明") splits the pre-mapping into
+ * invRms, the mixing projection and the Sinkhorn stage, and names invRms and the Sinkhorn
+ * stage as operators of their own; the Sinkhorn operator takes the mixes and the rsqrt as
+ * inputs instead of computing them. These two entry points run those stages alone, on
+ * the same per-token arithmetic as mhc_pre_forward; they serve callers that already hold
+ * the mixes (a projection of their own) and tests that check one stage at a time.
+ *
+ * mhc_pre_inv_rms: inv_rms[t] = 1 / sqrt(mean over the n*D entries of x[t]^2 + norm_eps)
+ * (the same reading of the mean as mhc_pre_forward; aclnnMhcPreV2 guide, section 3).
+ * Squares and sums in fp64, one rounding to f32.
+ *   params     validated as for mhc_pre_forward (T, n, D and norm_eps are used)
+ *   x          bf16 [T, n, D], 16-byte aligned
+ *   inv_rms    f32  [T]
+ * Pointers may be NULL only when T == 0. Asynchronous on `stream`, no workspace, no
+ * allocation. Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
+mhc_status mhc_pre_inv_rms(const mhc_pre_params* params, const uint16_t* x, float* inv_rms,
+                           void* stream);
+
+/* mhc_pre_sinkhorn: from the mixes hMix (the un-normalised projection, mhc_pre_forward's
+ * h_mix) and invRms, everything the forward derives from them: hPre, hPost, the Sinkhorn
+ * of the res logits with its planes, and hIn (aclnnMhcPreSinkhorn guide, m.mzlw.cn/news/
+ * 197063, sections 3.1 and 3.2; aclnnMhcPreV2 guide, section 3). Outputs follow the rules
+ * of mhc_pre_tensors, except that h_pre is always required (it carries the hIn weights
+ * when pre_mix is not given).
+ *   params     as for mhc_pre_forward; need_backward makes sum_out / norm_out mandatory
+ *              (n_alpha == 3)
+ * Inputs:  x bf16 [T, n, D] (16-byte aligned), h_mix f32 [T, M], inv_rms f32 [T],
+ *          alpha f32 [n_alpha], bias f32 [M], pre_mix f32 [T, n] (optional)
+ * Outputs: h_in bf16 [T, D] (16-byte aligned), h_pre, h_post f32 [T, n], h_res f32 [T, n, n]
+ *          (required when n_alpha == 3), sum_out / norm_out as in mhc_pre_tensors
+ * Pointers may be NULL only when T == 0. Asynchronous on `stream`, no workspace, no
+ * allocation. Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
+typedef struct mhc_pre_sinkhorn_tensors {
+    const uint16_t* x;
+    const float* h_mix;
+    const float* inv_rms;
+    const float* alpha;
+    const float* bias;
+    const float* pre_mix;
+    uint16_t* h_in;
+    float* h_pre;
+    float* h_post;
+    float* h_res;
+    float* sum_out;
+    float* norm_out;
+} mhc_pre_sinkhorn_tensors;
+
+mhc_status mhc_pre_sinkhorn(const mhc_pre_params* params, const mhc_pre_sinkhorn_tensors* tensors,
+                            void* stream);
+
 /* ------------------------------------------------------------------ hc_post
  *
  * The mHC post-mapping (HcPre guide, mhpn.cn/news/2282827, section "mHC 架构与 HcPre 的

@@ -16,12 +16,13 @@ import math
 
 from ._binding import (FORWARD_EVENTS, MHC_ERR_NULLPTR, MHC_ERR_PARAM_INVALID,
                        MHC_ERR_RUNTIME, MHC_OK, STAGES, MhcError, Params, bwd_workspace_size,
-                       forward_path, raw_post,
+                       forward_path, raw_inv_rms, raw_post, raw_sinkhorn,
                        load, make_bwd_params, make_params, packed_size, raw_backward,
                        raw_forward, raw_forward_timed, raw_prepack, status_string, version,
                        workspace_size)
 
-__all__ = ["PreForward", "PreBackward", "mhc_pre", "mhc_pre_backward", "mhc_post", "prepack", "version",
+__all__ = ["PreForward", "PreBackward", "mhc_pre", "mhc_pre_backward", "mhc_post", "mhc_pre_inv_rms",
+           "mhc_pre_sinkhorn", "prepack", "version",
            "status_string", "MhcError", "FORWARD_EVENTS", "STAGES",
            "make_params", "packed_size", "workspace_size", "load",
            "MHC_OK", "MHC_ERR_NULLPTR", "MHC_ERR_PARAM_INVALID", "MHC_ERR_RUNTIME"]
@@ -313,3 +314,53 @@ def mhc_post(x, residual, post, comb, *, out=None):
     if st != MHC_OK:
         raise MhcError(st, "mhc_post")
     return out
+
+
+def mhc_pre_inv_rms(x, *, norm_eps=1e-6):
+    """invRms alone: x bf16 [T, n, D] -> f32 [T] on x's device and torch's current stream."""
+    torch = _torch()
+    T, n, D = x.shape
+    _check(x, "x", torch.bfloat16, (T, n, D), x.device)
+    out = torch.empty((T,), dtype=torch.float32, device=x.device)
+    params = make_params(T, n, D, norm_eps=norm_eps)
+    st = raw_inv_rms(params, _ptr(x), _ptr(out), _stream(x.device))
+    if st != MHC_OK:
+        raise MhcError(st, "mhc_pre_inv_rms")
+    return out
+
+
+def mhc_pre_sinkhorn(x, h_mix, inv_rms, alpha, bias, pre_mix=None, *, num_iters=20, hc_eps=1e-6,
+                     need_backward=False):
+    """The Sinkhorn stage alone, from given mixes h_mix f32 [T, M] and inv_rms f32 [T]
+    with x bf16 [T, n, D]. Returns (h_in, h_pre, h_post, h_res, extras); extras holds
+    sum_out and norm_out when need_backward is set and alpha has 3 entries."""
+    torch = _torch()
+    T, n, D = x.shape
+    dev = x.device
+    n_alpha = int(alpha.shape[0])
+    M = n * n + 2 * n if n_alpha == 3 else 2 * n
+    _check(x, "x", torch.bfloat16, (T, n, D), dev)
+    _check(h_mix, "h_mix", torch.float32, (T, M), dev)
+    _check(inv_rms, "inv_rms", torch.float32, (T,), dev)
+    _check(alpha, "alpha", torch.float32, (n_alpha,), dev)
+    _check(bias, "bias", torch.float32, (M,), dev)
+    if pre_mix is not None:
+        _check(pre_mix, "pre_mix", torch.float32, (T, n), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"h_in": torch.empty((T, D), dtype=torch.bfloat16, device=dev),
+           "h_pre": torch.empty((T, n), **f32), "h_post": torch.empty((T, n), **f32),
+           "h_res": torch.empty((T, n, n), **f32)}
+    extras = {}
+    if need_backward and n_alpha == 3:
+        extras["sum_out"] = torch.empty((2 * num_iters, T, n), **f32)
+        extras["norm_out"] = torch.empty((2 * num_iters, T, n, n), **f32)
+    params = make_params(T, n, D, n_alpha=n_alpha, num_iters=num_iters, hc_eps=hc_eps,
+                         need_backward=need_backward)
+    ptrs = {"x": _ptr(x), "h_mix": _ptr(h_mix), "inv_rms": _ptr(inv_rms), "alpha": _ptr(alpha),
+            "bias": _ptr(bias), "pre_mix": None if pre_mix is None else _ptr(pre_mix)}
+    ptrs.update({k: _ptr(v) for k, v in out.items()})
+    ptrs.update({k: _ptr(v) for k, v in extras.items()})
+    st = raw_sinkhorn(params, ptrs, _stream(dev))
+    if st != MHC_OK:
+        raise MhcError(st, "mhc_pre_sinkhorn")
+    return out["h_in"], out["h_pre"], out["h_post"], out["h_res"], extras

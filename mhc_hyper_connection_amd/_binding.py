@@ -57,7 +57,7 @@ class BwdTensors(ctypes.Structure):
 EXPORTS = ("mhc_version", "mhc_status_string", "mhc_pre_packed_size",
            "mhc_pre_workspace_size", "mhc_pre_prepack", "mhc_pre_forward",
            "mhc_pre_forward_timed", "mhc_pre_forward_path", "mhc_pre_backward_workspace_size",
-           "mhc_pre_backward", "mhc_post")
+           "mhc_pre_backward", "mhc_post", "mhc_pre_inv_rms", "mhc_pre_sinkhorn")
 
 # MHC_FORWARD_EVENTS: events of mhc_pre_forward_timed (before the first kernel, then one
 # after each of pack, projection, epilogue, hIn)
@@ -73,6 +73,14 @@ class PostParams(ctypes.Structure):
 
 class PostTensors(ctypes.Structure):
     _fields_ = [(f, ctypes.c_void_p) for f in ("x", "residual", "post", "comb", "out")]
+
+
+SINKHORN_TENSOR_FIELDS = ("x", "h_mix", "inv_rms", "alpha", "bias", "pre_mix", "h_in", "h_pre",
+                          "h_post", "h_res", "sum_out", "norm_out")
+
+
+class SinkhornTensors(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in SINKHORN_TENSOR_FIELDS]
 
 
 def load(path: str | None = None):
@@ -108,6 +116,10 @@ def load(path: str | None = None):
     lib.mhc_pre_backward.restype = ctypes.c_int32
     lib.mhc_post.restype = ctypes.c_int32
     lib.mhc_post.argtypes = [ctypes.POINTER(PostParams), ctypes.POINTER(PostTensors), ctypes.c_void_p]
+    lib.mhc_pre_inv_rms.restype = ctypes.c_int32
+    lib.mhc_pre_inv_rms.argtypes = [ctypes.POINTER(Params), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mhc_pre_sinkhorn.restype = ctypes.c_int32
+    lib.mhc_pre_sinkhorn.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(SinkhornTensors), ctypes.c_void_p]
     lib.mhc_pre_forward_path.restype = ctypes.c_int32
     lib.mhc_pre_forward_path.argtypes = [ctypes.POINTER(Params), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
     lib.mhc_pre_backward.argtypes = [ctypes.POINTER(BwdParams), ctypes.POINTER(BwdTensors),
@@ -195,3 +207,12 @@ def raw_post(T, n, D, x_ptr, residual_ptr, post_ptr, comb_ptr, out_ptr, stream) 
     p = PostParams(int(T), int(n), int(D))
     t = PostTensors(x_ptr, residual_ptr, post_ptr, comb_ptr, out_ptr)
     return int(load().mhc_post(ctypes.byref(p), ctypes.byref(t), stream))
+
+
+def raw_inv_rms(params: Params, x_ptr, inv_rms_ptr, stream) -> int:
+    return int(load().mhc_pre_inv_rms(ctypes.byref(params), x_ptr, inv_rms_ptr, stream))
+
+
+def raw_sinkhorn(params: Params, ptrs: dict, stream) -> int:
+    t = SinkhornTensors(*[ptrs.get(f) for f in SINKHORN_TENSOR_FIELDS])
+    return int(load().mhc_pre_sinkhorn(ctypes.byref(params), ctypes.byref(t), stream))

@@ -305,3 +305,63 @@ mhc_status mhc_post(const mhc_post_params* params, const mhc_post_tensors* t, vo
 }
 
 }  // extern "C"
+
+extern "C" {
+
+mhc_status mhc_pre_inv_rms(const mhc_pre_params* params, const uint16_t* x, float* inv_rms, void* stream)
+{
+    if (!params) return MHC_ERR_NULLPTR;
+    mhc::Geometry g;
+    mhc_status st = check_params(params, &g);
+    if (st != MHC_OK) return st;
+    if (params->T < 0) return MHC_ERR_PARAM_INVALID;
+    if (params->T == 0) return MHC_OK;
+    if (!x || !inv_rms) return MHC_ERR_NULLPTR;
+    if (!aligned(x, 16) || !aligned(inv_rms, 4)) return MHC_ERR_PARAM_INVALID;
+    return mhc::launch_inv_rms(params->T, params->n, params->D, params->norm_eps, x, inv_rms, stream) == 0
+               ? MHC_OK
+               : MHC_ERR_RUNTIME;
+}
+
+mhc_status mhc_pre_sinkhorn(const mhc_pre_params* params, const mhc_pre_sinkhorn_tensors* t, void* stream)
+{
+    if (!params || !t) return MHC_ERR_NULLPTR;
+    mhc::Geometry g;
+    mhc_status st = check_params(params, &g);
+    if (st != MHC_OK) return st;
+    if (params->T < 0) return MHC_ERR_PARAM_INVALID;
+    const bool res_branch = params->n_alpha == 3;
+    if (!res_branch && (t->sum_out || t->norm_out)) return MHC_ERR_PARAM_INVALID;
+    if (params->T == 0) return MHC_OK;
+    if (!t->x || !t->h_mix || !t->inv_rms || !t->alpha || !t->bias || !t->h_in || !t->h_pre || !t->h_post)
+        return MHC_ERR_NULLPTR;
+    if (res_branch && !t->h_res) return MHC_ERR_NULLPTR;
+    if (params->need_backward && res_branch && (!t->sum_out || !t->norm_out)) return MHC_ERR_PARAM_INVALID;
+    if (!aligned(t->x, 16) || !aligned(t->h_in, 16)) return MHC_ERR_PARAM_INVALID;
+    const void* f32s[] = {t->h_mix, t->inv_rms, t->alpha, t->bias, t->pre_mix, t->h_pre, t->h_post,
+                          t->h_res, t->sum_out, t->norm_out};
+    for (const void* q : f32s)
+        if (q && !aligned(q, 4)) return MHC_ERR_PARAM_INVALID;
+
+    mhc::ForwardArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.x = t->x;
+    a.alpha = t->alpha;
+    a.bias = t->bias;
+    a.pre_mix = t->pre_mix;
+    a.h_in = t->h_in;
+    a.h_pre = t->h_pre;
+    a.h_post = t->h_post;
+    a.h_res = t->h_res;
+    a.sum_out = res_branch ? t->sum_out : nullptr;
+    a.norm_out = res_branch ? t->norm_out : nullptr;
+    a.num_iters = params->num_iters;
+    a.norm_eps = params->norm_eps;
+    a.hc_eps = params->hc_eps;
+    return mhc::launch_pre_sinkhorn(params->T, params->n, params->D, params->n_alpha, a, t->h_mix, t->inv_rms,
+                                    stream) == 0
+               ? MHC_OK
+               : MHC_ERR_RUNTIME;
+}
+
+}  // extern "C"

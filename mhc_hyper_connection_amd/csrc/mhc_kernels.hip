@@ -28,6 +28,11 @@
 //                    keep their weights in LDS and each tile's x in registers until its hPre
 //                    (summed by a designated workgroup, exchanged through tagged words) is
 //                    known, so x is read once; the epilogue follows.
+// Standalone stages (the HcPre guide, mhpn.cn/news/2282827, "function description", names
+// invRms and the Sinkhorn stage as operators of their own):
+//   inv_rms_kernel   invRms alone: one wave per token, squares and sums in fp64.
+//   mix_gates_kernel the Sinkhorn stage from given mixes and invRms: the epilogue's gates and
+//                    Sinkhorn for 8 tokens per workgroup; hin_kernel follows.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -551,6 +556,101 @@ hin_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wts,
         o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
     // hIn is not read again by this forward: stream it past the caches
     __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(h_in + t * (int64_t)D + d8 * 8));
+}
+
+// ------------------------------------------------------------------ standalone stages
+
+// invRms alone: one wave per token, kThreads / 64 tokens per workgroup. A lane widens its
+// bf16 values to fp64 and adds their squares in fp64 (a bf16 square is exact there); the
+// 64 lane sums are added in fp64 across the wave.
+template <int N>
+__global__ void __launch_bounds__(kThreads)
+inv_rms_kernel(const uint16_t* __restrict__ x, float* __restrict__ inv_rms, int64_t T, int D,
+               double norm_eps)
+{
+    const int lane = threadIdx.x % 64;
+    const int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
+    if (t >= T) return;
+    const int units = N * D / 8;   // 16-byte units of the token
+    const u32x4* xt = reinterpret_cast<const u32x4*>(x + t * (int64_t)N * D);
+    double acc = 0.0;
+    int u = lane;
+    for (; u + 192 < units; u += 256) {   // four loads in flight per lane
+        u32x4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = __builtin_nontemporal_load(xt + u + 64 * j);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double lo = bf16_lo(v[j][e]), hi = bf16_hi(v[j][e]);
+                acc = fma(lo, lo, acc);
+                acc = fma(hi, hi, acc);
+            }
+    }
+    for (; u < units; u += 64) {
+        const u32x4 v = __builtin_nontemporal_load(xt + u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const double lo = bf16_lo(v[e]), hi = bf16_hi(v[e]);
+            acc = fma(lo, lo, acc);
+            acc = fma(hi, hi, acc);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o /= 2) acc += __shfl_xor(acc, o);
+    if (lane == 0) inv_rms[t] = (float)inv_rms_of(acc, (double)N * D, norm_eps);
+}
+
+// The Sinkhorn stage alone: kOutTokens tokens per workgroup, from given mixes and invRms
+// to hPre, hPost and the Sinkhorn (hIn follows in hin_kernel). The gates are those of
+// epilogue_kernel, fed with the f32 inputs widened to fp64.
+template <int N, int A>
+__global__ void __launch_bounds__(kThreads)
+mix_gates_kernel(KArgs k, const float* __restrict__ h_mix, const float* __restrict__ inv_in)
+{
+    using C = Cfg<N, A>;
+    constexpr int NN = C::NN, M = C::M, OB = C::OB;
+    __shared__ float Ls[OB * NN];
+    const ForwardArgs& a = k.a;
+    const int tid = threadIdx.x;
+    const int64_t tf = (int64_t)blockIdx.x * OB;
+    const int nb = k.T - tf < OB ? (int)(k.T - tf) : OB;
+    const float eps = (float)a.hc_eps;
+    for (int it = tid; it < nb * M; it += kThreads) {
+        const int q = it / M, m = it % M;
+        const int64_t t = tf + q;
+        const double h = (double)h_mix[t * M + m];
+        const double inv = (double)inv_in[t];
+        if (m < N) a.h_pre[t * N + m] = gate_pre(h, inv, a.alpha[0], a.bias[m], eps);
+        else if (m < 2 * N) a.h_post[t * N + m - N] = gate_post(h, inv, a.alpha[1], a.bias[m], eps, A == 2);
+        else Ls[q * NN + (m - 2 * N)] = res_logit(h, inv, a.alpha[2], a.bias[m]);
+    }
+    if constexpr (A == 3) {
+        __syncthreads();
+        sinkhorn<N>(k, Ls, tf, nb);
+    } else if (a.h_res) {
+        for (int it = tid; it < nb * NN; it += kThreads) a.h_res[tf * NN + it] = 0.f;
+    }
+}
+
+template <int N, int A>
+hipError_t launch_stage(int64_t T, int D, const ForwardArgs& a, const float* h_mix, const float* inv_rms,
+                        hipStream_t st)
+{
+    KArgs k;
+    std::memset(&k, 0, sizeof k);
+    k.a = a;
+    k.T = T;
+    k.D = D;
+    hipLaunchKernelGGL((mix_gates_kernel<N, A>), dim3((unsigned)((T + kOutTokens - 1) / kOutTokens)),
+                       dim3(kThreads), 0, st, k, h_mix, inv_rms);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t items = T * (int64_t)(D / 8);
+    hipLaunchKernelGGL(hin_kernel<N>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, a.x,
+                       a.pre_mix ? a.pre_mix : a.h_pre, a.h_in, T, D);
+    return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ single-read forward
@@ -1077,6 +1177,32 @@ int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void
     hipLaunchKernelGGL(prepack_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, phi, gamma,
                        static_cast<u32x4*>(packed), g.n, g.D, g.M, g.NC, g.nks, total);
     return (int)hipGetLastError();
+}
+
+int launch_inv_rms(int64_t T, int n, int D, double norm_eps, const uint16_t* x, float* inv_rms,
+                   void* stream)
+{
+    if (T <= 0) return 0;
+    constexpr int per_block = kThreads / 64;
+    const dim3 grid((unsigned)((T + per_block - 1) / per_block));
+    hipStream_t st = (hipStream_t)stream;
+    if (n == 4) hipLaunchKernelGGL(inv_rms_kernel<4>, grid, dim3(kThreads), 0, st, x, inv_rms, T, D, norm_eps);
+    else if (n == 8) hipLaunchKernelGGL(inv_rms_kernel<8>, grid, dim3(kThreads), 0, st, x, inv_rms, T, D, norm_eps);
+    else return (int)hipErrorInvalidValue;
+    return (int)hipGetLastError();
+}
+
+int launch_pre_sinkhorn(int64_t T, int n, int D, int n_alpha, const ForwardArgs& a, const float* h_mix,
+                        const float* inv_rms, void* stream)
+{
+    if (T <= 0) return 0;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipErrorInvalidValue;
+    if (n == 4 && n_alpha == 3) e = launch_stage<4, 3>(T, D, a, h_mix, inv_rms, st);
+    else if (n == 4 && n_alpha == 2) e = launch_stage<4, 2>(T, D, a, h_mix, inv_rms, st);
+    else if (n == 8 && n_alpha == 3) e = launch_stage<8, 3>(T, D, a, h_mix, inv_rms, st);
+    else if (n == 8 && n_alpha == 2) e = launch_stage<8, 2>(T, D, a, h_mix, inv_rms, st);
+    return (int)e;
 }
 
 int record_event(void* event, void* stream)

@@ -306,6 +306,13 @@ int launch_forward(const Plan& p, const ForwardArgs& a, void* stream, void* cons
 // device: 1 the single-read kernel, 0 the four-kernel path.
 int forward_path(const Plan& p, bool has_pre_mix);
 int record_event(void* event, void* stream);
+// Standalone stages (mhc_kernels.hip). launch_pre_sinkhorn reads h_mix / inv_rms from the
+// given inputs, and from a: x, alpha, bias, pre_mix, the outputs h_in, h_pre, h_post, h_res,
+// sum_out, norm_out, num_iters and hc_eps. 0 or the HIP error code.
+int launch_inv_rms(int64_t T, int n, int D, double norm_eps, const uint16_t* x, float* inv_rms,
+                   void* stream);
+int launch_pre_sinkhorn(int64_t T, int n, int D, int n_alpha, const ForwardArgs& a, const float* h_mix,
+                        const float* inv_rms, void* stream);
 // hc_post (mhc_post.hip): out = post x + comb residual per token; 0 or the HIP error code.
 int launch_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* residual, const float* post,
                 const float* comb, uint16_t* out, void* stream);

@@ -37,6 +37,14 @@ hc_post inputs (``post_inputs``), drawn in this order:
   residual  [T, n, D]  N(0, 1) -> bf16   (the n streams; chunked as above)
   post      [T, n]     U(0, 2)           (the range of 2 sigmoid)
   comb      [T, n, n]  U(0.05, 0.45)     (the range of the Sinkhorn matrix entries at n = 4)
+Standalone-stage inputs (``stage_inputs``: invRms alone and the Sinkhorn stage from given
+mixes), drawn in this order:
+  x         [T, n, D]  N(0, 1) -> bf16 (chunked as above)
+  alpha     [3] or [2] U(0.5, 1.5)
+  bias      [M]        N(0, 0.1)
+  h_mix     [T, M]     N(0, 1)         (mixes of O(1), as phi's scaling gives the forward)
+  inv_rms   [T]        U(0.5, 1.5)     (x ~ N(0, 1) gives invRms near 1)
+  pre_mix   [T, n]     U(0, 1)         (when asked for)
 The saved forward values are drawn independently, in the ranges the forward produces:
 the backward is a function of all of them, whatever forward they came from. (Parity
 tests of the Sinkhorn backward take the planes from the oracle's forward instead, so
@@ -232,3 +240,35 @@ def post_inputs(T: int, n: int, D: int, *, seed: int = 21) -> PostInputs:
     post = rng.uniform(0.0, 2.0, size=(T, n)).astype(np.float32)
     comb = rng.uniform(0.05, 0.45, size=(T, n, n)).astype(np.float32)
     return PostInputs(T, n, D, x, residual, post, comb)
+
+
+@dataclass
+class StageInputs:
+    T: int
+    n: int
+    D: int
+    n_alpha: int
+    x: np.ndarray          # uint16 [T, n, D] bf16 bits
+    alpha: np.ndarray      # float32 [n_alpha]
+    bias: np.ndarray       # float32 [M]
+    h_mix: np.ndarray      # float32 [T, M]
+    inv_rms: np.ndarray    # float32 [T]
+    pre_mix: np.ndarray | None = None   # float32 [T, n]
+
+    @property
+    def M(self) -> int:
+        return self.n * self.n + 2 * self.n if self.n_alpha == 3 else 2 * self.n
+
+
+def stage_inputs(T: int, n: int, D: int, *, n_alpha: int = 3, pre_mix: bool = False,
+                 seed: int = 31) -> StageInputs:
+    """Inputs of the standalone stages with the recipe in the module docstring."""
+    rng = np.random.default_rng(seed)
+    M = n * n + 2 * n if n_alpha == 3 else 2 * n
+    x = _bf16_normal(rng, T * n * D).reshape(T, n, D)
+    alpha = rng.uniform(0.5, 1.5, size=n_alpha).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(M)).astype(np.float32)
+    hmix = rng.standard_normal((T, M), dtype=np.float32)
+    inv = rng.uniform(0.5, 1.5, size=T).astype(np.float32)
+    pm = rng.uniform(0.0, 1.0, size=(T, n)).astype(np.float32) if pre_mix else None
+    return StageInputs(T, n, D, n_alpha, x, alpha, bias, hmix, inv, pm)
