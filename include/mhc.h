@@ -53,7 +53,8 @@ typedef int32_t mhc_status;
 
 /* Problem description (host memory; read during the call only).
  *   T              tokens, >= 0
- *   n              hyper-streams (hcMult): 4 or 8
+ *   n              hyper-streams (hcMult): 4, 6 or 8 (the aclnnMhcPreV2 guide, section 7.3,
+ *                  allows these three); the MhcPre backward takes 4 or 8
  *   D              hidden size per stream: a multiple of 8 in [8, 16384]; with n == 8 and
  *                  n_alpha == 3 at most 8192
  *   n_alpha        3 (pre/post/res branches, phi has n*n+2n rows) or
@@ -362,7 +363,7 @@ mhc_status mhc_pre_sinkhorn(const mhc_pre_params* params, const mhc_pre_sinkhorn
  * indexed by comb's first index, which fuses nothing although the text says the streams
  * are fused; the sum runs over the residual's stream here. fp32 fused multiply-adds
  * (post term first, then j in order), one rounding to bf16.
- *   T >= 0; n: 4 or 8; D: a multiple of 8 in [8, 16384]
+ *   T >= 0; n: 4, 6 or 8; D: a multiple of 8 in [8, 16384]
  *   x        bf16 [T, D]       16-byte aligned    (the attention / MLP output)
  *   residual bf16 [T, n, D]    16-byte aligned    (the n streams)
  *   post     f32  [T, n]

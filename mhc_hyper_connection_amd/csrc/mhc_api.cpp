@@ -291,7 +291,7 @@ extern "C" {
 mhc_status mhc_post(const mhc_post_params* params, const mhc_post_tensors* t, void* stream)
 {
     if (!params || !t) return MHC_ERR_NULLPTR;
-    if (params->T < 0 || (params->n != 4 && params->n != 8)) return MHC_ERR_PARAM_INVALID;
+    if (params->T < 0 || (params->n != 4 && params->n != 6 && params->n != 8)) return MHC_ERR_PARAM_INVALID;
     if (params->D < 8 || params->D % 8 != 0 || params->D > mhc::kMaxD) return MHC_ERR_PARAM_INVALID;
     if (params->T == 0) return MHC_OK;
     if (!t->x || !t->residual || !t->post || !t->comb || !t->out) return MHC_ERR_NULLPTR;

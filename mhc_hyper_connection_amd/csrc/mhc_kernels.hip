@@ -53,10 +53,10 @@ struct Cfg {
     static constexpr int NT = (3 * M + 15) / 16;
     static constexpr int NC = 16 * NT;
     static constexpr int SK = (A == 3) ? 1 : (N == 4 ? 4 : 2);   // K-steps per stage
-    static constexpr int RING = (N == 8 && A == 3) ? 3 : (A == 3 ? 7 : 5);   // LDS weight slots: stages in flight + 1
+    static constexpr int RING = (N == 8 && A == 3) ? 3 : (N == 6 && A == 3) ? 5 : (A == 3 ? 7 : 5);   // LDS weight slots: stages in flight + 1
     static constexpr int NN = N * N;
     static constexpr int PPS = (N + 4) / 4 * 4;   // pre-branch record: n sums, square, padding
-    static constexpr int V = PPS + (M - N);       // floats per partial record
+    static constexpr int V = (PPS + (M - N) + 3) / 4 * 4;   // floats per partial record (16-byte multiple)
     static constexpr int CH = V / 4;              // 16-byte chunks per record
     static constexpr int KU = 4 * NC;             // 16-byte units per K-step of packed weights
     static constexpr int STAGE_U = SK * KU;
@@ -318,7 +318,7 @@ proj_kernel(KArgs k)
             const int m = v < N ? v : N + (v - PPS);
             float val;
             if (v == N) val = lds_ss[tl];
-            else if (v > N && v < PPS) val = 0.f;
+            else if ((v > N && v < PPS) || v >= PPS + (M - N)) val = 0.f;   // padding
             else val = (float)((double)rr[m] + (double)rr[M + m] + (double)rr[2 * M + m]);
             o[e] = __float_as_uint(val);
         }
@@ -390,47 +390,92 @@ __device__ __forceinline__ float col_sum(float v)
     return v;
 }
 
+// n = 6: 36 entries do not tile a wave, so each matrix takes a wave of its own (lanes 36
+// to 63 idle) and the sums gather the row's (column's) lanes by shuffles, in index order.
+template <int N>
+__device__ __forceinline__ float sk_row_sum(float v, int r)
+{
+    if constexpr (N == 6) {
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < N; ++c) s += __shfl(v, r * N + c);
+        return s;
+    } else {
+        return row_sum<N>(v);
+    }
+}
+template <int N>
+__device__ __forceinline__ float sk_row_max(float v, int r)
+{
+    if constexpr (N == 6) {
+        float m = __shfl(v, r * N);
+#pragma unroll
+        for (int c = 1; c < N; ++c) m = fmaxf(m, __shfl(v, r * N + c));
+        return m;
+    } else {
+        return row_max<N>(v);
+    }
+}
+template <int N>
+__device__ __forceinline__ float sk_col_sum(float v, int c)
+{
+    if constexpr (N == 6) {
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < N; ++r) s += __shfl(v, r * N + c);
+        return s;
+    } else {
+        return col_sum<N>(v);
+    }
+}
+
 // Sinkhorn of nb tokens (the first is token tfirst) whose logits are in Ls ([nb][N*N]):
-// one lane per matrix entry, 2*num_iters steps, every plane stored.
+// one lane per matrix entry, 2*num_iters steps, every plane stored. A matrix takes SW
+// consecutive lanes (N*N, or a whole wave for n = 6); a lane past the N*N entries of
+// its matrix computes along and stores nothing.
 template <int N>
 __device__ void sinkhorn(const KArgs& k, const float* Ls, int64_t tfirst, int nb)
 {
     constexpr int NN = N * N;
+    constexpr int SW = 64 % NN == 0 ? NN : 64;
+    static_assert(kThreads % SW == 0, "a pass is whole matrices");
     const ForwardArgs& a = k.a;
     const int tid = threadIdx.x;
-    const int e = tid % NN, r = e / N, c = e % N;
+    const int e = tid % SW;
+    const bool used = SW == NN || e < NN;
+    const int r = used ? e / N : 0, c = used ? e % N : 0;
     const float eps = (float)a.hc_eps;
     const int steps = 2 * a.num_iters;
-    for (int base = 0; base < nb * NN; base += kThreads) {
-        const int q = (base + tid) / NN;
-        const bool live = q < nb;
-        const int64_t t1 = tfirst + base / NN;   // first token of this pass
-        const int nlive = nb - base / NN;          // tokens of this pass that exist
-        const int qq = q - base / NN;              // token within the pass
+    for (int base = 0; base < nb * SW; base += kThreads) {
+        const int q = (base + tid) / SW;
+        const bool live = used && q < nb;
+        const int64_t t1 = tfirst + base / SW;   // first token of this pass
+        const int nlive = nb - base / SW;          // tokens of this pass that exist
+        const int qq = q - base / SW;              // token within the pass
         float v = live ? Ls[q * NN + e] : 0.f;
-        const float mx = row_max<N>(v);
+        const float mx = sk_row_max<N>(v, r);
         const float ex = expf(v - mx);
-        float sum = row_sum<N>(ex);
+        float sum = sk_row_sum<N>(ex, r);
         v = ex / sum + eps;
         for (int step = 0; step < steps; ++step) {
             if (step > 0) {
-                if (step & 1) sum = col_sum<N>(v) + eps;
-                else sum = row_sum<N>(v) + eps;
+                if (step & 1) sum = sk_col_sum<N>(v, c) + eps;
+                else sum = sk_row_sum<N>(v, r) + eps;
                 v = v / sum;
             }
             // this pass's tokens of plane `step`; lanes past them fall outside the range
             if (a.sum_out) {
                 const rsrc_t rs = make_rsrc(a.sum_out + ((int64_t)step * k.T + t1) * N, (int64_t)nlive * N * 4);
-                const bool writer = (step & 1) ? (r == 0) : (c == 0);
+                const bool writer = used && ((step & 1) ? (r == 0) : (c == 0));
                 if (writer) st_buf(rs, (uint32_t)(qq * N + ((step & 1) ? c : r)) * 4, sum);
             }
             if (a.norm_out) {
                 const rsrc_t rn = make_rsrc(a.norm_out + ((int64_t)step * k.T + t1) * NN, (int64_t)nlive * NN * 4);
-                st_buf(rn, (uint32_t)(qq * NN + e) * 4, v);
+                if (used) st_buf(rn, (uint32_t)(qq * NN + e) * 4, v);
             }
         }
         const rsrc_t rh = make_rsrc(a.h_res + t1 * NN, (int64_t)nlive * NN * 4);
-        st_buf(rh, (uint32_t)(qq * NN + e) * 4, v);
+        if (used) st_buf(rh, (uint32_t)(qq * NN + e) * 4, v);
     }
 }
 
@@ -1187,6 +1232,7 @@ int launch_inv_rms(int64_t T, int n, int D, double norm_eps, const uint16_t* x, 
     const dim3 grid((unsigned)((T + per_block - 1) / per_block));
     hipStream_t st = (hipStream_t)stream;
     if (n == 4) hipLaunchKernelGGL(inv_rms_kernel<4>, grid, dim3(kThreads), 0, st, x, inv_rms, T, D, norm_eps);
+    else if (n == 6) hipLaunchKernelGGL(inv_rms_kernel<6>, grid, dim3(kThreads), 0, st, x, inv_rms, T, D, norm_eps);
     else if (n == 8) hipLaunchKernelGGL(inv_rms_kernel<8>, grid, dim3(kThreads), 0, st, x, inv_rms, T, D, norm_eps);
     else return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
@@ -1202,6 +1248,8 @@ int launch_pre_sinkhorn(int64_t T, int n, int D, int n_alpha, const ForwardArgs&
     else if (n == 4 && n_alpha == 2) e = launch_stage<4, 2>(T, D, a, h_mix, inv_rms, st);
     else if (n == 8 && n_alpha == 3) e = launch_stage<8, 3>(T, D, a, h_mix, inv_rms, st);
     else if (n == 8 && n_alpha == 2) e = launch_stage<8, 2>(T, D, a, h_mix, inv_rms, st);
+    else if (n == 6 && n_alpha == 3) e = launch_stage<6, 3>(T, D, a, h_mix, inv_rms, st);
+    else if (n == 6 && n_alpha == 2) e = launch_stage<6, 2>(T, D, a, h_mix, inv_rms, st);
     return (int)e;
 }
 
@@ -1253,12 +1301,16 @@ int launch_forward(const Plan& p, const ForwardArgs& a_in, void* stream, void* c
     if (n == 4 && na == 2 && (v.nt != Cfg<4, 2>::NT || v.sk != Cfg<4, 2>::SK)) return (int)hipErrorInvalidValue;
     if (n == 8 && na == 3 && (v.nt != Cfg<8, 3>::NT || v.sk != Cfg<8, 3>::SK)) return (int)hipErrorInvalidValue;
     if (n == 8 && na == 2 && (v.nt != Cfg<8, 2>::NT || v.sk != Cfg<8, 2>::SK)) return (int)hipErrorInvalidValue;
+    if (n == 6 && na == 3 && (v.nt != Cfg<6, 3>::NT || v.sk != Cfg<6, 3>::SK)) return (int)hipErrorInvalidValue;
+    if (n == 6 && na == 2 && (v.nt != Cfg<6, 2>::NT || v.sk != Cfg<6, 2>::SK)) return (int)hipErrorInvalidValue;
     hipError_t e = hipErrorInvalidValue;
     if (n == 4 && na == 3 && nks == 16) e = launch_group<4, 3, 16>(p, k, st, events);
     else if (n == 4 && na == 2 && nks == 32) e = launch_group<4, 2, 32>(p, k, st, events);
     else if (n == 4 && na == 2 && nks == 16) e = launch_group<4, 2, 16>(p, k, st, events);
     else if (n == 8 && na == 3 && nks == 8) e = launch_group<8, 3, 8>(p, k, st, events);
     else if (n == 8 && na == 2 && nks == 16) e = launch_group<8, 2, 16>(p, k, st, events);
+    else if (n == 6 && na == 3 && nks == 12) e = launch_group<6, 3, 12>(p, k, st, events);
+    else if (n == 6 && na == 2 && nks == 12) e = launch_group<6, 2, 12>(p, k, st, events);
     return (int)e;
 }
 

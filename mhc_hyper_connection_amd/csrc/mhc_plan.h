@@ -101,13 +101,15 @@ inline Variant variant_of(int n, int n_alpha)
     else if (n == 4 && n_alpha == 2) { v.nt = 2; v.sk = 4; v.nks_big = 32; v.nks_small = 16; }
     else if (n == 8 && n_alpha == 3) { v.nt = 15; v.sk = 1; v.nks_big = 8; v.nks_small = 8; }
     else if (n == 8 && n_alpha == 2) { v.nt = 3; v.sk = 2; v.nks_big = 16; v.nks_small = 16; }
+    else if (n == 6 && n_alpha == 3) { v.nt = 9; v.sk = 1; v.nks_big = 12; v.nks_small = 12; }
+    else if (n == 6 && n_alpha == 2) { v.nt = 3; v.sk = 2; v.nks_big = 12; v.nks_small = 12; }
     return v;
 }
 
 // Returns false for a combination the kernels do not support.
 inline bool make_geometry(int n, int D, int n_alpha, Geometry* g)
 {
-    if (n != 4 && n != 8) return false;
+    if (n != 4 && n != 6 && n != 8) return false;
     if (D <= 0 || D % 8 != 0 || D > kMaxD) return false;
     if (n_alpha != 2 && n_alpha != 3) return false;
     Geometry r;
@@ -240,10 +242,11 @@ MHC_HOST_DEVICE inline int64_t packed_slice(int s, int NKS, int NC) { return (in
 
 // Partial record of a task for one token: the pre-branch sums and the square sum,
 // padded to pp_stride(n) floats ([pre_0 .. pre_{n-1}, sq, 0...], a 16-byte multiple),
-// then the remaining M - n projections; rec_stride floats in all. A tile's records
+// then the remaining M - n projections, padded to a 16-byte multiple (only n = 6 needs
+// it); rec_stride floats in all. A tile's records
 // form one block of S * 64 records, slice-major. Offsets in floats.
 MHC_HOST_DEVICE inline int pp_stride(int n) { return (n + 1 + 3) / 4 * 4; }
-MHC_HOST_DEVICE inline int rec_stride(int n, int M) { return pp_stride(n) + (M - n); }
+MHC_HOST_DEVICE inline int rec_stride(int n, int M) { return (pp_stride(n) + (M - n) + 3) / 4 * 4; }
 MHC_HOST_DEVICE inline int64_t rec_tile(int64_t tile, int S, int n, int M)
 {
     return tile * S * kTileTokens * rec_stride(n, M);

@@ -74,6 +74,7 @@ int launch_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* resi
     const dim3 grid((unsigned)((items + 255) / 256));
     hipStream_t st = (hipStream_t)stream;
     if (n == 4) hipLaunchKernelGGL(post_kernel<4>, grid, dim3(256), 0, st, x, residual, post, comb, out, T, D);
+    else if (n == 6) hipLaunchKernelGGL(post_kernel<6>, grid, dim3(256), 0, st, x, residual, post, comb, out, T, D);
     else if (n == 8) hipLaunchKernelGGL(post_kernel<8>, grid, dim3(256), 0, st, x, residual, post, comb, out, T, D);
     else return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();

@@ -88,7 +88,7 @@ def test_null_params_workspace_and_weights():
     assert fwd(_p(T=0, n_alpha=2), _ptrs(h_res=None)) == B.MHC_OK
 
 
-@pytest.mark.parametrize("kw", [dict(n=6), dict(n=2), dict(n=16), dict(D=0), dict(D=-8), dict(D=12),
+@pytest.mark.parametrize("kw", [dict(n=5), dict(n=7), dict(n=2), dict(n=16), dict(D=0), dict(D=-8), dict(D=12),
                                 dict(D=16392), dict(n=8, D=8200),
                                 dict(n_alpha=4), dict(n_alpha=1), dict(num_iters=0),
                                 dict(norm_eps=0.0), dict(norm_eps=float("nan")),
@@ -163,5 +163,5 @@ def test_timed_forward_validates_events_first():
     assert lib.mhc_pre_forward_timed(ctypes.byref(_p()), ctypes.byref(t), FAKE, WS_BIG, None,
                                      five, 4) == B.MHC_ERR_PARAM_INVALID
     # then the forward's own validation, before any HIP call
-    assert B.raw_forward_timed(_p(n=6), _ptrs(), FAKE, WS_BIG, None, [FAKE] * 5) == B.MHC_ERR_PARAM_INVALID
+    assert B.raw_forward_timed(_p(n=5), _ptrs(), FAKE, WS_BIG, None, [FAKE] * 5) == B.MHC_ERR_PARAM_INVALID
     assert B.raw_forward_timed(_p(), _ptrs(x=None), FAKE, WS_BIG, None, [FAKE] * 5) == B.MHC_ERR_NULLPTR

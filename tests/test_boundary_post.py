@@ -13,7 +13,7 @@ def call(T, n, D, ptrs=(16, 16, 16, 16, 16)):
     return B.load().mhc_post(ctypes.byref(p), ctypes.byref(t), None)
 
 
-@pytest.mark.parametrize("T,n,D,want", [(-1, 4, 64, B.MHC_ERR_PARAM_INVALID), (4, 6, 64, B.MHC_ERR_PARAM_INVALID),
+@pytest.mark.parametrize("T,n,D,want", [(-1, 4, 64, B.MHC_ERR_PARAM_INVALID), (4, 5, 64, B.MHC_ERR_PARAM_INVALID), (4, 7, 64, B.MHC_ERR_PARAM_INVALID),
                                         (4, 4, 60, B.MHC_ERR_PARAM_INVALID), (4, 4, 0, B.MHC_ERR_PARAM_INVALID),
                                         (4, 4, 16392, B.MHC_ERR_PARAM_INVALID), (0, 4, 64, B.MHC_OK)])
 def test_sizes(T, n, D, want):

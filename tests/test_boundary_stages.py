@@ -29,7 +29,7 @@ def test_inv_rms_validation():
     assert inv_rms(B.make_params(4, 4, 64), out=0) == B.MHC_ERR_NULLPTR
     assert inv_rms(B.make_params(4, 4, 64), x=8) == B.MHC_ERR_PARAM_INVALID        # x not 16-byte aligned
     assert inv_rms(B.make_params(4, 4, 64), out=18) == B.MHC_ERR_PARAM_INVALID     # out not 4-byte aligned
-    assert inv_rms(B.make_params(4, 6, 64)) == B.MHC_ERR_PARAM_INVALID
+    assert inv_rms(B.make_params(4, 5, 64)) == B.MHC_ERR_PARAM_INVALID
     assert inv_rms(B.make_params(4, 4, 60)) == B.MHC_ERR_PARAM_INVALID
     assert inv_rms(B.make_params(4, 4, 64, norm_eps=0.0)) == B.MHC_ERR_PARAM_INVALID
     assert inv_rms(B.make_params(-1, 4, 64)) == B.MHC_ERR_PARAM_INVALID

@@ -51,6 +51,13 @@ SMALL = [
     ("T513", lambda: synth.custom(513, 4, 4096, seed=35)),
     ("iters1", lambda: synth.custom(64, 4, 256, need_backward=True, num_iters=1, seed=36)),
     ("iters3", lambda: synth.custom(64, 4, 256, need_backward=True, num_iters=3, seed=37)),
+    # n = 6 (the third stream count the aclnnMhcPreV2 guide allows): 36-entry Sinkhorn
+    # matrices, 12-step slices, padded records
+    ("n6_alpha3_bwd", lambda: synth.custom(130, 6, 1024, need_backward=True, seed=60)),
+    ("n6_alpha3_D7168_gamma", lambda: synth.custom(70, 6, 7168, gamma=True, need_backward=True, seed=61)),
+    ("n6_alpha2_premix_D520", lambda: synth.custom(65, 6, 520, n_alpha=2, pre_mix=True, need_backward=True, seed=62)),
+    ("n6_alpha3_premix_D24_T9", lambda: synth.custom(9, 6, 24, pre_mix=True, need_backward=True, seed=63)),
+    ("n6_D16384_T3", lambda: synth.custom(3, 6, 16384, need_backward=True, seed=64)),
 ]
 
 

@@ -28,7 +28,8 @@ def gpu_inv_rms(x_bits):
 
 
 INV_CASES = [("T1_n4_D8", 1, 4, 8), ("T7_n4_D40", 7, 4, 40), ("T130_n8_D24", 130, 8, 24),
-             ("T65_n8_D7168", 65, 8, 7168), ("T300_n4_D7168", 300, 4, 7168), ("T5_n4_D16384", 5, 4, 16384)]
+             ("T65_n8_D7168", 65, 8, 7168), ("T300_n4_D7168", 300, 4, 7168), ("T5_n4_D16384", 5, 4, 16384),
+             ("T33_n6_D520", 33, 6, 520)]
 
 
 @pytest.mark.parametrize("name,T,n,D", INV_CASES, ids=[c[0] for c in INV_CASES])
@@ -82,6 +83,8 @@ SK_CASES = [  # name, T, n, D, n_alpha, pre_mix, need_backward, num_iters
     ("T70_n4_D520_premix", 70, 4, 520, 3, True, True, 20),
     ("T300_n4_D7168", 300, 4, 7168, 3, False, True, 20),
     ("T64_n8_D4096_it3", 64, 8, 4096, 3, False, True, 3),
+    ("T13_n6_D48", 13, 6, 48, 3, False, True, 20),
+    ("T21_n6_D64_alpha2_premix", 21, 6, 64, 2, True, False, 20),
 ]
 
 
