@@ -187,9 +187,11 @@ mhc_status mhc_pre_forward_path(const mhc_pre_params* params, int32_t has_pre_mi
  * or on the single-read path: the projection writes hIn then) has its two events recorded
  * back to back, so elapsed time between events[i] and events[i+1] is kernel i's duration
  * (plus the launch gap) whatever the inputs; with T == 0 all five are recorded back to
- * back. Computes exactly what mhc_pre_forward computes.
- * Errors: as mhc_pre_forward; NULLPTR also for a NULL events array or handle;
- * PARAM_INVALID when num_events != MHC_FORWARD_EVENTS. */
+ * back. A NULL entry is not recorded: a caller that only wants some boundaries (each
+ * record costs a few microseconds on the stream) passes NULL for the others. Computes
+ * exactly what mhc_pre_forward computes.
+ * Errors: as mhc_pre_forward; NULLPTR also for a NULL events array; PARAM_INVALID when
+ * num_events != MHC_FORWARD_EVENTS. */
 mhc_status mhc_pre_forward_timed(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  void* const* events, int32_t num_events);

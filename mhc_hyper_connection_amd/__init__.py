@@ -124,9 +124,10 @@ class PreForward:
     # -- forward -----------------------------------------------------------------------
     def __call__(self, x, phi, alpha, bias, gamma=None, pre_mix=None, *, phi_packed=None,
                  out=None, events=None):
-        """events: optional list of FORWARD_EVENTS torch.cuda.Event(enable_timing=True),
-        each recorded at least once before (so that its HIP event exists); the call then
-        records them around its kernels (STAGES order), see mhc_pre_forward_timed."""
+        """events: optional list of FORWARD_EVENTS torch.cuda.Event(enable_timing=True) or
+        None, each event recorded at least once before (so that its HIP event exists); the
+        call then records them around its kernels (STAGES order) and skips the None
+        entries, see mhc_pre_forward_timed."""
         torch = _torch()
         T, n, D, M, dev = self.T, self.n, self.D, self.M, self.device
         _check(x, "x", torch.bfloat16, (T, n, D), dev)
@@ -149,7 +150,8 @@ class PreForward:
                 raise MhcError(st, "mhc_pre_forward")
         else:
             st = raw_forward_timed(self.params, ptrs, _ptr(self.workspace), self.ws_bytes,
-                                   _stream(dev), [e.cuda_event or None for e in events])
+                                   _stream(dev),
+                                   [None if e is None else (e.cuda_event or None) for e in events])
             if st != MHC_OK:
                 raise MhcError(st, "mhc_pre_forward_timed")
         return out

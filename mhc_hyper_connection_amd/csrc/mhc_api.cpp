@@ -142,7 +142,7 @@ mhc_status forward_impl(const mhc_pre_params* params, const mhc_pre_tensors* t,
 
     if (params->T == 0) {   // empty input: success, no kernel launched
         for (int i = 0; events && i <= mhc::kStages; ++i)
-            if (mhc::record_event(events[i], stream) != 0) return MHC_ERR_RUNTIME;
+            if (events[i] && mhc::record_event(events[i], stream) != 0) return MHC_ERR_RUNTIME;
         return MHC_OK;
     }
 
@@ -194,8 +194,6 @@ mhc_status mhc_pre_forward_timed(const mhc_pre_params* params, const mhc_pre_ten
                                  void* const* events, int32_t num_events)
 {
     if (!events) return MHC_ERR_NULLPTR;
-    for (int i = 0; i < num_events && i <= mhc::kStages; ++i)
-        if (!events[i]) return MHC_ERR_NULLPTR;
     if (num_events != MHC_FORWARD_EVENTS) return MHC_ERR_PARAM_INVALID;
     return forward_impl(params, t, workspace, workspace_bytes, stream, events);
 }

@@ -1121,10 +1121,11 @@ fused_kernel(FArgs f)
     }
 }
 
-// Records events[i] (a caller-created hipEvent_t) on the stream when events is given.
+// Records events[i] (a caller-created hipEvent_t) on the stream when events is given and
+// its entry is not NULL.
 hipError_t mark(void* const* events, int i, hipStream_t st)
 {
-    return events ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
+    return events && events[i] ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
 }
 
 template <int N, int A, int NKS>

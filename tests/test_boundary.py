@@ -154,12 +154,13 @@ def test_timed_forward_validates_events_first():
     lib = B.load()
     t = B.Tensors(*[_ptrs().get(f) for f in B.TENSOR_FIELDS])
     five = (ctypes.c_void_p * 5)(*([FAKE] * 5))
-    # NULL array or a NULL handle: NULLPTR; wrong count: PARAM_INVALID
+    # NULL array: NULLPTR; wrong count: PARAM_INVALID (NULL entries are boundaries the
+    # caller does not want recorded)
     assert lib.mhc_pre_forward_timed(ctypes.byref(_p()), ctypes.byref(t), FAKE, WS_BIG, None,
                                      None, 5) == B.MHC_ERR_NULLPTR
     holes = (ctypes.c_void_p * 5)(FAKE, FAKE, None, FAKE, FAKE)
     assert lib.mhc_pre_forward_timed(ctypes.byref(_p()), ctypes.byref(t), FAKE, WS_BIG, None,
-                                     holes, 5) == B.MHC_ERR_NULLPTR
+                                     holes, 4) == B.MHC_ERR_PARAM_INVALID
     assert lib.mhc_pre_forward_timed(ctypes.byref(_p()), ctypes.byref(t), FAKE, WS_BIG, None,
                                      five, 4) == B.MHC_ERR_PARAM_INVALID
     # then the forward's own validation, before any HIP call
