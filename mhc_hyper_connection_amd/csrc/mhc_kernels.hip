@@ -18,7 +18,7 @@
 //                    x x^T. The task writes one partial record per token. With pre_mix the
 //                    hIn weights are inputs, and the task also writes its slice of hIn
 //                    from the registers it already holds (x is read once).
-//   epilogue_kernel  one workgroup per 8 tokens: sums the S partial records of each token
+//   epilogue_kernel  one workgroup per 16 (n = 4) or 8 tokens: sums the S partial records of each token
 //                    in a fixed order (fp64), then invRms, hMix, the gates, the Sinkhorn
 //                    planes (one lane per matrix entry, sums across lanes by DPP) and,
 //                    without pre_mix, the hIn weights.
@@ -32,7 +32,7 @@
 // invRms and the Sinkhorn stage as operators of their own):
 //   inv_rms_kernel   invRms alone: one wave per token, squares and sums in fp64.
 //   mix_gates_kernel the Sinkhorn stage from given mixes and invRms: the epilogue's gates and
-//                    Sinkhorn for 8 tokens per workgroup; hin_kernel follows.
+//                    Sinkhorn for out_tokens(n) tokens per workgroup; hin_kernel follows.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -60,7 +60,7 @@ struct Cfg {
     static constexpr int CH = V / 4;              // 16-byte chunks per record
     static constexpr int KU = 4 * NC;             // 16-byte units per K-step of packed weights
     static constexpr int STAGE_U = SK * KU;
-    static constexpr int OB = kOutTokens;         // tokens per epilogue workgroup
+    static constexpr int OB = out_tokens(N);      // tokens per epilogue workgroup
     static_assert(STAGE_U % 64 == 0, "a stage is whole 64-lane load instructions");
     static constexpr int PROJ_LDS = RING * STAGE_U * 16 > kTileTokens * NC * 4 ? RING * STAGE_U * 16 : kTileTokens * NC * 4;
 };
@@ -481,7 +481,7 @@ __device__ void sinkhorn(const KArgs& k, const float* Ls, int64_t tfirst, int nb
 
 // ------------------------------------------------------------------ epilogue
 
-// Tokens [8 b, 8 b + 8) of workgroup b (all in one tile). A load item is (token, group,
+// Tokens [OB b, OB b + OB) of workgroup b, OB = out_tokens(N) (all in one tile). A load item is (token, group,
 // chunk): one 16-byte chunk of the token's record from the slices of one summation group
 // (slices [g GS, (g+1) GS)), summed in slice order in fp64; the group sums are then added
 // in group order. Every output of the tokens follows from the totals.
@@ -647,7 +647,7 @@ inv_rms_kernel(const uint16_t* __restrict__ x, float* __restrict__ inv_rms, int6
     if (lane == 0) inv_rms[t] = (float)inv_rms_of(acc, (double)N * D, norm_eps);
 }
 
-// The Sinkhorn stage alone: kOutTokens tokens per workgroup, from given mixes and invRms
+// The Sinkhorn stage alone: out_tokens(N) tokens per workgroup, from given mixes and invRms
 // to hPre, hPost and the Sinkhorn (hIn follows in hin_kernel). The gates are those of
 // epilogue_kernel, fed with the f32 inputs widened to fp64.
 template <int N, int A>
@@ -688,7 +688,8 @@ hipError_t launch_stage(int64_t T, int D, const ForwardArgs& a, const float* h_m
     k.a = a;
     k.T = T;
     k.D = D;
-    hipLaunchKernelGGL((mix_gates_kernel<N, A>), dim3((unsigned)((T + kOutTokens - 1) / kOutTokens)),
+    constexpr int OB = Cfg<N, A>::OB;
+    hipLaunchKernelGGL((mix_gates_kernel<N, A>), dim3((unsigned)((T + OB - 1) / OB)),
                        dim3(kThreads), 0, st, k, h_mix, inv_rms);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -104,8 +104,9 @@ static int check(int n, int D, int na, long long T)
         return fail("record local", n, D, na, T, rec_loc(p.S - 1, 63, n, g.M), recb / 4);
     if ((rec_loc(0, 1, n, g.M) * 4) % 16) return fail("record alignment", n, D, na, T, 0, 0);
     // epilogue workgroups: 8 tokens each, inside one tile
-    if (kTileTokens % kOutTokens) return fail("epilogue tokens", n, D, na, T, kOutTokens, 0);
-    if (p.out_blocks * kOutTokens < T || (p.out_blocks - 1) * kOutTokens >= T) return fail("epilogue grid", n, D, na, T, p.out_blocks, 0);
+    const int ob = out_tokens(n);
+    if (kTileTokens % ob) return fail("epilogue tokens", n, D, na, T, ob, 0);
+    if (p.out_blocks * ob < T || (p.out_blocks - 1) * ob >= T) return fail("epilogue grid", n, D, na, T, p.out_blocks, 0);
     // workspace sections: ordered, 256-aligned, large enough
     const size_t secs[] = {p.off_packed, p.off_wts, p.off_rec, p.ws_bytes};
     for (int i = 0; i < 4; ++i)
