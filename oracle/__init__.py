@@ -38,7 +38,8 @@ def build(force: bool = True) -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("n_alpha", ctypes.c_int32), ("num_iters", ctypes.c_int32),
-                ("norm_eps", ctypes.c_double), ("hc_eps", ctypes.c_double)]
+                ("norm_eps", ctypes.c_double), ("hc_eps", ctypes.c_double),
+                ("x_f16", ctypes.c_int32)]
 
 
 class _Out(ctypes.Structure):
@@ -71,6 +72,11 @@ def _bind(lib):
         ctypes.c_int64, ctypes.POINTER(_Out), ctypes.c_int]
     lib.oracle_bf16_from_double.restype = ctypes.c_uint16
     lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+    if hasattr(lib, "oracle_f16_from_double"):
+        lib.oracle_f16_from_double.restype = ctypes.c_uint16
+        lib.oracle_f16_from_double.argtypes = [ctypes.c_double]
+        lib.oracle_f16_to_double.restype = ctypes.c_double
+        lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_bf16_to_double.restype = ctypes.c_double
     lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -117,6 +123,15 @@ def bf16_from_double(v: float, lib=None) -> int:
     return int((lib or _load()).oracle_bf16_from_double(float(v)))
 
 
+def f16_from_double(v: float, lib=None) -> int:
+    """Nearest binary16 (ties to even) of a double, as 16 raw bits."""
+    return int((lib or _load()).oracle_f16_from_double(float(v)))
+
+
+def f16_to_double(bits: int, lib=None) -> float:
+    return float((lib or _load()).oracle_f16_to_double(int(bits) & 0xFFFF))
+
+
 def bf16_to_double(bits: int, lib=None) -> float:
     return float((lib or _load()).oracle_bf16_to_double(int(bits) & 0xFFFF))
 
@@ -144,7 +159,7 @@ class OracleResult:
 
 def forward(x_bits, phi, alpha, bias, gamma=None, pre_mix=None, *, num_iters=20,
             norm_eps=1e-6, hc_eps=1e-6, tokens=None, want_h_in=True,
-            want_sinkhorn_steps=True, nthreads=0, lib=None) -> OracleResult:
+            want_sinkhorn_steps=True, nthreads=0, x_f16=False, lib=None) -> OracleResult:
     """Run the oracle.
 
     x_bits: uint16 bf16 bit patterns, shape [T, n, D]. phi: float32 [M, n*D].
@@ -184,7 +199,7 @@ def forward(x_bits, phi, alpha, bias, gamma=None, pre_mix=None, *, num_iters=20,
         h_in=np.empty((ntok, D)) if want_h_in else None,
         h_in_bf16=np.empty((ntok, D), dtype=np.uint16) if want_h_in else None)
     out = _Out(*[_ptr(getattr(res, f)) for f, _ in _Out._fields_])
-    cfg = _Cfg(T, n, D, n_alpha, int(num_iters), float(norm_eps), float(hc_eps))
+    cfg = _Cfg(T, n, D, n_alpha, int(num_iters), float(norm_eps), float(hc_eps), int(bool(x_f16)))
     rc = (lib or _load()).oracle_pre_forward(
         ctypes.byref(cfg), _ptr(x_bits), _ptr(phi), _ptr(alpha), _ptr(bias), _ptr(gamma),
         _ptr(pre_mix), _ptr(tok), ntok, ctypes.byref(out), int(nthreads))
@@ -193,21 +208,21 @@ def forward(x_bits, phi, alpha, bias, gamma=None, pre_mix=None, *, num_iters=20,
     return res
 
 
-def inv_rms(x_bits, *, norm_eps=1e-6, nthreads=0, lib=None) -> np.ndarray:
+def inv_rms(x_bits, *, norm_eps=1e-6, nthreads=0, x_f16=False, lib=None) -> np.ndarray:
     """invRms alone: x_bits uint16 bf16 bits [T, n, D] -> float64 [T]."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     if x_bits.ndim != 3:
         raise ValueError("x must be [T, n, D]")
     T, n, D = x_bits.shape
     out = np.empty(T)
-    cfg = _Cfg(T, n, D, 3, 1, float(norm_eps), 0.0)
+    cfg = _Cfg(T, n, D, 3, 1, float(norm_eps), 0.0, int(bool(x_f16)))
     if (lib or _load()).oracle_inv_rms(ctypes.byref(cfg), _ptr(x_bits), _ptr(out), int(nthreads)) != 0:
         raise ValueError("oracle rejected the problem description")
     return out
 
 
 def pre_sinkhorn(x_bits, h_mix, inv_rms_in, alpha, bias, pre_mix=None, *, num_iters=20,
-                 hc_eps=1e-6, want_sinkhorn_steps=True, nthreads=0, lib=None) -> OracleResult:
+                 hc_eps=1e-6, want_sinkhorn_steps=True, nthreads=0, x_f16=False, lib=None) -> OracleResult:
     """The Sinkhorn stage alone: from given mixes h_mix [T, M] and invRms [T] (converted
     to float64 exactly) and x [T, n, D] to hPre, hPost, hRes, the Sinkhorn planes and hIn.
     The result's inv_rms and h_mix fields echo the inputs."""
@@ -235,7 +250,7 @@ def pre_sinkhorn(x_bits, h_mix, inv_rms_in, alpha, bias, pre_mix=None, *, num_it
     ptrs = {f: _ptr(getattr(res, f)) for f, _ in _Out._fields_}
     ptrs["inv_rms"] = ptrs["h_mix"] = None
     out = _Out(*[ptrs[f] for f, _ in _Out._fields_])
-    cfg = _Cfg(T, n, D, n_alpha, int(num_iters), 1e-6, float(hc_eps))
+    cfg = _Cfg(T, n, D, n_alpha, int(num_iters), 1e-6, float(hc_eps), int(bool(x_f16)))
     rc = (lib or _load()).oracle_pre_sinkhorn(
         ctypes.byref(cfg), _ptr(x_bits), _ptr(h_mix), _ptr(inv_in), _ptr(alpha), _ptr(bias),
         _ptr(pre_mix), ctypes.byref(out), int(nthreads))

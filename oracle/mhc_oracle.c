@@ -41,6 +41,8 @@
  *       else hPre ([V2]; [HC] pre_mix). hPre is still computed and returned.
  *   R10 With alpha of 2 entries there is no res branch: hRes = 0, and no Sinkhorn
  *       intermediates exist ([V2]).
+ *   R17 x may be bf16 or binary16 (fp16) ([SK] 5.1 and [V2] 5.1 list both); hIn takes
+ *       x's format and is rounded to it once from double; the arithmetic is unchanged.
  */
 #include <math.h>
 #include <stddef.h>
@@ -93,6 +95,47 @@ uint16_t oracle_bf16_from_double(double v)
     return (uint16_t)(u >> 16);
 }
 
+/* ---------------------------------------------------------------- binary16 <-> double */
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits; subnormals below 2^-14.
+ * Widening is exact. */
+double oracle_f16_to_double(uint16_t bits)
+{
+    const int sgn = bits >> 15, ex = (bits >> 10) & 0x1F, fr = bits & 0x3FF;
+    double mag;
+    if (ex == 0x1F) mag = fr ? NAN : INFINITY;
+    else if (ex == 0) mag = ldexp((double)fr, -24);                 /* subnormal or zero */
+    else mag = ldexp(1.0 + (double)fr / 1024.0, ex - 15);
+    return sgn ? -mag : mag;
+}
+
+/* Round a double to the nearest binary16 (11 significant bits, exponent range 2^-14 to
+ * 2^15, subnormal spacing 2^-24), ties to even, in one step. */
+uint16_t oracle_f16_from_double(double v)
+{
+    const uint16_t sgn = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return (uint16_t)(sgn | 0x7E00u);
+    if (isinf(v)) return (uint16_t)(sgn | 0x7C00u);
+    const double a = fabs(v);
+    if (a == 0.0) return sgn;
+    int e2;
+    frexp(a, &e2);
+    int e = e2 - 1;                /* a in [2^e, 2^(e+1)) */
+    if (e < -14) e = -14;          /* below the normal range the spacing stays 2^-24 */
+    const double ulp = ldexp(1.0, e - 10);
+    const double q = a / ulp;      /* exact: scaling by a power of two */
+    const double lo = floor(q), frac = q - lo;   /* round half to even, written out */
+    const double qh = frac > 0.5 ? lo + 1.0 : (frac < 0.5 ? lo : (fmod(lo, 2.0) == 0.0 ? lo : lo + 1.0));
+    const double r = qh * ulp;     /* the rounded magnitude, exact in binary16 or 2^16 */
+    if (r >= 65536.0) return (uint16_t)(sgn | 0x7C00u);
+    if (r < ldexp(1.0, -14)) return (uint16_t)(sgn | (uint16_t)(r / ldexp(1.0, -24)));
+    int re2;
+    const double f = frexp(r, &re2);   /* r = f 2^re2, f in [0.5, 1) */
+    const int ex = re2 - 1 + 15;
+    const uint16_t fr = (uint16_t)((2.0 * f - 1.0) * 1024.0);
+    return (uint16_t)(sgn | (uint16_t)(ex << 10) | fr);
+}
+
 /* ---------------------------------------------------------------- problem description */
 
 typedef struct oracle_cfg {
@@ -103,9 +146,11 @@ typedef struct oracle_cfg {
     int32_t num_iters;
     double norm_eps;
     double hc_eps;
+    int32_t x_f16;    /* 0: x and hIn are bf16; 1: binary16 (R17) */
 } oracle_cfg;
 
-/* Outputs are optional (NULL = not wanted); all are double, laid out for the ntok
+/* Outputs are optional (NULL = not wanted); all are double (h_in_bf16: the 16-bit
+ * storage format of x, bf16 or binary16), laid out for the ntok
  * requested tokens in request order:
  *   inv_rms [ntok], h_mix [ntok][M], h_pre [ntok][n], h_post [ntok][n],
  *   h_res [ntok][n][n], sum_out [2*it][ntok][n], norm_out [2*it][ntok][n][n],
@@ -134,14 +179,24 @@ static int mix_rows(const oracle_cfg* c)
     return c->n_alpha == 3 ? c->n * c->n + 2 * c->n : 2 * c->n;
 }
 
+/* An element of x (or its 16-bit storage format, which hIn shares), widened exactly. */
+static double x_val(const oracle_cfg* c, uint16_t bits)
+{
+    return c->x_f16 ? oracle_f16_to_double(bits) : oracle_bf16_to_double(bits);
+}
+static uint16_t x_round(const oracle_cfg* c, double v)
+{
+    return c->x_f16 ? oracle_f16_from_double(v) : oracle_bf16_from_double(v);
+}
+
 /* invRms = (mean(xFlat^2) + normEps)^(-1/2) of one token's K = n*D entries xt, the
  * mean taken over all of them (R1, R2). */
-static double token_inv_rms(const uint16_t* xt, int n, int D, double norm_eps)
+static double token_inv_rms(const oracle_cfg* c, const uint16_t* xt, int n, int D, double norm_eps)
 {
     const int64_t K = (int64_t)n * D;
     double ss = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-        double v = oracle_bf16_to_double(xt[k]);
+        double v = x_val(c, xt[k]);
         ss += v * v;
     }
     return 1.0 / sqrt(ss / (double)K + norm_eps);
@@ -246,9 +301,9 @@ static void finish_token(const oracle_cfg* c, int64_t ntok, int64_t slot, int64_
         for (int d = 0; d < D; ++d) {
             double acc = 0.0;
             for (int i = 0; i < n; ++i)
-                acc += wgt[i] * oracle_bf16_to_double(xt[(int64_t)i * D + d]);
+                acc += wgt[i] * x_val(c, xt[(int64_t)i * D + d]);
             if (o->h_in) o->h_in[slot * D + d] = acc;
-            if (o->h_in_bf16) o->h_in_bf16[slot * D + d] = oracle_bf16_from_double(acc);
+            if (o->h_in_bf16) o->h_in_bf16[slot * D + d] = x_round(c, acc);
         }
     }
 }
@@ -264,14 +319,14 @@ static void one_token(const oracle_cfg* c, int64_t ntok, int64_t slot, int64_t t
     const uint16_t* xt = x + t * K;
     double* hmix = scratch;                     /* [M] */
 
-    const double inv_rms = token_inv_rms(xt, c->n, c->D, c->norm_eps);
+    const double inv_rms = token_inv_rms(c, xt, c->n, c->D, c->norm_eps);
 
     /* hMix = xGamma . phi^T with xGamma = xFlat (.) gammaFlat (R3). */
     for (int m = 0; m < M; ++m) {
         const float* row = phi + (int64_t)m * K;
         double acc = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            double xg = oracle_bf16_to_double(xt[k]);
+            double xg = x_val(c, xt[k]);
             if (gamma) xg *= (double)gamma[k];
             acc += xg * (double)row[k];
         }
@@ -335,7 +390,7 @@ int oracle_inv_rms(const oracle_cfg* c, const uint16_t* x, double* inv_rms, int 
     (void)nthreads;
 #endif
 #pragma omp parallel for schedule(static)
-    for (int64_t t = 0; t < c->T; ++t) inv_rms[t] = token_inv_rms(x + t * K, c->n, c->D, c->norm_eps);
+    for (int64_t t = 0; t < c->T; ++t) inv_rms[t] = token_inv_rms(c, x + t * K, c->n, c->D, c->norm_eps);
     return 0;
 }
 

@@ -39,10 +39,10 @@ MUTANTS = {
     "one_step_short": ("for (int k = 0; k < steps; ++k) {", "for (int k = 0; k < steps - 1; ++k) {"),
     "hin_weights_hpost": ("wgt[i] = pre_mix ? (double)pre_mix[t * n + i] : hpre[i];",
                           "wgt[i] = pre_mix ? (double)pre_mix[t * n + i] : hpost[i];"),
-    "hin_reads_interleaved_x": ("oracle_bf16_to_double(xt[(int64_t)i * D + d]);",
-                                "oracle_bf16_to_double(xt[(int64_t)d * n + i]);"),
-    "hin_on_normalised_x": ("acc += wgt[i] * oracle_bf16_to_double(xt[(int64_t)i * D + d]);",
-                            "acc += wgt[i] * inv_rms * oracle_bf16_to_double(xt[(int64_t)i * D + d]);"),
+    "hin_reads_interleaved_x": ("x_val(c, xt[(int64_t)i * D + d]);",
+                                "x_val(c, xt[(int64_t)d * n + i]);"),
+    "hin_on_normalised_x": ("acc += wgt[i] * x_val(c, xt[(int64_t)i * D + d]);",
+                            "acc += wgt[i] * inv_rms * x_val(c, xt[(int64_t)i * D + d]);"),
     "bf16_ties_away": ("else qr = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "else qr = fl + 1.0;"),
     "bf16_truncates": ("if (diff > 0.5) qr = fl + 1.0;", "if (diff > 2.0) qr = fl + 1.0;"),
 }

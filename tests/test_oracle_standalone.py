@@ -216,8 +216,8 @@ MUTANTS = {
                          "finish_token(c, c->T, t, t, x, h_mix, inv_rms[t],"),
     "inv_rms_of_token_0": ("finish_token(c, c->T, t, t, x, h_mix + t * M, inv_rms[t],",
                            "finish_token(c, c->T, t, t, x, h_mix + t * M, inv_rms[0],"),
-    "x_of_token_0": ("inv_rms[t] = token_inv_rms(x + t * K, c->n, c->D, c->norm_eps);",
-                     "inv_rms[t] = token_inv_rms(x, c->n, c->D, c->norm_eps);"),
+    "x_of_token_0": ("inv_rms[t] = token_inv_rms(c, x + t * K, c->n, c->D, c->norm_eps);",
+                     "inv_rms[t] = token_inv_rms(c, x, c->n, c->D, c->norm_eps);"),
     "rms_mean_over_D": ("ss / (double)K + norm_eps", "ss / (double)D + norm_eps"),
 }
 
