@@ -62,7 +62,12 @@ typedef int32_t mhc_status;
  *   num_iters      Sinkhorn iterations, >= 1 (ignored when n_alpha == 2)
  *   norm_eps       > 0 (RMS guard);  hc_eps >= 0 (gate / Sinkhorn guard)
  *   need_backward  0 or 1; with 1 the backward intermediates are mandatory outputs
- *   reserved       must be 0 */
+ *   x_dtype        MHC_DTYPE_BF16 (0) or MHC_DTYPE_F16 (1): the 16-bit format of x and hIn
+ *                  (the aclnnMhcPreSinkhorn and aclnnMhcPreV2 guides, section 5.1, list
+ *                  BF16 and FLOAT16). With fp16 the weights are packed as three fp16 terms
+ *                  scaled by 1, 2^11, 2^22 (phi * gamma must stay within 65504 in
+ *                  magnitude), the four-kernel path runs, and the standalone stages read
+ *                  and write fp16 too. hc_post and the backward take bf16 only. */
 typedef struct mhc_pre_params {
     int64_t T;
     int32_t n;
@@ -72,8 +77,11 @@ typedef struct mhc_pre_params {
     double norm_eps;
     double hc_eps;
     int32_t need_backward;
-    int32_t reserved;
+    int32_t x_dtype;
 } mhc_pre_params;
+
+#define MHC_DTYPE_BF16 0
+#define MHC_DTYPE_F16 1
 
 /* Device pointers. M = n*n + 2n (n_alpha == 3) or 2n (n_alpha == 2); it = num_iters.
  * Inputs:

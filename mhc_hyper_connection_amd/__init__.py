@@ -68,7 +68,7 @@ class PreForward:
     """
 
     def __init__(self, T, n, D, n_alpha=3, *, num_iters=20, norm_eps=1e-6, hc_eps=1e-6,
-                 need_backward=False, device="cuda"):
+                 need_backward=False, device="cuda", x_f16=False):
         torch = _torch()
         load()
         self.T, self.n, self.D, self.n_alpha = int(T), int(n), int(D), int(n_alpha)
@@ -78,7 +78,9 @@ class PreForward:
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
-        self.params = make_params(T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward)
+        self.x_f16 = bool(x_f16)
+        self.xdt = torch.float16 if self.x_f16 else torch.bfloat16   # x and hIn
+        self.params = make_params(T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward, self.x_f16)
         self.ws_bytes = workspace_size(self.params)
         self.packed_bytes = packed_size(self.params)
         # zero-filled once: its first bytes hold the call counter the library keeps
@@ -96,7 +98,7 @@ class PreForward:
         T, n, D, M, dev = self.T, self.n, self.D, self.M, self.device
         f32 = dict(dtype=torch.float32, device=dev)
         want = self.need_backward if intermediates is None else bool(intermediates)
-        out = {"h_in": torch.empty((T, D), dtype=torch.bfloat16, device=dev),
+        out = {"h_in": torch.empty((T, D), dtype=self.xdt, device=dev),
                "h_post": torch.empty((T, n), **f32),
                "h_res": torch.empty((T, n, n), **f32)}
         if want:
@@ -130,7 +132,7 @@ class PreForward:
         entries, see mhc_pre_forward_timed."""
         torch = _torch()
         T, n, D, M, dev = self.T, self.n, self.D, self.M, self.device
-        _check(x, "x", torch.bfloat16, (T, n, D), dev)
+        _check(x, "x", self.xdt, (T, n, D), dev)
         if phi_packed is None:
             _check(phi, "phi", torch.float32, (M, n * D), dev)
         _check(alpha, "alpha", torch.float32, (self.n_alpha,), dev)
@@ -160,12 +162,12 @@ class PreForward:
 _RUNNERS: dict = {}
 
 
-def _runner(T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward, device):
-    key = (T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward, str(device))
+def _runner(T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward, device, x_f16=False):
+    key = (T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward, str(device), x_f16)
     r = _RUNNERS.get(key)
     if r is None:
         r = PreForward(T, n, D, n_alpha, num_iters=num_iters, norm_eps=norm_eps, hc_eps=hc_eps,
-                       need_backward=need_backward, device=device)
+                       need_backward=need_backward, device=device, x_f16=x_f16)
         _RUNNERS[key] = r
     return r
 
@@ -178,7 +180,7 @@ def prepack(phi, gamma=None, *, n, n_alpha=3):
 
 def mhc_pre(x, phi, alpha, bias, gamma=None, pre_mix=None, *, num_iters=20, norm_eps=1e-6,
             hc_eps=1e-6, need_backward=False, phi_packed=None):
-    """Fused pre-mapping forward. x: bf16 [T, n, D] or [B, S, n, D].
+    """Fused pre-mapping forward. x: bf16 or fp16 [T, n, D] or [B, S, n, D]; hIn takes x's dtype.
 
     Returns (h_in, h_post, h_res, extras); extras holds inv_rms, h_mix, h_pre, sum_out
     and norm_out when need_backward is set. Shapes follow x's leading dimensions.
@@ -187,7 +189,8 @@ def mhc_pre(x, phi, alpha, bias, gamma=None, pre_mix=None, *, num_iters=20, norm
     n, D = int(x.shape[-2]), int(x.shape[-1])
     T = math.prod(lead) if lead else 1
     n_alpha = int(alpha.shape[0])
-    r = _runner(T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward, x.device)
+    r = _runner(T, n, D, n_alpha, num_iters, norm_eps, hc_eps, need_backward, x.device,
+                x.dtype == _torch().float16)
     xf = x.reshape(T, n, D)
     pm = None if pre_mix is None else pre_mix.reshape(T, n)
     out = r(xf, phi, alpha, bias, gamma, pm, phi_packed=phi_packed)
@@ -319,12 +322,13 @@ def mhc_post(x, residual, post, comb, *, out=None):
 
 
 def mhc_pre_inv_rms(x, *, norm_eps=1e-6):
-    """invRms alone: x bf16 [T, n, D] -> f32 [T] on x's device and torch's current stream."""
+    """invRms alone: x bf16 or fp16 [T, n, D] -> f32 [T] on x's device and torch's current stream."""
     torch = _torch()
     T, n, D = x.shape
-    _check(x, "x", torch.bfloat16, (T, n, D), x.device)
+    f16 = x.dtype == torch.float16
+    _check(x, "x", torch.float16 if f16 else torch.bfloat16, (T, n, D), x.device)
     out = torch.empty((T,), dtype=torch.float32, device=x.device)
-    params = make_params(T, n, D, norm_eps=norm_eps)
+    params = make_params(T, n, D, norm_eps=norm_eps, x_f16=f16)
     st = raw_inv_rms(params, _ptr(x), _ptr(out), _stream(x.device))
     if st != MHC_OK:
         raise MhcError(st, "mhc_pre_inv_rms")
@@ -334,14 +338,15 @@ def mhc_pre_inv_rms(x, *, norm_eps=1e-6):
 def mhc_pre_sinkhorn(x, h_mix, inv_rms, alpha, bias, pre_mix=None, *, num_iters=20, hc_eps=1e-6,
                      need_backward=False):
     """The Sinkhorn stage alone, from given mixes h_mix f32 [T, M] and inv_rms f32 [T]
-    with x bf16 [T, n, D]. Returns (h_in, h_pre, h_post, h_res, extras); extras holds
+    with x bf16 or fp16 [T, n, D] (hIn in the same dtype). Returns (h_in, h_pre, h_post, h_res, extras); extras holds
     sum_out and norm_out when need_backward is set and alpha has 3 entries."""
     torch = _torch()
     T, n, D = x.shape
     dev = x.device
     n_alpha = int(alpha.shape[0])
     M = n * n + 2 * n if n_alpha == 3 else 2 * n
-    _check(x, "x", torch.bfloat16, (T, n, D), dev)
+    xdt = torch.float16 if x.dtype == torch.float16 else torch.bfloat16
+    _check(x, "x", xdt, (T, n, D), dev)
     _check(h_mix, "h_mix", torch.float32, (T, M), dev)
     _check(inv_rms, "inv_rms", torch.float32, (T,), dev)
     _check(alpha, "alpha", torch.float32, (n_alpha,), dev)
@@ -349,7 +354,7 @@ def mhc_pre_sinkhorn(x, h_mix, inv_rms, alpha, bias, pre_mix=None, *, num_iters=
     if pre_mix is not None:
         _check(pre_mix, "pre_mix", torch.float32, (T, n), dev)
     f32 = dict(dtype=torch.float32, device=dev)
-    out = {"h_in": torch.empty((T, D), dtype=torch.bfloat16, device=dev),
+    out = {"h_in": torch.empty((T, D), dtype=xdt, device=dev),
            "h_pre": torch.empty((T, n), **f32), "h_post": torch.empty((T, n), **f32),
            "h_res": torch.empty((T, n, n), **f32)}
     extras = {}
@@ -357,7 +362,7 @@ def mhc_pre_sinkhorn(x, h_mix, inv_rms, alpha, bias, pre_mix=None, *, num_iters=
         extras["sum_out"] = torch.empty((2 * num_iters, T, n), **f32)
         extras["norm_out"] = torch.empty((2 * num_iters, T, n, n), **f32)
     params = make_params(T, n, D, n_alpha=n_alpha, num_iters=num_iters, hc_eps=hc_eps,
-                         need_backward=need_backward)
+                         need_backward=need_backward, x_f16=xdt == torch.float16)
     ptrs = {"x": _ptr(x), "h_mix": _ptr(h_mix), "inv_rms": _ptr(inv_rms), "alpha": _ptr(alpha),
             "bias": _ptr(bias), "pre_mix": None if pre_mix is None else _ptr(pre_mix)}
     ptrs.update({k: _ptr(v) for k, v in out.items()})

@@ -28,7 +28,7 @@ class Params(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("n_alpha", ctypes.c_int32), ("num_iters", ctypes.c_int32),
                 ("norm_eps", ctypes.c_double), ("hc_eps", ctypes.c_double),
-                ("need_backward", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("need_backward", ctypes.c_int32), ("x_dtype", ctypes.c_int32)]
 
 
 TENSOR_FIELDS = ("x", "phi", "alpha", "bias", "gamma", "pre_mix", "phi_packed", "h_in",
@@ -137,10 +137,13 @@ def status_string(status: int) -> str:
     return load().mhc_status_string(int(status)).decode()
 
 
+DTYPE_BF16, DTYPE_F16 = 0, 1
+
+
 def make_params(T, n, D, n_alpha=3, num_iters=20, norm_eps=1e-6, hc_eps=1e-6,
-                need_backward=False) -> Params:
+                need_backward=False, x_f16=False) -> Params:
     return Params(int(T), int(n), int(D), int(n_alpha), int(num_iters), float(norm_eps),
-                  float(hc_eps), int(bool(need_backward)), 0)
+                  float(hc_eps), int(bool(need_backward)), DTYPE_F16 if x_f16 else DTYPE_BF16)
 
 
 def packed_size(params: Params) -> int:

@@ -22,13 +22,14 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 mhc_status check_params(const mhc_pre_params* p, mhc::Geometry* g)
 {
     if (!p) return MHC_ERR_NULLPTR;
-    if (p->reserved != 0) return MHC_ERR_PARAM_INVALID;
+    if (p->x_dtype != MHC_DTYPE_BF16 && p->x_dtype != MHC_DTYPE_F16) return MHC_ERR_PARAM_INVALID;
     if (p->need_backward != 0 && p->need_backward != 1) return MHC_ERR_PARAM_INVALID;
     if (!(p->norm_eps > 0.0)) return MHC_ERR_PARAM_INVALID;      // also rejects NaN
     if (!(p->hc_eps >= 0.0)) return MHC_ERR_PARAM_INVALID;
     if (p->n_alpha == 3 && p->num_iters < 1) return MHC_ERR_PARAM_INVALID;
     if (p->num_iters < 0 || p->num_iters > 1000) return MHC_ERR_PARAM_INVALID;
     if (!mhc::make_geometry(p->n, p->D, p->n_alpha, g)) return MHC_ERR_PARAM_INVALID;
+    g->x_f16 = p->x_dtype == MHC_DTYPE_F16;
     return MHC_OK;
 }
 
@@ -316,7 +317,7 @@ mhc_status mhc_pre_inv_rms(const mhc_pre_params* params, const uint16_t* x, floa
     if (params->T == 0) return MHC_OK;
     if (!x || !inv_rms) return MHC_ERR_NULLPTR;
     if (!aligned(x, 16) || !aligned(inv_rms, 4)) return MHC_ERR_PARAM_INVALID;
-    return mhc::launch_inv_rms(params->T, params->n, params->D, params->norm_eps, x, inv_rms, stream) == 0
+    return mhc::launch_inv_rms(params->T, params->n, params->D, params->norm_eps, x, inv_rms, g.x_f16, stream) == 0
                ? MHC_OK
                : MHC_ERR_RUNTIME;
 }
@@ -356,8 +357,8 @@ mhc_status mhc_pre_sinkhorn(const mhc_pre_params* params, const mhc_pre_sinkhorn
     a.num_iters = params->num_iters;
     a.norm_eps = params->norm_eps;
     a.hc_eps = params->hc_eps;
-    return mhc::launch_pre_sinkhorn(params->T, params->n, params->D, params->n_alpha, a, t->h_mix, t->inv_rms,
-                                    stream) == 0
+    return mhc::launch_pre_sinkhorn(params->T, params->n, params->D, params->n_alpha, g.x_f16, a, t->h_mix,
+                                    t->inv_rms, stream) == 0
                ? MHC_OK
                : MHC_ERR_RUNTIME;
 }

@@ -38,6 +38,24 @@ __device__ __forceinline__ double bf16_bits_to_double(uint32_t b)
     return (double)__uint_as_float(b << 16);
 }
 
+// binary16 (fp16) storage of x and hIn: the same helpers for the other 16-bit format.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+// Two floats -> a packed fp16 pair (lo in bits 0-15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+// Element access for a kernel compiled for either format (H: fp16).
+template <bool H> __device__ __forceinline__ float x16_lo(uint32_t w) { return H ? f16_lo(w) : bf16_lo(w); }
+template <bool H> __device__ __forceinline__ float x16_hi(uint32_t w) { return H ? f16_hi(w) : bf16_hi(w); }
+template <bool H> __device__ __forceinline__ uint32_t pack_x16(float lo, float hi)
+{
+    return H ? pack_f16x2(lo, hi) : pack_bf16x2(lo, hi);
+}
+
 // s_waitcnt vmcnt(n): at most n vector memory operations of this wave outstanding. Called
 // from fully unrolled loops with n a constant after unrolling; each case is one instruction.
 #define MHC_VM_CASE(n) \

@@ -94,6 +94,23 @@ __device__ __forceinline__ void split3(double p, uint32_t (&tb)[3])
     tb[2] = f32_to_bf16_bits((float)r2);
 }
 
+// The fp16 form: the terms would fall below fp16's normal range, so each remainder is
+// scaled by 2^11 before it is rounded: p = hi + 2^-11 mid + 2^-22 lo, and the projection
+// scales the mid and lo column sums back (exact powers of two). Exact to ~2^-33 relative
+// for |p| in [2^-14, 65504]; larger weights overflow fp16.
+__device__ __forceinline__ void split3_f16(double p, uint32_t (&tb)[3])
+{
+    const _Float16 h0 = (_Float16)(float)p;
+    const double r1 = (p - (double)(float)h0) * 2048.0;
+    const _Float16 h1 = (_Float16)(float)r1;
+    const double r2 = (r1 - (double)(float)h1) * 2048.0;
+    const _Float16 h2 = (_Float16)(float)r2;
+    tb[0] = __builtin_bit_cast(uint16_t, h0);
+    tb[1] = __builtin_bit_cast(uint16_t, h1);
+    tb[2] = __builtin_bit_cast(uint16_t, h2);
+}
+
+template <bool H>
 __global__ void __launch_bounds__(256)
 prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
                u32x4* __restrict__ packed, int n, int D, int M, int NC, int nks, int64_t total)
@@ -116,7 +133,8 @@ prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
             double p = (double)phi[(int64_t)m * K + k0 + e];
             if (gamma) p *= (double)gamma[k0 + e];
             uint32_t tb[3];
-            split3(p, tb);
+            if constexpr (H) split3_f16(p, tb);
+            else split3(p, tb);
             w[e >> 1] |= tb[term] << (16 * (e & 1));
         }
     }
@@ -130,7 +148,7 @@ prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
 // the sum is local to the lane. fp32 FMA in stream order, one rounding to bf16. `hres`
 // covers the tile's rows of hIn (rows past T are dropped by its range); `lim` excludes
 // octets past D.
-template <int N, int NKS>
+template <int N, int NKS, bool H>
 __device__ __forceinline__ void hin_store(rsrc_t hres, uint32_t off, const u32x4 (&xr)[NKS],
                                           const float (&w)[N], int lim)
 {
@@ -144,14 +162,14 @@ __device__ __forceinline__ void hin_store(rsrc_t hres, uint32_t off, const u32x4
             const u32x4 v = xr[blk * N + i];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = fmaf(w[i], bf16_lo(v[e]), acc[2 * e]);
-                acc[2 * e + 1] = fmaf(w[i], bf16_hi(v[e]), acc[2 * e + 1]);
+                acc[2 * e] = fmaf(w[i], x16_lo<H>(v[e]), acc[2 * e]);
+                acc[2 * e + 1] = fmaf(w[i], x16_hi<H>(v[e]), acc[2 * e + 1]);
             }
         }
         u32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+            o[e] = pack_x16<H>(acc[2 * e], acc[2 * e + 1]);
         if (kBlock * blk < lim)
             __builtin_amdgcn_raw_buffer_store_b128(o, hres, (int)(off + 2 * kBlock * blk), 0, 0);
     }
@@ -203,7 +221,7 @@ constexpr int younger_than_stage(int c)
     return n;
 }
 
-template <int N, int A, int NKS>
+template <int N, int A, int NKS, bool H>
 __global__ void __launch_bounds__(kThreads, 3)
 proj_kernel(KArgs k)
 {
@@ -270,13 +288,24 @@ proj_kernel(KArgs k)
             if constexpr (NT > 8) __builtin_amdgcn_sched_barrier(0);
             const u32x4 z = {0u, 0u, 0u, 0u};
             const u32x4 xa = kBlock * (st / N) < lim ? xr[st] : z;
-            const bf16x8 Av = __builtin_bit_cast(bf16x8, xa);
-            sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Av, sq, 0, 0, 0);
+            if constexpr (H) {
+                const f16x8 Av = __builtin_bit_cast(f16x8, xa);
+                sq = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, Av, sq, 0, 0, 0);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const u32x4 bv = w[kk * 4 * NC + nt * 16];
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, __builtin_bit_cast(bf16x8, bv),
-                                                                  acc[nt], 0, 0, 0);
+                for (int nt = 0; nt < NT; ++nt) {
+                    const u32x4 bv = w[kk * 4 * NC + nt * 16];
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Av, __builtin_bit_cast(f16x8, bv),
+                                                                     acc[nt], 0, 0, 0);
+                }
+            } else {
+                const bf16x8 Av = __builtin_bit_cast(bf16x8, xa);
+                sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Av, sq, 0, 0, 0);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const u32x4 bv = w[kk * 4 * NC + nt * 16];
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, __builtin_bit_cast(bf16x8, bv),
+                                                                      acc[nt], 0, 0, 0);
+                }
             }
         }
     }
@@ -301,7 +330,7 @@ proj_kernel(KArgs k)
 #pragma unroll
         for (int i = 0; i < N; ++i) wv[i] = k.a.pre_mix[tok * N + i];
         const rsrc_t hres = make_rsrc(k.a.h_in + t0 * k.D, (int64_t)ntile * k.D * 2);
-        hin_store<N, NKS>(hres, (uint32_t)(((int64_t)row * k.D + kBlock * b0 + 8 * grp) * 2), xr, wv, lim);
+        hin_store<N, NKS, H>(hres, (uint32_t)(((int64_t)row * k.D + kBlock * b0 + 8 * grp) * 2), xr, wv, lim);
     }
     __syncthreads();
 
@@ -319,6 +348,8 @@ proj_kernel(KArgs k)
             float val;
             if (v == N) val = lds_ss[tl];
             else if ((v > N && v < PPS) || v >= PPS + (M - N)) val = 0.f;   // padding
+            else if (H)   // the fp16 terms carry scales 1, 2^11, 2^22 (split3_f16)
+                val = (float)((double)rr[m] + 0x1p-11 * (double)rr[M + m] + 0x1p-22 * (double)rr[2 * M + m]);
             else val = (float)((double)rr[m] + (double)rr[M + m] + (double)rr[2 * M + m]);
             o[e] = __float_as_uint(val);
         }
@@ -570,7 +601,7 @@ epilogue_kernel(KArgs k)
 
 // ------------------------------------------------------------------ hIn
 
-template <int N>
+template <int N, bool H>
 __global__ void __launch_bounds__(256)
 hin_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wts,
            uint16_t* __restrict__ h_in, int64_t T, int D)
@@ -591,14 +622,14 @@ hin_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wts,
         const u32x4 v = *reinterpret_cast<const u32x4*>(x + (t * N + i) * (int64_t)D + d8 * 8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            acc[2 * e] = fmaf(w[i], bf16_lo(v[e]), acc[2 * e]);
-            acc[2 * e + 1] = fmaf(w[i], bf16_hi(v[e]), acc[2 * e + 1]);
+            acc[2 * e] = fmaf(w[i], x16_lo<H>(v[e]), acc[2 * e]);
+            acc[2 * e + 1] = fmaf(w[i], x16_hi<H>(v[e]), acc[2 * e + 1]);
         }
     }
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+        o[e] = pack_x16<H>(acc[2 * e], acc[2 * e + 1]);
     // hIn is not read again by this forward: stream it past the caches
     __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(h_in + t * (int64_t)D + d8 * 8));
 }
@@ -608,7 +639,7 @@ hin_kernel(const uint16_t* __restrict__ x, const float* __restrict__ wts,
 // invRms alone: one wave per token, kThreads / 64 tokens per workgroup. A lane widens its
 // bf16 values to fp64 and adds their squares in fp64 (a bf16 square is exact there); the
 // 64 lane sums are added in fp64 across the wave.
-template <int N>
+template <int N, bool H>
 __global__ void __launch_bounds__(kThreads)
 inv_rms_kernel(const uint16_t* __restrict__ x, float* __restrict__ inv_rms, int64_t T, int D,
                double norm_eps)
@@ -628,7 +659,7 @@ inv_rms_kernel(const uint16_t* __restrict__ x, float* __restrict__ inv_rms, int6
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const double lo = bf16_lo(v[j][e]), hi = bf16_hi(v[j][e]);
+                const double lo = x16_lo<H>(v[j][e]), hi = x16_hi<H>(v[j][e]);
                 acc = fma(lo, lo, acc);
                 acc = fma(hi, hi, acc);
             }
@@ -637,7 +668,7 @@ inv_rms_kernel(const uint16_t* __restrict__ x, float* __restrict__ inv_rms, int6
         const u32x4 v = __builtin_nontemporal_load(xt + u);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const double lo = bf16_lo(v[e]), hi = bf16_hi(v[e]);
+            const double lo = x16_lo<H>(v[e]), hi = x16_hi<H>(v[e]);
             acc = fma(lo, lo, acc);
             acc = fma(hi, hi, acc);
         }
@@ -679,7 +710,7 @@ mix_gates_kernel(KArgs k, const float* __restrict__ h_mix, const float* __restri
     }
 }
 
-template <int N, int A>
+template <int N, int A, bool H>
 hipError_t launch_stage(int64_t T, int D, const ForwardArgs& a, const float* h_mix, const float* inv_rms,
                         hipStream_t st)
 {
@@ -694,7 +725,7 @@ hipError_t launch_stage(int64_t T, int D, const ForwardArgs& a, const float* h_m
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t items = T * (int64_t)(D / 8);
-    hipLaunchKernelGGL(hin_kernel<N>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, a.x,
+    hipLaunchKernelGGL((hin_kernel<N, H>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, a.x,
                        a.pre_mix ? a.pre_mix : a.h_pre, a.h_in, T, D);
     return hipGetLastError();
 }
@@ -1129,12 +1160,12 @@ hipError_t mark(void* const* events, int i, hipStream_t st)
     return events && events[i] ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
 }
 
-template <int N, int A, int NKS>
+template <int N, int A, int NKS, bool H>
 hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st, void* const* events)
 {
     // Workgroups map to tasks so that each XCD's L2 holds the weights of a few slices
     // only (task_of_block).
-    hipLaunchKernelGGL((proj_kernel<N, A, NKS>), dim3((unsigned)p.proj_blocks), dim3(kThreads), 0, st, k);
+    hipLaunchKernelGGL((proj_kernel<N, A, NKS, H>), dim3((unsigned)p.proj_blocks), dim3(kThreads), 0, st, k);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) e = mark(events, kStageProj + 1, st);
     if (e != hipSuccess) return e;
@@ -1144,7 +1175,7 @@ hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st, void* con
     if (e == hipSuccess && k.a.pre_mix) e = mark(events, kStageHin + 1, st);
     if (e != hipSuccess || k.a.pre_mix) return e;
     const int64_t items = p.T * (int64_t)(p.g.D / 8);
-    hipLaunchKernelGGL(hin_kernel<N>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, k.a.x, k.a.wts,
+    hipLaunchKernelGGL((hin_kernel<N, H>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, k.a.x, k.a.wts,
                        k.a.h_in, p.T, p.g.D);
     e = hipGetLastError();
     return e == hipSuccess ? mark(events, kStageHin + 1, st) : e;
@@ -1221,37 +1252,50 @@ int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void
 {
     const int64_t total = (int64_t)(g.nks + kPadSteps) * 4 * g.NC;
     const unsigned blocks = (unsigned)((total + 255) / 256);
-    hipLaunchKernelGGL(prepack_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, phi, gamma,
-                       static_cast<u32x4*>(packed), g.n, g.D, g.M, g.NC, g.nks, total);
+    if (g.x_f16)
+        hipLaunchKernelGGL(prepack_kernel<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, phi, gamma,
+                           static_cast<u32x4*>(packed), g.n, g.D, g.M, g.NC, g.nks, total);
+    else
+        hipLaunchKernelGGL(prepack_kernel<false>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, phi, gamma,
+                           static_cast<u32x4*>(packed), g.n, g.D, g.M, g.NC, g.nks, total);
     return (int)hipGetLastError();
 }
 
 int launch_inv_rms(int64_t T, int n, int D, double norm_eps, const uint16_t* x, float* inv_rms,
-                   void* stream)
+                   int x_f16, void* stream)
 {
     if (T <= 0) return 0;
     constexpr int per_block = kThreads / 64;
     const dim3 grid((unsigned)((T + per_block - 1) / per_block));
     hipStream_t st = (hipStream_t)stream;
-    if (n == 4) hipLaunchKernelGGL(inv_rms_kernel<4>, grid, dim3(kThreads), 0, st, x, inv_rms, T, D, norm_eps);
-    else if (n == 6) hipLaunchKernelGGL(inv_rms_kernel<6>, grid, dim3(kThreads), 0, st, x, inv_rms, T, D, norm_eps);
-    else if (n == 8) hipLaunchKernelGGL(inv_rms_kernel<8>, grid, dim3(kThreads), 0, st, x, inv_rms, T, D, norm_eps);
+#define MHC_INV_RMS(NV, HV) hipLaunchKernelGGL((inv_rms_kernel<NV, HV>), grid, dim3(kThreads), 0, st, x, inv_rms, T, D, norm_eps)
+    if (n == 4 && !x_f16) MHC_INV_RMS(4, false);
+    else if (n == 6 && !x_f16) MHC_INV_RMS(6, false);
+    else if (n == 8 && !x_f16) MHC_INV_RMS(8, false);
+    else if (n == 4) MHC_INV_RMS(4, true);
+    else if (n == 6) MHC_INV_RMS(6, true);
+    else if (n == 8) MHC_INV_RMS(8, true);
+#undef MHC_INV_RMS
     else return (int)hipErrorInvalidValue;
     return (int)hipGetLastError();
 }
 
-int launch_pre_sinkhorn(int64_t T, int n, int D, int n_alpha, const ForwardArgs& a, const float* h_mix,
-                        const float* inv_rms, void* stream)
+int launch_pre_sinkhorn(int64_t T, int n, int D, int n_alpha, int x_f16, const ForwardArgs& a,
+                        const float* h_mix, const float* inv_rms, void* stream)
 {
     if (T <= 0) return 0;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = hipErrorInvalidValue;
-    if (n == 4 && n_alpha == 3) e = launch_stage<4, 3>(T, D, a, h_mix, inv_rms, st);
-    else if (n == 4 && n_alpha == 2) e = launch_stage<4, 2>(T, D, a, h_mix, inv_rms, st);
-    else if (n == 8 && n_alpha == 3) e = launch_stage<8, 3>(T, D, a, h_mix, inv_rms, st);
-    else if (n == 8 && n_alpha == 2) e = launch_stage<8, 2>(T, D, a, h_mix, inv_rms, st);
-    else if (n == 6 && n_alpha == 3) e = launch_stage<6, 3>(T, D, a, h_mix, inv_rms, st);
-    else if (n == 6 && n_alpha == 2) e = launch_stage<6, 2>(T, D, a, h_mix, inv_rms, st);
+    const bool h = x_f16 != 0;
+#define MHC_STAGE(NV, AV) (h ? launch_stage<NV, AV, true>(T, D, a, h_mix, inv_rms, st) \
+                             : launch_stage<NV, AV, false>(T, D, a, h_mix, inv_rms, st))
+    if (n == 4 && n_alpha == 3) e = MHC_STAGE(4, 3);
+    else if (n == 4 && n_alpha == 2) e = MHC_STAGE(4, 2);
+    else if (n == 8 && n_alpha == 3) e = MHC_STAGE(8, 3);
+    else if (n == 8 && n_alpha == 2) e = MHC_STAGE(8, 2);
+    else if (n == 6 && n_alpha == 3) e = MHC_STAGE(6, 3);
+    else if (n == 6 && n_alpha == 2) e = MHC_STAGE(6, 2);
+#undef MHC_STAGE
     return (int)e;
 }
 
@@ -1306,13 +1350,17 @@ int launch_forward(const Plan& p, const ForwardArgs& a_in, void* stream, void* c
     if (n == 6 && na == 3 && (v.nt != Cfg<6, 3>::NT || v.sk != Cfg<6, 3>::SK)) return (int)hipErrorInvalidValue;
     if (n == 6 && na == 2 && (v.nt != Cfg<6, 2>::NT || v.sk != Cfg<6, 2>::SK)) return (int)hipErrorInvalidValue;
     hipError_t e = hipErrorInvalidValue;
-    if (n == 4 && na == 3 && nks == 16) e = launch_group<4, 3, 16>(p, k, st, events);
-    else if (n == 4 && na == 2 && nks == 32) e = launch_group<4, 2, 32>(p, k, st, events);
-    else if (n == 4 && na == 2 && nks == 16) e = launch_group<4, 2, 16>(p, k, st, events);
-    else if (n == 8 && na == 3 && nks == 8) e = launch_group<8, 3, 8>(p, k, st, events);
-    else if (n == 8 && na == 2 && nks == 16) e = launch_group<8, 2, 16>(p, k, st, events);
-    else if (n == 6 && na == 3 && nks == 12) e = launch_group<6, 3, 12>(p, k, st, events);
-    else if (n == 6 && na == 2 && nks == 12) e = launch_group<6, 2, 12>(p, k, st, events);
+    const bool h = p.g.x_f16 != 0;
+#define MHC_GROUP(NV, AV, KV) (h ? launch_group<NV, AV, KV, true>(p, k, st, events) \
+                                 : launch_group<NV, AV, KV, false>(p, k, st, events))
+    if (n == 4 && na == 3 && nks == 16) e = MHC_GROUP(4, 3, 16);
+    else if (n == 4 && na == 2 && nks == 32) e = MHC_GROUP(4, 2, 32);
+    else if (n == 4 && na == 2 && nks == 16) e = MHC_GROUP(4, 2, 16);
+    else if (n == 8 && na == 3 && nks == 8) e = MHC_GROUP(8, 3, 8);
+    else if (n == 8 && na == 2 && nks == 16) e = MHC_GROUP(8, 2, 16);
+    else if (n == 6 && na == 3 && nks == 12) e = MHC_GROUP(6, 3, 12);
+    else if (n == 6 && na == 2 && nks == 12) e = MHC_GROUP(6, 2, 12);
+#undef MHC_GROUP
     return (int)e;
 }
 

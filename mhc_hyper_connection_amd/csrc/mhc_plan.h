@@ -81,6 +81,7 @@ struct Geometry {
     int NC = 0;          // 16 * NT
     int nblk = 0;        // d-blocks: ceil(D / 32)
     int nks = 0;         // K-steps holding data: nblk * n
+    int x_f16 = 0;       // x and hIn in binary16 (else bf16); weights packed as fp16 terms
     size_t packed_bytes = 0;
 };
 
@@ -193,7 +194,7 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     p.proj_blocks = proj_blocks(p.tiles, p.S);
     p.out_blocks = (T + out_tokens(g.n) - 1) / out_tokens(g.n);
     p.FP = kFMembers;
-    p.fused_geom = g.n == 4 && g.n_alpha == 3 && g.nblk >= kFMembers && (g.nblk + p.FP - 1) / p.FP <= kFMaxBlocks;
+    p.fused_geom = g.n == 4 && g.n_alpha == 3 && !g.x_f16 && g.nblk >= kFMembers && (g.nblk + p.FP - 1) / p.FP <= kFMaxBlocks;
     p.FGS = (p.FP + 7) / 8;
     p.FNG = (p.FP + p.FGS - 1) / p.FGS;
     p.tiles16 = (T + kFTok - 1) / kFTok;
@@ -315,9 +316,9 @@ int record_event(void* event, void* stream);
 // given inputs, and from a: x, alpha, bias, pre_mix, the outputs h_in, h_pre, h_post, h_res,
 // sum_out, norm_out, num_iters and hc_eps. 0 or the HIP error code.
 int launch_inv_rms(int64_t T, int n, int D, double norm_eps, const uint16_t* x, float* inv_rms,
-                   void* stream);
-int launch_pre_sinkhorn(int64_t T, int n, int D, int n_alpha, const ForwardArgs& a, const float* h_mix,
-                        const float* inv_rms, void* stream);
+                   int x_f16, void* stream);
+int launch_pre_sinkhorn(int64_t T, int n, int D, int n_alpha, int x_f16, const ForwardArgs& a,
+                        const float* h_mix, const float* inv_rms, void* stream);
 // hc_post (mhc_post.hip): out = post x + comb residual per token; 0 or the HIP error code.
 int launch_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* residual, const float* post,
                 const float* comb, uint16_t* out, void* stream);

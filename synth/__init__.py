@@ -7,7 +7,8 @@ drawn activations into the bf16 tensor the operator consumes.
 
 Recipe (per workload, NumPy PCG64 seeded with ``seed``), tensors drawn in this
 order, each in C order:
-  x       [T, n, D]  float32 N(0, 1), then rounded to bf16 (nearest, ties to even);
+  x       [T, n, D]  float32 N(0, 1), then rounded to bf16 (nearest, ties to even), or
+                     to binary16 for an fp16 workload (NumPy's float16 conversion);
                      drawn in chunks of ``X_CHUNK`` values (the stream is identical
                      to a single draw, the chunking only bounds host memory)
   phi     [M, n*D]   float32 N(0, 1) / sqrt(n*D)   (std 1/sqrt(n*D): mixes stay O(1))
@@ -94,6 +95,7 @@ class Workload:
     hc_eps: float = 1e-6
     seed: int = 0
     note: str = ""
+    x_f16: bool = False     # x (and hIn) in binary16 instead of bf16
 
     @property
     def M(self) -> int:
@@ -141,7 +143,8 @@ def generate(wl: Workload, seed: int | None = None) -> Inputs:
     x = np.empty(total, dtype=np.uint16)
     for start in range(0, total, X_CHUNK):
         stop = min(total, start + X_CHUNK)
-        x[start:stop] = f32_to_bf16_bits(rng.standard_normal(stop - start, dtype=np.float32))
+        v = rng.standard_normal(stop - start, dtype=np.float32)
+        x[start:stop] = v.astype(np.float16).view(np.uint16) if wl.x_f16 else f32_to_bf16_bits(v)
     x = x.reshape(wl.T, wl.n, wl.D)
     K = wl.K
     phi = (rng.standard_normal((wl.M, K), dtype=np.float32) / np.float32(np.sqrt(K))).astype(np.float32)
@@ -154,10 +157,10 @@ def generate(wl: Workload, seed: int | None = None) -> Inputs:
 
 def custom(T: int, n: int, D: int, *, n_alpha: int = 3, gamma: bool = False,
            pre_mix: bool = False, need_backward: bool = False, num_iters: int = 20,
-           seed: int = 7, name: str = "custom") -> Inputs:
+           seed: int = 7, name: str = "custom", x_f16: bool = False) -> Inputs:
     """Same distributions at any shape (test sizes: tails, page example shapes)."""
     wl = Workload(name, T=T, n=n, D=D, n_alpha=n_alpha, gamma=gamma, pre_mix=pre_mix,
-                  need_backward=need_backward, num_iters=num_iters, seed=seed)
+                  need_backward=need_backward, num_iters=num_iters, seed=seed, x_f16=x_f16)
     return generate(wl)
 
 
@@ -261,11 +264,15 @@ class StageInputs:
 
 
 def stage_inputs(T: int, n: int, D: int, *, n_alpha: int = 3, pre_mix: bool = False,
-                 seed: int = 31) -> StageInputs:
-    """Inputs of the standalone stages with the recipe in the module docstring."""
+                 seed: int = 31, x_f16: bool = False) -> StageInputs:
+    """Inputs of the standalone stages with the recipe in the module docstring (x_f16: x
+    rounded to binary16 instead of bf16)."""
     rng = np.random.default_rng(seed)
     M = n * n + 2 * n if n_alpha == 3 else 2 * n
-    x = _bf16_normal(rng, T * n * D).reshape(T, n, D)
+    if x_f16:
+        x = rng.standard_normal(T * n * D, dtype=np.float32).astype(np.float16).view(np.uint16).reshape(T, n, D)
+    else:
+        x = _bf16_normal(rng, T * n * D).reshape(T, n, D)
     alpha = rng.uniform(0.5, 1.5, size=n_alpha).astype(np.float32)
     bias = (0.1 * rng.standard_normal(M)).astype(np.float32)
     hmix = rng.standard_normal((T, M), dtype=np.float32)

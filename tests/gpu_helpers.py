@@ -34,18 +34,20 @@ def device():
     return torch.device("cuda", 0)
 
 
-def to_dev(a, dev):
+def to_dev(a, dev, f16=False):
+    """numpy -> device tensor; uint16 arrays are bf16 bits (fp16 bits with f16)."""
     torch = torch_mod()
     if a is None:
         return None
     if a.dtype == np.uint16:
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+            torch.float16 if f16 else torch.bfloat16).to(dev)
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
 def to_host(t):
     torch = torch_mod()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.cpu().numpy()
 
@@ -61,8 +63,8 @@ def gpu_forward(inp: Inputs, *, need_backward=None, intermediates=True, packed=F
     if runner is None:
         runner = mhc.PreForward(wl.T, wl.n, wl.D, wl.n_alpha, num_iters=wl.num_iters,
                                 norm_eps=wl.norm_eps, hc_eps=wl.hc_eps, need_backward=nb,
-                                device=dev)
-    x = to_dev(inp.x, dev)
+                                device=dev, x_f16=wl.x_f16)
+    x = to_dev(inp.x, dev, wl.x_f16)
     phi = to_dev(inp.phi, dev)
     alpha = to_dev(inp.alpha, dev)
     bias = to_dev(inp.bias, dev)
@@ -73,8 +75,8 @@ def gpu_forward(inp: Inputs, *, need_backward=None, intermediates=True, packed=F
     results = []
     for _ in range(repeat):
         for v in out.values():
-            if v.dtype == torch.bfloat16:
-                v.view(torch.int16).fill_(0x7FC0)   # NaN: anything not written shows
+            if v.dtype in (torch.bfloat16, torch.float16):
+                v.view(torch.int16).fill_(0x7FC0 if v.dtype == torch.bfloat16 else 0x7E00)   # NaN
             else:
                 v.fill_(float("nan"))
         runner(x, None if packed else phi, alpha, bias, None if packed else gamma, pre_mix,
@@ -87,7 +89,7 @@ def gpu_forward(inp: Inputs, *, need_backward=None, intermediates=True, packed=F
 def run_oracle(inp: Inputs, tokens=None, want_steps=True):
     wl = inp.wl
     return oracle.forward(inp.x, inp.phi, inp.alpha, inp.bias, inp.gamma, inp.pre_mix,
-                          num_iters=wl.num_iters, norm_eps=wl.norm_eps, hc_eps=wl.hc_eps,
+                          num_iters=wl.num_iters, norm_eps=wl.norm_eps, hc_eps=wl.hc_eps, x_f16=wl.x_f16,
                           tokens=tokens, want_sinkhorn_steps=want_steps)
 
 
@@ -111,9 +113,10 @@ def bf16_ordered(bits):
     return np.where(b & 0x8000, -(b & 0x7FFF), b)
 
 
-def _hin_check(g_bits, ref_double, ref_bits, scale, report):
+def _hin_check(g_bits, ref_double, ref_bits, scale, report, f16=False):
+    # sign-magnitude 16-bit formats: the ordered distance counts ulps in bf16 and fp16 alike
     dist = np.abs(bf16_ordered(g_bits) - bf16_ordered(ref_bits))
-    g = bf16_bits_to_f32(g_bits).astype(np.float64)
+    g = (np.asarray(g_bits, np.uint16).view(np.float16) if f16 else bf16_bits_to_f32(g_bits)).astype(np.float64)
     within_ulp = dist <= 1
     within_cancel = np.abs(g - ref_double) <= HIN_CANCEL * scale
     ok = within_ulp | within_cancel
@@ -142,10 +145,10 @@ def compare(gpu: dict, orc, inp: Inputs, tokens=None, *, check_steps=True):
     if check_steps and "sum_out" in gpu and orc.sum_out is not None:
         _fp32_check("sum_out", gpu["sum_out"][:, tok], orc.sum_out, rep)
         _fp32_check("norm_out", gpu["norm_out"][:, tok], orc.norm_out, rep)
-    x = bf16_bits_to_f32(inp.x[tok]).astype(np.float64)            # [ntok, n, D]
+    x = (inp.x[tok].view(np.float16) if wl.x_f16 else bf16_bits_to_f32(inp.x[tok])).astype(np.float64)
     w = (inp.pre_mix[tok].astype(np.float64) if inp.pre_mix is not None else orc.h_pre)
     scale = np.einsum("ti,tid->td", np.abs(w), np.abs(x))
-    _hin_check(gpu["h_in"][tok], orc.h_in, orc.h_in_bf16, scale, rep)
+    _hin_check(gpu["h_in"][tok], orc.h_in, orc.h_in_bf16, scale, rep, wl.x_f16)
     failing = {k: v for k, v in rep.items() if v.get("fail", 0)}
     if failing:
         raise AssertionError(f"parity failures: {failing}")

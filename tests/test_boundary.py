@@ -97,10 +97,20 @@ def test_invalid_attributes(kw):
     assert fwd(_p(**kw)) == B.MHC_ERR_PARAM_INVALID
 
 
-def test_reserved_and_need_backward_values():
-    p = _p()
-    p.reserved = 1
-    assert fwd(p) == B.MHC_ERR_PARAM_INVALID
+def test_x_dtype_and_need_backward_values():
+    for bad in (2, -1, 7):
+        p = _p()
+        p.x_dtype = bad
+        assert fwd(p) == B.MHC_ERR_PARAM_INVALID
+    p = _p(T=0)
+    p.x_dtype = B.DTYPE_F16
+    assert fwd(p) == B.MHC_OK
+    # fp16 never takes the single-read kernel
+    path = ctypes.c_int32(-1)
+    p = _p(T=1 << 16, D=7168)
+    p.x_dtype = B.DTYPE_F16
+    assert B.load().mhc_pre_forward_path(ctypes.byref(p), 0, ctypes.byref(path)) == B.MHC_OK
+    assert path.value == 0
     p = _p()
     p.need_backward = 2
     assert fwd(p) == B.MHC_ERR_PARAM_INVALID

@@ -58,6 +58,14 @@ SMALL = [
     ("n6_alpha2_premix_D520", lambda: synth.custom(65, 6, 520, n_alpha=2, pre_mix=True, need_backward=True, seed=62)),
     ("n6_alpha3_premix_D24_T9", lambda: synth.custom(9, 6, 24, pre_mix=True, need_backward=True, seed=63)),
     ("n6_D16384_T3", lambda: synth.custom(3, 6, 16384, need_backward=True, seed=64)),
+    # binary16 x and hIn: fp16 matrix-core products against weights split into three
+    # scaled fp16 terms
+    ("f16_n4_alpha3_bwd", lambda: synth.custom(130, 4, 1024, need_backward=True, x_f16=True, seed=80)),
+    ("f16_n4_D7168_gamma", lambda: synth.custom(70, 4, 7168, gamma=True, need_backward=True, x_f16=True, seed=81)),
+    ("f16_n8_alpha2_premix_D520", lambda: synth.custom(65, 8, 520, n_alpha=2, pre_mix=True, need_backward=True,
+                                                       x_f16=True, seed=82)),
+    ("f16_n6_D40_T9", lambda: synth.custom(9, 6, 40, need_backward=True, x_f16=True, seed=83)),
+    ("f16_n4_T1024_D4096_gamma", lambda: synth.custom(1024, 4, 4096, gamma=True, x_f16=True, seed=84)),
 ]
 
 

@@ -120,3 +120,35 @@ def test_stages_empty_input():
     h_in, h_pre, h_post, h_res, ex = mhc.mhc_pre_sinkhorn(d(si.x), d(si.h_mix), d(si.inv_rms), d(si.alpha),
                                                           d(si.bias), need_backward=True)
     assert h_in.shape == (0, 64) and ex["norm_out"].shape == (40, 0, 4, 4)
+
+
+@pytest.mark.parametrize("T,n,D,na,pm", [(33, 4, 520, 3, False), (20, 8, 64, 2, True), (11, 6, 48, 3, True)])
+def test_stages_f16(T, n, D, na, pm):
+    # binary16 x and hIn through both standalone stages
+    import mhc_hyper_connection_amd as mhc
+    import torch
+    print(f"[case] stages f16 T={T} n={n} D={D} alpha={na} pre_mix={pm}", file=sys.stderr, flush=True)
+    dev = device()
+    si = synth.stage_inputs(T, n, D, n_alpha=na, pre_mix=pm, seed=90 + T, x_f16=True)
+    x = to_dev(si.x, dev, True)
+    g_inv = to_host(mhc.mhc_pre_inv_rms(x))
+    r_inv = oracle.inv_rms(si.x, x_f16=True)
+    assert float(np.max(np.abs(g_inv.astype(np.float64) - r_inv) / r_inv)) <= 2.0 ** -23
+    d = lambda a: None if a is None else to_dev(a, dev)
+    h_in, h_pre, h_post, h_res, ex = mhc.mhc_pre_sinkhorn(x, d(si.h_mix), d(si.inv_rms), d(si.alpha), d(si.bias),
+                                                          d(si.pre_mix), need_backward=True)
+    torch.cuda.synchronize(dev)
+    assert h_in.dtype == torch.float16
+    r = oracle.pre_sinkhorn(si.x, si.h_mix, si.inv_rms, si.alpha, si.bias, si.pre_mix, x_f16=True)
+    rep = {}
+    _fp32_check("h_pre", to_host(h_pre), r.h_pre, rep)
+    _fp32_check("h_post", to_host(h_post), r.h_post, rep)
+    if na == 3:
+        _fp32_check("h_res", to_host(h_res), r.h_res, rep)
+        _fp32_check("norm_out", to_host(ex["norm_out"]), r.norm_out, rep)
+    xf = si.x.view(np.float16).astype(np.float64)
+    w = si.pre_mix.astype(np.float64) if si.pre_mix is not None else r.h_pre
+    _hin_check(to_host(h_in), r.h_in, r.h_in_bf16, np.einsum("ti,tid->td", np.abs(w), np.abs(xf)), rep, True)
+    print(f"[parity-stages-f16] {summary(rep)}", file=sys.stderr, flush=True)
+    failing = {k: v for k, v in rep.items() if v.get("fail", 0)}
+    assert not failing, f"parity failures: {failing}"
