@@ -341,6 +341,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens of the workload the CPU oracle baseline runs on (bounded)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--graph-replays", type=int, default=0,
+                    help="after the timed steps, capture one step into a HIP graph and report "
+                         "its per-replay time over this many replays (four-kernel path only)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain copy of this size first (for counter calibration)")
     ap.add_argument("--op", choices=("forward", "backward", "post"), default="forward",
@@ -469,6 +472,23 @@ def main():
                  "frac": b_call / (call_avg * 1e-6) / 1e9 / HBM_PEAK_GBS},
         "kernels": kernels,
     }
+    if args.graph_replays > 0 and not single_read:
+        # launch-bound sizes: the same step replayed from a captured graph (outside the
+        # timed region; a capturing stream never takes the cooperative kernel)
+        print(f"[bench] graph replays {args.graph_replays}", file=sys.stderr, flush=True)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(x, phi, alpha, bias, gamma, pre_mix, out=out)
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.graph_replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        us = 1e3 * e0.elapsed_time(e1) / args.graph_replays
+        line["graph"] = {"replays": args.graph_replays, "us_per_call": us,
+                         "tokens_per_s": wl.T / (us * 1e-6)}
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)

@@ -18,7 +18,7 @@
 //                    x x^T. The task writes one partial record per token. With pre_mix the
 //                    hIn weights are inputs, and the task also writes its slice of hIn
 //                    from the registers it already holds (x is read once).
-//   epilogue_kernel  one workgroup per 16 (n = 4) or 8 tokens: sums the S partial records of each token
+//   epilogue_kernel  one workgroup per 16 (n = 4, T >= 8192) or 8 tokens: sums the S partial records of each token
 //                    in a fixed order (fp64), then invRms, hMix, the gates, the Sinkhorn
 //                    planes (one lane per matrix entry, sums across lanes by DPP) and,
 //                    without pre_mix, the hIn weights.
@@ -32,7 +32,7 @@
 // invRms and the Sinkhorn stage as operators of their own):
 //   inv_rms_kernel   invRms alone: one wave per token, squares and sums in fp64.
 //   mix_gates_kernel the Sinkhorn stage from given mixes and invRms: the epilogue's gates and
-//                    Sinkhorn for out_tokens(n) tokens per workgroup; hin_kernel follows.
+//                    Sinkhorn for 8 or 16 tokens per workgroup; hin_kernel follows.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -60,7 +60,6 @@ struct Cfg {
     static constexpr int CH = V / 4;              // 16-byte chunks per record
     static constexpr int KU = 4 * NC;             // 16-byte units per K-step of packed weights
     static constexpr int STAGE_U = SK * KU;
-    static constexpr int OB = out_tokens(N);      // tokens per epilogue workgroup
     static_assert(STAGE_U % 64 == 0, "a stage is whole 64-lane load instructions");
     static constexpr int PROJ_LDS = RING * STAGE_U * 16 > kTileTokens * NC * 4 ? RING * STAGE_U * 16 : kTileTokens * NC * 4;
 };
@@ -512,16 +511,16 @@ __device__ void sinkhorn(const KArgs& k, const float* Ls, int64_t tfirst, int nb
 
 // ------------------------------------------------------------------ epilogue
 
-// Tokens [OB b, OB b + OB) of workgroup b, OB = out_tokens(N) (all in one tile). A load item is (token, group,
+// Tokens [OB b, OB b + OB) of workgroup b, OB = out_tokens(N, T) (all in one tile). A load item is (token, group,
 // chunk): one 16-byte chunk of the token's record from the slices of one summation group
 // (slices [g GS, (g+1) GS)), summed in slice order in fp64; the group sums are then added
 // in group order. Every output of the tokens follows from the totals.
-template <int N, int A>
+template <int N, int A, int OB>
 __global__ void __launch_bounds__(kThreads)
 epilogue_kernel(KArgs k)
 {
     using C = Cfg<N, A>;
-    constexpr int NN = C::NN, V = C::V, CH = C::CH, M = C::M, PPS = C::PPS, OB = C::OB;
+    constexpr int NN = C::NN, V = C::V, CH = C::CH, M = C::M, PPS = C::PPS;
     static_assert(kTileTokens % OB == 0, "a workgroup's tokens lie in one tile");
     __shared__ double gs[OB * V * 8];    // [token][value][group]; group 0 then holds the total
     __shared__ float Ls[OB * NN];
@@ -678,15 +677,15 @@ inv_rms_kernel(const uint16_t* __restrict__ x, float* __restrict__ inv_rms, int6
     if (lane == 0) inv_rms[t] = (float)inv_rms_of(acc, (double)N * D, norm_eps);
 }
 
-// The Sinkhorn stage alone: out_tokens(N) tokens per workgroup, from given mixes and invRms
+// The Sinkhorn stage alone: OB = out_tokens(N, T) tokens per workgroup, from given mixes and invRms
 // to hPre, hPost and the Sinkhorn (hIn follows in hin_kernel). The gates are those of
 // epilogue_kernel, fed with the f32 inputs widened to fp64.
-template <int N, int A>
+template <int N, int A, int OB>
 __global__ void __launch_bounds__(kThreads)
 mix_gates_kernel(KArgs k, const float* __restrict__ h_mix, const float* __restrict__ inv_in)
 {
     using C = Cfg<N, A>;
-    constexpr int NN = C::NN, M = C::M, OB = C::OB;
+    constexpr int NN = C::NN, M = C::M;
     __shared__ float Ls[OB * NN];
     const ForwardArgs& a = k.a;
     const int tid = threadIdx.x;
@@ -719,9 +718,12 @@ hipError_t launch_stage(int64_t T, int D, const ForwardArgs& a, const float* h_m
     k.a = a;
     k.T = T;
     k.D = D;
-    constexpr int OB = Cfg<N, A>::OB;
-    hipLaunchKernelGGL((mix_gates_kernel<N, A>), dim3((unsigned)((T + OB - 1) / OB)),
-                       dim3(kThreads), 0, st, k, h_mix, inv_rms);
+    if (N == 4 && out_tokens(N, T) == 16)
+        hipLaunchKernelGGL((mix_gates_kernel<N, A, 16>), dim3((unsigned)((T + 15) / 16)), dim3(kThreads), 0, st, k,
+                           h_mix, inv_rms);
+    else
+        hipLaunchKernelGGL((mix_gates_kernel<N, A, 8>), dim3((unsigned)((T + 7) / 8)), dim3(kThreads), 0, st, k,
+                           h_mix, inv_rms);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t items = T * (int64_t)(D / 8);
@@ -1169,7 +1171,10 @@ hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st, void* con
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) e = mark(events, kStageProj + 1, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((epilogue_kernel<N, A>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
+    if (N == 4 && p.OB == 16)
+        hipLaunchKernelGGL((epilogue_kernel<N, A, 16>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
+    else
+        hipLaunchKernelGGL((epilogue_kernel<N, A, 8>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
     e = hipGetLastError();
     if (e == hipSuccess) e = mark(events, kStageEpi + 1, st);
     if (e == hipSuccess && k.a.pre_mix) e = mark(events, kStageHin + 1, st);
@@ -1233,7 +1238,10 @@ hipError_t launch_fused(const Plan& p, const ForwardArgs& a, int G, hipStream_t 
     k.S = p.FP;
     k.GS = p.FGS;
     k.NG = p.FNG;
-    hipLaunchKernelGGL((epilogue_kernel<4, 3>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
+    if (p.OB == 16)
+        hipLaunchKernelGGL((epilogue_kernel<4, 3, 16>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
+    else
+        hipLaunchKernelGGL((epilogue_kernel<4, 3, 8>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
     e = hipGetLastError();
     if (e == hipSuccess) e = mark(events, kStageEpi + 1, st);
     if (e == hipSuccess) e = mark(events, kStageHin + 1, st);

@@ -56,9 +56,10 @@ constexpr int kMaxD = 16384;
 constexpr int kMaxN = 8;
 constexpr int64_t kBigTasks = 1024;    // prefer the large slice when it still gives this many tasks
 constexpr int kMaxSlices = 256;        // slices per tile
-// Tokens per epilogue workgroup: 16 for n = 4 (16 Sinkhorn matrices of 16 lanes fill the
-// 256 threads), else 8.
-MHC_HOST_DEVICE constexpr int out_tokens(int n) { return n == 4 ? 16 : 8; }
+// Tokens per epilogue workgroup: 16 for n = 4 with many tokens (16 Sinkhorn matrices of 16
+// lanes fill the 256 threads), else 8 (more workgroups share the work of a small T).
+constexpr int64_t kWideEpilogueTokens = 8192;
+MHC_HOST_DEVICE constexpr int out_tokens(int n, int64_t T) { return n == 4 && T >= kWideEpilogueTokens ? 16 : 8; }
 
 // Single-read kernel (see above).
 constexpr int kFTok = 16;              // tokens per tile
@@ -165,7 +166,8 @@ struct Plan {
     int NG = 0;               // summation groups: ceil(S / GS) <= 8
     int64_t tasks = 0;        // tiles * S
     int64_t proj_blocks = 0;  // projection workgroups (tasks plus padding, see task_of_block)
-    int64_t out_blocks = 0;   // epilogue workgroups: ceil(T / out_tokens(n))
+    int OB = 8;               // tokens per epilogue workgroup: out_tokens(n, T)
+    int64_t out_blocks = 0;   // epilogue workgroups: ceil(T / OB)
     // single-read variant
     bool fused_geom = false;  // the geometry admits it (n = 4, alpha[3], <= 7 blocks per member)
     int FP = 0;               // members per group
@@ -192,7 +194,8 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     p.NG = (p.S + p.GS - 1) / p.GS;
     p.tasks = p.tiles * p.S;
     p.proj_blocks = proj_blocks(p.tiles, p.S);
-    p.out_blocks = (T + out_tokens(g.n) - 1) / out_tokens(g.n);
+    p.OB = out_tokens(g.n, T);
+    p.out_blocks = (T + p.OB - 1) / p.OB;
     p.FP = kFMembers;
     p.fused_geom = g.n == 4 && g.n_alpha == 3 && !g.x_f16 && g.nblk >= kFMembers && (g.nblk + p.FP - 1) / p.FP <= kFMaxBlocks;
     p.FGS = (p.FP + 7) / 8;

@@ -104,7 +104,8 @@ static int check(int n, int D, int na, long long T)
         return fail("record local", n, D, na, T, rec_loc(p.S - 1, 63, n, g.M), recb / 4);
     if ((rec_loc(0, 1, n, g.M) * 4) % 16) return fail("record alignment", n, D, na, T, 0, 0);
     // epilogue workgroups: 8 tokens each, inside one tile
-    const int ob = out_tokens(n);
+    const int ob = p.OB;
+    if (ob != out_tokens(n, T) || (ob != 8 && ob != 16)) return fail("epilogue token count", n, D, na, T, ob, 0);
     if (kTileTokens % ob) return fail("epilogue tokens", n, D, na, T, ob, 0);
     if (p.out_blocks * ob < T || (p.out_blocks - 1) * ob >= T) return fail("epilogue grid", n, D, na, T, p.out_blocks, 0);
     // workspace sections: ordered, 256-aligned, large enough
