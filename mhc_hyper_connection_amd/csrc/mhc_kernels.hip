@@ -109,6 +109,10 @@ __device__ __forceinline__ void split3_f16(double p, uint32_t (&tb)[3])
     tb[2] = __builtin_bit_cast(uint16_t, h2);
 }
 
+// One thread per (K-step k, K-group g, phi row m): reads the row's 8 weights of that
+// octet once, splits each into its three terms and writes the three 16-byte units of
+// columns m, M + m and 2M + m; threads m < NC - 3M also zero padding column 3M + m.
+// K-steps past the data and octets past D are written as zeros.
 template <bool H>
 __global__ void __launch_bounds__(256)
 prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
@@ -116,17 +120,15 @@ prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
 {
     const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (u >= total) return;
-    const int c = (int)(u % NC);
-    const int64_t r = u / NC;
+    const int m = (int)(u % M);
+    const int64_t r = u / M;
     const int g = (int)(r % 4);
     const int64_t k = r / 4;
     const int64_t K = (int64_t)n * D;
-    u32x4 w = {0u, 0u, 0u, 0u};
+    u32x4 w[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     const int d = kBlock * (int)(k / n) + 8 * g;
-    if (c < 3 * M && k < nks && d < D) {
+    if (k < nks && d < D) {
         const int64_t k0 = (k % n) * (int64_t)D + d;
-        const int term = c / M;
-        const int m = c % M;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             double p = (double)phi[(int64_t)m * K + k0 + e];
@@ -134,10 +136,14 @@ prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
             uint32_t tb[3];
             if constexpr (H) split3_f16(p, tb);
             else split3(p, tb);
-            w[e >> 1] |= tb[term] << (16 * (e & 1));
+#pragma unroll
+            for (int t = 0; t < 3; ++t) w[t][e >> 1] |= tb[t] << (16 * (e & 1));
         }
     }
-    packed[u] = w;
+    u32x4* row = packed + r * NC;
+#pragma unroll
+    for (int t = 0; t < 3; ++t) row[t * M + m] = w[t];
+    if (m < NC - 3 * M) row[3 * M + m] = u32x4{0u, 0u, 0u, 0u};
 }
 
 // ------------------------------------------------------------------ hIn from registers
@@ -1258,7 +1264,9 @@ int forward_path(const Plan& p, bool has_pre_mix)
 int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void* packed,
                    void* stream)
 {
-    const int64_t total = (int64_t)(g.nks + kPadSteps) * 4 * g.NC;
+    // one thread per (K-step, K-group, phi row); the padding columns fit the row threads
+    if (g.NC - 3 * g.M > g.M) return (int)hipErrorInvalidValue;
+    const int64_t total = (int64_t)(g.nks + kPadSteps) * 4 * g.M;
     const unsigned blocks = (unsigned)((total + 255) / 256);
     if (g.x_f16)
         hipLaunchKernelGGL(prepack_kernel<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, phi, gamma,

@@ -33,6 +33,8 @@ static int check(int n, int D, int na, long long T)
     const Plan p = make_plan(g, T);
     const Variant v = variant_of(n, na);
     if (v.nt != g.NT) return fail("variant nt", n, D, na, T, v.nt, g.NT);
+    // the pack kernel's row threads also zero the padding columns [3M, NC)
+    if (g.NC - 3 * g.M > g.M || g.NC < 3 * g.M) return fail("pack padding columns", n, D, na, T, g.NC, g.M);
     if (p.NKS % n || p.NKS % v.sk) return fail("slice not whole blocks/stages", n, D, na, T, p.NKS, v.sk);
     if (p.NKS > kPadSteps) return fail("slice longer than the zero tail", n, D, na, T, p.NKS, kPadSteps);
     // every K-step with data is in some slice; the last slice's loads stay in the packed buffer
