@@ -543,27 +543,46 @@ epilogue_kernel(KArgs k)
     if (blockIdx.x == 0 && tid == 0) a.sync[0] = a.sync[0] + 1u;
 
     const rsrc_t rec = make_rsrc(a.rec + rec_tile(tile, k.S, N, M), (int64_t)k.S * kTileTokens * V * 4);
+    // two items per thread and pass, their loads issued together (eight in flight)
     const int items = nb * k.NG * CH;
-    for (int it = tid; it < items; it += kThreads) {
-        const int ch = it % CH, g = (it / CH) % k.NG, q = it / (CH * k.NG);
-        const int sb = group_begin(k.GS, g), se = group_end(k.S, k.GS, g);
-        double acc[4] = {0.0, 0.0, 0.0, 0.0};
-        for (int c0 = sb; c0 < se; c0 += 4) {
-            u32x4 ov[4];
+    for (int it0 = tid; it0 < items; it0 += 2 * kThreads) {
+        int ch[2], g[2], q[2], sb[2], se[2];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t off = c0 + c < se ? (uint32_t)(rec_loc(c0 + c, tl0 + q, N, M) + 4 * ch) * 4 : kOutOfRange;
-                ov[c] = __builtin_amdgcn_raw_buffer_load_b128(rec, (int)off, 0, 0);
-            }
+        for (int h = 0; h < 2; ++h) {
+            const int it = it0 + h * kThreads;
+            ch[h] = it % CH;
+            g[h] = (it / CH) % k.NG;
+            q[h] = it / (CH * k.NG);
+            sb[h] = group_begin(k.GS, g[h]);
+            se[h] = it < items ? group_end(k.S, k.GS, g[h]) : sb[h];   // no slices: nothing loaded
+        }
+        double acc[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+        for (int c0 = 0; c0 < k.GS; c0 += 4) {
+            u32x4 ov[2][4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (c0 + c < se) {
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(ov[c][e]);
+                for (int c = 0; c < 4; ++c) {
+                    const int sl = sb[h] + c0 + c;
+                    const uint32_t off = sl < se[h] ? (uint32_t)(rec_loc(sl, tl0 + q[h], N, M) + 4 * ch[h]) * 4
+                                                    : kOutOfRange;
+                    ov[h][c] = __builtin_amdgcn_raw_buffer_load_b128(rec, (int)off, 0, 0);
                 }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (sb[h] + c0 + c < se[h]) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[h][e] += (double)__uint_as_float(ov[h][c][e]);
+                    }
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) gs[(q * V + 4 * ch + e) * 8 + g] = acc[e];
+        for (int h = 0; h < 2; ++h)
+            if (it0 + h * kThreads < items) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gs[(q[h] * V + 4 * ch[h] + e) * 8 + g[h]] = acc[h][e];
+            }
     }
     __syncthreads();
     for (int it = tid; it < nb * V; it += kThreads) {
