@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import compare, gpu_forward, run_oracle, summary
+from gpu_helpers import compare, gpu_forward, run_oracle, summary, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -126,3 +126,27 @@ def test_deterministic_and_flag_invariant():
     packed = gpu_forward(inp, packed=True)
     for k in runs[0]:
         assert np.array_equal(packed[k].view(np.uint8), runs[0][k].view(np.uint8)), k
+
+
+def test_timed_forward_with_unrecorded_boundaries():
+    # mhc_pre_forward_timed skips NULL event entries: the outputs equal the untimed call's
+    # bit for bit, and the recorded pairs give positive durations
+    import mhc_hyper_connection_amd as mhc
+    import torch
+    print("[case] timed forward with NULL events", file=sys.stderr, flush=True)
+    inp = synth.custom(300, 4, 1024, need_backward=True, seed=96)
+    plain = gpu_forward(inp)
+    dev = torch.device("cuda", 0)
+    wl = inp.wl
+    r = mhc.PreForward(wl.T, wl.n, wl.D, wl.n_alpha, need_backward=True, device=dev)
+    x, phi, alpha, bias = (to_dev(a, dev) for a in (inp.x, inp.phi, inp.alpha, inp.bias))
+    ev = [torch.cuda.Event(enable_timing=True) if i in (0, 2, 4) else None for i in range(mhc.FORWARD_EVENTS)]
+    for e in ev:
+        if e is not None:
+            e.record()
+    torch.cuda.synchronize(dev)
+    out = r(x, phi, alpha, bias, events=ev)
+    torch.cuda.synchronize(dev)
+    assert ev[0].elapsed_time(ev[2]) > 0 and ev[2].elapsed_time(ev[4]) > 0
+    for k, v in out.items():
+        assert np.array_equal(to_host(v).view(np.uint8), plain[k].view(np.uint8)), k
