@@ -7,6 +7,7 @@ compared element by element, and properties that hold at any size are checked on
 every token: gate ranges, Sinkhorn column sums after the last (column) step, and the
 step relation normOut[k] = normOut[k-1] / sumOut[k] between the emitted planes.
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -23,7 +24,11 @@ _CACHE = {}
 def _inputs(name):
     if name not in _CACHE:
         _CACHE.clear()
-        _CACHE[name] = synth.generate(synth.WORKLOADS[name])
+        if name.endswith("_f16"):   # the same workload with x and hIn in binary16
+            wl = dataclasses.replace(synth.WORKLOADS[name[:-4]], name=name, x_f16=True)
+        else:
+            wl = synth.WORKLOADS[name]
+        _CACHE[name] = synth.generate(wl)
     return _CACHE[name]
 
 
@@ -47,7 +52,7 @@ def test_workload_full_compare(name):
     _log(name, rep)
 
 
-@pytest.mark.parametrize("name", ["large_prefill_bwd", "wide_premix"])
+@pytest.mark.parametrize("name", ["large_prefill_bwd", "wide_premix", "large_prefill_bwd_f16"])
 def test_workload_sampled_and_properties(name):
     inp = _inputs(name)
     wl = inp.wl
