@@ -89,6 +89,10 @@ def _bind(lib):
         lib.oracle_mhc_post.restype = ctypes.c_int
         lib.oracle_mhc_post.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp,
                                         dp, dp, dp]
+    if hasattr(lib, "oracle_mhc_post_fmt"):
+        lib.oracle_mhc_post_fmt.restype = ctypes.c_int
+        lib.oracle_mhc_post_fmt.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, dp, dp, dp, dp,
+                                            dp, dp, dp, ctypes.c_int]
     if hasattr(lib, "oracle_pre_sinkhorn"):
         lib.oracle_inv_rms.restype = ctypes.c_int
         lib.oracle_inv_rms.argtypes = [ctypes.POINTER(_Cfg), dp, dp, ctypes.c_int]
@@ -372,7 +376,7 @@ class PostResult:
     out_abs: np.ndarray    # float64 [T, n, D], sum of |terms|
 
 
-def post(x_bits, residual_bits, post_w, comb, lib=None) -> PostResult:
+def post(x_bits, residual_bits, post_w, comb, lib=None, x_f16=False) -> PostResult:
     """hc_post: out[t, i, d] = post[t, i] x[t, d] + sum_j comb[t, i, j] residual[t, j, d]
     (x [T, D] and residual [T, n, D] as bf16 bits, post [T, n], comb [T, n, n] float32)."""
     lib = lib or _load()
@@ -385,8 +389,12 @@ def post(x_bits, residual_bits, post_w, comb, lib=None) -> PostResult:
     ob = np.zeros((T, n, D), dtype=np.uint16)
     o = np.zeros((T, n, D), dtype=np.float64)
     oa = np.zeros((T, n, D), dtype=np.float64)
-    st = lib.oracle_mhc_post(T, n, D, _ptr(x_bits), _ptr(residual_bits), _ptr(post_w), _ptr(comb),
-                             _ptr(ob), _ptr(o), _ptr(oa))
+    if x_f16:   # binary16 x, residual and out
+        st = lib.oracle_mhc_post_fmt(T, n, D, _ptr(x_bits), _ptr(residual_bits), _ptr(post_w), _ptr(comb),
+                                     _ptr(ob), _ptr(o), _ptr(oa), 1)
+    else:
+        st = lib.oracle_mhc_post(T, n, D, _ptr(x_bits), _ptr(residual_bits), _ptr(post_w), _ptr(comb),
+                                 _ptr(ob), _ptr(o), _ptr(oa))
     if st != 0:
         raise ValueError(f"oracle_mhc_post status {st}")
     return PostResult(ob, o, oa)

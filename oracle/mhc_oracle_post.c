@@ -18,10 +18,14 @@
 
 double oracle_bf16_to_double(uint16_t bits);
 uint16_t oracle_bf16_from_double(double v);
+double oracle_f16_to_double(uint16_t bits);
+uint16_t oracle_f16_from_double(double v);
 
-int oracle_mhc_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* residual,
-                    const float* post, const float* comb, uint16_t* out_bf16, double* out,
-                    double* out_abs)
+/* x_f16: x, residual and out in binary16 instead of bf16 (the 16-bit format of the
+ * pre-mapping's x and hIn); the arithmetic is unchanged. */
+int oracle_mhc_post_fmt(int64_t T, int n, int D, const uint16_t* x, const uint16_t* residual,
+                        const float* post, const float* comb, uint16_t* out_bf16, double* out,
+                        double* out_abs, int x_f16)
 {
     if (T < 0 || n < 1 || D < 1) return 1;
 #pragma omp parallel for schedule(static)
@@ -29,21 +33,29 @@ int oracle_mhc_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* 
         for (int i = 0; i < n; ++i) {
             const double p = (double)post[t * n + i];
             for (int d = 0; d < D; ++d) {
-                const double xv = oracle_bf16_to_double(x[t * D + d]);
+                const double xv = x_f16 ? oracle_f16_to_double(x[t * D + d]) : oracle_bf16_to_double(x[t * D + d]);
                 double acc = p * xv;
                 double mag = fabs(p * xv);
                 for (int j = 0; j < n; ++j) {
                     const double c = (double)comb[(t * n + i) * n + j];
-                    const double r = oracle_bf16_to_double(residual[(t * n + j) * (int64_t)D + d]);
+                    const uint16_t rb = residual[(t * n + j) * (int64_t)D + d];
+                    const double r = x_f16 ? oracle_f16_to_double(rb) : oracle_bf16_to_double(rb);
                     acc += c * r;
                     mag += fabs(c * r);
                 }
                 const int64_t o = (t * n + i) * (int64_t)D + d;
                 if (out) out[o] = acc;
                 if (out_abs) out_abs[o] = mag;
-                if (out_bf16) out_bf16[o] = oracle_bf16_from_double(acc);
+                if (out_bf16) out_bf16[o] = x_f16 ? oracle_f16_from_double(acc) : oracle_bf16_from_double(acc);
             }
         }
     }
     return 0;
+}
+
+int oracle_mhc_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* residual,
+                    const float* post, const float* comb, uint16_t* out_bf16, double* out,
+                    double* out_abs)
+{
+    return oracle_mhc_post_fmt(T, n, D, x, residual, post, comb, out_bf16, out, out_abs, 0);
 }

@@ -83,7 +83,28 @@ def pin_einsum(lib):
     assert np.all(r.out_abs >= np.abs(r.out) - 1e-12)
 
 
-PINS = [pin_permutation, pin_post_only, pin_einsum]
+def pin_f16_permutation_and_einsum(lib=None):
+    # binary16 storage: a permutation comb with post = 0 returns the picked residual rows
+    # bit for bit, and the unrounded output equals NumPy's float64 einsum, rounded to fp16
+    T, n, D = 3, 4, 24
+    rng = np.random.default_rng(77)
+    x = (rng.standard_normal((T, D)) * 2).astype(np.float16).view(np.uint16)
+    res = (rng.standard_normal((T, n, D)) * 2).astype(np.float16).view(np.uint16)
+    perm = [1, 2, 3, 0]
+    comb = np.zeros((T, n, n), np.float32)
+    comb[:, np.arange(n), perm] = 1.0
+    r = oracle.post(x, res, np.zeros((T, n), np.float32), comb, lib=lib, x_f16=True)
+    assert np.array_equal(r.out_bf16, res[:, perm, :]), "fp16 permutation"
+    post_w = rng.uniform(0, 2, (T, n)).astype(np.float32)
+    comb = rng.uniform(0.05, 0.45, (T, n, n)).astype(np.float32)
+    r = oracle.post(x, res, post_w, comb, lib=lib, x_f16=True)
+    xf, rf = x.view(np.float16).astype(np.float64), res.view(np.float16).astype(np.float64)
+    want = post_w[:, :, None] * xf[:, None, :] + np.einsum("tij,tjd->tid", comb.astype(np.float64), rf)
+    assert np.allclose(r.out, want, rtol=1e-12, atol=0), "fp16 einsum"
+    assert np.array_equal(r.out_bf16, want.astype(np.float16).view(np.uint16)), "fp16 rounding"
+
+
+PINS = [pin_permutation, pin_post_only, pin_einsum, pin_f16_permutation_and_einsum]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -97,6 +118,8 @@ MUTANTS = {
     "post_term_dropped": ("double acc = p * xv;", "double acc = 0.0;"),
     "post_from_next_stream": ("const double p = (double)post[t * n + i];", "const double p = (double)post[t * n + (i + 1) % n];"),
     "residual_term_dropped": ("acc += c * r;", "(void)r;"),
+    "f16_residual_read_as_bf16": ("const double r = x_f16 ? oracle_f16_to_double(rb) : oracle_bf16_to_double(rb);",
+                                  "const double r = oracle_bf16_to_double(rb);"),
 }
 
 
