@@ -67,7 +67,8 @@ typedef int32_t mhc_status;
  *                  BF16 and FLOAT16). With fp16 the weights are packed as three fp16 terms
  *                  scaled by 1, 2^11, 2^22 (phi * gamma must stay within 65504 in
  *                  magnitude), the four-kernel path runs, and the standalone stages read
- *                  and write fp16 too. hc_post and the backward take bf16 only. */
+ *                  and write fp16 too. hc_post takes either format (its own x_dtype);
+ *                  the backward takes bf16 only. */
 typedef struct mhc_pre_params {
     int64_t T;
     int32_t n;
@@ -385,6 +386,8 @@ typedef struct mhc_post_params {
     int64_t T;
     int32_t n;
     int32_t D;
+    int32_t x_dtype;    /* MHC_DTYPE_BF16 or MHC_DTYPE_F16: the format of x, residual and out */
+    int32_t reserved;   /* must be 0 */
 } mhc_post_params;
 
 typedef struct mhc_post_tensors {

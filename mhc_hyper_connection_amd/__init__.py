@@ -308,14 +308,16 @@ def mhc_post(x, residual, post, comb, *, out=None):
     torch = _torch()
     T, n, D = residual.shape
     dev = residual.device
-    _check(x, "x", torch.bfloat16, (T, D), dev)
-    _check(residual, "residual", torch.bfloat16, (T, n, D), dev)
+    xdt = torch.float16 if residual.dtype == torch.float16 else torch.bfloat16
+    _check(x, "x", xdt, (T, D), dev)
+    _check(residual, "residual", xdt, (T, n, D), dev)
     _check(post, "post", torch.float32, (T, n), dev)
     _check(comb, "comb", torch.float32, (T, n, n), dev)
     if out is None:
-        out = torch.empty((T, n, D), dtype=torch.bfloat16, device=dev)
-    _check(out, "out", torch.bfloat16, (T, n, D), dev)
-    st = raw_post(T, n, D, _ptr(x), _ptr(residual), _ptr(post), _ptr(comb), _ptr(out), _stream(dev))
+        out = torch.empty((T, n, D), dtype=xdt, device=dev)
+    _check(out, "out", xdt, (T, n, D), dev)
+    st = raw_post(T, n, D, _ptr(x), _ptr(residual), _ptr(post), _ptr(comb), _ptr(out), _stream(dev),
+                  xdt == torch.float16)
     if st != MHC_OK:
         raise MhcError(st, "mhc_post")
     return out

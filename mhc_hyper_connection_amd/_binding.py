@@ -68,7 +68,8 @@ _lib = None
 
 
 class PostParams(ctypes.Structure):
-    _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("D", ctypes.c_int32)]
+    _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("x_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class PostTensors(ctypes.Structure):
@@ -206,8 +207,8 @@ def raw_backward(params: BwdParams, ptrs: dict, ws_ptr, ws_bytes, stream) -> int
     return int(load().mhc_pre_backward(ctypes.byref(params), ctypes.byref(t), ws_ptr, ws_bytes, stream))
 
 
-def raw_post(T, n, D, x_ptr, residual_ptr, post_ptr, comb_ptr, out_ptr, stream) -> int:
-    p = PostParams(int(T), int(n), int(D))
+def raw_post(T, n, D, x_ptr, residual_ptr, post_ptr, comb_ptr, out_ptr, stream, x_f16=False) -> int:
+    p = PostParams(int(T), int(n), int(D), 1 if x_f16 else 0, 0)
     t = PostTensors(x_ptr, residual_ptr, post_ptr, comb_ptr, out_ptr)
     return int(load().mhc_post(ctypes.byref(p), ctypes.byref(t), stream))
 

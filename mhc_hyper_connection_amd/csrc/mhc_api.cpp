@@ -292,13 +292,15 @@ mhc_status mhc_post(const mhc_post_params* params, const mhc_post_tensors* t, vo
     if (!params || !t) return MHC_ERR_NULLPTR;
     if (params->T < 0 || (params->n != 4 && params->n != 6 && params->n != 8)) return MHC_ERR_PARAM_INVALID;
     if (params->D < 8 || params->D % 8 != 0 || params->D > mhc::kMaxD) return MHC_ERR_PARAM_INVALID;
+    if (params->x_dtype != MHC_DTYPE_BF16 && params->x_dtype != MHC_DTYPE_F16) return MHC_ERR_PARAM_INVALID;
+    if (params->reserved != 0) return MHC_ERR_PARAM_INVALID;
     if (params->T == 0) return MHC_OK;
     if (!t->x || !t->residual || !t->post || !t->comb || !t->out) return MHC_ERR_NULLPTR;
     if (!aligned(t->x, 16) || !aligned(t->residual, 16) || !aligned(t->out, 16) || !aligned(t->post, 4) ||
         !aligned(t->comb, 4))
         return MHC_ERR_PARAM_INVALID;
     return mhc::launch_post(params->T, params->n, params->D, t->x, t->residual, t->post, t->comb, t->out,
-                            stream) == 0
+                            params->x_dtype == MHC_DTYPE_F16, stream) == 0
                ? MHC_OK
                : MHC_ERR_RUNTIME;
 }

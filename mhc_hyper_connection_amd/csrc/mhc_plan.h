@@ -324,6 +324,6 @@ int launch_pre_sinkhorn(int64_t T, int n, int D, int n_alpha, int x_f16, const F
                         const float* h_mix, const float* inv_rms, void* stream);
 // hc_post (mhc_post.hip): out = post x + comb residual per token; 0 or the HIP error code.
 int launch_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* residual, const float* post,
-                const float* comb, uint16_t* out, void* stream);
+                const float* comb, uint16_t* out, int x_f16, void* stream);
 
 }  // namespace mhc

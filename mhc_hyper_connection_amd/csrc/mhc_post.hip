@@ -9,7 +9,7 @@
 // the n residual streams (16-byte loads, consecutive threads on consecutive octets), the
 // token's post and comb (shared by the token's threads, cached), and writes the octet of
 // each of the n output streams. fp32 fused multiply-adds in the order post term, then
-// j = 0 .. n-1; one rounding to bf16. Memory-bound: per token 2D + 2nD bytes read
+// j = 0 .. n-1; one rounding to bf16 (fp16 when the tensors are fp16). Memory-bound: per token 2D + 2nD bytes read
 // (+ 4n + 4n^2), 2nD written.
 #include <hip/hip_runtime.h>
 
@@ -21,7 +21,7 @@
 namespace mhc {
 namespace {
 
-template <int N>
+template <int N, bool H>
 __global__ void __launch_bounds__(256)
 post_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ residual,
             const float* __restrict__ post, const float* __restrict__ comb,
@@ -46,19 +46,19 @@ post_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ residua
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            acc[2 * e] = p * bf16_lo(xv[e]);
-            acc[2 * e + 1] = p * bf16_hi(xv[e]);
+            acc[2 * e] = p * x16_lo<H>(xv[e]);
+            acc[2 * e + 1] = p * x16_hi<H>(xv[e]);
         }
 #pragma unroll
         for (int j = 0; j < N; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = fmaf(c[j], bf16_lo(rv[j][e]), acc[2 * e]);
-                acc[2 * e + 1] = fmaf(c[j], bf16_hi(rv[j][e]), acc[2 * e + 1]);
+                acc[2 * e] = fmaf(c[j], x16_lo<H>(rv[j][e]), acc[2 * e]);
+                acc[2 * e + 1] = fmaf(c[j], x16_hi<H>(rv[j][e]), acc[2 * e + 1]);
             }
         u32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+        for (int e = 0; e < 4; ++e) o[e] = pack_x16<H>(acc[2 * e], acc[2 * e + 1]);
         // the output is not read again here: stream it past the caches
         __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + (t * N + i) * (int64_t)D + d8 * 8));
     }
@@ -67,16 +67,21 @@ post_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ residua
 }  // namespace
 
 int launch_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* residual, const float* post,
-                const float* comb, uint16_t* out, void* stream)
+                const float* comb, uint16_t* out, int x_f16, void* stream)
 {
     if (T <= 0) return 0;
     const int64_t items = T * (int64_t)(D / 8);
     const dim3 grid((unsigned)((items + 255) / 256));
     hipStream_t st = (hipStream_t)stream;
-    if (n == 4) hipLaunchKernelGGL(post_kernel<4>, grid, dim3(256), 0, st, x, residual, post, comb, out, T, D);
-    else if (n == 6) hipLaunchKernelGGL(post_kernel<6>, grid, dim3(256), 0, st, x, residual, post, comb, out, T, D);
-    else if (n == 8) hipLaunchKernelGGL(post_kernel<8>, grid, dim3(256), 0, st, x, residual, post, comb, out, T, D);
+#define MHC_POST(NV, HV) hipLaunchKernelGGL((post_kernel<NV, HV>), grid, dim3(256), 0, st, x, residual, post, comb, out, T, D)
+    if (n == 4 && !x_f16) MHC_POST(4, false);
+    else if (n == 6 && !x_f16) MHC_POST(6, false);
+    else if (n == 8 && !x_f16) MHC_POST(8, false);
+    else if (n == 4) MHC_POST(4, true);
+    else if (n == 6) MHC_POST(6, true);
+    else if (n == 8) MHC_POST(8, true);
     else return (int)hipErrorInvalidValue;
+#undef MHC_POST
     return (int)hipGetLastError();
 }
 

@@ -7,8 +7,8 @@ import pytest
 from mhc_hyper_connection_amd import _binding as B
 
 
-def call(T, n, D, ptrs=(16, 16, 16, 16, 16)):
-    p = B.PostParams(T, n, D)
+def call(T, n, D, ptrs=(16, 16, 16, 16, 16), x_dtype=0, reserved=0):
+    p = B.PostParams(T, n, D, x_dtype, reserved)
     t = B.PostTensors(*[ctypes.c_void_p(v) if v else None for v in ptrs])
     return B.load().mhc_post(ctypes.byref(p), ctypes.byref(t), None)
 
@@ -25,3 +25,9 @@ def test_null_and_alignment():
     assert call(4, 4, 64, (16, 0, 16, 16, 16)) == B.MHC_ERR_NULLPTR
     assert call(4, 4, 64, (16, 16, 16, 16, 8)) == B.MHC_ERR_PARAM_INVALID    # out not 16-byte aligned
     assert call(4, 4, 64, (16, 16, 18, 16, 16)) == B.MHC_ERR_PARAM_INVALID   # post not 4-byte aligned
+
+
+def test_format_fields():
+    assert call(4, 4, 64, x_dtype=2) == B.MHC_ERR_PARAM_INVALID
+    assert call(4, 4, 64, reserved=1) == B.MHC_ERR_PARAM_INVALID
+    assert call(0, 4, 64, x_dtype=1) == B.MHC_OK

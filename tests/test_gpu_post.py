@@ -93,3 +93,27 @@ def test_post_large_workload_shape():
     rng = np.random.default_rng(3)
     tok = np.unique(np.concatenate([[0, 1, 8191, 16383], rng.integers(0, 16384, 28)]))
     check(gpu_post(pi), pi, tokens=tok)
+
+
+@pytest.mark.parametrize("T,n,D", [(33, 4, 520), (17, 8, 64), (9, 6, 7168)])
+def test_post_parity_f16(T, n, D):
+    # binary16 x, residual and out
+    import mhc_hyper_connection_amd as mhc
+    import torch
+    print(f"[case] post f16 T={T} n={n} D={D}", file=sys.stderr, flush=True)
+    rng = np.random.default_rng(100 + T)
+    x = rng.standard_normal((T, D), dtype=np.float32).astype(np.float16).view(np.uint16)
+    res = rng.standard_normal((T, n, D), dtype=np.float32).astype(np.float16).view(np.uint16)
+    post = rng.uniform(0.0, 2.0, (T, n)).astype(np.float32)
+    comb = rng.uniform(0.05, 0.45, (T, n, n)).astype(np.float32)
+    dev = device()
+    out = mhc.mhc_post(to_dev(x, dev, True), to_dev(res, dev, True), to_dev(post, dev), to_dev(comb, dev))
+    torch.cuda.synchronize(dev)
+    assert out.dtype == torch.float16
+    g = to_host(out)
+    ref = oracle.post(x, res, post, comb, x_f16=True)
+    dist = np.abs(bf16_ordered(g) - bf16_ordered(ref.out_bf16))
+    cancel = np.abs(g.view(np.float16).astype(np.float64) - ref.out) <= 2.0 ** -20 * ref.out_abs
+    bad = ~((dist <= 1) | cancel)
+    print(f"[parity-post-f16] fail={int(bad.sum())}/{bad.size} max_ulp={int(dist.max())}", file=sys.stderr, flush=True)
+    assert not bad.any()
