@@ -377,8 +377,10 @@ class PostResult:
 
 
 def post(x_bits, residual_bits, post_w, comb, lib=None, x_f16=False) -> PostResult:
-    """hc_post: out[t, i, d] = post[t, i] x[t, d] + sum_j comb[t, i, j] residual[t, j, d]
-    (x [T, D] and residual [T, n, D] as bf16 bits, post [T, n], comb [T, n, n] float32)."""
+    """hc_post: out[t, j, d] = post[t, j] x[t, d] + sum_i comb[t, i, j] residual[t, i, d]
+    (x [T, D] and residual [T, n, D] as bf16 bits, post [T, n], comb [T, n, n] float32):
+    the HcPre guide's printed expression on its 4-D comb_frag, where the summed index is
+    comb's first one."""
     lib = lib or _load()
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     residual_bits = np.ascontiguousarray(residual_bits, dtype=np.uint16)
