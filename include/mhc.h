@@ -369,11 +369,11 @@ mhc_status mhc_pre_sinkhorn(const mhc_pre_params* params, const mhc_pre_sinkhorn
  * The mHC post-mapping (HcPre guide, mhpn.cn/news/2282827, section "mHC 架构与 HcPre 的
  * 定位"): the layer output x is expanded back into the n streams by post (the forward's
  * hPost) and added to the streams fused across streams by comb (the forward's hRes):
- *     out[t][i][d] = post[t][i] x[t][d] + sum_j comb[t][i][j] residual[t][j][d]
- * The expression the guide prints sums comb over its second index against a residual
- * indexed by comb's first index, which fuses nothing although the text says the streams
- * are fused; the sum runs over the residual's stream here. fp32 fused multiply-adds
- * (post term first, then j in order), one rounding to bf16.
+ *     out[t][j][d] = post[t][j] x[t][d] + sum_i comb[t][i][j] residual[t][i][d]
+ * This is the guide's printed broadcast expression evaluated on the [b, s, n, n] comb_frag
+ * its section "返回值说明" documents: the sum runs over comb's first index, so output
+ * stream j takes column j of comb (comb transposed times the residual streams). fp32 fused
+ * multiply-adds (post term first, then i in order), one rounding to bf16.
  *   T >= 0; n: 4, 6 or 8; D: a multiple of 8 in [8, 16384]
  *   x        bf16 [T, D]       16-byte aligned    (the attention / MLP output)
  *   residual bf16 [T, n, D]    16-byte aligned    (the n streams)

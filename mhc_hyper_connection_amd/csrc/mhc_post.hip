@@ -1,16 +1,16 @@
 // mhc_post.hip -- gfx950 kernel of hc_post, the mHC post-mapping (HcPre guide,
 // mhpn.cn/news/2282827, section "mHC 架构与 HcPre 的定位": the layer output expanded into
-// the n streams by post, added to the streams fused across streams by comb):
-//     out[t][i][d] = post[t][i] x[t][d] + sum_j comb[t][i][j] residual[t][j][d]
-// (the guide's printed expression mixes nothing; the summed index of comb is the
-// residual's stream, the usual res-mapping product).
+// the n streams by post, added to the streams fused across streams by comb). The guide's
+// broadcast expression, on the [b, s, n, n] comb_frag its section "返回值说明" documents,
+// sums over comb's first index, so output stream j takes column j of comb:
+//     out[t][j][d] = post[t][j] x[t][d] + sum_i comb[t][i][j] residual[t][i][d]
 //
 // One thread per octet (8 positions) of one token: it reads the octet of x and of each of
 // the n residual streams (16-byte loads, consecutive threads on consecutive octets), the
 // token's post and comb (shared by the token's threads, cached), and writes the octet of
 // each of the n output streams. fp32 fused multiply-adds in the order post term, then
-// j = 0 .. n-1; one rounding to bf16 (fp16 when the tensors are fp16). Memory-bound: per token 2D + 2nD bytes read
-// (+ 4n + 4n^2), 2nD written.
+// i = 0 .. n-1; one rounding to bf16 (fp16 when the tensors are fp16). Memory-bound: per
+// token 2D + 2nD bytes read (+ 4n + 4n^2), 2nD written.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -35,14 +35,14 @@ post_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ residua
     const u32x4 xv = *reinterpret_cast<const u32x4*>(x + t * (int64_t)D + d8 * 8);
     u32x4 rv[N];
 #pragma unroll
-    for (int j = 0; j < N; ++j)
-        rv[j] = *reinterpret_cast<const u32x4*>(residual + (t * N + j) * (int64_t)D + d8 * 8);
+    for (int i = 0; i < N; ++i)
+        rv[i] = *reinterpret_cast<const u32x4*>(residual + (t * N + i) * (int64_t)D + d8 * 8);
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const float p = post[t * N + i];
-        float c[N];
+    for (int j = 0; j < N; ++j) {   // output stream
+        const float p = post[t * N + j];
+        float c[N];                 // column j of comb
 #pragma unroll
-        for (int j = 0; j < N; ++j) c[j] = comb[(t * N + i) * N + j];
+        for (int i = 0; i < N; ++i) c[i] = comb[(t * N + i) * N + j];
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -50,17 +50,17 @@ post_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ residua
             acc[2 * e + 1] = p * x16_hi<H>(xv[e]);
         }
 #pragma unroll
-        for (int j = 0; j < N; ++j)
+        for (int i = 0; i < N; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = fmaf(c[j], x16_lo<H>(rv[j][e]), acc[2 * e]);
-                acc[2 * e + 1] = fmaf(c[j], x16_hi<H>(rv[j][e]), acc[2 * e + 1]);
+                acc[2 * e] = fmaf(c[i], x16_lo<H>(rv[i][e]), acc[2 * e]);
+                acc[2 * e + 1] = fmaf(c[i], x16_hi<H>(rv[i][e]), acc[2 * e + 1]);
             }
         u32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = pack_x16<H>(acc[2 * e], acc[2 * e + 1]);
         // the output is not read again here: stream it past the caches
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + (t * N + i) * (int64_t)D + d8 * 8));
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + (t * N + j) * (int64_t)D + d8 * 8));
     }
 }
 

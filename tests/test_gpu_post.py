@@ -58,8 +58,8 @@ def test_post_parity(name, T, n, D, seed):
 
 
 def test_post_permutation_is_exact():
-    # a non-symmetric permutation as comb and post = 0: every output row is exactly the
-    # residual row the permutation picks
+    # a non-symmetric permutation as comb and post = 0: output stream perm(i) is exactly
+    # residual stream i (the sum runs over comb's first index)
     print("[case] post permutation", file=sys.stderr, flush=True)
     pi = synth.post_inputs(40, 4, 256, seed=7)
     pi.post[:] = 0.0
@@ -68,7 +68,7 @@ def test_post_permutation_is_exact():
         pi.comb[:, i, (i + 1) % 4] = 1.0
     g = gpu_post(pi)
     for i in range(4):
-        assert np.array_equal(g[:, i, :], pi.residual[:, (i + 1) % 4, :])
+        assert np.array_equal(g[:, (i + 1) % 4, :], pi.residual[:, i, :])
 
 
 def test_post_empty_and_reproducible():
@@ -87,12 +87,12 @@ def test_post_empty_and_reproducible():
 
 def test_post_large_workload_shape():
     # the large prefill shape (T = 16384, n = 4, D = 7168), as the benchmark runs it:
-    # sampled tokens against the oracle
+    # every token against the oracle
     print("[case] post large T=16384 D=7168", file=sys.stderr, flush=True)
     pi = synth.post_inputs(16384, 4, 7168, seed=1004)
-    rng = np.random.default_rng(3)
-    tok = np.unique(np.concatenate([[0, 1, 8191, 16383], rng.integers(0, 16384, 28)]))
-    check(gpu_post(pi), pi, tokens=tok)
+    g = gpu_post(pi)
+    for t0 in range(0, pi.T, 2048):   # every token, in chunks that bound host memory
+        check(g, pi, tokens=np.arange(t0, min(pi.T, t0 + 2048)))
 
 
 @pytest.mark.parametrize("T,n,D", [(33, 4, 520), (17, 8, 64), (9, 6, 7168)])
