@@ -89,12 +89,19 @@ def _bound_check(name, g, r, a, rtol, atab, rep):
 def compare(g, o, bi, tokens=None):
     tok = np.arange(bi.T) if tokens is None else np.asarray(tokens)
     rep = {}
-    gx = g["grad_x"][tok]
-    dist = np.abs(bf16_ordered(gx) - bf16_ordered(o.grad_x_bf16))
-    cancel = np.abs(bf16_bits_to_f32(gx).astype(np.float64) - o.grad_x) <= 2.0 ** -18 * o.grad_x_abs
-    ok = (dist <= 1) | cancel
-    rep["grad_x"] = dict(n=int(dist.size), fail=int((~ok).sum()), max_ulp=int(dist.max()) if dist.size else 0,
-                         cancel_branch=int(((dist > 1) & cancel).sum()))
+    gx_all = g["grad_x"][tok]
+    nel = fails = max_ulp = cancel_used = 0
+    for r0 in range(0, len(tok), 1024):   # rows in chunks: bounded temporaries at the large shape
+        sl = slice(r0, min(len(tok), r0 + 1024))
+        gx = gx_all[sl]
+        dist = np.abs(bf16_ordered(gx) - bf16_ordered(o.grad_x_bf16[sl]))
+        cancel = np.abs(bf16_bits_to_f32(gx).astype(np.float64) - o.grad_x[sl]) <= 2.0 ** -18 * o.grad_x_abs[sl]
+        ok = (dist <= 1) | cancel
+        nel += int(dist.size)
+        fails += int((~ok).sum())
+        max_ulp = max(max_ulp, int(dist.max()) if dist.size else 0)
+        cancel_used += int(((dist > 1) & cancel).sum())
+    rep["grad_x"] = dict(n=nel, fail=fails, max_ulp=max_ulp, cancel_branch=cancel_used)
     _bound_check("grad_phi", g["grad_phi"], o.grad_phi, o.grad_phi_abs, 2e-4, 2.0 ** -14, rep)
     _bound_check("grad_alpha", g["grad_alpha"], o.grad_alpha, o.grad_alpha_abs, 1e-6, 2.0 ** -30, rep)
     _bound_check("grad_bias", g["grad_bias"], o.grad_bias, o.grad_bias_abs, 1e-6, 2.0 ** -30, rep)
@@ -147,22 +154,19 @@ def test_backward_bitwise_reproducible():
 
 
 def test_backward_mid_workload_shape():
-    # the mid prefill shape (T = 4096, n = 4, D = 4096, gamma): every cross-token
-    # gradient in full, gradX on sampled rows (first, last, tile edges, random)
+    # the mid prefill shape (T = 4096, n = 4, D = 4096, gamma): every gradient, every row
     print("[case] backward mid T=4096 D=4096 gamma", file=sys.stderr, flush=True)
     bi = synth.backward_inputs(4096, 4, 4096, gamma=True, seed=14)
-    rng = np.random.default_rng(0)
-    tok = np.unique(np.concatenate([[0, 63, 64, 2047, 2048, 4095], rng.integers(0, 4096, 26)]))
-    compare(gpu_backward(bi), run_oracle(bi, tokens=tok), bi, tokens=tok)
+    compare(gpu_backward(bi), run_oracle(bi), bi)
 
 
 def test_backward_large_workload_shape():
-    # the large prefill shape (T = 16384, n = 4, D = 7168), as the benchmark runs it
+    # the large prefill shape (T = 16384, n = 4, D = 7168), as the benchmark runs it:
+    # every gradient in full, every row of gradX
     print("[case] backward large T=16384 D=7168", file=sys.stderr, flush=True)
     bi = synth.backward_inputs(16384, 4, 7168, seed=15)
-    rng = np.random.default_rng(1)
-    tok = np.unique(np.concatenate([[0, 1, 63, 64, 8191, 16383], rng.integers(0, 16384, 26)]))
-    compare(gpu_backward(bi), run_oracle(bi, tokens=tok), bi, tokens=tok)
+    rep = compare(gpu_backward(bi), run_oracle(bi), bi)
+    assert rep["grad_x"]["n"] == 16384 * 4 * 7168
 
 
 SINKHORN_CASES = [
@@ -187,6 +191,5 @@ def test_sinkhorn_backward_large_workload_shape():
     # the large prefill shape with its 20 Sinkhorn iterations: the training step's backward
     print("[case] sinkhorn backward large T=16384 D=7168 it=20", file=sys.stderr, flush=True)
     bi = sinkhorn_inputs(16384, 4, 7168, 20, seed=47)
-    rng = np.random.default_rng(2)
-    tok = np.unique(np.concatenate([[0, 1, 63, 64, 8191, 16383], rng.integers(0, 16384, 26)]))
-    compare(gpu_backward(bi), run_oracle(bi, tokens=tok), bi, tokens=tok)
+    rep = compare(gpu_backward(bi), run_oracle(bi), bi)
+    assert rep["grad_x"]["n"] == 16384 * 4 * 7168

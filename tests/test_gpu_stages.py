@@ -46,17 +46,16 @@ def test_inv_rms_parity(name, T, n, D):
     assert rel <= 2.0 ** -23
 
 
-def test_inv_rms_large_sampled():
+def test_inv_rms_large_every_token():
     # a long-prefill slice at the widest hidden size: 8192 tokens of n = 4, D = 7168,
-    # the oracle on 64 sampled tokens (first, last and a spread between)
+    # every token against the oracle
     T, n, D = 8192, 4, 7168
-    print(f"[case] inv_rms T{T}_n{n}_D{D} sampled", file=sys.stderr, flush=True)
+    print(f"[case] inv_rms T{T}_n{n}_D{D} every token", file=sys.stderr, flush=True)
     si = synth.stage_inputs(T, n, D, seed=47)
     g = gpu_inv_rms(si.x)
-    tok = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(3).integers(0, T, 62)]))
-    r = oracle.inv_rms(si.x[tok])
-    rel = float(np.max(np.abs(g[tok].astype(np.float64) - r) / r))
-    print(f"[parity-inv-rms] sampled max_rel={rel:.2e}", file=sys.stderr, flush=True)
+    r = oracle.inv_rms(si.x)
+    rel = float(np.max(np.abs(g.astype(np.float64) - r) / r))
+    print(f"[parity-inv-rms] every token max_rel={rel:.2e}", file=sys.stderr, flush=True)
     assert rel <= 2.0 ** -23
 
 
