@@ -8,17 +8,23 @@ phi (pack, projection, per-token epilogue, hIn kernels). Inputs are seeded synth
 tensors (synth), resident in HBM before timing. Prints one JSON line.
 
 Measured in this run:
-  value        tokens/s over exactly K steps, wall clock between two device syncs;
-  roofline     of the dominant kernel (the one with the largest average duration),
-               its duration from HIP events that the library records on the launch
-               stream around each of its kernels (mhc_pre_forward_timed);
+  value        tokens/s over exactly K back-to-back steps, wall clock between two device
+               syncs (inputs resident in HBM);
+  roofline     of the dominant kernel (the one with the largest average duration), its
+               duration from HIP events that the library records on the launch stream around
+               each of its kernels (mhc_pre_forward_timed), in a second pass of K steps, each
+               preceded (outside the events) by a 512 MiB write that evicts the 256 MB
+               Infinity Cache, so that no step reads its inputs from the previous step's cache
+               lines (decode is timed back to back without it);
+  waits_timed_out  mhc_pre_wait_status after the timed steps (1: a single-read wait gave up);
   cpu_baseline the fp64 C oracle on the host cores, on a bounded sample of tokens.
-Read from profiles/ (measured by rocprofv3 counter runs of this same script):
-  roofline.traffic  HBM bytes per launch of that kernel from FETCH_SIZE and
-               WRITE_SIZE, each divided by the factor the same counter reads for a
-               plain device copy of known size; null when no counter summary exists
-               for this kernel and workload, or when the kernel source has changed
-               since it was taken (source SHA-256 recorded beside the counts).
+Read from profiles/ (rocprofv3 runs of this same script, taken while the kernel sources hash
+to the SHA-256 recorded beside the figures; otherwise null):
+  roofline.traffic  HBM bytes per launch of that kernel from FETCH_SIZE and WRITE_SIZE, each
+               divided by the factor the same counter reads for a plain device copy of known
+               size;
+  roofline.rocprof_avg_us / frac_rocprof  that kernel's average duration in the kernel
+               trace, and the fraction of peak it gives.
 """
 from __future__ import annotations
 
@@ -38,7 +44,7 @@ KERNEL_SOURCES = ("mhc_hyper_connection_amd/csrc/mhc_kernels.hip",
 KERNEL_NAMES = {"pack": "prepack_kernel", "projection": "proj_kernel",
                 "epilogue": "epilogue_kernel", "hin": "hin_kernel"}
 # the single-read path runs one kernel in the projection stage and none in the hIn stage
-KERNEL_NAMES_SINGLE_READ = dict(KERNEL_NAMES, projection="fused_kernel", hin="(none)")
+KERNEL_NAMES_SINGLE_READ = dict(KERNEL_NAMES, projection="single_read_kernel", hin="(none)")
 
 
 def algorithmic_bytes(wl, *, intermediates: bool) -> int:
@@ -126,6 +132,27 @@ def counter_traffic(kernel: str, workload: str):
     except (KeyError, ValueError):
         return None, "counter summary incomplete"
     return fetch + write, os.path.relpath(path, ROOT)
+
+
+def trace_average(kernel: str, workload: str):
+    """rocprofv3 average duration (µs) of `kernel` from profiles/<kernel>_<workload>_trace.md,
+    or None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_trace.md")
+    if not os.path.exists(path):
+        return None, "no trace summary"
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip().strip("`").strip()
+            if ":" in line and line.split(":", 1)[0].strip() in ("source_sha256", "avg_us"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    try:
+        if vals["source_sha256"] != kernel_source_sha():
+            return None, "kernel changed since the trace was taken"
+        return float(vals["avg_us"]), os.path.relpath(path, ROOT)
+    except (KeyError, ValueError):
+        return None, "trace summary incomplete"
 
 
 def cpu_baseline(inp, max_tokens: int):
@@ -344,6 +371,9 @@ def main():
     ap.add_argument("--graph-replays", type=int, default=0,
                     help="after the timed steps, capture one step into a HIP graph and report "
                          "its per-replay time over this many replays (four-kernel path only)")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="size of the write that evicts the Infinity Cache before each step of the "
+                         "per-kernel pass (0: none; decode never flushes)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain copy of this size first (for counter calibration)")
     ap.add_argument("--op", choices=("forward", "backward", "post"), default="forward",
@@ -401,10 +431,27 @@ def main():
         run(x, phi, alpha, bias, gamma, pre_mix, out=out)
     torch.cuda.synchronize(dev)
 
-    # one set of events per timed step; each is recorded once here so that its HIP
-    # event exists before the library records it. Boundaries around a stage that launches
-    # nothing (the pack and hIn stages of the single-read path) are not recorded: each
-    # record costs a few microseconds on the stream.
+    # timed region: exactly K back-to-back steps, bracketed by device synchronisation
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run(x, phi, alpha, bias, gamma, pre_mix, out=out)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    waits_timed_out = run.wait_status()
+    if waits_timed_out:
+        print("[bench] WARNING: a single-read wait gave up (its tokens hold NaN)", file=sys.stderr, flush=True)
+
+    # per-kernel durations: a second pass of K steps with HIP events on the launch stream;
+    # one set of events per step, each recorded once here so that its HIP event exists
+    # before the library records it. Boundaries around a stage that launches nothing (the
+    # pack and hIn stages of the single-read path) are not recorded: each record costs a
+    # few microseconds on the stream. Before each step (outside its events) a 512 MiB
+    # write evicts the Infinity Cache, except for decode (launch-bound, back to back).
+    flush = None
+    if args.flush_mib > 0 and wl.name != "decode":
+        flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
     wanted = [True] * mhc.FORWARD_EVENTS
     if single_read:
         wanted[0] = wanted[-1] = False
@@ -415,15 +462,15 @@ def main():
             if e is not None:
                 e.record(stream)
     torch.cuda.synchronize(dev)
-
-    # timed region: exactly K steps, bracketed by device synchronisation
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    for row in evs:
+    print(f"[bench] per-kernel pass {args.steps} steps" + (" (cache flushed)" if flush is not None else ""),
+          file=sys.stderr, flush=True)
+    for step, row in enumerate(evs):
+        if flush is not None:
+            flush.fill_(step & 0xFF)
         run(x, phi, alpha, bias, gamma, pre_mix, out=out, events=row)
     torch.cuda.synchronize(dev)
-    elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / args.steps
+    waits_timed_out |= run.wait_status()
+    del flush
 
     kernels = {}
     for i, stage in enumerate(mhc.STAGES):
@@ -442,6 +489,7 @@ def main():
     kd = kernels[dom]
     achieved = kd["algorithmic_bytes"] / (kd["avg_us"] * 1e-6) / 1e9
     traffic, traffic_src = counter_traffic(names[dom], wl.name)
+    rp_us, rp_src = trace_average(names[dom], wl.name)
     b_call = algorithmic_bytes(wl, intermediates=wl.need_backward)
     call_avg = sum(call_us) / len(call_us)
 
@@ -466,7 +514,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": kd["kernel"], "algorithmic_bytes": kd["algorithmic_bytes"],
-                     "avg_launch_us": kd["avg_us"], "traffic_source": traffic_src},
+                     "avg_launch_us": kd["avg_us"], "traffic_source": traffic_src,
+                     "rocprof_avg_us": rp_us,
+                     "frac_rocprof": None if rp_us is None else kd["algorithmic_bytes"] / (rp_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "rocprof_source": rp_src},
+        "waits_timed_out": waits_timed_out,
         "call": {"algorithmic_bytes": b_call, "avg_us": call_avg,
                  "achieved_GBs": b_call / (call_avg * 1e-6) / 1e9,
                  "frac": b_call / (call_avg * 1e-6) / 1e9 / HBM_PEAK_GBS},

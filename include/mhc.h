@@ -175,6 +175,21 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
 mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Whether a single-read forward that used `workspace` has given up one of its waits since
+ * the last report. The single-read kernel's workgroups wait for values other workgroups of
+ * their group publish; each wait is bounded (about 0.3 s of polling), and one that gives up
+ * leaves NaN in the hIn and hPre of the tokens concerned (mhc_pre_forward has already
+ * returned MHC_OK by then: it is asynchronous). This call synchronises `stream` (the stream
+ * those forwards ran on; NULL = the default stream), then sets *timed_out to 1 if the
+ * workspace's time-out flag is set, else 0, and clears the flag. In normal operation the
+ * waits end by construction and the flag stays 0; it can be set when the workgroups of one
+ * XCD cannot all run at once (another workload holding compute units for that long).
+ *   workspace        the forward's workspace (>= 256 bytes, 256-byte aligned)
+ *   workspace_bytes  its size
+ * Errors: NULLPTR (workspace or timed_out), PARAM_INVALID (workspace too small or
+ * misaligned), RUNTIME (a HIP call failed). */
+mhc_status mhc_pre_wait_status(void* workspace, size_t workspace_bytes, void* stream, int32_t* timed_out);
+
 /* Which path mhc_pre_forward would take for these parameters on the current device:
  * *path = 1 the single-read kernel, 0 the four-kernel path (has_pre_mix: whether pre_mix
  * will be given). Errors: NULLPTR, PARAM_INVALID. */

@@ -18,8 +18,8 @@ from ._binding import (FORWARD_EVENTS, MHC_ERR_NULLPTR, MHC_ERR_PARAM_INVALID,
                        MHC_ERR_RUNTIME, MHC_OK, STAGES, MhcError, Params, bwd_workspace_size,
                        forward_path, raw_inv_rms, raw_post, raw_sinkhorn,
                        load, make_bwd_params, make_params, packed_size, raw_backward,
-                       raw_forward, raw_forward_timed, raw_prepack, status_string, version,
-                       workspace_size)
+                       raw_forward, raw_forward_timed, raw_prepack, raw_wait_status, status_string,
+                       version, workspace_size)
 
 __all__ = ["PreForward", "PreBackward", "mhc_pre", "mhc_pre_backward", "mhc_post", "mhc_pre_inv_rms",
            "mhc_pre_sinkhorn", "prepack", "version",
@@ -89,6 +89,12 @@ class PreForward:
     def path(self, has_pre_mix=False):
         """1 when calls take the single-read kernel on this device, else 0."""
         return forward_path(self.params, has_pre_mix)
+
+    def wait_status(self):
+        """mhc_pre_wait_status on this launcher's workspace: 1 if a single-read wait gave up
+        since the last query (its tokens then hold NaN), else 0. Synchronises the current
+        stream; clears the flag."""
+        return raw_wait_status(_ptr(self.workspace), self.workspace.numel(), _stream(self.device))
 
     # -- outputs -----------------------------------------------------------------------
     def alloc_outputs(self, *, intermediates=None):

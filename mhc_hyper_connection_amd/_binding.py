@@ -57,7 +57,8 @@ class BwdTensors(ctypes.Structure):
 EXPORTS = ("mhc_version", "mhc_status_string", "mhc_pre_packed_size",
            "mhc_pre_workspace_size", "mhc_pre_prepack", "mhc_pre_forward",
            "mhc_pre_forward_timed", "mhc_pre_forward_path", "mhc_pre_backward_workspace_size",
-           "mhc_pre_backward", "mhc_post", "mhc_pre_inv_rms", "mhc_pre_sinkhorn")
+           "mhc_pre_backward", "mhc_post", "mhc_pre_inv_rms", "mhc_pre_sinkhorn",
+           "mhc_pre_wait_status")
 
 # MHC_FORWARD_EVENTS: events of mhc_pre_forward_timed (before the first kernel, then one
 # after each of pack, projection, epilogue, hIn)
@@ -123,6 +124,9 @@ def load(path: str | None = None):
     lib.mhc_pre_sinkhorn.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(SinkhornTensors), ctypes.c_void_p]
     lib.mhc_pre_forward_path.restype = ctypes.c_int32
     lib.mhc_pre_forward_path.argtypes = [ctypes.POINTER(Params), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.mhc_pre_wait_status.restype = ctypes.c_int32
+    lib.mhc_pre_wait_status.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                        ctypes.POINTER(ctypes.c_int32)]
     lib.mhc_pre_backward.argtypes = [ctypes.POINTER(BwdParams), ctypes.POINTER(BwdTensors),
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     if path is None:
@@ -220,3 +224,14 @@ def raw_inv_rms(params: Params, x_ptr, inv_rms_ptr, stream) -> int:
 def raw_sinkhorn(params: Params, ptrs: dict, stream) -> int:
     t = SinkhornTensors(*[ptrs.get(f) for f in SINKHORN_TENSOR_FIELDS])
     return int(load().mhc_pre_sinkhorn(ctypes.byref(params), ctypes.byref(t), stream))
+
+
+def raw_wait_status(ws_ptr, ws_bytes, stream) -> int:
+    """mhc_pre_wait_status: 1 if a single-read wait gave up since the last query (clears it)."""
+    out = ctypes.c_int32(0)
+    st = load().mhc_pre_wait_status(ctypes.c_void_p(ws_ptr), ctypes.c_size_t(ws_bytes), stream,
+                                    ctypes.byref(out))
+    if st != MHC_OK:
+        raise MhcError(st, "mhc_pre_wait_status")
+    return int(out.value)
+

@@ -171,6 +171,8 @@ mhc_status forward_impl(const mhc_pre_params* params, const mhc_pre_tensors* t,
     a.rec = reinterpret_cast<float*>(ws + plan.off_rec);
     a.prx = plan.fused_geom ? reinterpret_cast<uint64_t*>(ws + plan.off_prx) : nullptr;
     a.hpx = plan.fused_geom ? reinterpret_cast<uint64_t*>(ws + plan.off_hpx) : nullptr;
+    a.spx = plan.sr_geom ? reinterpret_cast<uint64_t*>(ws + plan.off_spx) : nullptr;
+    a.shx = plan.sr_geom ? reinterpret_cast<uint64_t*>(ws + plan.off_shx) : nullptr;
     a.sync = reinterpret_cast<uint32_t*>(ws + plan.off_sync);
     a.num_iters = params->num_iters;
     a.norm_eps = params->norm_eps;
@@ -186,6 +188,15 @@ mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* 
                            void* workspace, size_t workspace_bytes, void* stream)
 {
     return forward_impl(params, t, workspace, workspace_bytes, stream, nullptr);
+}
+
+mhc_status mhc_pre_wait_status(void* workspace, size_t workspace_bytes, void* stream, int32_t* timed_out)
+{
+    if (!workspace || !timed_out) return MHC_ERR_NULLPTR;
+    if (workspace_bytes < 256 || !aligned(workspace, 256)) return MHC_ERR_PARAM_INVALID;
+    return mhc::read_and_clear_wait_flag(static_cast<uint32_t*>(workspace), timed_out, stream) == 0
+               ? MHC_OK
+               : MHC_ERR_RUNTIME;
 }
 
 static_assert(MHC_FORWARD_EVENTS == mhc::kStages + 1, "one event per kernel boundary");

@@ -643,6 +643,7 @@ hipError_t launch_all(const Plan& p, const Args& a, hipStream_t st)
 
 int launch_backward(const Plan& p, const Args& a, void* stream)
 {
+    clear_pending_error();
     hipStream_t st = (hipStream_t)stream;
     const Geometry& g = p.g;
     if (p.T == 0) {

@@ -73,6 +73,11 @@ __device__ __forceinline__ void wait_vm(int n)
 #undef MHC_VM_CASE8
 #undef MHC_VM_CASE
 
+// Each launch is checked with hipGetLastError, which reports the last error of any HIP call
+// of this thread: an entry point first clears one left pending by an earlier, unrelated call,
+// so that it is not taken for a failed launch.
+inline void clear_pending_error() { (void)hipGetLastError(); }
+
 // Buffer resources: a base address and a byte range in four scalar registers; vector
 // accesses take a 32-bit byte offset, and loads outside the range return zero (stores
 // outside it are dropped), which bounds every access of a ragged tile in hardware.

@@ -69,6 +69,7 @@ post_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ residua
 int launch_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* residual, const float* post,
                 const float* comb, uint16_t* out, int x_f16, void* stream)
 {
+    clear_pending_error();
     if (T <= 0) return 0;
     const int64_t items = T * (int64_t)(D / 8);
     const dim3 grid((unsigned)((items + 255) / 256));

@@ -176,3 +176,16 @@ def test_timed_forward_validates_events_first():
     # then the forward's own validation, before any HIP call
     assert B.raw_forward_timed(_p(n=5), _ptrs(), FAKE, WS_BIG, None, [FAKE] * 5) == B.MHC_ERR_PARAM_INVALID
     assert B.raw_forward_timed(_p(), _ptrs(x=None), FAKE, WS_BIG, None, [FAKE] * 5) == B.MHC_ERR_NULLPTR
+
+
+def test_wait_status_validation():
+    # mhc_pre_wait_status rejects before any HIP call: NULL workspace or output, a workspace
+    # smaller than its 256-byte head, a misaligned one
+    lib = B.load()
+    out = ctypes.c_int32(7)
+    assert lib.mhc_pre_wait_status(None, 1 << 20, None, ctypes.byref(out)) == B.MHC_ERR_NULLPTR
+    assert lib.mhc_pre_wait_status(ctypes.c_void_p(FAKE), 1 << 20, None, None) == B.MHC_ERR_NULLPTR
+    assert lib.mhc_pre_wait_status(ctypes.c_void_p(FAKE), 255, None, ctypes.byref(out)) == B.MHC_ERR_PARAM_INVALID
+    assert lib.mhc_pre_wait_status(ctypes.c_void_p(FAKE + 64), 1 << 20, None, ctypes.byref(out)) == B.MHC_ERR_PARAM_INVALID
+    assert out.value == 7   # untouched on error
+

@@ -1,9 +1,12 @@
-"""The single-read forward kernel (n = 4, alpha[3], no pre_mix, 1024 <= D <= 7168): path
-selection on the device, and parity with the fp64 oracle under the acceptance rule of
-gpu_helpers, at the sizes where it is chosen by itself (the large workload test covers that at
-full size) and, forced by MHC_FORWARD_PATH=fused, at small and ragged sizes: partial last
-tiles of 16 tokens, groups with unequal numbers of tiles, members with unequal numbers of
-d-blocks, a partial last d-block, gamma, and the output set without intermediates."""
+"""The single-read forward kernel (n = 4, alpha[3], no pre_mix, 32 to 224 d-blocks of 32
+positions, T >= 2048): path selection on the device, and parity with the fp64 oracle under
+the acceptance rule of gpu_helpers, at the sizes where it is chosen by itself (the large
+workload test covers that at full size) and, forced by MHC_FORWARD_PATH=fused, at small and
+ragged sizes: partial last tiles of 32 tokens, groups with unequal numbers of tiles,
+members with unequal numbers of d-blocks (one or two per wave, or none), a partial last
+d-block, gamma, and the output set without intermediates. The wait time-out is driven from
+the host (a test switch makes every exchange wait give up after a few polls, all kernels
+exit normally) and must show through mhc_pre_wait_status."""
 import sys
 
 import numpy as np
@@ -22,15 +25,16 @@ def _runner(wl, nb):
 
 
 def _timeout_flag(runner):
-    # the library's wait time-out flag: the second 32-bit word of the workspace
-    return int(runner.workspace[4:8].cpu().numpy().view(np.uint32)[0])
+    # the library's wait time-out flag, read and cleared through the C-ABI
+    return runner.wait_status()
 
 
 @pytest.mark.parametrize("T,D,pre_mix,n,n_alpha,want", [
     (16384, 7168, False, 4, 3, 1), (8192, 4096, False, 4, 3, 1), (8192, 1024, False, 4, 3, 1),
-    (64, 7168, False, 4, 3, 0), (8191, 4096, False, 4, 3, 0), (4096, 4096, False, 4, 3, 0),
-    (16384, 7168, True, 4, 3, 0), (8192, 8192, False, 4, 3, 0), (8192, 992, False, 4, 3, 0),
-    (8192, 1016, False, 4, 3, 1), (8192, 2048, False, 8, 3, 0), (8192, 2048, False, 4, 2, 0)])
+    (64, 7168, False, 4, 3, 0), (2047, 7168, False, 4, 3, 0), (2048, 7168, False, 4, 3, 1),
+    (4096, 4096, False, 4, 3, 1), (16384, 7168, True, 4, 3, 0), (8192, 8192, False, 4, 3, 0),
+    (8192, 992, False, 4, 3, 0), (8192, 1016, False, 4, 3, 1), (8192, 2048, False, 8, 3, 0),
+    (8192, 2048, False, 4, 2, 0)])
 def test_path_selection(T, D, pre_mix, n, n_alpha, want, monkeypatch):
     import mhc_hyper_connection_amd as mhc
     monkeypatch.delenv("MHC_FORWARD_PATH", raising=False)
@@ -103,3 +107,25 @@ def test_single_read_with_prepacked_weights(monkeypatch):
     for k in g_packed:
         assert np.array_equal(g_packed[k].view(np.uint8), g_inline[k].view(np.uint8)), k
     assert _timeout_flag(r) == 0
+
+
+def test_wait_time_out_is_reported(monkeypatch):
+    # every exchange wait made to give up (the kernel then never sees the tag it waits for,
+    # and stops polling after a few tries): the call still returns, hIn and hPre hold NaN,
+    # and mhc_pre_wait_status reports the time-out once, then clears it
+    import mhc_hyper_connection_amd as mhc
+    monkeypatch.setenv("MHC_FORWARD_PATH", "fused")
+    monkeypatch.setenv("MHC_TEST_EXCHANGE_NEVER_READY", "1")
+    print("[case] single-read forced wait time-out T=1000 D=2048", file=sys.stderr, flush=True)
+    inp = synth.custom(1000, 4, 2048, need_backward=True, seed=61)
+    r = _runner(inp.wl, True)
+    assert r.path() == 1
+    g = gpu_forward(inp, runner=r)
+    assert r.wait_status() == 1
+    assert r.wait_status() == 0
+    hin = g["h_in"].view(np.int16)
+    assert np.all((hin & 0x7F80) == 0x7F80) and np.all((hin & 0x7F) != 0)   # bf16 NaN everywhere
+    assert np.all(np.isnan(g["h_pre"]))
+    monkeypatch.delenv("MHC_TEST_EXCHANGE_NEVER_READY")
+    compare(gpu_forward(inp, runner=r), run_oracle(inp), inp)
+    assert r.wait_status() == 0
