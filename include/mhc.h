@@ -175,6 +175,22 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
 mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* mhc_pre_forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation,
+ * outputs and errors, without a workspace argument. The workspace is a device array of
+ * 64 MiB that the library holds on every GPU it runs on, from the first such call on that
+ * GPU (whose device must be current) to the end of the process; it is zero-filled when the
+ * library is loaded and keeps the last call's contents. The call itself allocates nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (different
+ * streams, other host threads) race and must not be made. A problem whose
+ * mhc_pre_workspace_size exceeds 64 MiB is rejected with MHC_ERR_PARAM_INVALID (it fits
+ * up to 7808 tokens at n = 4, D = 7168; 12544 at D = 4096; 25216 at n = 8, D = 2048). The
+ * wait-time-out flag of this workspace is not readable through mhc_pre_wait_status.
+ * Errors: NULLPTR, PARAM_INVALID, RUNTIME (also when the array's address cannot be
+ * obtained on the current device). */
+mhc_status mhc_pre_forward_noalloc(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
+                                   void* stream);
+
 /* Whether a single-read forward that used `workspace` has given up one of its waits since
  * the last report. The single-read kernel's workgroups wait for values other workgroups of
  * their group publish; each wait is bounded (about 0.3 s of polling), and one that gives up

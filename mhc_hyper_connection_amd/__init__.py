@@ -18,7 +18,8 @@ from ._binding import (FORWARD_EVENTS, MHC_ERR_NULLPTR, MHC_ERR_PARAM_INVALID,
                        MHC_ERR_RUNTIME, MHC_OK, STAGES, MhcError, Params, bwd_workspace_size,
                        forward_path, raw_inv_rms, raw_post, raw_sinkhorn,
                        load, make_bwd_params, make_params, packed_size, raw_backward,
-                       raw_forward, raw_forward_timed, raw_prepack, raw_wait_status, status_string,
+                       raw_forward, raw_forward_noalloc, raw_forward_timed, raw_prepack, raw_wait_status,
+                       status_string,
                        version, workspace_size)
 
 __all__ = ["PreForward", "PreBackward", "mhc_pre", "mhc_pre_backward", "mhc_post", "mhc_pre_inv_rms",
@@ -131,11 +132,12 @@ class PreForward:
 
     # -- forward -----------------------------------------------------------------------
     def __call__(self, x, phi, alpha, bias, gamma=None, pre_mix=None, *, phi_packed=None,
-                 out=None, events=None):
+                 out=None, events=None, noalloc=False):
         """events: optional list of FORWARD_EVENTS torch.cuda.Event(enable_timing=True) or
         None, each event recorded at least once before (so that its HIP event exists); the
         call then records them around its kernels (STAGES order) and skips the None
-        entries, see mhc_pre_forward_timed."""
+        entries, see mhc_pre_forward_timed. noalloc: call mhc_pre_forward_noalloc instead
+        (the library's per-GPU scratch array as workspace; no events)."""
         torch = _torch()
         T, n, D, M, dev = self.T, self.n, self.D, self.M, self.device
         _check(x, "x", self.xdt, (T, n, D), dev)
@@ -151,7 +153,11 @@ class PreForward:
                 "gamma": _ptr(gamma), "pre_mix": _ptr(pre_mix), "phi_packed": _ptr(phi_packed)}
         for k, v in out.items():
             ptrs[k] = _ptr(v)
-        if events is None:
+        if noalloc:
+            st = raw_forward_noalloc(self.params, ptrs, _stream(dev))
+            if st != MHC_OK:
+                raise MhcError(st, "mhc_pre_forward_noalloc")
+        elif events is None:
             st = raw_forward(self.params, ptrs, _ptr(self.workspace), self.ws_bytes,
                              _stream(dev))
             if st != MHC_OK:

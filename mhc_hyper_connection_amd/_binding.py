@@ -58,7 +58,7 @@ EXPORTS = ("mhc_version", "mhc_status_string", "mhc_pre_packed_size",
            "mhc_pre_workspace_size", "mhc_pre_prepack", "mhc_pre_forward",
            "mhc_pre_forward_timed", "mhc_pre_forward_path", "mhc_pre_backward_workspace_size",
            "mhc_pre_backward", "mhc_post", "mhc_pre_inv_rms", "mhc_pre_sinkhorn",
-           "mhc_pre_wait_status")
+           "mhc_pre_wait_status", "mhc_pre_forward_noalloc")
 
 # MHC_FORWARD_EVENTS: events of mhc_pre_forward_timed (before the first kernel, then one
 # after each of pack, projection, epilogue, hIn)
@@ -124,6 +124,8 @@ def load(path: str | None = None):
     lib.mhc_pre_sinkhorn.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(SinkhornTensors), ctypes.c_void_p]
     lib.mhc_pre_forward_path.restype = ctypes.c_int32
     lib.mhc_pre_forward_path.argtypes = [ctypes.POINTER(Params), ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    lib.mhc_pre_forward_noalloc.restype = ctypes.c_int32
+    lib.mhc_pre_forward_noalloc.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(Tensors), ctypes.c_void_p]
     lib.mhc_pre_wait_status.restype = ctypes.c_int32
     lib.mhc_pre_wait_status.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                         ctypes.POINTER(ctypes.c_int32)]
@@ -235,3 +237,8 @@ def raw_wait_status(ws_ptr, ws_bytes, stream) -> int:
         raise MhcError(st, "mhc_pre_wait_status")
     return int(out.value)
 
+
+def raw_forward_noalloc(params: Params, ptrs: dict, stream) -> int:
+    """mhc_pre_forward_noalloc: the forward with the library's per-GPU scratch array as workspace."""
+    t = Tensors(*[ptrs.get(f) for f in TENSOR_FIELDS])
+    return int(load().mhc_pre_forward_noalloc(ctypes.byref(params), ctypes.byref(t), stream))

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libmhc.so")
 ARCH = os.environ.get("MHC_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = [os.path.join(CSRC, "mhc_kernels.hip"), os.path.join(CSRC, "mhc_bwd.hip"), os.path.join(CSRC, "mhc_post.hip"),
-           os.path.join(CSRC, "mhc_api.cpp")]
+           os.path.join(CSRC, "mhc_scratch.hip"), os.path.join(CSRC, "mhc_api.cpp")]
 # -amdgpu-mfma-vgpr-form=1 keeps matrix-core sources and accumulators in ordinary VGPRs.
 # With the default accumulation-register form, this toolchain's code for the projection
 # kernel produced wrong sums on gfx950 (deterministically, for every schedule tried); the

@@ -190,6 +190,21 @@ mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* 
     return forward_impl(params, t, workspace, workspace_bytes, stream, nullptr);
 }
 
+mhc_status mhc_pre_forward_noalloc(const mhc_pre_params* params, const mhc_pre_tensors* t, void* stream)
+{
+    // the checks that need no device first, in the order mhc_pre_forward makes them; the
+    // workspace comes from the library's per-GPU scratch array
+    if (!params || !t) return MHC_ERR_NULLPTR;
+    mhc::Geometry g;
+    mhc_status st = check_params(params, &g);
+    if (st != MHC_OK) return st;
+    if (params->T < 0) return MHC_ERR_PARAM_INVALID;
+    if (mhc::make_plan(g, params->T).ws_bytes > mhc::kScratchBytes) return MHC_ERR_PARAM_INVALID;
+    void* ws = nullptr;
+    if (mhc::scratch_for_current_device(&ws) != 0) return MHC_ERR_RUNTIME;
+    return forward_impl(params, t, ws, mhc::kScratchBytes, stream, nullptr);
+}
+
 mhc_status mhc_pre_wait_status(void* workspace, size_t workspace_bytes, void* stream, int32_t* timed_out)
 {
     if (!workspace || !timed_out) return MHC_ERR_NULLPTR;

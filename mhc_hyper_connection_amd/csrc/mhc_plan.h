@@ -368,6 +368,11 @@ int launch_inv_rms(int64_t T, int n, int D, double norm_eps, const uint16_t* x, 
                    int x_f16, void* stream);
 int launch_pre_sinkhorn(int64_t T, int n, int D, int n_alpha, int x_f16, const ForwardArgs& a,
                         const float* h_mix, const float* inv_rms, void* stream);
+// mhc_scratch.hip: the device array that mhc_pre_forward_noalloc uses as its workspace
+// (kScratchBytes per GPU), and its address on the current device, looked up once per device.
+// 0 or the HIP error code.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+int scratch_for_current_device(void** ptr);
 
 // hc_post (mhc_post.hip): out = post x + comb residual per token; 0 or the HIP error code.
 int launch_post(int64_t T, int n, int D, const uint16_t* x, const uint16_t* residual, const float* post,

@@ -189,3 +189,13 @@ def test_wait_status_validation():
     assert lib.mhc_pre_wait_status(ctypes.c_void_p(FAKE + 64), 1 << 20, None, ctypes.byref(out)) == B.MHC_ERR_PARAM_INVALID
     assert out.value == 7   # untouched on error
 
+
+def test_noalloc_validation():
+    # mhc_pre_forward_noalloc: NULL arguments, and a problem whose workspace exceeds the
+    # library's 64 MiB array, are refused before any HIP call
+    lib = B.load()
+    assert lib.mhc_pre_forward_noalloc(None, None, None) == B.MHC_ERR_NULLPTR
+    big = _p(T=65536, D=7168, need_backward=True)
+    assert B.workspace_size(big) > (64 << 20)
+    assert B.raw_forward_noalloc(big, _ptrs(), None) == B.MHC_ERR_PARAM_INVALID
+    assert B.raw_forward_noalloc(_p(n=5), _ptrs(), None) == B.MHC_ERR_PARAM_INVALID
