@@ -44,7 +44,7 @@ KERNEL_SOURCES = ("mhc_hyper_connection_amd/csrc/mhc_kernels.hip",
 KERNEL_NAMES = {"pack": "prepack_kernel", "projection": "proj_kernel",
                 "epilogue": "epilogue_kernel", "hin": "hin_kernel"}
 # the single-read path runs one kernel in the projection stage and none in the hIn stage
-KERNEL_NAMES_SINGLE_READ = dict(KERNEL_NAMES, projection="single_read_kernel", hin="(none)")
+KERNEL_NAMES_SINGLE_READ = dict(KERNEL_NAMES, projection="fused_kernel", hin="(none)")
 
 
 def algorithmic_bytes(wl, *, intermediates: bool) -> int:
@@ -526,7 +526,7 @@ def main():
     }
     if args.graph_replays > 0 and not single_read:
         # launch-bound sizes: the same step replayed from a captured graph (outside the
-        # timed region; a capturing stream never takes the cooperative kernel)
+        # timed region)
         print(f"[bench] graph replays {args.graph_replays}", file=sys.stderr, flush=True)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):

@@ -161,11 +161,13 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
  *   four-kernel path: a projection kernel (which with pre_mix also writes hIn), a
  *     per-token epilogue and, without pre_mix, an hIn kernel (x is read twice);
  *   single-read path (n == 4, n_alpha == 3, no pre_mix, 992 < D <= 7168 (32 to 224
- *     blocks of 32 positions), T >= 8192, not while
- *     the stream is capturing a graph): one cooperative kernel computes the projection,
- *     hPre and hIn, x read once, then the per-token epilogue. It occupies every compute
- *     unit until done; its workgroups wait on each other, each wait bounded (a wait that
- *     times out leaves NaN in hIn for the tokens concerned).
+ *     blocks of 32 positions), T >= 8192, a device of 8 XCDs with 32 compute units each):
+ *     one kernel computes the projection, hPre and hIn, x read once, then the per-token
+ *     epilogue. Its workgroups (one per compute unit, in one group of 32 per XCD) wait on
+ *     each other, each wait bounded: it needs every compute unit of an XCD at once, as an
+ *     otherwise idle device gives; a wait that times out (other work holding compute
+ *     units that long) leaves NaN in hIn for the tokens concerned, which
+ *     mhc_pre_wait_status reports. Both paths can be captured into a HIP graph.
  * The two paths sum the projection's partial products in different groupings, so their
  * outputs may differ in the last bits; each meets the same accuracy. Within a call, hIn
  * uses exactly the hPre it emits. Results are bitwise reproducible for the same inputs,

@@ -24,10 +24,11 @@
 //                    without pre_mix, the hIn weights.
 //   hin_kernel       without pre_mix: hIn[t, d] = sum_i hPre[t, i] x[t, i, d].
 //   fused_kernel     the single-read path (n = 4, alpha[3], no pre_mix, large T), in place
-//                    of proj_kernel and hin_kernel: one cooperative launch whose workgroups
-//                    keep their weights in LDS and each tile's x in registers until its hPre
-//                    (summed by a designated workgroup, exchanged through tagged words) is
-//                    known, so x is read once; the epilogue follows.
+//                    of proj_kernel and hin_kernel: one launch whose workgroups (a group of
+//                    32 per XCD) keep their weights in LDS and each tile's x in registers
+//                    until its hPre (summed by a designated workgroup, exchanged through
+//                    tagged words in the XCD's L2) is known, so x is read once; the epilogue
+//                    follows.
 // Standalone stages (the HcPre guide, mhpn.cn/news/2282827, "function description", names
 // invRms and the Sinkhorn stage as operators of their own):
 //   inv_rms_kernel   invRms alone: one wave per token, squares and sums in fp64.
@@ -542,7 +543,7 @@ epilogue_kernel(KArgs k)
     // the epilogue is the call's last reader of the counter's value: the next call's tag;
     // the single-read kernel's per-XCD arrival counters start from zero again
     if (blockIdx.x == 0 && tid == 0) a.sync[0] = a.sync[0] + 1u;
-    if (blockIdx.x == 0 && tid < kSMaxGroups) a.sync[kSTicket0 + tid] = 0u;
+    if (blockIdx.x == 0 && tid < kXcds) a.sync[kTicket0 + tid] = 0u;
 
     const rsrc_t rec = make_rsrc(a.rec + rec_tile(tile, k.S, N, M), (int64_t)k.S * kTileTokens * V * 4);
     // two items per thread and pass, their loads issued together (eight in flight)
@@ -828,10 +829,13 @@ struct FArgs {
     int64_t tiles16;
     int D;
     int nblk;
-    int G;       // groups (of kFMembers members)
+    int G;               // groups (of kFMembers members): XCDs taking part
 };
 
-// One workgroup = member s of group g (blockIdx = s G + g). Waves 0 .. 6 compute: wave w
+// One workgroup = member s of group g: g is its XCD (hardware XCC id), s its arrival order
+// on that XCD (a workgroup that arrives after the group is full, or on an XCD beyond the
+// G groups needed, leaves), so the tagged words a group exchanges stay in one L2. Waves
+// 0 .. 6 compute: wave w
 // owns d-block member_begin + w and, for a tile of 16 tokens, its n K-steps (the n streams
 // of the block), so a lane holds the n streams of one octet and hIn is local to it. Wave 7
 // is the control wave: it alone waits on other workgroups. Round r of the group is tile
@@ -851,9 +855,11 @@ struct FArgs {
 //     hPre; then polls the hPre of round k - 2 and hands it to the compute waves through
 //     LDS slot (k - 2) mod 4 and its flag.
 // Every wait at round r is for work other members finish by their round r - 1, so with
-// all workgroups resident (cooperative launch) the waits end; a wait that does not end
-// within kSpinLimit polls sets sync[1] and yields NaN hPre for that tile.
-template <int N, int A>
+// all workgroups of a group resident at once (one per compute unit of the XCD, which an
+// otherwise idle device gives) the waits end; a wait that does not end within
+// kSpinLimit polls sets sync[1] and yields NaN hPre for that tile. NeverReady: the
+// instance for the test of that path, whose waits accept no tag and give up after 8 polls.
+template <int N, int A, bool NeverReady>
 __global__ void __launch_bounds__(kFThreads, 1)
 fused_kernel(FArgs f)
 {
@@ -881,11 +887,24 @@ fused_kernel(FArgs f)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int j = lane & 15, grp = lane >> 4;
-    const int g = (int)(blockIdx.x % f.G), s = (int)(blockIdx.x / f.G);
+    __shared__ int sh_member;
+    if (tid == 0) {
+        uint32_t xcc;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+        const int x = (int)(xcc & 0xFu) % kXcds;
+        const uint32_t t = __hip_atomic_fetch_add(a.sync + kTicket0 + x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh_member = t < (uint32_t)P && x < f.G ? x * P + (int)t : -1;
+    }
+    __syncthreads();
+    const int gm = __builtin_amdgcn_readfirstlane(sh_member);
+    if (gm < 0) return;   // the group of this XCD is full, or not needed
+    const int g = gm / P, s = gm % P;
     const int b_lo = member_begin(s, f.nblk, P);
     const int nb = member_begin(s + 1, f.nblk, P) - b_lo;
     const int64_t R = g < f.tiles16 ? (f.tiles16 - g + f.G - 1) / f.G : 0;   // rounds of group g
     const uint32_t tag = (f.a.sync[0] << 1) | 1u;
+    const uint32_t want = NeverReady ? tag ^ 0x40000000u : tag;   // the tag a wait accepts
+    constexpr int spin_limit = kSpinLimit;
 
     if (a.packed) {   // the member's K-steps of the packed weights, without the zero columns past 3M
         const u32x4* src = static_cast<const u32x4*>(a.packed) + (int64_t)b_lo * N * 4 * NC;
@@ -1119,7 +1138,7 @@ fused_kernel(FArgs f)
         auto records_ready = [&]() {
             bool ok = true;
 #pragma unroll
-            for (int q = 0; q < P; ++q) ok &= tag_is(pre[q], tag) & tag_is(pss[q], tag);
+            for (int q = 0; q < P; ++q) ok = ok && tag_is(pre[q], want) && tag_is(pss[q], want);
             return __all(ok);
         };
         const float alpha0 = a.alpha[0];
@@ -1139,7 +1158,7 @@ fused_kernel(FArgs f)
                 load_records(jt);
                 bool ok = records_ready();
                 for (int it = 0; !ok && !failed; ++it) {
-                    if (it == kSpinLimit) { fail(); break; }
+                    if (it == spin_limit) { fail(); break; }
                     __builtin_amdgcn_s_sleep(2);
                     load_records(jt);
                     ok = records_ready();
@@ -1166,401 +1185,18 @@ fused_kernel(FArgs f)
             if (rp >= 0 && rp < R) {
                 const uint64_t* src = a.hpx + hpx_at(rp * f.G + g, tq, iq, N);
                 uint64_t w = get_tagged_l2(src);
-                bool ok = tag_is(w, tag);
+                bool ok = tag_is(w, want);
                 for (int it = 0; !__all(ok) && !failed; ++it) {
-                    if (it == kSpinLimit) { fail(); break; }
+                    if (it == spin_limit) { fail(); break; }
                     __builtin_amdgcn_s_sleep(1);
                     w = (it & 1) ? get_tagged(src) : get_tagged_l2(src);   // every other poll device-coherent
-                    ok = tag_is(w, tag);
+                    ok = tag_is(w, want);
                 }
                 hp_lds[rp % NS][lane] = ok ? tagged_value(w) : __builtin_nanf("");
                 asm volatile("" : : : "memory");
                 if (lane == 0) __hip_atomic_store(&hp_flag[rp % NS], (uint32_t)rp + 1u, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
             }
-        }
-    }
-}
-
-// ------------------------------------------------------------------ single-read forward, XCD groups
-
-struct SArgs {
-    ForwardArgs a;
-    int64_t T;
-    int64_t K;
-    int64_t tiles32;
-    int D;
-    int nblk;
-    int G;             // groups: XCDs taking part
-    uint32_t tag_xor;  // 0, except in the test that forces every exchange wait to give up
-    int spin_limit;    // polls before an exchange wait gives up
-};
-
-// A workgroup of the single-read kernel is member s of group g: g is its XCD (hardware XCC
-// id), s its arrival order on that XCD; a workgroup that arrives after the group is full
-// leaves. Member s owns the d-blocks [s nblk / 32, (s + 1) nblk / 32) (at most 7) and keeps
-// their packed weights in LDS. Group g walks the 32-token tiles g, g + G, ... in rounds.
-// Wave w = (token half tg = w / 4, block pair db = w % 4) loads, per round, its 16 tokens'
-// two d-blocks of all n = 4 streams (a 128-byte line of each token row and stream, 8
-// 16-byte loads per lane), projects them on the matrix cores and keeps them in registers
-// for kSLag rounds, until the tile's hPre is known; hIn is then local to each lane.
-// Round r, in order:
-//   - the loads of tile r + 1 go out (one round of prefetch);
-//   - the member designated for tile r - 1 (member (r - 1) mod 32) checks the exchanged
-//     sums of that tile (loaded at the end of round r - 1), sums them per wave over 8
-//     members into LDS, and the last of a token half's 4 waves publishes (and emits) that
-//     half's hPre;
-//   - tile r's projection (hi, mid and lo folded in fp32) goes to LDS partials;
-//   - one barrier;
-//   - tile r's partial record (the 4 waves of a token half summed in order), stored for the
-//     per-token epilogue and, for the pre sums and the square, as tagged words;
-//   - hIn of tile r - 2 from registers, with hPre read from the published words;
-//   - loads: the published hPre of tile r - 1, and, on the member designated for tile r,
-//     the exchanged sums of tile r.
-// Exchanged and published values are 64-bit words (value, tag of call and round) written
-// and read as relaxed device-scope atomics (sc1): a reader sees an older word or the whole
-// new one, the tag tells which, and no ordering between words is needed. They live in
-// rings of kSPreSlots rounds per group; no member gets more than about two rounds ahead of
-// another (each needs every member's sums of a tile two rounds back), well inside the ring.
-template <int N, int A>
-__global__ void __launch_bounds__(kSThreads, 1)
-single_read_kernel(SArgs f)
-{
-    constexpr int M = 24, NT = 5, NCL = 72, P = kSMembers;
-    static_assert(N == 4 && A == 3, "single-read kernel: n = 4 with alpha[3]");
-    static_assert(Cfg<N, A>::NT == NT && Cfg<N, A>::M == M && Cfg<N, A>::V == 28, "record layout");
-    __shared__ u32x4 wl[kSMaxBlocks * N * 4 * NCL];    // the member's packed weights (72 columns)
-    constexpr int PS = 26;                              // rows 0 .. 23, the square, one pad
-    __shared__ float part[2][kSWaves][16][PS];          // each wave's sums, by round parity
-    __shared__ float gsum[2][2][4][16][kSPreVals];      // exchanged sums per (token half, member group)
-    __shared__ uint32_t gcnt[2][2];                     // member groups summed, per (round parity, token half)
-    __shared__ int sh_member;
-    const ForwardArgs& a = f.a;
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
-    const int j = lane & 15, grp = lane >> 4;
-    const int tg = wave >> 2, db = wave & 3;
-
-    if (tid < 4) gcnt[tid / 2][tid % 2] = 0u;
-    if (tid == 0) {
-        uint32_t xcc;
-        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-        const int x = (int)(xcc & 0xFu) % kSMaxGroups;
-        const uint32_t t = __hip_atomic_fetch_add(a.sync + kSTicket0 + x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sh_member = t < (uint32_t)P && x < f.G ? x * P + (int)t : -1;
-    }
-    __syncthreads();
-    const int gm = __builtin_amdgcn_readfirstlane(sh_member);
-    if (gm < 0) return;   // the group of this XCD is full
-    const int g = gm / P, s = gm % P;
-    const int64_t R = g < f.tiles32 ? (f.tiles32 - g + f.G - 1) / f.G : 0;   // rounds of group g
-    if (R == 0) return;
-    const int b_lo = member_begin(s, f.nblk, P);
-    const int nb = member_begin(s + 1, f.nblk, P) - b_lo;
-    const uint32_t call = a.sync[0];
-    auto tag_of = [&](int64_t r) { return ((((call << 8) | (uint32_t)(r & 255)) << 1) | 1u); };
-
-    // the member's weights into LDS: copied from phi_packed, or split from phi (and gamma)
-    // with the pack kernel's arithmetic
-    if (a.packed) {
-        const u32x4* src = static_cast<const u32x4*>(a.packed) + (int64_t)b_lo * N * 4 * Cfg<N, A>::NC;
-        const int units = nb * N * 4 * NCL;
-        for (int u = tid; u < units; u += kSThreads) wl[u] = src[(int64_t)(u / NCL) * Cfg<N, A>::NC + u % NCL];
-    } else {
-        const int items = nb * N * 4 * M;
-        for (int it = tid; it < items; it += kSThreads) {
-            const int m = it % M, row = it / M;
-            const int kk = row / 4, og = row % 4;
-            const int k = b_lo * N + kk;
-            const int d = kBlock * (k / N) + 8 * og;
-            u32x4 w3[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-            if (d < f.D) {
-                const int64_t k0 = (int64_t)(k % N) * f.D + d;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    double p = (double)a.phi[(int64_t)m * f.K + k0 + e];
-                    if (a.gamma) p *= (double)a.gamma[k0 + e];
-                    uint32_t tb[3];
-                    split3(p, tb);
-#pragma unroll
-                    for (int term = 0; term < 3; ++term) w3[term][e >> 1] |= tb[term] << (16 * (e & 1));
-                }
-            }
-#pragma unroll
-            for (int term = 0; term < 3; ++term) wl[row * NCL + term * M + m] = w3[term];
-        }
-    }
-    // K-steps past the member's blocks: zeros (a wave with a missing block multiplies them
-    // by zero x)
-    for (int uu = nb * N * 4 * NCL + tid; uu < kSMaxBlocks * N * 4 * NCL; uu += kSThreads) wl[uu] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-
-    // this wave's two d-blocks (member-relative 2 db, 2 db + 1; the member may own fewer).
-    // Every load and store of the round loop is issued unconditionally, a missing block, an
-    // octet past D, a token past T or a round outside the group's range getting an offset
-    // outside its buffer (loads return zero, stores are dropped): the compiler then counts
-    // exactly the memory operations younger than each one it waits for.
-    const int mb0 = 2 * db;
-    const int bg = b_lo + mb0;                       // global index of the wave's first block
-    const bool ok0 = mb0 < nb && kBlock * bg + 8 * grp < f.D;
-    const bool ok1 = mb0 + 1 < nb && kBlock * (bg + 1) + 8 * grp < f.D;
-    // LDS K-steps of the two blocks (a missing block reads real, finite weights against
-    // zero x)
-    const int kb0 = (mb0 < kSMaxBlocks ? mb0 : kSMaxBlocks - 1) * N;
-    const int kb1 = (mb0 + 1 < kSMaxBlocks ? mb0 + 1 : kSMaxBlocks - 1) * N;
-    const int row = 16 * tg + j;                     // the lane's token within the tile
-    const uint32_t xo = (uint32_t)(((int64_t)row * f.K + kBlock * bg + 8 * grp) * 2);
-    const uint32_t ho = (uint32_t)(((int64_t)row * f.D + kBlock * bg + 8 * grp) * 2);
-    const float alpha0 = a.alpha[0];
-    const float eps = (float)a.hc_eps;
-    float bias_pre[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) bias_pre[i] = a.bias[i];
-
-    u32x4 xr[kSRing][2][N];   // [slot][block][stream]
-    // tile of round q into dst: stream-major, the two blocks of a stream back to back (one
-    // 128-byte line per token row); rows past T and rounds past the group's last read zero
-    auto load_round = [&](int64_t q, u32x4 (&dst)[2][N]) {
-        const bool live = q < R;
-        const int64_t t0 = live ? (q * f.G + g) * kSTok : 0;
-        const int64_t nt = f.T - t0 < kSTok ? f.T - t0 : kSTok;
-        const rsrc_t xres = make_rsrc(a.x + t0 * f.K, live ? nt * f.K * 2 : 0);
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const uint32_t o = xo + 2 * (uint32_t)f.D * i;
-            dst[0][i] = __builtin_amdgcn_raw_buffer_load_b128(xres, (int)(ok0 ? o : kOutOfRange), 0, 0);
-            dst[1][i] = __builtin_amdgcn_raw_buffer_load_b128(xres, (int)(ok1 ? o + 64 : kOutOfRange), 0, 0);
-        }
-    };
-    // exchanged words of tile q the designated member's lane reads: member 8 db + lane / 8,
-    // tokens 2 (lane % 8) and the next of this token half, the five sums of each (ten
-    // consecutive words)
-    const int xm = 8 * db + (lane >> 3);
-    const int xt = 16 * tg + 2 * (lane & 7);
-    const uint32_t xoff = (uint32_t)(((xm * kSTok + xt) * kSPreVals) * 8);
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    u32x2 pw[2 * kSPreVals];
-    u32x2 hw;   // the published hPre word of (the lane's token j, stream grp)
-    auto load_exchange = [&](int64_t q) {
-        const bool live = q >= 0 && q < R;
-        const rsrc_t er = make_rsrc(a.spx + spx_at(g, live ? q : 0, 0, 0, 0),
-                                    live ? (int64_t)kSMembers * kSTok * kSPreVals * 8 : 0);
-#pragma unroll
-        for (int e = 0; e < 2 * kSPreVals; ++e) pw[e] = __builtin_amdgcn_raw_buffer_load_b64(er, (int)(xoff + 8 * e), 0, 16);
-    };
-    auto load_hpre = [&](int64_t q) {
-        const bool live = q >= 0 && q < R;
-        const rsrc_t hr = make_rsrc(a.shx + shx_at(g, live ? q : 0, 0, 0), live ? (int64_t)kSTok * 4 * 8 : 0);
-        hw = __builtin_amdgcn_raw_buffer_load_b64(hr, (int)((row * 4 + grp) * 8), 0, 16);
-    };
-    // a bounded wait: poll (reload) until `ready`, else record the time-out
-    bool failed = false;
-    auto wait_for = [&](auto ready, auto reload) {
-        if (failed || ready()) return;
-        int it = 0;
-        for (; it < f.spin_limit; ++it) {
-            __builtin_amdgcn_s_sleep(2);
-            reload();
-            if (ready()) break;
-        }
-        if (it == f.spin_limit) {
-            failed = true;
-            if (lane == 0) __hip_atomic_store(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    };
-
-    load_round(0, xr[0]);
-    for (int64_t r0 = 0; r0 < R + kSLag; r0 += kSRing) {
-#pragma unroll
-        for (int u = 0; u < kSRing; ++u) {
-            const int64_t r = r0 + u;
-            if (r >= R + kSLag) break;
-            const int pb = (int)(r & 1);
-            // one round of prefetch; the slot held tile r - 3, whose hIn was stored in round r - 1
-            load_round(r + 1, xr[(u + 1) % kSRing]);
-
-            // the member designated for tile r - 1: every member's exchanged sums present,
-            // else poll again; then a fixed tree over the wave's 8 members (lane bits 3 .. 5),
-            // every lane of a token pair ending with the same bits
-            const bool desig = r >= 1 && r - 1 < R && (int)((r - 1) % P) == s;
-            if (desig) {
-                const uint32_t want = tag_of(r - 1) ^ f.tag_xor;
-                wait_for([&]() {
-                    bool ok = true;
-#pragma unroll
-                    for (int e = 0; e < 2 * kSPreVals; ++e) ok = ok && pw[e][1] == want;
-                    return __all(ok);
-                }, [&]() { load_exchange(r - 1); });
-                float sv[2 * kSPreVals];
-#pragma unroll
-                for (int e = 0; e < 2 * kSPreVals; ++e) {
-                    float v = failed ? __builtin_nanf("") : __uint_as_float(pw[e][0]);
-                    v += dpp<kRowRor8>(v);
-                    v += __shfl_xor(v, 16);
-                    v += __shfl_xor(v, 32);
-                    sv[e] = v;
-                }
-                if (lane < 8) {
-#pragma unroll
-                    for (int e = 0; e < 2 * kSPreVals; ++e)
-                        gsum[pb][tg][db][2 * lane + e / kSPreVals][e % kSPreVals] = sv[e];
-                }
-                // the last of the token half's 4 waves to get here (an LDS counter; each wave's
-                // sums are written before it counts) computes hPre of those 16 tokens from the 4
-                // member-group sums (fp64, in group order) and publishes and emits it at once,
-                // before this member's projection: lane (j, grp) gives token 16 tg + j, stream grp
-                asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-                uint32_t before = 0;
-                if (lane == 0) before = __hip_atomic_fetch_add(&gcnt[pb][tg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                before = __builtin_amdgcn_readfirstlane(before);
-                if (before == 3) {
-                    asm volatile("" : : : "memory");
-                    if (lane == 0) gcnt[pb][tg] = 0u;   // counted again two rounds on, after a barrier
-                    const int64_t q = r - 1;
-                    const int64_t t0 = (q * f.G + g) * kSTok;
-                    const int64_t nt = f.T - t0 < kSTok ? f.T - t0 : kSTok;
-                    double tot[kSPreVals];
-#pragma unroll
-                    for (int v = 0; v < kSPreVals; ++v) {
-                        double acc = 0.0;
-#pragma unroll
-                        for (int d2 = 0; d2 < 4; ++d2) acc += (double)gsum[pb][tg][d2][j][v];
-                        tot[v] = acc;
-                    }
-                    const double inv = inv_rms_of(tot[N], (double)f.K, a.norm_eps);
-                    float hv = 0.f;
-#pragma unroll
-                    for (int i = 0; i < N; ++i)
-                        if (grp == i) hv = gate_pre(tot[i], inv, alpha0, bias_pre[i], eps);
-                    const rsrc_t hr = make_rsrc(a.shx + shx_at(g, q, 0, 0), (int64_t)kSTok * 4 * 8);
-                    const u32x2 w = {__float_as_uint(hv), tag_of(q)};
-                    __builtin_amdgcn_raw_buffer_store_b64(w, hr, (int)((row * 4 + grp) * 8), 0, 16);
-                    const rsrc_t pr = make_rsrc(a.h_pre ? a.h_pre + t0 * N : a.h_post, a.h_pre ? nt * N * 4 : 0);
-                    st_buf(pr, (uint32_t)(row * N + grp) * 4, hv);
-                }
-            }
-
-            // tile r's projection: 8 K-steps (2 blocks x 4 streams) of 6 products each
-            {
-                f32x4 acc[NT];
-                f32x4 sq = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int bb = 0; bb < 2; ++bb) {
-#pragma unroll
-                    for (int i = 0; i < N; ++i) {
-                        const u32x4* wb = wl + ((bb == 0 ? kb0 : kb1) + i) * 4 * NCL + grp * NCL;
-                        u32x4 bw[NT];
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt) {
-                            const int col = 16 * nt + j < NCL ? 16 * nt + j : 16 * nt + j - 16;
-                            bw[nt] = wb[col];
-                        }
-                        const bf16x8 Av = __builtin_bit_cast(bf16x8, xr[u][bb][i]);
-                        sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Av, sq, 0, 0, 0);
-#pragma unroll
-                        for (int nt = 0; nt < NT; ++nt)
-                            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, __builtin_bit_cast(bf16x8, bw[nt]),
-                                                                              acc[nt], 0, 0, 0);
-                    }
-                }
-                // phi row m's hi, mid and lo are columns m, M + m, 2M + m: lane j of a 16-lane
-                // row holds row m = j (and 16 + j when j < 8), its mid term in lane (j + 8) mod 16
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int t = 4 * grp + q;
-                    const float m1 = dpp<kRowRor8>(acc[1][q]), m2 = dpp<kRowRor8>(acc[2][q]);
-                    part[pb][wave][t][j] = (acc[0][q] + (j < 8 ? m1 : m2)) + acc[3][q];
-                    if (j < 8) part[pb][wave][t][16 + j] = (acc[1][q] + m2) + acc[4][q];
-                }
-                const int rr = j - 4 * grp;
-                if (rr >= 0 && rr < 4) part[pb][wave][j][24] = sq[rr];
-            }
-            __syncthreads();
-
-            {
-                // the partial record of tokens 4 wave .. 4 wave + 3 of the tile: the 4 waves of
-                // the token half summed in order. Record value v: the pre sums (0 .. 3), the
-                // square (4), padding (5 .. 7), the other rows (8 .. 27 = rows 4 .. 23)
-                const bool live = r < R;
-                const int64_t jt = live ? r * f.G + g : 0;
-                const int64_t t0 = jt * kSTok;
-                const int ntile = live ? (int)(f.T - t0 < kSTok ? f.T - t0 : kSTok) : 0;
-                const int q = lane / 14, c = lane % 14;
-                const int tt = 4 * wave + q;          // token of the tile
-                const int t16 = 4 * db + q;           // token within its half
-                const bool on = lane < 56;
-                float val[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int v = 2 * c + h;
-                    const int idx = v < N ? v : (v == N ? 24 : (v < 8 ? -1 : v - N));
-                    float sum = 0.f;
-#pragma unroll
-                    for (int d2 = 0; d2 < 4; ++d2) sum += on && idx >= 0 ? part[pb][tg * 4 + d2][t16 < 16 ? t16 : 0][idx >= 0 ? idx : 0] : 0.f;
-                    val[h] = sum;
-                }
-                const rsrc_t rec = make_rsrc(a.rec + rec_tile(jt / 2, P, N, M), (int64_t)P * kTileTokens * 28 * 4);
-                const uint32_t off = on && tt < ntile ? (uint32_t)(rec_loc(s, kSTok * (int)(jt % 2) + tt, N, M) + 2 * c) * 4
-                                                      : kOutOfRange;
-                const u32x2 pv = {__float_as_uint(val[0]), __float_as_uint(val[1])};
-                __builtin_amdgcn_raw_buffer_store_b64(pv, rec, (int)off, 0, 0);
-                // the exchanged words: v = 2c and 2c + 1 while <= 4 (every token of a live round,
-                // also those past T, so that the exchange of a ragged tile completes)
-                const uint32_t tag = tag_of(r);
-                const rsrc_t er = make_rsrc(a.spx + spx_at(g, live ? r : 0, s, 0, 0),
-                                            live ? (int64_t)kSTok * kSPreVals * 8 : 0);
-                const uint32_t eo = (uint32_t)((tt * kSPreVals + 2 * c) * 8);
-                const u32x2 w0 = {__float_as_uint(val[0]), tag};
-                const u32x2 w1 = {__float_as_uint(val[1]), tag};
-                __builtin_amdgcn_raw_buffer_store_b64(w0, er, (int)(on && 2 * c <= N ? eo : kOutOfRange), 0, 16);
-                __builtin_amdgcn_raw_buffer_store_b64(w1, er, (int)(on && 2 * c + 1 <= N ? eo + 8 : kOutOfRange), 0, 16);
-            }
-
-            {
-                // hIn of tile r - 2 from the registers that still hold its x, with the
-                // published hPre (loaded at the end of round r - 1)
-                const int64_t rh = r - kSLag;
-                const bool live = rh >= 0 && rh < R;
-                const int64_t t0 = live ? (rh * f.G + g) * kSTok : 0;
-                const int64_t nt = live ? (f.T - t0 < kSTok ? f.T - t0 : kSTok) : 0;
-                if (live) {
-                    const uint32_t want = tag_of(rh) ^ f.tag_xor;
-                    wait_for([&]() { return __all(hw[1] == want); }, [&]() { load_hpre(rh); });
-                }
-                const float mine = failed ? __builtin_nanf("") : __uint_as_float(hw[0]);
-                float hp[N];
-#pragma unroll
-                for (int i = 0; i < N; ++i) hp[i] = __shfl(mine, j + 16 * i);   // lane (j, i) holds stream i
-                const int uh = (u + kSRing - kSLag) % kSRing;
-                const rsrc_t hres = make_rsrc(a.h_in + t0 * f.D, nt * f.D * 2);
-#pragma unroll
-                for (int bb = 0; bb < 2; ++bb) {
-                    float hacc[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) hacc[e] = 0.f;
-#pragma unroll
-                    for (int i = 0; i < N; ++i) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            hacc[2 * e] = fmaf(hp[i], bf16_lo(xr[uh][bb][i][e]), hacc[2 * e]);
-                            hacc[2 * e + 1] = fmaf(hp[i], bf16_hi(xr[uh][bb][i][e]), hacc[2 * e + 1]);
-                        }
-                    }
-                    u32x4 o;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(hacc[2 * e], hacc[2 * e + 1]);
-                    const bool okb = bb == 0 ? ok0 : ok1;
-                    __builtin_amdgcn_raw_buffer_store_b128(o, hres, (int)(okb ? ho + 64 * bb : kOutOfRange), 0, 0);
-                }
-            }
-
-            // the published hPre of tile r - 1 (for the next round's hIn) and, on the member
-            // designated for tile r, every member's exchanged sums of tile r
-            load_hpre(r - 1);
-            if (r < R && (int)(r % P) == s) load_exchange(r);
         }
     }
 }
@@ -1596,17 +1232,32 @@ hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st, void* con
     return e == hipSuccess ? mark(events, kStageHin + 1, st) : e;
 }
 
-// Groups of the single-read kernel on the current device, 0 when it cannot run here.
+// Whether a kernel's code keeps everything in registers. The single-read kernel's x loads
+// are invisible to the compiler (inline assembly, waited for by hand): were it to spill
+// registers to scratch memory, it could spill or reuse a register such a load has yet to
+// write. The kernel is refused then (the four-kernel path serves), never run.
+bool no_scratch(const void* fn)
+{
+    hipFuncAttributes at;
+    return hipFuncGetAttributes(&at, fn) == hipSuccess && at.localSizeBytes == 0;
+}
+
+// Groups of the single-read kernel on the current device (one per XCD, at most one per
+// tile), 0 when it cannot run here: the kernel needs kXcds XCDs of kFMembers compute units,
+// one workgroup on each, and code without scratch memory.
 int fused_groups(const Plan& p)
 {
-    int dev = 0, coop = 0, cus = 0, per_cu = 0;
+    int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<4, 3>, kFThreads, 0) != hipSuccess ||
+    if (cus != kXcds * kFMembers) return 0;
+    if (!no_scratch(reinterpret_cast<const void*>(fused_kernel<4, 3, false>)) ||
+        !no_scratch(reinterpret_cast<const void*>(fused_kernel<4, 3, true>)))
+        return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<4, 3, false>, kFThreads, 0) != hipSuccess ||
         per_cu < 1)
         return 0;
-    int64_t G = (int64_t)cus * per_cu / p.FP;
+    int64_t G = kXcds;
     if (G > p.tiles16) G = p.tiles16;
     return (int)G;
 }
@@ -1620,9 +1271,7 @@ bool fused_wanted(const Plan& p, bool has_pre_mix)
     return forced || p.T >= kFMinTokens;
 }
 
-// *launched is false when the cooperative launch itself was refused (nothing ran).
-hipError_t launch_fused(const Plan& p, const ForwardArgs& a, int G, hipStream_t st, void* const* events,
-                        bool* launched)
+hipError_t launch_fused(const Plan& p, const ForwardArgs& a, int G, hipStream_t st, void* const* events)
 {
     FArgs f;
     f.a = a;
@@ -1632,83 +1281,21 @@ hipError_t launch_fused(const Plan& p, const ForwardArgs& a, int G, hipStream_t 
     f.D = p.g.D;
     f.nblk = p.g.nblk;
     f.G = G;
-    void* args[] = {&f};
-    hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fused_kernel<4, 3>),
-                                              dim3((unsigned)(G * p.FP)), dim3(kFThreads), args, 0, st);
-    if (e == hipSuccess) e = hipGetLastError();
-    *launched = e == hipSuccess;
-    if (e == hipSuccess) e = mark(events, kStageProj + 1, st);
-    if (e != hipSuccess) return e;
-    KArgs k;
-    k.a = a;
-    k.T = p.T;
-    k.K = p.g.K;
-    k.tiles = p.tiles;
-    k.D = p.g.D;
-    k.S = p.FP;
-    k.GS = p.FGS;
-    k.NG = p.FNG;
-    if (p.OB == 16)
-        hipLaunchKernelGGL((epilogue_kernel<4, 3, 16>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
-    else
-        hipLaunchKernelGGL((epilogue_kernel<4, 3, 8>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = mark(events, kStageEpi + 1, st);
-    if (e == hipSuccess) e = mark(events, kStageHin + 1, st);
-    return e;
-}
-
-// Groups (XCDs) the single-read kernel with XCD groups uses on the current device: 0 when
-// it cannot run here (fewer than one group of compute units, or not one workgroup per CU).
-int sr_groups()
-{
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, single_read_kernel<4, 3>, kSThreads, 0) != hipSuccess ||
-        per_cu < 1)
-        return 0;
-    const int G = cus / kSMembers;
-    return G < kSMaxGroups ? G : kSMaxGroups;
-}
-
-bool sr_wanted(const Plan& p, bool has_pre_mix)
-{
-    if (!p.sr_geom || has_pre_mix || p.T <= 0) return false;
-    const char* env = std::getenv("MHC_FORWARD_PATH");
-    if (env && std::strcmp(env, "classic") == 0) return false;
-    const bool forced = env && std::strcmp(env, "fused") == 0;
-    return forced || p.T >= kSMinTokens;
-}
-
-hipError_t launch_single_read(const Plan& p, const ForwardArgs& a, int G, hipStream_t st, void* const* events)
-{
-    SArgs f;
-    f.a = a;
-    f.T = p.T;
-    f.K = p.g.K;
-    f.tiles32 = p.tiles32;
-    f.D = p.g.D;
-    f.nblk = p.g.nblk;
-    f.G = G;
-    f.tag_xor = 0u;
-    f.spin_limit = 1 << 17;
     // test hook: every exchange wait gives up after a few polls (all kernels still exit
     // normally); the time-out then shows in the workspace's flag
     const char* never = std::getenv("MHC_TEST_EXCHANGE_NEVER_READY");
-    if (never && std::strcmp(never, "1") == 0) {
-        f.tag_xor = 0x40000000u;
-        f.spin_limit = 8;
-    }
-    // one workgroup per compute unit: kSMembers land on each XCD (the hardware deals
-    // workgroups to the XCDs in turn); one that finds its XCD's group full leaves
-    hipLaunchKernelGGL((single_read_kernel<4, 3>), dim3((unsigned)(G * kSMembers)), dim3(kSThreads), 0, st, f);
+    const bool test_never_ready = never && std::strcmp(never, "1") == 0;
+    // one workgroup per compute unit: the hardware deals workgroups to the XCDs in turn,
+    // kFMembers to each; a workgroup whose XCD's group is full (or not needed) leaves
+    if (test_never_ready)
+        hipLaunchKernelGGL((fused_kernel<4, 3, true>), dim3((unsigned)(kXcds * p.FP)), dim3(kFThreads), 0, st, f);
+    else
+        hipLaunchKernelGGL((fused_kernel<4, 3, false>), dim3((unsigned)(kXcds * p.FP)), dim3(kFThreads), 0, st, f);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) e = mark(events, kStageProj + 1, st);
     if (e != hipSuccess) return e;
     KArgs k;
     k.a = a;
-    k.a.h_pre = nullptr;   // emitted by the single-read kernel: the exact weights hIn used
     k.T = p.T;
     k.K = p.g.K;
     k.tiles = p.tiles;
@@ -1730,7 +1317,6 @@ hipError_t launch_single_read(const Plan& p, const ForwardArgs& a, int G, hipStr
 
 int forward_path(const Plan& p, bool has_pre_mix)
 {
-    if (sr_wanted(p, has_pre_mix) && sr_groups() > 0) return 1;
     return fused_wanted(p, has_pre_mix) && fused_groups(p) > 0 ? 1 : 0;
 }
 
@@ -1818,27 +1404,13 @@ int launch_forward(const Plan& p, const ForwardArgs& a_in, void* stream, void* c
     hipStream_t st = (hipStream_t)stream;
     ForwardArgs a = a_in;
     if (mark(events, kStagePack, st) != hipSuccess) return (int)hipErrorUnknown;
-    if (sr_wanted(p, a.pre_mix != nullptr)) {
+    if (fused_wanted(p, a.pre_mix != nullptr)) {
         // unpacked weights are packed inside the kernel
-        const int G = sr_groups();
+        const int G = fused_groups(p);
         if (G > 0) {
             hipError_t e = mark(events, kStagePack + 1, st);
             if (e != hipSuccess) return (int)e;
-            return (int)launch_single_read(p, a, G, st, events);
-        }
-    }
-    if (fused_wanted(p, a.pre_mix != nullptr)) {
-        // a cooperative launch is not taken into a graph being captured: the four-kernel
-        // path serves then. Unpacked weights are packed inside the kernel.
-        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        const int G = fused_groups(p);
-        if (G > 0 && hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) {
-            hipError_t e = mark(events, kStagePack + 1, st);
-            if (e != hipSuccess) return (int)e;
-            bool launched = false;
-            e = launch_fused(p, a, G, st, events, &launched);
-            if (launched) return (int)e;
-            (void)hipGetLastError();   // refused: the four-kernel path below serves
+            return (int)launch_fused(p, a, G, st, events);
         }
     }
     if (!a.packed) {

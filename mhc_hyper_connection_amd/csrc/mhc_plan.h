@@ -72,21 +72,10 @@ constexpr int kFAhead = 2;             // rounds between a tile's x loads and it
 constexpr int kFLag = kFRing - kFAhead;   // rounds between a tile's projection and its hIn
 constexpr int64_t kFMinTokens = 8192;  // below this the four-kernel path is used (ramp and drain dominate)
 
-// Single-read kernel with XCD groups (see the work decomposition above): a group is the
-// workgroups of one XCD (the hardware's XCC id), so the values its members exchange stay
-// in that XCD's L2; member = arrival order on the XCD.
-constexpr int kSTok = 32;              // tokens per round: two halves of 16 (one matrix-core row block each)
-constexpr int kSMembers = 32;          // members per group
-constexpr int kSMaxBlocks = 7;         // d-blocks per member (two per block-pair wave, the last wave one)
-constexpr int kSWaves = 8;             // (token half, block pair) waves
-constexpr int kSThreads = 64 * kSWaves;
-constexpr int kSRing = 4;              // x register slots: the round's tile, the next one, two awaiting hPre
-constexpr int kSLag = 2;               // rounds between a tile's projection and its hIn
-constexpr int kSPreSlots = 8;          // rounds of exchanged pre-branch sums kept per group (a ring)
-constexpr int kSMaxGroups = 8;         // XCDs
-constexpr int kSPreVals = 5;           // exchanged per token: the n = 4 pre sums and the square sum
-constexpr int kSTicket0 = 8;           // sync word of XCD 0's arrival counter (8 words)
-constexpr int64_t kSMinTokens = 2048;  // below this the four-kernel path is used
+// Groups of the single-read kernel: one per XCD (the hardware's XCC id), so the values
+// its members exchange stay in that XCD's L2; member = arrival order on the XCD.
+constexpr int kXcds = 8;               // XCDs (groups at most)
+constexpr int kTicket0 = 8;            // sync word of XCD 0's arrival counter (kXcds words)
 
 struct Geometry {
     int n = 0;
@@ -190,10 +179,6 @@ struct Plan {
     int FGS = 0, FNG = 0;     // summation groups over the FP member records (as GS, NG)
     int64_t tiles16 = 0;      // ceil(T / 16)
     // single-read kernel with XCD groups
-    bool sr_geom = false;     // n = 4, alpha[3], bf16, 32 .. 224 d-blocks
-    int64_t tiles32 = 0;      // ceil(T / 32)
-    size_t off_spx = 0;       // exchanged pre-branch sums: [groups][slots][members][32][5] tagged words
-    size_t off_shx = 0;       // published hPre: [groups][slots][32][4] tagged words
     size_t off_prx = 0, off_hpx = 0, off_sync = 0;
     size_t off_packed = 0, off_wts = 0, off_rec = 0, ws_bytes = 0;
 };
@@ -222,9 +207,7 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     p.FGS = (p.FP + 7) / 8;
     p.FNG = (p.FP + p.FGS - 1) / p.FGS;
     p.tiles16 = (T + kFTok - 1) / kFTok;
-    p.sr_geom = g.n == 4 && g.n_alpha == 3 && !g.x_f16 && g.nblk >= kSMembers && g.nblk <= kSMembers * kSMaxBlocks;
-    p.tiles32 = (T + kSTok - 1) / kSTok;
-    const int rec_slices = (p.fused_geom || p.sr_geom) && p.FP > p.S ? p.FP : p.S;
+    const int rec_slices = p.fused_geom && p.FP > p.S ? p.FP : p.S;
     // the call counter first, at the same offset for every problem size
     size_t off = 0;
     p.off_sync = off;
@@ -235,12 +218,6 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     off = align_up(off + (size_t)T * g.n * sizeof(float), 256);
     p.off_rec = off;
     off = align_up(off + (size_t)p.tiles * rec_slices * kTileTokens * rec_stride(g.n, g.M) * sizeof(float), 256);
-    if (p.sr_geom) {
-        p.off_spx = off;
-        off = align_up(off + (size_t)kSMaxGroups * kSPreSlots * kSMembers * kSTok * kSPreVals * 8, 256);
-        p.off_shx = off;
-        off = align_up(off + (size_t)kSMaxGroups * kSPreSlots * kSTok * 4 * 8, 256);
-    }
     if (p.fused_geom) {
         p.off_prx = off;
         off = align_up(off + (size_t)p.tiles16 * p.FP * kFTok * (g.n + 1) * 8, 256);
@@ -298,17 +275,6 @@ MHC_HOST_DEVICE inline int64_t prx_at(int64_t jt, int P, int s, int t, int v, in
     return ((jt * P + s) * kFTok + t) * (n + 1) + v;
 }
 MHC_HOST_DEVICE inline int64_t hpx_at(int64_t jt, int t, int i, int n) { return (jt * kFTok + t) * n + i; }
-// Single-read kernel with XCD groups: word of the exchanged sum v (the four pre sums, then
-// the square) of (group g, round r, member s, token t of the 32-token tile); word of the
-// published hPre of (group g, round r, token t, stream i).
-MHC_HOST_DEVICE inline int64_t spx_at(int g, int64_t r, int s, int t, int v)
-{
-    return ((((int64_t)g * kSPreSlots + r % kSPreSlots) * kSMembers + s) * kSTok + t) * kSPreVals + v;
-}
-MHC_HOST_DEVICE inline int64_t shx_at(int g, int64_t r, int t, int i)
-{
-    return (((int64_t)g * kSPreSlots + r % kSPreSlots) * kSTok + t) * 4 + i;
-}
 
 // Everything a forward launch needs (device pointers are raw).
 struct ForwardArgs {
@@ -332,8 +298,6 @@ struct ForwardArgs {
     float* rec;        // partial records, one block per tile
     uint64_t* prx;     // single-read kernel: tagged pre-branch records
     uint64_t* hpx;     // single-read kernel: tagged hPre per tile
-    uint64_t* spx;     // single-read kernel with XCD groups: exchanged pre-branch sums (a ring)
-    uint64_t* shx;     // single-read kernel with XCD groups: published hPre (a ring)
     uint32_t* sync;    // [0] call counter (the epilogue adds 1; the single-read kernel's tag),
                        // [1] set when a single-read wait timed out,
                        // [8 .. 15] arrivals per XCD (the epilogue clears them)

@@ -1,8 +1,10 @@
 """The forward captured into a HIP graph (torch.cuda.CUDAGraph on torch's current stream):
-the four-kernel path records no memset and no host synchronisation, so it can be
-captured; a stream being captured never takes the cooperative single-read kernel.
-Every replay, with eager work of the program between replays, must equal the eager
-call bit for bit (the forward is deterministic), and the eager call meets the oracle."""
+neither path records a memset or a host synchronisation, so both can be captured (the
+single-read path forced by MHC_FORWARD_PATH=fused in the last case: its kernel and the
+epilogue keep the call counter and the per-XCD arrival counters in the workspace, which
+each replay advances and clears as an eager call does). Every replay, with eager work of
+the program between replays, must equal the eager call bit for bit (the forward is
+deterministic), and the eager call meets the oracle."""
 import sys
 
 import numpy as np
@@ -14,15 +16,19 @@ from gpu_helpers import compare, device, run_oracle, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T,D,packed", [(64, 7168, True), (64, 7168, False), (4096, 1024, True)])
-def test_graph_replays_match_eager(T, D, packed):
+@pytest.mark.parametrize("T,D,packed,fused", [(64, 7168, True, False), (64, 7168, False, False),
+                                               (4096, 1024, True, False), (1500, 2048, False, True)])
+def test_graph_replays_match_eager(T, D, packed, fused, monkeypatch):
     import mhc_hyper_connection_amd as mhc
     import torch
-    print(f"[case] graph T={T} D={D} packed={packed}", file=sys.stderr, flush=True)
+    if fused:
+        monkeypatch.setenv("MHC_FORWARD_PATH", "fused")
+    print(f"[case] graph T={T} D={D} packed={packed} single-read={fused}", file=sys.stderr, flush=True)
     dev = device()
     inp = synth.custom(T, 4, D, need_backward=True, seed=95)
     wl = inp.wl
     r = mhc.PreForward(wl.T, wl.n, wl.D, wl.n_alpha, num_iters=wl.num_iters, need_backward=True, device=dev)
+    assert r.path() == (1 if fused else 0)
     x, phi, alpha, bias = (to_dev(a, dev) for a in (inp.x, inp.phi, inp.alpha, inp.bias))
     pk = r.prepack(phi) if packed else None
     eager = r(x, None if packed else phi, alpha, bias, phi_packed=pk)
