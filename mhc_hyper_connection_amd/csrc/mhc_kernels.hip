@@ -817,6 +817,30 @@ __device__ __forceinline__ void wait_vm_only()
 {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(K) : "memory");
 }
+// s_waitcnt vmcnt(n) for a wave-uniform n (a scalar branch to the instruction with that
+// count); n at most the deepest prefetch's count
+__device__ __forceinline__ void wait_vm_upto(int n)
+{
+    switch (n) {
+    case 0: wait_vm_only<0>(); break;
+    case 1: wait_vm_only<1>(); break;
+    case 2: wait_vm_only<2>(); break;
+    case 3: wait_vm_only<3>(); break;
+    case 4: wait_vm_only<4>(); break;
+    case 5: wait_vm_only<5>(); break;
+    case 6: wait_vm_only<6>(); break;
+    case 7: wait_vm_only<7>(); break;
+    case 8: wait_vm_only<8>(); break;
+    case 9: wait_vm_only<9>(); break;
+    case 10: wait_vm_only<10>(); break;
+    case 11: wait_vm_only<11>(); break;
+    case 12: wait_vm_only<12>(); break;
+    case 13: wait_vm_only<13>(); break;
+    case 14: wait_vm_only<14>(); break;
+    default: wait_vm_only<0>(); break;   // (never: a wait for everything is always safe)
+    static_assert(kFMaxYounger <= 14, "a case per count");
+    }
+}
 __device__ __forceinline__ void ring_ready(u32x4 (&v)[4])
 {
     asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]) : : "memory");
@@ -963,7 +987,7 @@ fused_kernel(FArgs f)
 #pragma unroll
             for (int i = 0; i < N; ++i) dst[i] = load_ring(desc, xo + 2 * (uint32_t)f.D * i);
         };
-        static_assert(N == 4 && kFAhead == 2, "wait counts: four loads per round, one younger round");
+        static_assert(N == kFLoads, "wait counts: one x load per stream and round");
         if (has_blk) {
 #pragma unroll
             for (int q = 0; q < kFAhead; ++q)
@@ -982,20 +1006,8 @@ fused_kernel(FArgs f)
                 if (r >= R + kFLag) break;
                 const int pb = (int)(r & 1);
                 if (r < R && has_blk) {
-                    // this round's x. Issued after its loads, in round r - 1: that round's
-                    // two record stores (every round < R has them), its hIn store (from round
-                    // kFLag on) and the loads of round r + 1 (where it exists); memory
-                    // operations complete in issue order
-                    const bool st1 = r >= 1, hs1 = r - 1 >= kFLag, ld1 = r + 1 < R;
-                    if (ld1) {
-                        if (st1 && hs1) wait_vm_only<2 + 1 + N>();
-                        else if (st1) wait_vm_only<2 + N>();
-                        else wait_vm_only<N>();
-                    } else {
-                        if (st1 && hs1) wait_vm_only<2 + 1>();
-                        else if (st1) wait_vm_only<2>();
-                        else wait_vm_only<0>();
-                    }
+                    // this round's x
+                    wait_vm_upto(fused_younger_than_x(r, R));
                     ring_ready(xr[u]);
                     f32x4 acc[NT];
                     f32x4 sq = {0.f, 0.f, 0.f, 0.f};
@@ -1127,18 +1139,22 @@ fused_kernel(FArgs f)
                 __hip_atomic_store(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             failed = true;
         };
-        uint64_t pre[P], pss[P];
-        auto load_records = [&](int64_t jt) {
+        // the tagged pre-branch records of tile jt, half of the members at a time (members
+        // q0 .. q0 + P/2 - 1: whole summation groups; fewer registers than all at once)
+        constexpr int PH = P / 2;
+        static_assert(PH % GS == 0, "whole summation groups per half");
+        uint64_t pre[PH], pss[PH];
+        auto load_records = [&](int64_t jt, int q0) {
 #pragma unroll
-            for (int q = 0; q < P; ++q) {
-                pre[q] = get_tagged(a.prx + prx_at(jt, P, q, tq, iq, N));
-                pss[q] = get_tagged(a.prx + prx_at(jt, P, q, tq, N, N));
+            for (int q = 0; q < PH; ++q) {
+                pre[q] = get_tagged(a.prx + prx_at(jt, P, q0 + q, tq, iq, N));
+                pss[q] = get_tagged(a.prx + prx_at(jt, P, q0 + q, tq, N, N));
             }
         };
         auto records_ready = [&]() {
             bool ok = true;
 #pragma unroll
-            for (int q = 0; q < P; ++q) ok = ok && tag_is(pre[q], want) && tag_is(pss[q], want);
+            for (int q = 0; q < PH; ++q) ok = ok && tag_is(pre[q], want) && tag_is(pss[q], want);
             return __all(ok);
         };
         const float alpha0 = a.alpha[0];
@@ -1155,27 +1171,31 @@ fused_kernel(FArgs f)
             wait_lds_at_least(&cbar, (uint32_t)(NW * (k + 2 < R + kFLag ? k + 2 : R + kFLag)));
             if (k < R && k % P == s) {
                 const int64_t jt = k * f.G + g;
-                load_records(jt);
-                bool ok = records_ready();
-                for (int it = 0; !ok && !failed; ++it) {
-                    if (it == spin_limit) { fail(); break; }
-                    __builtin_amdgcn_s_sleep(2);
-                    load_records(jt);
-                    ok = records_ready();
-                }
                 // the epilogue's order: members in groups of GS, each group in member
                 // order from 0.0, then the group totals in order from 0.0
                 double hs = 0.0, ss = 0.0;
-#pragma unroll
-                for (int q0 = 0; q0 < P; q0 += GS) {
-                    double ga = 0.0, gb = 0.0;
-#pragma unroll
-                    for (int q = q0; q < q0 + GS; ++q) {
-                        ga += (double)tagged_value(pre[q]);
-                        gb += (double)tagged_value(pss[q]);
+                bool ok = true;
+                for (int h0 = 0; h0 < P; h0 += PH) {
+                    load_records(jt, h0);
+                    bool ready = records_ready();
+                    for (int it = 0; !ready && !failed; ++it) {
+                        if (it == spin_limit) { fail(); break; }
+                        __builtin_amdgcn_s_sleep(2);
+                        load_records(jt, h0);
+                        ready = records_ready();
                     }
-                    hs += ga;
-                    ss += gb;
+                    ok = ok && ready;
+#pragma unroll
+                    for (int q0 = 0; q0 < PH; q0 += GS) {
+                        double ga = 0.0, gb = 0.0;
+#pragma unroll
+                        for (int q = q0; q < q0 + GS; ++q) {
+                            ga += (double)tagged_value(pre[q]);
+                            gb += (double)tagged_value(pss[q]);
+                        }
+                        hs += ga;
+                        ss += gb;
+                    }
                 }
                 const double inv = inv_rms_of(ss, (double)f.K, a.norm_eps);
                 const float hp = ok ? gate_pre(hs, inv, alpha0, bias_i, eps) : __builtin_nanf("");

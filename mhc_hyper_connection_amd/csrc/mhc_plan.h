@@ -70,6 +70,7 @@ constexpr int kFThreads = 64 * kFWaves;
 constexpr int kFRing = 8;              // x register slots, one per round
 constexpr int kFAhead = 2;             // rounds between a tile's x loads and its projection
 constexpr int kFLag = kFRing - kFAhead;   // rounds between a tile's projection and its hIn
+constexpr int kFLoads = 4;             // x loads of a compute wave per round (one per stream, n = 4)
 constexpr int64_t kFMinTokens = 8192;  // below this the four-kernel path is used (ramp and drain dominate)
 
 // Groups of the single-read kernel: one per XCD (the hardware's XCC id), so the values
@@ -275,6 +276,30 @@ MHC_HOST_DEVICE inline int64_t prx_at(int64_t jt, int P, int s, int t, int v, in
     return ((jt * P + s) * kFTok + t) * (n + 1) + v;
 }
 MHC_HOST_DEVICE inline int64_t hpx_at(int64_t jt, int t, int i, int n) { return (jt * kFTok + t) * n + i; }
+
+// Single-read kernel, a compute wave with a d-block (R rounds): the memory operations it
+// issues in round j after its x wait (the two record stores in rounds < R, the hIn store
+// from round kFLag on, the kFLoads x loads of round j + kFAhead where that round exists),
+// and how many of its operations are issued after round r's x loads and before round r's
+// x wait (the later prologue loads when r < kFAhead, else every operation of the rounds in
+// between). Operations complete in issue order, so waiting until no more than that many
+// are outstanding waits for round r's x.
+MHC_HOST_DEVICE inline int fused_round_ops(int64_t j, int64_t R)
+{
+    return (j < R ? 2 : 0) + (j >= kFLag ? 1 : 0) + (j + kFAhead < R ? kFLoads : 0);
+}
+MHC_HOST_DEVICE inline int fused_younger_than_x(int64_t r, int64_t R)
+{
+    int c = 0;
+    if (r < kFAhead) {
+        for (int64_t q = r + 1; q < kFAhead; ++q) c += q < R ? kFLoads : 0;
+        for (int64_t j = 0; j < r; ++j) c += fused_round_ops(j, R);
+    } else {
+        for (int64_t j = r - kFAhead + 1; j < r; ++j) c += fused_round_ops(j, R);
+    }
+    return c;
+}
+constexpr int kFMaxYounger = (kFAhead - 1) * (2 + 1 + kFLoads);   // the largest such count
 
 // Everything a forward launch needs (device pointers are raw).
 struct ForwardArgs {
