@@ -364,6 +364,135 @@ proj_kernel(KArgs k)
     }
 }
 
+// ------------------------------------------------------------------ projection on the VALU
+
+// The projection with plain fp32 FMAs instead of the matrix cores, for the four-kernel path:
+// the same tasks (64-token tile, slice of NKS K-steps) and the same partial records, so the
+// epilogue and hIn kernels are unchanged. Weights: phiT[k][m] = phi[m][k] gamma[k] in fp32
+// (the product rounded once), K rows of M, read by whole rows with scalar loads: every lane
+// of a wave uses the same weight row at once. A lane is a token of the tile; wave w takes
+// the d positions [DW w, DW (w + 1)) of the slice (all n streams of each), so with pre_mix
+// its hIn is local; the four waves' sums meet in LDS and are added in wave order.
+__global__ void __launch_bounds__(256) pack_valu_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
+                                                        float* __restrict__ phiT, int64_t K, int M)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // element (k, m) of phiT, m fastest
+    if (i >= K * M) return;
+    const int64_t kk = i / M;
+    const int m = (int)(i % M);
+    double w = (double)phi[(int64_t)m * K + kk];
+    if (gamma) w *= (double)gamma[kk];
+    phiT[i] = (float)w;
+}
+
+template <int N, int A, int NKS, bool H>
+__global__ void __launch_bounds__(kThreads, 2)
+proj_valu_kernel(KArgs k, const float* __restrict__ phiT)
+{
+    using C = Cfg<N, A>;
+    constexpr int M = C::M, CH = C::CH, PPS = C::PPS;
+    constexpr int NBS = NKS / N;                 // d-blocks of a slice
+    constexpr int DW = NBS * kBlock / 4;         // d positions per wave
+    constexpr int NL = DW / 8;                   // 16-byte x loads per stream and lane
+    static_assert(NKS % N == 0 && DW % 8 == 0 && M <= 32, "slice and weight shapes of the VALU projection");
+    __shared__ float red[4][kTileTokens][M + 1];   // each wave's sums of the M rows, then the square
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the weight rows are scalar loads
+    const int lane = tid & 63;
+    int64_t tile;
+    int s;
+    if (!task_of_block(blockIdx.x, k.tiles, k.S, &tile, &s)) return;   // padding workgroup
+    const int64_t t0 = tile * kTileTokens;
+    const int ntile = tile_tokens(k, t0);
+    const int d_lo = kBlock * s * NBS + wave * DW;   // this wave's first d position
+
+    // x of token t0 + lane: stream i, positions [d_lo, d_lo + DW); past D or T: zero
+    const rsrc_t xres = make_rsrc(k.a.x + t0 * k.K, (int64_t)ntile * k.K * 2);
+    u32x4 xr[N][NL];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            const int d = d_lo + 8 * l;
+            const uint32_t off = d < k.D ? (uint32_t)(((int64_t)lane * k.K + (int64_t)i * k.D + d) * 2) : kOutOfRange;
+            xr[i][l] = __builtin_amdgcn_raw_buffer_load_b128(xres, (int)off, 0, 0);
+        }
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.f;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            const int d0 = d_lo + 8 * l;
+            if (d0 >= k.D) continue;   // (the same for every lane) positions past D have no weights
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xe = (e & 1) ? x16_hi<H>(xr[i][l][e >> 1]) : x16_lo<H>(xr[i][l][e >> 1]);
+                // one weight row, the same for every lane: read from the constant address
+                // space, so that the loads are scalar (the weights are not written meanwhile)
+                const __attribute__((address_space(4))) float* w =
+                    (const __attribute__((address_space(4))) float*)(phiT + ((int64_t)i * k.D + d0 + e) * M);
+                sq = fmaf(xe, xe, sq);
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[m] = fmaf(xe, w[m], acc[m]);
+            }
+        }
+#pragma unroll
+    for (int m = 0; m < M; ++m) red[wave][lane][m] = acc[m];
+    red[wave][lane][M] = sq;
+
+    // With pre_mix the hIn weights are known: this wave's positions of hIn from the x registers.
+    if (k.a.pre_mix) {
+        const int64_t tok = t0 + lane < k.T ? t0 + lane : k.T - 1;
+        float wv[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) wv[i] = k.a.pre_mix[tok * N + i];
+        const rsrc_t hres = make_rsrc(k.a.h_in + t0 * k.D, (int64_t)ntile * k.D * 2);
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            float h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = 0.f;
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[2 * e] = fmaf(wv[i], x16_lo<H>(xr[i][l][e]), h[2 * e]);
+                    h[2 * e + 1] = fmaf(wv[i], x16_hi<H>(xr[i][l][e]), h[2 * e + 1]);
+                }
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = pack_x16<H>(h[2 * e], h[2 * e + 1]);
+            const int d = d_lo + 8 * l;
+            const uint32_t off = d < k.D ? (uint32_t)(((int64_t)lane * k.D + d) * 2) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(o, hres, (int)off, 0, 0);
+        }
+    }
+    __syncthreads();
+
+    // partial records of the slice, 16 bytes per store: the waves' sums in wave order (fp32)
+    const rsrc_t rec = make_rsrc(k.a.rec + rec_tile(tile, k.S, N, M), (int64_t)k.S * kTileTokens * C::V * 4);
+    for (int idx = tid; idx < kTileTokens * CH; idx += kThreads) {
+        const int tl = idx / CH, ch = idx % CH;
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int v = 4 * ch + e;
+            const int m = v < N ? v : (v == N ? M : N + (v - PPS));   // row, or M for the square
+            float val = 0.f;
+            if (!((v > N && v < PPS) || v >= PPS + (M - N))) {   // not padding
+#pragma unroll
+                for (int w = 0; w < 4; ++w) val += red[w][tl][m];
+            }
+            o[e] = __float_as_uint(val);
+        }
+        const uint32_t off = tl < ntile ? (uint32_t)(rec_loc(s, tl, N, M) + 4 * ch) * 4 : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(o, rec, (int)off, 0, 0);
+    }
+}
+
 // ------------------------------------------------------------------ per-token math
 
 __device__ __forceinline__ float sigmoidf_stable(float z)
@@ -1229,11 +1358,20 @@ hipError_t mark(void* const* events, int i, hipStream_t st)
 }
 
 template <int N, int A, int NKS, bool H>
-hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st, void* const* events)
+hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st, void* const* events, const float* phiT)
 {
     // Workgroups map to tasks so that each XCD's L2 holds the weights of a few slices
-    // only (task_of_block).
-    hipLaunchKernelGGL((proj_kernel<N, A, NKS, H>), dim3((unsigned)p.proj_blocks), dim3(kThreads), 0, st, k);
+    // only (task_of_block). phiT: the VALU projection's weights, or NULL for the matrix cores.
+    if constexpr (Cfg<N, A>::M <= 32) {
+        if (phiT)
+            hipLaunchKernelGGL((proj_valu_kernel<N, A, NKS, H>), dim3((unsigned)p.proj_blocks), dim3(kThreads), 0, st, k,
+                               phiT);
+        else
+            hipLaunchKernelGGL((proj_kernel<N, A, NKS, H>), dim3((unsigned)p.proj_blocks), dim3(kThreads), 0, st, k);
+    } else {
+        if (phiT) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((proj_kernel<N, A, NKS, H>), dim3((unsigned)p.proj_blocks), dim3(kThreads), 0, st, k);
+    }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) e = mark(events, kStageProj + 1, st);
     if (e != hipSuccess) return e;
@@ -1335,6 +1473,21 @@ hipError_t launch_fused(const Plan& p, const ForwardArgs& a, int G, hipStream_t 
 
 }  // namespace
 
+// Whether the four-kernel path projects on the VALU (fp32 FMA) rather than the matrix
+// cores: MHC_PROJECTION = "valu" or "mfma" decides; otherwise the measured choice, the
+// matrix cores (on MI355X the VALU projection kernel took 1.9 to 3.8 times as long on every
+// workload of the benchmark, fp32 FMA at about a third of the VALU's fp32 peak against a
+// matrix-core projection bound by memory). The VALU path needs phi itself (it packs its own
+// fp32 weights) and M <= 32.
+static bool projection_on_valu(const Plan& p, const ForwardArgs& a)
+{
+    if (!a.phi || p.g.M > 32) return false;
+    const char* env = std::getenv("MHC_PROJECTION");
+    if (env && std::strcmp(env, "valu") == 0) return true;
+    if (env && std::strcmp(env, "mfma") == 0) return false;
+    return false;
+}
+
 int forward_path(const Plan& p, bool has_pre_mix)
 {
     return fused_wanted(p, has_pre_mix) && fused_groups(p) > 0 ? 1 : 0;
@@ -1433,7 +1586,16 @@ int launch_forward(const Plan& p, const ForwardArgs& a_in, void* stream, void* c
             return (int)launch_fused(p, a, G, st, events);
         }
     }
-    if (!a.packed) {
+    // the projection on the VALU (fp32 weights packed here, from phi) or the matrix cores
+    const bool valu = projection_on_valu(p, a);
+    const float* phiT = nullptr;
+    if (valu) {
+        const int64_t items = p.g.K * (int64_t)p.g.M;
+        hipLaunchKernelGGL(pack_valu_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, a.phi, a.gamma,
+                           static_cast<float*>(a.packed_ws), p.g.K, p.g.M);
+        if (hipGetLastError() != hipSuccess) return (int)hipErrorUnknown;
+        phiT = static_cast<const float*>(a.packed_ws);
+    } else if (!a.packed) {
         if (launch_prepack(p.g, a.phi, a.gamma, a.packed_ws, stream) != 0) return (int)hipErrorUnknown;
         a.packed = a.packed_ws;
     }
@@ -1460,8 +1622,8 @@ int launch_forward(const Plan& p, const ForwardArgs& a_in, void* stream, void* c
     if (n == 6 && na == 2 && (v.nt != Cfg<6, 2>::NT || v.sk != Cfg<6, 2>::SK)) return (int)hipErrorInvalidValue;
     hipError_t e = hipErrorInvalidValue;
     const bool h = p.g.x_f16 != 0;
-#define MHC_GROUP(NV, AV, KV) (h ? launch_group<NV, AV, KV, true>(p, k, st, events) \
-                                 : launch_group<NV, AV, KV, false>(p, k, st, events))
+#define MHC_GROUP(NV, AV, KV) (h ? launch_group<NV, AV, KV, true>(p, k, st, events, phiT) \
+                                 : launch_group<NV, AV, KV, false>(p, k, st, events, phiT))
     if (n == 4 && na == 3 && nks == 16) e = MHC_GROUP(4, 3, 16);
     else if (n == 4 && na == 2 && nks == 32) e = MHC_GROUP(4, 2, 32);
     else if (n == 4 && na == 2 && nks == 16) e = MHC_GROUP(4, 2, 16);
