@@ -45,6 +45,9 @@ KERNEL_NAMES = {"pack": "prepack_kernel", "projection": "proj_kernel",
                 "epilogue": "epilogue_kernel", "hin": "hin_kernel"}
 # the single-read path runs one kernel in the projection stage and none in the hIn stage
 KERNEL_NAMES_SINGLE_READ = dict(KERNEL_NAMES, projection="fused_kernel", hin="(none)")
+# the one-launch path of a few tokens: one kernel, timed as the projection stage
+KERNEL_NAMES_ONE_LAUNCH = dict(pack="(none)", projection="decode_kernel", epilogue="(none)", hin="(none)")
+PATH_NAMES = {0: "four-kernel", 1: "single-read", 2: "one-launch"}
 
 
 def algorithmic_bytes(wl, *, intermediates: bool) -> int:
@@ -68,7 +71,7 @@ def algorithmic_bytes(wl, *, intermediates: bool) -> int:
     return b
 
 
-def stage_bytes(wl, stage: str, single_read: bool = False) -> int:
+def stage_bytes(wl, stage: str, single_read: bool = False, one_launch: bool = False) -> int:
     """Algorithmic bytes of one launch of a kernel: what that step of the method must
     read and write once. Intermediates of this implementation (packed weights, partial
     records, the hIn weights, the values exchanged between workgroups) are not counted.
@@ -78,9 +81,13 @@ def stage_bytes(wl, stage: str, single_read: bool = False) -> int:
                   single-read kernel writes hIn too (2D per token)
       epilogue    the per-token outputs: hPost, hRes, and the requested intermediates
       hin         x read once and hIn written once (2K + 2D per token); nothing on the
-                  single-read path"""
+                  single-read path
+    On the one-launch path the projection stage's kernel is the whole call
+    (algorithmic_bytes) and the other stages launch nothing."""
     T, n, D, M, it = wl.T, wl.n, wl.D, wl.M, wl.num_iters
     K = n * D
+    if one_launch:
+        return algorithmic_bytes(wl, intermediates=wl.need_backward) if stage == "projection" else 0
     if stage == "pack":
         return M * K * 4 + (K * 4 if wl.gamma else 0)
     if stage == "projection":
@@ -370,7 +377,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph-replays", type=int, default=0,
                     help="after the timed steps, capture one step into a HIP graph and report "
-                         "its per-replay time over this many replays (four-kernel path only)")
+                         "its per-replay time over this many replays")
+    ap.add_argument("--prepacked-calls", type=int, default=0,
+                    help="after the timed steps, time this many back-to-back calls with weights "
+                         "packed once beforehand (mhc_pre_prepack), as a serving loop calls it")
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="size of the write that evicts the Infinity Cache before each step of the "
                          "per-kernel pass (0: none; decode never flushes)")
@@ -419,8 +429,9 @@ def main():
                          need_backward=wl.need_backward, device=dev)
     out = run.alloc_outputs()
     stream = torch.cuda.current_stream(dev)
-    single_read = run.path(pre_mix is not None) == 1
-    names = KERNEL_NAMES_SINGLE_READ if single_read else KERNEL_NAMES
+    path = run.path(pre_mix is not None)
+    single_read, one_launch = path == 1, path == 2
+    names = KERNEL_NAMES_ONE_LAUNCH if one_launch else KERNEL_NAMES_SINGLE_READ if single_read else KERNEL_NAMES
 
     if args.calib_copy_mib > 0:
         print(f"[bench] calibration copy {args.calib_copy_mib} MiB", file=sys.stderr, flush=True)
@@ -441,13 +452,13 @@ def main():
     ms_step = elapsed * 1e3 / args.steps
     waits_timed_out = run.wait_status()
     if waits_timed_out:
-        print("[bench] WARNING: a single-read wait gave up (its tokens hold NaN)", file=sys.stderr, flush=True)
+        print("[bench] WARNING: a kernel's wait gave up (its tokens hold NaN)", file=sys.stderr, flush=True)
 
     # per-kernel durations: a second pass of K steps with HIP events on the launch stream;
     # one set of events per step, each recorded once here so that its HIP event exists
     # before the library records it. Boundaries around a stage that launches nothing (the
-    # pack and hIn stages of the single-read path) are not recorded: each record costs a
-    # few microseconds on the stream. Before each step (outside its events) a 512 MiB
+    # pack and hIn stages of the single-read path; all but the one kernel of the one-launch
+    # path) are not recorded: each record costs a few microseconds on the stream. Before each step (outside its events) a 512 MiB
     # write evicts the Infinity Cache, except for decode (launch-bound, back to back).
     flush = None
     if args.flush_mib > 0 and wl.name != "decode":
@@ -455,6 +466,8 @@ def main():
     wanted = [True] * mhc.FORWARD_EVENTS
     if single_read:
         wanted[0] = wanted[-1] = False
+    if one_launch:
+        wanted = [False, True, True, False, False]
     evs = [[torch.cuda.Event(enable_timing=True) if w else None for w in wanted]
            for _ in range(args.steps)]
     for row in evs:
@@ -476,13 +489,13 @@ def main():
     for i, stage in enumerate(mhc.STAGES):
         if not (wanted[i] and wanted[i + 1]):
             kernels[stage] = {"kernel": names[stage], "avg_us": 0.0, "min_us": 0.0,
-                              "algorithmic_bytes": stage_bytes(wl, stage, single_read),
+                              "algorithmic_bytes": stage_bytes(wl, stage, single_read, one_launch),
                               "note": "launches nothing on this path; not recorded"}
             continue
         ms = [row[i].elapsed_time(row[i + 1]) for row in evs]
         kernels[stage] = {"kernel": names[stage], "avg_us": 1e3 * sum(ms) / len(ms),
                           "min_us": 1e3 * min(ms),
-                          "algorithmic_bytes": stage_bytes(wl, stage, single_read)}
+                          "algorithmic_bytes": stage_bytes(wl, stage, single_read, one_launch)}
     first, last = wanted.index(True), len(wanted) - 1 - wanted[::-1].index(True)
     call_us = [1e3 * row[first].elapsed_time(row[last]) for row in evs]
     dom = max(kernels, key=lambda s: kernels[s]["avg_us"])
@@ -509,7 +522,7 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "n": wl.n, "D": wl.D, "n_alpha": wl.n_alpha,
                    "gamma": wl.gamma, "pre_mix": wl.pre_mix, "need_backward": wl.need_backward,
                    "num_iters": wl.num_iters,
-                   "path": "single-read" if single_read else "four-kernel",
+                   "path": PATH_NAMES[path],
                    "step": "weight pack + forward (one mhc_pre_forward call, unpacked phi)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -524,7 +537,24 @@ def main():
                  "frac": b_call / (call_avg * 1e-6) / 1e9 / HBM_PEAK_GBS},
         "kernels": kernels,
     }
-    if args.graph_replays > 0 and not single_read:
+    if args.prepacked_calls > 0:
+        # serving-loop form: weights packed once, then back-to-back calls, HIP events around
+        # all of them on the launch stream (outside the timed region)
+        print(f"[bench] prepacked calls {args.prepacked_calls}", file=sys.stderr, flush=True)
+        pk = run.prepack(phi, gamma)
+        for _ in range(10):
+            run(x, None, alpha, bias, None, pre_mix, phi_packed=pk, out=out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.prepacked_calls):
+            run(x, None, alpha, bias, None, pre_mix, phi_packed=pk, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        waits_timed_out |= run.wait_status()
+        line["waits_timed_out"] = waits_timed_out
+        us = 1e3 * e0.elapsed_time(e1) / args.prepacked_calls
+        line["prepacked"] = {"calls": args.prepacked_calls, "us_per_call": us, "tokens_per_s": wl.T / (us * 1e-6)}
+    if args.graph_replays > 0:
         # launch-bound sizes: the same step replayed from a captured graph (outside the
         # timed region)
         print(f"[bench] graph replays {args.graph_replays}", file=sys.stderr, flush=True)

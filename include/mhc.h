@@ -157,7 +157,8 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
  * least mhc_pre_workspace_size bytes, 256-byte aligned, zero-filled before its first use.
  * When tensors->phi_packed is NULL the weights are packed from phi (and gamma): by a pack
  * kernel into the workspace on the four-kernel path, inside the kernel on the single-read
- * path. Then one of two kernel sequences (mhc_pre_forward_path tells which):
+ * and one-launch paths. Then one of three kernel sequences (mhc_pre_forward_path tells
+ * which):
  *   four-kernel path: a projection kernel (which with pre_mix also writes hIn), a
  *     per-token epilogue and, without pre_mix, an hIn kernel (x is read twice);
  *   single-read path (n == 4, n_alpha == 3, no pre_mix, 992 < D <= 7168 (32 to 224
@@ -167,12 +168,19 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
  *     each other, each wait bounded: it needs every compute unit of an XCD at once, as an
  *     otherwise idle device gives; a wait that times out (other work holding compute
  *     units that long) leaves NaN in hIn for the tokens concerned, which
- *     mhc_pre_wait_status reports. Both paths can be captured into a HIP graph.
- * The two paths sum the projection's partial products in different groupings, so their
+ *     mhc_pre_wait_status reports;
+ *   one-launch path (n == 4, n_alpha == 3, no pre_mix, T <= 64, the device able to hold
+ *     ceil(D / 32) workgroups of 256 threads at once): the whole forward in one kernel,
+ *     one workgroup per block of 32 positions; its workgroups meet at two device-wide
+ *     barriers (bounded waits, as above: a time-out leaves every output NaN, or only hIn
+ *     when it comes at the second barrier, and mhc_pre_wait_status reports it).
+ * Every path can be captured into a HIP graph.
+ * The paths sum the projection's partial products in different groupings, so their
  * outputs may differ in the last bits; each meets the same accuracy. Within a call, hIn
  * uses exactly the hPre it emits. Results are bitwise reproducible for the same inputs,
  * parameters and path. The environment variable MHC_FORWARD_PATH = "classic" or
- * "fused" (for tests) overrides the choice where the single-read kernel can run.
+ * "fused" (for tests) overrides the choice: "classic" the four-kernel path, "fused" the
+ * single-read kernel where its geometry allows it (neither then takes the one-launch path).
  * Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
 mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
                            void* workspace, size_t workspace_bytes, void* stream);
@@ -193,15 +201,17 @@ mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* 
 mhc_status mhc_pre_forward_noalloc(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
                                    void* stream);
 
-/* Whether a single-read forward that used `workspace` has given up one of its waits since
- * the last report. The single-read kernel's workgroups wait for values other workgroups of
- * their group publish; each wait is bounded (about 0.3 s of polling), and one that gives up
- * leaves NaN in the hIn and hPre of the tokens concerned (mhc_pre_forward has already
+/* Whether a single-read or one-launch forward that used `workspace` has given up one of
+ * its waits since the last report. The single-read kernel's workgroups wait for values
+ * other workgroups of their group publish, the one-launch kernel's for every workgroup at
+ * its two barriers; each wait is bounded (about 0.3 s of polling), and one that gives up
+ * leaves NaN in outputs of the tokens concerned (mhc_pre_forward has already
  * returned MHC_OK by then: it is asynchronous). This call synchronises `stream` (the stream
  * those forwards ran on; NULL = the default stream), then sets *timed_out to 1 if the
  * workspace's time-out flag is set, else 0, and clears the flag. In normal operation the
- * waits end by construction and the flag stays 0; it can be set when the workgroups of one
- * XCD cannot all run at once (another workload holding compute units for that long).
+ * waits end by construction and the flag stays 0; it can be set when the workgroups that
+ * wait for each other cannot all run at once (another workload holding compute units for
+ * that long).
  *   workspace        the forward's workspace (>= 256 bytes, 256-byte aligned)
  *   workspace_bytes  its size
  * Errors: NULLPTR (workspace or timed_out), PARAM_INVALID (workspace too small or
@@ -209,7 +219,8 @@ mhc_status mhc_pre_forward_noalloc(const mhc_pre_params* params, const mhc_pre_t
 mhc_status mhc_pre_wait_status(void* workspace, size_t workspace_bytes, void* stream, int32_t* timed_out);
 
 /* Which path mhc_pre_forward would take for these parameters on the current device:
- * *path = 1 the single-read kernel, 0 the four-kernel path (has_pre_mix: whether pre_mix
+ * *path = 2 the one-launch kernel, 1 the single-read kernel, 0 the four-kernel path
+ * (has_pre_mix: whether pre_mix
  * will be given). Errors: NULLPTR, PARAM_INVALID. */
 mhc_status mhc_pre_forward_path(const mhc_pre_params* params, int32_t has_pre_mix, int32_t* path);
 
@@ -225,8 +236,9 @@ mhc_status mhc_pre_forward_path(const mhc_pre_params* params, int32_t has_pre_mi
  *   events[3] after the per-token epilogue kernel,
  *   events[4] after the hIn kernel.
  * A kernel the call does not launch (the pack when phi_packed is given or on the
- * single-read path, which packs inside its kernel; the hIn kernel when pre_mix is given
- * or on the single-read path: the projection writes hIn then) has its two events recorded
+ * single-read and one-launch paths, which pack inside their kernel; the epilogue and hIn
+ * kernels on the one-launch path; the hIn kernel when pre_mix is given or on the
+ * single-read path: the projection writes hIn then) has its two events recorded
  * back to back, so elapsed time between events[i] and events[i+1] is kernel i's duration
  * (plus the launch gap) whatever the inputs; with T == 0 all five are recorded back to
  * back. A NULL entry is not recorded: a caller that only wants some boundaries (each

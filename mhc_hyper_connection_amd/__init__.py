@@ -39,7 +39,12 @@ def _ptr(t):
 
 
 def _stream(device):
+    # torch's current stream on `device` as a raw handle (the direct getter: a fraction of
+    # the cost of building a torch.cuda.Stream object on every call)
     torch = _torch()
+    getter = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if getter is not None and device.index is not None:
+        return ctypes_void(getter(device.index))
     return ctypes_void(torch.cuda.current_stream(device).cuda_stream)
 
 
@@ -53,11 +58,11 @@ def _check(t, name, dtype, shape, device):
         return
     if t.dtype != dtype:
         raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if t.device != device:
+    if t.get_device() != (device.index if device.type == "cuda" else -1):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
@@ -88,12 +93,13 @@ class PreForward:
         self.workspace = torch.zeros(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
 
     def path(self, has_pre_mix=False):
-        """1 when calls take the single-read kernel on this device, else 0."""
+        """2 when calls take the one-launch kernel on this device, 1 the single-read kernel,
+        0 the four-kernel path."""
         return forward_path(self.params, has_pre_mix)
 
     def wait_status(self):
-        """mhc_pre_wait_status on this launcher's workspace: 1 if a single-read wait gave up
-        since the last query (its tokens then hold NaN), else 0. Synchronises the current
+        """mhc_pre_wait_status on this launcher's workspace: 1 if a wait of the single-read
+        or one-launch kernel gave up since the last query (its tokens then hold NaN), else 0. Synchronises the current
         stream; clears the flag."""
         return raw_wait_status(_ptr(self.workspace), self.workspace.numel(), _stream(self.device))
 

@@ -171,6 +171,8 @@ mhc_status forward_impl(const mhc_pre_params* params, const mhc_pre_tensors* t,
     a.rec = reinterpret_cast<float*>(ws + plan.off_rec);
     a.prx = plan.fused_geom ? reinterpret_cast<uint64_t*>(ws + plan.off_prx) : nullptr;
     a.hpx = plan.fused_geom ? reinterpret_cast<uint64_t*>(ws + plan.off_hpx) : nullptr;
+    a.dpart = plan.decode_geom ? reinterpret_cast<uint64_t*>(ws + plan.off_dpart) : nullptr;
+    a.dhp = plan.decode_geom ? reinterpret_cast<uint64_t*>(ws + plan.off_dhp) : nullptr;
     a.sync = reinterpret_cast<uint32_t*>(ws + plan.off_sync);
     a.num_iters = params->num_iters;
     a.norm_eps = params->norm_eps;

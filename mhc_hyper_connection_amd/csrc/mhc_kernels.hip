@@ -39,6 +39,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "mhc_device.h"
 #include "mhc_plan.h"
@@ -599,20 +600,19 @@ __device__ __forceinline__ float sk_col_sum(float v, int c)
 // one lane per matrix entry, 2*num_iters steps, every plane stored. A matrix takes SW
 // consecutive lanes (N*N, or a whole wave for n = 6); a lane past the N*N entries of
 // its matrix computes along and stores nothing.
-template <int N>
-__device__ void sinkhorn(const KArgs& k, const float* Ls, int64_t tfirst, int nb)
+// THREADS consecutive threads (tid = 0 .. THREADS - 1) take part; T sizes the plane arrays.
+template <int N, int THREADS>
+__device__ void sinkhorn_by(const ForwardArgs& a, int64_t T, const float* Ls, int64_t tfirst, int nb, int tid)
 {
     constexpr int NN = N * N;
     constexpr int SW = 64 % NN == 0 ? NN : 64;
-    static_assert(kThreads % SW == 0, "a pass is whole matrices");
-    const ForwardArgs& a = k.a;
-    const int tid = threadIdx.x;
+    static_assert(THREADS % SW == 0, "a pass is whole matrices");
     const int e = tid % SW;
     const bool used = SW == NN || e < NN;
     const int r = used ? e / N : 0, c = used ? e % N : 0;
     const float eps = (float)a.hc_eps;
     const int steps = 2 * a.num_iters;
-    for (int base = 0; base < nb * SW; base += kThreads) {
+    for (int base = 0; base < nb * SW; base += THREADS) {
         const int q = (base + tid) / SW;
         const bool live = used && q < nb;
         const int64_t t1 = tfirst + base / SW;   // first token of this pass
@@ -631,18 +631,23 @@ __device__ void sinkhorn(const KArgs& k, const float* Ls, int64_t tfirst, int nb
             }
             // this pass's tokens of plane `step`; lanes past them fall outside the range
             if (a.sum_out) {
-                const rsrc_t rs = make_rsrc(a.sum_out + ((int64_t)step * k.T + t1) * N, (int64_t)nlive * N * 4);
+                const rsrc_t rs = make_rsrc(a.sum_out + ((int64_t)step * T + t1) * N, (int64_t)nlive * N * 4);
                 const bool writer = used && ((step & 1) ? (r == 0) : (c == 0));
                 if (writer) st_buf(rs, (uint32_t)(qq * N + ((step & 1) ? c : r)) * 4, sum);
             }
             if (a.norm_out) {
-                const rsrc_t rn = make_rsrc(a.norm_out + ((int64_t)step * k.T + t1) * NN, (int64_t)nlive * NN * 4);
+                const rsrc_t rn = make_rsrc(a.norm_out + ((int64_t)step * T + t1) * NN, (int64_t)nlive * NN * 4);
                 if (used) st_buf(rn, (uint32_t)(qq * NN + e) * 4, v);
             }
         }
         const rsrc_t rh = make_rsrc(a.h_res + t1 * NN, (int64_t)nlive * NN * 4);
         if (used) st_buf(rh, (uint32_t)(qq * NN + e) * 4, v);
     }
+}
+template <int N>
+__device__ void sinkhorn(const KArgs& k, const float* Ls, int64_t tfirst, int nb)
+{
+    sinkhorn_by<N, kThreads>(k.a, k.T, Ls, tfirst, nb, (int)threadIdx.x);
 }
 
 // ------------------------------------------------------------------ epilogue
@@ -1350,6 +1355,405 @@ fused_kernel(FArgs f)
     }
 }
 
+// ------------------------------------------------------------------ one-launch small-T forward
+
+struct DArgs {
+    ForwardArgs a;
+    int64_t T;
+    int64_t K;
+    int D;
+    int nblk;
+};
+
+// v / s for the Sinkhorn's positive operands (v in [0, 2], s in [eps, 5]: no scaling
+// needed): the hardware reciprocal (1 ulp), the quotient, and one Newton correction of it
+// from its exact fma residual; within an ulp of the correctly rounded quotient, and equal
+// to it in almost every case, in four dependent operations instead of the ten of a full
+// IEEE division.
+__device__ __forceinline__ float div_pos(float v, float s)
+{
+    const float r = __builtin_amdgcn_rcpf(s);
+    const float q = v * r;
+    return fmaf(fmaf(-q, s, v), r, q);
+}
+
+// The Sinkhorn of one token's 4 x 4 residual logits Ls[0 .. 15] (the steps of sinkhorn_by,
+// its sums in the same order, its divisions by div_pos), entry (r, c) in lane 4 r + c of a
+// 16-lane group; `live` false: the group computes along and stores nothing. PLANES: sum_out
+// and norm_out of every step are stored too.
+template <bool PLANES>
+__device__ __forceinline__ void sinkhorn4(const ForwardArgs& a, int64_t T, const float* Ls, int64_t tk, bool live, int e)
+{
+    constexpr int N = 4, NN = 16;
+    const int r = e >> 2, c = e & 3;
+    const float eps = (float)a.hc_eps;
+    const int iters = a.num_iters;
+    auto planes = [&](int step, float sum, float v, bool col) {
+        if (!PLANES || !live) return;
+        if (a.sum_out && (col ? r == 0 : c == 0)) a.sum_out[((int64_t)step * T + tk) * N + (col ? c : r)] = sum;
+        if (a.norm_out) a.norm_out[((int64_t)step * T + tk) * NN + e] = v;
+    };
+    float v = live ? Ls[e] : 0.f;
+    const float mx = row_max<N>(v);
+    const float ex = expf(v - mx);
+    float sum = row_sum<N>(ex);
+    v = div_pos(ex, sum) + eps;
+    if (iters > 0) planes(0, sum, v, false);
+    for (int k = 0; k < iters; ++k) {
+        sum = col_sum<N>(v) + eps;             // step 2k + 1: columns
+        v = div_pos(v, sum);
+        planes(2 * k + 1, sum, v, true);
+        if (k + 1 < iters) {
+            sum = row_sum<N>(v) + eps;         // step 2k + 2: rows
+            v = div_pos(v, sum);
+            planes(2 * k + 2, sum, v, false);
+        }
+    }
+    if (live) a.h_res[tk * NN + e] = v;
+}
+
+// The whole forward of up to kDecodeTokens tokens in one launch (n = 4, alpha[3]): workgroup
+// b owns d-block b (32 positions of each stream).
+//   Phase 1: its weights into LDS (copied from phi_packed, or split from phi and gamma as
+//   the pack kernel splits them), x of every token for its block into registers (wave w:
+//   tokens 16 w .. 16 w + 15), the projection and the squares on the matrix cores, and the
+//   block's partial record of every token to the workspace.
+//   Phase 2, workgroups b < T, for tokens b, b + nblk, ..: the token's records summed over
+//   the blocks (fp64: in block order within each of 10 partitions, then the partitions in
+//   order), then the per-token math of the epilogue kernel (hMix, invRms, hPre, hPost), hPre
+//   to the workspace, and the Sinkhorn planes and hRes (on one wave while the others go on).
+//   Phase 3: hIn of the block from the x registers, once every token's hPre is there.
+// The records and hPre cross workgroups (and XCDs, whose L2 caches are not coherent with
+// each other) as tagged words: value and the call's tag in one 64-bit word, stored and
+// loaded as device-scope atomics, and a reader polls a word until it carries this call's
+// tag. No barrier and no fence at device scope (on this GPU such a fence writes back or
+// invalidates a whole L2). The tag comes from flag word b, which only workgroup b reads
+// and writes, adding 1 per call to flags b, b + nblk, .. (all kDecodeMaxBlocks of them):
+// every flag holds the same count at the start of a call, whatever the grids of earlier
+// calls, so every workgroup derives the same tag, and a word of an earlier call never
+// carries it. The polls are bounded: a time-out sets sync[1] and the outputs that depend
+// on it are NaN (all of the token's at a record, hIn at an hPre). Workgroups wait on each
+// other, so all nblk of them must be resident at once: the path is taken only where the
+// device holds them.
+template <int N, int A, bool NeverReady>
+__global__ void __launch_bounds__(kThreads)
+decode_kernel(DArgs f)
+{
+    using C = Cfg<N, A>;
+    constexpr int M = C::M, NT = C::NT, NC = C::NC, NN = C::NN, NCL = 3 * M;
+    constexpr int R = M + 1;                        // record values: n pre sums, the square, M - n sums
+    constexpr int RS = kDecodeRecWords;             // record stride in words (R and a pad word)
+    static_assert(RS == R + 1 && RS % 2 == 0, "record layout: whole 16-byte chunks");
+    static_assert(N == 4 && A == 3 && NT == 5 && NCL == 72, "the single-read kernel's column pairing");
+    static_assert(kDecodeTokens == 4 * 16, "one matrix row per token, 16 per wave");
+    constexpr int MP = 32;
+    constexpr int NPART = 10;                       // partitions of the block sum
+    constexpr int BATCH = 32;                       // record words in flight per thread
+    static_assert(NPART * R <= kThreads, "one thread per (partition, value)");
+    __shared__ u32x4 wl[N * 4 * NCL];               // the block's packed weights
+    __shared__ float part[4][16][MP];               // each wave's row sums
+    __shared__ float part_sq[4][16];
+    __shared__ double red[NPART][R];
+    __shared__ float Ls[kDecodeTokens * NN];        // residual logits of this workgroup's tokens
+    __shared__ float gpar[3 + M];                   // alpha, bias
+    __shared__ u32x4 xs[64][N];                     // wave 3's x while it runs the Sinkhorn
+    __shared__ uint32_t sh_epoch;
+    __shared__ int sh_bad;
+    const ForwardArgs& a = f.a;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int j = lane & 15, grp = lane >> 4;
+    const int b = blockIdx.x;
+    const int nblk = f.nblk;
+    uint32_t* const flags = a.sync + kDecodeFlag0;
+    uint64_t* const rec = reinterpret_cast<uint64_t*>(a.dpart);
+    uint64_t* const hpw = reinterpret_cast<uint64_t*>(a.dhp);
+
+    if (tid == 0) sh_epoch = __hip_atomic_load(flags + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) sh_bad = 0;
+    if (tid < A) gpar[tid] = a.alpha[tid];
+    if (tid < M) gpar[3 + tid] = a.bias[tid];
+
+    // phase 1: x (first: the longest wait), weights, projection
+    const int t = 16 * wave + j;                     // the lane's token
+    const bool wave_live = 16 * wave < f.T;          // the wave has tokens
+    const bool oct_ok = kBlock * b + 8 * grp < f.D;
+    const rsrc_t xres = make_rsrc(a.x, f.T * f.K * 2);
+    u32x4 xr[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t off = oct_ok && t < f.T ? (uint32_t)(((int64_t)t * f.K + (int64_t)i * f.D + kBlock * b + 8 * grp) * 2)
+                                               : kOutOfRange;
+        xr[i] = __builtin_amdgcn_raw_buffer_load_b128(xres, (int)off, 0, 0);
+    }
+    constexpr int WU = N * 4 * NCL;                  // 16-byte weight units of the block
+    if (a.packed) {
+        // every load issued before the first LDS store
+        constexpr int PER = (WU + kThreads - 1) / kThreads;
+        const u32x4* src = static_cast<const u32x4*>(a.packed) + (int64_t)b * N * 4 * NC;
+        u32x4 wv[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int u = tid + k * kThreads;
+            if (u < WU) wv[k] = src[(int64_t)(u / NCL) * NC + u % NCL];
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int u = tid + k * kThreads;
+            if (u < WU) wl[u] = wv[k];
+        }
+    } else {
+        // (phi row m, K-step kk, octet og) items: their phi and gamma loads first, then the splits
+        constexpr int PER = (N * 4 * M + kThreads - 1) / kThreads;
+        float pv[PER][8], gv[PER][8];
+        // an item's 8 weights (and gammas) are consecutive and start at a multiple of 8
+        // elements: two 16-byte loads each where the arrays are 16-byte aligned
+        const bool vec = ((reinterpret_cast<uintptr_t>(a.phi) | reinterpret_cast<uintptr_t>(a.gamma)) & 15) == 0;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int it = tid + k * kThreads;
+            const int m = it % M, row = it / M, kk = row / 4, og = row % 4;
+            const int d = kBlock * b + 8 * og;
+            const bool live = it < N * 4 * M && d < f.D;
+            const int64_t k0 = (int64_t)kk * f.D + d;
+            if (vec) {
+                const float4 z = {0.f, 0.f, 0.f, 0.f}, o = {1.f, 1.f, 1.f, 1.f};
+                const float4* pp4 = reinterpret_cast<const float4*>(a.phi + (int64_t)m * f.K + k0);
+                const float4* gp4 = reinterpret_cast<const float4*>(a.gamma + k0);
+                const float4 p0 = live ? pp4[0] : z, p1 = live ? pp4[1] : z;
+                const float4 g0 = live && a.gamma ? gp4[0] : o, g1 = live && a.gamma ? gp4[1] : o;
+                pv[k][0] = p0.x; pv[k][1] = p0.y; pv[k][2] = p0.z; pv[k][3] = p0.w;
+                pv[k][4] = p1.x; pv[k][5] = p1.y; pv[k][6] = p1.z; pv[k][7] = p1.w;
+                gv[k][0] = g0.x; gv[k][1] = g0.y; gv[k][2] = g0.z; gv[k][3] = g0.w;
+                gv[k][4] = g1.x; gv[k][5] = g1.y; gv[k][6] = g1.z; gv[k][7] = g1.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pv[k][e] = live ? a.phi[(int64_t)m * f.K + k0 + e] : 0.f;
+                    gv[k][e] = live && a.gamma ? a.gamma[k0 + e] : 1.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int it = tid + k * kThreads;
+            if (it >= N * 4 * M) continue;
+            const int m = it % M, row = it / M;      // row = K-step * 4 + octet
+            u32x4 w3[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const double p = a.gamma ? (double)pv[k][e] * (double)gv[k][e] : (double)pv[k][e];
+                uint32_t tb[3];
+                split3(p, tb);
+#pragma unroll
+                for (int term = 0; term < 3; ++term) w3[term][e >> 1] |= tb[term] << (16 * (e & 1));
+            }
+#pragma unroll
+            for (int term = 0; term < 3; ++term) wl[row * NCL + term * M + m] = w3[term];
+        }
+    }
+    __syncthreads();   // the weights, parameters and epoch are in LDS
+    const uint32_t epoch = sh_epoch;
+    const uint32_t tag = 2u * epoch + 1u;            // odd: never the zero of a fresh workspace
+    const uint32_t want = NeverReady ? tag ^ 0x40000000u : tag;
+    if (wave_live) {
+        f32x4 acc[NT];
+        f32x4 sq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const u32x4* wb = wl + i * 4 * NCL + grp * NCL;
+            const bf16x8 Av = __builtin_bit_cast(bf16x8, xr[i]);
+            sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Av, sq, 0, 0, 0);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int col = 16 * nt + j < NCL ? 16 * nt + j : 16 * nt + j - 16;
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, __builtin_bit_cast(bf16x8, wb[col]), acc[nt], 0, 0, 0);
+            }
+        }
+        // phi row m's hi, mid and lo are columns m, M + m, 2M + m (as in the single-read kernel)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int tt = 4 * grp + q;
+            const float m1 = dpp<kRowRor8>(acc[1][q]), m2 = dpp<kRowRor8>(acc[2][q]);
+            part[wave][tt][j] = (acc[0][q] + (j < 8 ? m1 : m2)) + acc[3][q];
+            part[wave][tt][16 + j] = (acc[1][q] + m2) + acc[4][q];   // j >= 8: padding
+        }
+        const int rr = j - 4 * grp;
+        if (rr >= 0 && rr < 4) part_sq[wave][j] = sq[rr];
+    }
+    __syncthreads();
+    // the block's partial record of every token ([token][block][word]: a token's records
+    // are one run): word w < n the pre sums, n the square, n + 1 + i the sum of phi row n + i,
+    // then a pad word (zero). All LDS reads first, then the stores.
+    const int T32 = (int)f.T;
+    {
+        constexpr int PER = (int)((kDecodeTokens * RS + kThreads - 1) / kThreads);
+        float val[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int idx = tid + k * kThreads;
+            const int tk = idx / RS, w = idx - tk * RS;
+            const int tq = tk < T32 ? tk : 0;
+            val[k] = w < N ? part[tq >> 4][tq & 15][w] : w == N ? part_sq[tq >> 4][tq & 15]
+                   : w < R ? part[tq >> 4][tq & 15][w - 1] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int idx = tid + k * kThreads;
+            const int tk = idx / RS, w = idx - tk * RS;
+            if (tk < T32) put_tagged(rec + (tk * nblk + b) * RS + w, tag, val[k]);
+        }
+    }
+
+    // phase 2: the tokens of this workgroup
+    const int ntok = b < T32 ? (T32 - b + nblk - 1) / nblk : 0;
+    const float eps = (float)a.hc_eps;
+    for (int q = 0; q < ntok; ++q) {
+        const int tk = b + q * nblk;
+        // first word 0 of every block's record (one poll word per block: light traffic while
+        // the records land), then every word, each checked again
+        {
+            bool bad = false;
+            for (int i = tid; i < nblk; i += kThreads) {
+                const uint64_t* p = rec + (tk * nblk + i) * RS;
+                int it = 0;
+                for (; it < kSpinLimit && !tag_is(get_tagged(p), want); ++it) __builtin_amdgcn_s_sleep(1);
+                bad = bad || it == kSpinLimit;
+            }
+            if (bad) sh_bad = 1;
+        }
+        __syncthreads();
+        // thread (pp, v): the words v of the blocks of partition pp, in block order, fp64
+        const int pp = tid / R, v = tid % R;
+        if (pp < NPART && !sh_bad) {
+            const int lo = pp * nblk / NPART, hi = (pp + 1) * nblk / NPART;
+            const uint64_t* src = rec + tk * nblk * RS + v;
+            double sacc = 0.0;
+            bool bad = false;
+            for (int b0 = lo; b0 < hi; b0 += BATCH) {
+                const int nb = hi - b0 < BATCH ? hi - b0 : BATCH;
+                uint64_t w[BATCH];
+#pragma unroll
+                for (int e = 0; e < BATCH; ++e) w[e] = e < nb ? get_tagged(src + (b0 + e) * RS) : 0;
+                int it = 0;
+                for (; it < kSpinLimit; ++it) {
+                    bool all = true;
+#pragma unroll
+                    for (int e = 0; e < BATCH; ++e) all = all && (e >= nb || tag_is(w[e], want));
+                    if (all) break;
+                    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+                    for (int e = 0; e < BATCH; ++e)
+                        if (e < nb && !tag_is(w[e], want)) w[e] = get_tagged(src + (b0 + e) * RS);
+                }
+                bad = bad || it == kSpinLimit;
+#pragma unroll
+                for (int e = 0; e < BATCH; ++e) sacc += e < nb ? (double)tagged_value(w[e]) : 0.0;   // + 0: exact
+            }
+            red[pp][v] = sacc;
+            if (bad) sh_bad = 1;
+        }
+        __syncthreads();
+        if (tid == 0 && sh_bad) __hip_atomic_store(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid < R) {
+            double tot = 0.0;
+#pragma unroll
+            for (int k = 0; k < NPART; ++k) tot += red[k][tid];
+            red[0][tid] = sh_bad ? __builtin_nan("") : tot;
+        }
+        __syncthreads();
+        // the epilogue kernel's per-token math
+        if (tid < M) {
+            const int m = tid;
+            const double inv = inv_rms_of(red[0][N], (double)f.K, a.norm_eps);
+            const double h = red[0][m < N ? m : m + 1];
+            if (a.h_mix) a.h_mix[tk * M + m] = (float)h;
+            if (m == 0 && a.inv_rms) a.inv_rms[tk] = (float)inv;
+            if (m < N) {
+                const float hv = gate_pre(h, inv, gpar[0], gpar[3 + m], eps);
+                if (a.h_pre) a.h_pre[tk * N + m] = hv;
+                put_tagged(hpw + tk * N + m, tag, hv);
+            } else if (m < 2 * N) {
+                a.h_post[tk * N + m - N] = gate_post(h, inv, gpar[1], gpar[3 + m], eps, false);
+            } else {
+                Ls[q * NN + (m - 2 * N)] = res_logit(h, inv, gpar[2], gpar[3 + m]);
+            }
+        }
+    }
+    // the Sinkhorn planes and hRes, one token per 16-lane group: up to 4 tokens all on wave
+    // 3, which hands its x to wave 0 for hIn first; more tokens on every wave
+    const bool one_wave = ntok > 0 && ntok <= 4;
+    if (one_wave && wave == 3) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) xs[lane][i] = xr[i];
+    }
+    if (ntok > 0) {
+        __syncthreads();   // Ls, xs
+        const bool planes = a.sum_out || a.norm_out;
+        if (!one_wave || wave == 3) {
+            for (int q0 = one_wave ? 0 : 4 * wave; q0 < ntok; q0 += one_wave ? 4 : 16) {
+                const int q = q0 + grp;
+                const bool live = q < ntok;
+                const float* L = Ls + (live ? q : 0) * NN;
+                if (planes) sinkhorn4<true>(a, f.T, L, b + q * nblk, live, j);
+                else sinkhorn4<false>(a, f.T, L, b + q * nblk, live, j);
+            }
+        }
+    }
+
+    // phase 3: hIn of the block, from the registers that hold its x (wave 0 also does wave
+    // 3's tokens from LDS when wave 3 runs the Sinkhorn)
+    auto hin_token = [&](int tt, const u32x4 (&xv)[N]) {
+        uint64_t w[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) w[i] = get_tagged(hpw + tt * N + i);
+        int it = 0;
+        for (; it < kSpinLimit; ++it) {
+            bool all = true;
+#pragma unroll
+            for (int i = 0; i < N; ++i) all = all && tag_is(w[i], want);
+            if (all) break;
+            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                if (!tag_is(w[i], want)) w[i] = get_tagged(hpw + tt * N + i);
+        }
+        const bool ok = it < kSpinLimit;
+        if (!ok) __hip_atomic_store(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float hacc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hacc[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const float wi = ok ? tagged_value(w[i]) : __builtin_nanf("");
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hacc[2 * e] = fmaf(wi, bf16_lo(xv[i][e]), hacc[2 * e]);
+                hacc[2 * e + 1] = fmaf(wi, bf16_hi(xv[i][e]), hacc[2 * e + 1]);
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(hacc[2 * e], hacc[2 * e + 1]);
+        const rsrc_t hres = make_rsrc(a.h_in, f.T * f.D * 2);
+        __builtin_amdgcn_raw_buffer_store_b128(o, hres, (int)(oct_ok ? (uint32_t)((tt * f.D + kBlock * b + 8 * grp) * 2) : kOutOfRange), 0, 0);
+    };
+    if (!(one_wave && wave == 3) && t < T32) hin_token(t, xr);
+    if (one_wave && wave == 0 && 48 + j < T32) {
+        u32x4 xv[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) xv[i] = xs[lane][i];
+        hin_token(48 + j, xv);
+    }
+    // this call's count into flags b, b + nblk, ..: the next call's epoch
+    if (wave == 0)
+        for (int v = b + nblk * lane; v < kDecodeMaxBlocks; v += nblk * 64)
+            __hip_atomic_store(flags + v, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Records events[i] (a caller-created hipEvent_t) on the stream when events is given and
 // its entry is not NULL.
 hipError_t mark(void* const* events, int i, hipStream_t st)
@@ -1400,21 +1804,48 @@ bool no_scratch(const void* fn)
     return hipFuncGetAttributes(&at, fn) == hipSuccess && at.localSizeBytes == 0;
 }
 
+// What the path choice needs to know of a device, found once per device (these queries
+// cost about a microsecond per call otherwise): its compute units, and for the single-read
+// and one-launch kernels whether their code keeps everything in registers and how many of
+// their workgroups a compute unit holds.
+struct DeviceFacts {
+    int cus = 0;
+    bool fused_ok = false;     // no scratch, at least one workgroup per compute unit
+    int decode_per_cu = 0;     // 0: the one-launch kernel cannot run here
+};
+constexpr int kMaxDevices = 64;
+
+const DeviceFacts* device_facts()
+{
+    static DeviceFacts facts[kMaxDevices];
+    static std::once_flag once[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(once[dev], [dev]() {
+        DeviceFacts f;
+        if (hipDeviceGetAttribute(&f.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) f.cus = 0;
+        int per_cu = 0;
+        f.fused_ok = no_scratch(reinterpret_cast<const void*>(fused_kernel<4, 3, false>)) &&
+                     no_scratch(reinterpret_cast<const void*>(fused_kernel<4, 3, true>)) &&
+                     hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<4, 3, false>, kFThreads, 0) == hipSuccess &&
+                     per_cu >= 1;
+        per_cu = 0;
+        if (no_scratch(reinterpret_cast<const void*>(decode_kernel<4, 3, false>)) &&
+            no_scratch(reinterpret_cast<const void*>(decode_kernel<4, 3, true>)) &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<4, 3, false>, kThreads, 0) == hipSuccess)
+            f.decode_per_cu = per_cu;
+        facts[dev] = f;
+    });
+    return &facts[dev];
+}
+
 // Groups of the single-read kernel on the current device (one per XCD, at most one per
 // tile), 0 when it cannot run here: the kernel needs kXcds XCDs of kFMembers compute units,
 // one workgroup on each, and code without scratch memory.
 int fused_groups(const Plan& p)
 {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (cus != kXcds * kFMembers) return 0;
-    if (!no_scratch(reinterpret_cast<const void*>(fused_kernel<4, 3, false>)) ||
-        !no_scratch(reinterpret_cast<const void*>(fused_kernel<4, 3, true>)))
-        return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<4, 3, false>, kFThreads, 0) != hipSuccess ||
-        per_cu < 1)
-        return 0;
+    const DeviceFacts* d = device_facts();
+    if (!d || d->cus != kXcds * kFMembers || !d->fused_ok) return 0;
     int64_t G = kXcds;
     if (G > p.tiles16) G = p.tiles16;
     return (int)G;
@@ -1427,6 +1858,41 @@ bool fused_wanted(const Plan& p, bool has_pre_mix)
     if (env && std::strcmp(env, "classic") == 0) return false;
     const bool forced = env && std::strcmp(env, "fused") == 0;
     return forced || p.T >= kFMinTokens;
+}
+
+// Whether the one-launch kernel serves this call on the current device: the geometry
+// admits it, no pre_mix, MHC_FORWARD_PATH does not ask for another path, code without
+// scratch memory, and the device holds all nblk workgroups at once.
+bool decode_wanted(const Plan& p, bool has_pre_mix)
+{
+    if (!p.decode_geom || has_pre_mix || p.T <= 0) return false;
+    const char* env = std::getenv("MHC_FORWARD_PATH");
+    if (env && (std::strcmp(env, "classic") == 0 || std::strcmp(env, "fused") == 0)) return false;
+    const DeviceFacts* d = device_facts();
+    return d && (int64_t)d->decode_per_cu * d->cus >= p.g.nblk;
+}
+
+hipError_t launch_decode(const Plan& p, const ForwardArgs& a, hipStream_t st, void* const* events)
+{
+    DArgs f;
+    f.a = a;
+    f.T = p.T;
+    f.K = p.g.K;
+    f.D = p.g.D;
+    f.nblk = p.g.nblk;
+    hipError_t e = mark(events, kStagePack + 1, st);
+    if (e != hipSuccess) return e;
+    // test hook, as for the single-read kernel: every barrier wait gives up at its limit
+    const char* never = std::getenv("MHC_TEST_EXCHANGE_NEVER_READY");
+    if (never && std::strcmp(never, "1") == 0)
+        hipLaunchKernelGGL((decode_kernel<4, 3, true>), dim3((unsigned)p.g.nblk), dim3(kThreads), 0, st, f);
+    else
+        hipLaunchKernelGGL((decode_kernel<4, 3, false>), dim3((unsigned)p.g.nblk), dim3(kThreads), 0, st, f);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark(events, kStageProj + 1, st);
+    if (e == hipSuccess) e = mark(events, kStageEpi + 1, st);
+    if (e == hipSuccess) e = mark(events, kStageHin + 1, st);
+    return e;
 }
 
 hipError_t launch_fused(const Plan& p, const ForwardArgs& a, int G, hipStream_t st, void* const* events)
@@ -1490,6 +1956,7 @@ static bool projection_on_valu(const Plan& p, const ForwardArgs& a)
 
 int forward_path(const Plan& p, bool has_pre_mix)
 {
+    if (decode_wanted(p, has_pre_mix)) return 2;
     return fused_wanted(p, has_pre_mix) && fused_groups(p) > 0 ? 1 : 0;
 }
 
@@ -1577,6 +2044,7 @@ int launch_forward(const Plan& p, const ForwardArgs& a_in, void* stream, void* c
     hipStream_t st = (hipStream_t)stream;
     ForwardArgs a = a_in;
     if (mark(events, kStagePack, st) != hipSuccess) return (int)hipErrorUnknown;
+    if (decode_wanted(p, a.pre_mix != nullptr)) return (int)launch_decode(p, a, st, events);   // packs in the kernel
     if (fused_wanted(p, a.pre_mix != nullptr)) {
         // unpacked weights are packed inside the kernel
         const int G = fused_groups(p);

@@ -78,6 +78,18 @@ constexpr int64_t kFMinTokens = 8192;  // below this the four-kernel path is use
 constexpr int kXcds = 8;               // XCDs (groups at most)
 constexpr int kTicket0 = 8;            // sync word of XCD 0's arrival counter (kXcds words)
 
+// One-launch forward of a few tokens (n = 4, alpha[3], no pre_mix): one workgroup per
+// d-block projects every token's x of its block, two grid-wide barriers separate the
+// blocks' partial records, the per-token math and hIn.
+constexpr int64_t kDecodeTokens = 64;  // tokens at most (4 waves x 16 matrix rows)
+constexpr int kDecodeMaxBlocks = kMaxD / kBlock;   // barrier flag words (one per possible d-block)
+constexpr int kDecodeFlag0 = 256;      // sync word of the first flag
+constexpr int kDecodeRecWords = 26;    // tagged words per partial record (n = 4, alpha[3]): M + 1 and a pad
+
+// The workspace's sync section: the call counter, the time-out flag, the per-XCD arrival
+// counters and the one-launch kernel's barrier flags, at the same offsets for every size.
+constexpr size_t kSyncBytes = 4096;
+
 struct Geometry {
     int n = 0;
     int D = 0;
@@ -181,6 +193,10 @@ struct Plan {
     int64_t tiles16 = 0;      // ceil(T / 16)
     // single-read kernel with XCD groups
     size_t off_prx = 0, off_hpx = 0, off_sync = 0;
+    // one-launch kernel of a few tokens: the geometry admits it; its partial records
+    // ([T][nblk][kDecodeRecWords] tagged 64-bit words) and hPre ([T][n] tagged words)
+    bool decode_geom = false;
+    size_t off_dpart = 0, off_dhp = 0;
     size_t off_packed = 0, off_wts = 0, off_rec = 0, ws_bytes = 0;
 };
 
@@ -212,7 +228,7 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     // the call counter first, at the same offset for every problem size
     size_t off = 0;
     p.off_sync = off;
-    off += 256;
+    off += kSyncBytes;
     p.off_packed = off;
     off = align_up(off + g.packed_bytes, 256);
     p.off_wts = off;
@@ -224,6 +240,13 @@ inline Plan make_plan(const Geometry& g, int64_t T)
         off = align_up(off + (size_t)p.tiles16 * p.FP * kFTok * (g.n + 1) * 8, 256);
         p.off_hpx = off;
         off = align_up(off + (size_t)p.tiles16 * kFTok * g.n * 8, 256);
+    }
+    p.decode_geom = g.n == 4 && g.n_alpha == 3 && !g.x_f16 && T <= kDecodeTokens;
+    if (p.decode_geom) {
+        p.off_dpart = off;
+        off = align_up(off + (size_t)T * g.nblk * kDecodeRecWords * 8, 256);
+        p.off_dhp = off;
+        off = align_up(off + (size_t)T * g.n * 8, 256);
     }
     p.ws_bytes = off;
     return p;
@@ -323,9 +346,12 @@ struct ForwardArgs {
     float* rec;        // partial records, one block per tile
     uint64_t* prx;     // single-read kernel: tagged pre-branch records
     uint64_t* hpx;     // single-read kernel: tagged hPre per tile
+    uint64_t* dpart;   // one-launch kernel: tagged partial records of the d-blocks
+    uint64_t* dhp;     // one-launch kernel: tagged hPre
     uint32_t* sync;    // [0] call counter (the epilogue adds 1; the single-read kernel's tag),
                        // [1] set when a single-read wait timed out,
-                       // [8 .. 15] arrivals per XCD (the epilogue clears them)
+                       // [8 .. 15] arrivals per XCD (the epilogue clears them),
+                       // [256 .. 256 + kDecodeMaxBlocks) the one-launch kernel's barrier flags
     int num_iters;
     double norm_eps;
     double hc_eps;
@@ -344,7 +370,7 @@ int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void
 // weight pack, projection, epilogue and hIn kernels.
 int launch_forward(const Plan& p, const ForwardArgs& a, void* stream, void* const* events);
 // Which kernels launch_forward runs for this plan and these arguments on the current
-// device: 1 the single-read kernel, 0 the four-kernel path.
+// device: 2 the one-launch kernel, 1 the single-read kernel, 0 the four-kernel path.
 int forward_path(const Plan& p, bool has_pre_mix);
 int record_event(void* event, void* stream);
 // Reads the workspace's time-out flag (sync word 1) after synchronising the stream, then

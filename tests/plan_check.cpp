@@ -118,7 +118,7 @@ static int check(int n, int D, int na, long long T)
     if (p.off_rec < p.off_wts + (size_t)T * n * 4) return fail("wts size", n, D, na, T, p.off_rec, 0);
     if (p.ws_bytes < p.off_rec + (size_t)p.tiles * recb) return fail("record size", n, D, na, T, p.ws_bytes, 0);
     // the call counter sits first, at the same offset for every size
-    if (p.off_sync != 0 || p.off_packed < 256) return fail("sync section", n, D, na, T, p.off_sync, p.off_packed);
+    if (p.off_sync != 0 || p.off_packed < kSyncBytes) return fail("sync section", n, D, na, T, p.off_sync, p.off_packed);
     // single-read variant
     const bool want = n == 4 && na == 3 && g.nblk >= kFMembers && (g.nblk + kFMembers - 1) / kFMembers <= kFMaxBlocks;
     if (p.fused_geom != want) return fail("single-read admission", n, D, na, T, p.fused_geom, want);
@@ -157,6 +157,24 @@ static int check(int n, int D, int na, long long T)
             if (hpx_at(p.tiles16 - 1, kFTok - 1, n - 1, n) + 1 != hw) return fail("hpx index", n, D, na, T, hw, 0);
             if (p.ws_bytes < p.off_hpx + (size_t)hw * 8) return fail("hpx area", n, D, na, T, p.ws_bytes, 0);
         }
+    }
+    // one-launch kernel of a few tokens: its sync words inside the 256-byte sync section,
+    // after the per-XCD counters; partial records [T][nblk][rs] and hPre [T][n] in order
+    if (kDecodeFlag0 < kTicket0 + kXcds || (size_t)(kDecodeFlag0 + kDecodeMaxBlocks) * 4 > kSyncBytes ||
+        kDecodeMaxBlocks * kBlock < kMaxD)
+        return fail("decode flag words", n, D, na, T, kDecodeFlag0, kDecodeMaxBlocks);
+    const bool dwant = n == 4 && na == 3 && T <= kDecodeTokens;
+    if (p.decode_geom != dwant) return fail("decode admission", n, D, na, T, p.decode_geom, dwant);
+    if (p.decode_geom) {
+        const size_t end_before = p.fused_geom ? p.off_hpx + (size_t)p.tiles16 * kFTok * n * 8 : p.off_rec + (size_t)p.tiles * recb;
+        if (p.off_dpart % 256 || p.off_dhp % 256 || p.off_dpart < end_before) return fail("decode sections", n, D, na, T, p.off_dpart, end_before);
+        if (kDecodeRecWords != g.M + 2 || kDecodeRecWords % 2) return fail("decode record words", n, D, na, T, kDecodeRecWords, g.M);
+        const long long last = ((T - 1) * g.nblk + (g.nblk - 1LL)) * kDecodeRecWords + kDecodeRecWords;   // one past the last word
+        if (p.off_dhp < p.off_dpart + (size_t)last * 8) return fail("decode records", n, D, na, T, p.off_dhp, last);
+        if (p.ws_bytes < p.off_dhp + (size_t)T * n * 8) return fail("decode hPre", n, D, na, T, p.ws_bytes, 0);
+        // x and hIn byte offsets of the last lane (token T-1, stream n-1, last block, octet 3)
+        const long long xo = (((T - 1) * g.K) + (long long)(n - 1) * D + kBlock * (g.nblk - 1LL) + 24) * 2 + 16;
+        if (xo >= (1LL << 31)) return fail("decode x offsets", n, D, na, T, xo, 0);
     }
     return 0;
 }

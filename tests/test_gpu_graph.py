@@ -1,8 +1,10 @@
 """The forward captured into a HIP graph (torch.cuda.CUDAGraph on torch's current stream):
-neither path records a memset or a host synchronisation, so both can be captured (the
-single-read path forced by MHC_FORWARD_PATH=fused in the last case: its kernel and the
-epilogue keep the call counter and the per-XCD arrival counters in the workspace, which
-each replay advances and clears as an eager call does). Every replay, with eager work of
+no path records a memset or a host synchronisation, so each can be captured (the
+one-launch path in the first two cases, whose kernel clears its barrier counters in the
+workspace at its end; the four-kernel path, forced by MHC_FORWARD_PATH=classic at 64
+tokens; the single-read path forced by MHC_FORWARD_PATH=fused in the last case: its kernel
+and the epilogue keep the call counter and the per-XCD arrival counters in the workspace,
+which each replay advances and clears as an eager call does). Every replay, with eager work of
 the program between replays, must equal the eager call bit for bit (the forward is
 deterministic), and the eager call meets the oracle."""
 import sys
@@ -16,19 +18,22 @@ from gpu_helpers import compare, device, run_oracle, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T,D,packed,fused", [(64, 7168, True, False), (64, 7168, False, False),
-                                               (4096, 1024, True, False), (1500, 2048, False, True)])
-def test_graph_replays_match_eager(T, D, packed, fused, monkeypatch):
+@pytest.mark.parametrize("T,D,packed,path", [(64, 7168, True, 2), (64, 7168, False, 2), (64, 7168, True, 0),
+                                              (4096, 1024, True, 0), (1500, 2048, False, 1)])
+def test_graph_replays_match_eager(T, D, packed, path, monkeypatch):
     import mhc_hyper_connection_amd as mhc
     import torch
-    if fused:
+    monkeypatch.delenv("MHC_FORWARD_PATH", raising=False)
+    if path == 1:
         monkeypatch.setenv("MHC_FORWARD_PATH", "fused")
-    print(f"[case] graph T={T} D={D} packed={packed} single-read={fused}", file=sys.stderr, flush=True)
+    elif path == 0 and T <= 64:
+        monkeypatch.setenv("MHC_FORWARD_PATH", "classic")
+    print(f"[case] graph T={T} D={D} packed={packed} path={path}", file=sys.stderr, flush=True)
     dev = device()
     inp = synth.custom(T, 4, D, need_backward=True, seed=95)
     wl = inp.wl
     r = mhc.PreForward(wl.T, wl.n, wl.D, wl.n_alpha, num_iters=wl.num_iters, need_backward=True, device=dev)
-    assert r.path() == (1 if fused else 0)
+    assert r.path() == path
     x, phi, alpha, bias = (to_dev(a, dev) for a in (inp.x, inp.phi, inp.alpha, inp.bias))
     pk = r.prepack(phi) if packed else None
     eager = r(x, None if packed else phi, alpha, bias, phi_packed=pk)

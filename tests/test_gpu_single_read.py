@@ -32,7 +32,7 @@ def _timeout_flag(runner):
 
 @pytest.mark.parametrize("T,D,pre_mix,n,n_alpha,want", [
     (16384, 7168, False, 4, 3, 1), (8192, 4096, False, 4, 3, 1), (8192, 1024, False, 4, 3, 1),
-    (64, 7168, False, 4, 3, 0), (8191, 7168, False, 4, 3, 0), (8192, 7168, False, 4, 3, 1),
+    (64, 7168, False, 4, 3, 2), (8191, 7168, False, 4, 3, 0), (8192, 7168, False, 4, 3, 1),
     (4096, 4096, False, 4, 3, 0), (16384, 7168, True, 4, 3, 0), (8192, 8192, False, 4, 3, 0),
     (8192, 992, False, 4, 3, 0), (8192, 1016, False, 4, 3, 1), (8192, 2048, False, 8, 3, 0),
     (8192, 2048, False, 4, 2, 0)])
