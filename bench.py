@@ -173,7 +173,7 @@ def cpu_baseline(inp, max_tokens: int):
     t0 = time.perf_counter()
     oracle.forward(inp.x, inp.phi, inp.alpha, inp.bias, inp.gamma, inp.pre_mix,
                    num_iters=inp.wl.num_iters, norm_eps=inp.wl.norm_eps, hc_eps=inp.wl.hc_eps,
-                   tokens=tokens)
+                   x_f16=inp.wl.x_f16, tokens=tokens)
     dt = time.perf_counter() - t0
     return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {ntok} of {T} tokens of the same workload, all outputs, "
@@ -371,7 +371,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="large_prefill_bwd")
+    ap.add_argument("--workload", default="large_prefill_bwd",
+                    help="a synth workload; a name ending in _f16 runs that workload with x and "
+                         "hIn in binary16")
     ap.add_argument("--cpu-tokens", type=int, default=65536,
                     help="tokens of the workload the CPU oracle baseline runs on (bounded)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -410,7 +412,11 @@ def main():
     import mhc_hyper_connection_amd as mhc
     import synth
 
-    wl = synth.WORKLOADS[args.workload]
+    f16 = args.workload.endswith("_f16")
+    wl = synth.WORKLOADS[args.workload[:-4] if f16 else args.workload]
+    if f16:
+        import dataclasses
+        wl = dataclasses.replace(wl, name=args.workload, x_f16=True)
     print(f"[bench] generating {wl.name}: T={wl.T} n={wl.n} D={wl.D}", file=sys.stderr, flush=True)
     inp = synth.generate(wl)
     dev = torch.device("cuda", 0)
@@ -419,14 +425,14 @@ def main():
         if a is None:
             return None
         if a.dtype.name == "uint16":
-            return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a.view("int16")).view(torch.float16 if f16 else torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
     x, phi, alpha, bias, gamma, pre_mix = map(up, (inp.x, inp.phi, inp.alpha, inp.bias,
                                                    inp.gamma, inp.pre_mix))
     run = mhc.PreForward(wl.T, wl.n, wl.D, wl.n_alpha, num_iters=wl.num_iters,
                          norm_eps=wl.norm_eps, hc_eps=wl.hc_eps,
-                         need_backward=wl.need_backward, device=dev)
+                         need_backward=wl.need_backward, device=dev, x_f16=f16)
     out = run.alloc_outputs()
     stream = torch.cuda.current_stream(dev)
     path = run.path(pre_mix is not None)
@@ -517,7 +523,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f16" if f16 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "n": wl.n, "D": wl.D, "n_alpha": wl.n_alpha,
                    "gamma": wl.gamma, "pre_mix": wl.pre_mix, "need_backward": wl.need_backward,

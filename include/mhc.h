@@ -171,9 +171,10 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
  *     mhc_pre_wait_status reports;
  *   one-launch path (n == 4, n_alpha == 3, no pre_mix, T <= 64, the device able to hold
  *     ceil(D / 32) workgroups of 256 threads at once): the whole forward in one kernel,
- *     one workgroup per block of 32 positions; its workgroups meet at two device-wide
- *     barriers (bounded waits, as above: a time-out leaves every output NaN, or only hIn
- *     when it comes at the second barrier, and mhc_pre_wait_status reports it).
+ *     one workgroup per block of 32 positions, which exchange their partial sums and hPre
+ *     through the workspace (bounded waits, as above: a time-out leaves the token's
+ *     outputs NaN, or only hIn when it comes at hPre, and mhc_pre_wait_status reports it).
+ *   The single-read and one-launch paths take bf16 or fp16 x.
  * Every path can be captured into a HIP graph.
  * The paths sum the projection's partial products in different groupings, so their
  * outputs may differ in the last bits; each meets the same accuracy. Within a call, hIn

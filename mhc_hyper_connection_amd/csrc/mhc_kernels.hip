@@ -111,6 +111,27 @@ __device__ __forceinline__ void split3_f16(double p, uint32_t (&tb)[3])
     tb[2] = __builtin_bit_cast(uint16_t, h2);
 }
 
+// The three-term split for x's format: bf16 terms, or scaled fp16 terms.
+template <bool H>
+__device__ __forceinline__ void split3_x(double p, uint32_t (&tb)[3])
+{
+    if constexpr (H) split3_f16(p, tb);
+    else split3(p, tb);
+}
+// Scales of the mid and lo term sums (split3_f16 scales the remainders by 2^11 each).
+template <bool H> constexpr float kMidScale = H ? 0x1p-11f : 1.f;
+template <bool H> constexpr float kLoScale = H ? 0x1p-22f : 1.f;
+
+// One 16 x 16 x 32 matrix-core step on x's format (fp16 or bf16 operands, fp32 sums).
+template <bool H>
+__device__ __forceinline__ f32x4 mfma_x16(u32x4 a, u32x4 b, f32x4 c)
+{
+    if constexpr (H)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // One thread per (K-step k, K-group g, phi row m): reads the row's 8 weights of that
 // octet once, splits each into its three terms and writes the three 16-byte units of
 // columns m, M + m and 2M + m; threads m < NC - 3M also zero padding column 3M + m.
@@ -1017,7 +1038,7 @@ struct FArgs {
 // otherwise idle device gives) the waits end; a wait that does not end within
 // kSpinLimit polls sets sync[1] and yields NaN hPre for that tile. NeverReady: the
 // instance for the test of that path, whose waits accept no tag and give up after 8 polls.
-template <int N, int A, bool NeverReady>
+template <int N, int A, bool NeverReady, bool H>
 __global__ void __launch_bounds__(kFThreads, 1)
 fused_kernel(FArgs f)
 {
@@ -1083,7 +1104,7 @@ fused_kernel(FArgs f)
                     double p = (double)a.phi[(int64_t)m * f.K + k0 + e];
                     if (a.gamma) p *= (double)a.gamma[k0 + e];
                     uint32_t tb[3];
-                    split3(p, tb);
+                    split3_x<H>(p, tb);
 #pragma unroll
                     for (int term = 0; term < 3; ++term) w3[term][e >> 1] |= tb[term] << (16 * (e & 1));
                 }
@@ -1164,12 +1185,10 @@ fused_kernel(FArgs f)
 #pragma unroll
                         for (int di = 0; di < 2; ++di) {
                             const u32x4 z = {0u, 0u, 0u, 0u};
-                            const bf16x8 Av = __builtin_bit_cast(bf16x8, oct_ok ? xr[u][i0 + di] : z);
-                            sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Av, sq, 0, 0, 0);
+                            const u32x4 Av = oct_ok ? xr[u][i0 + di] : z;
+                            sq = mfma_x16<H>(Av, Av, sq);
 #pragma unroll
-                            for (int nt = 0; nt < NT; ++nt)
-                                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    Av, __builtin_bit_cast(bf16x8, bw[di][nt]), acc[nt], 0, 0, 0);
+                            for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_x16<H>(Av, bw[di][nt], acc[nt]);
                         }
                     }
                     // phi row m's hi, mid and lo are columns m, M + m, 2M + m: lane j of a
@@ -1180,8 +1199,8 @@ fused_kernel(FArgs f)
                     for (int q = 0; q < 4; ++q) {
                         const int t = 4 * grp + q;
                         const float m1 = dpp<kRowRor8>(acc[1][q]), m2 = dpp<kRowRor8>(acc[2][q]);
-                        part[pb][wave][t][j] = (acc[0][q] + (j < 8 ? m1 : m2)) + acc[3][q];
-                        part[pb][wave][t][16 + j] = (acc[1][q] + m2) + acc[4][q];   // j >= 8: padding
+                        part[pb][wave][t][j] = (acc[0][q] + kMidScale<H> * (j < 8 ? m1 : m2)) + kLoScale<H> * acc[3][q];
+                        part[pb][wave][t][16 + j] = (acc[1][q] + kMidScale<H> * m2) + kLoScale<H> * acc[4][q];   // j >= 8: padding
                     }
                     const int rr = j - 4 * grp;
                     if (rr >= 0 && rr < 4) part_sq[pb][wave][j] = sq[rr];
@@ -1251,13 +1270,13 @@ fused_kernel(FArgs f)
                     for (int i = 0; i < N; ++i) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            hacc[2 * e] = fmaf(w[i], bf16_lo(xr[us][i][e]), hacc[2 * e]);
-                            hacc[2 * e + 1] = fmaf(w[i], bf16_hi(xr[us][i][e]), hacc[2 * e + 1]);
+                            hacc[2 * e] = fmaf(w[i], x16_lo<H>(xr[us][i][e]), hacc[2 * e]);
+                            hacc[2 * e + 1] = fmaf(w[i], x16_hi<H>(xr[us][i][e]), hacc[2 * e + 1]);
                         }
                     }
                     u32x4 o;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(hacc[2 * e], hacc[2 * e + 1]);
+                    for (int e = 0; e < 4; ++e) o[e] = pack_x16<H>(hacc[2 * e], hacc[2 * e + 1]);
                     const rsrc_t hres = make_rsrc(a.h_in + t0 * f.D, nt * f.D * 2);
                     __builtin_amdgcn_raw_buffer_store_b128(o, hres, (int)(oct_ok ? ho : kOutOfRange), 0, 0);
                 }
@@ -1435,7 +1454,7 @@ __device__ __forceinline__ void sinkhorn4(const ForwardArgs& a, int64_t T, const
 // on it are NaN (all of the token's at a record, hIn at an hPre). Workgroups wait on each
 // other, so all nblk of them must be resident at once: the path is taken only where the
 // device holds them.
-template <int N, int A, bool NeverReady>
+template <int N, int A, bool NeverReady, bool H>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(DArgs f)
 {
@@ -1545,7 +1564,7 @@ decode_kernel(DArgs f)
             for (int e = 0; e < 8; ++e) {
                 const double p = a.gamma ? (double)pv[k][e] * (double)gv[k][e] : (double)pv[k][e];
                 uint32_t tb[3];
-                split3(p, tb);
+                split3_x<H>(p, tb);
 #pragma unroll
                 for (int term = 0; term < 3; ++term) w3[term][e >> 1] |= tb[term] << (16 * (e & 1));
             }
@@ -1565,12 +1584,11 @@ decode_kernel(DArgs f)
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const u32x4* wb = wl + i * 4 * NCL + grp * NCL;
-            const bf16x8 Av = __builtin_bit_cast(bf16x8, xr[i]);
-            sq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, Av, sq, 0, 0, 0);
+            sq = mfma_x16<H>(xr[i], xr[i], sq);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const int col = 16 * nt + j < NCL ? 16 * nt + j : 16 * nt + j - 16;
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Av, __builtin_bit_cast(bf16x8, wb[col]), acc[nt], 0, 0, 0);
+                acc[nt] = mfma_x16<H>(xr[i], wb[col], acc[nt]);
             }
         }
         // phi row m's hi, mid and lo are columns m, M + m, 2M + m (as in the single-read kernel)
@@ -1578,8 +1596,8 @@ decode_kernel(DArgs f)
         for (int q = 0; q < 4; ++q) {
             const int tt = 4 * grp + q;
             const float m1 = dpp<kRowRor8>(acc[1][q]), m2 = dpp<kRowRor8>(acc[2][q]);
-            part[wave][tt][j] = (acc[0][q] + (j < 8 ? m1 : m2)) + acc[3][q];
-            part[wave][tt][16 + j] = (acc[1][q] + m2) + acc[4][q];   // j >= 8: padding
+            part[wave][tt][j] = (acc[0][q] + kMidScale<H> * (j < 8 ? m1 : m2)) + kLoScale<H> * acc[3][q];
+            part[wave][tt][16 + j] = (acc[1][q] + kMidScale<H> * m2) + kLoScale<H> * acc[4][q];   // j >= 8: padding
         }
         const int rr = j - 4 * grp;
         if (rr >= 0 && rr < 4) part_sq[wave][j] = sq[rr];
@@ -1731,13 +1749,13 @@ decode_kernel(DArgs f)
             const float wi = ok ? tagged_value(w[i]) : __builtin_nanf("");
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                hacc[2 * e] = fmaf(wi, bf16_lo(xv[i][e]), hacc[2 * e]);
-                hacc[2 * e + 1] = fmaf(wi, bf16_hi(xv[i][e]), hacc[2 * e + 1]);
+                hacc[2 * e] = fmaf(wi, x16_lo<H>(xv[i][e]), hacc[2 * e]);
+                hacc[2 * e + 1] = fmaf(wi, x16_hi<H>(xv[i][e]), hacc[2 * e + 1]);
             }
         }
         u32x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(hacc[2 * e], hacc[2 * e + 1]);
+        for (int e = 0; e < 4; ++e) o[e] = pack_x16<H>(hacc[2 * e], hacc[2 * e + 1]);
         const rsrc_t hres = make_rsrc(a.h_in, f.T * f.D * 2);
         __builtin_amdgcn_raw_buffer_store_b128(o, hres, (int)(oct_ok ? (uint32_t)((tt * f.D + kBlock * b + 8 * grp) * 2) : kOutOfRange), 0, 0);
     };
@@ -1810,10 +1828,25 @@ bool no_scratch(const void* fn)
 // their workgroups a compute unit holds.
 struct DeviceFacts {
     int cus = 0;
-    bool fused_ok = false;     // no scratch, at least one workgroup per compute unit
-    int decode_per_cu = 0;     // 0: the one-launch kernel cannot run here
+    bool fused_ok[2] = {false, false};   // [fp16 x]: no scratch, at least one workgroup per compute unit
+    int decode_per_cu[2] = {0, 0};       // [fp16 x]: 0, the one-launch kernel cannot run here
 };
 constexpr int kMaxDevices = 64;
+
+template <bool H>
+void fill_facts(DeviceFacts& f)
+{
+    int per_cu = 0;
+    f.fused_ok[H] = no_scratch(reinterpret_cast<const void*>(fused_kernel<4, 3, false, H>)) &&
+                    no_scratch(reinterpret_cast<const void*>(fused_kernel<4, 3, true, H>)) &&
+                    hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<4, 3, false, H>, kFThreads, 0) == hipSuccess &&
+                    per_cu >= 1;
+    per_cu = 0;
+    if (no_scratch(reinterpret_cast<const void*>(decode_kernel<4, 3, false, H>)) &&
+        no_scratch(reinterpret_cast<const void*>(decode_kernel<4, 3, true, H>)) &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<4, 3, false, H>, kThreads, 0) == hipSuccess)
+        f.decode_per_cu[H] = per_cu;
+}
 
 const DeviceFacts* device_facts()
 {
@@ -1824,16 +1857,8 @@ const DeviceFacts* device_facts()
     std::call_once(once[dev], [dev]() {
         DeviceFacts f;
         if (hipDeviceGetAttribute(&f.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) f.cus = 0;
-        int per_cu = 0;
-        f.fused_ok = no_scratch(reinterpret_cast<const void*>(fused_kernel<4, 3, false>)) &&
-                     no_scratch(reinterpret_cast<const void*>(fused_kernel<4, 3, true>)) &&
-                     hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<4, 3, false>, kFThreads, 0) == hipSuccess &&
-                     per_cu >= 1;
-        per_cu = 0;
-        if (no_scratch(reinterpret_cast<const void*>(decode_kernel<4, 3, false>)) &&
-            no_scratch(reinterpret_cast<const void*>(decode_kernel<4, 3, true>)) &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<4, 3, false>, kThreads, 0) == hipSuccess)
-            f.decode_per_cu = per_cu;
+        fill_facts<false>(f);
+        fill_facts<true>(f);
         facts[dev] = f;
     });
     return &facts[dev];
@@ -1845,7 +1870,7 @@ const DeviceFacts* device_facts()
 int fused_groups(const Plan& p)
 {
     const DeviceFacts* d = device_facts();
-    if (!d || d->cus != kXcds * kFMembers || !d->fused_ok) return 0;
+    if (!d || d->cus != kXcds * kFMembers || !d->fused_ok[p.g.x_f16 ? 1 : 0]) return 0;
     int64_t G = kXcds;
     if (G > p.tiles16) G = p.tiles16;
     return (int)G;
@@ -1869,7 +1894,7 @@ bool decode_wanted(const Plan& p, bool has_pre_mix)
     const char* env = std::getenv("MHC_FORWARD_PATH");
     if (env && (std::strcmp(env, "classic") == 0 || std::strcmp(env, "fused") == 0)) return false;
     const DeviceFacts* d = device_facts();
-    return d && (int64_t)d->decode_per_cu * d->cus >= p.g.nblk;
+    return d && (int64_t)d->decode_per_cu[p.g.x_f16 ? 1 : 0] * d->cus >= p.g.nblk;
 }
 
 hipError_t launch_decode(const Plan& p, const ForwardArgs& a, hipStream_t st, void* const* events)
@@ -1884,10 +1909,15 @@ hipError_t launch_decode(const Plan& p, const ForwardArgs& a, hipStream_t st, vo
     if (e != hipSuccess) return e;
     // test hook, as for the single-read kernel: every barrier wait gives up at its limit
     const char* never = std::getenv("MHC_TEST_EXCHANGE_NEVER_READY");
-    if (never && std::strcmp(never, "1") == 0)
-        hipLaunchKernelGGL((decode_kernel<4, 3, true>), dim3((unsigned)p.g.nblk), dim3(kThreads), 0, st, f);
-    else
-        hipLaunchKernelGGL((decode_kernel<4, 3, false>), dim3((unsigned)p.g.nblk), dim3(kThreads), 0, st, f);
+    const bool nr = never && std::strcmp(never, "1") == 0;
+    const dim3 grid((unsigned)p.g.nblk), block(kThreads);
+    if (p.g.x_f16) {
+        if (nr) hipLaunchKernelGGL((decode_kernel<4, 3, true, true>), grid, block, 0, st, f);
+        else hipLaunchKernelGGL((decode_kernel<4, 3, false, true>), grid, block, 0, st, f);
+    } else {
+        if (nr) hipLaunchKernelGGL((decode_kernel<4, 3, true, false>), grid, block, 0, st, f);
+        else hipLaunchKernelGGL((decode_kernel<4, 3, false, false>), grid, block, 0, st, f);
+    }
     e = hipGetLastError();
     if (e == hipSuccess) e = mark(events, kStageProj + 1, st);
     if (e == hipSuccess) e = mark(events, kStageEpi + 1, st);
@@ -1911,10 +1941,14 @@ hipError_t launch_fused(const Plan& p, const ForwardArgs& a, int G, hipStream_t 
     const bool test_never_ready = never && std::strcmp(never, "1") == 0;
     // one workgroup per compute unit: the hardware deals workgroups to the XCDs in turn,
     // kFMembers to each; a workgroup whose XCD's group is full (or not needed) leaves
-    if (test_never_ready)
-        hipLaunchKernelGGL((fused_kernel<4, 3, true>), dim3((unsigned)(kXcds * p.FP)), dim3(kFThreads), 0, st, f);
-    else
-        hipLaunchKernelGGL((fused_kernel<4, 3, false>), dim3((unsigned)(kXcds * p.FP)), dim3(kFThreads), 0, st, f);
+    const dim3 grid((unsigned)(kXcds * p.FP)), block(kFThreads);
+    if (p.g.x_f16) {
+        if (test_never_ready) hipLaunchKernelGGL((fused_kernel<4, 3, true, true>), grid, block, 0, st, f);
+        else hipLaunchKernelGGL((fused_kernel<4, 3, false, true>), grid, block, 0, st, f);
+    } else {
+        if (test_never_ready) hipLaunchKernelGGL((fused_kernel<4, 3, true, false>), grid, block, 0, st, f);
+        else hipLaunchKernelGGL((fused_kernel<4, 3, false, false>), grid, block, 0, st, f);
+    }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) e = mark(events, kStageProj + 1, st);
     if (e != hipSuccess) return e;

@@ -187,7 +187,7 @@ struct Plan {
     int OB = 8;               // tokens per epilogue workgroup: out_tokens(n, T)
     int64_t out_blocks = 0;   // epilogue workgroups: ceil(T / OB)
     // single-read variant
-    bool fused_geom = false;  // the geometry admits it (n = 4, alpha[3], <= 7 blocks per member)
+    bool fused_geom = false;  // the geometry admits it (n = 4, alpha[3], <= 7 blocks per member; bf16 or fp16 x)
     int FP = 0;               // members per group
     int FGS = 0, FNG = 0;     // summation groups over the FP member records (as GS, NG)
     int64_t tiles16 = 0;      // ceil(T / 16)
@@ -220,7 +220,7 @@ inline Plan make_plan(const Geometry& g, int64_t T)
     p.OB = out_tokens(g.n, T);
     p.out_blocks = (T + p.OB - 1) / p.OB;
     p.FP = kFMembers;
-    p.fused_geom = g.n == 4 && g.n_alpha == 3 && !g.x_f16 && g.nblk >= kFMembers && (g.nblk + p.FP - 1) / p.FP <= kFMaxBlocks;
+    p.fused_geom = g.n == 4 && g.n_alpha == 3 && g.nblk >= kFMembers && (g.nblk + p.FP - 1) / p.FP <= kFMaxBlocks;
     p.FGS = (p.FP + 7) / 8;
     p.FNG = (p.FP + p.FGS - 1) / p.FGS;
     p.tiles16 = (T + kFTok - 1) / kFTok;
@@ -241,7 +241,7 @@ inline Plan make_plan(const Geometry& g, int64_t T)
         p.off_hpx = off;
         off = align_up(off + (size_t)p.tiles16 * kFTok * g.n * 8, 256);
     }
-    p.decode_geom = g.n == 4 && g.n_alpha == 3 && !g.x_f16 && T <= kDecodeTokens;
+    p.decode_geom = g.n == 4 && g.n_alpha == 3 && T <= kDecodeTokens;
     if (p.decode_geom) {
         p.off_dpart = off;
         off = align_up(off + (size_t)T * g.nblk * kDecodeRecWords * 8, 256);

@@ -1,13 +1,13 @@
-"""The one-launch forward of a few tokens (n = 4, alpha[3], no pre_mix, T <= 64): path
-selection on the device, and parity with the fp64 oracle under the acceptance rule of
+"""The one-launch forward of a few tokens (n = 4, alpha[3], no pre_mix, T <= 64, bf16 or
+fp16 x): path selection on the device, and parity with the fp64 oracle under the acceptance rule of
 gpu_helpers over the sizes it serves: one token, tokens that fill 1 to 4 matrix-row waves
 and ragged counts, fewer tokens than workgroups and more (a workgroup then takes several
 tokens), a single d-block, a partial last d-block, the largest D (512 workgroups), gamma,
 the output set without intermediates, packed and unpacked weights (bit-equal), repeated
-calls through one workspace (its barrier counters return to zero), the same inputs on the
-four-kernel path, and a barrier time-out driven from the host (a test switch makes every
-barrier wait give up at its poll limit; every workgroup still exits normally) that must
-leave NaN outputs and show through mhc_pre_wait_status."""
+calls through one workspace (each call's tag comes from flag words every call advances),
+the same inputs on the four-kernel path, and a wait time-out driven from the host (a test
+switch makes every poll accept no tag, so each gives up at its limit; every workgroup
+still exits normally) that must leave NaN outputs and show through mhc_pre_wait_status."""
 import sys
 
 import numpy as np
@@ -22,18 +22,19 @@ pytestmark = pytest.mark.gpu
 def _runner(wl, nb):
     import mhc_hyper_connection_amd as mhc
     return mhc.PreForward(wl.T, wl.n, wl.D, wl.n_alpha, num_iters=wl.num_iters, norm_eps=wl.norm_eps,
-                          hc_eps=wl.hc_eps, need_backward=nb, device=device())
+                          hc_eps=wl.hc_eps, need_backward=nb, device=device(), x_f16=wl.x_f16)
 
 
 @pytest.mark.parametrize("T,D,pre_mix,n,n_alpha,want", [
     (1, 7168, False, 4, 3, 2), (64, 7168, False, 4, 3, 2), (65, 7168, False, 4, 3, 0),
     (64, 7168, True, 4, 3, 0), (64, 16384, False, 4, 3, 2), (8, 8, False, 4, 3, 2),
     (16, 1024, False, 4, 2, 0), (16, 1024, False, 8, 3, 0), (16, 1024, False, 6, 3, 0)])
-def test_path_selection(T, D, pre_mix, n, n_alpha, want, monkeypatch):
+@pytest.mark.parametrize("f16", [False, True])
+def test_path_selection(T, D, pre_mix, n, n_alpha, want, f16, monkeypatch):
     import mhc_hyper_connection_amd as mhc
     monkeypatch.delenv("MHC_FORWARD_PATH", raising=False)
     device()
-    p = mhc.make_params(T, n, D, n_alpha)
+    p = mhc.make_params(T, n, D, n_alpha, x_f16=f16)
     assert mhc.forward_path(p, pre_mix) == want
 
 
@@ -48,26 +49,29 @@ def test_path_override(monkeypatch):
 
 
 CASES = [
-    # (name, T, D, gamma, need_backward, intermediates, seed)
-    ("T1_D7168", 1, 7168, False, False, True, 151),
-    ("T2_D1024_bwd", 2, 1024, False, True, True, 152),
-    ("T16_D4096_gamma_bwd", 16, 4096, True, True, True, 153),
-    ("T17_D7168_bwd", 17, 7168, False, True, True, 154),
-    ("T33_D40_partial_block", 33, 40, False, True, True, 155),
-    ("T48_D8_one_block", 48, 8, True, True, True, 156),
-    ("T63_D5128_gamma", 63, 5128, True, False, True, 157),
-    ("T64_D7168_bwd", 64, 7168, False, True, True, 158),
-    ("T64_D1024_two_tokens_per_wg", 64, 1024, True, True, True, 159),
-    ("T64_D16384", 64, 16384, False, True, True, 160),
-    ("T40_D2048_no_intermediates", 40, 2048, False, False, False, 161),
+    # (name, T, D, gamma, need_backward, intermediates, fp16 x, seed)
+    ("T1_D7168", 1, 7168, False, False, True, False, 151),
+    ("T2_D1024_bwd", 2, 1024, False, True, True, False, 152),
+    ("T16_D4096_gamma_bwd", 16, 4096, True, True, True, False, 153),
+    ("T17_D7168_bwd", 17, 7168, False, True, True, False, 154),
+    ("T33_D40_partial_block", 33, 40, False, True, True, False, 155),
+    ("T48_D8_one_block", 48, 8, True, True, True, False, 156),
+    ("T63_D5128_gamma", 63, 5128, True, False, True, False, 157),
+    ("T64_D7168_bwd", 64, 7168, False, True, True, False, 158),
+    ("T64_D1024_two_tokens_per_wg", 64, 1024, True, True, True, False, 159),
+    ("T64_D16384", 64, 16384, False, True, True, False, 160),
+    ("T40_D2048_no_intermediates", 40, 2048, False, False, False, False, 161),
+    ("f16_T1_D7168", 1, 7168, False, False, True, True, 171),
+    ("f16_T33_D40_partial_block", 33, 40, True, True, True, True, 172),
+    ("f16_T64_D7168_gamma_bwd", 64, 7168, True, True, True, True, 173),
 ]
 
 
-@pytest.mark.parametrize("name,T,D,gamma,nb,inter,seed", CASES, ids=[c[0] for c in CASES])
-def test_decode_parity(name, T, D, gamma, nb, inter, seed, monkeypatch):
+@pytest.mark.parametrize("name,T,D,gamma,nb,inter,f16,seed", CASES, ids=[c[0] for c in CASES])
+def test_decode_parity(name, T, D, gamma, nb, inter, f16, seed, monkeypatch):
     monkeypatch.delenv("MHC_FORWARD_PATH", raising=False)
-    print(f"[case] one-launch {name} T={T} D={D} gamma={gamma} need_backward={nb}", file=sys.stderr, flush=True)
-    inp = synth.custom(T, 4, D, gamma=gamma, need_backward=nb, seed=seed)
+    print(f"[case] one-launch {name} T={T} D={D} gamma={gamma} need_backward={nb} f16={f16}", file=sys.stderr, flush=True)
+    inp = synth.custom(T, 4, D, gamma=gamma, need_backward=nb, seed=seed, x_f16=f16)
     r = _runner(inp.wl, nb)
     assert r.path() == 2
     gpu = gpu_forward(inp, runner=r, intermediates=inter)
@@ -110,14 +114,14 @@ def test_decode_and_four_kernel_path_agree_with_oracle(monkeypatch):
     compare(gpu_forward(inp, runner=r), orc, inp)
 
 
-def test_decode_barrier_time_out_is_reported(monkeypatch):
-    # every barrier wait made to give up (about 0.3 s each): the call still returns, every
-    # output is NaN (the first barrier guards the records every output comes from), and
+def test_decode_wait_time_out_is_reported(monkeypatch):
+    # every poll made to give up (about 0.3 s each): the call still returns, every output is
+    # NaN (the records every output comes from are never accepted), and
     # mhc_pre_wait_status reports the time-out once, then clears it; the next normal call
     # through the same workspace meets the oracle
     monkeypatch.delenv("MHC_FORWARD_PATH", raising=False)
     monkeypatch.setenv("MHC_TEST_EXCHANGE_NEVER_READY", "1")
-    print("[case] one-launch forced barrier time-out T=20 D=2048", file=sys.stderr, flush=True)
+    print("[case] one-launch forced wait time-out T=20 D=2048", file=sys.stderr, flush=True)
     inp = synth.custom(20, 4, 2048, need_backward=True, seed=164)
     r = _runner(inp.wl, True)
     assert r.path() == 2

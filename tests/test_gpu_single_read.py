@@ -1,5 +1,5 @@
 """The single-read forward kernel (n = 4, alpha[3], no pre_mix, 32 to 224 d-blocks of 32
-positions, T >= 8192; one group of 32 workgroups per XCD): path selection on the device,
+positions, T >= 8192, bf16 or fp16 x; one group of 32 workgroups per XCD): path selection on the device,
 and parity with the fp64 oracle under the acceptance rule of gpu_helpers, at the sizes
 where it is chosen by itself (the large workload test covers that at full size) and,
 forced by MHC_FORWARD_PATH=fused, at small and ragged sizes: partial last tiles of 16
@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 def _runner(wl, nb):
     import mhc_hyper_connection_amd as mhc
     return mhc.PreForward(wl.T, wl.n, wl.D, wl.n_alpha, num_iters=wl.num_iters, norm_eps=wl.norm_eps,
-                          hc_eps=wl.hc_eps, need_backward=nb, device=device())
+                          hc_eps=wl.hc_eps, need_backward=nb, device=device(), x_f16=wl.x_f16)
 
 
 def _timeout_flag(runner):
@@ -36,31 +36,37 @@ def _timeout_flag(runner):
     (4096, 4096, False, 4, 3, 0), (16384, 7168, True, 4, 3, 0), (8192, 8192, False, 4, 3, 0),
     (8192, 992, False, 4, 3, 0), (8192, 1016, False, 4, 3, 1), (8192, 2048, False, 8, 3, 0),
     (8192, 2048, False, 4, 2, 0)])
-def test_path_selection(T, D, pre_mix, n, n_alpha, want, monkeypatch):
+@pytest.mark.parametrize("f16", [False, True])
+def test_path_selection(T, D, pre_mix, n, n_alpha, want, f16, monkeypatch):
+    # the same choice for bf16 and fp16 x
     import mhc_hyper_connection_amd as mhc
     monkeypatch.delenv("MHC_FORWARD_PATH", raising=False)
     device()
-    p = mhc.make_params(T, n, D, n_alpha)
+    p = mhc.make_params(T, n, D, n_alpha, x_f16=f16)
     assert mhc.forward_path(p, pre_mix) == want
 
 
 CASES = [
-    # (name, T, D, gamma, need_backward, intermediates, seed)
-    ("T1_D1024", 1, 1024, False, True, True, 51),
-    ("T17_D1024_bwd", 17, 1024, False, True, True, 52),
-    ("T100_D1032_gamma", 100, 1032, True, False, True, 53),
-    ("T129_D2048_no_intermediates", 129, 2048, False, False, False, 54),
-    ("T300_D4096_gamma_bwd", 300, 4096, True, True, True, 55),
-    ("T1000_D7168_bwd", 1000, 7168, False, True, True, 56),
-    ("T2100_D3000_gamma", 2100, 3000, True, False, True, 57),
+    # (name, T, D, gamma, need_backward, intermediates, fp16 x, seed)
+    ("T1_D1024", 1, 1024, False, True, True, False, 51),
+    ("T17_D1024_bwd", 17, 1024, False, True, True, False, 52),
+    ("T100_D1032_gamma", 100, 1032, True, False, True, False, 53),
+    ("T129_D2048_no_intermediates", 129, 2048, False, False, False, False, 54),
+    ("T300_D4096_gamma_bwd", 300, 4096, True, True, True, False, 55),
+    ("T1000_D7168_bwd", 1000, 7168, False, True, True, False, 56),
+    ("T2100_D3000_gamma", 2100, 3000, True, False, True, False, 57),
+    ("f16_T17_D1024_bwd", 17, 1024, False, True, True, True, 151),
+    ("f16_T300_D4096_gamma_bwd", 300, 4096, True, True, True, True, 152),
+    ("f16_T1000_D7168_bwd", 1000, 7168, False, True, True, True, 153),
+    ("f16_T2100_D3000_gamma", 2100, 3000, True, False, True, True, 154),
 ]
 
 
-@pytest.mark.parametrize("name,T,D,gamma,nb,inter,seed", CASES, ids=[c[0] for c in CASES])
-def test_forced_single_read_parity(name, T, D, gamma, nb, inter, seed, monkeypatch):
+@pytest.mark.parametrize("name,T,D,gamma,nb,inter,f16,seed", CASES, ids=[c[0] for c in CASES])
+def test_forced_single_read_parity(name, T, D, gamma, nb, inter, f16, seed, monkeypatch):
     monkeypatch.setenv("MHC_FORWARD_PATH", "fused")
-    print(f"[case] single-read {name} T={T} D={D} gamma={gamma} need_backward={nb}", file=sys.stderr, flush=True)
-    inp = synth.custom(T, 4, D, gamma=gamma, need_backward=nb, seed=seed)
+    print(f"[case] single-read {name} T={T} D={D} gamma={gamma} need_backward={nb} f16={f16}", file=sys.stderr, flush=True)
+    inp = synth.custom(T, 4, D, gamma=gamma, need_backward=nb, seed=seed, x_f16=f16)
     r = _runner(inp.wl, nb)
     assert r.path() == 1
     gpu = gpu_forward(inp, runner=r, intermediates=inter)
@@ -94,13 +100,14 @@ def test_classic_path_still_served(monkeypatch):
     compare(gpu_forward(inp, runner=r), run_oracle(inp), inp)
 
 
-def test_single_read_with_prepacked_weights(monkeypatch):
+@pytest.mark.parametrize("f16", [False, True])
+def test_single_read_with_prepacked_weights(f16, monkeypatch):
     # phi packed once by mhc_pre_prepack and passed in (the kernel then copies the packed
     # slices instead of packing phi itself): same acceptance, and the same bits as packing
     # inside the kernel
     monkeypatch.setenv("MHC_FORWARD_PATH", "fused")
-    print("[case] single-read prepacked T=500 D=2048 gamma", file=sys.stderr, flush=True)
-    inp = synth.custom(500, 4, 2048, gamma=True, need_backward=True, seed=60)
+    print(f"[case] single-read prepacked T=500 D=2048 gamma f16={f16}", file=sys.stderr, flush=True)
+    inp = synth.custom(500, 4, 2048, gamma=True, need_backward=True, seed=60, x_f16=f16)
     r = _runner(inp.wl, True)
     g_packed = gpu_forward(inp, runner=r, packed=True)
     compare(g_packed, run_oracle(inp), inp)
