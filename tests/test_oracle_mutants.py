@@ -19,6 +19,11 @@ MUTANTS = {
     "rms_mean_over_D": ("ss / (double)K + norm_eps", "ss / (double)D + norm_eps"),
     "rms_without_norm_eps": ("sqrt(ss / (double)K + norm_eps)", "sqrt(ss / (double)K)"),
     "rms_on_x_squared_twice": ("ss += v * v;", "ss += v * v * v * v;"),
+    # reading R2: invRms of raw x, not of the gamma-scaled x the projection uses
+    "rms_on_gamma_scaled_x": ("    const double inv_rms = token_inv_rms(c, xt, c->n, c->D, c->norm_eps);",
+                              "    double inv_rms; { double ss = 0.0; for (int64_t k = 0; k < K; ++k) {"
+                              " double v = x_val(c, xt[k]) * (gamma ? (double)gamma[k] : 1.0); ss += v * v; }"
+                              " inv_rms = 1.0 / sqrt(ss / (double)K + c->norm_eps); }"),
     "gamma_indexed_by_d_only": ("if (gamma) xg *= (double)gamma[k];", "if (gamma) xg *= (double)gamma[k % c->D];"),
     "phi_transposed": ("acc += xg * (double)row[k];", "acc += xg * (double)phi[k * M + m]; (void)row;"),
     "w_not_normalised": ("double p_pre = hmix[i] * inv_rms;", "double p_pre = hmix[i];"),
