@@ -1381,7 +1381,8 @@ struct DArgs {
     int64_t T;
     int64_t K;
     int D;
-    int nblk;
+    int nblk;    // d-blocks
+    int nwg;     // workgroups: ceil(nblk / BPW)
 };
 
 // v / s for the Sinkhorn's positive operands (v in [0, 2], s in [eps, 5]: no scaling
@@ -1432,29 +1433,31 @@ __device__ __forceinline__ void sinkhorn4(const ForwardArgs& a, int64_t T, const
 }
 
 // The whole forward of up to kDecodeTokens tokens in one launch (n = 4, alpha[3]): workgroup
-// b owns d-block b (32 positions of each stream).
+// b owns BPW d-blocks, BPW b .. BPW b + BPW - 1 (32 positions of each stream each; two
+// blocks a workgroup halve the records every token's owner reads, where there are still
+// at least as many workgroups as tokens).
 //   Phase 1: its weights into LDS (copied from phi_packed, or split from phi and gamma as
-//   the pack kernel splits them), x of every token for its block into registers (wave w:
+//   the pack kernel splits them), x of every token for its blocks into registers (wave w:
 //   tokens 16 w .. 16 w + 15), the projection and the squares on the matrix cores, and the
-//   block's partial record of every token to the workspace.
-//   Phase 2, workgroups b < T, for tokens b, b + nblk, ..: the token's records summed over
-//   the blocks (fp64: in block order within each of 10 partitions, then the partitions in
+//   workgroup's partial record of every token to the workspace.
+//   Phase 2, workgroups b < T, for tokens b, b + nwg, ..: the token's records summed over
+//   the workgroups (fp64: in workgroup order within each of 10 partitions, then the partitions in
 //   order), then the per-token math of the epilogue kernel (hMix, invRms, hPre, hPost), hPre
 //   to the workspace, and the Sinkhorn planes and hRes (on one wave while the others go on).
-//   Phase 3: hIn of the block from the x registers, once every token's hPre is there.
+//   Phase 3: hIn of the blocks from the x registers, once every token's hPre is there.
 // The records and hPre cross workgroups (and XCDs, whose L2 caches are not coherent with
 // each other) as tagged words: value and the call's tag in one 64-bit word, stored and
 // loaded as device-scope atomics, and a reader polls a word until it carries this call's
 // tag. No barrier and no fence at device scope (on this GPU such a fence writes back or
 // invalidates a whole L2). The tag comes from flag word b, which only workgroup b reads
-// and writes, adding 1 per call to flags b, b + nblk, .. (all kDecodeMaxBlocks of them):
+// and writes, adding 1 per call to flags b, b + nwg, .. (all kDecodeMaxBlocks of them):
 // every flag holds the same count at the start of a call, whatever the grids of earlier
 // calls, so every workgroup derives the same tag, and a word of an earlier call never
 // carries it. The polls are bounded: a time-out sets sync[1] and the outputs that depend
 // on it are NaN (all of the token's at a record, hIn at an hPre). Workgroups wait on each
-// other, so all nblk of them must be resident at once: the path is taken only where the
+// other, so all nwg of them must be resident at once: the path is taken only where the
 // device holds them.
-template <int N, int A, bool NeverReady, bool H>
+template <int N, int A, bool NeverReady, bool H, int BPW>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(DArgs f)
 {
@@ -1469,13 +1472,14 @@ decode_kernel(DArgs f)
     constexpr int NPART = 10;                       // partitions of the block sum
     constexpr int BATCH = 32;                       // record words in flight per thread
     static_assert(NPART * R <= kThreads, "one thread per (partition, value)");
-    __shared__ u32x4 wl[N * 4 * NCL];               // the block's packed weights
+    static_assert(BPW == 1 || BPW == 2, "one or two d-blocks a workgroup");
+    __shared__ u32x4 wl[BPW * N * 4 * NCL];         // the blocks' packed weights
     __shared__ float part[4][16][MP];               // each wave's row sums
     __shared__ float part_sq[4][16];
     __shared__ double red[NPART][R];
     __shared__ float Ls[kDecodeTokens * NN];        // residual logits of this workgroup's tokens
     __shared__ float gpar[3 + M];                   // alpha, bias
-    __shared__ u32x4 xs[64][N];                     // wave 3's x while it runs the Sinkhorn
+    __shared__ u32x4 xs[64][BPW][N];                // wave 3's x while it runs the Sinkhorn
     __shared__ uint32_t sh_epoch;
     __shared__ int sh_bad;
     const ForwardArgs& a = f.a;
@@ -1483,8 +1487,8 @@ decode_kernel(DArgs f)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int j = lane & 15, grp = lane >> 4;
-    const int b = blockIdx.x;
-    const int nblk = f.nblk;
+    const int b = blockIdx.x;                        // workgroup
+    const int nwg = f.nwg;
     uint32_t* const flags = a.sync + kDecodeFlag0;
     uint64_t* const rec = reinterpret_cast<uint64_t*>(a.dpart);
     uint64_t* const hpw = reinterpret_cast<uint64_t*>(a.dhp);
@@ -1497,20 +1501,26 @@ decode_kernel(DArgs f)
     // phase 1: x (first: the longest wait), weights, projection
     const int t = 16 * wave + j;                     // the lane's token
     const bool wave_live = 16 * wave < f.T;          // the wave has tokens
-    const bool oct_ok = kBlock * b + 8 * grp < f.D;
+    // bit e: the lane's octet of block e lies before D
+    const uint32_t oct_ok = (kBlock * (BPW * b) + 8 * grp < f.D ? 1u : 0u) |
+                            (BPW > 1 && kBlock * (BPW * b + 1) + 8 * grp < f.D ? 2u : 0u);
     const rsrc_t xres = make_rsrc(a.x, f.T * f.K * 2);
-    u32x4 xr[N];
+    u32x4 xr[BPW][N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const uint32_t off = oct_ok && t < f.T ? (uint32_t)(((int64_t)t * f.K + (int64_t)i * f.D + kBlock * b + 8 * grp) * 2)
-                                               : kOutOfRange;
-        xr[i] = __builtin_amdgcn_raw_buffer_load_b128(xres, (int)off, 0, 0);
-    }
-    constexpr int WU = N * 4 * NCL;                  // 16-byte weight units of the block
+    for (int e = 0; e < BPW; ++e)
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const uint32_t off = ((oct_ok >> e) & 1u) && t < f.T
+                                     ? (uint32_t)(((int64_t)t * f.K + (int64_t)i * f.D + kBlock * (BPW * b + e) + 8 * grp) * 2)
+                                     : kOutOfRange;
+            xr[e][i] = __builtin_amdgcn_raw_buffer_load_b128(xres, (int)off, 0, 0);
+        }
+    constexpr int WU = BPW * N * 4 * NCL;            // 16-byte weight units of the blocks
     if (a.packed) {
-        // every load issued before the first LDS store
+        // every load issued before the first LDS store (a second block past the data reads
+        // the packed buffer's zero K-steps)
         constexpr int PER = (WU + kThreads - 1) / kThreads;
-        const u32x4* src = static_cast<const u32x4*>(a.packed) + (int64_t)b * N * 4 * NC;
+        const u32x4* src = static_cast<const u32x4*>(a.packed) + (int64_t)(BPW * b) * N * 4 * NC;
         u32x4 wv[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
@@ -1524,7 +1534,8 @@ decode_kernel(DArgs f)
         }
     } else {
         // (phi row m, K-step kk, octet og) items: their phi and gamma loads first, then the splits
-        constexpr int PER = (N * 4 * M + kThreads - 1) / kThreads;
+        constexpr int ITEMS = BPW * N * 4 * M;
+        constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
         float pv[PER][8], gv[PER][8];
         // an item's 8 weights (and gammas) are consecutive and start at a multiple of 8
         // elements: two 16-byte loads each where the arrays are 16-byte aligned
@@ -1532,10 +1543,10 @@ decode_kernel(DArgs f)
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int it = tid + k * kThreads;
-            const int m = it % M, row = it / M, kk = row / 4, og = row % 4;
-            const int d = kBlock * b + 8 * og;
-            const bool live = it < N * 4 * M && d < f.D;
-            const int64_t k0 = (int64_t)kk * f.D + d;
+            const int m = it % M, row = it / M, kl = row / 4, og = row % 4;   // K-step kl of the workgroup's
+            const int d = kBlock * (BPW * b + kl / N) + 8 * og;                 // blocks: stream kl % N
+            const bool live = it < ITEMS && d < f.D;
+            const int64_t k0 = (int64_t)(kl % N) * f.D + d;
             if (vec) {
                 const float4 z = {0.f, 0.f, 0.f, 0.f}, o = {1.f, 1.f, 1.f, 1.f};
                 const float4* pp4 = reinterpret_cast<const float4*>(a.phi + (int64_t)m * f.K + k0);
@@ -1557,7 +1568,7 @@ decode_kernel(DArgs f)
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int it = tid + k * kThreads;
-            if (it >= N * 4 * M) continue;
+            if (it >= ITEMS) continue;
             const int m = it % M, row = it / M;      // row = K-step * 4 + octet
             u32x4 w3[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
 #pragma unroll
@@ -1582,15 +1593,17 @@ decode_kernel(DArgs f)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const u32x4* wb = wl + i * 4 * NCL + grp * NCL;
-            sq = mfma_x16<H>(xr[i], xr[i], sq);
+        for (int e = 0; e < BPW; ++e)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int col = 16 * nt + j < NCL ? 16 * nt + j : 16 * nt + j - 16;
-                acc[nt] = mfma_x16<H>(xr[i], wb[col], acc[nt]);
+            for (int i = 0; i < N; ++i) {
+                const u32x4* wb = wl + (e * N + i) * 4 * NCL + grp * NCL;
+                sq = mfma_x16<H>(xr[e][i], xr[e][i], sq);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const int col = 16 * nt + j < NCL ? 16 * nt + j : 16 * nt + j - 16;
+                    acc[nt] = mfma_x16<H>(xr[e][i], wb[col], acc[nt]);
+                }
             }
-        }
         // phi row m's hi, mid and lo are columns m, M + m, 2M + m (as in the single-read kernel)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1603,7 +1616,7 @@ decode_kernel(DArgs f)
         if (rr >= 0 && rr < 4) part_sq[wave][j] = sq[rr];
     }
     __syncthreads();
-    // the block's partial record of every token ([token][block][word]: a token's records
+    // the workgroup's partial record of every token ([token][workgroup][word]: a token's records
     // are one run): word w < n the pre sums, n the square, n + 1 + i the sum of phi row n + i,
     // then a pad word (zero). All LDS reads first, then the stores.
     const int T32 = (int)f.T;
@@ -1622,21 +1635,21 @@ decode_kernel(DArgs f)
         for (int k = 0; k < PER; ++k) {
             const int idx = tid + k * kThreads;
             const int tk = idx / RS, w = idx - tk * RS;
-            if (tk < T32) put_tagged(rec + (tk * nblk + b) * RS + w, tag, val[k]);
+            if (tk < T32) put_tagged(rec + (tk * nwg + b) * RS + w, tag, val[k]);
         }
     }
 
     // phase 2: the tokens of this workgroup
-    const int ntok = b < T32 ? (T32 - b + nblk - 1) / nblk : 0;
+    const int ntok = b < T32 ? (T32 - b + nwg - 1) / nwg : 0;
     const float eps = (float)a.hc_eps;
     for (int q = 0; q < ntok; ++q) {
-        const int tk = b + q * nblk;
+        const int tk = b + q * nwg;
         // first word 0 of every block's record (one poll word per block: light traffic while
         // the records land), then every word, each checked again
         {
             bool bad = false;
-            for (int i = tid; i < nblk; i += kThreads) {
-                const uint64_t* p = rec + (tk * nblk + i) * RS;
+            for (int i = tid; i < nwg; i += kThreads) {
+                const uint64_t* p = rec + (tk * nwg + i) * RS;
                 int it = 0;
                 for (; it < kSpinLimit && !tag_is(get_tagged(p), want); ++it) __builtin_amdgcn_s_sleep(1);
                 bad = bad || it == kSpinLimit;
@@ -1647,8 +1660,8 @@ decode_kernel(DArgs f)
         // thread (pp, v): the words v of the blocks of partition pp, in block order, fp64
         const int pp = tid / R, v = tid % R;
         if (pp < NPART && !sh_bad) {
-            const int lo = pp * nblk / NPART, hi = (pp + 1) * nblk / NPART;
-            const uint64_t* src = rec + tk * nblk * RS + v;
+            const int lo = pp * nwg / NPART, hi = (pp + 1) * nwg / NPART;
+            const uint64_t* src = rec + tk * nwg * RS + v;
             double sacc = 0.0;
             bool bad = false;
             for (int b0 = lo; b0 < hi; b0 += BATCH) {
@@ -1706,7 +1719,9 @@ decode_kernel(DArgs f)
     const bool one_wave = ntok > 0 && ntok <= 4;
     if (one_wave && wave == 3) {
 #pragma unroll
-        for (int i = 0; i < N; ++i) xs[lane][i] = xr[i];
+        for (int e = 0; e < BPW; ++e)
+#pragma unroll
+            for (int i = 0; i < N; ++i) xs[lane][e][i] = xr[e][i];
     }
     if (ntok > 0) {
         __syncthreads();   // Ls, xs
@@ -1716,15 +1731,15 @@ decode_kernel(DArgs f)
                 const int q = q0 + grp;
                 const bool live = q < ntok;
                 const float* L = Ls + (live ? q : 0) * NN;
-                if (planes) sinkhorn4<true>(a, f.T, L, b + q * nblk, live, j);
-                else sinkhorn4<false>(a, f.T, L, b + q * nblk, live, j);
+                if (planes) sinkhorn4<true>(a, f.T, L, b + q * nwg, live, j);
+                else sinkhorn4<false>(a, f.T, L, b + q * nwg, live, j);
             }
         }
     }
 
     // phase 3: hIn of the block, from the registers that hold its x (wave 0 also does wave
     // 3's tokens from LDS when wave 3 runs the Sinkhorn)
-    auto hin_token = [&](int tt, const u32x4 (&xv)[N]) {
+    auto hin_token = [&](int tt, const u32x4 (&xw)[BPW][N]) __attribute__((always_inline)) {
         uint64_t w[N];
 #pragma unroll
         for (int i = 0; i < N; ++i) w[i] = get_tagged(hpw + tt * N + i);
@@ -1741,34 +1756,42 @@ decode_kernel(DArgs f)
         }
         const bool ok = it < kSpinLimit;
         if (!ok) __hip_atomic_store(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        float hacc[8];
+        float wv[N];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) hacc[e] = 0.f;
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const float wi = ok ? tagged_value(w[i]) : __builtin_nanf("");
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                hacc[2 * e] = fmaf(wi, x16_lo<H>(xv[i][e]), hacc[2 * e]);
-                hacc[2 * e + 1] = fmaf(wi, x16_hi<H>(xv[i][e]), hacc[2 * e + 1]);
-            }
-        }
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = pack_x16<H>(hacc[2 * e], hacc[2 * e + 1]);
+        for (int i = 0; i < N; ++i) wv[i] = ok ? tagged_value(w[i]) : __builtin_nanf("");
         const rsrc_t hres = make_rsrc(a.h_in, f.T * f.D * 2);
-        __builtin_amdgcn_raw_buffer_store_b128(o, hres, (int)(oct_ok ? (uint32_t)((tt * f.D + kBlock * b + 8 * grp) * 2) : kOutOfRange), 0, 0);
+#pragma unroll
+        for (int bl = 0; bl < BPW; ++bl) {
+            float hacc[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hacc[e] = 0.f;
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hacc[2 * e] = fmaf(wv[i], x16_lo<H>(xw[bl][i][e]), hacc[2 * e]);
+                    hacc[2 * e + 1] = fmaf(wv[i], x16_hi<H>(xw[bl][i][e]), hacc[2 * e + 1]);
+                }
+            }
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = pack_x16<H>(hacc[2 * e], hacc[2 * e + 1]);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                o, hres, (int)(((oct_ok >> bl) & 1u) ? (uint32_t)((tt * f.D + kBlock * (BPW * b + bl) + 8 * grp) * 2) : kOutOfRange), 0, 0);
+        }
     };
     if (!(one_wave && wave == 3) && t < T32) hin_token(t, xr);
     if (one_wave && wave == 0 && 48 + j < T32) {
-        u32x4 xv[N];
+        u32x4 xv[BPW][N];
 #pragma unroll
-        for (int i = 0; i < N; ++i) xv[i] = xs[lane][i];
+        for (int e = 0; e < BPW; ++e)
+#pragma unroll
+            for (int i = 0; i < N; ++i) xv[e][i] = xs[lane][e][i];
         hin_token(48 + j, xv);
     }
-    // this call's count into flags b, b + nblk, ..: the next call's epoch
+    // this call's count into flags b, b + nwg, ..: the next call's epoch
     if (wave == 0)
-        for (int v = b + nblk * lane; v < kDecodeMaxBlocks; v += nblk * 64)
+        for (int v = b + nwg * lane; v < kDecodeMaxBlocks; v += nwg * 64)
             __hip_atomic_store(flags + v, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1823,15 +1846,26 @@ bool no_scratch(const void* fn)
 }
 
 // What the path choice needs to know of a device, found once per device (these queries
-// cost about a microsecond per call otherwise): its compute units, and for the single-read
-// and one-launch kernels whether their code keeps everything in registers and how many of
-// their workgroups a compute unit holds.
+// cost about a microsecond per call otherwise): its compute units, whether the single-read
+// kernel's code keeps everything in registers, and how many workgroups of the single-read
+// and one-launch kernels a compute unit holds.
 struct DeviceFacts {
     int cus = 0;
-    bool fused_ok[2] = {false, false};   // [fp16 x]: no scratch, at least one workgroup per compute unit
-    int decode_per_cu[2] = {0, 0};       // [fp16 x]: 0, the one-launch kernel cannot run here
+    bool fused_ok[2] = {false, false};       // [fp16 x]: no scratch, at least one workgroup per compute unit
+    int decode_per_cu[2][2] = {{0, 0}, {0, 0}};   // [fp16 x][blocks a workgroup - 1]: 0, cannot run here
 };
 constexpr int kMaxDevices = 64;
+
+// Workgroups of the one-launch kernel a compute unit holds at once. (Its loads are all the
+// compiler's own, so unlike the single-read kernel it needs no scratch-free guarantee.)
+template <bool H, int BPW>
+int decode_per_cu()
+{
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<4, 3, false, H, BPW>, kThreads, 0) == hipSuccess)
+        return per_cu;
+    return 0;
+}
 
 template <bool H>
 void fill_facts(DeviceFacts& f)
@@ -1841,11 +1875,8 @@ void fill_facts(DeviceFacts& f)
                     no_scratch(reinterpret_cast<const void*>(fused_kernel<4, 3, true, H>)) &&
                     hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_kernel<4, 3, false, H>, kFThreads, 0) == hipSuccess &&
                     per_cu >= 1;
-    per_cu = 0;
-    if (no_scratch(reinterpret_cast<const void*>(decode_kernel<4, 3, false, H>)) &&
-        no_scratch(reinterpret_cast<const void*>(decode_kernel<4, 3, true, H>)) &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_kernel<4, 3, false, H>, kThreads, 0) == hipSuccess)
-        f.decode_per_cu[H] = per_cu;
+    f.decode_per_cu[H][0] = decode_per_cu<H, 1>();
+    f.decode_per_cu[H][1] = decode_per_cu<H, 2>();
 }
 
 const DeviceFacts* device_facts()
@@ -1885,16 +1916,31 @@ bool fused_wanted(const Plan& p, bool has_pre_mix)
     return forced || p.T >= kFMinTokens;
 }
 
+// Blocks a workgroup of the one-launch kernel takes on the current device. With packed
+// weights passed in, two where that still leaves a workgroup per token (half the records
+// for every token's owner to read); with weights split inside the kernel, one, so that the
+// split (the larger cost there) stays spread over every d-block's workgroup. 0 when the
+// device cannot hold all its workgroups at once.
+int decode_blocks_per_wg(const Plan& p, bool packed)
+{
+    const DeviceFacts* d = device_facts();
+    if (!d) return 0;
+    const int h = p.g.x_f16 ? 1 : 0;
+    const int64_t nwg2 = (p.g.nblk + 1) / 2;
+    if (packed && nwg2 >= p.T && (int64_t)d->decode_per_cu[h][1] * d->cus >= nwg2) return 2;
+    if ((int64_t)d->decode_per_cu[h][0] * d->cus >= p.g.nblk) return 1;
+    return 0;
+}
+
 // Whether the one-launch kernel serves this call on the current device: the geometry
-// admits it, no pre_mix, MHC_FORWARD_PATH does not ask for another path, code without
-// scratch memory, and the device holds all nblk workgroups at once.
+// admits it, no pre_mix, MHC_FORWARD_PATH does not ask for another path, and the device
+// holds all its workgroups at once.
 bool decode_wanted(const Plan& p, bool has_pre_mix)
 {
     if (!p.decode_geom || has_pre_mix || p.T <= 0) return false;
     const char* env = std::getenv("MHC_FORWARD_PATH");
     if (env && (std::strcmp(env, "classic") == 0 || std::strcmp(env, "fused") == 0)) return false;
-    const DeviceFacts* d = device_facts();
-    return d && (int64_t)d->decode_per_cu[p.g.x_f16 ? 1 : 0] * d->cus >= p.g.nblk;
+    return decode_blocks_per_wg(p, false) > 0;
 }
 
 hipError_t launch_decode(const Plan& p, const ForwardArgs& a, hipStream_t st, void* const* events)
@@ -1905,19 +1951,24 @@ hipError_t launch_decode(const Plan& p, const ForwardArgs& a, hipStream_t st, vo
     f.K = p.g.K;
     f.D = p.g.D;
     f.nblk = p.g.nblk;
+    const int bpw = decode_blocks_per_wg(p, a.packed != nullptr);
+    if (bpw == 0) return hipErrorInvalidValue;
+    f.nwg = (p.g.nblk + bpw - 1) / bpw;
     hipError_t e = mark(events, kStagePack + 1, st);
     if (e != hipSuccess) return e;
-    // test hook, as for the single-read kernel: every barrier wait gives up at its limit
+    // test hook, as for the single-read kernel: every wait gives up at its limit
     const char* never = std::getenv("MHC_TEST_EXCHANGE_NEVER_READY");
     const bool nr = never && std::strcmp(never, "1") == 0;
-    const dim3 grid((unsigned)p.g.nblk), block(kThreads);
-    if (p.g.x_f16) {
-        if (nr) hipLaunchKernelGGL((decode_kernel<4, 3, true, true>), grid, block, 0, st, f);
-        else hipLaunchKernelGGL((decode_kernel<4, 3, false, true>), grid, block, 0, st, f);
+    const dim3 grid((unsigned)f.nwg), block(kThreads);
+#define MHC_DECODE(NR, HV, BV) hipLaunchKernelGGL((decode_kernel<4, 3, NR, HV, BV>), grid, block, 0, st, f)
+    if (bpw == 2) {
+        if (p.g.x_f16) { if (nr) MHC_DECODE(true, true, 2); else MHC_DECODE(false, true, 2); }
+        else { if (nr) MHC_DECODE(true, false, 2); else MHC_DECODE(false, false, 2); }
     } else {
-        if (nr) hipLaunchKernelGGL((decode_kernel<4, 3, true, false>), grid, block, 0, st, f);
-        else hipLaunchKernelGGL((decode_kernel<4, 3, false, false>), grid, block, 0, st, f);
+        if (p.g.x_f16) { if (nr) MHC_DECODE(true, true, 1); else MHC_DECODE(false, true, 1); }
+        else { if (nr) MHC_DECODE(true, false, 1); else MHC_DECODE(false, false, 1); }
     }
+#undef MHC_DECODE
     e = hipGetLastError();
     if (e == hipSuccess) e = mark(events, kStageProj + 1, st);
     if (e == hipSuccess) e = mark(events, kStageEpi + 1, st);
