@@ -54,12 +54,13 @@ class _BwdIn(ctypes.Structure):
         (name, ctypes.c_void_p) for name in
         ("x", "phi", "alpha", "grad_h_in", "grad_h_post", "grad_h_res", "inv_rms",
          "h_mix", "h_pre", "h_post", "gamma", "grad_x_post")] + [
-        ("num_iters", ctypes.c_int32), ("sum_out", ctypes.c_void_p), ("norm_out", ctypes.c_void_p)]
+        ("num_iters", ctypes.c_int32), ("sum_out", ctypes.c_void_p), ("norm_out", ctypes.c_void_p),
+        ("x_f16", ctypes.c_int32)]
 
 
 class _BwdOut(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
-                ("grad_x", "grad_x_bf16", "grad_x_abs", "grad_phi", "grad_phi_abs",
+                ("grad_x", "grad_x_bits", "grad_x_abs", "grad_phi", "grad_phi_abs",
                  "grad_alpha", "grad_alpha_abs", "grad_bias", "grad_bias_abs",
                  "grad_gamma", "grad_gamma_abs", "g_mix")]
 
@@ -307,7 +308,7 @@ def mhcpre_forward_f64(x, phi, alpha, bias, gamma=None, *, norm_eps=1e-6, hc_eps
 @dataclass
 class BackwardResult:
     grad_x: np.ndarray        # [ntok, n, D] float64, unrounded
-    grad_x_bf16: np.ndarray   # [ntok, n, D] bf16 bits
+    grad_x_bits: np.ndarray   # [ntok, n, D] bits of x's format (bf16, or fp16 with x_f16)
     grad_x_abs: np.ndarray    # sum of |terms| per gradX element
     grad_phi: np.ndarray      # [M, n*D]
     grad_phi_abs: np.ndarray
@@ -322,9 +323,10 @@ class BackwardResult:
 
 def backward(x_bits, phi, alpha, grad_h_in_bits, grad_h_post, grad_h_res, inv_rms, h_mix,
              h_pre, h_post, gamma=None, grad_x_post_bits=None, *, hc_eps=1e-6, tokens=None,
-             num_iters=0, sum_out=None, norm_out=None, nthreads=0, lib=None) -> BackwardResult:
+             num_iters=0, sum_out=None, norm_out=None, nthreads=0, x_f16=False, lib=None) -> BackwardResult:
     """The MhcPre backward in fp64 from the inputs the GPU receives: x, gradHIn and
-    gradXPost as bf16 bits; phi [n*n + 2n, n*D], alpha [3], gradHPost [T, n],
+    gradXPost as bf16 bits (fp16 bits with x_f16: gradX then rounds to fp16, the
+    MhcPreBackward guide's section 8.2 giving gradX gradHIn's type); phi [n*n + 2n, n*D], alpha [3], gradHPost [T, n],
     gradHRes [T, n, n], invRms [T], hMix [T, M], hPre [T, n], hPost [T, n], gamma [n, D]
     as float32. gradX rows are returned for ``tokens`` (default: all); every other
     gradient sums over all tokens. num_iters >= 1: the MhcPreSinkhorn backward, reading
@@ -360,7 +362,7 @@ def backward(x_bits, phi, alpha, grad_h_in_bits, grad_h_post, grad_h_res, inv_rm
     bin_ = _BwdIn(T, n, D, float(hc_eps), *[_ptr(a) for a in (
         x_bits, phi, alpha, ghin, ghpost, ghres, inv_rms, h_mix, h_pre, h_post, gamma,
         grad_x_post_bits)], int(num_iters), _ptr(sum_out) if num_iters else None,
-        _ptr(norm_out) if num_iters else None)
+        _ptr(norm_out) if num_iters else None, int(bool(x_f16)))
     bout = _BwdOut(*[_ptr(getattr(r, f)) for f, _ in _BwdOut._fields_])
     rc = (lib or _load()).oracle_pre_backward(ctypes.byref(bin_), _ptr(tok), ntok,
                                               ctypes.byref(bout), int(nthreads))

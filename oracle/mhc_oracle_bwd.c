@@ -22,8 +22,9 @@
  *
  * The backward takes the forward's saved values (invRms, hMix, hPre, hPost) as inputs, as
  * [BW] section 1 describes, and does not recompute them. Every input converts to double
- * exactly; every sum and product is in double; gradX is also returned rounded once to
- * bf16 (round to nearest, ties to even), since it takes gradHIn's bf16 type ([BW] 8.2).
+ * exactly; every sum and product is in double; gradX is also returned rounded once
+ * (round to nearest, ties to even) to gradHIn's type, bf16 or fp16 ([BW] 8.2: gradX
+ * inherits grad_h_in's BF16/FP16 type; x, gradHIn and gradXPost then share that format).
  *
  * Readings (also listed with the design notes of the repository):
  *   B1 alpha_res's gradient sums gradHRes times pRes = w[2n:] (the input of the affine map;
@@ -57,6 +58,8 @@
 
 double oracle_bf16_to_double(uint16_t bits);
 uint16_t oracle_bf16_from_double(double v);
+double oracle_f16_to_double(uint16_t bits);
+uint16_t oracle_f16_from_double(double v);
 
 static double sigm(double z)
 {
@@ -150,10 +153,10 @@ typedef struct oracle_bwd_in {
     int32_t n;
     int32_t D;
     double hc_eps;
-    const uint16_t* x;            /* bf16 [T][n][D] */
+    const uint16_t* x;            /* bf16 or fp16 (x_f16) [T][n][D] */
     const float* phi;             /* [M][n*D] */
     const float* alpha;           /* [3] */
-    const uint16_t* grad_h_in;    /* bf16 [T][D] */
+    const uint16_t* grad_h_in;    /* x's format [T][D] */
     const float* grad_h_post;     /* [T][n] */
     const float* grad_h_res;      /* [T][n][n] */
     const float* inv_rms;         /* [T] */
@@ -161,17 +164,28 @@ typedef struct oracle_bwd_in {
     const float* h_pre;           /* [T][n] */
     const float* h_post;          /* [T][n] */
     const float* gamma;           /* [n][D] or NULL */
-    const uint16_t* grad_x_post;  /* bf16 [T][n][D] or NULL */
+    const uint16_t* grad_x_post;  /* x's format [T][n][D] or NULL */
     int32_t num_iters;            /* 0: MhcPre; >= 1: MhcPreSinkhorn (planes below) */
     const float* sum_out;         /* [2 it][T][n] */
     const float* norm_out;        /* [2 it][T][n][n] */
+    int32_t x_f16;                /* 0: x, gradHIn, gradXPost and gradX bf16; 1: fp16 */
 } oracle_bwd_in;
+
+/* A 16-bit value of x's format (exact), and the nearest one to a double. */
+static double x16_value(const oracle_bwd_in* in, uint16_t bits)
+{
+    return in->x_f16 ? oracle_f16_to_double(bits) : oracle_bf16_to_double(bits);
+}
+static uint16_t x16_round(const oracle_bwd_in* in, double v)
+{
+    return in->x_f16 ? oracle_f16_from_double(v) : oracle_bf16_from_double(v);
+}
 
 /* gradX rows are produced for the listed tokens (ntok rows, request order); the other
  * outputs always cover all T tokens. Any output may be NULL. */
 typedef struct oracle_bwd_out {
     double* grad_x;           /* [ntok][n][D] unrounded */
-    uint16_t* grad_x_bf16;    /* [ntok][n][D] */
+    uint16_t* grad_x_bits;    /* [ntok][n][D], rounded to x's format */
     double* grad_x_abs;       /* [ntok][n][D]: sum of |terms| of each gradX element */
     double* grad_phi;         /* [M][n*D] */
     double* grad_phi_abs;
@@ -201,8 +215,8 @@ static void token_head(const oracle_bwd_in* in, int64_t t, double* gmix, double*
     for (int i = 0; i < n; ++i) {
         double acc = 0.0;
         for (int d = 0; d < D; ++d)
-            acc += oracle_bf16_to_double(in->grad_h_in[t * D + d]) *
-                   oracle_bf16_to_double(in->x[t * K + (int64_t)i * D + d]);
+            acc += x16_value(in, in->grad_h_in[t * D + d]) *
+                   x16_value(in, in->x[t * K + (int64_t)i * D + d]);
         /* 3.2 sigmoid of the pre branch: s = hPre - hcEps, derivative s (1 - s) */
         const double s = (double)in->h_pre[t * n + i] - eps;
         const double g2 = acc * s * (1.0 - s);
@@ -319,7 +333,7 @@ int oracle_pre_backward(const oracle_bwd_in* in, const int64_t* tokens, int64_t 
         double sp[80], spa[80], sg = 0.0, sga = 0.0;
         for (int m = 0; m < M; ++m) { sp[m] = 0.0; spa[m] = 0.0; }
         for (int64_t t = 0; t < T; ++t) {
-            const double xv = oracle_bf16_to_double(in->x[t * K + k]);
+            const double xv = x16_value(in, in->x[t * K + k]);
             const double xrs = xv * gk;
             double xg = 0.0, xga = 0.0;
             for (int m = 0; m < M; ++m) {
@@ -350,7 +364,7 @@ int oracle_pre_backward(const oracle_bwd_in* in, const int64_t* tokens, int64_t 
             const double hp = in->h_pre[t * n + i];
             for (int d = 0; d < D; ++d) {
                 const int64_t k = (int64_t)i * D + d;
-                const double xv = oracle_bf16_to_double(in->x[t * K + k]);
+                const double xv = x16_value(in, in->x[t * K + k]);
                 double mm = 0.0, mma = 0.0;
                 for (int m = 0; m < M; ++m) {
                     const double p = gmix[t * M + m] * (double)in->phi[(int64_t)m * K + k];
@@ -358,18 +372,18 @@ int oracle_pre_backward(const oracle_bwd_in* in, const int64_t* tokens, int64_t 
                     mma += fabs(p);
                 }
                 const double gk = in->gamma ? (double)in->gamma[k] : 1.0;
-                const double v3 = oracle_bf16_to_double(in->grad_h_in[t * D + d]) * hp;
+                const double v3 = x16_value(in, in->grad_h_in[t * D + d]) * hp;
                 const double vr = -c3 * xv;
                 double g = v3 + mm * gk + vr;
                 double ga = fabs(v3) + mma * fabs(gk) + fabs(vr);
                 if (in->grad_x_post) {
-                    const double gp = oracle_bf16_to_double(in->grad_x_post[t * K + k]);
+                    const double gp = x16_value(in, in->grad_x_post[t * K + k]);
                     g += gp;
                     ga += fabs(gp);
                 }
                 const int64_t at = j * K + k;
                 if (o->grad_x) o->grad_x[at] = g;
-                if (o->grad_x_bf16) o->grad_x_bf16[at] = oracle_bf16_from_double(g);
+                if (o->grad_x_bits) o->grad_x_bits[at] = x16_round(in, g);
                 if (o->grad_x_abs) o->grad_x_abs[at] = ga;
             }
         }

@@ -18,6 +18,9 @@ What pins what:
                        guide, section 7): closed forms derived by hand below
   summation scale      the returned sums of |terms| bound the sums and equal them
                        when every term is non-negative
+  fp16 x / gradHIn     (gradX then takes fp16, the MhcPreBackward guide's section 8.2)
+                       the same finite differences on fp16-exact inputs that bf16 cannot
+                       hold; gradX's fp16 bits against numpy's correctly rounded float16
   Sinkhorn backward    (MhcPreSinkhorn: hRes is the Sinkhorn of the affine logits) the
                        same finite differences through the double forward with the
                        Sinkhorn steps, n = 4 and 8, 1 to 20 iterations; the double
@@ -51,21 +54,28 @@ def _bf16(a):
     return bits, bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def problem(T=3, n=4, D=8, gamma=True, x_post=True, seed=0):
-    """A small random MhcPre backward problem with bf16-exact x, gradHIn, gradXPost."""
+def _f16(a):
+    h = np.asarray(a, dtype=np.float16)
+    return h.view(np.uint16).copy(), h.astype(np.float64)
+
+
+def problem(T=3, n=4, D=8, gamma=True, x_post=True, seed=0, f16=False):
+    """A small random MhcPre backward problem with bf16-exact (or, f16, fp16-exact) x,
+    gradHIn, gradXPost."""
     rng = np.random.default_rng(seed)
     M, K = n * n + 2 * n, n * D
-    p = {}
-    p["x_bits"], p["x"] = _bf16(rng.normal(0, 1, (T, n, D)))
+    x16 = _f16 if f16 else _bf16
+    p = {"x_f16": f16}
+    p["x_bits"], p["x"] = x16(rng.normal(0, 1, (T, n, D)))
     p["phi"] = rng.normal(0, K ** -0.5, (M, K)).astype(np.float32)
     p["alpha"] = np.array([0.8, 1.1, 0.9], np.float32)
     p["bias"] = rng.normal(0, 0.5, M).astype(np.float32)
     p["gamma"] = rng.uniform(0.5, 1.5, (n, D)).astype(np.float32) if gamma else None
-    p["ghin_bits"], p["ghin"] = _bf16(rng.normal(0, 1, (T, D)))
+    p["ghin_bits"], p["ghin"] = x16(rng.normal(0, 1, (T, D)))
     p["ghpost"] = rng.normal(0, 1, (T, n)).astype(np.float32)
     p["ghres"] = rng.normal(0, 1, (T, n, n)).astype(np.float32)
     if x_post:
-        p["gxp_bits"], p["gxp"] = _bf16(rng.normal(0, 1, (T, n, D)))
+        p["gxp_bits"], p["gxp"] = x16(rng.normal(0, 1, (T, n, D)))
     else:
         p["gxp_bits"], p["gxp"] = None, None
     return p
@@ -91,7 +101,7 @@ def backward(p, fwd=None, lib=None, **kw):
     return oracle.backward(p["x_bits"], p["phi"], p["alpha"], p["ghin_bits"], p["ghpost"],
                            p["ghres"], f.inv_rms, f.h_mix, f.h_pre, f.h_post, p["gamma"],
                            p["gxp_bits"], num_iters=it, sum_out=f.sum_out, norm_out=f.norm_out,
-                           lib=lib, **kw)
+                           x_f16=p.get("x_f16", False), lib=lib, **kw)
 
 
 def _fd(p, name, lib=None):
@@ -130,6 +140,28 @@ def pin_fd_n4_plain(lib=None):
 
 def pin_fd_n8(lib=None):
     _check_fd(problem(T=1, n=8, D=4, gamma=True, x_post=False, seed=3), lib)
+
+
+def pin_fd_n4_f16(lib=None):
+    p = problem(T=2, n=4, D=8, gamma=True, x_post=True, seed=31, f16=True)
+    # the inputs use fp16's extra significand bits: read as bf16 they would be other numbers
+    assert np.any(p["x_bits"] & 0x7) and np.any(p["ghin_bits"] & 0x7)
+    _check_fd(p, lib)
+
+
+def pin_f16_grad_x_rounding(lib=None):
+    # gradX is returned once rounded to fp16: numpy's float64 -> float16 conversion rounds
+    # to nearest, ties to even
+    p = problem(T=3, n=4, D=8, gamma=True, x_post=True, seed=32, f16=True)
+    r = backward(p, lib=lib)
+    want = r.grad_x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(r.grad_x_bits, want), "gradX's fp16 bits are not the nearest fp16"
+    # and in bf16 mode the bits are within half a bf16 ulp of the value
+    q = problem(T=3, n=4, D=8, gamma=True, x_post=True, seed=32)
+    rq = backward(q, lib=lib)
+    got = bf16_bits_to_f32(rq.grad_x_bits).astype(np.float64)
+    lo = np.abs(rq.grad_x - got) <= np.abs(rq.grad_x) * 2.0 ** -8   # half an ulp: 2^-8 of the leading power of two at most
+    assert np.all(lo), "gradX's bf16 bits are not within half a bf16 ulp"
 
 
 def pin_forward64_matches_forward(lib=None):

@@ -94,7 +94,7 @@ def compare(g, o, bi, tokens=None):
     for r0 in range(0, len(tok), 1024):   # rows in chunks: bounded temporaries at the large shape
         sl = slice(r0, min(len(tok), r0 + 1024))
         gx = gx_all[sl]
-        dist = np.abs(bf16_ordered(gx) - bf16_ordered(o.grad_x_bf16[sl]))
+        dist = np.abs(bf16_ordered(gx) - bf16_ordered(o.grad_x_bits[sl]))
         cancel = np.abs(bf16_bits_to_f32(gx).astype(np.float64) - o.grad_x[sl]) <= 2.0 ** -18 * o.grad_x_abs[sl]
         ok = (dist <= 1) | cancel
         nel += int(dist.size)

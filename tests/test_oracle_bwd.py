@@ -48,8 +48,12 @@ MUTANTS = {
     "x_post_dropped": ("g += gp;", "(void)gp;"),
     "phi_row_col_swapped": ("const double p = gmix[t * M + m] * (double)in->phi[(int64_t)m * K + k];",
                             "const double p = gmix[t * M + m] * (double)in->phi[(int64_t)(k % M) * K + (k / M) + m];"),
-    "hpre_grad_reads_stream_0": ("oracle_bf16_to_double(in->x[t * K + (int64_t)i * D + d]);",
-                                 "oracle_bf16_to_double(in->x[t * K + d]);"),
+    "hpre_grad_reads_stream_0": ("x16_value(in, in->x[t * K + (int64_t)i * D + d]);",
+                                 "x16_value(in, in->x[t * K + d]);"),
+    "f16_inputs_read_as_bf16": ("return in->x_f16 ? oracle_f16_to_double(bits) : oracle_bf16_to_double(bits);",
+                                "return oracle_bf16_to_double(bits);"),
+    "f16_grad_x_rounded_to_bf16": ("return in->x_f16 ? oracle_f16_from_double(v) : oracle_bf16_from_double(v);",
+                                   "return oracle_bf16_from_double(v);"),
     "sk_bwd_reads_previous_plane": ("const float* A = in->norm_out + ((int64_t)k * T + t) * n * n;",
                                     "const float* A = in->norm_out + ((int64_t)(k - 1) * T + t) * n * n;"),
     "sk_bwd_no_division": ("gl[e] = (gl[e] - u) / (double)sk[i];", "gl[e] = (gl[e] - u);"),
