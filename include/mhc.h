@@ -287,18 +287,20 @@ mhc_status mhc_pre_forward_timed(const mhc_pre_params* params, const mhc_pre_ten
  *   hc_eps     >= 0: the hcEps the forward used (hPre = sigmoid(...) + hcEps)
  *   num_iters  0: MhcPre backward (affine hRes); 1 .. 1000: MhcPreSinkhorn backward with
  *              that many Sinkhorn iterations
- *   reserved   must be 0 */
+ *   x_f16      0: x, grad_h_in, grad_x_post and grad_x hold bf16; 1: all four hold fp16
+ *              (IEEE binary16). The guide's section 8.2 gives gradX gradHIn's type, BF16
+ *              or FP16. Other values: PARAM_INVALID. */
 typedef struct mhc_pre_bwd_params {
     int64_t T;
     int32_t n;
     int32_t D;
     double hc_eps;
     int32_t num_iters;
-    int32_t reserved;
+    int32_t x_f16;
 } mhc_pre_bwd_params;
 
-/* Device pointers, M = n*n + 2n, K = n*D. Inputs (x, grad_h_in and grad_x_post bf16
- * bits, the rest float32):
+/* Device pointers, M = n*n + 2n, K = n*D. Inputs (x, grad_h_in and grad_x_post 16-bit
+ * values in the format x_f16 names, the rest float32):
  *   x            [T, n, D], 16-byte aligned                            required
  *   phi          [M, K]                                                required
  *   alpha        [3]                                                   required
@@ -312,7 +314,7 @@ typedef struct mhc_pre_bwd_params {
  *   gamma        [n, D]                                                optional
  *   grad_x_post  [T, n, D], 16-byte aligned: added to gradX            optional
  * Outputs (must not alias inputs or each other):
- *   grad_x       bf16 [T, n, D], 16-byte aligned                       required
+ *   grad_x       [T, n, D] in x's format, 16-byte aligned              required
  *   grad_phi     [M, K]                                                required
  *   grad_alpha   [3]                                                   required
  *   grad_bias    [M]                                                   required

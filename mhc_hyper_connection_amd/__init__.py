@@ -229,10 +229,11 @@ def mhc_pre(x, phi, alpha, bias, gamma=None, pre_mix=None, *, num_iters=20, norm
 class PreBackward:
     """Launcher of the MhcPre backward for one problem size (MhcPreBackward guide,
     0539edu.com/news/4871844, section 3); with num_iters >= 1 the MhcPreSinkhorn backward
-    (the forward's Sinkhorn planes are then inputs). Owns its workspace; calls through
-    one instance must not overlap."""
+    (the forward's Sinkhorn planes are then inputs). x_f16: x, grad_h_in, grad_x_post
+    and grad_x in float16 (else bfloat16). Owns its workspace; calls through one
+    instance must not overlap."""
 
-    def __init__(self, T, n, D, *, hc_eps=1e-6, num_iters=0, device="cuda"):
+    def __init__(self, T, n, D, *, hc_eps=1e-6, num_iters=0, x_f16=False, device="cuda"):
         torch = _torch()
         load()
         self.T, self.n, self.D = int(T), int(n), int(D)
@@ -241,7 +242,8 @@ class PreBackward:
         if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self.num_iters = int(num_iters)
-        self.params = make_bwd_params(T, n, D, hc_eps, num_iters)
+        self.x_f16 = bool(x_f16)
+        self.params = make_bwd_params(T, n, D, hc_eps, num_iters, self.x_f16)
         self.ws_bytes = bwd_workspace_size(self.params)
         self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=self.device)
 
@@ -249,7 +251,8 @@ class PreBackward:
         torch = _torch()
         T, n, D, M, dev = self.T, self.n, self.D, self.M, self.device
         f32 = dict(dtype=torch.float32, device=dev)
-        out = {"grad_x": torch.empty((T, n, D), dtype=torch.bfloat16, device=dev),
+        x16 = torch.float16 if self.x_f16 else torch.bfloat16
+        out = {"grad_x": torch.empty((T, n, D), dtype=x16, device=dev),
                "grad_phi": torch.empty((M, n * D), **f32), "grad_alpha": torch.empty((3,), **f32),
                "grad_bias": torch.empty((M,), **f32)}
         if gamma:
@@ -260,7 +263,8 @@ class PreBackward:
                  h_post, gamma=None, grad_x_post=None, *, sum_out=None, norm_out=None, out=None):
         torch = _torch()
         T, n, D, M, dev = self.T, self.n, self.D, self.M, self.device
-        bf, f32 = torch.bfloat16, torch.float32
+        bf = torch.float16 if self.x_f16 else torch.bfloat16
+        f32 = torch.float32
         for t, name, dt, shape in ((x, "x", bf, (T, n, D)), (phi, "phi", f32, (M, n * D)),
                                    (alpha, "alpha", f32, (3,)), (grad_h_in, "grad_h_in", bf, (T, D)),
                                    (grad_h_post, "grad_h_post", f32, (T, n)),
@@ -278,6 +282,15 @@ class PreBackward:
             _check(norm_out, "norm_out", f32, (2 * it, T, n, n), dev)
         if out is None:
             out = self.alloc_outputs(gamma is not None)
+        else:
+            want = {"grad_x": (bf, (T, n, D)), "grad_phi": (f32, (M, n * D)), "grad_alpha": (f32, (3,)),
+                    "grad_bias": (f32, (M,))}
+            if gamma is not None:
+                want["grad_gamma"] = (f32, (n, D))
+            if set(out) != set(want):
+                raise ValueError(f"out must hold exactly {sorted(want)}")
+            for k, (dt, shape) in want.items():
+                _check(out[k], k, dt, shape, dev)
         ptrs = {"x": _ptr(x), "phi": _ptr(phi), "alpha": _ptr(alpha), "grad_h_in": _ptr(grad_h_in),
                 "grad_h_post": _ptr(grad_h_post), "grad_h_res": _ptr(grad_h_res),
                 "inv_rms": _ptr(inv_rms), "h_mix": _ptr(h_mix), "h_pre": _ptr(h_pre),
@@ -298,17 +311,19 @@ def mhc_pre_backward(x, phi, alpha, grad_h_in, grad_h_post, grad_h_res, inv_rms,
                      h_post, gamma=None, grad_x_post=None, *, hc_eps=1e-6, num_iters=0,
                      sum_out=None, norm_out=None):
     """MhcPre backward (num_iters == 0) or MhcPreSinkhorn backward (num_iters >= 1, with
-    the forward's sum_out [2it, ..., n] and norm_out [2it, ..., n, n]). x: bf16 [T, n, D]
-    or [B, S, n, D]; the other per-token tensors follow x's leading dimensions. Returns
-    dict grad_x, grad_phi, grad_alpha, grad_bias (and grad_gamma when gamma is given)."""
+    the forward's sum_out [2it, ..., n] and norm_out [2it, ..., n, n]). x: bf16 or fp16
+    [T, n, D] or [B, S, n, D] (grad_h_in, grad_x_post and the returned grad_x in the same
+    format); the other per-token tensors follow x's leading dimensions. Returns dict
+    grad_x, grad_phi, grad_alpha, grad_bias (and grad_gamma when gamma is given)."""
     lead = tuple(x.shape[:-2])
     n, D = int(x.shape[-2]), int(x.shape[-1])
     T = math.prod(lead) if lead else 1
-    key = (T, n, D, hc_eps, num_iters, str(x.device))
+    f16 = x.dtype == _torch().float16
+    key = (T, n, D, hc_eps, num_iters, f16, str(x.device))
     r = _BWD_RUNNERS.get(key)
     if r is None:
         r = _BWD_RUNNERS[key] = PreBackward(T, n, D, hc_eps=hc_eps, num_iters=num_iters,
-                                            device=x.device)
+                                            x_f16=f16, device=x.device)
     M = n * n + 2 * n
     rs = lambda t, *shape: None if t is None else t.reshape(*shape)
     out = r(x.reshape(T, n, D), phi, alpha, rs(grad_h_in, T, D), rs(grad_h_post, T, n),

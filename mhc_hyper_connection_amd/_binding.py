@@ -42,7 +42,7 @@ class Tensors(ctypes.Structure):
 class BwdParams(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("n", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("hc_eps", ctypes.c_double), ("num_iters", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("x_f16", ctypes.c_int32)]
 
 
 BWD_TENSOR_FIELDS = ("x", "phi", "alpha", "grad_h_in", "grad_h_post", "grad_h_res", "inv_rms",
@@ -197,8 +197,8 @@ def raw_forward_timed(params: Params, ptrs: dict, ws_ptr, ws_bytes, stream, even
                                             stream, arr, len(events)))
 
 
-def make_bwd_params(T, n, D, hc_eps=1e-6, num_iters=0) -> BwdParams:
-    return BwdParams(int(T), int(n), int(D), float(hc_eps), int(num_iters), 0)
+def make_bwd_params(T, n, D, hc_eps=1e-6, num_iters=0, x_f16=False) -> BwdParams:
+    return BwdParams(int(T), int(n), int(D), float(hc_eps), int(num_iters), int(bool(x_f16)))
 
 
 def bwd_workspace_size(params: BwdParams) -> int:

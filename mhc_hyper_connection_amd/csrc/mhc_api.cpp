@@ -232,11 +232,11 @@ namespace {
 mhc_status check_bwd_params(const mhc_pre_bwd_params* p, mhc::bwd::Geometry* g)
 {
     if (!p) return MHC_ERR_NULLPTR;
-    if (p->reserved != 0) return MHC_ERR_PARAM_INVALID;
+    if (p->x_f16 != 0 && p->x_f16 != 1) return MHC_ERR_PARAM_INVALID;
     if (p->num_iters < 0 || p->num_iters > 1000) return MHC_ERR_PARAM_INVALID;
     if (!(p->hc_eps >= 0.0)) return MHC_ERR_PARAM_INVALID;    // also rejects NaN
     if (p->T < 0) return MHC_ERR_PARAM_INVALID;
-    if (!mhc::bwd::make_geometry(p->n, p->D, g)) return MHC_ERR_PARAM_INVALID;
+    if (!mhc::bwd::make_geometry(p->n, p->D, g, p->x_f16 == 1)) return MHC_ERR_PARAM_INVALID;
     return MHC_OK;
 }
 

@@ -24,6 +24,8 @@
 //                       matrix cores with x transposed through LDS; group sums to partials
 //   bwd_reduce_*        fixed-order fp64 sums of the partials (gradPhi, gradGamma) and
 //                       of the per-token terms (gradAlpha, gradBias)
+// x, gradHIn, gradXPost and gradX are bf16, or all fp16 (the guide's section 8.2: gradX
+// takes gradHIn's type); template flag H selects fp16.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -50,6 +52,22 @@ __device__ __forceinline__ Split3 split3(float v)
     const float r2 = r1 - __uint_as_float(s.t[1] << 16);
     s.t[2] = f32_to_bf16_bits(r2);
     return s;
+}
+
+// Eight fp16 values -> two bf16 operands whose sum is each value exactly: hi = RNE(v)
+// keeps 8 of its 11 significant bits; lo = v - hi is a multiple of v's fp16 ulp of at most
+// 4 of them (3 significant bits), well inside bf16's exponent range.
+__device__ __forceinline__ void split_f16x8(u32x4 w, bf16x8& hi, bf16x8& lo)
+{
+    u32x4 h, l;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+        const float v0 = f16_lo(w[e2]), v1 = f16_hi(w[e2]);
+        h[e2] = pack_bf16x2(v0, v1);
+        l[e2] = pack_bf16x2(v0 - bf16_lo(h[e2]), v1 - bf16_hi(h[e2]));
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 // ------------------------------------------------------------------ weight pack
 
@@ -198,7 +216,7 @@ __device__ __forceinline__ double wave_sum(double v)
 // One wave per token (4 per workgroup). Outputs: gMix [T][KS][3][32] (three bf16 terms
 // of each f32 value, zero past M), c3 [T], terms [3 + M][T] (fp64: the token's alpha
 // terms, then its bias terms).
-template <int N>
+template <int N, bool H>
 __global__ void __launch_bounds__(256)
 bwd_token_kernel(Args a, int64_t T, int D)
 {
@@ -209,8 +227,9 @@ bwd_token_kernel(Args a, int64_t T, int D)
     if (t >= T) return;
     const int64_t K = (int64_t)N * D;
 
-    // 3.1: gHPre_i = sum_d gradHIn[d] x[i, d]; a bf16 x bf16 product is exact in fp32,
-    // the sums run in fp64 (per lane, then across lanes)
+    // 3.1: gHPre_i = sum_d gradHIn[d] x[i, d]; a product of two bf16 or two fp16 values is
+    // exact in fp32 (at most 22 significant bits), the sums run in fp64 (per lane, then
+    // across lanes)
     double acc[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.0;
@@ -223,8 +242,8 @@ bwd_token_kernel(Args a, int64_t T, int D)
             const u32x4 xv = *reinterpret_cast<const u32x4*>(xt + (int64_t)i * D + 8 * o);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                acc[i] += (double)(bf16_lo(gh[e]) * bf16_lo(xv[e]));
-                acc[i] += (double)(bf16_hi(gh[e]) * bf16_hi(xv[e]));
+                acc[i] += (double)(x16_lo<H>(gh[e]) * x16_lo<H>(xv[e]));
+                acc[i] += (double)(x16_hi<H>(gh[e]) * x16_hi<H>(xv[e]));
             }
         }
     }
@@ -325,11 +344,14 @@ struct MainCfg {
     static constexpr int MAIN_BYTES = PACK_BYTES + XT_BYTES + GT_BYTES;
     static constexpr int LDS_BYTES = MAIN_BYTES > RED_BYTES ? MAIN_BYTES : RED_BYTES;
     static_assert((RB * CB) % 4 == 0, "gradPhi blocks divide among the four waves");
+    static_assert(CB % 4 == 0, "wave w's gradPhi blocks use column blocks w, w + 4, ..");
     static_assert(XT_BYTES % 16 == 0 && PACK_BYTES % 16 == 0, "LDS regions stay 16-byte aligned");
 };
 
-// GAMMA: gamma given (gradX scales xrsGrad, gradGamma is summed); XPOST: gradXPost given.
-template <int N, int SGN, int KS, bool GAMMA, bool XPOST>
+// GAMMA: gamma given (gradX scales xrsGrad, gradGamma is summed); XPOST: gradXPost given;
+// H: x, gradHIn, gradXPost and gradX in fp16 (x then enters gMix^T . x as two exact bf16
+// terms, six products instead of three).
+template <int N, int SGN, int KS, bool GAMMA, bool XPOST, bool H>
 __global__ void __launch_bounds__(kThreads, GAMMA ? 2 : 3)
 bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, int64_t tasks)
 {
@@ -443,7 +465,7 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) xg[4 * h + r] = acc[r];
             }
-            // gradX = gradHIn hPre + xrsGrad gamma - c3 x (+ gradXPost), one RNE to bf16
+            // gradX = gradHIn hPre + xrsGrad gamma - c3 x (+ gradXPost), one RNE to x's format
             u32x4 o;
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
@@ -451,14 +473,14 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, 
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl) {
                     const int e = 2 * e2 + hl;
-                    const float xe = hl ? bf16_hi(xv[s][e2]) : bf16_lo(xv[s][e2]);
-                    const float ge = hl ? bf16_hi(gh[e2]) : bf16_lo(gh[e2]);
+                    const float xe = hl ? x16_hi<H>(xv[s][e2]) : x16_lo<H>(xv[s][e2]);
+                    const float ge = hl ? x16_hi<H>(gh[e2]) : x16_lo<H>(gh[e2]);
                     v[hl] = fmaf(ge, hp[s], GAMMA ? xg[e] * gam[GAMMA ? s : 0][e] : xg[e]);
                     v[hl] = fmaf(-c3, xe, v[hl]);
-                    if constexpr (XPOST) v[hl] += hl ? bf16_hi(xp[s][e2]) : bf16_lo(xp[s][e2]);
+                    if constexpr (XPOST) v[hl] += hl ? x16_hi<H>(xp[s][e2]) : x16_lo<H>(xp[s][e2]);
                     if constexpr (GAMMA) gg[s][e] = fmaf(xe, xg[e], gg[s][e]);
                 }
-                o[e2] = pack_bf16x2(v[0], v[1]);
+                o[e2] = pack_x16<H>(v[0], v[1]);
             }
             const uint32_t off = dval ? (uint32_t)(((int64_t)row * K + (int64_t)(sg * SGN + s) * D + d0) * 2) : kOutOfRange;
             __builtin_amdgcn_raw_buffer_store_b128(o, rgx, (int)off, 0, 0);
@@ -480,7 +502,19 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, 
         __syncthreads();
 
         // gradPhi partial: C[m][col] += sum over the tile's tokens of gMix[t][m] x[t][col];
-        // A = gMix^T (rows m, three terms), B = x (columns), 32 tokens per K-step
+        // A = gMix^T (rows m, three terms), B = x (columns), 32 tokens per K-step. Block
+        // bi = wave + 4 q has column block (wave + 4 q) % CB = wave + 4 (q % NCW): fp16 x
+        // is split into its two bf16 terms once per column block and K-step.
+        constexpr int NCW = CB / 4;
+        bf16x8 bxh[H ? NCW : 1][2], bxl[H ? NCW : 1][2];
+        if constexpr (H) {
+#pragma unroll
+            for (int c = 0; c < NCW; ++c)
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+                    split_f16x8(*reinterpret_cast<const u32x4*>(xT + tslot(16 * (wave + 4 * c) + j, 32 * kt + 8 * grp)),
+                                bxh[c][kt], bxl[c][kt]);
+        }
 #pragma unroll
         for (int q = 0; q < BPW; ++q) {
             const int bi = wave + 4 * q;
@@ -491,10 +525,20 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, 
 #pragma unroll
                 for (int p = 0; p < 3; ++p)
                     at[p] = *reinterpret_cast<const bf16x8*>(gT + tslot(p * MP + 16 * rb + j, 32 * kt + 8 * grp));
-                const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xT + tslot(16 * cb + j, 32 * kt + 8 * grp));
+                if constexpr (H) {
+                    const int c = q % NCW;
 #pragma unroll
-                for (int p = 2; p >= 0; --p)
-                    pacc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at[p], bv, pacc[q], 0, 0, 0);
+                    for (int p = 2; p >= 0; --p)
+                        pacc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at[p], bxl[c][kt], pacc[q], 0, 0, 0);
+#pragma unroll
+                    for (int p = 2; p >= 0; --p)
+                        pacc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at[p], bxh[c][kt], pacc[q], 0, 0, 0);
+                } else {
+                    const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xT + tslot(16 * cb + j, 32 * kt + 8 * grp));
+#pragma unroll
+                    for (int p = 2; p >= 0; --p)
+                        pacc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at[p], bv, pacc[q], 0, 0, 0);
+                }
             }
         }
         __syncthreads();   // xT and gT are rewritten by the next tile
@@ -595,14 +639,14 @@ bwd_zero_kernel(Args a, int64_t MK, int64_t K, int M)
     if (idx < M) a.grad_bias[idx] = 0.f;
 }
 
-template <int N, int SGN, int KS, bool GAMMA, bool XPOST>
+template <int N, int SGN, int KS, bool GAMMA, bool XPOST, bool H>
 void launch_main(const Plan& p, const Args& a, hipStream_t st)
 {
-    hipLaunchKernelGGL((bwd_main_kernel<N, SGN, KS, GAMMA, XPOST>), dim3((unsigned)p.main_blocks),
+    hipLaunchKernelGGL((bwd_main_kernel<N, SGN, KS, GAMMA, XPOST, H>), dim3((unsigned)p.main_blocks),
                        dim3(kThreads), 0, st, a, p.T, p.g.D, p.g.nblk, p.tpg, p.tiles, p.main_tasks);
 }
 
-template <int N, int SGN, int KS>
+template <int N, int SGN, int KS, bool H>
 hipError_t launch_all(const Plan& p, const Args& a, hipStream_t st)
 {
     const Geometry& g = p.g;
@@ -618,15 +662,15 @@ hipError_t launch_all(const Plan& p, const Args& a, hipStream_t st)
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(bwd_token_kernel<N>, dim3((unsigned)p.token_blocks), dim3(256), 0, st, a, p.T, g.D);
+    hipLaunchKernelGGL((bwd_token_kernel<N, H>), dim3((unsigned)p.token_blocks), dim3(256), 0, st, a, p.T, g.D);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.gamma) {
-        if (a.grad_x_post) launch_main<N, SGN, KS, true, true>(p, a, st);
-        else launch_main<N, SGN, KS, true, false>(p, a, st);
+        if (a.grad_x_post) launch_main<N, SGN, KS, true, true, H>(p, a, st);
+        else launch_main<N, SGN, KS, true, false, H>(p, a, st);
     } else {
-        if (a.grad_x_post) launch_main<N, SGN, KS, false, true>(p, a, st);
-        else launch_main<N, SGN, KS, false, false>(p, a, st);
+        if (a.grad_x_post) launch_main<N, SGN, KS, false, true, H>(p, a, st);
+        else launch_main<N, SGN, KS, false, false, H>(p, a, st);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -651,8 +695,10 @@ int launch_backward(const Plan& p, const Args& a, void* stream)
         hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((MK + 255) / 256)), dim3(256), 0, st, a, MK, g.K, g.M);
         return (int)hipGetLastError();
     }
-    if (g.n == 4 && g.SGN == 4 && g.KS == 1) return (int)launch_all<4, 4, 1>(p, a, st);
-    if (g.n == 8 && g.SGN == 2 && g.KS == 3) return (int)launch_all<8, 2, 3>(p, a, st);
+    if (g.n == 4 && g.SGN == 4 && g.KS == 1)
+        return (int)(g.x_f16 ? launch_all<4, 4, 1, true>(p, a, st) : launch_all<4, 4, 1, false>(p, a, st));
+    if (g.n == 8 && g.SGN == 2 && g.KS == 3)
+        return (int)(g.x_f16 ? launch_all<8, 2, 3, true>(p, a, st) : launch_all<8, 2, 3, false>(p, a, st));
     return (int)hipErrorInvalidValue;
 }
 

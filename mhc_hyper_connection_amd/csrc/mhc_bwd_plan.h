@@ -52,6 +52,7 @@ struct Geometry {
     int nblk = 0;        // d-blocks: ceil(D / 32)
     int SGN = 0;         // streams per main-pass workgroup
     int NSG = 0;         // stream groups: n / SGN
+    int x_f16 = 0;       // x, gradHIn, gradXPost and gradX in fp16 (else bf16)
     size_t pack_bytes = 0;
 };
 
@@ -68,7 +69,7 @@ MHC_BWD_HOST_DEVICE inline int64_t pack_at(int b, int i, int n, int KS)
 // 8g .. 8g+7 across the two halves (rows 4g .. 4g+3 of each).
 MHC_BWD_HOST_DEVICE inline int pack_col(int h, int row) { return 8 * (row / 4) + 4 * h + (row % 4); }
 
-inline bool make_geometry(int n, int D, Geometry* g)
+inline bool make_geometry(int n, int D, Geometry* g, bool x_f16 = false)
 {
     if (n != 4 && n != 8) return false;
     if (D < 8 || D % 8 != 0 || D > kMaxD) return false;
@@ -83,6 +84,7 @@ inline bool make_geometry(int n, int D, Geometry* g)
     r.SGN = n == 4 ? 4 : 2;
     r.NSG = n / r.SGN;
     r.pack_bytes = (size_t)r.nblk * n * pack_units_per_stream(r.KS) * 16;
+    r.x_f16 = x_f16 ? 1 : 0;
     *g = r;
     return true;
 }

@@ -31,6 +31,7 @@ MhcPre backward inputs (``backward_inputs``; M = n*n + 2n), drawn in this order:
   h_post       [T, n]     U(0, 2)          (the range of 2 sigmoid)
   gamma        [n, D]     U(0.5, 1.5)      (when asked for)
   grad_x_post  [T, n, D]  N(0, 1) -> bf16  (when asked for)
+  (x_f16: x, grad_h_in and grad_x_post rounded to binary16 instead, as for the forward)
   sum_out      [2 it, T, n]     U(0.9, 1.1)    (when Sinkhorn planes are asked for)
   norm_out     [2 it, T, n, n]  U(0.05, 0.45)
 hc_post inputs (``post_inputs``), drawn in this order:
@@ -164,11 +165,12 @@ def custom(T: int, n: int, D: int, *, n_alpha: int = 3, gamma: bool = False,
     return generate(wl)
 
 
-def _bf16_normal(rng, count: int) -> np.ndarray:
+def _x16_normal(rng, count: int, f16: bool = False) -> np.ndarray:
     out = np.empty(count, dtype=np.uint16)
     for start in range(0, count, X_CHUNK):
         stop = min(count, start + X_CHUNK)
-        out[start:stop] = f32_to_bf16_bits(rng.standard_normal(stop - start, dtype=np.float32))
+        v = rng.standard_normal(stop - start, dtype=np.float32)
+        out[start:stop] = v.astype(np.float16).view(np.uint16) if f16 else f32_to_bf16_bits(v)
     return out
 
 
@@ -193,6 +195,7 @@ class BwdInputs:
     num_iters: int = 0                     # >= 1: Sinkhorn planes below
     sum_out: np.ndarray | None = None      # float32 [2 it, T, n]
     norm_out: np.ndarray | None = None     # float32 [2 it, T, n, n]
+    x_f16: bool = False                    # x, grad_h_in, grad_x_post as binary16 bits
 
     @property
     def M(self) -> int:
@@ -200,14 +203,14 @@ class BwdInputs:
 
 
 def backward_inputs(T: int, n: int, D: int, *, gamma: bool = False, x_post: bool = False,
-                    sinkhorn_iters: int = 0, seed: int = 11) -> BwdInputs:
+                    sinkhorn_iters: int = 0, seed: int = 11, x_f16: bool = False) -> BwdInputs:
     """Inputs of the MhcPre backward with the recipe in the module docstring."""
     rng = np.random.default_rng(seed)
     M, K = n * n + 2 * n, n * D
-    x = _bf16_normal(rng, T * K).reshape(T, n, D)
+    x = _x16_normal(rng, T * K, x_f16).reshape(T, n, D)
     phi = (rng.standard_normal((M, K), dtype=np.float32) / np.float32(np.sqrt(K))).astype(np.float32)
     alpha = rng.uniform(0.5, 1.5, size=3).astype(np.float32)
-    ghin = _bf16_normal(rng, T * D).reshape(T, D)
+    ghin = _x16_normal(rng, T * D, x_f16).reshape(T, D)
     ghpost = rng.standard_normal((T, n), dtype=np.float32)
     ghres = rng.standard_normal((T, n, n), dtype=np.float32)
     inv = rng.uniform(0.5, 1.5, size=T).astype(np.float32)
@@ -215,8 +218,9 @@ def backward_inputs(T: int, n: int, D: int, *, gamma: bool = False, x_post: bool
     hpre = (rng.uniform(0.0, 1.0, size=(T, n)) + 1e-6).astype(np.float32)
     hpost = rng.uniform(0.0, 2.0, size=(T, n)).astype(np.float32)
     g = rng.uniform(0.5, 1.5, size=(n, D)).astype(np.float32) if gamma else None
-    gxp = _bf16_normal(rng, T * K).reshape(T, n, D) if x_post else None
-    bi = BwdInputs(T, n, D, x, phi, alpha, ghin, ghpost, ghres, inv, hmix, hpre, hpost, g, gxp)
+    gxp = _x16_normal(rng, T * K, x_f16).reshape(T, n, D) if x_post else None
+    bi = BwdInputs(T, n, D, x, phi, alpha, ghin, ghpost, ghres, inv, hmix, hpre, hpost, g, gxp,
+                   x_f16=x_f16)
     if sinkhorn_iters:
         bi.num_iters = sinkhorn_iters
         bi.sum_out = rng.uniform(0.9, 1.1, size=(2 * sinkhorn_iters, T, n)).astype(np.float32)
@@ -238,8 +242,8 @@ class PostInputs:
 def post_inputs(T: int, n: int, D: int, *, seed: int = 21) -> PostInputs:
     """Inputs of hc_post with the recipe in the module docstring."""
     rng = np.random.default_rng(seed)
-    x = _bf16_normal(rng, T * D).reshape(T, D)
-    residual = _bf16_normal(rng, T * n * D).reshape(T, n, D)
+    x = _x16_normal(rng, T * D).reshape(T, D)
+    residual = _x16_normal(rng, T * n * D).reshape(T, n, D)
     post = rng.uniform(0.0, 2.0, size=(T, n)).astype(np.float32)
     comb = rng.uniform(0.05, 0.45, size=(T, n, n)).astype(np.float32)
     return PostInputs(T, n, D, x, residual, post, comb)
@@ -272,7 +276,7 @@ def stage_inputs(T: int, n: int, D: int, *, n_alpha: int = 3, pre_mix: bool = Fa
     if x_f16:
         x = rng.standard_normal(T * n * D, dtype=np.float32).astype(np.float16).view(np.uint16).reshape(T, n, D)
     else:
-        x = _bf16_normal(rng, T * n * D).reshape(T, n, D)
+        x = _x16_normal(rng, T * n * D).reshape(T, n, D)
     alpha = rng.uniform(0.5, 1.5, size=n_alpha).astype(np.float32)
     bias = (0.1 * rng.standard_normal(M)).astype(np.float32)
     hmix = rng.standard_normal((T, M), dtype=np.float32)

@@ -59,10 +59,14 @@ def test_invalid_attributes(kw):
         B.bwd_workspace_size(p)
 
 
-def test_reserved_fields():
-    p = B.make_bwd_params(128, 4, 256)
-    p.reserved = 1
-    assert bwd(p) == B.MHC_ERR_PARAM_INVALID
+def test_format_flag_and_iterations():
+    for v in (-1, 2):
+        p = B.make_bwd_params(128, 4, 256)
+        p.x_f16 = v
+        assert bwd(p) == B.MHC_ERR_PARAM_INVALID, v
+    # fp16 needs the same workspace as bf16
+    assert B.bwd_workspace_size(B.make_bwd_params(128, 4, 256, x_f16=True)) == \
+        B.bwd_workspace_size(B.make_bwd_params(128, 4, 256))
     for it in (-1, 1001):
         p = B.make_bwd_params(128, 4, 256, num_iters=it)
         assert bwd(p) == B.MHC_ERR_PARAM_INVALID, it

@@ -2,11 +2,14 @@
 fp64 oracle (oracle/mhc_oracle_bwd.c), on seeded synthetic inputs (synth.backward_inputs).
 
 Acceptance rule, derived from the arithmetic of the GPU path:
-  gradX (bf16), every element: within 1 bf16 ulp of the oracle's correctly rounded value,
-      or |gpu - ref| <= 2^-18 * A, A = the sum of |terms| of the element (the oracle's
-      grad_x_abs). gradX is formed in fp32 from five terms, one of them a split-bf16
-      matrix-core product accurate to ~2^-22 of its terms, so the fp32 error is far below
-      2^-18 A; the branch matters only where the terms cancel.
+  gradX (bf16, or fp16 with fp16 inputs), every element: within 1 ulp of the oracle's
+      correctly rounded value, or |gpu - ref| <= 2^-18 * A, A = the sum of |terms| of the
+      element (the oracle's grad_x_abs). gradX is formed in fp32 from five terms, one of
+      them a split-bf16 matrix-core product accurate to ~2^-22 of its terms, so the fp32
+      error e is far below 2^-18 A. Rounding a value within e of the exact one lands within
+      1 ulp of the correctly rounded result whenever e < 1 ulp; otherwise the result is
+      within half an ulp + e <= 1.5 e of the exact value. The rule is the same for both
+      formats; the branch matters only where the terms cancel.
   gradPhi, gradGamma (f32), every element: |gpu - ref| <= 2e-4 |ref| + 2^-14 A, A the
       oracle's sum of |terms|. Each is an fp32 sum over the tokens of one group (up to a
       few hundred rounding steps into the accumulator, each <= 2^-24 of a partial sum
@@ -33,8 +36,8 @@ def gpu_backward(bi, repeat=1):
     import torch
     dev = device()
     it = bi.num_iters
-    r = mhc.PreBackward(bi.T, bi.n, bi.D, hc_eps=bi.hc_eps, num_iters=it, device=dev)
-    args = [to_dev(a, dev) for a in (bi.x, bi.phi, bi.alpha, bi.grad_h_in, bi.grad_h_post,
+    r = mhc.PreBackward(bi.T, bi.n, bi.D, hc_eps=bi.hc_eps, num_iters=it, x_f16=bi.x_f16, device=dev)
+    args = [to_dev(a, dev, bi.x_f16) for a in (bi.x, bi.phi, bi.alpha, bi.grad_h_in, bi.grad_h_post,
                                      bi.grad_h_res, bi.inv_rms, bi.h_mix, bi.h_pre, bi.h_post,
                                      bi.gamma, bi.grad_x_post)]
     planes = {}
@@ -44,8 +47,8 @@ def gpu_backward(bi, repeat=1):
     results = []
     for _ in range(repeat):
         for v in out.values():
-            if v.dtype == torch.bfloat16:
-                v.view(torch.int16).fill_(0x7FC0)   # NaN: anything not written shows
+            if v.dtype in (torch.bfloat16, torch.float16):   # NaN: anything not written shows
+                v.view(torch.int16).fill_(0x7FC0 if v.dtype == torch.bfloat16 else 0x7E00)
             else:
                 v.fill_(float("nan"))
         r(*args, out=out, **planes)
@@ -58,22 +61,22 @@ def run_oracle(bi, tokens=None):
     return oracle.backward(bi.x, bi.phi, bi.alpha, bi.grad_h_in, bi.grad_h_post, bi.grad_h_res,
                            bi.inv_rms, bi.h_mix, bi.h_pre, bi.h_post, bi.gamma, bi.grad_x_post,
                            hc_eps=bi.hc_eps, tokens=tokens, num_iters=bi.num_iters,
-                           sum_out=bi.sum_out, norm_out=bi.norm_out)
+                           sum_out=bi.sum_out, norm_out=bi.norm_out, x_f16=bi.x_f16)
 
 
-def sinkhorn_inputs(T, n, D, it, *, gamma=False, post=False, seed=31):
+def sinkhorn_inputs(T, n, D, it, *, gamma=False, post=False, seed=31, f16=False):
     """MhcPreSinkhorn backward inputs: the forward's saved values (invRms, hMix, hPre,
     hPost, sumOut, normOut) come from the fp64 oracle forward on seeded inputs, rounded
     to float32 as the forward emits them; the incoming gradients are seeded draws."""
-    inp = synth.custom(T, n, D, gamma=gamma, need_backward=True, num_iters=it, seed=seed)
+    inp = synth.custom(T, n, D, gamma=gamma, need_backward=True, num_iters=it, seed=seed, x_f16=f16)
     f = oracle.forward(inp.x, inp.phi, inp.alpha, inp.bias, inp.gamma, num_iters=it,
-                       want_h_in=False)
-    g = synth.backward_inputs(T, n, D, x_post=post, seed=seed + 1000)
+                       want_h_in=False, x_f16=f16)
+    g = synth.backward_inputs(T, n, D, x_post=post, seed=seed + 1000, x_f16=f16)
     f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
     return synth.BwdInputs(T, n, D, inp.x, inp.phi, inp.alpha, g.grad_h_in, g.grad_h_post,
                            g.grad_h_res, f32(f.inv_rms), f32(f.h_mix), f32(f.h_pre), f32(f.h_post),
                            inp.gamma, g.grad_x_post, num_iters=it, sum_out=f32(f.sum_out),
-                           norm_out=f32(f.norm_out))
+                           norm_out=f32(f.norm_out), x_f16=f16)
 
 
 def _bound_check(name, g, r, a, rtol, atab, rep):
@@ -95,7 +98,8 @@ def compare(g, o, bi, tokens=None):
         sl = slice(r0, min(len(tok), r0 + 1024))
         gx = gx_all[sl]
         dist = np.abs(bf16_ordered(gx) - bf16_ordered(o.grad_x_bits[sl]))
-        cancel = np.abs(bf16_bits_to_f32(gx).astype(np.float64) - o.grad_x[sl]) <= 2.0 ** -18 * o.grad_x_abs[sl]
+        gv = gx.view(np.float16) if bi.x_f16 else bf16_bits_to_f32(gx)
+        cancel = np.abs(gv.astype(np.float64) - o.grad_x[sl]) <= 2.0 ** -18 * o.grad_x_abs[sl]
         ok = (dist <= 1) | cancel
         nel += int(dist.size)
         fails += int((~ok).sum())
@@ -135,6 +139,47 @@ def test_backward_parity(name, T, n, D, gamma, post, seed):
     print(f"[case] backward {name} T={T} n={n} D={D} gamma={gamma} post={post}", file=sys.stderr, flush=True)
     bi = synth.backward_inputs(T, n, D, gamma=gamma, x_post=post, seed=seed)
     compare(gpu_backward(bi), run_oracle(bi), bi)
+
+
+F16_CASES = [
+    # fp16 x, gradHIn, gradXPost and gradX: (name, T, n, D, gamma, grad_x_post, seed)
+    ("f16_T1_D8", 1, 4, 8, False, False, 61),
+    ("f16_T65_D40_ragged_gamma_post", 65, 4, 40, True, True, 62),
+    ("f16_T200_D7168_gamma_post", 200, 4, 7168, True, True, 63),
+    ("f16_T300_D1000", 300, 4, 1000, False, False, 64),
+    ("f16_n8_T70_D256_gamma_post", 70, 8, 256, True, True, 65),
+    ("f16_n8_T129_D2048", 129, 8, 2048, False, False, 66),
+    ("f16_T4097_D256_groups", 4097, 4, 256, True, False, 67),
+]
+
+
+@pytest.mark.parametrize("name,T,n,D,gamma,post,seed", F16_CASES, ids=[c[0] for c in F16_CASES])
+def test_backward_parity_f16(name, T, n, D, gamma, post, seed):
+    print(f"[case] backward {name} T={T} n={n} D={D} gamma={gamma} post={post}", file=sys.stderr, flush=True)
+    bi = synth.backward_inputs(T, n, D, gamma=gamma, x_post=post, seed=seed, x_f16=True)
+    compare(gpu_backward(bi), run_oracle(bi), bi)
+
+
+def test_backward_f16_through_the_wrapper():
+    # mhc_pre_backward picks fp16 from x's dtype, on [B, S, n, D] tensors: the same bits
+    # as the launcher it builds
+    import mhc_hyper_connection_amd as mhc
+    print("[case] backward f16 wrapper B=2 S=33 n=4 D=512", file=sys.stderr, flush=True)
+    bi = synth.backward_inputs(66, 4, 512, gamma=True, x_post=True, seed=68, x_f16=True)
+    want = gpu_backward(bi)
+    dev = device()
+    t = lambda a: to_dev(a, dev, True)
+    got = mhc.mhc_pre_backward(t(bi.x).reshape(2, 33, 4, 512), t(bi.phi), t(bi.alpha),
+                               t(bi.grad_h_in).reshape(2, 33, 512), t(bi.grad_h_post).reshape(2, 33, 4),
+                               t(bi.grad_h_res).reshape(2, 33, 4, 4), t(bi.inv_rms).reshape(2, 33),
+                               t(bi.h_mix).reshape(2, 33, -1), t(bi.h_pre).reshape(2, 33, 4),
+                               t(bi.h_post).reshape(2, 33, 4), t(bi.gamma),
+                               t(bi.grad_x_post).reshape(2, 33, 4, 512), hc_eps=bi.hc_eps)
+    import torch
+    assert got["grad_x"].dtype == torch.float16 and got["grad_x"].shape == (2, 33, 4, 512)
+    for k, v in got.items():
+        h = to_host(v.reshape(want[k].shape))
+        assert np.array_equal(h.view(np.uint8), want[k].view(np.uint8)), k
 
 
 def test_backward_empty_tokens():
@@ -185,6 +230,20 @@ def test_sinkhorn_backward_parity(name, T, n, D, it, gamma, post, seed):
     print(f"[case] sinkhorn backward {name} T={T} n={n} D={D} it={it}", file=sys.stderr, flush=True)
     bi = sinkhorn_inputs(T, n, D, it, gamma=gamma, post=post, seed=seed)
     compare(gpu_backward(bi), run_oracle(bi), bi)
+
+
+def test_sinkhorn_backward_f16():
+    print("[case] sinkhorn backward f16 T=130 n=4 D=512 it=3 gamma post", file=sys.stderr, flush=True)
+    bi = sinkhorn_inputs(130, 4, 512, 3, gamma=True, post=True, seed=48, f16=True)
+    compare(gpu_backward(bi), run_oracle(bi), bi)
+
+
+def test_backward_large_workload_shape_f16():
+    # the large prefill shape with fp16 x and gradients: every gradient, every row
+    print("[case] backward large f16 T=16384 D=7168", file=sys.stderr, flush=True)
+    bi = synth.backward_inputs(16384, 4, 7168, seed=16, x_f16=True)
+    rep = compare(gpu_backward(bi), run_oracle(bi), bi)
+    assert rep["grad_x"]["n"] == 16384 * 4 * 7168
 
 
 def test_sinkhorn_backward_large_workload_shape():
