@@ -225,7 +225,7 @@ def cpu_baseline_bwd(bi, max_tokens: int):
                     bi.h_post[:ntok], bi.gamma, None if bi.grad_x_post is None else bi.grad_x_post[:ntok],
                     hc_eps=bi.hc_eps, num_iters=it,
                     sum_out=bi.sum_out[:, :ntok] if it else None,
-                    norm_out=bi.norm_out[:, :ntok] if it else None)
+                    norm_out=bi.norm_out[:, :ntok] if it else None, x_f16=bi.x_f16)
     dt = time.perf_counter() - t0
     return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {ntok} of {bi.T} tokens as a problem of their own, every gradient, "
@@ -235,7 +235,8 @@ def cpu_baseline_bwd(bi, max_tokens: int):
 def main_backward(args):
     """--op backward: one step = one mhc_pre_backward call at the large prefill shape
     (T = 16384, n = 4, D = 7168, no gamma, no gradXPost), through --bwd-iters Sinkhorn
-    iterations (20, as the forward's; 0 = the MhcPre backward)."""
+    iterations (20, as the forward's; 0 = the MhcPre backward); --bwd-f16: x, gradHIn and
+    gradX in fp16."""
     import torch
 
     import mhc_hyper_connection_amd as mhc
@@ -244,19 +245,20 @@ def main_backward(args):
     T, n, D = 16384, 4, 7168
     print(f"[bench] generating backward inputs T={T} n={n} D={D}", file=sys.stderr, flush=True)
     it = args.bwd_iters
-    bi = synth.backward_inputs(T, n, D, sinkhorn_iters=it, seed=1003)
+    f16 = args.bwd_f16
+    bi = synth.backward_inputs(T, n, D, sinkhorn_iters=it, seed=1003, x_f16=f16)
     dev = torch.device("cuda", 0)
 
     def up(a):
         if a is None:
             return None
         if a.dtype.name == "uint16":
-            return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(a.view("int16")).view(torch.float16 if f16 else torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
     args_dev = [up(a) for a in (bi.x, bi.phi, bi.alpha, bi.grad_h_in, bi.grad_h_post, bi.grad_h_res,
                                 bi.inv_rms, bi.h_mix, bi.h_pre, bi.h_post, bi.gamma, bi.grad_x_post)]
-    run = mhc.PreBackward(T, n, D, hc_eps=bi.hc_eps, num_iters=it, device=dev)
+    run = mhc.PreBackward(T, n, D, hc_eps=bi.hc_eps, num_iters=it, x_f16=f16, device=dev)
     out = run.alloc_outputs(bi.gamma is not None)
     planes = {"sum_out": up(bi.sum_out), "norm_out": up(bi.norm_out)} if it else {}
     stream = torch.cuda.current_stream(dev)
@@ -281,9 +283,10 @@ def main_backward(args):
     line = {
         "metric": BWD_METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16" if f16 else "bf16",
         "data": "synthetic",
-        "config": {"workload": "large_prefill_backward", "T": T, "n": n, "D": D, "gamma": False,
+        "config": {"workload": "large_prefill_backward" + ("_f16" if f16 else ""), "T": T, "n": n, "D": D,
+                   "gamma": False,
                    "grad_x_post": False, "num_iters": it,
                    "step": "one mhc_pre_backward call (all of its kernels)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -393,6 +396,8 @@ def main():
                          "MhcPre backward at the large prefill shape; post: hc_post at that shape")
     ap.add_argument("--bwd-iters", type=int, default=20,
                     help="Sinkhorn iterations of the backward (0: the MhcPre backward)")
+    ap.add_argument("--bwd-f16", action="store_true",
+                    help="the backward with x, gradHIn and gradX in fp16 (else bf16)")
     ap.add_argument("--cpu-tokens-bwd", type=int, default=16384,
                     help="tokens the CPU oracle baseline of the backward runs on (bounded)")
     args = ap.parse_args()

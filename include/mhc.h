@@ -54,7 +54,8 @@ typedef int32_t mhc_status;
 /* Problem description (host memory; read during the call only).
  *   T              tokens, >= 0
  *   n              hyper-streams (hcMult): 4, 6 or 8 (the aclnnMhcPreV2 guide, section 7.3,
- *                  allows these three); the MhcPre backward takes 4 or 8
+ *                  allows these three; the MhcPreBackward guide, section 5, the same
+ *                  three for the backward)
  *   D              hidden size per stream: a multiple of 8 in [8, 16384]; with n == 8 and
  *                  n_alpha == 3 at most 8192
  *   n_alpha        3 (pre/post/res branches, phi has n*n+2n rows) or
@@ -283,7 +284,7 @@ mhc_status mhc_pre_forward_timed(const mhc_pre_params* params, const mhc_pre_ten
  *
  * Problem description (host memory):
  *   T          tokens, >= 0
- *   n          4 or 8;  D  a multiple of 8 in [8, 16384]
+ *   n          4, 6 or 8;  D  a multiple of 8 in [8, 16384]
  *   hc_eps     >= 0: the hcEps the forward used (hPre = sigmoid(...) + hcEps)
  *   num_iters  0: MhcPre backward (affine hRes); 1 .. 1000: MhcPreSinkhorn backward with
  *              that many Sinkhorn iterations

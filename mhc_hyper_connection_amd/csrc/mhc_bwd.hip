@@ -107,27 +107,41 @@ bwd_pack_kernel(const float* __restrict__ phi, u32x4* __restrict__ pack, int n, 
 // ------------------------------------------------------------------ Sinkhorn backward
 
 // MhcPreSinkhorn only: the residual logits' gradient through the forward's saved planes,
-// fp64. 64 / (N*N) tokens per wave, one lane per matrix entry e = r N + c. With G =
+// fp64. 64 / (N*N) tokens per wave (one for n = 6, whose 36 entries do not tile a wave:
+// lanes 36 to 63 then compute along from clamped addresses and store nothing), one lane
+// per matrix entry e = r N + c. With G =
 // gradHRes and, for k = 2 it - 1 down to 1, A_k = norm_out[k], s_k = sum_out[k]: a column
 // step (k odd) passes G -> (G - sum_r G A_k) / s_k[c], a row step the same along the row;
 // the first step (row softmax + eps) passes P (G - rowsum(G P)), P = A_0 - eps. The
 // planes' loads and the reciprocals 1 / s_k go out ahead of the chain (all steps up to
 // kSkAll, else kSkChunk at a time); row and column sums move values by DPP within a
-// 16-lane row (across rows by __shfl_xor for the n = 8 columns).
+// 16-lane row (across rows by __shfl_xor for the n = 8 columns); for n = 6 each lane
+// gathers its row's (column's) entries by shuffles, in index order.
 constexpr int kSkAll = 40;
 constexpr int kSkChunk = 8;
 template <int N>
-__device__ __forceinline__ double sk_row_sum(double v)
+__device__ __forceinline__ double sk_row_sum(double v, int r)
 {
+    if constexpr (N == 6) {
+        double s = 0.0;
+#pragma unroll
+        for (int c = 0; c < N; ++c) s += __shfl(v, r * N + c);
+        return s;
+    }
     v += dpp<kQuadXor1>(v);
     v += dpp<kQuadXor2>(v);
     if constexpr (N == 8) v += dpp<kRowHalfMirror>(v);
     return v;
 }
 template <int N>
-__device__ __forceinline__ double sk_col_sum(double v)
+__device__ __forceinline__ double sk_col_sum(double v, int c)
 {
-    if constexpr (N == 4) {
+    if constexpr (N == 6) {
+        double s = 0.0;
+#pragma unroll
+        for (int r = 0; r < N; ++r) s += __shfl(v, r * N + c);
+        return s;
+    } else if constexpr (N == 4) {
         v += dpp<kRowRor4>(v);
         v += dpp<kRowRor8>(v);
     } else {
@@ -138,9 +152,9 @@ __device__ __forceinline__ double sk_col_sum(double v)
     return v;
 }
 template <int N>
-__device__ __forceinline__ double sk_step(double G, float A, double rs, int k)
+__device__ __forceinline__ double sk_step(double G, float A, double rs, int k, int r, int c)
 {
-    const double u = (k & 1) ? sk_col_sum<N>(G * (double)A) : sk_row_sum<N>(G * (double)A);
+    const double u = (k & 1) ? sk_col_sum<N>(G * (double)A, c) : sk_row_sum<N>(G * (double)A, r);
     return (G - u) * rs;
 }
 
@@ -149,11 +163,14 @@ __global__ void __launch_bounds__(256)
 bwd_sinkhorn_kernel(Args a, int64_t T)
 {
     constexpr int NN = N * N;
-    constexpr int TPW = 64 / NN;                    // tokens per wave
+    constexpr int SW = 64 % NN == 0 ? NN : 64;      // lanes per matrix
+    constexpr int TPW = 64 / SW;                    // tokens per wave
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = lane % NN, er = e / N, ec = e % N;
-    const int64_t t = ((int64_t)blockIdx.x * 4 + wave) * TPW + lane / NN;
-    const bool live = t < T;                        // groups of NN lanes: live or not as a whole
+    const int e = lane < TPW * SW ? (lane % SW < NN ? lane % SW : NN - 1) : NN - 1;   // clamped entry
+    const bool ent = lane % SW < NN;                // the lane holds an entry of its matrix
+    const int er = e / N, ec = e % N;
+    const int64_t t = ((int64_t)blockIdx.x * 4 + wave) * TPW + lane / SW;
+    const bool live = t < T && ent;                 // groups of SW lanes: live or not as a whole
     const int64_t tt = live ? t : T - 1;            // loads stay in bounds and unpredicated
     const int steps = 2 * a.num_iters;
     // Loads under a branch make the compiler wait for each one before the next; every
@@ -180,7 +197,7 @@ bwd_sinkhorn_kernel(Args a, int64_t T)
 #pragma unroll
         for (int j = 0; j < kSkAll; ++j) {
             const int k = steps - 1 - j;
-            if (k >= 1) G = sk_step<N>(G, A[j], R[j], k);   // uniform across the wave
+            if (k >= 1) G = sk_step<N>(G, A[j], R[j], k, er, ec);   // uniform across the wave
         }
     } else {
         for (int k0 = steps - 1; k0 >= 1; k0 -= kSkChunk) {
@@ -195,12 +212,12 @@ bwd_sinkhorn_kernel(Args a, int64_t T)
 #pragma unroll
             for (int j = 0; j < kSkChunk; ++j) {
                 const int k = k0 - j;
-                if (k >= 1) G = sk_step<N>(G, A[j], R[j], k);
+                if (k >= 1) G = sk_step<N>(G, A[j], R[j], k, er, ec);
             }
         }
     }
     const double P = (double)A_at(0) - a.hc_eps;
-    const double u = sk_row_sum<N>(G * P);
+    const double u = sk_row_sum<N>(G * P, er);
     if (live) a.glog[t * NN + e] = P * (G - u);
 }
 
@@ -697,6 +714,8 @@ int launch_backward(const Plan& p, const Args& a, void* stream)
     }
     if (g.n == 4 && g.SGN == 4 && g.KS == 1)
         return (int)(g.x_f16 ? launch_all<4, 4, 1, true>(p, a, st) : launch_all<4, 4, 1, false>(p, a, st));
+    if (g.n == 6 && g.SGN == 2 && g.KS == 2)
+        return (int)(g.x_f16 ? launch_all<6, 2, 2, true>(p, a, st) : launch_all<6, 2, 2, false>(p, a, st));
     if (g.n == 8 && g.SGN == 2 && g.KS == 3)
         return (int)(g.x_f16 ? launch_all<8, 2, 3, true>(p, a, st) : launch_all<8, 2, 3, false>(p, a, st));
     return (int)hipErrorInvalidValue;

@@ -71,7 +71,7 @@ MHC_BWD_HOST_DEVICE inline int pack_col(int h, int row) { return 8 * (row / 4) +
 
 inline bool make_geometry(int n, int D, Geometry* g, bool x_f16 = false)
 {
-    if (n != 4 && n != 8) return false;
+    if (n != 4 && n != 6 && n != 8) return false;   // the guide's section 5: N = 4, 6, 8
     if (D < 8 || D % 8 != 0 || D > kMaxD) return false;
     Geometry r;
     r.n = n;

@@ -101,7 +101,7 @@ int main()
     const int Ds[] = {8, 16, 24, 32, 40, 256, 1000, 2048, 2056, 4096, 7168, 16384};
     const long long Ts[] = {0, 1, 3, 63, 64, 65, 130, 4096, 16384, 100003};
     long long cases = 0;
-    for (int n : {4, 8})
+    for (int n : {4, 6, 8})
         for (int D : Ds)
             for (long long T : Ts) {
                 if (check(n, D, T)) return 1;

@@ -9,7 +9,7 @@ What pins what:
   the whole backward   central finite differences of the scalar
                        L = <gradHIn, hIn> + <gradHPost, hPost> + <gradHRes, hRes>
                        through the fp64 MhcPre forward (every gradient is dL/d input),
-                       with and without gamma, n = 4 and n = 8
+                       with and without gamma, n = 4, 6 and 8
   the forward it uses  the bf16-input forward oracle (pinned on its own) on the same
                        bf16-exact inputs; hRes against its affine closed form
   alpha = 0            no gradient reaches hMix: gradPhi = gradGamma = 0 and
@@ -136,6 +136,15 @@ def pin_fd_n4_gamma(lib=None):
 
 def pin_fd_n4_plain(lib=None):
     _check_fd(problem(T=2, n=4, D=8, gamma=False, x_post=False, seed=2), lib)
+
+
+def pin_fd_n6(lib=None):
+    # n = 6 (the backward page's section 5 lists N = 4, 6, 8): 48 phi rows
+    _check_fd(problem(T=1, n=6, D=4, gamma=True, x_post=True, seed=33), lib)
+
+
+def pin_fd_sinkhorn_n6(lib=None):
+    _check_fd(_sinkhorn_problem(1, 6, 4, 2, seed=34), lib)
 
 
 def pin_fd_n8(lib=None):

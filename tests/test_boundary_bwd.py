@@ -48,7 +48,7 @@ def test_null_params_and_workspace():
     assert bwd(B.make_bwd_params(128, 4, 256), _ptrs(gamma=FAKE)) == B.MHC_ERR_NULLPTR
 
 
-@pytest.mark.parametrize("kw", [dict(n=6), dict(n=2), dict(D=0), dict(D=12), dict(D=16392),
+@pytest.mark.parametrize("kw", [dict(n=5), dict(n=2), dict(n=16), dict(D=0), dict(D=12), dict(D=16392),
                                 dict(T=-1), dict(hc_eps=-1.0), dict(hc_eps=float("nan"))])
 def test_invalid_attributes(kw):
     base = dict(T=128, n=4, D=256, hc_eps=1e-6)

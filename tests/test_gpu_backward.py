@@ -131,6 +131,13 @@ CASES = [
     ("n8_T70_D256_gamma_post", 70, 8, 256, True, True, 9),
     ("n8_T129_D2048", 129, 8, 2048, False, False, 10),
     ("T4097_D256_groups", 4097, 4, 256, True, False, 11),
+    # n = 6 (48 phi rows: two 32-row K-steps, two streams per main-pass workgroup)
+    ("n6_T1_D8", 1, 6, 8, False, False, 71),
+    ("n6_T17_D24", 17, 6, 24, False, False, 72),
+    ("n6_T70_D256_gamma_post", 70, 6, 256, True, True, 73),
+    ("n6_T129_D2048", 129, 6, 2048, False, False, 74),
+    ("n6_T300_D7168_gamma", 300, 6, 7168, True, False, 75),
+    ("n6_T4097_D256_groups_post", 4097, 6, 256, False, True, 76),
 ]
 
 
@@ -150,6 +157,7 @@ F16_CASES = [
     ("f16_n8_T70_D256_gamma_post", 70, 8, 256, True, True, 65),
     ("f16_n8_T129_D2048", 129, 8, 2048, False, False, 66),
     ("f16_T4097_D256_groups", 4097, 4, 256, True, False, 67),
+    ("f16_n6_T65_D512_gamma_post", 65, 6, 512, True, True, 69),
 ]
 
 
@@ -222,6 +230,9 @@ SINKHORN_CASES = [
     ("sk_n8_T17_D64_2it", 17, 8, 64, 2, True, False, 44),
     ("sk_n8_T70_D256_20it", 70, 8, 256, 20, False, True, 45),
     ("sk_T200_D7168_20it", 200, 4, 7168, 20, False, False, 46),
+    ("sk_n6_T1_D8_1it", 1, 6, 8, 1, False, False, 77),
+    ("sk_n6_T17_D64_2it_gamma", 17, 6, 64, 2, True, False, 78),
+    ("sk_n6_T70_D256_20it_post", 70, 6, 256, 20, False, True, 79),
 ]
 
 
