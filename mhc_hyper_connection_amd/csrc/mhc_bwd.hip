@@ -416,21 +416,28 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, 
     // soon as the current tile's registers are consumed and stay in flight through the
     // gradPhi phase. Rows past the tile and positions past D read as zero.
     const int row = 16 * wave + j;                   // the lane's token in a tile
-    u32x4 xv[SGN], xp[SGN], gh, gmt[KS][3];
+    // DB: x and gradHIn are loaded a whole tile ahead, into the other of two register sets
+    // (where the registers allow it: no gamma, and not fp16 with gradXPost); the rest of a
+    // tile's inputs after its predecessor's first phase, as with a single set
+    constexpr bool DB = !GAMMA && !(XPOST && H);
+    u32x4 xv[SGN], xv2[DB ? SGN : 1], xp[SGN], gh, gh2, gmt[KS][3];
     float hp[SGN], c3;
-    auto load_tile = [&](int64_t tl) {
+    auto load_xg = [&](int64_t tl, u32x4 (&xd)[SGN], u32x4& ghd) {
         const int64_t t0 = tl * kTile;
         const int ntile = (int)(T - t0 < kTile ? T - t0 : kTile);
-        const int64_t tok = t0 + row;
-        const bool tval = row < ntile;
         const rsrc_t rx = make_rsrc(a.x + t0 * K, (int64_t)ntile * K * 2);
         const rsrc_t rgh = make_rsrc(a.grad_h_in + t0 * D, (int64_t)ntile * D * 2);
-        const rsrc_t rgm = make_rsrc(a.gmix + t0 * (3 * MP), (int64_t)ntile * 3 * MP * 2);
 #pragma unroll
         for (int s = 0; s < SGN; ++s) {
             const uint32_t off = dval ? (uint32_t)(((int64_t)row * K + (int64_t)(sg * SGN + s) * D + d0) * 2) : kOutOfRange;
-            xv[s] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+            xd[s] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
         }
+        ghd = __builtin_amdgcn_raw_buffer_load_b128(rgh, dval ? (int)(((int64_t)row * D + d0) * 2) : (int)kOutOfRange, 0, 0);
+    };
+    auto load_rest = [&](int64_t tl) {
+        const int64_t t0 = tl * kTile;
+        const int ntile = (int)(T - t0 < kTile ? T - t0 : kTile);
+        const rsrc_t rgm = make_rsrc(a.gmix + t0 * (3 * MP), (int64_t)ntile * 3 * MP * 2);
         if constexpr (XPOST) {
             const rsrc_t rxp = make_rsrc(a.grad_x_post + t0 * K, (int64_t)ntile * K * 2);
 #pragma unroll
@@ -439,7 +446,6 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, 
                 xp[s] = __builtin_amdgcn_raw_buffer_load_b128(rxp, (int)off, 0, 0);
             }
         }
-        gh = __builtin_amdgcn_raw_buffer_load_b128(rgh, dval ? (int)(((int64_t)row * D + d0) * 2) : (int)kOutOfRange, 0, 0);
         // gMix terms of the lane's token: B operand of xrsGrad (K-step ks, term p)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -447,14 +453,24 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, 
             for (int p = 0; p < 3; ++p)
                 gmt[ks][p] = __builtin_amdgcn_raw_buffer_load_b128(
                     rgm, (int)((((int64_t)row * KS + ks) * 3 * 32 + 32 * p + 8 * grp) * 2), 0, 0);
+        // hPre and c3 through buffer loads too: rows past the tile read as zero with no
+        // branch (a load under a branch leaves the compiler no exact wait count)
+        const rsrc_t rhp = make_rsrc(a.h_pre + t0 * N, (int64_t)ntile * N * 4);
+        const rsrc_t rc3 = make_rsrc(a.c3 + t0, (int64_t)ntile * 4);
 #pragma unroll
-        for (int s = 0; s < SGN; ++s) hp[s] = tval ? a.h_pre[tok * N + sg * SGN + s] : 0.f;
-        c3 = tval ? a.c3[tok] : 0.f;
+        for (int s = 0; s < SGN; ++s)
+            hp[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rhp, (row * N + sg * SGN + s) * 4, 0, 0));
+        c3 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rc3, row * 4, 0, 0));
     };
 
     const int64_t tile_end = (g + 1) * tpg < tiles ? (g + 1) * tpg : tiles;
-    load_tile(g * tpg);
-    for (int64_t tile = g * tpg; tile < tile_end; ++tile) {
+    load_xg(g * tpg, xv, gh);
+    load_rest(g * tpg);
+    auto step = [&](int64_t tile, u32x4 (&xc)[SGN], u32x4& ghc, u32x4 (&xn)[SGN], u32x4& ghn) __attribute__((always_inline)) {
+        // the next tile's loads go out unconditionally (the last tile loads itself again), so
+        // that every wait below has an exact count
+        const int64_t nt = tile + 1 < tile_end ? tile + 1 : tile;
+        if constexpr (DB) load_xg(nt, xn, ghn);
         const int64_t t0 = tile * kTile;
         const int ntile = (int)(T - t0 < kTile ? T - t0 : kTile);
 
@@ -490,8 +506,8 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, 
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl) {
                     const int e = 2 * e2 + hl;
-                    const float xe = hl ? x16_hi<H>(xv[s][e2]) : x16_lo<H>(xv[s][e2]);
-                    const float ge = hl ? x16_hi<H>(gh[e2]) : x16_lo<H>(gh[e2]);
+                    const float xe = hl ? x16_hi<H>(xc[s][e2]) : x16_lo<H>(xc[s][e2]);
+                    const float ge = hl ? x16_hi<H>(ghc[e2]) : x16_lo<H>(ghc[e2]);
                     v[hl] = fmaf(ge, hp[s], GAMMA ? xg[e] * gam[GAMMA ? s : 0][e] : xg[e]);
                     v[hl] = fmaf(-c3, xe, v[hl]);
                     if constexpr (XPOST) v[hl] += hl ? x16_hi<H>(xp[s][e2]) : x16_lo<H>(xp[s][e2]);
@@ -504,7 +520,7 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, 
             // x of this tile, transposed: xT[local column][token]
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                xT[tslot(s * kDBlock + 8 * grp + e, row)] = (uint16_t)((xv[s][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+                xT[tslot(s * kDBlock + 8 * grp + e, row)] = (uint16_t)((xc[s][e >> 1] >> (16 * (e & 1))) & 0xffffu);
         }
         // gMix terms of this tile, transposed: gT[p][m][token]
 #pragma unroll
@@ -515,7 +531,8 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, 
                 for (int e = 0; e < 8; ++e)
                     gT[tslot(p * MP + 32 * ks + 8 * grp + e, row)] =
                         (uint16_t)((gmt[ks][p][e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        if (tile + 1 < tile_end) load_tile(tile + 1);
+        if constexpr (!DB) load_xg(nt, xn, ghn);
+        load_rest(nt);
         __syncthreads();
 
         // gradPhi partial: C[m][col] += sum over the tile's tokens of gMix[t][m] x[t][col];
@@ -559,6 +576,14 @@ bwd_main_kernel(Args a, int64_t T, int D, int nblk, int64_t tpg, int64_t tiles, 
             }
         }
         __syncthreads();   // xT and gT are rewritten by the next tile
+    };
+    if constexpr (DB) {
+        for (int64_t tile = g * tpg; tile < tile_end; tile += 2) {
+            step(tile, xv, gh, xv2, gh2);
+            if (tile + 1 < tile_end) step(tile + 1, xv2, gh2, xv, gh);
+        }
+    } else {
+        for (int64_t tile = g * tpg; tile < tile_end; ++tile) step(tile, xv, gh, xv, gh);
     }
 
     // gradPhi partial of the group: P[g][m][k], k = stream * D + d
