@@ -123,6 +123,24 @@ class PreForward:
                 out["norm_out"] = torch.empty((2 * self.num_iters, T, n, n), **f32)
         return out
 
+    def _check_out(self, out):
+        # every tensor the library writes: known name, dtype, shape, device, contiguous
+        torch = _torch()
+        T, n, D, M = self.T, self.n, self.D, self.M
+        it = self.num_iters
+        want = {"h_in": (self.xdt, (T, D)), "h_post": (torch.float32, (T, n)),
+                "h_res": (torch.float32, (T, n, n)), "inv_rms": (torch.float32, (T,)),
+                "h_mix": (torch.float32, (T, M)), "h_pre": (torch.float32, (T, n)),
+                "sum_out": (torch.float32, (2 * it, T, n)), "norm_out": (torch.float32, (2 * it, T, n, n))}
+        unknown = set(out) - set(want)
+        if unknown:
+            raise ValueError(f"out: unknown outputs {sorted(unknown)}")
+        for k in ("h_in", "h_post", "h_res"):
+            if out.get(k) is None:
+                raise ValueError(f"out[{k!r}] is required")
+        for k, v in out.items():
+            _check(v, k, *want[k], self.device)
+
     # -- weights -----------------------------------------------------------------------
     def prepack(self, phi, gamma=None, out=None):
         torch = _torch()
@@ -153,8 +171,15 @@ class PreForward:
         _check(bias, "bias", torch.float32, (M,), dev)
         _check(gamma, "gamma", torch.float32, (n, D), dev)
         _check(pre_mix, "pre_mix", torch.float32, (T, n), dev)
+        if phi_packed is not None:
+            if phi_packed.dtype != torch.uint8 or phi_packed.numel() < self.packed_bytes:
+                raise ValueError(f"phi_packed: uint8 of at least {self.packed_bytes} bytes expected "
+                                 "(mhc_pre_prepack's output)")
+            _check(phi_packed, "phi_packed", torch.uint8, tuple(phi_packed.shape), dev)
         if out is None:
             out = self.alloc_outputs()
+        else:
+            self._check_out(out)
         ptrs = {"x": _ptr(x), "phi": _ptr(phi), "alpha": _ptr(alpha), "bias": _ptr(bias),
                 "gamma": _ptr(gamma), "pre_mix": _ptr(pre_mix), "phi_packed": _ptr(phi_packed)}
         for k, v in out.items():
