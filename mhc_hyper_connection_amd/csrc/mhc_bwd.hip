@@ -73,17 +73,16 @@ __device__ __forceinline__ void split_f16x8(u32x4 w, bf16x8& hi, bf16x8& lo)
 
 // Unit u = (((((b * n + i) * 2 + h) * KS + ks) * 3 + p) * 64 + lane holds, for lane
 // (row = lane % 16, g = lane / 16), term p of phi[m][i D + d] for m = 32 ks + 8 g + e,
-// e = 0..7, at d = 32 b + pack_col(h, row); zero past M or D.
+// e = 0..7, at d = 32 b + pack_col(h, row); zero past M or D. One thread writes the three
+// terms of a (b, i, h, ks, lane), reading its eight weights once.
 __global__ void __launch_bounds__(256)
 bwd_pack_kernel(const float* __restrict__ phi, u32x4* __restrict__ pack, int n, int D, int M, int KS,
-                int64_t total)
+                int64_t triples)
 {
-    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (u >= total) return;
-    const int lane = (int)(u % 64);
-    int64_t r = u / 64;
-    const int p = (int)(r % 3);
-    r /= 3;
+    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (v >= triples) return;
+    const int lane = (int)(v % 64);
+    int64_t r = v / 64;
     const int ks = (int)(r % KS);
     r /= KS;
     const int h = (int)(r % 2);
@@ -93,15 +92,21 @@ bwd_pack_kernel(const float* __restrict__ phi, u32x4* __restrict__ pack, int n, 
     const int row = lane % 16, g = lane / 16;
     const int d = kDBlock * b + pack_col(h, row);
     const int64_t K = (int64_t)n * D;
-    u32x4 w = {0u, 0u, 0u, 0u};
+    u32x4 w[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
     if (d < D) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int m = 32 * ks + 8 * g + e;
-            if (m < M) w[e >> 1] |= split3(phi[(int64_t)m * K + (int64_t)i * D + d]).t[p] << (16 * (e & 1));
+            if (m < M) {
+                const Split3 sp = split3(phi[(int64_t)m * K + (int64_t)i * D + d]);
+#pragma unroll
+                for (int p = 0; p < 3; ++p) w[p][e >> 1] |= sp.t[p] << (16 * (e & 1));
+            }
         }
     }
-    pack[u] = w;
+    const int64_t base = (((((int64_t)b * n + i) * 2 + h) * KS + ks) * 3) * 64 + lane;
+#pragma unroll
+    for (int p = 0; p < 3; ++p) pack[base + 64 * p] = w[p];
 }
 
 // ------------------------------------------------------------------ Sinkhorn backward
@@ -625,8 +630,17 @@ bwd_reduce_cols_kernel(Args a, int64_t MK, int64_t K, int64_t G)
 {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx < MK) {
+        // the group partials in group order, eight loads issued before their sums
         double s = 0.0;
-        for (int64_t gg = 0; gg < G; ++gg) s += (double)a.pphi[gg * MK + idx];
+        int64_t gg = 0;
+        for (; gg + 8 <= G; gg += 8) {
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = a.pphi[(gg + q) * MK + idx];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) s += (double)v[q];
+        }
+        for (; gg < G; ++gg) s += (double)a.pphi[gg * MK + idx];
         if (a.gamma) s *= (double)a.gamma[idx % K];
         a.grad_phi[idx] = (float)s;
     } else if (idx < MK + K && a.gamma) {
@@ -692,9 +706,9 @@ template <int N, int SGN, int KS, bool H>
 hipError_t launch_all(const Plan& p, const Args& a, hipStream_t st)
 {
     const Geometry& g = p.g;
-    const int64_t units = (int64_t)g.nblk * g.n * pack_units_per_stream(g.KS);
-    hipLaunchKernelGGL(bwd_pack_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, st, a.phi,
-                       static_cast<u32x4*>(a.pack), g.n, g.D, g.M, g.KS, units);
+    const int64_t triples = (int64_t)g.nblk * g.n * pack_units_per_stream(g.KS) / 3;   // one thread each
+    hipLaunchKernelGGL(bwd_pack_kernel, dim3((unsigned)((triples + 255) / 256)), dim3(256), 0, st, a.phi,
+                       static_cast<u32x4*>(a.pack), g.n, g.D, g.M, g.KS, triples);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.num_iters > 0) {
