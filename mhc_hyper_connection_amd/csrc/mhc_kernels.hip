@@ -84,15 +84,28 @@ __device__ __forceinline__ int tile_tokens(const KArgs& k, int64_t t0)
 
 // ------------------------------------------------------------------ weight pre-pack
 
+// double -> float, round to nearest even, kept as a float: the empty asm statement stops
+// the compiler from merging this rounding with a following float -> bf16 (or fp16) one
+// into a single rounding, which it does in some code shapes and not in others. Every
+// pack of the weights (the pack kernel, the single-read and the one-launch kernels) then
+// rounds the same way, whatever code surrounds it, and the packed terms agree bit for bit.
+__device__ __forceinline__ float f64_to_f32(double d)
+{
+    float f = (float)d;
+    asm volatile("" : "+v"(f));
+    return f;
+}
+
 // phi * gamma (the exact product in double) as three bf16 terms, each the nearest bf16 of
-// what the previous ones leave: hi + mid + lo equals the product to ~2^-26 relative.
+// the nearest float of what the previous ones leave: hi + mid + lo equals the product to
+// ~2^-26 relative.
 __device__ __forceinline__ void split3(double p, uint32_t (&tb)[3])
 {
-    tb[0] = f32_to_bf16_bits((float)p);
+    tb[0] = f32_to_bf16_bits(f64_to_f32(p));
     const double r1 = p - bf16_bits_to_double(tb[0]);
-    tb[1] = f32_to_bf16_bits((float)r1);
+    tb[1] = f32_to_bf16_bits(f64_to_f32(r1));
     const double r2 = r1 - bf16_bits_to_double(tb[1]);
-    tb[2] = f32_to_bf16_bits((float)r2);
+    tb[2] = f32_to_bf16_bits(f64_to_f32(r2));
 }
 
 // The fp16 form: the terms would fall below fp16's normal range, so each remainder is
@@ -101,11 +114,11 @@ __device__ __forceinline__ void split3(double p, uint32_t (&tb)[3])
 // for |p| in [2^-14, 65504]; larger weights overflow fp16.
 __device__ __forceinline__ void split3_f16(double p, uint32_t (&tb)[3])
 {
-    const _Float16 h0 = (_Float16)(float)p;
+    const _Float16 h0 = (_Float16)f64_to_f32(p);
     const double r1 = (p - (double)(float)h0) * 2048.0;
-    const _Float16 h1 = (_Float16)(float)r1;
+    const _Float16 h1 = (_Float16)f64_to_f32(r1);
     const double r2 = (r1 - (double)(float)h1) * 2048.0;
-    const _Float16 h2 = (_Float16)(float)r2;
+    const _Float16 h2 = (_Float16)f64_to_f32(r2);
     tb[0] = __builtin_bit_cast(uint16_t, h0);
     tb[1] = __builtin_bit_cast(uint16_t, h1);
     tb[2] = __builtin_bit_cast(uint16_t, h2);
@@ -117,6 +130,35 @@ __device__ __forceinline__ void split3_x(double p, uint32_t (&tb)[3])
 {
     if constexpr (H) split3_f16(p, tb);
     else split3(p, tb);
+}
+// The same splits of a float weight (no gamma), in fp32: the same bits as split3_x of
+// (double)p (its double -> float roundings are then exact). Every remainder is exact in fp32 too: p - hi is a multiple of p's fp32 ulp
+// and at most half a bf16 (fp16) ulp of p, so it needs at most 16 (13) significant bits,
+// and the next remainder fewer still; the scalings by 2^11 are exact.
+__device__ __forceinline__ void split3_f32(float p, uint32_t (&tb)[3])
+{
+    tb[0] = f32_to_bf16_bits(p);
+    const float r1 = p - __uint_as_float(tb[0] << 16);
+    tb[1] = f32_to_bf16_bits(r1);
+    const float r2 = r1 - __uint_as_float(tb[1] << 16);
+    tb[2] = f32_to_bf16_bits(r2);
+}
+__device__ __forceinline__ void split3_f16_f32(float p, uint32_t (&tb)[3])
+{
+    const _Float16 h0 = (_Float16)p;
+    const float r1 = (p - (float)h0) * 2048.f;
+    const _Float16 h1 = (_Float16)r1;
+    const float r2 = (r1 - (float)h1) * 2048.f;
+    const _Float16 h2 = (_Float16)r2;
+    tb[0] = __builtin_bit_cast(uint16_t, h0);
+    tb[1] = __builtin_bit_cast(uint16_t, h1);
+    tb[2] = __builtin_bit_cast(uint16_t, h2);
+}
+template <bool H>
+__device__ __forceinline__ void split3_x32(float p, uint32_t (&tb)[3])
+{
+    if constexpr (H) split3_f16_f32(p, tb);
+    else split3_f32(p, tb);
 }
 // Scales of the mid and lo term sums (split3_f16 scales the remainders by 2^11 each).
 template <bool H> constexpr float kMidScale = H ? 0x1p-11f : 1.f;
@@ -1090,24 +1132,55 @@ fused_kernel(FArgs f)
         const int units = nb * N * 4 * NCL;
         for (int u = tid; u < units; u += kFThreads) wl[u] = src[(int64_t)(u / NCL) * NC + u % NCL];
     } else {          // packed here from phi (and gamma), as prepack_kernel packs them
-        const int items = nb * N * 4 * M;   // (K-step, octet row, phi row): three LDS units each
-        for (int it = tid; it < items; it += kFThreads) {
+        // (K-step, octet row, phi row) items, three LDS units each: every item's phi (and
+        // gamma) loads go out first, two 16-byte loads each where the arrays are 16-byte
+        // aligned (an item's 8 weights are consecutive and start at a multiple of 8
+        // elements), then the splits: in fp32 without gamma (the same bits), else of the
+        // product in fp64
+        const int items = nb * N * 4 * M;
+        constexpr int PER = (NW * N * 4 * M + kFThreads - 1) / kFThreads;
+        float pv[PER][8], gv[PER][8];
+        const bool vec = ((reinterpret_cast<uintptr_t>(a.phi) | reinterpret_cast<uintptr_t>(a.gamma)) & 15) == 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int it = tid + q * kFThreads;
             const int m = it % M, row = it / M;        // row = K-step * 4 + octet
             const int kk = row / 4, og = row % 4;
             const int k = b_lo * N + kk;               // K-step: d-block k / N, stream k % N
             const int d = kBlock * (k / N) + 8 * og;
-            u32x4 w3[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-            if (d < f.D) {
-                const int64_t k0 = (int64_t)(k % N) * f.D + d;
+            const bool live = it < items && d < f.D;
+            const int64_t k0 = (int64_t)(k % N) * f.D + d;
+            if (vec) {
+                const float4 z = {0.f, 0.f, 0.f, 0.f}, o = {1.f, 1.f, 1.f, 1.f};
+                const float4* pp4 = reinterpret_cast<const float4*>(a.phi + (int64_t)m * f.K + k0);
+                const float4* gp4 = reinterpret_cast<const float4*>(a.gamma + k0);
+                const float4 p0 = live ? pp4[0] : z, p1 = live ? pp4[1] : z;
+                const float4 g0 = live && a.gamma ? gp4[0] : o, g1 = live && a.gamma ? gp4[1] : o;
+                pv[q][0] = p0.x; pv[q][1] = p0.y; pv[q][2] = p0.z; pv[q][3] = p0.w;
+                pv[q][4] = p1.x; pv[q][5] = p1.y; pv[q][6] = p1.z; pv[q][7] = p1.w;
+                gv[q][0] = g0.x; gv[q][1] = g0.y; gv[q][2] = g0.z; gv[q][3] = g0.w;
+                gv[q][4] = g1.x; gv[q][5] = g1.y; gv[q][6] = g1.z; gv[q][7] = g1.w;
+            } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    double p = (double)a.phi[(int64_t)m * f.K + k0 + e];
-                    if (a.gamma) p *= (double)a.gamma[k0 + e];
-                    uint32_t tb[3];
-                    split3_x<H>(p, tb);
-#pragma unroll
-                    for (int term = 0; term < 3; ++term) w3[term][e >> 1] |= tb[term] << (16 * (e & 1));
+                    pv[q][e] = live ? a.phi[(int64_t)m * f.K + k0 + e] : 0.f;
+                    gv[q][e] = live && a.gamma ? a.gamma[k0 + e] : 1.f;
                 }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int it = tid + q * kFThreads;
+            if (it >= items) continue;
+            const int m = it % M, row = it / M;
+            u32x4 w3[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                uint32_t tb[3];
+                if (a.gamma) split3_x<H>((double)pv[q][e] * (double)gv[q][e], tb);
+                else split3_x32<H>(pv[q][e], tb);
+#pragma unroll
+                for (int term = 0; term < 3; ++term) w3[term][e >> 1] |= tb[term] << (16 * (e & 1));
             }
 #pragma unroll
             for (int term = 0; term < 3; ++term) wl[row * NCL + term * M + m] = w3[term];
@@ -1573,9 +1646,9 @@ decode_kernel(DArgs f)
             u32x4 w3[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const double p = a.gamma ? (double)pv[k][e] * (double)gv[k][e] : (double)pv[k][e];
-                uint32_t tb[3];
-                split3_x<H>(p, tb);
+                uint32_t tb[3];   // in fp32 without gamma (the same bits), else of the product in fp64
+                if (a.gamma) split3_x<H>((double)pv[k][e] * (double)gv[k][e], tb);
+                else split3_x32<H>(pv[k][e], tb);
 #pragma unroll
                 for (int term = 0; term < 3; ++term) w3[term][e >> 1] |= tb[term] << (16 * (e & 1));
             }
