@@ -22,8 +22,11 @@
  *
  * Layout and ownership. Every tensor is a caller-owned, contiguous, row-major device
  * buffer in the TND layout (a [B, S, n, D] input is the same bytes as [B*S, n, D]).
- * bf16 tensors are passed as raw 16-bit patterns. The library allocates nothing,
- * keeps no state between calls, and never synchronises the stream.
+ * bf16 and fp16 tensors are passed as raw 16-bit patterns. The library allocates nothing
+ * (the no-allocation entry point's array is static), never synchronises the stream except
+ * where an entry point says so (mhc_pre_wait_status), and keeps between calls only what a
+ * caller's workspace holds (call counters, which mhc_pre_workspace_size's buffer carries)
+ * and, per device, facts it queries once (compute units, which kernels fit).
  *
  * Errors. Every entry point validates on the host before any HIP call and returns:
  *   MHC_OK                 success (also for T == 0: nothing is launched);
@@ -67,9 +70,9 @@ typedef int32_t mhc_status;
  *                  (the aclnnMhcPreSinkhorn and aclnnMhcPreV2 guides, section 5.1, list
  *                  BF16 and FLOAT16). With fp16 the weights are packed as three fp16 terms
  *                  scaled by 1, 2^11, 2^22 (phi * gamma must stay within 65504 in
- *                  magnitude), the four-kernel path runs, and the standalone stages read
- *                  and write fp16 too. hc_post takes either format (its own x_dtype);
- *                  the backward takes bf16 only. */
+ *                  magnitude); every forward path takes it, and the standalone stages
+ *                  read and write fp16 too. hc_post takes either format (its own
+ *                  x_dtype), and so does the backward (mhc_pre_bwd_params.x_f16). */
 typedef struct mhc_pre_params {
     int64_t T;
     int32_t n;
@@ -87,7 +90,7 @@ typedef struct mhc_pre_params {
 
 /* Device pointers. M = n*n + 2n (n_alpha == 3) or 2n (n_alpha == 2); it = num_iters.
  * Inputs:
- *   x          bf16 [T, n, D], 16-byte aligned                           required
+ *   x          x_dtype [T, n, D], 16-byte aligned                        required
  *   phi        f32  [M, n*D]                          required unless phi_packed is given
  *   alpha      f32  [n_alpha]                                            required
  *   bias       f32  [M]                                                  required
@@ -96,7 +99,7 @@ typedef struct mhc_pre_params {
  *   phi_packed from mhc_pre_prepack for these (n, D, n_alpha, gamma)     optional; when
  *              given, phi and gamma are not read
  * Outputs (must not alias inputs or each other):
- *   h_in       bf16 [T, D], 16-byte aligned                              required
+ *   h_in       x_dtype [T, D], 16-byte aligned                           required
  *   h_post     f32  [T, n]                                               required
  *   h_res      f32  [T, n, n]    required when n_alpha == 3; with n_alpha == 2 it may be
  *                                NULL, else it is filled with zeros
@@ -374,7 +377,7 @@ mhc_status mhc_pre_backward(const mhc_pre_bwd_params* params, const mhc_pre_bwd_
  * (the same reading of the mean as mhc_pre_forward; aclnnMhcPreV2 guide, section 3).
  * Squares and sums in fp64, one rounding to f32.
  *   params     validated as for mhc_pre_forward (T, n, D and norm_eps are used)
- *   x          bf16 [T, n, D], 16-byte aligned
+ *   x          x_dtype [T, n, D], 16-byte aligned
  *   inv_rms    f32  [T]
  * Pointers may be NULL only when T == 0. Asynchronous on `stream`, no workspace, no
  * allocation. Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
@@ -389,9 +392,9 @@ mhc_status mhc_pre_inv_rms(const mhc_pre_params* params, const uint16_t* x, floa
  * when pre_mix is not given).
  *   params     as for mhc_pre_forward; need_backward makes sum_out / norm_out mandatory
  *              (n_alpha == 3)
- * Inputs:  x bf16 [T, n, D] (16-byte aligned), h_mix f32 [T, M], inv_rms f32 [T],
+ * Inputs:  x x_dtype [T, n, D] (16-byte aligned), h_mix f32 [T, M], inv_rms f32 [T],
  *          alpha f32 [n_alpha], bias f32 [M], pre_mix f32 [T, n] (optional)
- * Outputs: h_in bf16 [T, D] (16-byte aligned), h_pre, h_post f32 [T, n], h_res f32 [T, n, n]
+ * Outputs: h_in x_dtype [T, D] (16-byte aligned), h_pre, h_post f32 [T, n], h_res f32 [T, n, n]
  *          (required when n_alpha == 3), sum_out / norm_out as in mhc_pre_tensors
  * Pointers may be NULL only when T == 0. Asynchronous on `stream`, no workspace, no
  * allocation. Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
@@ -422,13 +425,13 @@ mhc_status mhc_pre_sinkhorn(const mhc_pre_params* params, const mhc_pre_sinkhorn
  * This is the guide's printed broadcast expression evaluated on the [b, s, n, n] comb_frag
  * its section "返回值说明" documents: the sum runs over comb's first index, so output
  * stream j takes column j of comb (comb transposed times the residual streams). fp32 fused
- * multiply-adds (post term first, then i in order), one rounding to bf16.
+ * multiply-adds (post term first, then i in order), one rounding to the 16-bit format.
  *   T >= 0; n: 4, 6 or 8; D: a multiple of 8 in [8, 16384]
- *   x        bf16 [T, D]       16-byte aligned    (the attention / MLP output)
- *   residual bf16 [T, n, D]    16-byte aligned    (the n streams)
- *   post     f32  [T, n]
- *   comb     f32  [T, n, n]
- *   out      bf16 [T, n, D]    16-byte aligned; must not alias the inputs
+ *   x        x_dtype [T, D]       16-byte aligned    (the attention / MLP output)
+ *   residual x_dtype [T, n, D]    16-byte aligned    (the n streams)
+ *   post     f32     [T, n]
+ *   comb     f32     [T, n, n]
+ *   out      x_dtype [T, n, D]    16-byte aligned; must not alias the inputs
  * Pointers may be NULL only when T == 0 (nothing is launched). Asynchronous on `stream`,
  * no workspace, no allocation. Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
 typedef struct mhc_post_params {

@@ -362,8 +362,9 @@ def mhc_pre_backward(x, phi, alpha, grad_h_in, grad_h_post, grad_h_res, inv_rms,
 def mhc_post(x, residual, post, comb, *, out=None):
     """hc_post: out[t, j, d] = post[t, j] x[t, d] + sum_i comb[t, i, j] residual[t, i, d]
     (the HcPre guide's broadcast expression on its 4-D comb: the sum is over comb's first index).
-    x bf16 [T, D], residual bf16 [T, n, D], post f32 [T, n], comb f32 [T, n, n] on one
-    device; returns (or fills) bf16 [T, n, D]. The stream is torch's current stream."""
+    x [T, D] and residual [T, n, D] both bf16 or both fp16, post f32 [T, n], comb f32
+    [T, n, n] on one device; returns (or fills) [T, n, D] in x's dtype. The stream is
+    torch's current stream."""
     torch = _torch()
     T, n, D = residual.shape
     dev = residual.device
