@@ -138,6 +138,10 @@ CASES = [
     ("n6_T129_D2048", 129, 6, 2048, False, False, 74),
     ("n6_T300_D7168_gamma", 300, 6, 7168, True, False, 75),
     ("n6_T4097_D256_groups_post", 4097, 6, 256, False, True, 76),
+    # the largest D the backward takes, for each n
+    ("Dmax_T70_D16384_gamma_post", 70, 4, 16384, True, True, 91),
+    ("n6_Dmax_T33_D16384", 33, 6, 16384, False, False, 92),
+    ("n8_Dmax_T20_D16384_gamma", 20, 8, 16384, True, False, 93),
 ]
 
 
@@ -158,6 +162,7 @@ F16_CASES = [
     ("f16_n8_T129_D2048", 129, 8, 2048, False, False, 66),
     ("f16_T4097_D256_groups", 4097, 4, 256, True, False, 67),
     ("f16_n6_T65_D512_gamma_post", 65, 6, 512, True, True, 69),
+    ("f16_Dmax_T40_D16384_gamma_post", 40, 4, 16384, True, True, 94),
 ]
 
 
@@ -233,6 +238,7 @@ SINKHORN_CASES = [
     ("sk_n6_T1_D8_1it", 1, 6, 8, 1, False, False, 77),
     ("sk_n6_T17_D64_2it_gamma", 17, 6, 64, 2, True, False, 78),
     ("sk_n6_T70_D256_20it_post", 70, 6, 256, 20, False, True, 79),
+    ("sk_Dmax_T30_D16384_20it_gamma", 30, 4, 16384, 20, True, False, 95),
 ]
 
 
