@@ -44,6 +44,10 @@ SMALL = [
     ("D40_partial_chunk", lambda: synth.custom(33, 4, 40, need_backward=True, seed=28)),
     ("D2056_tail", lambda: synth.custom(65, 4, 2056, gamma=True, seed=29)),
     ("n8_D24_partial", lambda: synth.custom(17, 8, 24, n_alpha=2, pre_mix=True, seed=30)),
+    # the largest D for each n and alpha length: n = 8 with alpha[3] stops at 8192
+    ("n8_alpha3_Dmax8192", lambda: synth.custom(20, 8, 8192, need_backward=True, seed=31)),
+    ("n8_alpha2_Dmax16384", lambda: synth.custom(9, 8, 16384, n_alpha=2, seed=32)),
+    ("n4_Dmax16384_T130_gamma", lambda: synth.custom(130, 4, 16384, gamma=True, need_backward=True, seed=33)),
     ("T1", lambda: synth.custom(1, 4, 7168, seed=31)),
     ("T2", lambda: synth.custom(2, 4, 4096, seed=32)),
     ("T7", lambda: synth.custom(7, 4, 5120, seed=33)),

@@ -47,7 +47,9 @@ def check(g, pi, tokens=None):
 
 CASES = [("T1_D8_n4", 1, 4, 8, 1), ("T3_D40_n4", 3, 4, 40, 2), ("T65_D520_n4", 65, 4, 520, 3),
          ("T17_D24_n8", 17, 8, 24, 4), ("T70_D2048_n8", 70, 8, 2048, 5), ("T300_D7168_n4", 300, 4, 7168, 6),
-         ("T37_D1032_n6", 37, 6, 1032, 7)]
+         ("T37_D1032_n6", 37, 6, 1032, 7),
+         # the largest D hc_post takes
+         ("T9_D16384_n4", 9, 4, 16384, 8), ("T20_D16384_n8", 20, 8, 16384, 9)]
 
 
 @pytest.mark.parametrize("name,T,n,D,seed", CASES, ids=[c[0] for c in CASES])
