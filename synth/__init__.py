@@ -107,8 +107,9 @@ class Workload:
         return self.n * self.D
 
 
-# The five workloads the method is measured on (sizes and distributions as stated
-# for this build's configurations; seeds 1001..1005).
+# The five measured workloads: a tiny prefill, a mid-size prefill with gamma, a large
+# training prefill with the backward intermediates, decode-size T, and a wide n = 8
+# stream set with alpha[2] and an external pre_mix (seeds 1001..1005).
 WORKLOADS = {
     "tiny": Workload("tiny", T=128, n=4, D=256, seed=1001,
                      note="T=128, n=4, D=256, no gamma, needBackward=false"),
