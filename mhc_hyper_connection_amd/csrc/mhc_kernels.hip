@@ -194,13 +194,33 @@ prepack_kernel(const float* __restrict__ phi, const float* __restrict__ gamma,
     const int d = kBlock * (int)(k / n) + 8 * g;
     if (k < nks && d < D) {
         const int64_t k0 = (k % n) * (int64_t)D + d;
+        // the octet's 8 weights (and gammas) are consecutive and start at a multiple of 8
+        // elements: two 16-byte loads each where the arrays are 16-byte aligned
+        float pv[8], gv[8];
+        const bool vec = ((reinterpret_cast<uintptr_t>(phi) | reinterpret_cast<uintptr_t>(gamma)) & 15) == 0;
+        if (vec) {
+            const float4* pp4 = reinterpret_cast<const float4*>(phi + (int64_t)m * K + k0);
+            const float4 p0 = pp4[0], p1 = pp4[1];
+            pv[0] = p0.x; pv[1] = p0.y; pv[2] = p0.z; pv[3] = p0.w;
+            pv[4] = p1.x; pv[5] = p1.y; pv[6] = p1.z; pv[7] = p1.w;
+            if (gamma) {
+                const float4* gp4 = reinterpret_cast<const float4*>(gamma + k0);
+                const float4 g0 = gp4[0], g1 = gp4[1];
+                gv[0] = g0.x; gv[1] = g0.y; gv[2] = g0.z; gv[3] = g0.w;
+                gv[4] = g1.x; gv[5] = g1.y; gv[6] = g1.z; gv[7] = g1.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = phi[(int64_t)m * K + k0 + e];
+                gv[e] = gamma ? gamma[k0 + e] : 1.f;
+            }
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            double p = (double)phi[(int64_t)m * K + k0 + e];
-            if (gamma) p *= (double)gamma[k0 + e];
-            uint32_t tb[3];
-            if constexpr (H) split3_f16(p, tb);
-            else split3(p, tb);
+            uint32_t tb[3];   // in fp32 without gamma (the same bits), else of the product in fp64
+            if (gamma) split3_x<H>((double)pv[e] * (double)gv[e], tb);
+            else split3_x32<H>(pv[e], tb);
 #pragma unroll
             for (int t = 0; t < 3; ++t) w[t][e >> 1] |= tb[t] << (16 * (e & 1));
         }
