@@ -47,7 +47,9 @@ KERNEL_NAMES = {"pack": "prepack_kernel", "projection": "proj_kernel",
 KERNEL_NAMES_SINGLE_READ = dict(KERNEL_NAMES, projection="fused_kernel", hin="(none)")
 # the one-launch path of a few tokens: one kernel, timed as the projection stage
 KERNEL_NAMES_ONE_LAUNCH = dict(pack="(none)", projection="decode_kernel", epilogue="(none)", hin="(none)")
-PATH_NAMES = {0: "four-kernel", 1: "single-read", 2: "one-launch"}
+# the streaming path packs the weights inside its projection kernel (no pack launch)
+KERNEL_NAMES_STREAM = dict(KERNEL_NAMES, pack="(none)", projection="proj_stream_kernel")
+PATH_NAMES = {0: "four-kernel", 1: "single-read", 2: "one-launch", 3: "streaming"}
 
 
 def algorithmic_bytes(wl, *, intermediates: bool) -> int:
@@ -441,8 +443,9 @@ def main():
     out = run.alloc_outputs()
     stream = torch.cuda.current_stream(dev)
     path = run.path(pre_mix is not None)
-    single_read, one_launch = path == 1, path == 2
-    names = KERNEL_NAMES_ONE_LAUNCH if one_launch else KERNEL_NAMES_SINGLE_READ if single_read else KERNEL_NAMES
+    single_read, one_launch, streaming = path == 1, path == 2, path == 3
+    names = (KERNEL_NAMES_ONE_LAUNCH if one_launch else KERNEL_NAMES_SINGLE_READ if single_read
+             else KERNEL_NAMES_STREAM if streaming else KERNEL_NAMES)
 
     if args.calib_copy_mib > 0:
         print(f"[bench] calibration copy {args.calib_copy_mib} MiB", file=sys.stderr, flush=True)
@@ -468,7 +471,8 @@ def main():
     # per-kernel durations: a second pass of K steps with HIP events on the launch stream;
     # one set of events per step, each recorded once here so that its HIP event exists
     # before the library records it. Boundaries around a stage that launches nothing (the
-    # pack and hIn stages of the single-read path; all but the one kernel of the one-launch
+    # pack and hIn stages of the single-read path, the pack stage of the streaming path and
+    # its hIn stage with pre_mix; all but the one kernel of the one-launch
     # path) are not recorded: each record costs a few microseconds on the stream. Before each step (outside its events) a 512 MiB
     # write evicts the Infinity Cache, except for decode (launch-bound, back to back).
     flush = None
@@ -477,6 +481,10 @@ def main():
     wanted = [True] * mhc.FORWARD_EVENTS
     if single_read:
         wanted[0] = wanted[-1] = False
+    if streaming:
+        wanted[0] = False
+        if pre_mix is not None:
+            wanted[-1] = False
     if one_launch:
         wanted = [False, True, True, False, False]
     evs = [[torch.cuda.Event(enable_timing=True) if w else None for w in wanted]

@@ -160,11 +160,17 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
  * every non-NULL output listed in mhc_pre_tensors. `workspace` is device memory of at
  * least mhc_pre_workspace_size bytes, 256-byte aligned, zero-filled before its first use.
  * When tensors->phi_packed is NULL the weights are packed from phi (and gamma): by a pack
- * kernel into the workspace on the four-kernel path, inside the kernel on the single-read
- * and one-launch paths. Then one of three kernel sequences (mhc_pre_forward_path tells
- * which):
+ * kernel into the workspace on the four-kernel path, inside the kernel on the streaming,
+ * single-read and one-launch paths. Then one of four kernel sequences
+ * (mhc_pre_forward_path tells which):
  *   four-kernel path: a projection kernel (which with pre_mix also writes hIn), a
  *     per-token epilogue and, without pre_mix, an hIn kernel (x is read twice);
+ *   streaming path (no pre_mix, D a multiple of 32, n == 4 with either alpha length or
+ *     n == 6 or 8 with n_alpha == 2, where neither kernel below serves): the same
+ *     epilogue and hIn kernels after a projection by persistent workgroups (one per
+ *     compute unit) that keep their slice of the packed weights in LDS, read x in
+ *     contiguous 1 KB runs of each token's row and load the next task's x while the
+ *     current one is on the matrix cores;
  *   single-read path (n == 4, n_alpha == 3, no pre_mix, 992 < D <= 7168 (32 to 224
  *     blocks of 32 positions), T >= 8192, a device of 8 XCDs with 32 compute units each):
  *     one kernel computes the projection, hPre and hIn, x read once, then the per-token
@@ -178,14 +184,15 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
  *     one workgroup per block of 32 positions, which exchange their partial sums and hPre
  *     through the workspace (bounded waits, as above: a time-out leaves the token's
  *     outputs NaN, or only hIn when it comes at hPre, and mhc_pre_wait_status reports it).
- *   The single-read and one-launch paths take bf16 or fp16 x.
+ *   Every path takes bf16 or fp16 x.
  * Every path can be captured into a HIP graph.
  * The paths sum the projection's partial products in different groupings, so their
  * outputs may differ in the last bits; each meets the same accuracy. Within a call, hIn
  * uses exactly the hPre it emits. Results are bitwise reproducible for the same inputs,
  * parameters and path. The environment variable MHC_FORWARD_PATH = "classic" or
  * "fused" (for tests) overrides the choice: "classic" the four-kernel path, "fused" the
- * single-read kernel where its geometry allows it (neither then takes the one-launch path).
+ * single-read kernel where its geometry allows it (neither then takes the one-launch path;
+ * "fused" falls back to the streaming or four-kernel path elsewhere).
  * Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
 mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
                            void* workspace, size_t workspace_bytes, void* stream);
@@ -224,7 +231,8 @@ mhc_status mhc_pre_forward_noalloc(const mhc_pre_params* params, const mhc_pre_t
 mhc_status mhc_pre_wait_status(void* workspace, size_t workspace_bytes, void* stream, int32_t* timed_out);
 
 /* Which path mhc_pre_forward would take for these parameters on the current device:
- * *path = 2 the one-launch kernel, 1 the single-read kernel, 0 the four-kernel path
+ * *path = 3 the streaming projection, 2 the one-launch kernel, 1 the single-read kernel,
+ * 0 the four-kernel path
  * (has_pre_mix: whether pre_mix
  * will be given). Errors: NULLPTR, PARAM_INVALID. */
 mhc_status mhc_pre_forward_path(const mhc_pre_params* params, int32_t has_pre_mix, int32_t* path);

@@ -1525,6 +1525,313 @@ __device__ __forceinline__ void sinkhorn4(const ForwardArgs& a, int64_t T, const
     if (live) a.h_res[tk * NN + e] = v;
 }
 
+// ------------------------------------------------------------------ streaming projection
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 47] (a scalar branch to the instruction
+// with that count); a larger n waits for everything, which is always safe.
+template <int K>
+__device__ __forceinline__ void wait_vm_case()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(K) : "memory");
+}
+template <int B>
+__device__ __forceinline__ bool wait_vm_range(int n)
+{
+    if constexpr (B < kStreamMaxWait + 1) {
+        if (n == B) {
+            wait_vm_case<B>();
+            return true;
+        }
+        return wait_vm_range<B + 1>(n);
+    } else {
+        return false;
+    }
+}
+__device__ __forceinline__ void wait_vm_n(int n)
+{
+    if (!wait_vm_range<0>(n)) wait_vm_case<0>();
+}
+// A ring load into a register whose previous value is still read: the register is the
+// asm statement's input and output, so the compiler keeps the value in place (the reads of
+// the old value it orders before the load) and never copies the register while the load is
+// in flight.
+__device__ __forceinline__ void reload_ring(u32x4& v, i32x4 desc, uint32_t off)
+{
+    asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "+v"(v) : "v"(off), "s"(desc) : "memory");
+}
+// s_barrier after this wave's LDS operations have completed, without the vector memory
+// wait a workgroup fence would add (x loads of the next task stay in flight across it).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+// The four-kernel path's projection (same 64-token tiles and partial-record layout, so the
+// epilogue and hIn kernels follow unchanged) for calls without pre_mix and with D a
+// multiple of 32, by persistent workgroups with a different split of K: slice s is the NKS
+// K-steps [NKS s, NKS s + NKS) of the flattened row (K-step g holds elements [32 g, 32 g + 32)
+// of x[t] as n*D values, i.e. stream g / nblk, d-block g mod nblk), so a task reads one
+// contiguous run of 64 NKS bytes of each token row. On MI355X such 1 KB runs stream at about
+// 6.2 TB/s, against about 4.5 TB/s for the 128 to 256-byte runs per stream of the
+// projection kernel's slices (all n streams of a few d-blocks, which hIn from registers
+// needs). Workgroup b keeps the packed weights of slice s = b mod S in LDS for the whole
+// launch (gathered from phi_packed, whose K-steps are d-block-major, or split from phi and
+// gamma by the workgroup itself as the pack kernel splits them: no pack launch), and its two
+// halves (waves 0-3 and 4-7) each walk the tiles h, h + 2W, h + 4W, .. with h = 2 (b / S) +
+// half and W workgroups per slice; each half holds two tasks' x in registers, the next
+// task's x streaming in while the current one runs on the matrix cores. With S a multiple
+// of 8 every workgroup of a slice runs on the same XCD (workgroups are dealt to the XCDs in
+// turn), whose L2 then serves the slice's weights to all of them.
+// Per task and half: wait for the task's x; 16 x 16 x 32 products of each wave's 16 tokens
+// (and x x^T for the squares) in K-step order, two K-steps at a time, each pair's registers
+// reloaded with the x of the task after next as soon as its products are issued (so about
+// two tasks' x stay in flight all along); column totals to LDS; barrier; the records;
+// barrier. The x loads are issued from inline assembly, invisible to the compiler, and
+// waited for with explicit counts (stream_younger_than_x); every thread issues the same
+// number of record stores per task (out-of-range offsets for the ones with nothing to
+// write), so the counts hold for every wave.
+template <int N, int A, int NKS, bool H>
+__global__ void __launch_bounds__(kSThreads, 1)
+proj_stream_kernel(KArgs k, int W, int NI)
+{
+    using C = Cfg<N, A>;
+    constexpr int NT = C::NT, NC = C::NC, M = C::M, CH = C::CH, PPS = C::PPS;
+    constexpr int WU = NKS * 4 * NC;               // 16-byte weight units of a slice
+    constexpr int NREC = stream_rec_stores(CH);    // record stores per thread and task
+    static_assert(stream_fits(N, A, NKS), "weights and column totals in LDS, x in registers");
+    __shared__ u32x4 wl[WU];
+    __shared__ float red[2][kTileTokens * NC];     // each half's column totals
+    __shared__ float lds_ss[2][kTileTokens];       // and squares
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = wave >> 2, hw = wave & 3;
+    const int htid = tid & (kThreads - 1);         // thread within the half
+    const int lane = tid & 63;
+    const int j = lane & 15, grp = lane >> 4;
+    const int row = hw * 16 + j;                   // the lane's token within its tile
+    const int s = (int)(blockIdx.x % (unsigned)k.S);
+    const int64_t h0 = 2 * (int64_t)(blockIdx.x / (unsigned)k.S) + half;   // first tile of this half
+    const int64_t hstep = 2 * (int64_t)W;
+    const int nblk = k.D / kBlock;
+    const int nks = N * nblk;                      // K-steps holding data
+    const int g0 = s * NKS;                        // the slice's first K-step
+    // the lane's octet of K-step g0 in its token's row; K-steps past the data read zero
+    const uint32_t xo = (uint32_t)(((int64_t)row * k.K + (int64_t)kBlock * g0 + 8 * grp) * 2);
+
+    u32x4 xr[2][NKS];
+    auto live = [&](int it) { return h0 + hstep * it < k.tiles; };
+    auto xoff = [&](int st) { return g0 + st < nks ? xo + 2 * kBlock * st : kOutOfRange; };
+    auto xdesc = [&](int it) {
+        const int64_t t0 = (h0 + hstep * it) * kTileTokens;
+        const int64_t nt = k.T - t0 < kTileTokens ? k.T - t0 : kTileTokens;
+        return raw_desc(k.a.x + t0 * k.K, (uint32_t)(nt * k.K * 2));
+    };
+    auto issue = [&](int it, u32x4 (&dst)[NKS]) {
+        const i32x4 desc = xdesc(it);
+#pragma unroll
+        for (int st = 0; st < NKS; ++st) dst[st] = load_ring(desc, xoff(st));
+    };
+    // x loads in flight once both first tasks' loads are out
+    const int x_out = (live(0) ? NKS : 0) + (live(1) ? NKS : 0);
+
+    // Prologue: the slice's weights first, then the x of tasks 0 and 1, all in flight at once;
+    // the weights are waited for by count (x keeps streaming meanwhile), then copied or split
+    // into LDS. (With phi not 16-byte aligned, the compiler's own loads split it, and the x
+    // loads go out after them.)
+    constexpr int PU = (WU + kSThreads - 1) / kSThreads;   // packed units a thread copies
+    constexpr int ITEMS = NKS * 4 * M;                     // (K-step, octet row, phi row) items
+    constexpr int PER = (ITEMS + kSThreads - 1) / kSThreads;
+    const bool vec = ((reinterpret_cast<uintptr_t>(k.a.phi) | reinterpret_cast<uintptr_t>(k.a.gamma)) & 15) == 0;
+    // split an item's 8 weights (times gamma) into its three LDS units, as prepack_kernel
+    // does: in fp32 without gamma (the same bits), else of the product in fp64
+    auto split_item = [&](int it, const float (&pv)[8], const float (&gv)[8]) {
+        const int m = it % M, rw = it / M;             // rw = K-step * 4 + octet
+        u32x4 w3[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint32_t tb[3];
+            if (k.a.gamma) split3_x<H>((double)pv[e] * (double)gv[e], tb);
+            else split3_x32<H>(pv[e], tb);
+#pragma unroll
+            for (int term = 0; term < 3; ++term) w3[term][e >> 1] |= tb[term] << (16 * (e & 1));
+        }
+#pragma unroll
+        for (int term = 0; term < 3; ++term) wl[rw * NC + term * M + m] = w3[term];
+    };
+    if (k.a.packed) {
+        // K-step g is packed K-step (g mod nblk) N + g / nblk; past the data: the packed
+        // buffer's zero K-steps
+        const i32x4 pd = raw_desc(k.a.packed, (uint32_t)((int64_t)(nks + kPadSteps) * 4 * NC * 16));
+        u32x4 pw[PU];
+#pragma unroll
+        for (int q = 0; q < PU; ++q) {
+            const int u = tid + q * kSThreads;
+            const int g = g0 + u / (4 * NC);
+            const int64_t pst = g < nks ? (int64_t)(g % nblk) * N + g / nblk : (int64_t)nks;
+            pw[q] = load_ring(pd, u < WU ? (uint32_t)((pst * 4 * NC + u % (4 * NC)) * 16) : kOutOfRange);
+        }
+        if (live(0)) issue(0, xr[0]);
+        if (live(1)) issue(1, xr[1]);
+        wait_vm_n(x_out);
+#pragma unroll
+        for (int q = 0; q < PU; ++q) {
+            asm volatile("" : "+v"(pw[q]) : : "memory");
+            const int u = tid + q * kSThreads;
+            if (u < WU) wl[u] = pw[q];
+        }
+    } else if (vec) {
+        // an item's 8 weights (and gammas) are consecutive and start at a multiple of 8
+        // elements: two 16-byte loads each; items past the data read zeros
+        const i32x4 phd = raw_desc(k.a.phi, (uint32_t)((int64_t)M * k.K * 4));
+        const i32x4 gmd = raw_desc(k.a.gamma, (uint32_t)(k.K * 4));
+        u32x4 pl[PER][2], gl[PER][2];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int it = tid + q * kSThreads;
+            const int m = it % M, rw = it / M;
+            const int g = g0 + rw / 4;
+            const bool ok = it < ITEMS && g < nks;
+            const int64_t k0 = (int64_t)kBlock * g + 8 * (rw % 4);   // flattened K index
+            const uint32_t po = ok ? (uint32_t)(((int64_t)m * k.K + k0) * 4) : kOutOfRange;
+            pl[q][0] = load_ring(phd, po);
+            pl[q][1] = load_ring(phd, ok ? po + 16 : kOutOfRange);
+            if (k.a.gamma) {
+                const uint32_t go = ok ? (uint32_t)(k0 * 4) : kOutOfRange;
+                gl[q][0] = load_ring(gmd, go);
+                gl[q][1] = load_ring(gmd, ok ? go + 16 : kOutOfRange);
+            }
+        }
+        if (live(0)) issue(0, xr[0]);
+        if (live(1)) issue(1, xr[1]);
+        wait_vm_n(x_out);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            asm volatile("" : "+v"(pl[q][0]), "+v"(pl[q][1]) : : "memory");
+            if (k.a.gamma) asm volatile("" : "+v"(gl[q][0]), "+v"(gl[q][1]) : : "memory");
+            const int it = tid + q * kSThreads;
+            if (it >= ITEMS) continue;
+            float pv[8], gv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = __uint_as_float(pl[q][e >> 2][e & 3]);
+                gv[e] = k.a.gamma ? __uint_as_float(gl[q][e >> 2][e & 3]) : 1.f;
+            }
+            split_item(it, pv, gv);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int it = tid + q * kSThreads;
+            if (it >= ITEMS) continue;
+            const int m = it % M, rw = it / M;
+            const int g = g0 + rw / 4;
+            const bool ok = g < nks;
+            const int64_t k0 = (int64_t)kBlock * g + 8 * (rw % 4);
+            float pv[8], gv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = ok ? k.a.phi[(int64_t)m * k.K + k0 + e] : 0.f;
+                gv[e] = ok && k.a.gamma ? k.a.gamma[k0 + e] : 1.f;
+            }
+            split_item(it, pv, gv);
+        }
+        if (live(0)) issue(0, xr[0]);
+        if (live(1)) issue(1, xr[1]);
+    }
+    if (!k.a.packed) {
+        // the padding columns 3M .. NC - 1 (their products land in columns no record reads)
+        if constexpr (NC > 3 * M) {
+            for (int u = tid; u < NKS * 4 * (NC - 3 * M); u += kSThreads)
+                wl[(u / (NC - 3 * M)) * NC + 3 * M + u % (NC - 3 * M)] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    lds_barrier();   // the weights are in LDS (the x loads stay in flight)
+
+    const u32x4* wb = wl + grp * NC + j;
+    for (int it0 = 0; it0 < NI; it0 += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int it = it0 + u;
+            if (it >= NI) break;                       // (the same for the whole workgroup)
+            const bool on = live(it);
+            const int64_t tile = h0 + hstep * it;
+            const int ntile = on ? tile_tokens(k, tile * kTileTokens) : 0;
+            if (on) {
+                wait_vm_n(stream_younger_than_x(it, live(it + 1), NKS, NREC));
+#pragma unroll
+                for (int st = 0; st < NKS; ++st) asm volatile("" : "+v"(xr[u][st]) : : "memory");
+                // the x of task it + 2 goes into each register pair once its products are issued
+                const bool next2 = live(it + 2);
+                const i32x4 desc2 = xdesc(next2 ? it + 2 : it);
+                f32x4 acc[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 sq = {0.f, 0.f, 0.f, 0.f};
+                // the weight operands of two K-steps read from LDS before their products
+#pragma unroll
+                for (int st0 = 0; st0 < NKS; st0 += 2) {
+                    u32x4 bw[2][NT];
+#pragma unroll
+                    for (int di = 0; di < 2; ++di)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) bw[di][nt] = wb[(st0 + di) * 4 * NC + nt * 16];
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int di = 0; di < 2; ++di) {
+                        const u32x4 xa = xr[u][st0 + di];
+                        sq = mfma_x16<H>(xa, xa, sq);
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_x16<H>(xa, bw[di][nt], acc[nt]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (next2) {
+#pragma unroll
+                        for (int di = 0; di < 2; ++di) reload_ring(xr[u][st0 + di], desc2, xoff(st0 + di));
+                    }
+                }
+                float* rd = red[half];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) rd[(hw * 16 + 4 * grp + r) * NC + nt * 16 + j] = acc[nt][r];
+                const int rr = j - 4 * grp;
+                if (rr >= 0 && rr < 4) lds_ss[half][hw * 16 + j] = sq[rr];
+            }
+            lds_barrier();   // A: the column totals of both halves are in LDS
+            if (on) {
+                // the records (hi + mid + lo of each phi row added in fp64, rounded once)
+                const float* rd = red[half];
+                const rsrc_t rec = make_rsrc(k.a.rec + rec_tile(tile, k.S, N, M), (int64_t)k.S * kTileTokens * C::V * 4);
+#pragma unroll
+                for (int q = 0; q < NREC; ++q) {
+                    const int idx0 = htid + q * kThreads;
+                    const bool ok = idx0 < kTileTokens * CH;
+                    const int idx = ok ? idx0 : 0;
+                    const int tl = idx / CH, ch = idx % CH;
+                    const float* rp = rd + tl * NC;
+                    u32x4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = 4 * ch + e;
+                        const int m = v < N ? v : N + (v - PPS);
+                        float val;
+                        if (v == N) val = lds_ss[half][tl];
+                        else if ((v > N && v < PPS) || v >= PPS + (M - N)) val = 0.f;   // padding
+                        else if (H)   // the fp16 terms carry scales 1, 2^11, 2^22 (split3_f16)
+                            val = (float)((double)rp[m] + 0x1p-11 * (double)rp[M + m] + 0x1p-22 * (double)rp[2 * M + m]);
+                        else val = (float)((double)rp[m] + (double)rp[M + m] + (double)rp[2 * M + m]);
+                        o[e] = __float_as_uint(val);
+                    }
+                    const uint32_t off = ok && tl < ntile ? (uint32_t)(rec_loc(s, tl, N, M) + 4 * ch) * 4 : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b128(o, rec, (int)off, 0, 0);
+                }
+            }
+            lds_barrier();   // B: both halves are done reading the column totals
+        }
+    }
+}
+
 // The whole forward of up to kDecodeTokens tokens in one launch (n = 4, alpha[3]): workgroup
 // b owns BPW d-blocks, BPW b .. BPW b + BPW - 1 (32 positions of each stream each; two
 // blocks a workgroup halve the records every token's owner reads, where there are still
@@ -1896,11 +2203,21 @@ hipError_t mark(void* const* events, int i, hipStream_t st)
 }
 
 template <int N, int A, int NKS, bool H>
-hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st, void* const* events, const float* phiT)
+hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st, void* const* events, const float* phiT,
+                        int stream_W)
 {
     // Workgroups map to tasks so that each XCD's L2 holds the weights of a few slices
     // only (task_of_block). phiT: the VALU projection's weights, or NULL for the matrix cores.
-    if constexpr (Cfg<N, A>::M <= 32) {
+    // stream_W > 0: the streaming projection with that many workgroups per slice.
+    if (stream_W > 0) {
+        if constexpr (stream_fits(N, A, NKS)) {
+            const int64_t NI = (p.tiles + 2 * (int64_t)stream_W - 1) / (2 * (int64_t)stream_W);
+            hipLaunchKernelGGL((proj_stream_kernel<N, A, NKS, H>), dim3((unsigned)(p.S * stream_W)), dim3(kSThreads),
+                               0, st, k, stream_W, (int)NI);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else if constexpr (Cfg<N, A>::M <= 32) {
         if (phiT)
             hipLaunchKernelGGL((proj_valu_kernel<N, A, NKS, H>), dim3((unsigned)p.proj_blocks), dim3(kThreads), 0, st, k,
                                phiT);
@@ -1946,7 +2263,30 @@ struct DeviceFacts {
     int cus = 0;
     bool fused_ok[2] = {false, false};       // [fp16 x]: no scratch, at least one workgroup per compute unit
     int decode_per_cu[2][2] = {{0, 0}, {0, 0}};   // [fp16 x][blocks a workgroup - 1]: 0, cannot run here
+    bool stream_ok[2][4] = {{false, false, false, false}, {false, false, false, false}};   // [fp16 x][stream_variant]
 };
+
+// The variants the streaming projection is compiled for (index into stream_ok), -1 others.
+int stream_variant(int n, int n_alpha, int nks)
+{
+    if (n == 4 && n_alpha == 3 && nks == 16) return 0;
+    if (n == 4 && n_alpha == 2 && nks == 16) return 1;
+    if (n == 8 && n_alpha == 2 && nks == 16) return 2;
+    if (n == 6 && n_alpha == 2 && nks == 12) return 3;
+    return -1;
+}
+
+// The streaming projection's x loads are invisible to the compiler, like the single-read
+// kernel's: it runs only from code without scratch memory, one workgroup per compute unit.
+template <int N, int A, int NKS, bool H>
+bool stream_kernel_ok()
+{
+    int per_cu = 0;
+    return no_scratch(reinterpret_cast<const void*>(proj_stream_kernel<N, A, NKS, H>)) &&
+           hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, proj_stream_kernel<N, A, NKS, H>, kSThreads, 0) ==
+               hipSuccess &&
+           per_cu >= 1;
+}
 constexpr int kMaxDevices = 64;
 
 // Workgroups of the one-launch kernel a compute unit holds at once. (Its loads are all the
@@ -1970,6 +2310,10 @@ void fill_facts(DeviceFacts& f)
                     per_cu >= 1;
     f.decode_per_cu[H][0] = decode_per_cu<H, 1>();
     f.decode_per_cu[H][1] = decode_per_cu<H, 2>();
+    f.stream_ok[H][0] = stream_kernel_ok<4, 3, 16, H>();
+    f.stream_ok[H][1] = stream_kernel_ok<4, 2, 16, H>();
+    f.stream_ok[H][2] = stream_kernel_ok<8, 2, 16, H>();
+    f.stream_ok[H][3] = stream_kernel_ok<6, 2, 12, H>();
 }
 
 const DeviceFacts* device_facts()
@@ -2132,10 +2476,32 @@ static bool projection_on_valu(const Plan& p, const ForwardArgs& a)
     return false;
 }
 
+// Workgroups per slice of the streaming projection on the current device (one workgroup
+// per compute unit at most, no more than the tile pairs), 0 when it does not serve: with
+// pre_mix (whose hIn the projection kernel writes from registers, which needs all n streams
+// of a position in a lane), D not a multiple of 32, a variant it is not compiled for, code
+// that cannot run here, or MHC_FORWARD_PATH = "classic" / MHC_PROJECTION = "valu" asking
+// for the four-kernel path.
+int stream_workgroups_per_slice(const Plan& p, bool has_pre_mix)
+{
+    if (has_pre_mix || p.g.D % kBlock != 0) return 0;
+    const char* env = std::getenv("MHC_FORWARD_PATH");
+    if (env && std::strcmp(env, "classic") == 0) return 0;
+    const char* pe = std::getenv("MHC_PROJECTION");
+    if (pe && std::strcmp(pe, "valu") == 0) return 0;
+    const int v = stream_variant(p.g.n, p.g.n_alpha, p.NKS);
+    const DeviceFacts* d = device_facts();
+    if (v < 0 || !d || d->cus <= 0 || p.S <= 0 || p.tiles <= 0 || !d->stream_ok[p.g.x_f16 ? 1 : 0][v]) return 0;
+    int64_t W = d->cus / p.S;
+    if (W > (p.tiles + 1) / 2) W = (p.tiles + 1) / 2;
+    return W < 1 ? 1 : (int)W;
+}
+
 int forward_path(const Plan& p, bool has_pre_mix)
 {
     if (decode_wanted(p, has_pre_mix)) return 2;
-    return fused_wanted(p, has_pre_mix) && fused_groups(p) > 0 ? 1 : 0;
+    if (fused_wanted(p, has_pre_mix) && fused_groups(p) > 0) return 1;
+    return stream_workgroups_per_slice(p, has_pre_mix) > 0 ? 3 : 0;
 }
 
 int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void* packed,
@@ -2232,8 +2598,10 @@ int launch_forward(const Plan& p, const ForwardArgs& a_in, void* stream, void* c
             return (int)launch_fused(p, a, G, st, events);
         }
     }
-    // the projection on the VALU (fp32 weights packed here, from phi) or the matrix cores
-    const bool valu = projection_on_valu(p, a);
+    // the streaming projection (weights packed inside the kernel), else the projection on
+    // the VALU (fp32 weights packed here, from phi) or the matrix cores
+    const int stream_W = stream_workgroups_per_slice(p, a.pre_mix != nullptr);
+    const bool valu = stream_W == 0 && projection_on_valu(p, a);
     const float* phiT = nullptr;
     if (valu) {
         const int64_t items = p.g.K * (int64_t)p.g.M;
@@ -2241,7 +2609,7 @@ int launch_forward(const Plan& p, const ForwardArgs& a_in, void* stream, void* c
                            static_cast<float*>(a.packed_ws), p.g.K, p.g.M);
         if (hipGetLastError() != hipSuccess) return (int)hipErrorUnknown;
         phiT = static_cast<const float*>(a.packed_ws);
-    } else if (!a.packed) {
+    } else if (!a.packed && stream_W == 0) {
         if (launch_prepack(p.g, a.phi, a.gamma, a.packed_ws, stream) != 0) return (int)hipErrorUnknown;
         a.packed = a.packed_ws;
     }
@@ -2268,10 +2636,9 @@ int launch_forward(const Plan& p, const ForwardArgs& a_in, void* stream, void* c
     if (n == 6 && na == 2 && (v.nt != Cfg<6, 2>::NT || v.sk != Cfg<6, 2>::SK)) return (int)hipErrorInvalidValue;
     hipError_t e = hipErrorInvalidValue;
     const bool h = p.g.x_f16 != 0;
-#define MHC_GROUP(NV, AV, KV) (h ? launch_group<NV, AV, KV, true>(p, k, st, events, phiT) \
-                                 : launch_group<NV, AV, KV, false>(p, k, st, events, phiT))
+#define MHC_GROUP(NV, AV, KV) (h ? launch_group<NV, AV, KV, true>(p, k, st, events, phiT, stream_W) \
+                                 : launch_group<NV, AV, KV, false>(p, k, st, events, phiT, stream_W))
     if (n == 4 && na == 3 && nks == 16) e = MHC_GROUP(4, 3, 16);
-    else if (n == 4 && na == 2 && nks == 32) e = MHC_GROUP(4, 2, 32);
     else if (n == 4 && na == 2 && nks == 16) e = MHC_GROUP(4, 2, 16);
     else if (n == 8 && na == 3 && nks == 8) e = MHC_GROUP(8, 3, 8);
     else if (n == 8 && na == 2 && nks == 16) e = MHC_GROUP(8, 2, 16);

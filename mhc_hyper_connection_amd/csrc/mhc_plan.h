@@ -73,6 +73,34 @@ constexpr int kFLag = kFRing - kFAhead;   // rounds between a tile's projection 
 constexpr int kFLoads = 4;             // x loads of a compute wave per round (one per stream, n = 4)
 constexpr int64_t kFMinTokens = 8192;  // below this the four-kernel path is used (ramp and drain dominate)
 
+// Streaming projection (proj_stream_kernel): persistent workgroups of two halves of
+// kThreads, each half on its own 64-token tile of the workgroup's slice.
+constexpr int kSThreads = 2 * kThreads;
+constexpr int kLdsBytes = 160 * 1024;  // LDS of a compute unit (gfx950)
+// Record stores a thread issues per task (64 tokens x CH 16-byte chunks over kThreads).
+MHC_HOST_DEVICE constexpr int stream_rec_stores(int CH) { return (kTileTokens * CH + kThreads - 1) / kThreads; }
+// Whether a variant's slice fits the streaming projection: its packed weights (NKS K-steps
+// of 4 x NC 16-byte units) and both halves' column totals in LDS, and two tasks' x (NKS
+// 16-byte registers each) per lane.
+MHC_HOST_DEVICE constexpr bool stream_fits(int n, int n_alpha, int nks)
+{
+    return nks <= 16 && nks % n == 0 &&
+           nks * 4 * (16 * ((3 * (n_alpha == 3 ? n * n + 2 * n : 2 * n) + 15) / 16)) * 16 +
+                   2 * kTileTokens * (16 * ((3 * (n_alpha == 3 ? n * n + 2 * n : 2 * n) + 15) / 16)) * 4 +
+                   2 * kTileTokens * 4 <=
+               kLdsBytes - 8 * 1024;
+}
+// Vector memory operations a half's wave has issued after the x loads of its task `it`
+// when it waits for them. Task 0's and 1's loads go out in the prologue; task it + 2's
+// during task it's products, before task it's record stores (nstore). So after task it's
+// loads come: task it + 1's loads (lg, if that task exists) and the record stores of tasks
+// it - 1 (for it >= 1) and it - 2 (for it >= 2).
+MHC_HOST_DEVICE constexpr int stream_younger_than_x(int it, bool next_live, int lg, int nstore)
+{
+    return (it >= 2 ? nstore : 0) + (it >= 1 ? nstore : 0) + (next_live ? lg : 0);
+}
+constexpr int kStreamMaxWait = 47;     // the largest vmcnt the streaming kernel waits down to
+
 // Groups of the single-read kernel: one per XCD (the hardware's XCC id), so the values
 // its members exchange stay in that XCD's L2; member = arrival order on the XCD.
 constexpr int kXcds = 8;               // XCDs (groups at most)
@@ -120,7 +148,7 @@ inline Variant variant_of(int n, int n_alpha)
 {
     Variant v;
     if (n == 4 && n_alpha == 3) { v.nt = 5; v.sk = 1; v.nks_big = 16; v.nks_small = 16; }
-    else if (n == 4 && n_alpha == 2) { v.nt = 2; v.sk = 4; v.nks_big = 32; v.nks_small = 16; }
+    else if (n == 4 && n_alpha == 2) { v.nt = 2; v.sk = 4; v.nks_big = 16; v.nks_small = 16; }
     else if (n == 8 && n_alpha == 3) { v.nt = 15; v.sk = 1; v.nks_big = 8; v.nks_small = 8; }
     else if (n == 8 && n_alpha == 2) { v.nt = 3; v.sk = 2; v.nks_big = 16; v.nks_small = 16; }
     else if (n == 6 && n_alpha == 3) { v.nt = 9; v.sk = 1; v.nks_big = 12; v.nks_small = 12; }

@@ -28,9 +28,9 @@ def _runner(wl, nb):
 
 
 @pytest.mark.parametrize("T,D,pre_mix,n,n_alpha,want", [
-    (1, 7168, False, 4, 3, 2), (64, 7168, False, 4, 3, 2), (65, 7168, False, 4, 3, 0),
+    (1, 7168, False, 4, 3, 2), (64, 7168, False, 4, 3, 2), (65, 7168, False, 4, 3, 3),
     (64, 7168, True, 4, 3, 0), (64, 16384, False, 4, 3, 2), (8, 8, False, 4, 3, 2),
-    (16, 1024, False, 4, 2, 0), (16, 1024, False, 8, 3, 0), (16, 1024, False, 6, 3, 0)])
+    (16, 1024, False, 4, 2, 3), (16, 1024, False, 8, 3, 0), (16, 1024, False, 6, 3, 0)])
 @pytest.mark.parametrize("f16", [False, True])
 def test_path_selection(T, D, pre_mix, n, n_alpha, want, f16, monkeypatch):
     import mhc_hyper_connection_amd as mhc

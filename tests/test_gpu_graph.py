@@ -1,8 +1,9 @@
 """The forward captured into a HIP graph (torch.cuda.CUDAGraph on torch's current stream):
 no path records a memset or a host synchronisation, so each can be captured (the
 one-launch path in the first two cases, whose kernel clears its barrier counters in the
-workspace at its end; the four-kernel path, forced by MHC_FORWARD_PATH=classic at 64
-tokens; the single-read path forced by MHC_FORWARD_PATH=fused in the last case: its kernel
+workspace at its end; the streaming path at 4096 tokens, with packed and unpacked weights;
+the four-kernel path, forced by MHC_FORWARD_PATH=classic; the single-read path forced by
+MHC_FORWARD_PATH=fused in the last case: its kernel
 and the epilogue keep the call counter and the per-XCD arrival counters in the workspace,
 which each replay advances and clears as an eager call does). Every replay, with eager work of
 the program between replays, must equal the eager call bit for bit (the forward is
@@ -19,14 +20,15 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("T,D,packed,path", [(64, 7168, True, 2), (64, 7168, False, 2), (64, 7168, True, 0),
-                                              (4096, 1024, True, 0), (1500, 2048, False, 1)])
+                                              (4096, 1024, True, 3), (4096, 1024, False, 3), (4096, 1024, True, 0),
+                                              (1500, 2048, False, 1)])
 def test_graph_replays_match_eager(T, D, packed, path, monkeypatch):
     import mhc_hyper_connection_amd as mhc
     import torch
     monkeypatch.delenv("MHC_FORWARD_PATH", raising=False)
     if path == 1:
         monkeypatch.setenv("MHC_FORWARD_PATH", "fused")
-    elif path == 0 and T <= 64:
+    elif path == 0:
         monkeypatch.setenv("MHC_FORWARD_PATH", "classic")
     print(f"[case] graph T={T} D={D} packed={packed} path={path}", file=sys.stderr, flush=True)
     dev = device()

@@ -32,10 +32,12 @@ def _timeout_flag(runner):
 
 @pytest.mark.parametrize("T,D,pre_mix,n,n_alpha,want", [
     (16384, 7168, False, 4, 3, 1), (8192, 4096, False, 4, 3, 1), (8192, 1024, False, 4, 3, 1),
-    (64, 7168, False, 4, 3, 2), (8191, 7168, False, 4, 3, 0), (8192, 7168, False, 4, 3, 1),
-    (4096, 4096, False, 4, 3, 0), (16384, 7168, True, 4, 3, 0), (8192, 8192, False, 4, 3, 0),
-    (8192, 992, False, 4, 3, 0), (8192, 1016, False, 4, 3, 1), (8192, 2048, False, 8, 3, 0),
-    (8192, 2048, False, 4, 2, 0)])
+    (64, 7168, False, 4, 3, 2), (8191, 7168, False, 4, 3, 3), (8192, 7168, False, 4, 3, 1),
+    (4096, 4096, False, 4, 3, 3), (16384, 7168, True, 4, 3, 0), (8192, 8192, False, 4, 3, 3),
+    (8192, 992, False, 4, 3, 3), (8192, 1016, False, 4, 3, 1), (8192, 2048, False, 8, 3, 0),
+    (8192, 2048, False, 4, 2, 3), (32768, 2048, True, 8, 2, 0), (8192, 2048, False, 6, 2, 3),
+    (8192, 1000, False, 4, 3, 1), (8192, 1000, True, 4, 3, 0),
+    (8192, 2048, False, 6, 3, 0)])
 @pytest.mark.parametrize("f16", [False, True])
 def test_path_selection(T, D, pre_mix, n, n_alpha, want, f16, monkeypatch):
     # the same choice for bf16 and fp16 x
