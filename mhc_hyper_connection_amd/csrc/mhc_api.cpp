@@ -129,7 +129,7 @@ mhc_status forward_impl(const mhc_pre_params* params, const mhc_pre_tensors* t,
     }
 
     // 4. workspace
-    const mhc::Plan plan = mhc::make_plan(g, params->T);
+    const mhc::Plan plan = mhc::make_plan(g, params->T, t->pre_mix != nullptr);
     if (workspace_bytes < plan.ws_bytes) return MHC_ERR_PARAM_INVALID;
 
     // 5. alignment: 16-byte vector access to x and hIn, 256-byte workspace sections

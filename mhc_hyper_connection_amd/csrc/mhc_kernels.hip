@@ -312,7 +312,7 @@ constexpr int younger_than_stage(int c)
 }
 
 template <int N, int A, int NKS, bool H>
-__global__ void __launch_bounds__(kThreads, 3)
+__global__ void __launch_bounds__(kThreads, NKS > 16 ? 2 : 3)
 proj_kernel(KArgs k)
 {
     using C = Cfg<N, A>;
@@ -2642,6 +2642,7 @@ int launch_forward(const Plan& p, const ForwardArgs& a_in, void* stream, void* c
     else if (n == 4 && na == 2 && nks == 16) e = MHC_GROUP(4, 2, 16);
     else if (n == 8 && na == 3 && nks == 8) e = MHC_GROUP(8, 3, 8);
     else if (n == 8 && na == 2 && nks == 16) e = MHC_GROUP(8, 2, 16);
+    else if (n == 8 && na == 2 && nks == 32) e = MHC_GROUP(8, 2, 32);
     else if (n == 6 && na == 3 && nks == 12) e = MHC_GROUP(6, 3, 12);
     else if (n == 6 && na == 2 && nks == 12) e = MHC_GROUP(6, 2, 12);
 #undef MHC_GROUP

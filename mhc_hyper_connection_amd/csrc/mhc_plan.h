@@ -142,6 +142,7 @@ struct Variant {
     int sk = 0;
     int nks_big = 0;
     int nks_small = 0;
+    int nks_premix = 0;   // the large slice of a call with pre_mix
 };
 
 inline Variant variant_of(int n, int n_alpha)
@@ -150,9 +151,10 @@ inline Variant variant_of(int n, int n_alpha)
     if (n == 4 && n_alpha == 3) { v.nt = 5; v.sk = 1; v.nks_big = 16; v.nks_small = 16; }
     else if (n == 4 && n_alpha == 2) { v.nt = 2; v.sk = 4; v.nks_big = 16; v.nks_small = 16; }
     else if (n == 8 && n_alpha == 3) { v.nt = 15; v.sk = 1; v.nks_big = 8; v.nks_small = 8; }
-    else if (n == 8 && n_alpha == 2) { v.nt = 3; v.sk = 2; v.nks_big = 16; v.nks_small = 16; }
+    else if (n == 8 && n_alpha == 2) { v.nt = 3; v.sk = 2; v.nks_big = 16; v.nks_small = 16; v.nks_premix = 32; }
     else if (n == 6 && n_alpha == 3) { v.nt = 9; v.sk = 1; v.nks_big = 12; v.nks_small = 12; }
     else if (n == 6 && n_alpha == 2) { v.nt = 3; v.sk = 2; v.nks_big = 12; v.nks_small = 12; }
+    if (v.nks_premix == 0) v.nks_premix = v.nks_big;
     return v;
 }
 
@@ -231,15 +233,21 @@ struct Plan {
 MHC_HOST_DEVICE inline int pp_stride(int n);
 MHC_HOST_DEVICE inline int rec_stride(int n, int M);
 
-inline Plan make_plan(const Geometry& g, int64_t T)
+// pre_mix: the plan of a call with pre_mix, whose projection writes hIn from the x it holds
+// and so reads all n streams of a few d-blocks per slice: at n = 8 with alpha[2] and many
+// tokens its slices are twice as long (32 K-steps: 256-byte runs of each stream's row, half
+// the partial records). Its workspace sections are never larger than those of the same call
+// without pre_mix (mhc_pre_workspace_size's plan).
+inline Plan make_plan(const Geometry& g, int64_t T, bool pre_mix = false)
 {
     Plan p;
     p.g = g;
     p.T = T;
     p.tiles = (T + kTileTokens - 1) / kTileTokens;
     const Variant v = variant_of(g.n, g.n_alpha);
-    const int s_big = (g.nks + v.nks_big - 1) / v.nks_big;
-    p.NKS = p.tiles * s_big >= kBigTasks ? v.nks_big : v.nks_small;
+    const int big = pre_mix ? v.nks_premix : v.nks_big;
+    const int s_big = (g.nks + big - 1) / big;
+    p.NKS = p.tiles * s_big >= kBigTasks ? big : v.nks_small;
     p.S = (g.nks + p.NKS - 1) / p.NKS;
     p.GS = (p.S + 7) / 8;
     p.NG = (p.S + p.GS - 1) / p.GS;

@@ -4,7 +4,8 @@
 // problem sizes it replays, with the offset helpers the kernels use (mhc_plan.h), every
 // index the fused kernel forms from the plan -- packed-weight stage loads, x / hIn byte
 // offsets, partial-record blocks, summation groups, output token shares, workspace
-// sections -- and checks each against the extent of the buffer it addresses. Prints
+// sections -- and checks each against the extent of the buffer it addresses, for plans of
+// calls without and with pre_mix. Prints
 // "ok <cases>" or the first violation and exits non-zero.
 #include <cstdio>
 #include <cstdlib>
@@ -20,7 +21,7 @@ static int fail(const char* what, int n, int D, int na, long long T, long long a
     return 1;
 }
 
-static int check(int n, int D, int na, long long T)
+static int check(int n, int D, int na, long long T, bool pm)
 {
     Geometry g;
     if (!make_geometry(n, D, na, &g)) {
@@ -30,7 +31,11 @@ static int check(int n, int D, int na, long long T)
         if ((nks + v0.nks_small - 1) / v0.nks_small > kMaxSlices) return 0;
         return fail("geometry", n, D, na, T, 0, 0);
     }
-    const Plan p = make_plan(g, T);
+    const Plan p = make_plan(g, T, pm);
+    // a call with pre_mix fits the workspace that mhc_pre_workspace_size reports (the plan
+    // without pre_mix)
+    if (pm && p.ws_bytes > make_plan(g, T).ws_bytes)
+        return fail("pre_mix workspace", n, D, na, T, (long long)p.ws_bytes, (long long)make_plan(g, T).ws_bytes);
     const Variant v = variant_of(n, na);
     if (v.nt != g.NT) return fail("variant nt", n, D, na, T, v.nt, g.NT);
     // the pack kernel's row threads also zero the padding columns [3M, NC)
@@ -191,10 +196,11 @@ int main()
     for (int n : {4, 6, 8})
         for (int na : {2, 3})
             for (int D : Ds)
-                for (long long T : Ts) {
-                    if (check(n, D, na, T)) return 1;
-                    ++cases;
-                }
+                for (long long T : Ts)
+                    for (bool pm : {false, true}) {
+                        if (check(n, D, na, T, pm)) return 1;
+                        ++cases;
+                    }
     std::printf("ok %lld\n", cases);
     return 0;
 }

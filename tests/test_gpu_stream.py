@@ -57,9 +57,11 @@ def test_stream_parity(name, T, n, D, na, gamma, nb, f16, seed, monkeypatch):
 
 
 @pytest.mark.parametrize("T,n,D,na,pm,want", [(300, 4, 7168, 3, True, 0), (300, 8, 2048, 2, True, 0),
-                                             (300, 4, 1000, 3, False, 0), (300, 4, 992, 3, False, 3)])
+                                             (4100, 8, 2048, 2, True, 0), (300, 4, 1000, 3, False, 0),
+                                             (300, 4, 992, 3, False, 3)])
 def test_stream_not_taken(T, n, D, na, pm, want, monkeypatch):
     # with pre_mix or D not a multiple of 32 the four-kernel path serves, and meets the oracle
+    # (n = 8, alpha[2] with pre_mix at T = 4100: its 32-K-step slices and a partial last tile)
     monkeypatch.delenv("MHC_FORWARD_PATH", raising=False)
     print(f"[case] path T={T} n={n} D={D} alpha[{na}] pre_mix={pm}", file=sys.stderr, flush=True)
     inp = synth.custom(T, n, D, n_alpha=na, pre_mix=pm, need_backward=True, seed=330 + n)
