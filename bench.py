@@ -41,15 +41,17 @@ METRIC = "tokens/s and achieved HBM GB/s (% of peak) for fused mHC pre fwd, n=4"
 KERNEL_SOURCES = ("mhc_hyper_connection_amd/csrc/mhc_kernels.hip",
                   "mhc_hyper_connection_amd/csrc/mhc_device.h",
                   "mhc_hyper_connection_amd/csrc/mhc_plan.h")
+# the classic path: without pre_mix the epilogue writes hIn too, so no kernel runs in the
+# hIn stage on any path
 KERNEL_NAMES = {"pack": "prepack_kernel", "projection": "proj_kernel",
-                "epilogue": "epilogue_kernel", "hin": "hin_kernel"}
+                "epilogue": "epilogue_kernel", "hin": "(none)"}
 # the single-read path runs one kernel in the projection stage and none in the hIn stage
 KERNEL_NAMES_SINGLE_READ = dict(KERNEL_NAMES, projection="fused_kernel", hin="(none)")
 # the one-launch path of a few tokens: one kernel, timed as the projection stage
 KERNEL_NAMES_ONE_LAUNCH = dict(pack="(none)", projection="decode_kernel", epilogue="(none)", hin="(none)")
 # the streaming path packs the weights inside its projection kernel (no pack launch)
 KERNEL_NAMES_STREAM = dict(KERNEL_NAMES, pack="(none)", projection="proj_stream_kernel")
-PATH_NAMES = {0: "four-kernel", 1: "single-read", 2: "one-launch", 3: "streaming"}
+PATH_NAMES = {0: "classic", 1: "single-read", 2: "one-launch", 3: "streaming"}
 
 
 def algorithmic_bytes(wl, *, intermediates: bool) -> int:
@@ -81,9 +83,10 @@ def stage_bytes(wl, stage: str, single_read: bool = False, one_launch: bool = Fa
       projection  x read once (2K per token) and phi once (4MK); with pre_mix it also
                   reads pre_mix (4n per token) and writes hIn (2D per token); the
                   single-read kernel writes hIn too (2D per token)
-      epilogue    the per-token outputs: hPost, hRes, and the requested intermediates
-      hin         x read once and hIn written once (2K + 2D per token); nothing on the
-                  single-read path
+      epilogue    the per-token outputs: hPost, hRes, and the requested intermediates;
+                  without pre_mix on the classic and streaming paths also x read once
+                  and hIn written once (2K + 2D per token)
+      hin         nothing (no path launches a kernel there)
     On the one-launch path the projection stage's kernel is the whole call
     (algorithmic_bytes) and the other stages launch nothing."""
     T, n, D, M, it = wl.T, wl.n, wl.D, wl.M, wl.num_iters
@@ -105,9 +108,11 @@ def stage_bytes(wl, stage: str, single_read: bool = False, one_launch: bool = Fa
             b += T * 4 + T * M * 4 + T * n * 4
             if wl.n_alpha == 3:
                 b += 2 * it * T * n * 4 + 2 * it * T * n * n * 4
+        if not (wl.pre_mix or single_read):
+            b += T * 2 * K + T * D * 2
         return b
     if stage == "hin":
-        return 0 if wl.pre_mix or single_read else T * 2 * K + T * D * 2
+        return 0
     raise ValueError(stage)
 
 
@@ -483,8 +488,8 @@ def main():
         wanted[0] = wanted[-1] = False
     if streaming:
         wanted[0] = False
-        if pre_mix is not None:
-            wanted[-1] = False
+    if not one_launch:
+        wanted[-1] = False   # no path launches a kernel in the hIn stage
     if one_launch:
         wanted = [False, True, True, False, False]
     evs = [[torch.cuda.Event(enable_timing=True) if w else None for w in wanted]

@@ -160,14 +160,14 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
  * every non-NULL output listed in mhc_pre_tensors. `workspace` is device memory of at
  * least mhc_pre_workspace_size bytes, 256-byte aligned, zero-filled before its first use.
  * When tensors->phi_packed is NULL the weights are packed from phi (and gamma): by a pack
- * kernel into the workspace on the four-kernel path, inside the kernel on the streaming,
+ * kernel into the workspace on the classic path, inside the kernel on the streaming,
  * single-read and one-launch paths. Then one of four kernel sequences
  * (mhc_pre_forward_path tells which):
- *   four-kernel path: a projection kernel (which with pre_mix also writes hIn), a
- *     per-token epilogue and, without pre_mix, an hIn kernel (x is read twice);
+ *   classic path: a projection kernel (which with pre_mix also writes hIn) and a
+ *     per-token epilogue, which without pre_mix also writes hIn (x is read twice);
  *   streaming path (no pre_mix, D a multiple of 32, n == 4 with either alpha length or
  *     n == 6 or 8 with n_alpha == 2, where neither kernel below serves): the same
- *     epilogue and hIn kernels after a projection by persistent workgroups (one per
+ *     epilogue (writing hIn) after a projection by persistent workgroups (one per
  *     compute unit) that keep their slice of the packed weights in LDS, read x in
  *     contiguous 1 KB runs of each token's row and load the next task's x while the
  *     current one is on the matrix cores;
@@ -190,9 +190,9 @@ mhc_status mhc_pre_prepack(const mhc_pre_params* params, const float* phi, const
  * outputs may differ in the last bits; each meets the same accuracy. Within a call, hIn
  * uses exactly the hPre it emits. Results are bitwise reproducible for the same inputs,
  * parameters and path. The environment variable MHC_FORWARD_PATH = "classic" or
- * "fused" (for tests) overrides the choice: "classic" the four-kernel path, "fused" the
+ * "fused" (for tests) overrides the choice: "classic" the classic path, "fused" the
  * single-read kernel where its geometry allows it (neither then takes the one-launch path;
- * "fused" falls back to the streaming or four-kernel path elsewhere).
+ * "fused" falls back to the streaming or classic path elsewhere).
  * Errors: NULLPTR, PARAM_INVALID, RUNTIME. */
 mhc_status mhc_pre_forward(const mhc_pre_params* params, const mhc_pre_tensors* tensors,
                            void* workspace, size_t workspace_bytes, void* stream);
@@ -232,7 +232,7 @@ mhc_status mhc_pre_wait_status(void* workspace, size_t workspace_bytes, void* st
 
 /* Which path mhc_pre_forward would take for these parameters on the current device:
  * *path = 3 the streaming projection, 2 the one-launch kernel, 1 the single-read kernel,
- * 0 the four-kernel path
+ * 0 the classic path
  * (has_pre_mix: whether pre_mix
  * will be given). Errors: NULLPTR, PARAM_INVALID. */
 mhc_status mhc_pre_forward_path(const mhc_pre_params* params, int32_t has_pre_mix, int32_t* path);

@@ -94,7 +94,7 @@ class PreForward:
 
     def path(self, has_pre_mix=False):
         """2 when calls take the one-launch kernel on this device, 1 the single-read kernel,
-        0 the four-kernel path."""
+        0 the classic path."""
         return forward_path(self.params, has_pre_mix)
 
     def wait_status(self):

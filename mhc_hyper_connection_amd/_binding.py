@@ -171,7 +171,7 @@ def workspace_size(params: Params) -> int:
 
 def forward_path(params: Params, has_pre_mix: bool) -> int:
     """mhc_pre_forward's path on the current device: 2 the one-launch kernel, 1 the
-    single-read kernel, 0 the four-kernel path."""
+    single-read kernel, 0 the classic path."""
     out = ctypes.c_int32(0)
     st = load().mhc_pre_forward_path(ctypes.byref(params), int(bool(has_pre_mix)), ctypes.byref(out))
     if st != MHC_OK:

@@ -21,8 +21,13 @@
 //   epilogue_kernel  one workgroup per 16 (n = 4, T >= 8192) or 8 tokens: sums the S partial records of each token
 //                    in a fixed order (fp64), then invRms, hMix, the gates, the Sinkhorn
 //                    planes (one lane per matrix entry, sums across lanes by DPP) and,
-//                    without pre_mix, the hIn weights.
-//   hin_kernel       without pre_mix: hIn[t, d] = sum_i hPre[t, i] x[t, i, d].
+//                    without pre_mix, hIn[t, d] = sum_i hPre[t, i] x[t, i, d] of its
+//                    tokens (after the streaming or classic projection), or the hIn
+//                    weights (after the single-read kernel, which has written hIn).
+//   proj_stream_kernel  the projection of the streaming path: persistent workgroups,
+//                    one slice of packed weights resident in LDS each, x read in
+//                    contiguous 1 KB runs of each token's row (see the kernel).
+//   hin_kernel       hIn of the standalone Sinkhorn stage.
 //   fused_kernel     the single-read path (n = 4, alpha[3], no pre_mix, large T), in place
 //                    of proj_kernel and hin_kernel: one launch whose workgroups (a group of
 //                    32 per XCD) keep their weights in LDS and each tile's x in registers
@@ -450,7 +455,7 @@ proj_kernel(KArgs k)
 
 // ------------------------------------------------------------------ projection on the VALU
 
-// The projection with plain fp32 FMAs instead of the matrix cores, for the four-kernel path:
+// The projection with plain fp32 FMAs instead of the matrix cores, for the classic path:
 // the same tasks (64-token tile, slice of NKS K-steps) and the same partial records, so the
 // epilogue and hIn kernels are unchanged. Weights: phiT[k][m] = phi[m][k] gamma[k] in fp32
 // (the product rounded once), K rows of M, read by whole rows with scalar loads: every lane
@@ -738,8 +743,10 @@ __device__ void sinkhorn(const KArgs& k, const float* Ls, int64_t tfirst, int nb
 // Tokens [OB b, OB b + OB) of workgroup b, OB = out_tokens(N, T) (all in one tile). A load item is (token, group,
 // chunk): one 16-byte chunk of the token's record from the slices of one summation group
 // (slices [g GS, (g+1) GS)), summed in slice order in fp64; the group sums are then added
-// in group order. Every output of the tokens follows from the totals.
-template <int N, int A, int OB>
+// in group order. Every output of the tokens follows from the totals. HIN: the workgroup
+// then also writes its tokens' hIn from hPre and x (each token's n x D values are one
+// contiguous run of x), as hin_kernel would, so no hIn launch follows; H: x in fp16.
+template <int N, int A, int OB, bool HIN = false, bool H = false>
 __global__ void __launch_bounds__(kThreads)
 epilogue_kernel(KArgs k)
 {
@@ -749,6 +756,7 @@ epilogue_kernel(KArgs k)
     __shared__ double gs[OB * V * 8];    // [token][value][group]; group 0 then holds the total
     __shared__ float Ls[OB * NN];
     __shared__ float gpar[3 + M];        // alpha, bias
+    __shared__ float hps[HIN ? OB * N : 1];   // the tokens' hPre (HIN)
     const ForwardArgs& a = k.a;
     const int tid = threadIdx.x;
     const int64_t tf = (int64_t)blockIdx.x * OB;
@@ -811,6 +819,28 @@ epilogue_kernel(KArgs k)
         gs[it * 8] = t;
     }
     __syncthreads();
+    // HIN: the first batch of x for hIn goes out now, to arrive while the gates and the
+    // Sinkhorn (LDS and stores only) run; rows past the call's tokens lie outside the ranges
+    constexpr int IB = HIN ? 16 / N : 1;   // octets of a thread per batch (16 or 12 loads)
+    const int D8 = k.D / 8;
+    const int hin_items = HIN ? nb * D8 : 0;
+    const rsrc_t xr = make_rsrc(a.x + tf * k.K, HIN ? (int64_t)nb * k.K * 2 : 0);
+    const rsrc_t hr = make_rsrc(a.h_in + tf * k.D, HIN ? (int64_t)nb * k.D * 2 : 0);
+    u32x4 xv[IB][N];
+    auto hin_batch = [&](int it0) {
+#pragma unroll
+        for (int u = 0; u < IB; ++u) {
+            const int it = it0 + u * kThreads;
+            const int q = it / D8, o = it % D8;
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                xv[u][i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    xr, (int)(it < hin_items ? (uint32_t)((q * N + i) * k.D + 8 * o) * 2 : kOutOfRange), 0, 0);
+        }
+    };
+    if constexpr (HIN) {
+        if (tid < hin_items) hin_batch(tid);
+    }
 
     const float eps = (float)a.hc_eps;
     const rsrc_t r_mix = make_rsrc(a.h_mix + tf * M, a.h_mix ? (int64_t)nb * M * 4 : 0);
@@ -827,19 +857,51 @@ epilogue_kernel(KArgs k)
         if (m < N) {
             const float hp = gate_pre(h, inv, gpar[0], gpar[3 + m], eps);
             st_buf(r_pre, (uint32_t)(q * N + m) * 4, hp);
-            st_buf(r_wts, (uint32_t)(q * N + m) * 4, hp);
+            if constexpr (HIN) hps[q * N + m] = hp;
+            else st_buf(r_wts, (uint32_t)(q * N + m) * 4, hp);
         } else if (m < 2 * N) {
             st_buf(r_post, (uint32_t)(q * N + m - N) * 4, gate_post(h, inv, gpar[1], gpar[3 + m], eps, A == 2));
         } else {
             Ls[q * NN + (m - 2 * N)] = res_logit(h, inv, gpar[2], gpar[3 + m]);
         }
     }
+    if constexpr (A == 3 || HIN) __syncthreads();
     if constexpr (A == 3) {
-        __syncthreads();
         sinkhorn<N>(k, Ls, tf, nb);
     } else {
         const rsrc_t r_res = make_rsrc(a.h_res + tf * NN, a.h_res ? (int64_t)nb * NN * 4 : 0);
         for (int it = tid; it < nb * NN; it += kThreads) st_buf(r_res, (uint32_t)it * 4, 0.f);
+    }
+    if constexpr (HIN) {
+        // hIn[t, d] = sum_i hPre[t, i] x[t, i, d], octet by octet (the arithmetic of
+        // hin_kernel: the same bits), IB octets of a thread per batch; the first batch was
+        // loaded before the gates and the Sinkhorn
+#pragma unroll 1
+        for (int it0 = tid; it0 < hin_items; it0 += IB * kThreads) {
+#pragma unroll
+            for (int u = 0; u < IB; ++u) {
+                const int it = it0 + u * kThreads;
+                if (it >= hin_items) continue;
+                const int q = it / D8, o = it % D8;
+                float acc[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+                for (int i = 0; i < N; ++i) {
+                    const float w = hps[q * N + i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[2 * e] = fmaf(w, x16_lo<H>(xv[u][i][e]), acc[2 * e]);
+                        acc[2 * e + 1] = fmaf(w, x16_hi<H>(xv[u][i][e]), acc[2 * e + 1]);
+                    }
+                }
+                u32x4 ov;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ov[e] = pack_x16<H>(acc[2 * e], acc[2 * e + 1]);
+                __builtin_amdgcn_raw_buffer_store_b128(ov, hr, (int)((uint32_t)(q * k.D + 8 * o) * 2), 0, 0);
+            }
+            if (it0 + IB * kThreads < hin_items) hin_batch(it0 + IB * kThreads);
+        }
     }
 }
 
@@ -1566,7 +1628,7 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
-// The four-kernel path's projection (same 64-token tiles and partial-record layout, so the
+// The classic path's projection (same 64-token tiles and partial-record layout, so the
 // epilogue and hIn kernels follow unchanged) for calls without pre_mix and with D a
 // multiple of 32, by persistent workgroups with a different split of K: slice s is the NKS
 // K-steps [NKS s, NKS s + NKS) of the flattened row (K-step g holds elements [32 g, 32 g + 32)
@@ -2230,25 +2292,30 @@ hipError_t launch_group(const Plan& p, const KArgs& k, hipStream_t st, void* con
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) e = mark(events, kStageProj + 1, st);
     if (e != hipSuccess) return e;
-    if (N == 4 && p.OB == 16)
-        hipLaunchKernelGGL((epilogue_kernel<N, A, 16>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
-    else
-        hipLaunchKernelGGL((epilogue_kernel<N, A, 8>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
+    // without pre_mix the epilogue also writes hIn (no hIn launch)
+    if (k.a.pre_mix) {
+        if (N == 4 && p.OB == 16)
+            hipLaunchKernelGGL((epilogue_kernel<N, A, 16>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
+        else
+            hipLaunchKernelGGL((epilogue_kernel<N, A, 8>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st, k);
+    } else {
+        if (N == 4 && p.OB == 16)
+            hipLaunchKernelGGL((epilogue_kernel<N, A, 16, true, H>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0,
+                               st, k);
+        else
+            hipLaunchKernelGGL((epilogue_kernel<N, A, 8, true, H>), dim3((unsigned)p.out_blocks), dim3(kThreads), 0, st,
+                               k);
+    }
     e = hipGetLastError();
     if (e == hipSuccess) e = mark(events, kStageEpi + 1, st);
-    if (e == hipSuccess && k.a.pre_mix) e = mark(events, kStageHin + 1, st);
-    if (e != hipSuccess || k.a.pre_mix) return e;
-    const int64_t items = p.T * (int64_t)(p.g.D / 8);
-    hipLaunchKernelGGL((hin_kernel<N, H>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, st, k.a.x, k.a.wts,
-                       k.a.h_in, p.T, p.g.D);
-    e = hipGetLastError();
-    return e == hipSuccess ? mark(events, kStageHin + 1, st) : e;
+    if (e == hipSuccess) e = mark(events, kStageHin + 1, st);
+    return e;
 }
 
 // Whether a kernel's code keeps everything in registers. The single-read kernel's x loads
 // are invisible to the compiler (inline assembly, waited for by hand): were it to spill
 // registers to scratch memory, it could spill or reuse a register such a load has yet to
-// write. The kernel is refused then (the four-kernel path serves), never run.
+// write. The kernel is refused then (the classic path serves), never run.
 bool no_scratch(const void* fn)
 {
     hipFuncAttributes at;
@@ -2461,7 +2528,7 @@ hipError_t launch_fused(const Plan& p, const ForwardArgs& a, int G, hipStream_t 
 
 }  // namespace
 
-// Whether the four-kernel path projects on the VALU (fp32 FMA) rather than the matrix
+// Whether the classic path projects on the VALU (fp32 FMA) rather than the matrix
 // cores: MHC_PROJECTION = "valu" or "mfma" decides; otherwise the measured choice, the
 // matrix cores (on MI355X the VALU projection kernel took 1.9 to 3.8 times as long on every
 // workload of the benchmark, fp32 FMA at about a third of the VALU's fp32 peak against a
@@ -2481,7 +2548,7 @@ static bool projection_on_valu(const Plan& p, const ForwardArgs& a)
 // pre_mix (whose hIn the projection kernel writes from registers, which needs all n streams
 // of a position in a lane), D not a multiple of 32, a variant it is not compiled for, code
 // that cannot run here, or MHC_FORWARD_PATH = "classic" / MHC_PROJECTION = "valu" asking
-// for the four-kernel path.
+// for the classic path.
 int stream_workgroups_per_slice(const Plan& p, bool has_pre_mix)
 {
     if (has_pre_mix || p.g.D % kBlock != 0) return 0;

@@ -71,7 +71,7 @@ constexpr int kFRing = 8;              // x register slots, one per round
 constexpr int kFAhead = 2;             // rounds between a tile's x loads and its projection
 constexpr int kFLag = kFRing - kFAhead;   // rounds between a tile's projection and its hIn
 constexpr int kFLoads = 4;             // x loads of a compute wave per round (one per stream, n = 4)
-constexpr int64_t kFMinTokens = 8192;  // below this the four-kernel path is used (ramp and drain dominate)
+constexpr int64_t kFMinTokens = 8192;  // below this the classic path is used (ramp and drain dominate)
 
 // Streaming projection (proj_stream_kernel): persistent workgroups of two halves of
 // kThreads, each half on its own 64-token tile of the workgroup's slice.
@@ -406,7 +406,7 @@ int launch_prepack(const Geometry& g, const float* phi, const float* gamma, void
 // weight pack, projection, epilogue and hIn kernels.
 int launch_forward(const Plan& p, const ForwardArgs& a, void* stream, void* const* events);
 // Which kernels launch_forward runs for this plan and these arguments on the current
-// device: 2 the one-launch kernel, 1 the single-read kernel, 0 the four-kernel path.
+// device: 2 the one-launch kernel, 1 the single-read kernel, 0 the classic path.
 int forward_path(const Plan& p, bool has_pre_mix);
 int record_event(void* event, void* stream);
 // Reads the workspace's time-out flag (sync word 1) after synchronising the stream, then

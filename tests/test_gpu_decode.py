@@ -7,7 +7,7 @@ the output set without intermediates, packed and unpacked weights, repeated
 calls through one workspace (each call's tag comes from flag words every call advances),
 packed weights passed in (then two d-blocks a workgroup where there are still as many
 workgroups as tokens: one token, an odd block count, a partial last block, 512 blocks),
-the same inputs on the four-kernel path, and a wait time-out driven from the host (a test
+the same inputs on the classic path, and a wait time-out driven from the host (a test
 switch makes every poll accept no tag, so each gives up at its limit; every workgroup
 still exits normally) that must leave NaN outputs and show through mhc_pre_wait_status."""
 import sys
@@ -139,7 +139,7 @@ def test_decode_repeated_calls_and_prepacked(D, monkeypatch):
 def test_decode_and_four_kernel_path_agree_with_oracle(monkeypatch):
     # the same inputs through both paths (different summation groupings): each meets the
     # oracle's acceptance rule
-    print("[case] one-launch vs four-kernel T=37 D=3072", file=sys.stderr, flush=True)
+    print("[case] one-launch vs classic T=37 D=3072", file=sys.stderr, flush=True)
     inp = synth.custom(37, 4, 3072, gamma=True, need_backward=True, seed=163)
     orc = run_oracle(inp)
     monkeypatch.delenv("MHC_FORWARD_PATH", raising=False)

@@ -2,7 +2,7 @@
 no path records a memset or a host synchronisation, so each can be captured (the
 one-launch path in the first two cases, whose kernel clears its barrier counters in the
 workspace at its end; the streaming path at 4096 tokens, with packed and unpacked weights;
-the four-kernel path, forced by MHC_FORWARD_PATH=classic; the single-read path forced by
+the classic path, forced by MHC_FORWARD_PATH=classic; the single-read path forced by
 MHC_FORWARD_PATH=fused in the last case: its kernel
 and the epilogue keep the call counter and the per-XCD arrival counters in the workspace,
 which each replay advances and clears as an eager call does). Every replay, with eager work of

@@ -93,7 +93,7 @@ def test_single_read_reproducible_and_repeated_calls(monkeypatch):
 
 
 def test_classic_path_still_served(monkeypatch):
-    # the four-kernel path on a shape the single-read kernel would take
+    # the classic path on a shape the single-read kernel would take
     monkeypatch.setenv("MHC_FORWARD_PATH", "classic")
     print("[case] classic forced T=8192 D=2048", file=sys.stderr, flush=True)
     inp = synth.custom(8192, 4, 2048, need_backward=True, seed=59)

@@ -6,10 +6,10 @@ with D a multiple of 32, that the single-read and one-launch kernels do not take
 oracle under the acceptance rule of gpu_helpers at small and ragged sizes: a partial last
 64-token tile, fewer tiles than the workgroups of a slice (halves with no task), a partial last
 slice (K-steps past the data), gamma, packed and unpacked weights. Its slices group the
-partial sums differently from the four-kernel path's, so the two agree with the oracle, not
+partial sums differently from the classic path's, so the two agree with the oracle, not
 bit for bit; the weights it splits itself must give the same bits as weights packed
 beforehand (gathered from the d-block-major packed layout), and repeated calls the same bits.
-With pre_mix, or D not a multiple of 32, the four-kernel path serves."""
+With pre_mix, or D not a multiple of 32, the classic path serves."""
 import sys
 
 import numpy as np
@@ -60,7 +60,7 @@ def test_stream_parity(name, T, n, D, na, gamma, nb, f16, seed, monkeypatch):
                                              (4100, 8, 2048, 2, True, 0), (300, 4, 1000, 3, False, 0),
                                              (300, 4, 992, 3, False, 3)])
 def test_stream_not_taken(T, n, D, na, pm, want, monkeypatch):
-    # with pre_mix or D not a multiple of 32 the four-kernel path serves, and meets the oracle
+    # with pre_mix or D not a multiple of 32 the classic path serves, and meets the oracle
     # (n = 8, alpha[2] with pre_mix at T = 4100: its 32-K-step slices and a partial last tile)
     monkeypatch.delenv("MHC_FORWARD_PATH", raising=False)
     print(f"[case] path T={T} n={n} D={D} alpha[{na}] pre_mix={pm}", file=sys.stderr, flush=True)

@@ -1,4 +1,4 @@
-"""The projection on the VALU (fp32 FMA, MHC_PROJECTION=valu) on the four-kernel path,
+"""The projection on the VALU (fp32 FMA, MHC_PROJECTION=valu) on the classic path,
 against the fp64 oracle under the acceptance rule of gpu_helpers: every M <= 32 variant
 (n = 4 with alpha[3] and alpha[2], n = 8 and n = 6 with alpha[2]), pre_mix (hIn written
 by the projection), gamma, partial last d-blocks and tiles, fp16 x, and both slice sizes
