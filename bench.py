@@ -13,8 +13,10 @@ Measured in this run:
   roofline     of the dominant kernel (the one with the largest average duration), its
                duration from HIP events that the library records on the launch stream around
                each of its kernels (mhc_pre_forward_timed), in a second pass of K steps, each
-               preceded (outside the events) by a 512 MiB write that evicts the 256 MB
+               preceded (outside the events) by a 512 MiB read that evicts the 256 MB
                Infinity Cache, so that no step reads its inputs from the previous step's cache
+               (a read leaves only clean lines behind: a write's dirty lines would be written
+               back during the next kernel and charged to it)
                lines (decode is timed back to back without it);
   waits_timed_out  mhc_pre_wait_status after the timed steps (1: a single-read wait gave up);
   cpu_baseline the fp64 C oracle on the host cores, on a bounded sample of tokens.
@@ -394,7 +396,7 @@ def main():
                     help="after the timed steps, time this many back-to-back calls with weights "
                          "packed once beforehand (mhc_pre_prepack), as a serving loop calls it")
     ap.add_argument("--flush-mib", type=int, default=512,
-                    help="size of the write that evicts the Infinity Cache before each step of the "
+                    help="size of the read that evicts the Infinity Cache before each step of the "
                          "per-kernel pass (0: none; decode never flushes)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run a plain copy of this size first (for counter calibration)")
@@ -479,10 +481,17 @@ def main():
     # pack and hIn stages of the single-read path, the pack stage of the streaming path and
     # its hIn stage with pre_mix; all but the one kernel of the one-launch
     # path) are not recorded: each record costs a few microseconds on the stream. Before each step (outside its events) a 512 MiB
-    # write evicts the Infinity Cache, except for decode (launch-bound, back to back).
+    # read evicts the Infinity Cache, except for decode (launch-bound, back to back). A read,
+    # not a write: a write would leave 256 MB of dirty lines that the next kernel's misses
+    # write back to HBM, charging that kernel with traffic that is not its own (a 32 µs
+    # projection measured 56 µs after such a write). The buffer is filled once, and the sync
+    # below lets those dirty lines drain before the pass.
     flush = None
+    flush_sink = None
     if args.flush_mib > 0 and wl.name != "decode":
-        flush = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+        flush = torch.full((args.flush_mib << 18,), 1, dtype=torch.int32, device=dev)
+        flush_sink = torch.empty((), dtype=torch.int32, device=dev)
+        torch.sum(flush, dim=0, dtype=torch.int32, out=flush_sink)
     wanted = [True] * mhc.FORWARD_EVENTS
     if single_read:
         wanted[0] = wanted[-1] = False
@@ -503,11 +512,11 @@ def main():
           file=sys.stderr, flush=True)
     for step, row in enumerate(evs):
         if flush is not None:
-            flush.fill_(step & 0xFF)
+            torch.sum(flush, dim=0, dtype=torch.int32, out=flush_sink)
         run(x, phi, alpha, bias, gamma, pre_mix, out=out, events=row)
     torch.cuda.synchronize(dev)
     waits_timed_out |= run.wait_status()
-    del flush
+    del flush, flush_sink
 
     kernels = {}
     for i, stage in enumerate(mhc.STAGES):
