@@ -110,6 +110,47 @@ static int check(int n, int D, int na, long long T, bool pm)
     if (((long long)rec_loc(p.S - 1, 63, n, g.M) + rs) * 4 != recb)
         return fail("record local", n, D, na, T, rec_loc(p.S - 1, 63, n, g.M), recb / 4);
     if ((rec_loc(0, 1, n, g.M) * 4) % 16) return fail("record alignment", n, D, na, T, 0, 0);
+    // streaming projection (no pre_mix, D a multiple of 32, the variants it is compiled for):
+    // slice s holds K-steps [s NKS, s NKS + NKS) of the flattened row; every K-step with data
+    // lies in exactly one slice; each lane's x octet stays inside its token's row; the gather
+    // from the d-block-major packed layout reads inside the packed buffer (K-steps past the
+    // data: its first zero K-step); the in-kernel split reads inside phi and gamma; a slice's
+    // weights and both halves' column totals fit LDS; the grid's halves cover every tile once
+    const bool stream_variant = (n == 4 && p.NKS == 16) || (n == 8 && na == 2 && p.NKS == 16) ||
+                                (n == 6 && na == 2 && p.NKS == 12);
+    if (!pm && D % kBlock == 0 && stream_variant) {
+        if (!stream_fits(n, na, p.NKS)) return fail("stream LDS", n, D, na, T, p.NKS, 0);
+        const int nblk = D / kBlock, nks = n * nblk;
+        if (nks != g.nks || (long long)nks * kBlock != g.K) return fail("stream K-steps", n, D, na, T, nks, g.nks);
+        const long long units = (long long)(g.nks + kPadSteps) * 4 * g.NC;
+        for (int sl = 0; sl < p.S; ++sl)
+            for (int st = 0; st < p.NKS; ++st) {
+                const int gk = sl * p.NKS + st;
+                if (gk >= nks) continue;   // past the data: x reads out of range, weights the zero step
+                const long long xlast = 63LL * g.K + (long long)kBlock * gk + 8 * 3 + 8;   // elements, exclusive
+                if (xlast > 64LL * g.K || (long long)kBlock * gk + 32 > g.K) return fail("stream x", n, D, na, T, gk, xlast);
+                const long long pst = (long long)(gk % nblk) * n + gk / nblk;
+                if (pst < 0 || pst >= nks || (pst + 1) * 4 * g.NC > units) return fail("stream gather", n, D, na, T, gk, pst);
+                // the packed K-step holds stream gk / nblk, d-block gk % nblk: the same 32 elements
+                if ((pst % n) * (long long)D + kBlock * (pst / n) != (long long)kBlock * gk)
+                    return fail("stream K order", n, D, na, T, gk, pst);
+            }
+        if ((long long)(nks + 1) * 4 * g.NC > units) return fail("stream zero step", n, D, na, T, nks, units);
+        for (int cus : {256, 304, 80}) {
+            long long W = cus / p.S;
+            if (W > (p.tiles + 1) / 2) W = (p.tiles + 1) / 2;
+            if (W < 1) W = 1;
+            const long long NI = (p.tiles + 2 * W - 1) / (2 * W);
+            std::vector<unsigned char> seen((size_t)p.tiles + 1, 0);
+            for (long long h = 0; h < 2 * W; ++h)
+                for (long long it = 0; it < NI; ++it) {
+                    const long long tile = h + 2 * W * it;
+                    if (tile < p.tiles && seen[(size_t)tile]++) return fail("stream tile twice", n, D, na, T, tile, W);
+                }
+            for (long long t = 0; t < p.tiles; ++t)
+                if (!seen[(size_t)t]) return fail("stream tile missed", n, D, na, T, t, W);
+        }
+    }
     // epilogue workgroups: 8 tokens each, inside one tile
     const int ob = p.OB;
     if (ob != out_tokens(n, T) || (ob != 8 && ob != 16)) return fail("epilogue token count", n, D, na, T, ob, 0);
