@@ -238,7 +238,7 @@ mhc_status mhc_pre_wait_status(void* workspace, size_t workspace_bytes, void* st
 mhc_status mhc_pre_forward_path(const mhc_pre_params* params, int32_t has_pre_mix, int32_t* path);
 
 /* Events mhc_pre_forward_timed records: one before the first kernel and one after each
- * of the forward's four kernels. */
+ * of the forward's four stages (weight pack, projection, epilogue, hIn). */
 #define MHC_FORWARD_EVENTS 5
 
 /* mhc_pre_forward, plus per-kernel timing: also records the caller's events (hipEvent_t
@@ -247,11 +247,12 @@ mhc_status mhc_pre_forward_path(const mhc_pre_params* params, int32_t has_pre_mi
  *   events[1] after it, before the projection kernel,
  *   events[2] after the projection kernel,
  *   events[3] after the per-token epilogue kernel,
- *   events[4] after the hIn kernel.
- * A kernel the call does not launch (the pack when phi_packed is given or on the
- * single-read and one-launch paths, which pack inside their kernel; the epilogue and hIn
- * kernels on the one-launch path; the hIn kernel when pre_mix is given or on the
- * single-read path: the projection writes hIn then) has its two events recorded
+ *   events[4] after the hIn stage, which launches no kernel on any forward path (the
+ *     projection writes hIn with pre_mix and on the single-read path, the epilogue
+ *     otherwise).
+ * A stage the call does not launch a kernel for (the pack when phi_packed is given or on
+ * the streaming, single-read and one-launch paths, which pack inside their kernel; the
+ * epilogue on the one-launch path; the hIn stage always) has its two events recorded
  * back to back, so elapsed time between events[i] and events[i+1] is kernel i's duration
  * (plus the launch gap) whatever the inputs; with T == 0 all five are recorded back to
  * back. A NULL entry is not recorded: a caller that only wants some boundaries (each
